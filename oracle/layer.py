@@ -1,0 +1,81 @@
+"""Oracle: the whole routed MoE FFN layer.
+
+TEST INFRASTRUCTURE ONLY (see the package docstring).
+
+route -> dispatch -> each distinct expert applied once to all of its rows
+(batch-union; "Show HN: colibri", section "What's implemented") -> combine:
+
+    out[t] = sum_j w[t, j] * Y[inv_perm[t*k + j]]  +  S[t]
+
+where Y holds the un-weighted expert outputs in permuted order and S is the
+shared expert ("Show HN: colibri": shared expert), an FFN of the same format
+applied to every token with weight 1 (no gate on the shared expert: the pages
+name none).
+"""
+from __future__ import annotations
+
+import dataclasses
+from typing import Callable, Optional
+
+import numpy as np
+
+from . import dispatch as dispatch_mod
+from . import ffn, router
+
+
+@dataclasses.dataclass
+class RouterSpec:
+    mode: str                    # "softmax" | "noaux_tc"
+    top_k: int
+    renormalize: bool = False
+    n_group: int = 1
+    topk_group: int = 1
+    routed_scaling_factor: float = 1.0
+    bias: Optional[np.ndarray] = None
+
+
+def route(x, wg, spec: RouterSpec):
+    if spec.mode == "softmax":
+        return router.route_softmax(x, wg, spec.top_k, spec.renormalize)
+    if spec.mode == "noaux_tc":
+        return router.route_noaux_tc(x, wg, spec.bias, spec.top_k, spec.n_group,
+                                     spec.topk_group, spec.routed_scaling_factor)
+    raise ValueError(f"unknown router mode {spec.mode}")
+
+
+def expert_rows(x, ex: ffn.QuantExpert, act_mode: str):
+    if act_mode == "f32":
+        return ffn.ffn_f32(x, ex)
+    if act_mode == "q8_0":
+        return ffn.ffn_q8(x, ex)[0]
+    raise ValueError(f"unknown act_mode {act_mode}")
+
+
+def combine(y_perm, w, inv_perm, shared_y=None):
+    t, k = w.shape
+    gathered = y_perm[np.asarray(inv_perm).reshape(t, k)]        # [T, k, d]
+    out = np.einsum("tk,tkd->td", np.asarray(w, np.float64), gathered)
+    if shared_y is not None:
+        out = out + shared_y
+    return out
+
+
+def layer_forward(x, wg, spec: RouterSpec, get_expert: Callable[[int], ffn.QuantExpert],
+                  shared: Optional[ffn.QuantExpert], act_mode: str):
+    """Returns a dict with idx, w, counts, offsets, perm, inv_perm, y_perm,
+    shared_y and out (fp64 [T, d])."""
+    x = np.asarray(x, np.float32)
+    n_experts = wg.shape[0]
+    idx, w, l = route(x, wg, spec)
+    counts, offsets, perm, inv = dispatch_mod.dispatch(idx, n_experts)
+    k = spec.top_k
+    t, d = x.shape
+    y_perm = np.zeros((t * k, d), dtype=np.float64)
+    for e in np.nonzero(counts)[0]:
+        lo, hi = offsets[e], offsets[e + 1]
+        tokens = perm[lo:hi] // k
+        y_perm[lo:hi] = expert_rows(x[tokens], get_expert(int(e)), act_mode)
+    shared_y = expert_rows(x, shared, act_mode) if shared is not None else None
+    out = combine(y_perm, w, inv, shared_y)
+    return dict(idx=idx, w=w, logits=l, counts=counts, offsets=offsets, perm=perm,
+                inv_perm=inv, y_perm=y_perm, shared_y=shared_y, out=out)

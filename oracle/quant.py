@@ -1,0 +1,118 @@
+"""Oracle: group-32 weight quantisation, int4 packing, Q8_0 activations.
+
+TEST INFRASTRUCTURE ONLY (see the package docstring).
+
+Weights ("mtlm-7m-base", section "Files": int8 export with group size 32;
+"Show HN: colibri", section "What's implemented": int8 / packed int4
+quantisation, dequantised on use). Each row of a matrix is cut into groups of
+32 consecutive elements along its input (reduction) axis; a group keeps one
+fp32 scale s and signed integer codes q with s*q approximating the weights:
+
+    amax = max |w| over the group
+    s    = amax / qmax            (qmax = 127 for int8, 7 for int4; fp32 divide)
+    q    = clamp(rne(w / s), -qmax, qmax)   (fp32 divide, round half to even)
+    amax == 0  ->  s = 0, q = 0
+
+The pages give no formula beyond "group size 32", "per-group scale" and
+"symmetric"; the symmetric absmax scale with round-half-to-even is the plainest
+reading. Codes are decided in fp32 so that a GPU quantiser can match them bit
+for bit.
+
+Packed int4 ("two nibbles per byte", symmetric): element 2i sits in the low
+nibble of byte i and element 2i+1 in the high nibble, each as a 4-bit two's
+complement number.
+
+Activations ("Show HN: colibri", section "What's implemented": Q8_0-style int8
+activations). Each row is cut into groups of 32; a group keeps an fp32 scale d
+and int8 codes, all steps in fp32:
+
+    amax = max |x|;  d = amax / 127;  id = (d == 0) ? 0 : 1 / d
+    q    = clamp(rne(x * id), -127, 127)
+"""
+from __future__ import annotations
+
+import numpy as np
+
+GROUP = 32
+
+
+def _groups(a: np.ndarray) -> np.ndarray:
+    if a.shape[-1] % GROUP:
+        raise ValueError(f"last dimension {a.shape[-1]} is not a multiple of {GROUP}")
+    return a.reshape(a.shape[:-1] + (a.shape[-1] // GROUP, GROUP))
+
+
+def qmax_for_bits(bits: int) -> int:
+    if bits == 8:
+        return 127
+    if bits == 4:
+        return 7
+    raise ValueError(f"unsupported weight bits {bits}")
+
+
+def quantize_weights(w: np.ndarray, bits: int):
+    """Group-32 symmetric quantisation of fp32 weights along the last axis.
+
+    Returns (q, s): q int8 codes with the shape of w, s fp32 scales with the
+    last axis divided by 32.
+    """
+    w = np.asarray(w, dtype=np.float32)
+    g = _groups(w)
+    qmax = np.float32(qmax_for_bits(bits))
+    amax = np.max(np.abs(g), axis=-1)
+    s = (amax / qmax).astype(np.float32)
+    q = np.zeros(g.shape, dtype=np.float32)
+    nz = s > 0
+    if np.any(nz):
+        r = g[nz] / s[nz][:, None]          # fp32 / fp32 -> fp32, IEEE rounding
+        q[nz] = np.clip(np.rint(r), -qmax, qmax)
+    return q.astype(np.int8).reshape(w.shape), s
+
+
+def dequantize(q: np.ndarray, s: np.ndarray) -> np.ndarray:
+    """s * q in fp64 (exact: an fp32 scale times a small integer)."""
+    g = _groups(np.asarray(q).astype(np.float64))
+    return (g * np.asarray(s, dtype=np.float64)[..., None]).reshape(np.shape(q))
+
+
+def pack_int4(q: np.ndarray) -> np.ndarray:
+    """Pack int4 codes (int8 array, values in [-8, 7]) two per byte."""
+    q = np.asarray(q)
+    if q.shape[-1] % 2:
+        raise ValueError("int4 packing needs an even last dimension")
+    if q.min(initial=0) < -8 or q.max(initial=0) > 7:
+        raise ValueError("int4 code out of range")
+    u = q.astype(np.int16) & 0xF
+    lo = u[..., 0::2]
+    hi = u[..., 1::2]
+    return (lo | (hi << 4)).astype(np.uint8)
+
+
+def unpack_int4(b: np.ndarray) -> np.ndarray:
+    """Inverse of pack_int4: bytes -> int8 codes (sign-extended nibbles)."""
+    b = np.asarray(b, dtype=np.uint8).astype(np.int16)
+    lo = b & 0xF
+    hi = (b >> 4) & 0xF
+    lo = np.where(lo >= 8, lo - 16, lo)
+    hi = np.where(hi >= 8, hi - 16, hi)
+    out = np.empty(b.shape[:-1] + (b.shape[-1] * 2,), dtype=np.int8)
+    out[..., 0::2] = lo
+    out[..., 1::2] = hi
+    return out
+
+
+def quantize_q8_0(x: np.ndarray):
+    """Q8_0-style activation quantisation along the last axis, fp32 steps.
+
+    Returns (q int8 with the shape of x, d fp32 with the last axis / 32).
+    """
+    x = np.asarray(x, dtype=np.float32)
+    g = _groups(x)
+    amax = np.max(np.abs(g), axis=-1)
+    d = (amax / np.float32(127)).astype(np.float32)
+    idv = np.zeros_like(d)
+    nz = d != 0
+    idv[nz] = np.float32(1) / d[nz]
+    prod = (g * idv[..., None]).astype(np.float32)   # fp32 multiply, no fusion
+    q = np.clip(np.rint(prod), -127, 127).astype(np.int8)
+    return q.reshape(x.shape), d

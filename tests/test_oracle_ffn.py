@@ -1,0 +1,170 @@
+"""Pins for the oracle's expert FFN and whole layer (CPU only).
+
+Dense masked evaluation (every expert applied to every token, weighted by the
+routing mask) against the sparse batch-union path; special cases that reduce
+to a dense SwiGLU or a dense softmax mixture; closed forms of SiLU and the
+SwiGLU orientation; brute-force integer dots; the Q8_0 error bound.
+"""
+import math
+
+import numpy as np
+import pytest
+
+from oracle import ffn, layer, quant
+import synth
+
+
+def _tiny_experts(lay, bits=None):
+    bits = bits or (8 if lay.wformat == "int8" else 4)
+    return [ffn.QuantExpert.from_fp32(synth.expert_weight(lay, e, "gate"),
+                                      synth.expert_weight(lay, e, "up"),
+                                      synth.expert_weight(lay, e, "down"), bits)
+            for e in range(lay.n_experts + (1 if lay.shared_expert else 0))]
+
+
+def _spec(lay, **over):
+    kw = dict(mode=lay.router, top_k=lay.top_k, renormalize=lay.renormalize,
+              n_group=lay.n_group, topk_group=lay.topk_group,
+              routed_scaling_factor=lay.routed_scaling_factor, bias=synth.score_bias(lay))
+    kw.update(over)
+    return layer.RouterSpec(**kw)
+
+
+def test_silu_closed_forms():
+    g = np.array([0.0, 30.0, -30.0, 1.0, -1.0])
+    s = ffn.silu(g)
+    assert s[0] == 0.0
+    assert abs(s[1] - 30.0) < 1e-9 and abs(s[2]) < 1e-9
+    assert abs((s[3] - s[4]) - 1.0) < 1e-15          # silu(x) - silu(-x) = x
+    assert abs(s[3] - 1.0 / (1.0 + math.exp(-1.0))) < 1e-15
+
+
+def test_swiglu_orientation_is_silu_of_gate_times_up():
+    # one-hot token through hand-built weights whose group scales are exact
+    # powers of two (amax = 127 * 2^-n): G = 127/64, U = 127/256
+    d, i = 32, 32
+    gate = np.zeros((i, d), np.float32)
+    up = np.zeros((i, d), np.float32)
+    down = np.zeros((d, i), np.float32)
+    gate[0, 0] = 127 / 64
+    up[0, 0] = 127 / 256
+    down[0, 0] = 127 / 128
+    ex = ffn.QuantExpert.from_fp32(gate, up, down, 8)
+    x = np.zeros((1, d), np.float32)
+    x[0, 0] = 1.0
+    y = ffn.ffn_f32(x, ex)
+    g, u = 127 / 64, 127 / 256
+    want = g / (1.0 + math.exp(-g)) * u * (127 / 128)  # silu(gate) * up, through down
+    assert ex.gate_s[0, 0] == 1 / 64 and ex.up_s[0, 0] == 1 / 256
+    assert abs(y[0, 0] - want) < 1e-12
+    assert abs(y[0, 0] - u / (1 + math.exp(-u)) * g * (127 / 128)) > 0.1   # swapped orientation
+
+
+@pytest.mark.parametrize("act_mode", ["f32", "q8_0"])
+def test_dense_masked_equals_sparse_tiny(act_mode):
+    lay = synth.LAYERS["tiny"]
+    x = synth.activations(lay, 16)
+    wg = synth.gate_weight(lay)
+    exps = _tiny_experts(lay)
+    spec = _spec(lay)
+    r = layer.layer_forward(x, wg, spec, lambda e: exps[e], None, act_mode)
+    # dense: every expert on every token, weighted by the routing mask
+    mask = np.zeros((16, lay.n_experts))
+    for t in range(16):
+        for j in range(lay.top_k):
+            mask[t, r["idx"][t, j]] += r["w"][t, j]
+    dense = np.zeros((16, lay.d_model))
+    for e in range(lay.n_experts):
+        ye = layer.expert_rows(x, exps[e], act_mode)
+        dense += mask[:, e:e + 1] * ye
+    assert np.allclose(r["out"], dense, rtol=0, atol=1e-12 * np.abs(dense).max())
+
+
+def test_single_expert_is_dense_swiglu():
+    lay = synth.variant(synth.LAYERS["tiny"], n_experts=1, top_k=1, renormalize=True)
+    x = synth.activations(lay, 16)
+    wg = synth.gate_weight(lay)
+    exps = _tiny_experts(lay)
+    r = layer.layer_forward(x, wg, _spec(lay), lambda e: exps[e], None, "f32")
+    assert np.all(r["idx"] == 0) and np.allclose(r["w"], 1.0)
+    wgt, wup, wdn = (quant.dequantize(q, s) for q, s in
+                     [(exps[0].gate_q, exps[0].gate_s), (exps[0].up_q, exps[0].up_s),
+                      (exps[0].down_q, exps[0].down_s)])
+    x64 = x.astype(np.float64)
+    g = x64 @ wgt.T
+    dense = ((g / (1 + np.exp(-g))) * (x64 @ wup.T)) @ wdn.T
+    assert np.allclose(r["out"], dense, rtol=1e-12, atol=1e-14)
+
+
+def test_all_experts_is_softmax_mixture():
+    lay = synth.variant(synth.LAYERS["tiny"], top_k=8, renormalize=False)
+    x = synth.activations(lay, 16)
+    wg = synth.gate_weight(lay)
+    exps = _tiny_experts(lay)
+    r = layer.layer_forward(x, wg, _spec(lay), lambda e: exps[e], None, "f32")
+    l = x.astype(np.float64) @ wg.astype(np.float64).T
+    p = np.exp(l - l.max(1, keepdims=True))
+    p /= p.sum(1, keepdims=True)
+    mix = sum(p[:, e:e + 1] * ffn.ffn_f32(x, exps[e]) for e in range(8))
+    assert np.allclose(r["out"], mix, rtol=1e-11, atol=1e-14)
+
+
+def test_shared_expert_adds_with_weight_one():
+    lay = synth.variant(synth.LAYERS["tiny"], shared_expert=True)
+    x = synth.activations(lay, 16)
+    wg = synth.gate_weight(lay)
+    exps = _tiny_experts(lay)
+    base = layer.layer_forward(x, wg, _spec(lay), lambda e: exps[e], None, "f32")
+    withs = layer.layer_forward(x, wg, _spec(lay), lambda e: exps[e], exps[lay.n_experts], "f32")
+    s = ffn.ffn_f32(x, exps[lay.n_experts])
+    assert np.allclose(withs["out"] - base["out"], s, rtol=1e-12, atol=1e-15)
+
+
+def test_group_dots_brute_force_python_ints():
+    rng = np.random.default_rng(4)
+    a = rng.integers(-127, 128, size=(3, 64)).astype(np.int8)
+    b = rng.integers(-127, 128, size=(5, 64)).astype(np.int8)
+    a[0, :32] = -127
+    b[0, :32] = -127                                   # the extreme group: 32*127*127
+    got = ffn.group_dots(a, b)
+    for m in range(3):
+        for n in range(5):
+            for g in range(2):
+                want = sum(int(a[m, k]) * int(b[n, k]) for k in range(32 * g, 32 * g + 32))
+                assert got[m, n, g] == want
+    assert got[0, 0, 0] == 32 * 127 * 127 and got[0, 0, 0] < 2 ** 31
+
+
+def test_q8_integer_dots_equal_product_form():
+    lay = synth.LAYERS["tiny"]
+    x = synth.activations(lay, 16)
+    ex = _tiny_experts(lay)[3]
+    _, parts = ffn.ffn_q8(x, ex)
+    dots = ffn.group_dots(parts["xq"], ex.gate_q)                     # [16, I, G]
+    g_int = np.einsum("mg,ng,mng->mn", parts["xd"].astype(np.float64),
+                      ex.gate_s.astype(np.float64), dots.astype(np.float64))
+    assert np.allclose(g_int, parts["g"], rtol=1e-13, atol=1e-15)
+
+
+def test_q8_vs_f32_first_projection_bound():
+    lay = synth.LAYERS["olmoe"]
+    x = synth.activations(lay, 4)
+    gate = synth.expert_weight(lay, 0, "gate")[:64]
+    q, s = quant.quantize_weights(gate, 8)
+    w = quant.dequantize(q, s)
+    xq, xd = quant.quantize_q8_0(x)
+    g_q8 = quant.dequantize(xq, xd) @ w.T
+    g_f32 = x.astype(np.float64) @ w.T
+    # |x - dequant(Q8_0(x))| <= d/2 per element, so the error is bounded by sum |w| d/2
+    bound = (np.abs(w)[None, :, :] * np.repeat(xd.astype(np.float64), 32, axis=1)[:, None, :] / 2).sum(-1)
+    assert np.all(np.abs(g_q8 - g_f32) <= bound * (1 + 1e-6))
+
+
+def test_layer_noaux_tc_weights_sum_to_scaling_factor():
+    lay = synth.variant(synth.LAYERS["tiny"], router="noaux_tc", n_group=4, topk_group=2,
+                        routed_scaling_factor=2.5, has_bias=True, n_experts=16, top_k=3)
+    x = synth.activations(lay, 16)
+    wg = synth.gate_weight(lay)
+    exps = _tiny_experts(lay)
+    r = layer.layer_forward(x, wg, _spec(lay), lambda e: exps[e], None, "f32")
+    assert np.allclose(r["w"].sum(1), 2.5, rtol=1e-12)

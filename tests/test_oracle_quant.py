@@ -1,0 +1,149 @@
+"""Pins for the oracle's quantisers (CPU only).
+
+Each check ties the oracle to something other than itself: numbers printed on
+the pages, hand-worked examples of the adopted definitions, bounds that hold
+for any correct round-to-nearest quantiser, and brute force over integer
+codes.
+"""
+import json
+import os
+
+import numpy as np
+import pytest
+
+from oracle import quant
+import synth
+
+
+def test_int8_g32_error_within_page_bound(golden_dir):
+    # mtlm-7m-base, section Files: int8 group-32 export, max abs error 1.7e-3.
+    bound = json.load(open(os.path.join(golden_dir, "page_numbers.json")))["int8_g32_max_abs_error"]["value"]
+    w = synth.expert_weight(synth.LAYERS["olmoe"], 0, "gate")
+    q, s = quant.quantize_weights(w, 8)
+    err = np.abs(quant.dequantize(q, s) - w.astype(np.float64)).max()
+    assert err <= bound
+    # and it is a round-to-nearest error, i.e. well below half a step of the largest scale
+    assert err <= 0.5 * s.max() * (1 + 1e-5)
+
+
+@pytest.mark.parametrize("bits", [8, 4])
+def test_round_trip_half_step_and_amax(bits):
+    rng = np.random.default_rng(7)
+    w = (rng.standard_normal((37, 96)) * rng.uniform(1e-4, 3, (37, 1))).astype(np.float32)
+    w[3, 32:64] = 0.0                                   # an all-zero group
+    q, s = quant.quantize_weights(w, bits)
+    qmax = 127 if bits == 8 else 7
+    assert q.dtype == np.int8 and s.dtype == np.float32
+    assert q.min() >= -qmax and q.max() <= qmax
+    deq = quant.dequantize(q, s)
+    step = np.repeat(s.astype(np.float64), 32, axis=1)
+    assert np.all(np.abs(w - deq) <= 0.5 * step * (1 + 1e-5) + 1e-30)
+    # the amax element of each non-zero group maps to +-qmax
+    g = w.reshape(37, 3, 32)
+    qa = q.reshape(37, 3, 32)
+    for r in range(37):
+        for j in range(3):
+            if s[r, j] == 0:
+                assert np.all(qa[r, j] == 0) and np.all(g[r, j] == 0)
+                continue
+            a = np.argmax(np.abs(g[r, j]))
+            assert abs(int(qa[r, j, a])) == qmax
+            assert np.sign(qa[r, j, a]) == np.sign(g[r, j, a])
+    assert s[3, 1] == 0 and np.all(q[3, 32:64] == 0)
+
+
+@pytest.mark.parametrize("bits", [8, 4])
+def test_codes_are_nearest_integers_brute_force(bits):
+    # brute force: for each element, no other code in range lands closer to w/s
+    rng = np.random.default_rng(11)
+    w = (rng.standard_normal((4, 64)) * 0.02).astype(np.float32)
+    q, s = quant.quantize_weights(w, bits)
+    qmax = 127 if bits == 8 else 7
+    codes = np.arange(-qmax, qmax + 1)
+    for r in range(4):
+        for c in range(64):
+            sc = float(s[r, c // 32])
+            ratio = float(w[r, c]) / sc
+            dist = np.abs(ratio - codes)
+            best = dist.min()
+            assert abs(ratio - int(q[r, c])) <= best + 1e-6
+
+
+def test_scale_is_amax_over_qmax_in_fp32():
+    w = np.zeros((1, 32), np.float32)
+    w[0, 5] = -0.3
+    w[0, 9] = 0.1
+    q8, s8 = quant.quantize_weights(w, 8)
+    q4, s4 = quant.quantize_weights(w, 4)
+    assert s8[0, 0] == np.float32(np.float32(0.3) / np.float32(127))
+    assert s4[0, 0] == np.float32(np.float32(0.3) / np.float32(7))
+    assert q8[0, 5] == -127 and q4[0, 5] == -7
+    # 0.1 / (0.3/127) = 42.33 -> 42 ; 0.1 / (0.3/7) = 2.33 -> 2
+    assert q8[0, 9] == 42 and q4[0, 9] == 2
+
+
+def test_int4_pack_matches_hand_worked_bytes(golden_dir):
+    for line in open(os.path.join(golden_dir, "int4_nibbles.txt")):
+        if line.startswith("#") or not line.strip():
+            continue
+        left, right = line.split("|")
+        codes = np.array([int(v) for v in left.split()], dtype=np.int8)
+        want = np.array([int(v, 16) for v in right.split()], dtype=np.uint8)
+        assert np.array_equal(quant.pack_int4(codes), want)
+        assert np.array_equal(quant.unpack_int4(want), codes)
+
+
+def test_int4_unpack_equals_int8_container():
+    # Show HN: colibri, section What's implemented: packing validated
+    # bit-identical to the int8 container. Every byte value round-trips.
+    allbytes = np.arange(256, dtype=np.uint8)
+    codes = quant.unpack_int4(allbytes)
+    assert codes.min() == -8 and codes.max() == 7
+    assert np.array_equal(quant.pack_int4(codes), allbytes)
+    w = (np.random.default_rng(3).standard_normal((16, 128)) * 0.02).astype(np.float32)
+    q, _ = quant.quantize_weights(w, 4)
+    assert np.array_equal(quant.unpack_int4(quant.pack_int4(q)), q)
+
+
+def test_q8_0_hand_worked_rounding(golden_dir):
+    for line in open(os.path.join(golden_dir, "q8_0_rounding.txt")):
+        if line.startswith("#") or not line.strip():
+            continue
+        xs, ds, qs = line.split("|")
+        x = np.array([float(v) for v in xs.split()], dtype=np.float32)[None, :]
+        want_q = np.array([int(v) for v in qs.split()], dtype=np.int8)[None, :]
+        assert x.shape == (1, 32) and want_q.shape == (1, 32)
+        q, d = quant.quantize_q8_0(x)
+        assert d[0, 0] == np.float32(float(ds))
+        assert np.array_equal(q, want_q)
+
+
+def test_q8_0_bounds_and_zero_group():
+    rng = np.random.default_rng(5)
+    x = rng.standard_normal((9, 64)).astype(np.float32)
+    x[2, :32] = 0
+    q, d = quant.quantize_q8_0(x)
+    assert np.all(q[2, :32] == 0) and d[2, 0] == 0
+    deq = quant.dequantize(q, d)
+    step = np.repeat(d.astype(np.float64), 32, axis=1)
+    assert np.all(np.abs(deq - x) <= 0.5 * step * (1 + 1e-5) + 1e-30)
+    g = np.abs(x.reshape(9, 2, 32))
+    a = g.argmax(axis=2)
+    qq = np.abs(q.reshape(9, 2, 32))
+    for r in range(9):
+        for j in range(2):
+            if d[r, j] > 0:
+                assert qq[r, j, a[r, j]] == 127
+
+
+def test_page_byte_accounting(golden_dir):
+    # Show HN: colibri, section The idea: ~19 MB per routed expert at int4;
+    # section Got a better machine?: ~11.4 GB of expert reads per cold token.
+    pn = json.load(open(os.path.join(golden_dir, "page_numbers.json")))
+    glm = synth.LAYERS["glm"]
+    payload = 0
+    for shape in [(glm.d_ff, glm.d_model), (glm.d_ff, glm.d_model), (glm.d_model, glm.d_ff)]:
+        payload += quant.pack_int4(np.zeros(shape, np.int8)).nbytes
+    assert abs(payload / 1e6 - pn["glm_routed_expert_mb_int4"]["value"]) < 0.5
+    cold = pn["glm_moe_layers"]["value"] * pn["glm_experts_per_token"]["value"] * payload
+    assert abs(cold / 1e9 - pn["glm_cold_token_gb"]["value"]) / pn["glm_cold_token_gb"]["value"] < 0.02

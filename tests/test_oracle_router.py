@@ -1,0 +1,163 @@
+"""Pins for the oracle's routers and dispatch (CPU only).
+
+Exhaustive search over expert and group subsets on tiny layers, exact-tie
+fixtures, closed-form weight sums, and special cases that reduce to a plainer
+router.
+"""
+import itertools
+
+import numpy as np
+import pytest
+
+from oracle import dispatch, router
+import synth
+
+
+def _beats(ka, ia, kb, ib):
+    """(key a, id a) is ranked before (key b, id b) under the tie rule."""
+    return ka > kb or (ka == kb and ia < ib)
+
+
+def _exhaustive_topk(keys, k):
+    """The unique subset whose every member beats every non-member."""
+    n = len(keys)
+    found = []
+    for sub in itertools.combinations(range(n), k):
+        rest = [j for j in range(n) if j not in sub]
+        if all(_beats(keys[a], a, keys[b], b) for a in sub for b in rest):
+            found.append(sub)
+    assert len(found) == 1
+    sub = list(found[0])
+    # order inside the subset: descending key, ties to lower id
+    sub.sort(key=lambda e: (-keys[e], e))
+    return sub
+
+
+@pytest.mark.parametrize("k", [1, 2, 3, 8])
+def test_softmax_topk_exhaustive_tiny(k):
+    lay = synth.LAYERS["tiny"]
+    x = synth.activations(lay, 16)
+    wg = synth.gate_weight(lay)
+    idx, w, l = router.route_softmax(x, wg, k, renormalize=False)
+    for t in range(16):
+        assert list(idx[t]) == _exhaustive_topk(list(l[t]), k)
+
+
+def test_softmax_weights_closed_forms():
+    lay = synth.LAYERS["tiny"]
+    x = synth.activations(lay, 16)
+    wg = synth.gate_weight(lay)
+    _, w_all, l = router.route_softmax(x, wg, 8, renormalize=False)
+    # k = E without renormalisation: the full softmax, which sums to 1
+    assert np.allclose(w_all.sum(axis=1), 1.0, atol=1e-12)
+    idx, w, _ = router.route_softmax(x, wg, 2, renormalize=False)
+    assert np.all(w.sum(axis=1) < 1.0)
+    # probability ratios are exp of logit differences
+    r = w[:, 0] / w[:, 1]
+    d = np.take_along_axis(l, idx, 1)
+    assert np.allclose(r, np.exp(d[:, 0] - d[:, 1]), rtol=1e-12)
+    idx2, w2, _ = router.route_softmax(x, wg, 2, renormalize=True)
+    assert np.array_equal(idx, idx2)
+    assert np.allclose(w2.sum(axis=1), 1.0, atol=1e-12)
+    assert np.allclose(w2, w / w.sum(axis=1, keepdims=True), rtol=1e-12)
+
+
+def test_exact_ties_go_to_lower_id():
+    x = np.random.default_rng(0).standard_normal((5, 64)).astype(np.float32)
+    wg = np.zeros((8, 64), np.float32)
+    idx, w, _ = router.route_softmax(x, wg, 3, renormalize=False)
+    assert np.all(idx == [0, 1, 2])
+    assert np.allclose(w, 1 / 8)
+    idx, w, _ = router.route_softmax(x, wg, 3, renormalize=True)
+    assert np.allclose(w, 1 / 3)
+    # duplicated rows: the lower id of the pair wins the tie
+    wg = (np.random.default_rng(1).standard_normal((8, 64)) * 0.02).astype(np.float32)
+    wg[6] = wg[2] = x[0] * 0.5       # both strongly aligned with token 0
+    idx, _, _ = router.route_softmax(x[:1], wg, 1, renormalize=False)
+    assert idx[0, 0] == 2
+    idx, _, _ = router.route_softmax(x[:1], wg, 2, renormalize=False)
+    assert list(idx[0]) == [2, 6]
+
+
+def _noaux_brute(l, b, k, n_group, topk_group, rsf):
+    s = 1 / (1 + np.exp(-l))
+    c = s + b
+    e = len(l)
+    gs = e // n_group
+    gscore = [sorted(c[g * gs:(g + 1) * gs])[::-1][:2] for g in range(n_group)]
+    gscore = [sum(v) for v in gscore]
+    kept = _exhaustive_topk(gscore, topk_group)
+    elig = [j for j in range(e) if j // gs in kept]
+    sub = _exhaustive_topk([c[j] for j in elig], k)
+    idx = [elig[j] for j in sub]
+    w = np.array([s[j] for j in idx])
+    return idx, w / w.sum() * rsf
+
+
+@pytest.mark.parametrize("e,n_group,topk_group,k", [(8, 4, 2, 2), (16, 4, 2, 3), (16, 8, 3, 4), (16, 2, 1, 8)])
+def test_noaux_tc_exhaustive(e, n_group, topk_group, k):
+    rng = np.random.default_rng(e * 100 + k)
+    x = rng.standard_normal((12, 64)).astype(np.float32)
+    wg = (rng.standard_normal((e, 64)) * 0.3).astype(np.float32)
+    b = (rng.standard_normal(e) * 0.1).astype(np.float32)
+    idx, w, l = router.route_noaux_tc(x, wg, b, k, n_group, topk_group, 2.5)
+    for t in range(12):
+        bi, bw = _noaux_brute(l[t], b.astype(np.float64), k, n_group, topk_group, 2.5)
+        assert list(idx[t]) == bi
+        assert np.allclose(w[t], bw, rtol=1e-12)
+    assert np.allclose(w.sum(axis=1), 2.5, rtol=1e-12)
+
+
+def test_noaux_tc_reduces_to_sigmoid_topk():
+    rng = np.random.default_rng(2)
+    x = rng.standard_normal((10, 32)).astype(np.float32)
+    wg = (rng.standard_normal((16, 32)) * 0.3).astype(np.float32)
+    idx, w, l = router.route_noaux_tc(x, wg, None, 4, 1, 1, 1.0)
+    idx_s, _, _ = router.route_softmax(x, wg, 4, renormalize=False)
+    assert np.array_equal(idx, idx_s)       # sigmoid is monotone
+    s = 1 / (1 + np.exp(-np.take_along_axis(l, idx, 1)))
+    assert np.allclose(w, s / s.sum(axis=1, keepdims=True), rtol=1e-12)
+
+
+def test_noaux_tc_group_score_is_top2_sum_not_max():
+    # group 0 = experts 0..3, group 1 = experts 4..7 (n_group 2, keep 1)
+    # group 0 has the single best expert; group 1 has the better top-2 sum
+    s = np.array([0.95, 0.05, 0.05, 0.05, 0.80, 0.78, 0.05, 0.05])
+    l = np.log(s / (1 - s))
+    wg = np.zeros((8, 8), np.float32)
+    wg[:, 0] = l.astype(np.float32)                       # logit_e = l_e
+    x = np.zeros((1, 8), np.float32)
+    x[0, 0] = 1.0
+    idx, w, _ = router.route_noaux_tc(x, wg, None, 2, 2, 1, 1.0)
+    assert sorted(idx[0]) == [4, 5]
+
+
+def test_noaux_tc_bias_selects_but_does_not_weigh():
+    x = np.zeros((1, 8), np.float32)
+    x[0, 0] = 1.0
+    wg = np.zeros((8, 8), np.float32)
+    wg[:, 0] = np.array([2.0, 1.0, 0.0, 0.0, 0.0, 0.0, 0.0, 0.0], np.float32)
+    b = np.zeros(8, np.float32)
+    b[7] = 0.9                                            # lifts expert 7 above expert 1
+    idx, w, _ = router.route_noaux_tc(x, wg, b, 2, 1, 1, 1.0)
+    assert list(idx[0]) == [7, 0]         # c7 = 0.5 + 0.9 > c0 = sigmoid(2)
+    s0, s7 = 1 / (1 + np.exp(-2.0)), 0.5
+    want = {0: s0 / (s0 + s7), 7: s7 / (s0 + s7)}
+    for j in range(2):
+        assert np.isclose(w[0, j], want[idx[0, j]], rtol=1e-12)
+
+
+def test_dispatch_invariants_and_brute_force():
+    rng = np.random.default_rng(9)
+    for t, k, e in [(16, 2, 8), (1, 8, 64), (33, 3, 5), (0, 2, 4)]:
+        idx = np.stack([rng.choice(e, size=k, replace=False) for _ in range(t)]) if t else np.zeros((0, k), int)
+        counts, offsets, perm, inv = dispatch.dispatch(idx, e)
+        flat = idx.reshape(-1)
+        assert counts.sum() == t * k and offsets[0] == 0 and offsets[-1] == t * k
+        assert sorted(perm.tolist()) == list(range(t * k))
+        assert np.array_equal(inv[perm], np.arange(t * k))
+        want = [f for ex in range(e) for f in range(t * k) if flat[f] == ex]
+        assert perm.tolist() == want
+        for ex in range(e):
+            seg = perm[offsets[ex]:offsets[ex + 1]]
+            assert np.all(flat[seg] == ex) and np.all(np.diff(seg) > 0)
