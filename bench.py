@@ -1,0 +1,232 @@
+#!/usr/bin/env python3
+"""Benchmark one MoE layer step on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--gpus 1]
+
+A step is one call of moe_layer_forward (router, dispatch, batch-union expert
+FFN, combine) over one batch of synthetic tokens, with the layer's weights
+already resident in HBM. The default workload is the OLMoE-1B-7B-shaped int8
+layer at a decode batch of 16 tokens. Steps rotate through several device
+copies of the experts so that repeated calls cannot be served from the
+256 MB Infinity Cache.
+
+Prints one JSON line: MoE-layer tokens/s, plus the roofline of the dominant
+kernel (its average duration measured with HIP events on the launch stream
+inside the timed region) and the oracle's rate on the host cores.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+INT8_PEAK_TOPS = 5000.0        # MI355X dense int8 matrix cores (5.0 POPS)
+MALL_DEFEAT_BYTES = 2 << 30    # rotate through at least this much weight memory
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="olmoe_b16")
+    ap.add_argument("--copies", type=int, default=0, help="device copies of the experts (0 = enough for 2 GB)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
+    return ap.parse_args()
+
+
+def source_digest(paths):
+    import hashlib
+    h = hashlib.sha256()
+    for p in paths:
+        h.update(open(p, "rb").read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(kernel_key: str, sources):
+    """HBM bytes per launch from committed rocprofv3 counter runs, if they were
+    taken on the current kernel source; else None."""
+    try:
+        rec = json.load(open(TRAFFIC_FILE)).get(kernel_key)
+    except (OSError, ValueError):
+        return None
+    if not rec or rec.get("source_digest") != source_digest(sources):
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def cpu_baseline(wl, target_s: float):
+    """The oracle (plain numpy) on the same workload, on this host's cores."""
+    import synth
+    from oracle import ffn as offn
+    from oracle import layer as olayer
+    try:
+        import threadpoolctl
+        threads = min(16, os.cpu_count() or 1)
+        ctl = threadpoolctl.threadpool_limits(threads)
+        info = threadpoolctl.threadpool_info()
+        cores = max([i.get("num_threads", 1) for i in info] + [1])
+    except Exception:           # threadpoolctl missing: numpy's own default
+        ctl, cores = None, os.cpu_count() or 1
+    shape = wl.layer
+    bits = 8 if shape.wformat == "int8" else 4
+    cache = {}
+
+    def expert(e):
+        if e not in cache:
+            cache[e] = offn.QuantExpert.from_fp32(synth.expert_weight(shape, e, "gate"),
+                                                  synth.expert_weight(shape, e, "up"),
+                                                  synth.expert_weight(shape, e, "down"), bits)
+        return cache[e]
+
+    spec = olayer.RouterSpec(mode=shape.router, top_k=shape.top_k, renormalize=shape.renormalize,
+                             n_group=shape.n_group, topk_group=shape.topk_group,
+                             routed_scaling_factor=shape.routed_scaling_factor, bias=synth.score_bias(shape))
+    wg = synth.gate_weight(shape)
+    shared = expert(shape.n_experts) if shape.shared_expert else None
+    # sample: the whole batch for decode; a prefix of tokens for prefill
+    n_tok = wl.tokens if wl.tokens <= 16 else 64
+    x = synth.activations(shape, wl.tokens)[:n_tok]
+    # untimed pass to quantise the experts the sample needs (weight preparation, not the layer)
+    olayer.layer_forward(x, wg, spec, expert, shared, wl.act_mode)
+    runs, elapsed = 0, 0.0
+    while elapsed < target_s and runs < 50:
+        t0 = time.perf_counter()
+        olayer.layer_forward(x, wg, spec, expert, shared, wl.act_mode)
+        elapsed += time.perf_counter() - t0
+        runs += 1
+    if ctl is not None:
+        ctl.unregister() if hasattr(ctl, "unregister") else None
+    return {"value": round(n_tok * runs / elapsed, 3), "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"{n_tok} of the {wl.tokens} tokens of {wl.name}, {runs} oracle layer_forward runs "
+                      f"({elapsed:.1f} s), experts quantised beforehand"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU: --gpus {args.gpus} is not supported (the MoE layer here runs on a "
+              f"single MI355X; expert-parallel sharding is a design note, not a measured path)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import synth
+    import quantized_expert_ffn_amd as qe
+    from quantized_expert_ffn_amd import accounting as acc
+    from quantized_expert_ffn_amd import device_layer as dl
+
+    wl = synth.workload(args.workload)
+    shape = wl.layer
+    act = qe.ACT_MODES[wl.act_mode]
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    qe.load()
+
+    per_copy = acc.expert_bytes(shape.d_model, shape.d_ff, shape.wformat) * (shape.n_experts + shape.shared_expert)
+    copies = args.copies or max(1, min(16, -(-MALL_DEFEAT_BYTES // per_copy)))
+    print(f"[bench] {wl.name}: building {copies} device copies of the layer "
+          f"({per_copy / 1e6:.1f} MB each)", file=sys.stderr, flush=True)
+    layer = dl.build(shape, dev, copies=copies)
+    T = wl.tokens
+    x = dl.activations(shape, T, dev)
+    out = torch.empty((T, shape.d_model), dtype=torch.float32, device=dev)
+    ws = qe.workspace(T, shape.top_k, shape.n_experts, shape.d_model, shape.d_ff, act, shape.shared_expert, dev)
+    stream = torch.cuda.current_stream(dev)
+    G = qe.STAGES.index("gateup")
+
+    def step(i, ev_pair=None):
+        c = i % copies
+        if ev_pair is None:
+            qe.moe_layer_forward(x, layer.gate_w, layer.params, layer.routed[c], layer.shared[c], act, out, ws)
+        else:
+            evs = [None] * (2 * qe.MOE_STAGE_COUNT)
+            evs[2 * G], evs[2 * G + 1] = ev_pair
+            qe.moe_layer_forward_timed(x, layer.gate_w, layer.params, layer.routed[c], layer.shared[c], act, out,
+                                       ws, evs)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize(dev)
+    print(f"[bench] warmup done ({args.warmup} steps)", file=sys.stderr, flush=True)
+
+    pairs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    torch.cuda.synchronize(dev)
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(args.warmup + i, pairs[i])
+    torch.cuda.synchronize(dev)
+    elapsed = time.perf_counter() - t0
+    kernel_ms = float(np.mean([a.elapsed_time(b) for a, b in pairs]))
+    ms_per_step = elapsed * 1e3 / args.steps
+    print(f"[bench] timed {args.steps} steps: {ms_per_step * 1e3:.1f} us/step, gate/up kernel "
+          f"{kernel_ms * 1e3:.1f} us", file=sys.stderr, flush=True)
+
+    # the routing of this batch (identical every step): distinct experts for the byte count
+    idx = torch.empty((T, shape.top_k), dtype=torch.int32, device=dev)
+    wts = torch.empty((T, shape.top_k), dtype=torch.float32, device=dev)
+    qe.moe_route(x, layer.gate_w, layer.params, idx, wts, ws)
+    counts = torch.empty(shape.n_experts, dtype=torch.int32, device=dev)
+    offsets = torch.empty(shape.n_experts + 1, dtype=torch.int32, device=dev)
+    perm = torch.empty(T * shape.top_k, dtype=torch.int32, device=dev)
+    inv = torch.empty(T * shape.top_k, dtype=torch.int32, device=dev)
+    qe.moe_dispatch(idx, shape.n_experts, counts, offsets, perm, inv)
+    counts_h = counts.cpu().numpy()
+
+    d, I, fmt = shape.d_model, shape.d_ff, shape.wformat
+    kernel_sources = [os.path.join(ROOT, "quantized_expert_ffn_amd", "csrc", f)
+                      for f in (("gemv.hip",) if wl.act_mode == "f32" else ("mfma_gemm.hip",))]
+    if wl.act_mode == "f32":
+        algo = acc.gateup_kernel_bytes(counts_h, T, shape.top_k, d, I, fmt, shape.shared_expert, "f32")
+        achieved = algo / (kernel_ms * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBS, 4)}
+        kkey = f"gateup_gemv_{wl.name}"
+    else:
+        ops = acc.gateup_ops(counts_h, T, d, I, shape.shared_expert)
+        achieved = ops / (kernel_ms * 1e-3) / 1e12
+        roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": INT8_PEAK_TOPS, "unit": "TFLOP/s",
+                "frac": round(achieved / INT8_PEAK_TOPS, 4)}
+        kkey = f"gateup_q8_mfma_{wl.name}"
+    roof["kernel"] = kkey
+    roof["traffic"] = measured_traffic(kkey, kernel_sources)
+
+    line = {
+        "metric": "MoE-layer tokens/s at 1 GPU (decode HBM GB/s or prefill int8 TOPS vs peak in roofline)",
+        "value": round(T * args.steps / elapsed, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32 activations x int8 weights" if wl.act_mode == "f32" else "int8 x int8 -> int32, fp32 scales",
+        "data": "synthetic (seeded N(0,1) activations, N(0,0.02) weights quantised on the GPU)",
+        "config": {"workload": wl.name, "tokens": T, "d_model": d, "n_experts": shape.n_experts, "d_ff": I,
+                   "top_k": shape.top_k, "router": shape.router, "weights": f"{fmt} group 32",
+                   "act_mode": wl.act_mode, "shared_expert": shape.shared_expert,
+                   "distinct_experts": int((counts_h > 0).sum()), "device_copies": copies},
+        "roofline": roof,
+    }
+    if not args.no_cpu_baseline:
+        print("[bench] oracle CPU baseline", file=sys.stderr, flush=True)
+        line["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)
+    else:
+        line["cpu_baseline"] = None
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

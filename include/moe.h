@@ -1,0 +1,276 @@
+/*
+ * moe.h - C ABI of libmoe: the routed Mixture-of-Experts FFN layer with
+ * group-quantised experts, on one AMD Instinct MI355X (gfx950).
+ *
+ * What the layer computes (the pages, cited by title and section):
+ *   - "I ran a 7B Mixture-of-Experts LLM in a language I built" (dev.to),
+ *     section "Mixture-of-Experts": each token runs only its top-k experts
+ *     (OLMoE: top 8 of 64 per layer), chosen by a softmax router.
+ *   - "Show HN: colibri - GLM-5.2 on a slow computer" (note.crab.center),
+ *     section "What's implemented": a DeepSeek-V3-style sigmoid router
+ *     (noaux_tc, routed_scaling_factor) and a shared expert; int8 / packed
+ *     int4 weights dequantised on use; Q8_0-style int8 activations with
+ *     integer dot products, used in batch while a single row stays in f32;
+ *     batch-union MoE, where each distinct expert of a batch is read once
+ *     and applied to every position routed to it.
+ *   - "mtlm-7m-base" (huggingface.co), section "Files": int8 weights with a
+ *     scale per group of 32; "What is and is not machin": SwiGLU with SiLU.
+ *
+ * Conventions shared by every entry point:
+ *   - Pointers marked "device" are HIP device memory owned by the caller; the
+ *     library allocates nothing, keeps no state between calls and never
+ *     frees caller memory. Host pointers (the parameter structs) are read
+ *     during the call only.
+ *   - Every call enqueues work on `stream` (NULL = the null stream) and
+ *     returns without waiting for the GPU. Calls on one stream run in order.
+ *   - Arguments are validated on the host before anything is enqueued; an
+ *     invalid or unsupported argument returns an error and enqueues nothing
+ *     (no silent fallback). A failed launch returns MOE_ERR_HIP.
+ *     moe_last_error_detail() gives a text for the last error of the
+ *     calling thread.
+ *   - T = 0 tokens is a valid no-op.
+ *   - All matrices are row-major and contiguous. d = d_model, I = d_ff,
+ *     E = routed experts, k = top_k, G_d = d / 32, G_I = I / 32.
+ *   - Weight formats (group 32 along each matrix's input axis, fp32 scale per
+ *     group, symmetric): MOE_W_INT8_G32 stores int8 codes in [-127, 127];
+ *     MOE_W_INT4_G32 stores codes in [-7, 7] as 4-bit two's complement, two
+ *     per byte, element 2i in the low nibble of byte i. A group's weights are
+ *     scale * code.
+ *   - Results are deterministic: the same inputs give bitwise equal outputs
+ *     (no floating-point atomics anywhere).
+ */
+#ifndef MOE_H
+#define MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    MOE_OK = 0,
+    MOE_ERR_INVALID_ARG = -1,   /* null pointer, negative size, inconsistent shapes */
+    MOE_ERR_UNSUPPORTED = -2,   /* a valid request this build does not run */
+    MOE_ERR_WORKSPACE = -3,     /* workspace missing or smaller than moe_workspace_size() */
+    MOE_ERR_HIP = -4            /* a HIP launch or runtime call failed */
+} moe_status;
+
+typedef enum {
+    MOE_ROUTER_SOFTMAX_TOPK = 0,     /* softmax over logits, top-k by logit */
+    MOE_ROUTER_SIGMOID_NOAUX_TC = 1  /* sigmoid, group-limited top-k on sigmoid + bias */
+} moe_router_mode;
+
+typedef enum {
+    MOE_W_INT8_G32 = 0,
+    MOE_W_INT4_G32 = 1
+} moe_weight_format;
+
+typedef enum {
+    MOE_ACT_F32 = 0,   /* fp32 activations x dequantised weights (decode GEMV path) */
+    MOE_ACT_Q8_0 = 1   /* Q8_0 int8 activations, int8 matrix-core dots (prefill / verify path) */
+} moe_act_mode;
+
+/* Timed stages of moe_layer_forward_timed. */
+typedef enum {
+    MOE_STAGE_ROUTE = 0,     /* router logits + top-k */
+    MOE_STAGE_DISPATCH = 1,  /* counts, offsets, permutation, work lists */
+    MOE_STAGE_QUANT_X = 2,   /* Q8_0 of the hidden states (Q8_0 mode only) */
+    MOE_STAGE_GATEUP = 3,    /* gate and up projections + SwiGLU (all experts) */
+    MOE_STAGE_DOWN = 4,      /* down projections (all experts) */
+    MOE_STAGE_COMBINE = 5,   /* weighted gather-sum + shared expert */
+    MOE_STAGE_COUNT = 6
+} moe_stage;
+
+/* Router parameters.
+ *   n_experts   E, 1 <= E <= 1024.
+ *   top_k       k, 1 <= k <= E.
+ *   mode        moe_router_mode.
+ *   renormalize softmax mode: nonzero divides the selected probabilities by
+ *               their sum; zero keeps the plain softmax probabilities.
+ *               Ignored by noaux_tc (which always normalises).
+ *   n_group, topk_group   noaux_tc: E splits into n_group contiguous groups
+ *               (E % n_group == 0, n_group <= 64); only the topk_group groups
+ *               with the largest sum of their two best scores stay eligible.
+ *               k <= topk_group * E / n_group. Ignored by softmax mode.
+ *   routed_scaling_factor noaux_tc: multiplies the normalised weights.
+ *   score_bias  noaux_tc: device fp32 [E] added to the sigmoid scores for
+ *               selection only (NULL = zero). Ignored by softmax mode.
+ */
+typedef struct {
+    int32_t n_experts;
+    int32_t top_k;
+    int32_t mode;
+    int32_t renormalize;
+    int32_t n_group;
+    int32_t topk_group;
+    float routed_scaling_factor;
+    const float* score_bias;
+} moe_router_params;
+
+/* A stack of n_experts quantised SwiGLU experts (device pointers).
+ *   gate_q, up_q : [E, I, d] int8 codes, or [E, I, d/2] packed int4 bytes
+ *   gate_s, up_s : [E, I, d/32] fp32 scales
+ *   down_q       : [E, d, I] int8, or [E, d, I/2] packed int4
+ *   down_s       : [E, d, I/32] fp32
+ * Expert e computes  y = (silu(x Wg^T) * (x Wu^T)) Wd^T  with W = scale*code.
+ * d % 32 == 0 and I % 32 == 0 are required.
+ */
+typedef struct {
+    int32_t n_experts;
+    int32_t d_model;
+    int32_t d_ff;
+    int32_t format;       /* moe_weight_format */
+    const void* gate_q;
+    const float* gate_s;
+    const void* up_q;
+    const float* up_s;
+    const void* down_q;
+    const float* down_s;
+} moe_experts;
+
+/* Bytes of device workspace the calls below need for this problem size.
+ * has_shared: nonzero when a shared expert is passed to moe_layer_forward.
+ * The same size serves moe_route, moe_dispatch, moe_expert_ffn and
+ * moe_layer_forward for the same (T, k, E, d, I, act_mode, has_shared).
+ * Returns 0 for invalid sizes. Any 256-byte-aligned device buffer works.
+ */
+size_t moe_workspace_size(int32_t T, int32_t k, int32_t E, int32_t d, int32_t d_ff,
+                          int32_t act_mode, int32_t has_shared);
+
+/* Group-32 symmetric weight quantiser ("mtlm-7m-base", section "Files";
+ * "Show HN: colibri", section "What's implemented": int8 / packed int4).
+ *   w      device fp32 [rows, cols], cols % 32 == 0
+ *   format MOE_W_INT8_G32 -> q is int8 [rows, cols];
+ *          MOE_W_INT4_G32 -> q is packed uint8 [rows, cols/2]
+ *   s      device fp32 [rows, cols/32]
+ * Per group: s = amax/qmax (qmax 127 or 7, fp32 divide), code =
+ * clamp(round_half_even(w/s), -qmax, qmax) (fp32 divide); amax == 0 gives
+ * s = 0 and codes 0.
+ */
+moe_status moe_quantize_weights(const float* w, int64_t rows, int32_t cols, int32_t format,
+                                void* q, float* s, hipStream_t stream);
+
+/* Q8_0-style activation quantiser ("Show HN: colibri", section "What's
+ * implemented": Q8_0-style int8 activations).
+ *   x [rows, cols] device fp32, cols % 32 == 0 -> q int8 [rows, cols],
+ *   d fp32 [rows, cols/32]. Per group, in fp32: d = amax/127,
+ *   inv = (d == 0) ? 0 : 1/d, q = clamp(round_half_even(x*inv), -127, 127).
+ */
+moe_status moe_quantize_q8_0(const float* x, int64_t rows, int32_t cols,
+                             int8_t* q, float* d, hipStream_t stream);
+
+/* Router ("I ran a 7B Mixture-of-Experts LLM...", section
+ * "Mixture-of-Experts": softmax top-k; "Show HN: colibri", section "What's
+ * implemented": sigmoid noaux_tc with routed_scaling_factor).
+ *   x        device fp32 [T, d];  gate_w device fp32 [E, d]
+ *   topk_idx device int32 [T, k]: selected experts, larger selection key
+ *            first (logit in softmax mode, sigmoid + bias in noaux_tc mode),
+ *            equal keys to the lower expert id.
+ *   topk_w   device fp32 [T, k]: the weight of each selected expert.
+ *   ws       device workspace (moe_workspace_size with this T, k, E, d).
+ * Logits are fp32 on the GPU; a selection whose margin lies within fp32
+ * rounding of the logits may differ from an exact-arithmetic ranking.
+ */
+moe_status moe_route(const float* x, int32_t T, int32_t d, const float* gate_w,
+                     const moe_router_params* p, int32_t* topk_idx, float* topk_w,
+                     void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* Dispatch for batch-union ("Show HN: colibri", section "What's
+ * implemented": each distinct expert is read once for all of its positions).
+ *   topk_idx device int32 [T, k], values in [0, E).
+ *   counts   device int32 [E]      assignments per expert
+ *   offsets  device int32 [E + 1]  exclusive prefix sum of counts
+ *   perm     device int32 [T*k]    flat assignments f = t*k + j, stably
+ *                                  sorted by expert (so by f within one)
+ *   inv_perm device int32 [T*k]    inv_perm[perm[p]] = p
+ * Entries of topk_idx outside [0, E) are skipped (not counted), leaving
+ * the permutation incomplete; they never cause an out-of-bounds access.
+ */
+moe_status moe_dispatch(const int32_t* topk_idx, int32_t T, int32_t k, int32_t E,
+                        int32_t* counts, int32_t* offsets, int32_t* perm, int32_t* inv_perm,
+                        void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* Batch-union expert FFN: every expert with rows runs once over all of them.
+ *   x       device fp32 [T, d]
+ *   ex      the routed experts (ex->n_experts = E, ex->d_model = d)
+ *   counts, offsets, perm   as produced by moe_dispatch for (T, k, E)
+ *   act_mode MOE_ACT_F32: fp32 activations times dequantised weights, fp32
+ *            accumulation. MOE_ACT_Q8_0: x is Q8_0-quantised per token, each
+ *            32-group gives an exact int32 dot on the int8 matrix cores,
+ *            rescaled by both group scales; H = silu(G)*U is Q8_0-quantised
+ *            again before the down projection.
+ *   y_perm  device fp32 [T*k, d]: row p is expert e's output for token
+ *           perm[p] / k, un-weighted, in permuted order.
+ */
+moe_status moe_expert_ffn(const float* x, int32_t T, int32_t k, const moe_experts* ex,
+                          const int32_t* counts, const int32_t* offsets, const int32_t* perm,
+                          int32_t act_mode, float* y_perm, void* ws, size_t ws_bytes,
+                          hipStream_t stream);
+
+/* Combine: out[t] = sum_{j<k} topk_w[t, j] * y_perm[inv_perm[t*k + j]] + shared_y[t],
+ * summed in slot order j = 0..k-1, then the shared term; no atomics.
+ *   y_perm device fp32 [T*k, d]; topk_w device fp32 [T, k];
+ *   inv_perm device int32 [T*k]; shared_y device fp32 [T, d] or NULL;
+ *   out device fp32 [T, d].
+ */
+moe_status moe_combine(const float* y_perm, const float* topk_w, const int32_t* inv_perm,
+                       const float* shared_y, int32_t T, int32_t k, int32_t d, float* out,
+                       hipStream_t stream);
+
+/* The whole layer: route -> dispatch -> batch-union experts -> combine.
+ *   x      device fp32 [T, d];  gate_w device fp32 [E, d]
+ *   routed E routed experts; shared NULL or one expert (n_experts == 1) of
+ *          the same d, format and d_ff, applied to every token with weight 1
+ *          ("Show HN: colibri": shared expert).
+ *   out    device fp32 [T, d]
+ *   ws     device workspace of moe_workspace_size(T, k, E, d, d_ff,
+ *          act_mode, shared != NULL) bytes.
+ */
+moe_status moe_layer_forward(const float* x, int32_t T, const float* gate_w,
+                             const moe_router_params* p, const moe_experts* routed,
+                             const moe_experts* shared, int32_t act_mode, float* out,
+                             void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* moe_layer_forward that also records stage_events[2*s] before and
+ * stage_events[2*s+1] after stage s (moe_stage) on `stream`. stage_events
+ * is a host array of 2*MOE_STAGE_COUNT hipEvent_t created by the caller;
+ * NULL entries are skipped. Stages that do not run are not recorded.
+ */
+moe_status moe_layer_forward_timed(const float* x, int32_t T, const float* gate_w,
+                                   const moe_router_params* p, const moe_experts* routed,
+                                   const moe_experts* shared, int32_t act_mode, float* out,
+                                   void* ws, size_t ws_bytes, const hipEvent_t* stage_events,
+                                   hipStream_t stream);
+
+/* Test hook for the Q8_0 path: runs the production int8 matrix-core kernels
+ * of moe_expert_ffn(act_mode = MOE_ACT_Q8_0) and also writes their exact
+ * int32 per-group dots and the Q8_0 codes of H. With R = T*k rows in
+ * permuted order:
+ *   dots_gate, dots_up  device int32 [R, I, d/32]  sum over a 32-group of
+ *                       xq * wq for gate and up
+ *   hq, hd              device int8 [R, I], fp32 [R, I/32]  Q8_0 of H
+ *   dots_down           device int32 [R, d, I/32]  sum over a 32-group of
+ *                       hq * wq for down
+ *   y_perm              device fp32 [R, d] as moe_expert_ffn
+ * Meant for small shapes; the dot arrays grow as R * I * d / 32.
+ */
+moe_status moe_debug_q8_expert_ffn(const float* x, int32_t T, int32_t k, const moe_experts* ex,
+                                   const int32_t* counts, const int32_t* offsets,
+                                   const int32_t* perm, int32_t* dots_gate, int32_t* dots_up,
+                                   int8_t* hq, float* hd, int32_t* dots_down, float* y_perm,
+                                   void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* Static text for a status code. */
+const char* moe_status_string(moe_status st);
+
+/* Detail text for the last error returned to the calling thread ("" if none). */
+const char* moe_last_error_detail(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_H */

@@ -1,0 +1,353 @@
+// The C ABI of libmoe (declared in include/moe.h): argument validation,
+// workspace carving and kernel sequencing. Every check runs on the host
+// before anything is enqueued, so a rejected call leaves the stream untouched
+// ("Show HN: colibri", section "OpenAI-compatible API": unsupported requests
+// return an explicit error rather than being ignored; section "Experimental
+// resident CUDA backend": a request that cannot run fails instead of silently
+// falling back).
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <string>
+
+#include "common.h"
+#include "kernels.h"
+
+namespace {
+
+thread_local std::string g_detail;
+
+moe_status fail(moe_status st, const char* fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof(buf), fmt, ap);
+    va_end(ap);
+    g_detail = buf;
+    return st;
+}
+
+moe_status ok() {
+    g_detail.clear();
+    return MOE_OK;
+}
+
+moe_status hip_fail(hipError_t e, const char* what) {
+    return fail(MOE_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+#define MOE_REQUIRE(cond, status, ...) \
+    do {                               \
+        if (!(cond)) return fail(status, __VA_ARGS__); \
+    } while (0)
+
+#define MOE_HIP(expr, what)                           \
+    do {                                              \
+        hipError_t _e = (expr);                       \
+        if (_e != hipSuccess) return hip_fail(_e, what); \
+    } while (0)
+
+moe_status check_router(const moe_router_params* p, int E_expected) {
+    MOE_REQUIRE(p != nullptr, MOE_ERR_INVALID_ARG, "router params is NULL");
+    const int E = p->n_experts, k = p->top_k;
+    MOE_REQUIRE(E >= 1, MOE_ERR_INVALID_ARG, "n_experts = %d must be >= 1", E);
+    MOE_REQUIRE(E_expected < 0 || E == E_expected, MOE_ERR_INVALID_ARG,
+                "router n_experts %d != experts n_experts %d", E, E_expected);
+    MOE_REQUIRE(E <= moe::kMaxExperts, MOE_ERR_UNSUPPORTED, "n_experts = %d > %d", E, moe::kMaxExperts);
+    MOE_REQUIRE(k >= 1 && k <= E, MOE_ERR_INVALID_ARG, "top_k = %d outside [1, n_experts = %d]", k, E);
+    MOE_REQUIRE(k <= 64, MOE_ERR_UNSUPPORTED, "top_k = %d > 64", k);
+    if (p->mode == MOE_ROUTER_SOFTMAX_TOPK) return MOE_OK;
+    MOE_REQUIRE(p->mode == MOE_ROUTER_SIGMOID_NOAUX_TC, MOE_ERR_INVALID_ARG, "unknown router mode %d", p->mode);
+    MOE_REQUIRE(p->n_group >= 1, MOE_ERR_INVALID_ARG, "n_group = %d must be >= 1", p->n_group);
+    MOE_REQUIRE(p->n_group <= moe::kMaxGroups, MOE_ERR_UNSUPPORTED, "n_group = %d > %d", p->n_group,
+                moe::kMaxGroups);
+    MOE_REQUIRE(E % p->n_group == 0, MOE_ERR_INVALID_ARG, "n_experts %d not divisible by n_group %d", E,
+                p->n_group);
+    MOE_REQUIRE(p->topk_group >= 1 && p->topk_group <= p->n_group, MOE_ERR_INVALID_ARG,
+                "topk_group = %d outside [1, n_group = %d]", p->topk_group, p->n_group);
+    MOE_REQUIRE(k <= p->topk_group * (E / p->n_group), MOE_ERR_INVALID_ARG,
+                "top_k = %d exceeds the %d experts of the kept groups", k, p->topk_group * (E / p->n_group));
+    MOE_REQUIRE(std::isfinite(p->routed_scaling_factor), MOE_ERR_INVALID_ARG, "routed_scaling_factor not finite");
+    return MOE_OK;
+}
+
+moe_status check_experts(const moe_experts* ex, const char* name, int act_mode) {
+    MOE_REQUIRE(ex != nullptr, MOE_ERR_INVALID_ARG, "%s experts is NULL", name);
+    MOE_REQUIRE(ex->n_experts >= 1, MOE_ERR_INVALID_ARG, "%s n_experts = %d", name, ex->n_experts);
+    MOE_REQUIRE(ex->d_model > 0 && ex->d_ff > 0, MOE_ERR_INVALID_ARG, "%s d_model %d / d_ff %d must be > 0", name,
+                ex->d_model, ex->d_ff);
+    MOE_REQUIRE(ex->d_model % moe::kGroup == 0 && ex->d_ff % moe::kGroup == 0, MOE_ERR_UNSUPPORTED,
+                "%s d_model %d and d_ff %d must be multiples of 32", name, ex->d_model, ex->d_ff);
+    MOE_REQUIRE(ex->format == MOE_W_INT8_G32 || ex->format == MOE_W_INT4_G32, MOE_ERR_INVALID_ARG,
+                "%s unknown weight format %d", name, ex->format);
+    MOE_REQUIRE(ex->gate_q && ex->gate_s && ex->up_q && ex->up_s && ex->down_q && ex->down_s, MOE_ERR_INVALID_ARG,
+                "%s has a NULL weight or scale pointer", name);
+    MOE_REQUIRE(aligned16(ex->gate_q) && aligned16(ex->up_q) && aligned16(ex->down_q), MOE_ERR_INVALID_ARG,
+                "%s weight codes must be 16-byte aligned", name);
+    MOE_REQUIRE(aligned16(ex->gate_s) && aligned16(ex->up_s) && aligned16(ex->down_s), MOE_ERR_INVALID_ARG,
+                "%s scales must be 16-byte aligned", name);
+    if (act_mode == MOE_ACT_F32)
+        MOE_REQUIRE(ex->d_model <= 8192 && ex->d_ff <= 8192, MOE_ERR_UNSUPPORTED,
+                    "%s: the f32 path supports d_model and d_ff up to 8192", name);
+    return MOE_OK;
+}
+
+moe_status check_act_mode(int act_mode) {
+    MOE_REQUIRE(act_mode == MOE_ACT_F32 || act_mode == MOE_ACT_Q8_0, MOE_ERR_INVALID_ARG, "unknown act_mode %d",
+                act_mode);
+    return MOE_OK;
+}
+
+template <class T>
+T* ws_at(void* ws, size_t off) {
+    return reinterpret_cast<T*>(static_cast<uint8_t*>(ws) + off);
+}
+
+void record(const hipEvent_t* ev, int idx, hipStream_t st) {
+    if (ev && ev[idx]) (void)hipEventRecord(ev[idx], st);
+}
+
+// The expert FFN over a prepared work list (slots / tiles / row_token in ws).
+moe_status run_experts(const float* x, int T, int k, const moe_experts& routed, const moe_experts* shared,
+                       int act_mode, const moe::WsLayout& L, void* ws, float* y, int32_t* dots_gate,
+                       int32_t* dots_up, int8_t* hq_out, float* hd_out, int32_t* dots_down,
+                       const hipEvent_t* ev, hipStream_t st) {
+    const int E = routed.n_experts, d = routed.d_model;
+    const int n = T * k;
+    const int has_shared = shared != nullptr;
+    const int* row_token = ws_at<int>(ws, L.row_token);
+    const int* slots = ws_at<int>(ws, L.slots);
+    const int* tiles = ws_at<int>(ws, L.tiles);
+    const int* meta = ws_at<int>(ws, L.meta);
+    if (act_mode == MOE_ACT_F32) {
+        const int max_slots = (E < n ? E : n) + has_shared;
+        float* h = ws_at<float>(ws, L.h);
+        record(ev, 2 * MOE_STAGE_GATEUP, st);
+        MOE_HIP(moe::launch_gemv(routed, shared, true, x, row_token, slots, meta, max_slots, T, h, st), "gate/up GEMV");
+        record(ev, 2 * MOE_STAGE_GATEUP + 1, st);
+        record(ev, 2 * MOE_STAGE_DOWN, st);
+        MOE_HIP(moe::launch_gemv(routed, shared, false, h, nullptr, slots, meta, max_slots, T, y, st), "down GEMV");
+        record(ev, 2 * MOE_STAGE_DOWN + 1, st);
+        return MOE_OK;
+    }
+    int8_t* xq = ws_at<int8_t>(ws, L.xq);
+    float* xd = ws_at<float>(ws, L.xd);
+    int8_t* hq = hq_out ? hq_out : ws_at<int8_t>(ws, L.h);
+    float* hd = hd_out ? hd_out : ws_at<float>(ws, L.hd);
+    record(ev, 2 * MOE_STAGE_QUANT_X, st);
+    MOE_HIP(moe::launch_quantize_q8_0(x, T, d, xq, xd, st), "Q8_0 of x");
+    record(ev, 2 * MOE_STAGE_QUANT_X + 1, st);
+    record(ev, 2 * MOE_STAGE_GATEUP, st);
+    MOE_HIP(moe::launch_q8_mfma(routed, shared, true, xq, xd, row_token, tiles, meta, L.max_tiles, hq, hd, nullptr,
+                                dots_gate, dots_up, st),
+            "gate/up int8 MFMA");
+    record(ev, 2 * MOE_STAGE_GATEUP + 1, st);
+    record(ev, 2 * MOE_STAGE_DOWN, st);
+    MOE_HIP(moe::launch_q8_mfma(routed, shared, false, hq, hd, nullptr, tiles, meta, L.max_tiles, nullptr, nullptr, y,
+                                dots_down, nullptr, st),
+            "down int8 MFMA");
+    record(ev, 2 * MOE_STAGE_DOWN + 1, st);
+    return MOE_OK;
+}
+
+moe_status expert_ffn_impl(const float* x, int32_t T, int32_t k, const moe_experts* ex, const int32_t* counts,
+                           const int32_t* offsets, const int32_t* perm, int32_t act_mode, float* y_perm,
+                           int32_t* dots_gate, int32_t* dots_up, int8_t* hq, float* hd, int32_t* dots_down,
+                           void* ws, size_t ws_bytes, hipStream_t st) {
+    moe_status s;
+    if ((s = check_act_mode(act_mode)) != MOE_OK) return s;
+    if ((s = check_experts(ex, "routed", act_mode)) != MOE_OK) return s;
+    MOE_REQUIRE(T >= 0, MOE_ERR_INVALID_ARG, "T = %d < 0", T);
+    MOE_REQUIRE(k >= 1 && k <= ex->n_experts, MOE_ERR_INVALID_ARG, "k = %d outside [1, %d]", k, ex->n_experts);
+    MOE_REQUIRE(ex->n_experts <= moe::kMaxExperts, MOE_ERR_UNSUPPORTED, "n_experts = %d > %d", ex->n_experts,
+                moe::kMaxExperts);
+    if (T == 0) return ok();
+    MOE_REQUIRE(x && counts && offsets && perm && y_perm, MOE_ERR_INVALID_ARG, "NULL tensor argument");
+    MOE_REQUIRE(aligned16(x) && aligned16(y_perm), MOE_ERR_INVALID_ARG, "x and y_perm must be 16-byte aligned");
+    const moe::WsLayout L = moe::ws_layout(T, k, ex->n_experts, ex->d_model, ex->d_ff, act_mode, 0);
+    MOE_REQUIRE(ws != nullptr && ws_bytes >= L.total, MOE_ERR_WORKSPACE, "workspace %zu bytes < %zu needed",
+                ws ? ws_bytes : 0, L.total);
+    MOE_REQUIRE(aligned16(ws), MOE_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
+    MOE_HIP(moe::launch_plan(counts, offsets, perm, T, k, ex->n_experts, 0, ws_at<int>(ws, L.row_token),
+                             ws_at<int>(ws, L.slots), ws_at<int>(ws, L.tiles), ws_at<int>(ws, L.meta), st),
+            "work-list kernel");
+    if ((s = run_experts(x, T, k, *ex, nullptr, act_mode, L, ws, y_perm, dots_gate, dots_up, hq, hd, dots_down,
+                         nullptr, st)) != MOE_OK)
+        return s;
+    return ok();
+}
+
+moe_status layer_forward_impl(const float* x, int32_t T, const float* gate_w, const moe_router_params* p,
+                              const moe_experts* routed, const moe_experts* shared, int32_t act_mode, float* out,
+                              void* ws, size_t ws_bytes, const hipEvent_t* ev, hipStream_t st) {
+    moe_status s;
+    if ((s = check_act_mode(act_mode)) != MOE_OK) return s;
+    if ((s = check_experts(routed, "routed", act_mode)) != MOE_OK) return s;
+    if ((s = check_router(p, routed->n_experts)) != MOE_OK) return s;
+    if (shared) {
+        if ((s = check_experts(shared, "shared", act_mode)) != MOE_OK) return s;
+        MOE_REQUIRE(shared->n_experts == 1, MOE_ERR_INVALID_ARG, "shared expert set must hold 1 expert, not %d",
+                    shared->n_experts);
+        MOE_REQUIRE(shared->d_model == routed->d_model && shared->d_ff == routed->d_ff &&
+                        shared->format == routed->format,
+                    MOE_ERR_UNSUPPORTED, "shared expert must match the routed d_model, d_ff and format");
+    }
+    MOE_REQUIRE(T >= 0, MOE_ERR_INVALID_ARG, "T = %d < 0", T);
+    if (T == 0) return ok();
+    MOE_REQUIRE(x && gate_w && out, MOE_ERR_INVALID_ARG, "NULL tensor argument");
+    MOE_REQUIRE(aligned16(x) && aligned16(gate_w) && aligned16(out), MOE_ERR_INVALID_ARG,
+                "x, gate_w and out must be 16-byte aligned");
+    const int E = routed->n_experts, k = p->top_k, d = routed->d_model;
+    const int has_shared = shared != nullptr;
+    const moe::WsLayout L = moe::ws_layout(T, k, E, d, routed->d_ff, act_mode, has_shared);
+    MOE_REQUIRE(ws != nullptr && ws_bytes >= L.total, MOE_ERR_WORKSPACE, "workspace %zu bytes < %zu needed",
+                ws ? ws_bytes : 0, L.total);
+    MOE_REQUIRE(aligned16(ws), MOE_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
+
+    int* idx = ws_at<int>(ws, L.idx);
+    float* w = ws_at<float>(ws, L.wts);
+    int* inv_perm = ws_at<int>(ws, L.inv_perm);
+    record(ev, 2 * MOE_STAGE_ROUTE, st);
+    MOE_HIP(moe::launch_router(x, T, d, gate_w, *p, ws_at<float>(ws, L.logits), idx, w, st), "router");
+    record(ev, 2 * MOE_STAGE_ROUTE + 1, st);
+    record(ev, 2 * MOE_STAGE_DISPATCH, st);
+    MOE_HIP(moe::launch_dispatch(idx, T, k, E, ws_at<int>(ws, L.counts), ws_at<int>(ws, L.offsets),
+                                 ws_at<int>(ws, L.perm), inv_perm, has_shared, ws_at<int>(ws, L.row_token),
+                                 ws_at<int>(ws, L.slots), ws_at<int>(ws, L.tiles), ws_at<int>(ws, L.meta), st),
+            "dispatch");
+    record(ev, 2 * MOE_STAGE_DISPATCH + 1, st);
+    float* y = ws_at<float>(ws, L.y);
+    if ((s = run_experts(x, T, k, *routed, shared, act_mode, L, ws, y, nullptr, nullptr, nullptr, nullptr, nullptr,
+                         ev, st)) != MOE_OK)
+        return s;
+    record(ev, 2 * MOE_STAGE_COMBINE, st);
+    MOE_HIP(moe::launch_combine(y, w, inv_perm, has_shared ? y + (size_t)T * k * d : nullptr, T, k, d, out, st),
+            "combine");
+    record(ev, 2 * MOE_STAGE_COMBINE + 1, st);
+    return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t moe_workspace_size(int32_t T, int32_t k, int32_t E, int32_t d, int32_t d_ff, int32_t act_mode,
+                          int32_t has_shared) {
+    if (T < 0 || k < 1 || E < 1 || k > E || d <= 0 || d_ff <= 0 || d % moe::kGroup || d_ff % moe::kGroup) return 0;
+    if (act_mode != MOE_ACT_F32 && act_mode != MOE_ACT_Q8_0) return 0;
+    return moe::ws_layout(T, k, E, d, d_ff, act_mode, has_shared ? 1 : 0).total;
+}
+
+moe_status moe_quantize_weights(const float* w, int64_t rows, int32_t cols, int32_t format, void* q, float* s,
+                                hipStream_t stream) {
+    MOE_REQUIRE(rows >= 0 && cols > 0, MOE_ERR_INVALID_ARG, "bad shape [%lld, %d]", (long long)rows, cols);
+    MOE_REQUIRE(cols % moe::kGroup == 0, MOE_ERR_UNSUPPORTED, "cols = %d is not a multiple of 32", cols);
+    MOE_REQUIRE(format == MOE_W_INT8_G32 || format == MOE_W_INT4_G32, MOE_ERR_INVALID_ARG, "unknown format %d",
+                format);
+    if (rows == 0) return ok();
+    MOE_REQUIRE(w && q && s, MOE_ERR_INVALID_ARG, "NULL tensor argument");
+    MOE_REQUIRE(aligned16(w) && aligned16(q), MOE_ERR_INVALID_ARG, "w and q must be 16-byte aligned");
+    MOE_HIP(moe::launch_quantize_weights(w, rows, cols, format == MOE_W_INT8_G32 ? 8 : 4, q, s, stream),
+            "weight quantiser");
+    return ok();
+}
+
+moe_status moe_quantize_q8_0(const float* x, int64_t rows, int32_t cols, int8_t* q, float* d, hipStream_t stream) {
+    MOE_REQUIRE(rows >= 0 && cols > 0, MOE_ERR_INVALID_ARG, "bad shape [%lld, %d]", (long long)rows, cols);
+    MOE_REQUIRE(cols % moe::kGroup == 0, MOE_ERR_UNSUPPORTED, "cols = %d is not a multiple of 32", cols);
+    if (rows == 0) return ok();
+    MOE_REQUIRE(x && q && d, MOE_ERR_INVALID_ARG, "NULL tensor argument");
+    MOE_REQUIRE(aligned16(x) && aligned16(q), MOE_ERR_INVALID_ARG, "x and q must be 16-byte aligned");
+    MOE_HIP(moe::launch_quantize_q8_0(x, rows, cols, q, d, stream), "Q8_0 quantiser");
+    return ok();
+}
+
+moe_status moe_route(const float* x, int32_t T, int32_t d, const float* gate_w, const moe_router_params* p,
+                     int32_t* topk_idx, float* topk_w, void* ws, size_t ws_bytes, hipStream_t stream) {
+    moe_status s;
+    if ((s = check_router(p, -1)) != MOE_OK) return s;
+    MOE_REQUIRE(T >= 0 && d > 0, MOE_ERR_INVALID_ARG, "bad shape T = %d, d = %d", T, d);
+    MOE_REQUIRE(d % 4 == 0, MOE_ERR_UNSUPPORTED, "d = %d is not a multiple of 4", d);
+    if (T == 0) return ok();
+    MOE_REQUIRE(x && gate_w && topk_idx && topk_w, MOE_ERR_INVALID_ARG, "NULL tensor argument");
+    MOE_REQUIRE(aligned16(x) && aligned16(gate_w), MOE_ERR_INVALID_ARG, "x and gate_w must be 16-byte aligned");
+    const size_t need = (size_t)T * p->n_experts * sizeof(float);
+    MOE_REQUIRE(ws != nullptr && ws_bytes >= need, MOE_ERR_WORKSPACE, "workspace %zu bytes < %zu needed",
+                ws ? ws_bytes : 0, need);
+    MOE_HIP(moe::launch_router(x, T, d, gate_w, *p, static_cast<float*>(ws), topk_idx, topk_w, stream), "router");
+    return ok();
+}
+
+moe_status moe_dispatch(const int32_t* topk_idx, int32_t T, int32_t k, int32_t E, int32_t* counts,
+                        int32_t* offsets, int32_t* perm, int32_t* inv_perm, void* ws, size_t ws_bytes,
+                        hipStream_t stream) {
+    (void)ws;
+    (void)ws_bytes;
+    MOE_REQUIRE(T >= 0 && k >= 1 && E >= 1 && k <= E, MOE_ERR_INVALID_ARG, "bad sizes T = %d, k = %d, E = %d", T,
+                k, E);
+    MOE_REQUIRE(E <= moe::kMaxExperts, MOE_ERR_UNSUPPORTED, "E = %d > %d", E, moe::kMaxExperts);
+    MOE_REQUIRE((int64_t)T * k <= (int64_t)1 << 30, MOE_ERR_UNSUPPORTED, "T*k too large");
+    MOE_REQUIRE(counts && offsets, MOE_ERR_INVALID_ARG, "NULL tensor argument");
+    if (T > 0) MOE_REQUIRE(topk_idx && perm && inv_perm, MOE_ERR_INVALID_ARG, "NULL tensor argument");
+    MOE_HIP(moe::launch_dispatch(topk_idx, T, k, E, counts, offsets, perm, inv_perm, 0, nullptr, nullptr, nullptr,
+                                 nullptr, stream),
+            "dispatch");
+    return ok();
+}
+
+moe_status moe_expert_ffn(const float* x, int32_t T, int32_t k, const moe_experts* ex, const int32_t* counts,
+                          const int32_t* offsets, const int32_t* perm, int32_t act_mode, float* y_perm, void* ws,
+                          size_t ws_bytes, hipStream_t stream) {
+    return expert_ffn_impl(x, T, k, ex, counts, offsets, perm, act_mode, y_perm, nullptr, nullptr, nullptr, nullptr,
+                           nullptr, ws, ws_bytes, stream);
+}
+
+moe_status moe_debug_q8_expert_ffn(const float* x, int32_t T, int32_t k, const moe_experts* ex,
+                                   const int32_t* counts, const int32_t* offsets, const int32_t* perm,
+                                   int32_t* dots_gate, int32_t* dots_up, int8_t* hq, float* hd, int32_t* dots_down,
+                                   float* y_perm, void* ws, size_t ws_bytes, hipStream_t stream) {
+    MOE_REQUIRE(dots_gate && dots_up && hq && hd && dots_down, MOE_ERR_INVALID_ARG, "NULL debug output");
+    return expert_ffn_impl(x, T, k, ex, counts, offsets, perm, MOE_ACT_Q8_0, y_perm, dots_gate, dots_up, hq, hd,
+                           dots_down, ws, ws_bytes, stream);
+}
+
+moe_status moe_combine(const float* y_perm, const float* topk_w, const int32_t* inv_perm, const float* shared_y,
+                       int32_t T, int32_t k, int32_t d, float* out, hipStream_t stream) {
+    MOE_REQUIRE(T >= 0 && k >= 1 && d > 0, MOE_ERR_INVALID_ARG, "bad sizes T = %d, k = %d, d = %d", T, k, d);
+    MOE_REQUIRE(d % 4 == 0, MOE_ERR_UNSUPPORTED, "d = %d is not a multiple of 4", d);
+    if (T == 0) return ok();
+    MOE_REQUIRE(y_perm && topk_w && inv_perm && out, MOE_ERR_INVALID_ARG, "NULL tensor argument");
+    MOE_REQUIRE(aligned16(y_perm) && aligned16(out) && (shared_y == nullptr || aligned16(shared_y)),
+                MOE_ERR_INVALID_ARG, "y_perm, shared_y and out must be 16-byte aligned");
+    MOE_HIP(moe::launch_combine(y_perm, topk_w, inv_perm, shared_y, T, k, d, out, stream), "combine");
+    return ok();
+}
+
+moe_status moe_layer_forward(const float* x, int32_t T, const float* gate_w, const moe_router_params* p,
+                             const moe_experts* routed, const moe_experts* shared, int32_t act_mode, float* out,
+                             void* ws, size_t ws_bytes, hipStream_t stream) {
+    return layer_forward_impl(x, T, gate_w, p, routed, shared, act_mode, out, ws, ws_bytes, nullptr, stream);
+}
+
+moe_status moe_layer_forward_timed(const float* x, int32_t T, const float* gate_w, const moe_router_params* p,
+                                   const moe_experts* routed, const moe_experts* shared, int32_t act_mode, float* out,
+                                   void* ws, size_t ws_bytes, const hipEvent_t* stage_events, hipStream_t stream) {
+    return layer_forward_impl(x, T, gate_w, p, routed, shared, act_mode, out, ws, ws_bytes, stage_events, stream);
+}
+
+const char* moe_status_string(moe_status st) {
+    switch (st) {
+        case MOE_OK: return "MOE_OK";
+        case MOE_ERR_INVALID_ARG: return "MOE_ERR_INVALID_ARG: invalid argument";
+        case MOE_ERR_UNSUPPORTED: return "MOE_ERR_UNSUPPORTED: unsupported request";
+        case MOE_ERR_WORKSPACE: return "MOE_ERR_WORKSPACE: workspace too small";
+        case MOE_ERR_HIP: return "MOE_ERR_HIP: HIP runtime error";
+    }
+    return "unknown moe_status";
+}
+
+const char* moe_last_error_detail(void) { return g_detail.c_str(); }
+
+}  // extern "C"

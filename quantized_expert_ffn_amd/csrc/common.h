@@ -1,0 +1,105 @@
+// Internal helpers shared by the libmoe HIP kernels (gfx950, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "moe.h"
+
+namespace moe {
+
+constexpr int kWave = 64;
+constexpr int kGroup = 32;            // quantisation group along the reduction axis
+constexpr int kMaxExperts = 1024;
+constexpr int kMaxGroups = 64;        // noaux_tc n_group limit (a bit mask of groups)
+
+// ---------------------------------------------------------------------------
+// Workspace layout. Every section is 256-byte aligned; the same function is
+// used to size the workspace and to carve it, so the two never disagree.
+// ---------------------------------------------------------------------------
+struct WsLayout {
+    size_t logits = 0;     // f32  [T, E]
+    size_t idx = 0;        // i32  [T, k]
+    size_t wts = 0;        // f32  [T, k]
+    size_t counts = 0;     // i32  [E]
+    size_t offsets = 0;    // i32  [E + 1]
+    size_t perm = 0;       // i32  [T*k]
+    size_t inv_perm = 0;   // i32  [T*k]
+    size_t row_token = 0;  // i32  [T*k + T]   permuted row -> token
+    size_t slots = 0;      // i32  [E + 1][4]  (expert, row_begin, n_rows, 0)
+    size_t tiles = 0;      // i32  [max_tiles][4] (expert, row_begin, row_end, 0)
+    size_t meta = 0;       // i32  [4]  n_slots, n_tiles, status, 0
+    size_t xq = 0;         // i8   [T, d]         (Q8_0)
+    size_t xd = 0;         // f32  [T, d/32]      (Q8_0)
+    size_t h = 0;          // f32  [R, I] (F32) or i8 [R, I] (Q8_0); R = T*k + T*shared
+    size_t hd = 0;         // f32  [R, I/32]      (Q8_0)
+    size_t y = 0;          // f32  [R, d]
+    size_t total = 0;
+    int max_tiles = 0;
+};
+
+constexpr int kTileRows = 64;         // rows (tokens) per int8-MFMA tile
+
+inline size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
+
+inline WsLayout ws_layout(int T, int k, int E, int d, int I, int act_mode, int has_shared) {
+    WsLayout L;
+    size_t off = 0;
+    auto take = [&](size_t bytes) { size_t o = off; off = align256(off + (bytes ? bytes : 1)); return o; };
+    const size_t n = (size_t)T * k;
+    const size_t R = n + (has_shared ? (size_t)T : 0);
+    L.max_tiles = (int)((n + kTileRows - 1) / kTileRows + (size_t)(E < (long long)n ? E : n) +
+                        (has_shared ? (T + kTileRows - 1) / kTileRows : 0));
+    L.logits = take((size_t)T * E * 4);
+    L.idx = take(n * 4);
+    L.wts = take(n * 4);
+    L.counts = take((size_t)E * 4);
+    L.offsets = take((size_t)(E + 1) * 4);
+    L.perm = take(n * 4);
+    L.inv_perm = take(n * 4);
+    L.row_token = take(R * 4);
+    L.slots = take((size_t)(E + 1) * 16);
+    L.tiles = take((size_t)(L.max_tiles > 0 ? L.max_tiles : 1) * 16);
+    L.meta = take(16);
+    if (act_mode == MOE_ACT_Q8_0) {
+        L.xq = take((size_t)T * d);
+        L.xd = take((size_t)T * (d / kGroup) * 4);
+        L.h = take(R * I);
+        L.hd = take(R * (I / kGroup) * 4);
+    } else {
+        L.h = take(R * I * 4);
+    }
+    L.y = take(R * d * 4);
+    L.total = off;
+    return L;
+}
+
+// ---------------------------------------------------------------------------
+// Device helpers
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, kWave);
+    return v;
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, kWave));
+    return v;
+}
+
+// Sum across aligned segments of `width` lanes (width a power of two <= 64).
+__device__ __forceinline__ float segment_sum(float v, int width) {
+    for (int off = width >> 1; off > 0; off >>= 1) v += __shfl_xor(v, off, kWave);
+    return v;
+}
+
+__device__ __forceinline__ float silu(float g) { return g / (1.0f + __expf(-g)); }
+
+__device__ __forceinline__ uint64_t lanemask_lt() {
+    const int lane = threadIdx.x & (kWave - 1);
+    return (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+}
+
+}  // namespace moe

@@ -1,0 +1,223 @@
+// Dispatch for batch-union MoE ("Show HN: colibri", section "What's
+// implemented": in prefill and verification each distinct expert is read once
+// and applied to every position routed to it).
+//
+// One block of 1024 threads does the whole job in LDS, with no atomics and no
+// host round trip:
+//   1. each of the 16 waves takes a contiguous chunk of the flat assignments
+//      f = t*k + j and walks it 64 at a time; lanes with the same expert find
+//      each other with one ballot per bit of the expert id, which gives every
+//      assignment its rank among equal experts earlier in the chunk, and a
+//      per-wave histogram row;
+//   2. the per-wave histograms are scanned (over waves, then over experts)
+//      into counts, offsets and each wave's starting position per expert;
+//   3. position = start + rank, so the permutation is stable by construction.
+// The same block then writes the work lists the expert kernels consume:
+// slots (one per expert with rows, then the shared expert), int8-MFMA tiles
+// of kTileRows rows, and the row -> token map.
+#include "common.h"
+#include "kernels.h"
+
+namespace moe {
+
+constexpr int kDispThreads = 1024;
+constexpr int kDispWaves = kDispThreads / kWave;
+
+// Exclusive scan of one value per thread over the whole block. `tmp` holds at
+// least kDispWaves + 1 ints. Returns the exclusive prefix; *total gets the sum.
+__device__ int block_exclusive_scan(int v, int* tmp, int* total) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    int incl = v;
+#pragma unroll
+    for (int off = 1; off < kWave; off <<= 1) {
+        const int o = __shfl_up(incl, off, kWave);
+        if (lane >= off) incl += o;
+    }
+    if (lane == kWave - 1) tmp[wave] = incl;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        int run = 0;
+        for (int w = 0; w < kDispWaves; ++w) {
+            const int c = tmp[w];
+            tmp[w] = run;
+            run += c;
+        }
+        tmp[kDispWaves] = run;
+    }
+    __syncthreads();
+    const int res = tmp[wave] + incl - v;
+    *total = tmp[kDispWaves];
+    __syncthreads();
+    return res;
+}
+
+// Work lists from counts/offsets (thread e < E holds counts[e], offsets[e]).
+__device__ void build_work_lists(int E, int cnt, int off, int n_rows_routed, int T, int has_shared,
+                                 int tile_rows, int* scan_tmp, int* __restrict__ slots, int* __restrict__ tiles,
+                                 int* __restrict__ meta) {
+    const int e = threadIdx.x;
+    const bool valid = e < E;
+    int n_active = 0;
+    const int act = (valid && cnt > 0) ? 1 : 0;
+    const int slot = block_exclusive_scan(act, scan_tmp, &n_active);
+    if (act) {
+        int4* s = reinterpret_cast<int4*>(slots) + slot;
+        *s = make_int4(e, off, cnt, 0);
+    }
+    int n_tiles = 0;
+    const int nt = valid ? (cnt + tile_rows - 1) / tile_rows : 0;
+    const int tbase = block_exclusive_scan(nt, scan_tmp, &n_tiles);
+    for (int i = 0; i < nt; ++i) {
+        const int rb = off + i * tile_rows;
+        const int re = min(off + cnt, rb + tile_rows);
+        reinterpret_cast<int4*>(tiles)[tbase + i] = make_int4(e, rb, re, 0);
+    }
+    if (has_shared) {
+        const int shared_tiles = (T + tile_rows - 1) / tile_rows;
+        for (int i = threadIdx.x; i < shared_tiles; i += blockDim.x) {
+            const int rb = n_rows_routed + i * tile_rows;
+            const int re = min(n_rows_routed + T, rb + tile_rows);
+            reinterpret_cast<int4*>(tiles)[n_tiles + i] = make_int4(E, rb, re, 0);
+        }
+        if (threadIdx.x == 0) reinterpret_cast<int4*>(slots)[n_active] = make_int4(E, n_rows_routed, T, 0);
+        n_tiles += shared_tiles;
+        n_active += 1;
+    }
+    if (threadIdx.x == 0) {
+        meta[0] = n_active;
+        meta[1] = n_tiles;
+    }
+}
+
+__global__ __launch_bounds__(kDispThreads) void dispatch_kernel(const int* __restrict__ idx, int T, int k, int E,
+                                                                 int* __restrict__ counts, int* __restrict__ offsets,
+                                                                 int* __restrict__ perm, int* __restrict__ inv_perm,
+                                                                 int has_shared, int tile_rows,
+                                                                 int* __restrict__ row_token,
+                                                                 int* __restrict__ slots, int* __restrict__ tiles,
+                                                                 int* __restrict__ meta) {
+    extern __shared__ int lds[];
+    int* hist = lds;                                  // [kDispWaves][E]
+    int* scan_tmp = lds + kDispWaves * E;             // [kDispWaves + 1]
+    __shared__ int bad_flag;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int n = T * k;
+    for (int i = tid; i < kDispWaves * E; i += kDispThreads) hist[i] = 0;
+    if (tid == 0) bad_flag = 0;
+    __syncthreads();
+
+    const int chunk = (((n + kDispWaves - 1) / kDispWaves) + kWave - 1) / kWave * kWave;
+    const int begin = wave * chunk;
+    const int end = min(n, begin + chunk);
+    const int nbits = E > 1 ? 32 - __clz(E - 1) : 0;
+    const uint64_t lt = lanemask_lt();
+    int* my_hist = hist + wave * E;
+
+    // pass 1: stable rank inside this wave's chunk
+    for (int base = begin; base < end; base += kWave) {
+        const int f = base + lane;
+        const bool valid = f < end;
+        const int e = valid ? idx[f] : 0;
+        const bool inr = valid && e >= 0 && e < E;
+        if (valid && !inr) bad_flag = 1;
+        uint64_t peers = __ballot(inr);
+        for (int b = 0; b < nbits; ++b) {
+            const bool bit = (e >> b) & 1;
+            const uint64_t m = __ballot(inr && bit);
+            peers &= bit ? m : ~m;
+        }
+        const int rank = __popcll(peers & lt);
+        const int prior = inr ? my_hist[e] : 0;
+        // the last lane of each peer set advances the histogram; every lane has
+        // read it above, and a wave executes its LDS operations in order
+        if (inr && rank == __popcll(peers) - 1) my_hist[e] = prior + __popcll(peers);
+        if (inr) inv_perm[f] = prior + rank;
+    }
+    __syncthreads();
+
+    // pass 2: scan over waves (per expert), then over experts
+    int cnt = 0;
+    if (tid < E) {
+        int run = 0;
+        for (int w = 0; w < kDispWaves; ++w) {
+            const int c = hist[w * E + tid];
+            hist[w * E + tid] = run;
+            run += c;
+        }
+        cnt = run;
+    }
+    int total = 0;
+    const int off = block_exclusive_scan(tid < E ? cnt : 0, scan_tmp, &total);
+    if (tid < E) {
+        counts[tid] = cnt;
+        offsets[tid] = off;
+        for (int w = 0; w < kDispWaves; ++w) hist[w * E + tid] += off;
+    }
+    if (tid == 0) offsets[E] = total;
+    __syncthreads();
+
+    // pass 3: final positions
+    for (int base = begin; base < end; base += kWave) {
+        const int f = base + lane;
+        if (f >= end) continue;
+        const int e = idx[f];
+        if (e < 0 || e >= E) continue;
+        const int pos = my_hist[e] + inv_perm[f];
+        perm[pos] = f;
+        inv_perm[f] = pos;
+        if (row_token) row_token[pos] = f / k;
+    }
+    if (row_token && has_shared)
+        for (int t = tid; t < T; t += kDispThreads) row_token[n + t] = t;
+
+    if (slots) {
+        build_work_lists(E, cnt, off, n, T, has_shared, tile_rows, scan_tmp, slots, tiles, meta);
+        __syncthreads();
+        if (tid == 0) meta[2] = bad_flag;
+    }
+}
+
+// Work lists for moe_expert_ffn from a caller's counts / offsets / perm.
+__global__ __launch_bounds__(kDispThreads) void plan_kernel(const int* __restrict__ counts,
+                                                             const int* __restrict__ offsets,
+                                                             const int* __restrict__ perm, int T, int k, int E,
+                                                             int has_shared, int tile_rows,
+                                                             int* __restrict__ row_token, int* __restrict__ slots,
+                                                             int* __restrict__ tiles, int* __restrict__ meta) {
+    __shared__ int scan_tmp[kDispWaves + 1];
+    const int tid = threadIdx.x;
+    const int n = T * k;
+    for (int p = tid; p < n; p += kDispThreads) {
+        const int f = perm[p];
+        row_token[p] = (f >= 0 && f < n) ? f / k : 0;
+    }
+    if (has_shared)
+        for (int t = tid; t < T; t += kDispThreads) row_token[n + t] = t;
+    // a caller's counts / offsets are clamped into [0, T*k) so that rows never
+    // leave the permuted range, whatever they hold
+    int off = tid < E ? offsets[tid] : 0;
+    off = min(max(off, 0), n);
+    int cnt = tid < E ? counts[tid] : 0;
+    cnt = min(max(cnt, 0), n - off);
+    build_work_lists(E, cnt, off, n, T, has_shared, tile_rows, scan_tmp, slots, tiles, meta);
+    if (tid == 0) meta[2] = 0;
+}
+
+size_t dispatch_lds_bytes(int E) { return (size_t)(kDispWaves * E + kDispWaves + 1) * sizeof(int); }
+
+hipError_t launch_dispatch(const int* idx, int T, int k, int E, int* counts, int* offsets, int* perm,
+                           int* inv_perm, int has_shared, int* row_token, int* slots, int* tiles, int* meta,
+                           hipStream_t st) {
+    hipLaunchKernelGGL(dispatch_kernel, dim3(1), dim3(kDispThreads), dispatch_lds_bytes(E), st, idx, T, k, E,
+                       counts, offsets, perm, inv_perm, has_shared, kTileRows, row_token, slots, tiles, meta);
+    return hipGetLastError();
+}
+
+hipError_t launch_plan(const int* counts, const int* offsets, const int* perm, int T, int k, int E, int has_shared,
+                       int* row_token, int* slots, int* tiles, int* meta, hipStream_t st) {
+    hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(kDispThreads), 0, st, counts, offsets, perm, T, k, E, has_shared,
+                       kTileRows, row_token, slots, tiles, meta);
+    return hipGetLastError();
+}
+
+}  // namespace moe

@@ -1,0 +1,125 @@
+// Group-32 quantisers: weights (int8 / packed int4) and Q8_0 activations.
+//
+// Weights: "mtlm-7m-base" (huggingface.co), section "Files" (int8, group size
+// 32) and "Show HN: colibri", section "What's implemented" (int8 / packed
+// int4 quantisation kernels). Activations: the same section's Q8_0-style int8
+// activations. Codes are decided in fp32 with IEEE division and
+// round-half-to-even, so a host implementation using the same fp32 steps
+// reaches the same bytes.
+#include "common.h"
+#include "kernels.h"
+
+namespace moe {
+
+// One thread per group of 32 consecutive weights of one row.
+template <int BITS>
+__global__ __launch_bounds__(256) void quantize_weights_kernel(const float* __restrict__ w,
+                                                               int64_t n_groups,
+                                                               uint8_t* __restrict__ q,
+                                                               float* __restrict__ s) {
+    const int64_t g = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (g >= n_groups) return;
+    const float4* src = reinterpret_cast<const float4*>(w + g * kGroup);
+    float v[kGroup];
+#pragma unroll
+    for (int i = 0; i < kGroup / 4; ++i) {
+        const float4 f = src[i];
+        v[4 * i + 0] = f.x;
+        v[4 * i + 1] = f.y;
+        v[4 * i + 2] = f.z;
+        v[4 * i + 3] = f.w;
+    }
+    float amax = 0.0f;
+#pragma unroll
+    for (int i = 0; i < kGroup; ++i) amax = fmaxf(amax, fabsf(v[i]));
+    constexpr float qmax = BITS == 8 ? 127.0f : 7.0f;
+    const float sc = __fdiv_rn(amax, qmax);
+    int code[kGroup];
+#pragma unroll
+    for (int i = 0; i < kGroup; ++i) {
+        float r = sc > 0.0f ? rintf(__fdiv_rn(v[i], sc)) : 0.0f;
+        r = fminf(fmaxf(r, -qmax), qmax);
+        code[i] = (int)r;
+    }
+    s[g] = sc;
+    if constexpr (BITS == 8) {
+        uint32_t packed[kGroup / 4];
+#pragma unroll
+        for (int i = 0; i < kGroup / 4; ++i)
+            packed[i] = (uint32_t)(code[4 * i] & 0xff) | ((uint32_t)(code[4 * i + 1] & 0xff) << 8) |
+                        ((uint32_t)(code[4 * i + 2] & 0xff) << 16) | ((uint32_t)(code[4 * i + 3] & 0xff) << 24);
+        uint4* dst = reinterpret_cast<uint4*>(q + g * kGroup);
+        dst[0] = make_uint4(packed[0], packed[1], packed[2], packed[3]);
+        dst[1] = make_uint4(packed[4], packed[5], packed[6], packed[7]);
+    } else {
+        uint32_t packed[kGroup / 8];
+#pragma unroll
+        for (int i = 0; i < kGroup / 8; ++i) {
+            uint32_t p = 0;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) p |= (uint32_t)(code[8 * i + j] & 0xf) << (4 * j);
+            packed[i] = p;
+        }
+        *reinterpret_cast<uint4*>(q + g * (kGroup / 2)) = make_uint4(packed[0], packed[1], packed[2], packed[3]);
+    }
+}
+
+// One thread per group of 32 activations of one row (fp32 steps).
+__global__ __launch_bounds__(256) void quantize_q8_0_kernel(const float* __restrict__ x, int64_t n_groups,
+                                                            int8_t* __restrict__ q, float* __restrict__ d) {
+    const int64_t g = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (g >= n_groups) return;
+    const float4* src = reinterpret_cast<const float4*>(x + g * kGroup);
+    float v[kGroup];
+#pragma unroll
+    for (int i = 0; i < kGroup / 4; ++i) {
+        const float4 f = src[i];
+        v[4 * i + 0] = f.x;
+        v[4 * i + 1] = f.y;
+        v[4 * i + 2] = f.z;
+        v[4 * i + 3] = f.w;
+    }
+    float amax = 0.0f;
+#pragma unroll
+    for (int i = 0; i < kGroup; ++i) amax = fmaxf(amax, fabsf(v[i]));
+    const float dd = __fdiv_rn(amax, 127.0f);
+    const float inv = dd != 0.0f ? __fdiv_rn(1.0f, dd) : 0.0f;
+    uint32_t packed[kGroup / 4];
+#pragma unroll
+    for (int i = 0; i < kGroup / 4; ++i) {
+        uint32_t p = 0;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            float r = rintf(__fmul_rn(v[4 * i + j], inv));
+            r = fminf(fmaxf(r, -127.0f), 127.0f);
+            p |= ((uint32_t)((int)r & 0xff)) << (8 * j);
+        }
+        packed[i] = p;
+    }
+    d[g] = dd;
+    uint4* dst = reinterpret_cast<uint4*>(q + g * kGroup);
+    dst[0] = make_uint4(packed[0], packed[1], packed[2], packed[3]);
+    dst[1] = make_uint4(packed[4], packed[5], packed[6], packed[7]);
+}
+
+hipError_t launch_quantize_weights(const float* w, int64_t rows, int cols, int bits, void* q, float* s,
+                                   hipStream_t st) {
+    const int64_t n_groups = rows * (cols / kGroup);
+    if (n_groups == 0) return hipSuccess;
+    const dim3 grid((unsigned)((n_groups + 255) / 256));
+    if (bits == 8)
+        hipLaunchKernelGGL(quantize_weights_kernel<8>, grid, dim3(256), 0, st, w, n_groups, (uint8_t*)q, s);
+    else
+        hipLaunchKernelGGL(quantize_weights_kernel<4>, grid, dim3(256), 0, st, w, n_groups, (uint8_t*)q, s);
+    return hipGetLastError();
+}
+
+hipError_t launch_quantize_q8_0(const float* x, int64_t rows, int cols, int8_t* q, float* d, hipStream_t st) {
+    const int64_t n_groups = rows * (cols / kGroup);
+    if (n_groups == 0) return hipSuccess;
+    const dim3 grid((unsigned)((n_groups + 255) / 256));
+    hipLaunchKernelGGL(quantize_q8_0_kernel, grid, dim3(256), 0, st, x, n_groups, q, d);
+    return hipGetLastError();
+}
+
+}  // namespace moe

@@ -1,0 +1,63 @@
+"""Helpers shared by the GPU parity tests: device layers built through the
+library, oracle experts built by the oracle from the same seeded fp32 weights,
+and the comparison rules."""
+from __future__ import annotations
+
+import functools
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import synth
+from oracle import ffn as offn
+from oracle import layer as olayer
+
+REL_TOL = 2e-3          # max|gpu - ref| <= REL_TOL * max|ref| (per output tensor)
+
+
+def need_gpu():
+    if not torch.cuda.is_available():
+        pytest.fail("GPU test run without a visible GPU")
+
+
+def say(*args):
+    print(*args, file=sys.stderr, flush=True)
+
+
+@functools.lru_cache(maxsize=4)
+def device_layer(name: str):
+    from quantized_expert_ffn_amd import device_layer as dl
+    shape = synth.LAYERS[name]
+    say(f"[gpu] building device layer {name}")
+    return dl.build(shape, "cuda")
+
+
+@functools.lru_cache(maxsize=2048)
+def oracle_expert(name: str, e: int) -> offn.QuantExpert:
+    shape = synth.LAYERS[name] if isinstance(name, str) else name
+    bits = 8 if shape.wformat == "int8" else 4
+    return offn.QuantExpert.from_fp32(synth.expert_weight(shape, e, "gate"), synth.expert_weight(shape, e, "up"),
+                                      synth.expert_weight(shape, e, "down"), bits)
+
+
+def router_spec(shape) -> olayer.RouterSpec:
+    return olayer.RouterSpec(mode=shape.router, top_k=shape.top_k, renormalize=shape.renormalize,
+                             n_group=shape.n_group, topk_group=shape.topk_group,
+                             routed_scaling_factor=shape.routed_scaling_factor, bias=synth.score_bias(shape))
+
+
+def assert_close_rel(gpu: np.ndarray, ref: np.ndarray, tol: float = REL_TOL, what: str = "output"):
+    gpu = np.asarray(gpu, np.float64)
+    ref = np.asarray(ref, np.float64)
+    assert gpu.shape == ref.shape, (gpu.shape, ref.shape)
+    assert np.all(np.isfinite(gpu)), f"{what}: non-finite GPU values"
+    scale = np.abs(ref).max()
+    err = np.abs(gpu - ref).max()
+    say(f"[parity] {what}: max|gpu-ref| = {err:.3e}, max|ref| = {scale:.3e}, rel = {err / max(scale, 1e-300):.3e}")
+    assert err <= tol * scale, f"{what}: max|gpu-ref| {err:.3e} > {tol} * max|ref| {scale:.3e}"
+
+
+def t2n(t: torch.Tensor) -> np.ndarray:
+    return t.detach().cpu().numpy()

@@ -1,0 +1,157 @@
+"""The C ABI on the host, without a GPU: the library loads, exports every
+entry point include/moe.h declares, and rejects bad arguments with the right
+status before anything is enqueued (no call here reaches a kernel)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from conftest import ROOT
+
+import quantized_expert_ffn_amd as qe
+from quantized_expert_ffn_amd import _lib
+
+HEADER = os.path.join(ROOT, "include", "moe.h")
+
+OK, INVALID, UNSUPPORTED, WORKSPACE = 0, -1, -2, -3
+FAKE = 0x10000          # an aligned, never dereferenced address
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[\w]+\s*\*?\s*(moe_\w+)\s*\(", text, flags=re.M)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(_lib.LIB_PATH):
+        pytest.fail("libmoe.so is not built: run `python -m quantized_expert_ffn_amd.build`")
+    return _lib.load()
+
+
+def test_exports_every_declared_symbol(lib):
+    names = declared_functions()
+    assert len(names) >= 12
+    for n in names:
+        assert hasattr(lib, n), f"{n} declared in moe.h but not exported"
+    assert set(names) == set(_lib.exported_names()), "binding and header disagree"
+
+
+def test_status_strings(lib):
+    assert qe.moe_status_string(0) == "MOE_OK"
+    for st in (INVALID, UNSUPPORTED, WORKSPACE, -4):
+        assert qe.moe_status_string(st).startswith("MOE_ERR_")
+
+
+def test_workspace_size_rules(lib):
+    ws = qe.moe_workspace_size
+    assert ws(16, 2, 8, 64, 128, 0, 0) > 0
+    assert ws(16, 2, 8, 64, 128, 1, 1) > ws(16, 2, 8, 64, 128, 1, 0)
+    assert ws(2048, 8, 64, 2048, 1024, 1, 0) > ws(16, 8, 64, 2048, 1024, 1, 0)
+    assert ws(0, 2, 8, 64, 128, 0, 0) > 0                     # T = 0 still valid
+    assert ws(16, 9, 8, 64, 128, 0, 0) == 0                   # k > E
+    assert ws(16, 2, 8, 65, 128, 0, 0) == 0                   # d % 32
+    assert ws(16, 2, 8, 64, 128, 7, 0) == 0                   # unknown act_mode
+    assert ws(-1, 2, 8, 64, 128, 0, 0) == 0
+
+
+def _params(**kw):
+    p = _lib.RouterParams()
+    p.n_experts, p.top_k, p.mode, p.renormalize = 8, 2, 0, 1
+    p.n_group, p.topk_group, p.routed_scaling_factor, p.score_bias = 1, 1, 1.0, None
+    for k, v in kw.items():
+        setattr(p, k, v)
+    return p
+
+
+def _experts(**kw):
+    e = _lib.Experts()
+    e.n_experts, e.d_model, e.d_ff, e.format = 8, 64, 128, 0
+    for f in ("gate_q", "gate_s", "up_q", "up_s", "down_q", "down_s"):
+        setattr(e, f, FAKE)
+    for k, v in kw.items():
+        setattr(e, k, v)
+    return e
+
+
+def _fwd(lib, T=4, params=None, routed=None, shared=None, act=0, ws_bytes=1 << 30, x=FAKE, out=FAKE, ws=FAKE):
+    params = params or _params()
+    routed = routed or _experts()
+    return lib.moe_layer_forward(x, T, FAKE, ctypes.byref(params), ctypes.byref(routed),
+                                 ctypes.byref(shared) if shared else None, act, out, ws, ws_bytes, None)
+
+
+def test_layer_forward_validation(lib):
+    assert _fwd(lib, T=0) == OK                                   # no-op, nothing enqueued
+    assert _fwd(lib, T=-1) == INVALID
+    assert _fwd(lib, x=None) == INVALID
+    assert _fwd(lib, act=5) == INVALID
+    assert _fwd(lib, params=_params(top_k=9)) == INVALID          # k > E
+    assert _fwd(lib, params=_params(top_k=0)) == INVALID
+    assert _fwd(lib, params=_params(n_experts=7)) == INVALID      # router E != experts E
+    assert _fwd(lib, params=_params(mode=3)) == INVALID
+    assert _fwd(lib, routed=_experts(d_model=65)) == UNSUPPORTED  # d % 32
+    assert _fwd(lib, routed=_experts(d_ff=100)) == UNSUPPORTED    # I % 32
+    assert _fwd(lib, routed=_experts(format=9)) == INVALID
+    assert _fwd(lib, routed=_experts(up_s=None)) == INVALID
+    assert _fwd(lib, routed=_experts(gate_q=FAKE + 4)) == INVALID  # misaligned codes
+    assert _fwd(lib, shared=_experts(n_experts=2)) == INVALID
+    assert _fwd(lib, shared=_experts(n_experts=1, d_ff=96)) == UNSUPPORTED
+    assert _fwd(lib, ws_bytes=16) == WORKSPACE
+    assert _fwd(lib, ws=None) == WORKSPACE
+    assert "workspace" in qe.moe_last_error_detail()
+
+
+def test_noaux_tc_validation(lib):
+    E = 16
+    base = dict(n_experts=E, mode=1, n_group=4, topk_group=2, top_k=3, routed_scaling_factor=2.5)
+    r = _experts(n_experts=E)
+
+    def run(**kw):
+        d = dict(base)
+        d.update(kw)
+        return _fwd(lib, T=0, params=_params(**d), routed=r)
+
+    assert run() == OK
+    assert run(n_group=5) == INVALID            # E % n_group
+    assert run(topk_group=5) == INVALID         # topk_group > n_group
+    assert run(top_k=9) == INVALID              # more than the 2 kept groups of 4 hold
+    assert run(n_group=0) == INVALID
+    assert run(routed_scaling_factor=float("inf")) == INVALID
+
+
+def test_route_dispatch_combine_validation(lib):
+    p = _params()
+    assert lib.moe_route(FAKE, 0, 64, FAKE, ctypes.byref(p), FAKE, FAKE, FAKE, 0, None) == OK
+    assert lib.moe_route(FAKE, 4, 64, FAKE, None, FAKE, FAKE, FAKE, 1 << 20, None) == INVALID
+    assert lib.moe_route(FAKE, 4, 64, FAKE, ctypes.byref(p), FAKE, FAKE, FAKE, 8, None) == WORKSPACE
+    big = _params(n_experts=2048, top_k=2)
+    assert lib.moe_route(FAKE, 4, 64, FAKE, ctypes.byref(big), FAKE, FAKE, FAKE, 1 << 30, None) == UNSUPPORTED
+    assert lib.moe_dispatch(FAKE, 4, 3, 2, FAKE, FAKE, FAKE, FAKE, None, 0, None) == INVALID   # k > E
+    assert lib.moe_dispatch(FAKE, 4, 2, 2000, FAKE, FAKE, FAKE, FAKE, None, 0, None) == UNSUPPORTED
+    assert lib.moe_dispatch(FAKE, 4, 2, 8, None, FAKE, FAKE, FAKE, None, 0, None) == INVALID
+    assert lib.moe_combine(FAKE, FAKE, FAKE, None, 0, 2, 64, FAKE, None) == OK
+    assert lib.moe_combine(FAKE, FAKE, FAKE, None, 4, 2, 66, FAKE, None) == UNSUPPORTED
+    assert lib.moe_combine(None, FAKE, FAKE, None, 4, 2, 64, FAKE, None) == INVALID
+    assert lib.moe_quantize_weights(FAKE, 4, 48, 0, FAKE, FAKE, None) == UNSUPPORTED
+    assert lib.moe_quantize_weights(FAKE, 4, 64, 3, FAKE, FAKE, None) == INVALID
+    assert lib.moe_quantize_weights(FAKE, 0, 64, 1, FAKE, FAKE, None) == OK
+    assert lib.moe_quantize_q8_0(FAKE, 4, 40, FAKE, FAKE, None) == UNSUPPORTED
+    e = _experts()
+    assert lib.moe_expert_ffn(FAKE, 4, 9, ctypes.byref(e), FAKE, FAKE, FAKE, 0, FAKE, FAKE, 1 << 30, None) == INVALID
+    assert lib.moe_expert_ffn(FAKE, 4, 2, ctypes.byref(e), FAKE, FAKE, FAKE, 0, FAKE, FAKE, 64, None) == WORKSPACE
+    assert lib.moe_expert_ffn(FAKE, 0, 2, ctypes.byref(e), FAKE, FAKE, FAKE, 1, FAKE, FAKE, 0, None) == OK
+    assert lib.moe_debug_q8_expert_ffn(FAKE, 4, 2, ctypes.byref(e), FAKE, FAKE, FAKE, None, FAKE, FAKE, FAKE, FAKE,
+                                       FAKE, FAKE, 1 << 30, None) == INVALID
+
+
+def test_accounting_matches_page_figures():
+    from quantized_expert_ffn_amd import accounting as acc
+    # ~19 MB per GLM routed expert at int4 is the payload; the scales add a quarter
+    glm = (6144, 2048)
+    payload = 3 * glm[0] * glm[1] // 2
+    assert abs(payload / 1e6 - 19) < 0.5
+    assert acc.expert_bytes(*glm, "int4") == payload + 3 * glm[0] * glm[1] // 32 * 4
+    assert acc.useful_ops([2, 0, 1], 3, 64, 128, False) == 2 * 3 * 3 * 64 * 128

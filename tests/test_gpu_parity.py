@@ -1,0 +1,386 @@
+"""GPU parity: the HIP library (through its C ABI) against the oracle.
+
+Bit-exact: quantised weight bytes and scales, Q8_0 codes and scales, expert
+indices (tokens whose selection margin is wider than fp32 logit rounding),
+counts, offsets, the permutation and its inverse, int32 group dots.
+Tolerance: every floating-point output tensor within 2e-3 * max|ref|.
+"""
+import numpy as np
+import pytest
+import torch
+
+import synth
+import quantized_expert_ffn_amd as qe
+from oracle import dispatch as odispatch
+from oracle import ffn as offn
+from oracle import layer as olayer
+from oracle import quant as oquant
+from oracle import router as orouter
+
+from gpu_common import (REL_TOL, assert_close_rel, device_layer, need_gpu, oracle_expert, router_spec, say, t2n)
+
+pytestmark = pytest.mark.gpu
+
+MARGIN_EPS = 1e-5      # logits closer than this may rank differently in fp32 vs fp64
+
+
+# ---------------------------------------------------------------------------
+# quantisers
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("fmt", ["int8", "int4"])
+def test_quantize_weights_bit_exact(fmt):
+    need_gpu()
+    rng = np.random.default_rng(21)
+    w = (rng.standard_normal((37, 96)) * rng.uniform(1e-4, 3, (37, 1))).astype(np.float32)
+    w[3, 32:64] = 0.0
+    w[4, :32] = 1e-30
+    bits = 8 if fmt == "int8" else 4
+    q_ref, s_ref = oquant.quantize_weights(w, bits)
+    stored = q_ref if bits == 8 else oquant.pack_int4(q_ref)
+    q = torch.empty(stored.shape, dtype=torch.int8 if bits == 8 else torch.uint8, device="cuda")
+    s = torch.empty(s_ref.shape, dtype=torch.float32, device="cuda")
+    qe.moe_quantize_weights(torch.from_numpy(w).cuda(), qe.FORMATS[fmt], q, s)
+    torch.cuda.synchronize()
+    assert np.array_equal(t2n(s), s_ref)
+    assert np.array_equal(t2n(q), stored)
+
+
+def test_quantize_q8_0_bit_exact(golden_dir):
+    need_gpu()
+    rng = np.random.default_rng(22)
+    x = (rng.standard_normal((33, 96)) * rng.uniform(1e-3, 50, (33, 1))).astype(np.float32)
+    x[2, :32] = 0.0
+    fx = [l for l in open(f"{golden_dir}/q8_0_rounding.txt") if l.strip() and not l.startswith("#")][0]
+    x[5, :32] = np.array([float(v) for v in fx.split("|")[0].split()], np.float32)
+    q_ref, d_ref = oquant.quantize_q8_0(x)
+    q = torch.empty(x.shape, dtype=torch.int8, device="cuda")
+    d = torch.empty(d_ref.shape, dtype=torch.float32, device="cuda")
+    qe.moe_quantize_q8_0(torch.from_numpy(x).cuda(), q, d)
+    torch.cuda.synchronize()
+    assert np.array_equal(t2n(d), d_ref)
+    assert np.array_equal(t2n(q), q_ref)
+
+
+# ---------------------------------------------------------------------------
+# router
+# ---------------------------------------------------------------------------
+def gpu_route(x, wg, params, k):
+    T = x.shape[0]
+    xd = torch.from_numpy(np.ascontiguousarray(x)).cuda()
+    wgd = torch.from_numpy(np.ascontiguousarray(wg)).cuda()
+    idx = torch.empty((T, k), dtype=torch.int32, device="cuda")
+    w = torch.empty((T, k), dtype=torch.float32, device="cuda")
+    ws = torch.empty(max(1, T * params.n_experts * 4), dtype=torch.uint8, device="cuda")
+    qe.moe_route(xd, wgd, params, idx, w, ws)
+    torch.cuda.synchronize()
+    return t2n(idx), t2n(w)
+
+
+def check_route(x, wg, spec: olayer.RouterSpec, bias=None):
+    E = wg.shape[0]
+    bias_d = torch.from_numpy(bias).cuda() if bias is not None else None
+    params = qe.router_params(E, spec.top_k, spec.mode, spec.renormalize, spec.n_group, spec.topk_group,
+                              spec.routed_scaling_factor, bias_d)
+    gi, gw = gpu_route(x, wg, params, spec.top_k)
+    ri, rw, l = olayer.route(x, wg, spec)
+    keys = orouter.selection_keys(l, spec.mode, spec.bias, spec.n_group, spec.topk_group)
+    margin = orouter.boundary_margin(keys, spec.top_k)
+    if spec.mode == "noaux_tc":
+        margin = np.minimum(margin, orouter.group_margin(l, spec.bias, spec.n_group, spec.topk_group))
+    near = margin < MARGIN_EPS
+    say(f"[route] T={x.shape[0]} E={E} k={spec.top_k} mode={spec.mode}: min margin {margin.min():.3e}, "
+        f"near-ties {int(near.sum())}")
+    # bit-exact wherever fp32 rounding cannot reorder the boundary
+    assert np.array_equal(gi[~near], ri[~near])
+    # near-tie tokens: the GPU choice must be a valid top-k within the margin
+    for t in np.nonzero(near)[0]:
+        sel = keys[t, gi[t]]
+        rest = np.delete(keys[t], gi[t])
+        assert sel.min() >= rest.max() - MARGIN_EPS
+    ok = ~near
+    assert np.allclose(gw[ok], rw[ok], rtol=1e-5, atol=1e-7)
+    return gi, gw
+
+
+def test_route_tiny_softmax():
+    need_gpu()
+    lay = synth.LAYERS["tiny"]
+    check_route(synth.activations(lay, 16), synth.gate_weight(lay), router_spec(lay))
+
+
+@pytest.mark.parametrize("renorm", [False, True])
+def test_route_exact_ties(renorm):
+    need_gpu()
+    x = np.random.default_rng(0).standard_normal((5, 64)).astype(np.float32)
+    wg = np.zeros((8, 64), np.float32)
+    p = qe.router_params(8, 3, "softmax", renorm)
+    gi, gw = gpu_route(x, wg, p, 3)
+    assert np.all(gi == [0, 1, 2])
+    assert np.allclose(gw, 1 / 3 if renorm else 1 / 8, rtol=1e-6)
+    wg = (np.random.default_rng(1).standard_normal((8, 64)) * 0.02).astype(np.float32)
+    wg[6] = wg[2] = x[0] * 0.5
+    gi, _ = gpu_route(x[:1], wg, qe.router_params(8, 2, "softmax", renorm), 2)
+    assert list(gi[0]) == [2, 6]
+    # sigmoid ties: all logits 0 -> all scores 0.5 -> lowest ids, weights rsf / k
+    gi, gw = gpu_route(x, np.zeros((16, 64), np.float32), qe.router_params(16, 4, "noaux_tc", False, 4, 2, 2.5), 4)
+    assert np.all(gi == [0, 1, 2, 3]) and np.allclose(gw, 2.5 / 4, rtol=1e-6)
+
+
+@pytest.mark.parametrize("e,n_group,topk_group,k", [(8, 4, 2, 2), (16, 4, 2, 3), (64, 8, 3, 6), (256, 8, 4, 8)])
+def test_route_noaux_tc_variants(e, n_group, topk_group, k):
+    need_gpu()
+    lay = synth.variant(synth.LAYERS["tiny"], router="noaux_tc", n_experts=e, n_group=n_group,
+                        topk_group=topk_group, top_k=k, has_bias=True, routed_scaling_factor=2.5)
+    x = synth.activations(lay, 64)
+    wg = (synth.gate_weight(lay) * 15).astype(np.float32)      # logits of order 1
+    spec = router_spec(lay)
+    check_route(x, wg, spec, synth.score_bias(lay))
+
+
+def test_route_max_experts_and_k():
+    need_gpu()
+    lay = synth.variant(synth.LAYERS["tiny"], n_experts=1024, top_k=64, renormalize=True)
+    x = synth.activations(lay, 37)
+    wg = (synth.gate_weight(lay) * 15).astype(np.float32)
+    check_route(x, wg, router_spec(lay))
+
+
+@pytest.mark.parametrize("name,tokens", [("olmoe", 16), ("olmoe_int4", 2048), ("glm", 4), ("qwen", 4096)])
+def test_route_full_size(name, tokens):
+    need_gpu()
+    lay = synth.LAYERS[name]
+    check_route(synth.activations(lay, tokens), synth.gate_weight(lay), router_spec(lay), synth.score_bias(lay))
+
+
+# ---------------------------------------------------------------------------
+# dispatch
+# ---------------------------------------------------------------------------
+def gpu_dispatch(idx, E):
+    T, k = idx.shape
+    n = max(1, T * k)
+    counts = torch.empty(E, dtype=torch.int32, device="cuda")
+    offsets = torch.empty(E + 1, dtype=torch.int32, device="cuda")
+    perm = torch.empty(n, dtype=torch.int32, device="cuda")
+    inv = torch.empty(n, dtype=torch.int32, device="cuda")
+    qe.moe_dispatch(torch.from_numpy(np.ascontiguousarray(idx, dtype=np.int32)).cuda(), E, counts, offsets,
+                    perm, inv)
+    torch.cuda.synchronize()
+    return t2n(counts), t2n(offsets), t2n(perm)[:T * k], t2n(inv)[:T * k]
+
+
+@pytest.mark.parametrize("T,k,E,zipf", [(16, 2, 8, False), (1, 8, 64, False), (16, 8, 64, False),
+                                        (2048, 8, 64, False), (4, 8, 256, False), (4096, 10, 512, True),
+                                        (64, 64, 1024, False), (3, 1, 1, False), (777, 3, 5, True)])
+def test_dispatch_bit_exact(T, k, E, zipf):
+    need_gpu()
+    rng = np.random.default_rng(T * 31 + k * 7 + E)
+    if zipf:
+        p = 1.0 / np.arange(1, E + 1) ** 1.1
+        p /= p.sum()
+        idx = np.stack([rng.choice(E, size=k, replace=False, p=p) for _ in range(T)])
+    else:
+        idx = np.stack([rng.choice(E, size=k, replace=False) for _ in range(T)])
+    got = gpu_dispatch(idx, E)
+    want = odispatch.dispatch(idx, E)
+    for g, w, nm in zip(got, want, ("counts", "offsets", "perm", "inv_perm")):
+        assert np.array_equal(g, w), nm
+
+
+def test_dispatch_empty_and_out_of_range():
+    need_gpu()
+    c, o, _, _ = gpu_dispatch(np.zeros((0, 2), np.int32), 8)
+    assert np.all(c == 0) and np.all(o == 0)
+    idx = np.array([[0, 3], [7, 9], [-1, 3]], np.int32)         # 9 and -1 are outside [0, 8)
+    c, o, perm, inv = gpu_dispatch(idx, 8)
+    assert c.tolist() == [1, 0, 0, 2, 0, 0, 0, 1] and o[-1] == 4
+    assert sorted(perm[:4].tolist()) == [0, 1, 2, 5]
+
+
+# ---------------------------------------------------------------------------
+# whole layer, small shapes (every output element)
+# ---------------------------------------------------------------------------
+def run_layer(dl, x_np, act_mode, copy=0, timed=False):
+    T = x_np.shape[0]
+    lay = dl.shape
+    x = torch.from_numpy(np.ascontiguousarray(x_np)).cuda()
+    out = torch.empty((T, lay.d_model), dtype=torch.float32, device="cuda")
+    ws = qe.workspace(T, lay.top_k, lay.n_experts, lay.d_model, lay.d_ff, qe.ACT_MODES[act_mode],
+                      dl.shared[copy] is not None)
+    if timed:
+        evs = [torch.cuda.Event(enable_timing=True) for _ in range(2 * qe.MOE_STAGE_COUNT)]
+        qe.moe_layer_forward_timed(x, dl.gate_w, dl.params, dl.routed[copy], dl.shared[copy],
+                                   qe.ACT_MODES[act_mode], out, ws, evs)
+    else:
+        qe.moe_layer_forward(x, dl.gate_w, dl.params, dl.routed[copy], dl.shared[copy], qe.ACT_MODES[act_mode],
+                             out, ws)
+    torch.cuda.synchronize()
+    return t2n(out)
+
+
+def oracle_layer(shape, x, act_mode, name=None):
+    key = name or shape
+    shared = oracle_expert(key, shape.n_experts) if shape.shared_expert else None
+    wg = synth.gate_weight(shape)
+    return olayer.layer_forward(x, wg, router_spec(shape), lambda e: oracle_expert(key, e), shared, act_mode)
+
+
+TINY_VARIANTS = {
+    "tiny": {},
+    "tiny_shared_noaux": dict(router="noaux_tc", n_experts=16, n_group=4, topk_group=2, top_k=3, has_bias=True,
+                              routed_scaling_factor=2.5, shared_expert=True),
+    "tiny_int4": dict(wformat="int4"),
+    "tiny_e1k1": dict(n_experts=1, top_k=1, renormalize=True),
+    "tiny_kE": dict(top_k=8, renormalize=False),
+    "tiny_wide": dict(d_model=96, d_ff=160, n_experts=6, top_k=3),
+}
+
+
+def tiny_layer(variant):
+    from quantized_expert_ffn_amd import device_layer as dl
+    shape = synth.variant(synth.LAYERS["tiny"], **TINY_VARIANTS[variant])
+    if variant not in _TINY:
+        _TINY[variant] = (shape, dl.build(shape, "cuda"))
+    return _TINY[variant]
+
+
+_TINY = {}
+
+
+@pytest.mark.parametrize("act_mode", ["f32", "q8_0"])
+@pytest.mark.parametrize("variant", list(TINY_VARIANTS))
+def test_layer_tiny(variant, act_mode):
+    need_gpu()
+    shape, dl = tiny_layer(variant)
+    for T in (16, 1, 67):
+        x = synth.activations(shape, T)
+        got = run_layer(dl, x, act_mode)
+        ref = oracle_layer(shape, x, act_mode)
+        assert_close_rel(got, ref["out"], what=f"{variant}/{act_mode}/T={T} out")
+
+
+def test_layer_zero_tokens_is_noop():
+    need_gpu()
+    shape, dl = tiny_layer("tiny")
+    out = torch.full((1, shape.d_model), 7.0, device="cuda")
+    ws = torch.empty(256, dtype=torch.uint8, device="cuda")
+    x = torch.empty((0, shape.d_model), dtype=torch.float32, device="cuda")
+    qe.moe_layer_forward(x, dl.gate_w, dl.params, dl.routed[0], None, qe.MOE_ACT_F32, out, ws)
+    torch.cuda.synchronize()
+    assert torch.all(out == 7.0)
+
+
+@pytest.mark.parametrize("act_mode", ["f32", "q8_0"])
+def test_layer_deterministic(act_mode):
+    need_gpu()
+    shape, dl = tiny_layer("tiny_shared_noaux")
+    x = synth.activations(shape, 67)
+    a = run_layer(dl, x, act_mode)
+    for _ in range(2):
+        assert np.array_equal(run_layer(dl, x, act_mode, timed=True), a)
+
+
+@pytest.mark.parametrize("act_mode", ["f32", "q8_0"])
+def test_expert_ffn_and_combine_pieces(act_mode):
+    """moe_route -> moe_dispatch -> moe_expert_ffn -> moe_combine against the oracle's
+    y_perm and out (routed only)."""
+    need_gpu()
+    shape, dl = tiny_layer("tiny_wide")
+    T = 41
+    x = synth.activations(shape, T)
+    ref = oracle_layer(synth.variant(shape, shared_expert=False), x, act_mode, name=shape)
+    k, E = shape.top_k, shape.n_experts
+    xd = torch.from_numpy(x).cuda()
+    idx = torch.empty((T, k), dtype=torch.int32, device="cuda")
+    w = torch.empty((T, k), dtype=torch.float32, device="cuda")
+    am = qe.ACT_MODES[act_mode]
+    ws = qe.workspace(T, k, E, shape.d_model, shape.d_ff, am, False)
+    qe.moe_route(xd, dl.gate_w, dl.params, idx, w, ws)
+    counts = torch.empty(E, dtype=torch.int32, device="cuda")
+    offsets = torch.empty(E + 1, dtype=torch.int32, device="cuda")
+    perm = torch.empty(T * k, dtype=torch.int32, device="cuda")
+    inv = torch.empty(T * k, dtype=torch.int32, device="cuda")
+    qe.moe_dispatch(idx, E, counts, offsets, perm, inv)
+    y = torch.empty((T * k, shape.d_model), dtype=torch.float32, device="cuda")
+    qe.moe_expert_ffn(xd, k, dl.routed[0], counts, offsets, perm, am, y, ws)
+    out = torch.empty((T, shape.d_model), dtype=torch.float32, device="cuda")
+    qe.moe_combine(y, w, inv, None, out)
+    torch.cuda.synchronize()
+    assert np.array_equal(t2n(idx), ref["idx"])
+    assert np.array_equal(t2n(perm), ref["perm"])
+    assert_close_rel(t2n(y), ref["y_perm"], what="y_perm")
+    assert_close_rel(t2n(out), ref["out"], what="out")
+
+
+@pytest.mark.parametrize("variant", ["tiny", "tiny_int4", "tiny_wide"])
+def test_q8_group_dots_bit_exact(variant):
+    """The production int8-MFMA kernels' exact int32 group dots, Q8_0(H) codes
+    and the down projection's dots fed the GPU's own H codes."""
+    need_gpu()
+    shape, dl = tiny_layer(variant)
+    T, k, E, d, I = 29, shape.top_k, shape.n_experts, shape.d_model, shape.d_ff
+    x = synth.activations(shape, T)
+    ref = oracle_layer(shape, x, "q8_0")
+    R = T * k
+    xd = torch.from_numpy(x).cuda()
+    counts = torch.from_numpy(ref["counts"]).cuda()
+    offsets = torch.from_numpy(ref["offsets"]).cuda()
+    perm = torch.from_numpy(ref["perm"]).cuda()
+    dg = torch.empty((R, I, d // 32), dtype=torch.int32, device="cuda")
+    du = torch.empty_like(dg)
+    hq = torch.empty((R, I), dtype=torch.int8, device="cuda")
+    hd = torch.empty((R, I // 32), dtype=torch.float32, device="cuda")
+    dd = torch.empty((R, d, I // 32), dtype=torch.int32, device="cuda")
+    y = torch.empty((R, d), dtype=torch.float32, device="cuda")
+    ws = qe.workspace(T, k, E, d, I, qe.MOE_ACT_Q8_0, False)
+    qe.moe_debug_q8_expert_ffn(xd, k, dl.routed[0], counts, offsets, perm, dg, du, hq, hd, dd, y, ws)
+    torch.cuda.synchronize()
+    dg, du, hq, hd, dd, y = map(t2n, (dg, du, hq, hd, dd, y))
+    xq, xdq = oquant.quantize_q8_0(x)
+    n_diff = 0
+    for e in range(E):
+        lo, hi = ref["offsets"][e], ref["offsets"][e + 1]
+        if hi == lo:
+            continue
+        ex = oracle_expert(shape, e)
+        toks = ref["perm"][lo:hi] // k
+        assert np.array_equal(dg[lo:hi], offn.group_dots(xq[toks], ex.gate_q)), f"gate dots e={e}"
+        assert np.array_equal(du[lo:hi], offn.group_dots(xq[toks], ex.up_q)), f"up dots e={e}"
+        assert np.array_equal(dd[lo:hi], offn.group_dots(hq[lo:hi], ex.down_q)), f"down dots e={e}"
+        _, parts = offn.ffn_q8(x[toks], ex)
+        diff = hq[lo:hi].astype(int) - parts["hq"].astype(int)
+        assert np.abs(diff).max() <= 1
+        n_diff += int(np.count_nonzero(diff))
+        y_ref, _ = offn.ffn_q8(x[toks], ex, hq_override=(hq[lo:hi], hd[lo:hi]))
+        assert_close_rel(y[lo:hi], y_ref, what=f"y e={e} (GPU H codes)")
+    say(f"[q8] {variant}: {n_diff} of {hq.size} H codes differ by 1 from the oracle's")
+    assert n_diff <= max(2, hq.size // 100)
+
+
+# ---------------------------------------------------------------------------
+# full-size workloads
+# ---------------------------------------------------------------------------
+SAMPLE = 48
+
+
+@pytest.mark.parametrize("wname", ["olmoe_b1", "olmoe_b16", "glm_b1", "glm_verify4", "olmoe_int4_prefill",
+                                   "qwen_prefill"])
+def test_layer_full_size(wname):
+    need_gpu()
+    wl = synth.workload(wname)
+    shape = wl.layer
+    dl = device_layer(shape.name)
+    x = synth.activations(shape, wl.tokens)
+    say(f"[gpu] {wname}: running the layer on T={wl.tokens}")
+    got = run_layer(dl, x, wl.act_mode)
+    rows = np.arange(wl.tokens)
+    if wl.tokens > SAMPLE:
+        rows = np.sort(np.random.default_rng(5).choice(wl.tokens, SAMPLE, replace=False))
+    say(f"[oracle] {wname}: {len(rows)} tokens")
+    ref = oracle_layer(shape, x[rows], wl.act_mode, name=shape.name)
+    assert_close_rel(got[rows], ref["out"], what=f"{wname} out")
+    # the same weights, byte for byte, on both sides (a few experts)
+    used = np.unique(ref["idx"])[:3]
+    for e in used:
+        ox = oracle_expert(shape.name, int(e))
+        assert np.array_equal(t2n(dl.routed[0].gate_q[e]), ox.stored("gate"))
+        assert np.array_equal(t2n(dl.routed[0].down_s[e]), ox.down_s)
