@@ -273,7 +273,8 @@ moe_status moe_route(const float* x, int32_t T, int32_t d, const float* gate_w, 
     if (T == 0) return ok();
     MOE_REQUIRE(x && gate_w && topk_idx && topk_w, MOE_ERR_INVALID_ARG, "NULL tensor argument");
     MOE_REQUIRE(aligned16(x) && aligned16(gate_w), MOE_ERR_INVALID_ARG, "x and gate_w must be 16-byte aligned");
-    const size_t need = (size_t)T * p->n_experts * sizeof(float);
+    const int S = moe::router_splits(T, p->n_experts, d);
+    const size_t need = (size_t)(S > 0 ? S : 1) * T * p->n_experts * sizeof(float);
     MOE_REQUIRE(ws != nullptr && ws_bytes >= need, MOE_ERR_WORKSPACE, "workspace %zu bytes < %zu needed",
                 ws ? ws_bytes : 0, need);
     MOE_HIP(moe::launch_router(x, T, d, gate_w, *p, static_cast<float*>(ws), topk_idx, topk_w, stream), "router");

@@ -9,41 +9,40 @@
 
 namespace moe {
 
-// One block per token; each thread owns float4 columns.
-__global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ y, const float* __restrict__ w,
-                                                      const int* __restrict__ inv_perm,
-                                                      const float* __restrict__ shared_y, int T, int k, int d,
-                                                      float* __restrict__ out) {
-    const int t = blockIdx.x;
-    if (t >= T) return;
-    const int d4 = d >> 2;
-    for (int c = threadIdx.x; c < d4; c += blockDim.x) {
-        float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-        for (int j = 0; j < k; ++j) {
-            const float wj = w[(size_t)t * k + j];
-            const int row = inv_perm[(size_t)t * k + j];
-            const float4 v = reinterpret_cast<const float4*>(y + (size_t)row * d)[c];
-            acc.x = fmaf(wj, v.x, acc.x);
-            acc.y = fmaf(wj, v.y, acc.y);
-            acc.z = fmaf(wj, v.z, acc.z);
-            acc.w = fmaf(wj, v.w, acc.w);
-        }
-        if (shared_y) {
-            const float4 s = reinterpret_cast<const float4*>(shared_y + (size_t)t * d)[c];
-            acc.x += s.x;
-            acc.y += s.y;
-            acc.z += s.z;
-            acc.w += s.w;
-        }
-        reinterpret_cast<float4*>(out + (size_t)t * d)[c] = acc;
+// Grid (column blocks of 256 floats, tokens); one wave per block, one float4
+// column per lane. The token's weights and row indices are uniform loads.
+__global__ __launch_bounds__(64) void combine_kernel(const float* __restrict__ y, const float* __restrict__ w,
+                                                     const int* __restrict__ inv_perm,
+                                                     const float* __restrict__ shared_y, int T, int k, int d,
+                                                     float* __restrict__ out) {
+    const int t = blockIdx.y;
+    const int c = blockIdx.x * 64 + threadIdx.x;
+    if (t >= T || c >= (d >> 2)) return;
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int j = 0; j < k; ++j) {
+        const float wj = w[(size_t)t * k + j];
+        const int row = inv_perm[(size_t)t * k + j];
+        const float4 v = reinterpret_cast<const float4*>(y + (size_t)row * d)[c];
+        acc.x = fmaf(wj, v.x, acc.x);
+        acc.y = fmaf(wj, v.y, acc.y);
+        acc.z = fmaf(wj, v.z, acc.z);
+        acc.w = fmaf(wj, v.w, acc.w);
     }
+    if (shared_y) {
+        const float4 s = reinterpret_cast<const float4*>(shared_y + (size_t)t * d)[c];
+        acc.x += s.x;
+        acc.y += s.y;
+        acc.z += s.z;
+        acc.w += s.w;
+    }
+    reinterpret_cast<float4*>(out + (size_t)t * d)[c] = acc;
 }
 
 hipError_t launch_combine(const float* y, const float* w, const int* inv_perm, const float* shared_y, int T, int k,
                           int d, float* out, hipStream_t st) {
     if (T == 0) return hipSuccess;
-    const int threads = d / 4 >= 256 ? 256 : ((d / 4 + 63) / 64) * 64;
-    hipLaunchKernelGGL(combine_kernel, dim3(T), dim3(threads), 0, st, y, w, inv_perm, shared_y, T, k, d, out);
+    const dim3 grid((d / 4 + 63) / 64, T);
+    hipLaunchKernelGGL(combine_kernel, grid, dim3(64), 0, st, y, w, inv_perm, shared_y, T, k, d, out);
     return hipGetLastError();
 }
 

@@ -40,6 +40,18 @@ struct WsLayout {
 
 constexpr int kTileRows = 64;         // rows (tokens) per int8-MFMA tile
 
+// Router logits: 0 = one block per expert (small T); S >= 1 = fp32 matrix-core
+// tiles of 64 x 64 with d cut into S slices, enough to give ~512 blocks.
+inline int router_splits(int T, int E, int d) {
+    if (T <= 16) return 0;
+    const int tiles = ((T + 63) / 64) * ((E + 63) / 64);
+    int s = (512 + tiles - 1) / tiles;
+    const int smax = d / 128 > 0 ? d / 128 : 1;
+    if (s > smax) s = smax;
+    return s < 1 ? 1 : s;
+}
+inline int router_kslice(int d, int S) { return ((d + S - 1) / S + 7) / 8 * 8; }
+
 inline size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
 
 inline WsLayout ws_layout(int T, int k, int E, int d, int I, int act_mode, int has_shared) {
@@ -50,7 +62,8 @@ inline WsLayout ws_layout(int T, int k, int E, int d, int I, int act_mode, int h
     const size_t R = n + (has_shared ? (size_t)T : 0);
     L.max_tiles = (int)((n + kTileRows - 1) / kTileRows + (size_t)(E < (long long)n ? E : n) +
                         (has_shared ? (T + kTileRows - 1) / kTileRows : 0));
-    L.logits = take((size_t)T * E * 4);
+    const int S = router_splits(T, E, d);
+    L.logits = take((size_t)(S > 0 ? S : 1) * T * E * 4);
     L.idx = take(n * 4);
     L.wts = take(n * 4);
     L.counts = take((size_t)E * 4);
@@ -86,12 +99,6 @@ __device__ __forceinline__ float wave_sum(float v) {
 __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll
     for (int off = 32; off > 0; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, kWave));
-    return v;
-}
-
-// Sum across aligned segments of `width` lanes (width a power of two <= 64).
-__device__ __forceinline__ float segment_sum(float v, int width) {
-    for (int off = width >> 1; off > 0; off >>= 1) v += __shfl_xor(v, off, kWave);
     return v;
 }
 

@@ -113,25 +113,36 @@ __global__ __launch_bounds__(kDispThreads) void dispatch_kernel(const int* __res
     const uint64_t lt = lanemask_lt();
     int* my_hist = hist + wave * E;
 
-    // pass 1: stable rank inside this wave's chunk
-    for (int base = begin; base < end; base += kWave) {
-        const int f = base + lane;
-        const bool valid = f < end;
-        const int e = valid ? idx[f] : 0;
-        const bool inr = valid && e >= 0 && e < E;
-        if (valid && !inr) bad_flag = 1;
-        uint64_t peers = __ballot(inr);
-        for (int b = 0; b < nbits; ++b) {
-            const bool bit = (e >> b) & 1;
-            const uint64_t m = __ballot(inr && bit);
-            peers &= bit ? m : ~m;
+    // pass 1: stable rank inside this wave's chunk; the expert ids of kPB
+    // segments are fetched together so their loads overlap
+    constexpr int kPB = 8;
+    for (int base = begin; base < end; base += kPB * kWave) {
+        int ev[kPB];
+#pragma unroll
+        for (int u = 0; u < kPB; ++u) {
+            const int f = base + u * kWave + lane;
+            ev[u] = f < end ? idx[f] : 0;
         }
-        const int rank = __popcll(peers & lt);
-        const int prior = inr ? my_hist[e] : 0;
-        // the last lane of each peer set advances the histogram; every lane has
-        // read it above, and a wave executes its LDS operations in order
-        if (inr && rank == __popcll(peers) - 1) my_hist[e] = prior + __popcll(peers);
-        if (inr) inv_perm[f] = prior + rank;
+#pragma unroll
+        for (int u = 0; u < kPB; ++u) {
+            const int f = base + u * kWave + lane;
+            const bool valid = f < end;
+            const int e = ev[u];
+            const bool inr = valid && e >= 0 && e < E;
+            if (valid && !inr) bad_flag = 1;
+            uint64_t peers = __ballot(inr);
+            for (int b = 0; b < nbits; ++b) {
+                const bool bit = (e >> b) & 1;
+                const uint64_t m = __ballot(inr && bit);
+                peers &= bit ? m : ~m;
+            }
+            const int rank = __popcll(peers & lt);
+            const int prior = inr ? my_hist[e] : 0;
+            // the last lane of each peer set advances the histogram; every lane has
+            // read it above, and a wave executes its LDS operations in order
+            if (inr && rank == __popcll(peers) - 1) my_hist[e] = prior + __popcll(peers);
+            if (inr) inv_perm[f] = prior + rank;
+        }
     }
     __syncthreads();
 
@@ -157,15 +168,24 @@ __global__ __launch_bounds__(kDispThreads) void dispatch_kernel(const int* __res
     __syncthreads();
 
     // pass 3: final positions
-    for (int base = begin; base < end; base += kWave) {
-        const int f = base + lane;
-        if (f >= end) continue;
-        const int e = idx[f];
-        if (e < 0 || e >= E) continue;
-        const int pos = my_hist[e] + inv_perm[f];
-        perm[pos] = f;
-        inv_perm[f] = pos;
-        if (row_token) row_token[pos] = f / k;
+    for (int base = begin; base < end; base += kPB * kWave) {
+        int ev[kPB], rv[kPB];
+#pragma unroll
+        for (int u = 0; u < kPB; ++u) {
+            const int f = base + u * kWave + lane;
+            ev[u] = f < end ? idx[f] : -1;
+            rv[u] = (f < end && ev[u] >= 0 && ev[u] < E) ? inv_perm[f] : 0;
+        }
+#pragma unroll
+        for (int u = 0; u < kPB; ++u) {
+            const int f = base + u * kWave + lane;
+            const int e = ev[u];
+            if (f >= end || e < 0 || e >= E) continue;
+            const int pos = my_hist[e] + rv[u];
+            perm[pos] = f;
+            inv_perm[f] = pos;
+            if (row_token) row_token[pos] = f / k;
+        }
     }
     if (row_token && has_shared)
         for (int t = tid; t < T; t += kDispThreads) row_token[n + t] = t;

@@ -45,9 +45,44 @@ struct GemvArgs {
     float* out;             // [rows, N]
 };
 
+template <int CTRL>
+__device__ __forceinline__ float dpp_src(float v) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, true));
+}
+
+// Sum over each aligned segment of `lpr` lanes; the total lands in the
+// segment's first lane (other lanes hold partial sums). DPP steps inside a
+// row of 16 lanes, a swizzle across 16, a lane read across 32.
+__device__ __forceinline__ float segment_reduce(float v, int lpr) {
+    if (lpr >= 2) v += dpp_src<0xB1>(v);    // quad_perm [1,0,3,2]
+    if (lpr >= 4) v += dpp_src<0x4E>(v);    // quad_perm [2,3,0,1]
+    if (lpr >= 8) v += dpp_src<0x141>(v);   // row_half_mirror
+    if (lpr >= 16) v += dpp_src<0x140>(v);  // row_mirror
+    if (lpr >= 32) v += __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(v), 0x401F));  // xor 16
+    if (lpr >= 64) v += __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
+    return v;
+}
+
+// Weight-stationary batch-union GEMV. A wave owns NP passes of rpp = 64/lpr
+// output rows; it issues the loads of all of them (NMAT matrices, NCH groups
+// per lane) at once, keeps the codes in registers, and then runs the slot's
+// tokens past them BT at a time, so each weight byte leaves HBM once per
+// slot whatever the number of tokens.
+// Hides a register's value from the optimiser, so the decode of the codes
+// stays inside the token loop instead of being hoisted as 4x more floats.
+__device__ __forceinline__ void opaque(uint32_t& v) { asm volatile("" : "+v"(v)); }
+
+// Passes per wave: enough rows that about 64 dwords of codes are in flight.
+__host__ __device__ constexpr int gemv_passes(int fmt, int nch, int nmat) {
+    return (64 / (nmat * nch * (fmt == MOE_W_INT8_G32 ? 8 : 4))) < 1 ? 1
+           : (64 / (nmat * nch * (fmt == MOE_W_INT8_G32 ? 8 : 4))) > 8 ? 8
+           : 64 / (nmat * nch * (fmt == MOE_W_INT8_G32 ? 8 : 4));
+}
+
 template <int FMT, int NCH, int BT, int NMAT>
 __global__ __launch_bounds__(256) void gemv_kernel(const GemvArgs a) {
-    constexpr int kDw = FMT == MOE_W_INT8_G32 ? 8 : 4;
+    constexpr int kDw = FMT == MOE_W_INT8_G32 ? 8 : 4;   // dwords per group
+    constexpr int NP = gemv_passes(FMT, NCH, NMAT);
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int slot = blockIdx.y;
     if (slot >= a.meta[0]) return;
@@ -62,17 +97,40 @@ __global__ __launch_bounds__(256) void gemv_kernel(const GemvArgs a) {
     const int rpp = kWave / lpr;
     const int sub = lane & (lpr - 1);
     const int rsub = lane / lpr;
-    const int n_begin = blockIdx.x * (4 * a.rows_per_wave) + wave * a.rows_per_wave;
+    const int n_base = (blockIdx.x * 4 + wave) * NP * rpp + rsub;
     const int row_bytes = FMT == MOE_W_INT8_G32 ? a.K : a.K / 2;
-    const uint8_t* wq[NMAT];
-    const float* wsc[NMAT];
+
+    // ---- all weight loads of this wave, up front ----
+    uint32_t wd[NP][NMAT][NCH][kDw];
+    float sc[NP][NMAT][NCH];
 #pragma unroll
-    for (int m = 0; m < NMAT; ++m) {
-        wq[m] = M[m].q + eo * M[m].q_stride;
-        wsc[m] = M[m].s + eo * M[m].s_stride;
+    for (int p = 0; p < NP; ++p) {
+        const int n = n_base + p * rpp;
+        const bool vn = n < a.N;
+#pragma unroll
+        for (int m = 0; m < NMAT; ++m) {
+            const uint8_t* rowp = M[m].q + eo * M[m].q_stride + (size_t)(vn ? n : 0) * row_bytes;
+            const float* srow = M[m].s + eo * M[m].s_stride + (size_t)(vn ? n : 0) * G;
+#pragma unroll
+            for (int c = 0; c < NCH; ++c) {
+                const int gi = c * lpr + sub;
+                const bool v = vn && gi < G;
+                const uint4* src = reinterpret_cast<const uint4*>(rowp + (size_t)(v ? gi : 0) * (kDw * 4));
+#pragma unroll
+                for (int h = 0; h < kDw / 4; ++h) {
+                    const uint4 u = v ? src[h] : make_uint4(0, 0, 0, 0);
+                    wd[p][m][c][4 * h + 0] = u.x;
+                    wd[p][m][c][4 * h + 1] = u.y;
+                    wd[p][m][c][4 * h + 2] = u.z;
+                    wd[p][m][c][4 * h + 3] = u.w;
+                }
+                sc[p][m][c] = v ? srow[gi] : 0.0f;
+            }
+        }
     }
 
     for (int tb = 0; tb < n_rows; tb += BT) {
+        // activations of BT tokens for this lane's groups
         float xr[BT][NCH][kGroup];
         float xs[BT][NCH];
 #pragma unroll
@@ -84,7 +142,8 @@ __global__ __launch_bounds__(256) void gemv_kernel(const GemvArgs a) {
             for (int c = 0; c < NCH; ++c) {
                 const int gi = c * lpr + sub;
                 const bool vg = vr && gi < G;
-                const float4* src = reinterpret_cast<const float4*>(a.x + (size_t)xrow * a.K + (size_t)gi * kGroup);
+                const float4* src =
+                    reinterpret_cast<const float4*>(a.x + (size_t)xrow * a.K + (size_t)(vg ? gi : 0) * kGroup);
                 float s = 0.0f;
 #pragma unroll
                 for (int q = 0; q < kGroup / 4; ++q) {
@@ -99,38 +158,13 @@ __global__ __launch_bounds__(256) void gemv_kernel(const GemvArgs a) {
             }
         }
 
-        for (int p = 0; p < a.rows_per_wave; p += rpp) {
-            const int n = n_begin + p + rsub;
-            const bool vn = n < a.N;
-            // issue every load of this pass before any arithmetic
-            uint32_t wd[NMAT][NCH][kDw];
-            float sc[NMAT][NCH];
 #pragma unroll
-            for (int m = 0; m < NMAT; ++m) {
-#pragma unroll
-                for (int c = 0; c < NCH; ++c) {
-                    const int gi = c * lpr + sub;
-                    const bool v = vn && gi < G;
-                    const uint4* src = reinterpret_cast<const uint4*>(
-                        wq[m] + (size_t)n * row_bytes + (size_t)gi * (kDw * 4));
-#pragma unroll
-                    for (int h = 0; h < kDw / 4; ++h) {
-                        const uint4 u = v ? src[h] : make_uint4(0, 0, 0, 0);
-                        wd[m][c][4 * h + 0] = u.x;
-                        wd[m][c][4 * h + 1] = u.y;
-                        wd[m][c][4 * h + 2] = u.z;
-                        wd[m][c][4 * h + 3] = u.w;
-                    }
-                    sc[m][c] = v ? wsc[m][(size_t)n * G + gi] : 0.0f;
-                }
-            }
+        for (int p = 0; p < NP; ++p) {
             float acc[NMAT][BT];
 #pragma unroll
-            for (int m = 0; m < NMAT; ++m)
+            for (int m = 0; m < NMAT; ++m) {
 #pragma unroll
                 for (int b = 0; b < BT; ++b) acc[m][b] = 0.0f;
-#pragma unroll
-            for (int m = 0; m < NMAT; ++m) {
 #pragma unroll
                 for (int c = 0; c < NCH; ++c) {
                     float dot[BT];
@@ -139,7 +173,9 @@ __global__ __launch_bounds__(256) void gemv_kernel(const GemvArgs a) {
                     if constexpr (FMT == MOE_W_INT8_G32) {
 #pragma unroll
                         for (int j = 0; j < 8; ++j) {
-                            const uint32_t u = wd[m][c][j] ^ 0x80808080u;
+                            uint32_t raw = wd[p][m][c][j];
+                            opaque(raw);
+                            const uint32_t u = raw ^ 0x80808080u;
                             const float f0 = (float)(u & 0xffu), f1 = (float)((u >> 8) & 0xffu);
                             const float f2 = (float)((u >> 16) & 0xffu), f3 = (float)(u >> 24);
 #pragma unroll
@@ -152,11 +188,13 @@ __global__ __launch_bounds__(256) void gemv_kernel(const GemvArgs a) {
                         }
 #pragma unroll
                         for (int b = 0; b < BT; ++b)
-                            acc[m][b] = fmaf(sc[m][c], fmaf(-128.0f, xs[b][c], dot[b]), acc[m][b]);
+                            acc[m][b] = fmaf(sc[p][m][c], fmaf(-128.0f, xs[b][c], dot[b]), acc[m][b]);
                     } else {
 #pragma unroll
                         for (int j = 0; j < 4; ++j) {
-                            const uint32_t u = wd[m][c][j] ^ 0x88888888u;
+                            uint32_t raw = wd[p][m][c][j];
+                            opaque(raw);
+                            const uint32_t u = raw ^ 0x88888888u;
                             const uint32_t lo = u & 0x0f0f0f0fu, hi = (u >> 4) & 0x0f0f0f0fu;
                             float f[8];
                             f[0] = (float)(lo & 0xffu);
@@ -174,15 +212,14 @@ __global__ __launch_bounds__(256) void gemv_kernel(const GemvArgs a) {
                         }
 #pragma unroll
                         for (int b = 0; b < BT; ++b)
-                            acc[m][b] = fmaf(sc[m][c], fmaf(-8.0f, xs[b][c], dot[b]), acc[m][b]);
+                            acc[m][b] = fmaf(sc[p][m][c], fmaf(-8.0f, xs[b][c], dot[b]), acc[m][b]);
                     }
                 }
+#pragma unroll
+                for (int b = 0; b < BT; ++b) acc[m][b] = segment_reduce(acc[m][b], lpr);
             }
-#pragma unroll
-            for (int m = 0; m < NMAT; ++m)
-#pragma unroll
-                for (int b = 0; b < BT; ++b) acc[m][b] = segment_sum(acc[m][b], lpr);
-            if (sub == 0 && vn) {
+            const int n = n_base + p * rpp;
+            if (sub == 0 && n < a.N) {
 #pragma unroll
                 for (int b = 0; b < BT; ++b) {
                     if (tb + b < n_rows) {
@@ -209,14 +246,14 @@ static hipError_t launch_gemv_fmt(GemvArgs a, int max_slots, int bt_hint, hipStr
     const int G = a.K / kGroup;
     const int nch = (G + a.lpr - 1) / a.lpr;
     const int rpp = kWave / a.lpr;
-    a.rows_per_wave = rpp > 4 ? rpp : 4;
+    a.rows_per_wave = gemv_passes(FMT, nch, NMAT) * rpp;
     const dim3 grid((a.N + 4 * a.rows_per_wave - 1) / (4 * a.rows_per_wave), max_slots);
-    const int bt = nch >= 3 ? 1 : (nch == 2 ? (bt_hint >= 2 ? 2 : 1) : (bt_hint >= 4 ? 4 : (bt_hint >= 2 ? 2 : 1)));
+    // tokens per register batch: a slot serves at most bt_hint tokens
+    const int bt = nch >= 3 ? 1 : (bt_hint >= 2 ? 2 : 1);
 #define MOE_GEMV(NCH, BT) hipLaunchKernelGGL((gemv_kernel<FMT, NCH, BT, NMAT>), grid, dim3(256), 0, st, a)
     switch (nch) {
         case 1:
-            if (bt == 4) MOE_GEMV(1, 4);
-            else if (bt == 2) MOE_GEMV(1, 2);
+            if (bt == 2) MOE_GEMV(1, 2);
             else MOE_GEMV(1, 1);
             break;
         case 2:

@@ -70,7 +70,7 @@ def gpu_route(x, wg, params, k):
     wgd = torch.from_numpy(np.ascontiguousarray(wg)).cuda()
     idx = torch.empty((T, k), dtype=torch.int32, device="cuda")
     w = torch.empty((T, k), dtype=torch.float32, device="cuda")
-    ws = torch.empty(max(1, T * params.n_experts * 4), dtype=torch.uint8, device="cuda")
+    ws = qe.workspace(T, k, params.n_experts, x.shape[1], 32, qe.MOE_ACT_F32, False)
     qe.moe_route(xd, wgd, params, idx, w, ws)
     torch.cuda.synchronize()
     return t2n(idx), t2n(w)
