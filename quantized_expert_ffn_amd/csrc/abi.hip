@@ -123,12 +123,27 @@ moe_status run_experts(const float* x, int T, int k, const moe_experts& routed, 
     const int* meta = ws_at<int>(ws, L.meta);
     if (act_mode == MOE_ACT_F32) {
         const int max_slots = (E < n ? E : n) + has_shared;
-        float* h = ws_at<float>(ws, L.h);
+        const int R = n + (has_shared ? T : 0);
+        const int fmt = routed.format;
+        _Float16* ahi = ws_at<_Float16>(ws, L.xq);
+        _Float16* alo = ws_at<_Float16>(ws, L.xd);
+        float* apow = ws_at<float>(ws, L.xp);
+        _Float16* hhi = ws_at<_Float16>(ws, L.h);
+        _Float16* hlo = ws_at<_Float16>(ws, L.hd);
+        float* hpow = ws_at<float>(ws, L.hp);
+        record(ev, 2 * MOE_STAGE_QUANT_X, st);
+        MOE_HIP(moe::launch_prep_act(fmt, x, row_token, slots, meta, max_slots, R, d, ahi, alo, apow, st),
+                "activation split");
+        record(ev, 2 * MOE_STAGE_QUANT_X + 1, st);
         record(ev, 2 * MOE_STAGE_GATEUP, st);
-        MOE_HIP(moe::launch_gemv(routed, shared, true, x, row_token, slots, meta, max_slots, T, h, st), "gate/up GEMV");
+        MOE_HIP(moe::launch_gemv(routed, shared, true, ahi, alo, apow, R, slots, meta, max_slots, hhi, hlo, hpow,
+                                 nullptr, st),
+                "gate/up GEMV");
         record(ev, 2 * MOE_STAGE_GATEUP + 1, st);
         record(ev, 2 * MOE_STAGE_DOWN, st);
-        MOE_HIP(moe::launch_gemv(routed, shared, false, h, nullptr, slots, meta, max_slots, T, y, st), "down GEMV");
+        MOE_HIP(moe::launch_gemv(routed, shared, false, hhi, hlo, hpow, R, slots, meta, max_slots, nullptr, nullptr,
+                                 nullptr, y, st),
+                "down GEMV");
         record(ev, 2 * MOE_STAGE_DOWN + 1, st);
         return MOE_OK;
     }
@@ -244,6 +259,8 @@ moe_status moe_quantize_weights(const float* w, int64_t rows, int32_t cols, int3
                                 hipStream_t stream) {
     MOE_REQUIRE(rows >= 0 && cols > 0, MOE_ERR_INVALID_ARG, "bad shape [%lld, %d]", (long long)rows, cols);
     MOE_REQUIRE(cols % moe::kGroup == 0, MOE_ERR_UNSUPPORTED, "cols = %d is not a multiple of 32", cols);
+    MOE_REQUIRE(rows % moe::kTile == 0, MOE_ERR_UNSUPPORTED, "rows = %lld is not a multiple of 32 (tiled layout)",
+                (long long)rows);
     MOE_REQUIRE(format == MOE_W_INT8_G32 || format == MOE_W_INT4_G32, MOE_ERR_INVALID_ARG, "unknown format %d",
                 format);
     if (rows == 0) return ok();

@@ -29,10 +29,12 @@ struct WsLayout {
     size_t slots = 0;      // i32  [E + 1][4]  (expert, row_begin, n_rows, 0)
     size_t tiles = 0;      // i32  [max_tiles][4] (expert, row_begin, row_end, 0)
     size_t meta = 0;       // i32  [4]  n_slots, n_tiles, status, 0
-    size_t xq = 0;         // i8   [T, d]         (Q8_0)
-    size_t xd = 0;         // f32  [T, d/32]      (Q8_0)
-    size_t h = 0;          // f32  [R, I] (F32) or i8 [R, I] (Q8_0); R = T*k + T*shared
-    size_t hd = 0;         // f32  [R, I/32]      (Q8_0)
+    size_t xq = 0;         // Q8_0: i8 [T, d]      F32: f16 hi parts [R, d]
+    size_t xd = 0;         // Q8_0: f32 [T, d/32]  F32: f16 lo parts [R, d]
+    size_t xp = 0;         //                      F32: f32 powers of two [d/32, R]
+    size_t h = 0;          // Q8_0: i8 [R, I]      F32: f16 hi parts [R, I];  R = T*k + T*shared
+    size_t hd = 0;         // Q8_0: f32 [R, I/32]  F32: f16 lo parts [R, I]
+    size_t hp = 0;         //                      F32: f32 powers of two [I/32, R]
     size_t y = 0;          // f32  [R, d]
     size_t total = 0;
     int max_tiles = 0;
@@ -80,11 +82,31 @@ inline WsLayout ws_layout(int T, int k, int E, int d, int I, int act_mode, int h
         L.h = take(R * I);
         L.hd = take(R * (I / kGroup) * 4);
     } else {
-        L.h = take(R * I * 4);
+        L.xq = take(R * d * 2);
+        L.xd = take(R * d * 2);
+        L.xp = take(R * (d / kGroup) * 4);
+        L.h = take(R * I * 2);
+        L.hd = take(R * I * 2);
+        L.hp = take(R * (I / kGroup) * 4);
     }
     L.y = take(R * d * 4);
     L.total = off;
     return L;
+}
+
+// ---------------------------------------------------------------------------
+// Weight layout in HBM: 32-row tiles, group-major inside a tile. For a matrix
+// of N rows (outputs) and K columns (reduction), G = K / 32 groups:
+//   codes  [N/32][G][32 rows][b]   b = 32 bytes (int8) or 16 bytes (int4)
+//   scales [N/32][G][32 rows]      fp32
+// so the 32 rows' codes of one group are one contiguous block (1 KB int8,
+// 512 B int4): a wave reads it with full cache lines straight into
+// matrix-core operand registers, or one row per lane.
+// ---------------------------------------------------------------------------
+constexpr int kTile = 32;
+
+__host__ __device__ __forceinline__ size_t tiled_index(size_t row, size_t g, size_t G) {
+    return ((row / kTile) * G + g) * kTile + (row % kTile);
 }
 
 // ---------------------------------------------------------------------------

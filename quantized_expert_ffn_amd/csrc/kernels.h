@@ -20,13 +20,15 @@ hipError_t launch_dispatch(const int* idx, int T, int k, int E, int* counts, int
 hipError_t launch_plan(const int* counts, const int* offsets, const int* perm, int T, int k, int E, int has_shared,
                        int* row_token, int* slots, int* tiles, int* meta, hipStream_t st);
 
-using ExpertsView = moe_experts;
-
-// gate/up (gateup = true: x [T, d] via row_token, out = H [R, I]) or
-// down (gateup = false: x = H [R, I], out = Y [R, d]).
-hipError_t launch_gemv(const ExpertsView& routed, const ExpertsView* shared, bool gateup, const float* x,
-                       const int* row_token, const int* slots, const int* meta, int max_slots, int bt_hint,
-                       float* out, hipStream_t st);
+// Decode path (fp32 activations). prep writes the activations of every
+// permuted row as exact f16 hi/lo parts + a power of two per (16-row tile of
+// a slot, 32-group);
+// the GEMV runs gate/up (x parts -> H parts) or down (H parts -> Y fp32).
+hipError_t launch_prep_act(int fmt, const float* x, const int* row_token, const int* slots, const int* meta,
+                           int max_slots, int R, int K, _Float16* ahi, _Float16* alo, float* apow, hipStream_t st);
+hipError_t launch_gemv(const moe_experts& routed, const moe_experts* shared, bool gateup, const _Float16* ahi,
+                       const _Float16* alo, const float* apow, int R, const int* slots, const int* meta, int max_slots,
+                       _Float16* hhi, _Float16* hlo, float* hpow, float* y, hipStream_t st);
 
 hipError_t launch_q8_mfma(const moe_experts& routed, const moe_experts* shared, bool gateup, const int8_t* a_q,
                           const float* a_s, const int* row_token, const int* tiles, const int* meta, int max_tiles,

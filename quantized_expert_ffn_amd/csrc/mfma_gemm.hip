@@ -109,20 +109,21 @@ __global__ __launch_bounds__(256) void q8_mfma_kernel(const MfmaArgs a) {
     const int sa_row = tid >> 2, sa_g = tid & 3;
     const bool sa_ok = sa_row < rows;
     const int sa_src = a.row_token ? a.row_token[row_begin + (sa_ok ? sa_row : 0)] : row_begin + (sa_ok ? sa_row : 0);
-    // B weight rows: brow in [0, 128) -> (matrix, output row)
-    auto b_src = [&](int brow, const uint8_t*& q, const float*& s, int& n, bool& ok) {
+    // B: 4 tiles of 32 weight rows per block (gate/up: 2 gate + 2 up tiles;
+    // down: 4 down tiles). Tile bt of the block -> matrix codes/scales + tile row.
+    auto b_tile = [&](int bt, const uint8_t*& q, const float*& s, int& tile) {
         if (GATEUP) {
-            const bool up = brow >= kBRows / 2;
-            n = n0 + (up ? brow - kBRows / 2 : brow);
+            const bool up = bt >= 2;
             q = up ? wq1 : wq0;
             s = up ? ws1 : ws0;
+            tile = n0 / kTile + (up ? bt - 2 : bt);
         } else {
-            n = n0 + brow;
             q = wq0;
             s = ws0;
+            tile = n0 / kTile + bt;
         }
-        ok = n < N;
     };
+    constexpr int kBpg = FMT == MOE_W_INT8_G32 ? 32 : 16;   // code bytes per row per group
 
     constexpr int kBLoads = FMT == MOE_W_INT8_G32 ? 4 : 2;
     uint4 ra[2];
@@ -142,45 +143,32 @@ __global__ __launch_bounds__(256) void q8_mfma_kernel(const MfmaArgs a) {
                        : make_uint4(0, 0, 0, 0);
         }
         rsa = (sa_ok && g0 + sa_g < G) ? a.a_s[(size_t)sa_src * G + g0 + sa_g] : 0.0f;
-        if constexpr (FMT == MOE_W_INT8_G32) {
+        // one (tile, group) block of codes is contiguous: a wave reads it whole
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int li = tid + 256 * r;
-                const int brow = li >> 3, chunk = li & 7;
-                const uint8_t* q;
-                const float* s;
-                int n;
-                bool ok;
-                b_src(brow, q, s, n, ok);
-                ok = ok && (k0 + chunk * 16) < K;
-                rb[r] = ok ? *reinterpret_cast<const uint4*>(q + (size_t)n * row_bytes + k0 + chunk * 16)
-                           : make_uint4(0, 0, 0, 0);
-            }
-        } else {
-#pragma unroll
-            for (int r = 0; r < 2; ++r) {
-                const int li = tid + 256 * r;
-                const int brow = li >> 2, g = li & 3;
-                const uint8_t* q;
-                const float* s;
-                int n;
-                bool ok;
-                b_src(brow, q, s, n, ok);
-                ok = ok && (g0 + g) < G;
-                rb[r] = ok ? *reinterpret_cast<const uint4*>(q + (size_t)n * row_bytes + (size_t)(g0 + g) * 16)
-                           : make_uint4(0, 0, 0, 0);
-            }
+        for (int r = 0; r < kBLoads; ++r) {
+            const int li = tid + 256 * r;
+            const int lanes_per_block = FMT == MOE_W_INT8_G32 ? 64 : 32;
+            const int blk = li / lanes_per_block, j = li % lanes_per_block;
+            const int bt = blk >> 2, g = blk & 3;
+            const uint8_t* q;
+            const float* sp;
+            int tile;
+            b_tile(bt, q, sp, tile);
+            const bool ok = tile * kTile < N && g0 + g < G;
+            rb[r] = ok ? *reinterpret_cast<const uint4*>(q + ((size_t)tile * G + g0 + g) * (kTile * kBpg) + j * 16)
+                       : make_uint4(0, 0, 0, 0);
         }
 #pragma unroll
         for (int r = 0; r < 2; ++r) {
             const int li = tid + 256 * r;
-            const int brow = li >> 2, g = li & 3;
+            const int blk = li >> 5, r32 = li & 31;
+            const int bt = blk >> 2, g = blk & 3;
             const uint8_t* q;
-            const float* s;
-            int n;
-            bool ok;
-            b_src(brow, q, s, n, ok);
-            rsb[r] = (ok && g0 + g < G) ? s[(size_t)n * G + g0 + g] * kWScale : 0.0f;
+            const float* sp;
+            int tile;
+            b_tile(bt, q, sp, tile);
+            const bool ok = tile * kTile < N && g0 + g < G;
+            rsb[r] = ok ? sp[((size_t)tile * G + g0 + g) * kTile + r32] * kWScale : 0.0f;
         }
     };
 
@@ -200,13 +188,16 @@ __global__ __launch_bounds__(256) void q8_mfma_kernel(const MfmaArgs a) {
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int li = tid + 256 * r;
-                *reinterpret_cast<uint4*>(B + (li >> 3) * kLdsRow + (li & 7) * 16) = rb[r];
+                const int blk = li >> 6, j = li & 63;
+                const int brow = (blk >> 2) * kTile + (j >> 1), g = blk & 3, half = j & 1;
+                *reinterpret_cast<uint4*>(B + brow * kLdsRow + g * kGroup + half * 16) = rb[r];
             }
         } else {
 #pragma unroll
             for (int r = 0; r < 2; ++r) {
                 const int li = tid + 256 * r;
-                const int brow = li >> 2, g = li & 3;
+                const int blk = li >> 5, r32 = li & 31;
+                const int brow = (blk >> 2) * kTile + r32, g = blk & 3;
                 uint4 w0, w1;
                 widen_int4x8(rb[r].x, w0.x, w0.y);
                 widen_int4x8(rb[r].y, w0.z, w0.w);
@@ -220,7 +211,8 @@ __global__ __launch_bounds__(256) void q8_mfma_kernel(const MfmaArgs a) {
 #pragma unroll
         for (int r = 0; r < 2; ++r) {
             const int li = tid + 256 * r;
-            SB[(li >> 2) * kGroupsPerStage + (li & 3)] = rsb[r];
+            const int blk = li >> 5, r32 = li & 31;
+            SB[((blk >> 2) * kTile + r32) * kGroupsPerStage + (blk & 3)] = rsb[r];
         }
     };
 

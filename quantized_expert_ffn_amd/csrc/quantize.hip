@@ -11,15 +11,17 @@
 
 namespace moe {
 
-// One thread per group of 32 consecutive weights of one row.
+// One thread per group of 32 consecutive weights of one row; the codes and the
+// scale are stored in the 32-row tiled layout (common.h).
 template <int BITS>
 __global__ __launch_bounds__(256) void quantize_weights_kernel(const float* __restrict__ w,
-                                                               int64_t n_groups,
+                                                               int64_t n_groups, int G,
                                                                uint8_t* __restrict__ q,
                                                                float* __restrict__ s) {
-    const int64_t g = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (g >= n_groups) return;
-    const float4* src = reinterpret_cast<const float4*>(w + g * kGroup);
+    const int64_t gi = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (gi >= n_groups) return;
+    const float4* src = reinterpret_cast<const float4*>(w + gi * kGroup);
+    const size_t g = tiled_index((size_t)(gi / G), (size_t)(gi % G), (size_t)G);
     float v[kGroup];
 #pragma unroll
     for (int i = 0; i < kGroup / 4; ++i) {
@@ -104,13 +106,14 @@ __global__ __launch_bounds__(256) void quantize_q8_0_kernel(const float* __restr
 
 hipError_t launch_quantize_weights(const float* w, int64_t rows, int cols, int bits, void* q, float* s,
                                    hipStream_t st) {
-    const int64_t n_groups = rows * (cols / kGroup);
+    const int G = cols / kGroup;
+    const int64_t n_groups = rows * G;
     if (n_groups == 0) return hipSuccess;
     const dim3 grid((unsigned)((n_groups + 255) / 256));
     if (bits == 8)
-        hipLaunchKernelGGL(quantize_weights_kernel<8>, grid, dim3(256), 0, st, w, n_groups, (uint8_t*)q, s);
+        hipLaunchKernelGGL(quantize_weights_kernel<8>, grid, dim3(256), 0, st, w, n_groups, G, (uint8_t*)q, s);
     else
-        hipLaunchKernelGGL(quantize_weights_kernel<4>, grid, dim3(256), 0, st, w, n_groups, (uint8_t*)q, s);
+        hipLaunchKernelGGL(quantize_weights_kernel<4>, grid, dim3(256), 0, st, w, n_groups, G, (uint8_t*)q, s);
     return hipGetLastError();
 }
 

@@ -61,3 +61,18 @@ def assert_close_rel(gpu: np.ndarray, ref: np.ndarray, tol: float = REL_TOL, wha
 
 def t2n(t: torch.Tensor) -> np.ndarray:
     return t.detach().cpu().numpy()
+
+
+def untile_codes(tiled: np.ndarray, n_rows: int, bytes_per_group: int) -> np.ndarray:
+    """Library weight codes (32-row tiles, group-major inside a tile:
+    [N/32][G][32][b]) back to row-major [N, G*b]."""
+    flat = np.asarray(tiled).reshape(-1)
+    g = flat.size // (n_rows * bytes_per_group)
+    return flat.reshape(n_rows // 32, g, 32, bytes_per_group).transpose(0, 2, 1, 3).reshape(n_rows, g * bytes_per_group)
+
+
+def untile_scales(tiled: np.ndarray, n_rows: int) -> np.ndarray:
+    """Library group scales ([N/32][G][32]) back to row-major [N, G]."""
+    flat = np.asarray(tiled).reshape(-1)
+    g = flat.size // n_rows
+    return flat.reshape(n_rows // 32, g, 32).transpose(0, 2, 1).reshape(n_rows, g)

@@ -135,8 +135,9 @@ def test_route_dispatch_combine_validation(lib):
     assert lib.moe_combine(FAKE, FAKE, FAKE, None, 0, 2, 64, FAKE, None) == OK
     assert lib.moe_combine(FAKE, FAKE, FAKE, None, 4, 2, 66, FAKE, None) == UNSUPPORTED
     assert lib.moe_combine(None, FAKE, FAKE, None, 4, 2, 64, FAKE, None) == INVALID
-    assert lib.moe_quantize_weights(FAKE, 4, 48, 0, FAKE, FAKE, None) == UNSUPPORTED
-    assert lib.moe_quantize_weights(FAKE, 4, 64, 3, FAKE, FAKE, None) == INVALID
+    assert lib.moe_quantize_weights(FAKE, 32, 48, 0, FAKE, FAKE, None) == UNSUPPORTED   # cols % 32
+    assert lib.moe_quantize_weights(FAKE, 40, 64, 0, FAKE, FAKE, None) == UNSUPPORTED   # rows % 32 (tiles)
+    assert lib.moe_quantize_weights(FAKE, 32, 64, 3, FAKE, FAKE, None) == INVALID
     assert lib.moe_quantize_weights(FAKE, 0, 64, 1, FAKE, FAKE, None) == OK
     assert lib.moe_quantize_q8_0(FAKE, 4, 40, FAKE, FAKE, None) == UNSUPPORTED
     e = _experts()

@@ -17,7 +17,8 @@ from oracle import layer as olayer
 from oracle import quant as oquant
 from oracle import router as orouter
 
-from gpu_common import (REL_TOL, assert_close_rel, device_layer, need_gpu, oracle_expert, router_spec, say, t2n)
+from gpu_common import (REL_TOL, assert_close_rel, device_layer, need_gpu, oracle_expert, router_spec, say, t2n,
+                        untile_codes, untile_scales)
 
 pytestmark = pytest.mark.gpu
 
@@ -31,7 +32,7 @@ MARGIN_EPS = 1e-5      # logits closer than this may rank differently in fp32 vs
 def test_quantize_weights_bit_exact(fmt):
     need_gpu()
     rng = np.random.default_rng(21)
-    w = (rng.standard_normal((37, 96)) * rng.uniform(1e-4, 3, (37, 1))).astype(np.float32)
+    w = (rng.standard_normal((64, 96)) * rng.uniform(1e-4, 3, (64, 1))).astype(np.float32)
     w[3, 32:64] = 0.0
     w[4, :32] = 1e-30
     bits = 8 if fmt == "int8" else 4
@@ -41,8 +42,8 @@ def test_quantize_weights_bit_exact(fmt):
     s = torch.empty(s_ref.shape, dtype=torch.float32, device="cuda")
     qe.moe_quantize_weights(torch.from_numpy(w).cuda(), qe.FORMATS[fmt], q, s)
     torch.cuda.synchronize()
-    assert np.array_equal(t2n(s), s_ref)
-    assert np.array_equal(t2n(q), stored)
+    assert np.array_equal(untile_scales(t2n(s), 64), s_ref)
+    assert np.array_equal(untile_codes(t2n(q), 64, 32 if bits == 8 else 16), stored)
 
 
 def test_quantize_q8_0_bit_exact(golden_dir):
@@ -380,7 +381,34 @@ def test_layer_full_size(wname):
     assert_close_rel(got[rows], ref["out"], what=f"{wname} out")
     # the same weights, byte for byte, on both sides (a few experts)
     used = np.unique(ref["idx"])[:3]
+    bpg = 32 if shape.wformat == "int8" else 16
     for e in used:
         ox = oracle_expert(shape.name, int(e))
-        assert np.array_equal(t2n(dl.routed[0].gate_q[e]), ox.stored("gate"))
-        assert np.array_equal(t2n(dl.routed[0].down_s[e]), ox.down_s)
+        assert np.array_equal(untile_codes(t2n(dl.routed[0].gate_q[e]), shape.d_ff, bpg), ox.stored("gate"))
+        assert np.array_equal(untile_scales(t2n(dl.routed[0].down_s[e]), shape.d_model), ox.down_s)
+
+
+@pytest.mark.parametrize("act_mode", ["f32", "q8_0"])
+def test_layer_hip_graph_replay(act_mode):
+    """The layer captured in a HIP graph: every replay, with eager work and
+    synchronisation between replays, equals the eager result bit for bit."""
+    need_gpu()
+    shape, dl = tiny_layer("tiny_shared_noaux")
+    T = 67
+    x = torch.from_numpy(synth.activations(shape, T)).cuda()
+    am = qe.ACT_MODES[act_mode]
+    ws = qe.workspace(T, shape.top_k, shape.n_experts, shape.d_model, shape.d_ff, am, True)
+    eager = torch.empty((T, shape.d_model), dtype=torch.float32, device="cuda")
+    qe.moe_layer_forward(x, dl.gate_w, dl.params, dl.routed[0], dl.shared[0], am, eager, ws)
+    torch.cuda.synchronize()
+    out = torch.zeros_like(eager)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        qe.moe_layer_forward(x, dl.gate_w, dl.params, dl.routed[0], dl.shared[0], am, out, ws)
+    for r in range(4):
+        out.zero_()
+        ws.fill_(0xAB)                      # eager work between replays, scrambling the workspace
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, eager), f"replay {r} differs"
