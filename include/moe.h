@@ -29,13 +29,27 @@
  *     moe_last_error_detail() gives a text for the last error of the
  *     calling thread.
  *   - T = 0 tokens is a valid no-op.
- *   - All matrices are row-major and contiguous. d = d_model, I = d_ff,
- *     E = routed experts, k = top_k, G_d = d / 32, G_I = I / 32.
+ *   - Activations and outputs are row-major and contiguous. d = d_model,
+ *     I = d_ff, E = routed experts, k = top_k, G_d = d / 32, G_I = I / 32.
  *   - Weight formats (group 32 along each matrix's input axis, fp32 scale per
  *     group, symmetric): MOE_W_INT8_G32 stores int8 codes in [-127, 127];
- *     MOE_W_INT4_G32 stores codes in [-7, 7] as 4-bit two's complement, two
- *     per byte, element 2i in the low nibble of byte i. A group's weights are
- *     scale * code.
+ *     MOE_W_INT4_G32 stores codes in [-7, 7] as 4-bit two's complement, eight
+ *     to a little-endian dword, the lower k in the lower nibble. A group's
+ *     weights are scale * code.
+ *   - Weight layout ("lane-tiled"; written by moe_quantize_weights, read by
+ *     every expert kernel). A matrix of N rows (outputs) and K columns
+ *     (inputs), N % 32 == 0, K % 64 == 0, is cut into 32-row tiles, tile t
+ *     holding rows 32t .. 32t+31. Inside a tile, "lane" l = nl + 16h
+ *     (0 <= nl < 16, 0 <= h < 4) owns, for each group g, the codes of
+ *     k = 32g + 8h .. 32g + 8h + 7 of rows 32t + nl and 32t + 16 + nl:
+ *       int8 codes   byte ((t*G + g)*64 + l)*16 + 8*(row >= 16) + (k % 8),
+ *                    G = K/32 (row = row % 32; K*N bytes in all);
+ *       int4 codes   dword ((t*P + g/2)*64 + l)*4 + 2*(g % 2) + (row >= 16),
+ *                    P = K/64, nibble k % 8 (K*N/2 bytes in all);
+ *       scales fp32  float (t*P + g/2)*64 + 4*nl + 2*(g % 2) + (row >= 16)
+ *                    (K*N/32 floats in all).
+ *     A wave thus reads 1 KB of operands per 16-byte load, and one scale load
+ *     covers two groups.
  *   - Results are deterministic: the same inputs give bitwise equal outputs
  *     (no floating-point atomics anywhere).
  */
@@ -110,13 +124,14 @@ typedef struct {
     const float* score_bias;
 } moe_router_params;
 
-/* A stack of n_experts quantised SwiGLU experts (device pointers).
- *   gate_q, up_q : [E, I, d] int8 codes, or [E, I, d/2] packed int4 bytes
- *   gate_s, up_s : [E, I, d/32] fp32 scales
- *   down_q       : [E, d, I] int8, or [E, d, I/2] packed int4
- *   down_s       : [E, d, I/32] fp32
+/* A stack of n_experts quantised SwiGLU experts (device pointers), each
+ * matrix in the lane-tiled layout above, experts back to back:
+ *   gate_q, up_q : per expert an [I x d] matrix: I*d bytes (int8) or I*d/2 (int4)
+ *   gate_s, up_s : per expert I*d/32 fp32
+ *   down_q       : per expert a [d x I] matrix: d*I bytes (int8) or d*I/2 (int4)
+ *   down_s       : per expert d*I/32 fp32
  * Expert e computes  y = (silu(x Wg^T) * (x Wu^T)) Wd^T  with W = scale*code.
- * d % 32 == 0 and I % 32 == 0 are required.
+ * d % 64 == 0 and I % 64 == 0 are required (MOE_ERR_UNSUPPORTED otherwise).
  */
 typedef struct {
     int32_t n_experts;
@@ -142,10 +157,13 @@ size_t moe_workspace_size(int32_t T, int32_t k, int32_t E, int32_t d, int32_t d_
 
 /* Group-32 symmetric weight quantiser ("mtlm-7m-base", section "Files";
  * "Show HN: colibri", section "What's implemented": int8 / packed int4).
- *   w      device fp32 [rows, cols], cols % 32 == 0
- *   format MOE_W_INT8_G32 -> q is int8 [rows, cols];
- *          MOE_W_INT4_G32 -> q is packed uint8 [rows, cols/2]
- *   s      device fp32 [rows, cols/32]
+ *   w      device fp32 [rows, cols] row-major, rows % 32 == 0, cols % 64 == 0
+ *          (a stack of matrices of the same cols, each with rows % 32 == 0,
+ *          may be passed as one call)
+ *   format MOE_W_INT8_G32 -> q holds rows*cols bytes;
+ *          MOE_W_INT4_G32 -> q holds rows*cols/2 bytes
+ *   s      device fp32, rows*cols/32 floats
+ *   q and s are written in the lane-tiled layout described at the top.
  * Per group: s = amax/qmax (qmax 127 or 7, fp32 divide), code =
  * clamp(round_half_even(w/s), -qmax, qmax) (fp32 divide); amax == 0 gives
  * s = 0 and codes 0.

@@ -153,8 +153,11 @@ def router_params(n_experts: int, top_k: int, mode: str = "softmax", renormalize
 class QuantExperts:
     """A stack of quantised SwiGLU experts in the library's layout (GPU tensors).
 
-    gate_q / up_q [E, I, d] (int8) or [E, I, d/2] (uint8, packed int4), scales
-    [E, I, d/32]; down_q [E, d, I] or [E, d, I/2], scales [E, d, I/32].
+    Tensor shapes give the per-expert storage size only: gate_q / up_q hold
+    I*d bytes (int8) or I*d/2 (packed int4) per expert, shaped [E, I, d] or
+    [E, I, d/2]; scales I*d/32 floats, shaped [E, I, d/32]; down_q / down_s
+    likewise with d and I swapped. The bytes inside are in the lane-tiled
+    layout of include/moe.h (32-row tiles, lane-ordered), not row-major.
     """
 
     def __init__(self, fmt: str, gate_q, gate_s, up_q, up_s, down_q, down_s):

@@ -78,8 +78,8 @@ moe_status check_experts(const moe_experts* ex, const char* name, int act_mode) 
     MOE_REQUIRE(ex->n_experts >= 1, MOE_ERR_INVALID_ARG, "%s n_experts = %d", name, ex->n_experts);
     MOE_REQUIRE(ex->d_model > 0 && ex->d_ff > 0, MOE_ERR_INVALID_ARG, "%s d_model %d / d_ff %d must be > 0", name,
                 ex->d_model, ex->d_ff);
-    MOE_REQUIRE(ex->d_model % moe::kGroup == 0 && ex->d_ff % moe::kGroup == 0, MOE_ERR_UNSUPPORTED,
-                "%s d_model %d and d_ff %d must be multiples of 32", name, ex->d_model, ex->d_ff);
+    MOE_REQUIRE(ex->d_model % (2 * moe::kGroup) == 0 && ex->d_ff % (2 * moe::kGroup) == 0, MOE_ERR_UNSUPPORTED,
+                "%s d_model %d and d_ff %d must be multiples of 64 (pairs of groups)", name, ex->d_model, ex->d_ff);
     MOE_REQUIRE(ex->format == MOE_W_INT8_G32 || ex->format == MOE_W_INT4_G32, MOE_ERR_INVALID_ARG,
                 "%s unknown weight format %d", name, ex->format);
     MOE_REQUIRE(ex->gate_q && ex->gate_s && ex->up_q && ex->up_s && ex->down_q && ex->down_s, MOE_ERR_INVALID_ARG,
@@ -97,6 +97,17 @@ moe_status check_experts(const moe_experts* ex, const char* name, int act_mode) 
 moe_status check_act_mode(int act_mode) {
     MOE_REQUIRE(act_mode == MOE_ACT_F32 || act_mode == MOE_ACT_Q8_0, MOE_ERR_INVALID_ARG, "unknown act_mode %d",
                 act_mode);
+    return MOE_OK;
+}
+
+// The f32 path addresses its activation parts ([R, max(d, I)] f16, R = T*k
+// rows plus T for a shared expert) with 32-bit offsets.
+moe_status check_f32_rows(int act_mode, int T, int k, int has_shared, const moe_experts* ex) {
+    if (act_mode != MOE_ACT_F32) return MOE_OK;
+    const int64_t R = (int64_t)T * k + (has_shared ? T : 0);
+    const int64_t K = ex->d_model > ex->d_ff ? ex->d_model : ex->d_ff;
+    MOE_REQUIRE(R * K * 2 < ((int64_t)1 << 31), MOE_ERR_UNSUPPORTED,
+                "the f32 path takes up to 2^30 activation values (T*k rows of max(d, d_ff)); use MOE_ACT_Q8_0");
     return MOE_OK;
 }
 
@@ -179,6 +190,7 @@ moe_status expert_ffn_impl(const float* x, int32_t T, int32_t k, const moe_exper
     MOE_REQUIRE(ex->n_experts <= moe::kMaxExperts, MOE_ERR_UNSUPPORTED, "n_experts = %d > %d", ex->n_experts,
                 moe::kMaxExperts);
     if (T == 0) return ok();
+    if ((s = check_f32_rows(act_mode, T, k, 0, ex)) != MOE_OK) return s;
     MOE_REQUIRE(x && counts && offsets && perm && y_perm, MOE_ERR_INVALID_ARG, "NULL tensor argument");
     MOE_REQUIRE(aligned16(x) && aligned16(y_perm), MOE_ERR_INVALID_ARG, "x and y_perm must be 16-byte aligned");
     const moe::WsLayout L = moe::ws_layout(T, k, ex->n_experts, ex->d_model, ex->d_ff, act_mode, 0);
@@ -211,6 +223,7 @@ moe_status layer_forward_impl(const float* x, int32_t T, const float* gate_w, co
     }
     MOE_REQUIRE(T >= 0, MOE_ERR_INVALID_ARG, "T = %d < 0", T);
     if (T == 0) return ok();
+    if ((s = check_f32_rows(act_mode, T, p->top_k, shared != nullptr, routed)) != MOE_OK) return s;
     MOE_REQUIRE(x && gate_w && out, MOE_ERR_INVALID_ARG, "NULL tensor argument");
     MOE_REQUIRE(aligned16(x) && aligned16(gate_w) && aligned16(out), MOE_ERR_INVALID_ARG,
                 "x, gate_w and out must be 16-byte aligned");
@@ -258,7 +271,8 @@ size_t moe_workspace_size(int32_t T, int32_t k, int32_t E, int32_t d, int32_t d_
 moe_status moe_quantize_weights(const float* w, int64_t rows, int32_t cols, int32_t format, void* q, float* s,
                                 hipStream_t stream) {
     MOE_REQUIRE(rows >= 0 && cols > 0, MOE_ERR_INVALID_ARG, "bad shape [%lld, %d]", (long long)rows, cols);
-    MOE_REQUIRE(cols % moe::kGroup == 0, MOE_ERR_UNSUPPORTED, "cols = %d is not a multiple of 32", cols);
+    MOE_REQUIRE(cols % (2 * moe::kGroup) == 0, MOE_ERR_UNSUPPORTED,
+                "cols = %d is not a multiple of 64 (pairs of groups)", cols);
     MOE_REQUIRE(rows % moe::kTile == 0, MOE_ERR_UNSUPPORTED, "rows = %lld is not a multiple of 32 (tiled layout)",
                 (long long)rows);
     MOE_REQUIRE(format == MOE_W_INT8_G32 || format == MOE_W_INT4_G32, MOE_ERR_INVALID_ARG, "unknown format %d",

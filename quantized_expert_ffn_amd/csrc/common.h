@@ -31,10 +31,10 @@ struct WsLayout {
     size_t meta = 0;       // i32  [4]  n_slots, n_tiles, status, 0
     size_t xq = 0;         // Q8_0: i8 [T, d]      F32: f16 hi parts [R, d]
     size_t xd = 0;         // Q8_0: f32 [T, d/32]  F32: f16 lo parts [R, d]
-    size_t xp = 0;         //                      F32: f32 powers of two [d/32, R]
+    size_t xp = 0;         //                      F32: f32 powers of two [R, d/32]
     size_t h = 0;          // Q8_0: i8 [R, I]      F32: f16 hi parts [R, I];  R = T*k + T*shared
     size_t hd = 0;         // Q8_0: f32 [R, I/32]  F32: f16 lo parts [R, I]
-    size_t hp = 0;         //                      F32: f32 powers of two [I/32, R]
+    size_t hp = 0;         //                      F32: f32 powers of two [R, I/32]
     size_t y = 0;          // f32  [R, d]
     size_t total = 0;
     int max_tiles = 0;
@@ -95,18 +95,40 @@ inline WsLayout ws_layout(int T, int k, int E, int d, int I, int act_mode, int h
 }
 
 // ---------------------------------------------------------------------------
-// Weight layout in HBM: 32-row tiles, group-major inside a tile. For a matrix
-// of N rows (outputs) and K columns (reduction), G = K / 32 groups:
-//   codes  [N/32][G][32 rows][b]   b = 32 bytes (int8) or 16 bytes (int4)
-//   scales [N/32][G][32 rows]      fp32
-// so the 32 rows' codes of one group are one contiguous block (1 KB int8,
-// 512 B int4): a wave reads it with full cache lines straight into
-// matrix-core operand registers, or one row per lane.
+// Weight layout in HBM. A matrix of N rows (outputs) and K columns (reduction
+// axis), N % 32 == 0 and K % 64 == 0, is cut into 32-row tiles; G = K / 32
+// groups, P = G / 2 group pairs. Inside a tile the data is ordered by lane of
+// a 64-lane wave: lane l = nl + 16 h (nl < 16, h < 4) holds, for one group,
+// the 8 codes k = 8h .. 8h+7 of rows nl and 16 + nl -- exactly its part of
+// the B operands of two 16x16x32 matrix-core products (rows 0-15, 16-31).
+//   int8 codes:  block (tile, group) of 1 KB; lane l's 16 bytes at l*16:
+//                [row nl: 8 codes][row 16+nl: 8 codes]
+//   int4 codes:  block (tile, pair) of 1 KB; lane l's 16 bytes at l*16, four
+//                dwords of 8 nibbles (low nibble = lower k):
+//                [row nl, g0][row 16+nl, g0][row nl, g1][row 16+nl, g1]
+//   scales fp32: block (tile, pair) of 64 floats; lane quad nl at nl*4:
+//                [row nl, g0][row 16+nl, g0][row nl, g1][row 16+nl, g1]
+// (g0 = 2p, g1 = 2p + 1.) One 16-byte load per lane thus moves 1 KB of a
+// wave's operands, and one scale load covers two groups.
 // ---------------------------------------------------------------------------
 constexpr int kTile = 32;
 
-__host__ __device__ __forceinline__ size_t tiled_index(size_t row, size_t g, size_t G) {
-    return ((row / kTile) * G + g) * kTile + (row % kTile);
+// byte offset of the 8 int8 codes (row, k = 8*(k8) .. +7), k8 = k / 8 in 0..K/8
+__host__ __device__ __forceinline__ size_t int8_code_offset(size_t row, size_t k8, size_t G) {
+    const size_t g = k8 >> 2, h = k8 & 3, r = row % kTile;
+    return ((row / kTile) * G + g) * 1024 + ((r & 15) + 16 * h) * 16 + (r >> 4) * 8;
+}
+
+// byte offset of the dword holding the 8 int4 codes (row, k = 8*k8 .. +7)
+__host__ __device__ __forceinline__ size_t int4_code_offset(size_t row, size_t k8, size_t G) {
+    const size_t g = k8 >> 2, h = k8 & 3, r = row % kTile;
+    return ((row / kTile) * (G / 2) + (g >> 1)) * 1024 + ((r & 15) + 16 * h) * 16 + ((g & 1) * 2 + (r >> 4)) * 4;
+}
+
+// float index of the scale of (row, group g)
+__host__ __device__ __forceinline__ size_t scale_index(size_t row, size_t g, size_t G) {
+    const size_t r = row % kTile;
+    return ((row / kTile) * (G / 2) + (g >> 1)) * 64 + (r & 15) * 4 + (g & 1) * 2 + (r >> 4);
 }
 
 // ---------------------------------------------------------------------------

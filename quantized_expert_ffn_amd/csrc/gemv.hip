@@ -19,10 +19,16 @@
 //   gate/up: per (expert, 32 weight rows): G and U for the expert's tokens,
 //            H = silu(G) * U written straight back as hi/lo + p per 32.
 //   down:    Y = H Wd^T, fp32, rows in permuted order.
-// Weight codes come straight from HBM into operand registers: in the 32-row
-// tiled layout, 16 rows x one group are 512 (int8) or 256 (int4) contiguous
-// bytes, which a wave reads as one load. Activation fragments come from L2;
-// token rows past an expert's count are masked, so they cost no traffic.
+// Weight codes come straight from HBM into operand registers: in the
+// lane-tiled layout one 16-byte load per lane brings a wave the B operands of
+// both 16-row halves of a 32-row tile for one group (int8) or two groups
+// (int4), and one more brings the scales of two groups. Every vector memory
+// instruction costs the CU's address unit about the same time whatever its
+// width, so the kernel issues few, wide ones: per pair of groups and 32-row
+// tile of two matrices, 4 (int8) or 2 (int4) code loads, 2 scale loads and 4
+// activation loads (hi/lo of two groups), the activations serving 64 weight
+// rows. Activation fragments come from L2; token rows past an expert's count
+// read as zeros.
 //
 // Codes to f16 without a conversion instruction: an unsigned byte u ORed
 // into 0x6400 is the f16 number 1024 + u; a packed f16 subtract of 1152
@@ -60,11 +66,12 @@ __device__ __forceinline__ v8h codes_to_f16(uint32_t w0, uint32_t w1) {
     } r;
     v2h off;
     if constexpr (FMT == MOE_W_INT8_G32) {
+        // byte pick: (code byte 0 or 1, 0x64) and (code byte 2 or 3, 0x64)
         const uint32_t a = w0 ^ 0x80808080u, b = w1 ^ 0x80808080u;
-        r.u[0] = and_or(a, 0x00ff00ffu, 0x64006400u);
-        r.u[1] = and_or(a >> 8, 0x00ff00ffu, 0x64006400u);
-        r.u[2] = and_or(b, 0x00ff00ffu, 0x64006400u);
-        r.u[3] = and_or(b >> 8, 0x00ff00ffu, 0x64006400u);
+        r.u[0] = __builtin_amdgcn_perm(a, 0x64646464u, 0x00060004u);
+        r.u[1] = __builtin_amdgcn_perm(a, 0x64646464u, 0x00070005u);
+        r.u[2] = __builtin_amdgcn_perm(b, 0x64646464u, 0x00060004u);
+        r.u[3] = __builtin_amdgcn_perm(b, 0x64646464u, 0x00070005u);
         off = v2h{(_Float16)-1152.0f, (_Float16)-1152.0f};
     } else {
         const uint32_t a = w0 ^ 0x88888888u;
@@ -146,14 +153,14 @@ __global__ __launch_bounds__(256) void prep_act_kernel(const float* __restrict__
                 *reinterpret_cast<v8h*>(alo + off) = lo;
             }
         }
-        if (g_ok && r == 0 && half == 0) apow[(size_t)g * R + row_begin + mt] = ldexpf(1.0f, ex - 15);
+        if (g_ok && r == 0 && half == 0) apow[(size_t)(row_begin + mt) * G + g] = ldexpf(1.0f, ex - 15);
     }
 }
 
 struct GemvArgs {
     const _Float16* ahi;    // activation parts [R, K] in slot order
     const _Float16* alo;
-    const float* apow;      // [K/32, R], at the first row of each 16-row tile
+    const float* apow;      // [R, K/32]: row = first row of a 16-row tile
     const int4* slots;      // (expert, row_begin, n_rows, 0)
     const int* meta;        // meta[0] = number of slots
     const uint8_t* q[2];    // routed codes: gate, up (gate/up) or down, down
@@ -165,26 +172,24 @@ struct GemvArgs {
     // gate/up output: H as parts + powers of two for the down kernel
     _Float16* hhi;
     _Float16* hlo;
-    float* hpow;            // [N/32, R], at the first row of each 16-row tile
+    float* hpow;            // [R, N/32]: row = first row of a 16-row tile
     // down output
     float* y;               // [R, N]
 };
 
-// Operands in flight per wave: NB groups ahead, weight codes (HBM) and
-// activation fragments (L2) alike. Loads retire in order, so a shallower
-// activation ring would make every wait cover the deeper weight loads too.
-__host__ __device__ constexpr int gemv_nb(int fmt, int nmat) { return (fmt == MOE_W_INT8_G32 && nmat == 2) ? 4 : 6; }
+constexpr int kMaxGemvGroups = 256;   // K <= 8192
 
-// Block: 2 x KS waves. Wave (wn, ks): weight rows 32 * tile + 16 wn .. + 16,
-// groups ks, ks + KS, ... of the reduction axis.
-template <int FMT, int NMAT, int KS>
-__global__ __launch_bounds__(128 * KS) void gemv_kernel(const GemvArgs a) {
-    constexpr int kDw = FMT == MOE_W_INT8_G32 ? 2 : 1;      // code dwords per lane per group
-    constexpr int kBpg = FMT == MOE_W_INT8_G32 ? 32 : 16;   // code bytes per row per group
-    constexpr int NB = gemv_nb(FMT, NMAT);
-    constexpr int kNA = NB;
-    __shared__ float red[KS > 1 ? 2 * KS : 1][NMAT][64][4];
-    __shared__ float hmax[2];
+// Block: KS waves splitting the group pairs of the reduction axis (wave ks:
+// pairs ks, ks + KS, ...). Each wave covers two 32-row matrix tiles: gate and
+// up of tile blockIdx.x (GATEUP), or down tiles 2 blockIdx.x and +1. NB pairs
+// of groups are in flight per wave: weight codes (HBM), scales and
+// activation fragments (L2) alike; loads retire in order, so every stream
+// keeps the same depth.
+template <int FMT, bool GATEUP, int NB, int KS>
+__global__ __launch_bounds__(64 * KS) void gemv_kernel(const GemvArgs a) {
+    constexpr int kCL = FMT == MOE_W_INT8_G32 ? 2 : 1;   // 16-byte code loads per tile per pair
+    __shared__ float pwtab[kMaxGemvGroups];
+    __shared__ float red[KS > 1 ? KS - 1 : 1][2][2][4][64];
 
     const int slot = blockIdx.y;
     if (slot >= a.meta[0]) return;
@@ -192,122 +197,158 @@ __global__ __launch_bounds__(128 * KS) void gemv_kernel(const GemvArgs a) {
     const int e = sl.x, row_begin = sl.y, n_rows = sl.z;
     const bool is_shared = e == a.E;
     const int64_t eo = is_shared ? 0 : e;
-    // the wave index is uniform across the wave; say so, so that group offsets
-    // stay in scalar registers
-    const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int wn = wave & 1, ks = wave >> 1;
-    const int K = a.K, N = a.N, G = K / kGroup, R = a.R;
+    const int lane = threadIdx.x & 63, ks = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int h = lane >> 4, nl = lane & 15;
-    const int tile = blockIdx.x;                       // 32-row tile of every matrix
-    const int n = tile * kTile + wn * 16 + nl;         // this lane's weight row (B operand column)
-    // operands through buffer resources: one lane offset per stream, the group
+    const int K = a.K, N = a.N, G = K / kGroup, P = G / 2, R = a.R;
+    const int n_tiles = N / kTile;
+    int tile[2];
+    tile[0] = GATEUP ? blockIdx.x : 2 * blockIdx.x;
+    tile[1] = GATEUP ? blockIdx.x : 2 * blockIdx.x + 1;   // may be n_tiles: reads as zeros, not stored
+
+    // operands through buffer resources: a lane offset per stream, the pair
     // step in a uniform register; offsets past a resource's end read as 0
-    __amdgpu_buffer_rsrc_t rq[NMAT], rs[NMAT];
+    __amdgpu_buffer_rsrc_t rq[2], rs[2];
+    int q_voff[2], s_voff[2];
 #pragma unroll
-    for (int m = 0; m < NMAT; ++m) {
+    for (int t = 0; t < 2; ++t) {
+        const int m = GATEUP ? t : 0;
         const uint8_t* qbase = (is_shared ? a.sq[m] : a.q[m]) + eo * a.q_stride;
         const float* sbase = (is_shared ? a.ss[m] : a.s[m]) + eo * a.s_stride;
-        rq[m] = __builtin_amdgcn_make_buffer_rsrc((void*)qbase, 0, (int)a.q_stride, 0x00020000);
-        rs[m] = __builtin_amdgcn_make_buffer_rsrc((void*)sbase, 0, (int)(a.s_stride * 4), 0x00020000);
+        rq[t] = __builtin_amdgcn_make_buffer_rsrc((void*)qbase, 0, (int)a.q_stride, 0x00020000);
+        rs[t] = __builtin_amdgcn_make_buffer_rsrc((void*)sbase, 0, (int)(a.s_stride * 4), 0x00020000);
+        q_voff[t] = tile[t] * (FMT == MOE_W_INT8_G32 ? G : P) * 1024 + lane * 16;
+        s_voff[t] = (tile[t] * P * 64 + nl * 4) * 4;
     }
-    const int q_voff = tile * G * (kTile * kBpg) + (wn * 16 + nl) * kBpg + (kBpg / 4) * h;
-    const int s_voff = (tile * G * kTile + wn * 16 + nl) * 4;
     const __amdgpu_buffer_rsrc_t rah = __builtin_amdgcn_make_buffer_rsrc((void*)a.ahi, 0, R * K * 2, 0x00020000);
     const __amdgpu_buffer_rsrc_t ral = __builtin_amdgcn_make_buffer_rsrc((void*)a.alo, 0, R * K * 2, 0x00020000);
-    const __amdgpu_buffer_rsrc_t rpw = __builtin_amdgcn_make_buffer_rsrc((void*)a.apow, 0, R * G * 4, 0x00020000);
-    const int n_my = (G - ks + KS - 1) / KS;           // groups of this wave: ks + KS * j
+    const int n_my = (P - ks + KS - 1) / KS;
 
     for (int mt = 0; mt < n_rows; mt += 16) {
         const int rows_here = min(16, n_rows - mt);
-        const bool a_ok = nl < rows_here;
-        // rows past the expert's count read past the resource: zeros, no traffic
-        const int a_voff = a_ok ? ((row_begin + mt + nl) * K + 8 * h) * 2 : 0x7ffffff0;
-        const int pw_off = (row_begin + mt) * 4;      // apow[g][row_begin + mt]: one per group for the tile
-        const int prow = row_begin + mt + 4 * h;        // output rows (tokens) 4h .. 4h + 3 of the tile
+        // rows past the expert's count read past the resource: zeros
+        const int a_voff = nl < rows_here ? ((row_begin + mt + nl) * K + 8 * h) * 2 : 0x7ffffff0;
+        const int prow = row_begin + mt + 4 * h;   // output rows (tokens) 4h .. 4h+3 of the tile
 
-        v4f acc[NMAT];
-#pragma unroll
-        for (int m = 0; m < NMAT; ++m) acc[m] = v4f{0.f, 0.f, 0.f, 0.f};
+        __syncthreads();   // the previous tile's readers of pwtab / red are done
+        for (int i = threadIdx.x; i < G; i += 64 * KS) pwtab[i] = a.apow[(size_t)(row_begin + mt) * G + i];
+        __syncthreads();
 
-        uint32_t wc[NB][NMAT][kDw];
-        float wsc[NB][NMAT];
-        v8h xh[kNA], xl[kNA];
-        float xpw[kNA];
-        auto load_b = [&](int sp, int j) {
-            const int g = ks + KS * (j < n_my ? j : 0);
+        v4f acc[2][2];
 #pragma unroll
-            for (int m = 0; m < NMAT; ++m) {
-                if constexpr (kDw == 2) {
-                    const auto v = __builtin_amdgcn_raw_buffer_load_b64(rq[m], q_voff, g * (kTile * kBpg), 0);
-                    wc[sp][m][0] = v[0];
-                    wc[sp][m][1] = v[1];
-                } else {
-                    wc[sp][m][0] = __builtin_amdgcn_raw_buffer_load_b32(rq[m], q_voff, g * (kTile * kBpg), 0);
-                }
-                wsc[sp][m] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs[m], s_voff, g * kTile * 4, 0));
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+            for (int r = 0; r < 2; ++r) acc[t][r] = v4f{0.f, 0.f, 0.f, 0.f};
+
+        uint4 wq[NB][2][kCL];
+        uint4 wsc[NB][2];
+        v8h xh[NB][2], xl[NB][2];
+        auto load = [&](int sp, int j) {
+            // past the end: the last pair again (L2-resident), so that every
+            // step issues the same loads and waits stay counted
+            const int p = ks + KS * (j < n_my ? j : n_my - 1);
+#pragma unroll
+            for (int t = 0; t < 2; ++t) {
+#pragma unroll
+                for (int c = 0; c < kCL; ++c)
+                    wq[sp][t][c] = __builtin_bit_cast(
+                        uint4, __builtin_amdgcn_raw_buffer_load_b128(rq[t], q_voff[t], (kCL * p + c) * 1024, 0));
+                wsc[sp][t] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rs[t], s_voff[t], p * 256, 0));
+            }
+#pragma unroll
+            for (int gi = 0; gi < 2; ++gi) {
+                xh[sp][gi] = __builtin_bit_cast(v8h, __builtin_amdgcn_raw_buffer_load_b128(rah, a_voff, (2 * p + gi) * 64, 0));
+                xl[sp][gi] = __builtin_bit_cast(v8h, __builtin_amdgcn_raw_buffer_load_b128(ral, a_voff, (2 * p + gi) * 64, 0));
             }
         };
-        auto load_a = [&](int sp, int j) {
-            const int g = ks + KS * (j < n_my ? j : 0);
-            xh[sp] = __builtin_bit_cast(v8h, __builtin_amdgcn_raw_buffer_load_b128(rah, a_voff, g * kGroup * 2, 0));
-            xl[sp] = __builtin_bit_cast(v8h, __builtin_amdgcn_raw_buffer_load_b128(ral, a_voff, g * kGroup * 2, 0));
-            xpw[sp] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rpw, pw_off, g * R * 4, 0));
+        auto step = [&](int jj, int j) {
+            const int p = ks + KS * j;
+            const float pw0 = pwtab[2 * p], pw1 = pwtab[2 * p + 1];
+#pragma unroll
+            for (int gi = 0; gi < 2; ++gi) {
+                const float pw = gi ? pw1 : pw0;
+#pragma unroll
+                for (int t = 0; t < 2; ++t) {
+                    v8h b0, b1;
+                    if constexpr (FMT == MOE_W_INT8_G32) {
+                        const uint4 c = wq[jj][t][gi];
+                        b0 = codes_to_f16<FMT>(c.x, c.y);
+                        b1 = codes_to_f16<FMT>(c.z, c.w);
+                    } else {
+                        const uint4 c = wq[jj][t][0];
+                        b0 = codes_to_f16<FMT>(gi ? c.z : c.x, 0u);
+                        b1 = codes_to_f16<FMT>(gi ? c.w : c.y, 0u);
+                    }
+                    v4f d0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(xh[jj][gi], b0, v4f{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+                    v4f d1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(xh[jj][gi], b1, v4f{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+                    d0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(xl[jj][gi], b0, d0, 0, 0, 0);
+                    d1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(xl[jj][gi], b1, d1, 0, 0, 0);
+                    const uint4 sc = wsc[jj][t];
+                    const float f0 = __builtin_bit_cast(float, gi ? sc.z : sc.x) * pw;
+                    const float f1 = __builtin_bit_cast(float, gi ? sc.w : sc.y) * pw;
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        acc[t][0][i] = fmaf(d0[i], f0, acc[t][0][i]);
+                        acc[t][1][i] = fmaf(d1[i], f1, acc[t][1][i]);
+                    }
+                }
+            }
         };
+        // whole rounds of NB steps: every step computes its ring slot and
+        // refills it NB pairs ahead; then the last n_my % NB steps, no loads
 #pragma unroll
-        for (int j = 0; j < kNA; ++j) load_a(j, j);
-#pragma unroll
-        for (int j = 0; j < NB; ++j) load_b(j, j);
-        for (int j0 = 0; j0 < n_my; j0 += NB) {
+        for (int jj = 0; jj < NB; ++jj) load(jj, jj);
+        int j0 = 0;
+        for (; j0 + NB <= n_my; j0 += NB) {
 #pragma unroll
             for (int jj = 0; jj < NB; ++jj) {
-                const int j = j0 + jj;
-                if (j >= n_my) break;
-                const float pw = xpw[jj % kNA];
-                const v8h ahi = xh[jj % kNA], alo = xl[jj % kNA];
-                load_a(jj % kNA, j + kNA);
-#pragma unroll
-                for (int m = 0; m < NMAT; ++m) {
-                    const v8h b = codes_to_f16<FMT>(wc[jj][m][0], wc[jj][m][kDw - 1]);
-                    v4f d = __builtin_amdgcn_mfma_f32_16x16x32_f16(ahi, b, v4f{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
-                    d = __builtin_amdgcn_mfma_f32_16x16x32_f16(alo, b, d, 0, 0, 0);
-                    const float f = wsc[jj][m] * pw;
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) acc[m][i] = fmaf(d[i], f, acc[m][i]);
-                }
-                load_b(jj, j + NB);
+                step(jj, j0 + jj);
+                // keep the refill here: issued later, its wait would cover
+                // the younger slots' loads too (they retire in order)
+                __builtin_amdgcn_sched_barrier(0);
+                load(jj, j0 + jj + NB);
+                __builtin_amdgcn_sched_barrier(0);
             }
         }
+#pragma unroll
+        for (int jj = 0; jj < NB - 1; ++jj)
+            if (j0 + jj < n_my) step(jj, j0 + jj);
 
-        // reduce the KS partial sums of each output, in slice order
+        // sum the KS partial results of each output in wave order
         if constexpr (KS > 1) {
+            if (ks > 0) {
 #pragma unroll
-            for (int m = 0; m < NMAT; ++m)
+                for (int t = 0; t < 2; ++t)
 #pragma unroll
-                for (int i = 0; i < 4; ++i) red[wave][m][lane][i] = acc[m][i];
+                    for (int r = 0; r < 2; ++r)
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) red[ks - 1][t][r][i][lane] = acc[t][r][i];
+            }
             __syncthreads();
             if (ks == 0) {
 #pragma unroll
-                for (int m = 0; m < NMAT; ++m)
+                for (int w = 0; w < KS - 1; ++w)
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        float s = red[wn][m][lane][i];
+                    for (int t = 0; t < 2; ++t)
 #pragma unroll
-                        for (int k2 = 1; k2 < KS; ++k2) s += red[wn + 2 * k2][m][lane][i];
-                        acc[m][i] = s;
-                    }
+                        for (int r = 0; r < 2; ++r)
+#pragma unroll
+                            for (int i = 0; i < 4; ++i) acc[t][r][i] += red[w][t][r][i][lane];
             }
         }
+        if (ks != 0) continue;
 
-        if constexpr (NMAT == 2) {
-            // H = silu(G) * U for tokens 4h + i and column n. This block holds
-            // the tile's 16 tokens x 32 columns, one group of the down
-            // projection's reduction axis: one power of two for all of it.
-            float hv[4], am = 0.0f;
+        if constexpr (GATEUP) {
+            // H = silu(G) * U for tokens 4h + i and columns nl, 16 + nl of the
+            // tile: 16 tokens x 32 columns, one group of the down projection's
+            // reduction axis, one power of two for all of it
+            float hv[2][4], am = 0.0f;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                hv[i] = (4 * h + i < rows_here) ? silu(acc[0][i]) * acc[1][i] : 0.0f;
-                am = fmaxf(am, fabsf(hv[i]));
-            }
+            for (int r = 0; r < 2; ++r)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    hv[r][i] = (4 * h + i < rows_here) ? silu(acc[0][r][i]) * acc[1][r][i] : 0.0f;
+                    am = fmaxf(am, fabsf(hv[r][i]));
+                }
             am = fmaxf(am, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(am), 0xB1, 0xF, 0xF, true)));
             am = fmaxf(am, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(am), 0x4E, 0xF, 0xF, true)));
             am = fmaxf(am, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(am), 0x141, 0xF, 0xF, true)));
@@ -319,41 +360,45 @@ __global__ __launch_bounds__(128 * KS) void gemv_kernel(const GemvArgs a) {
                 const float r3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(am), 48));
                 am = fmaxf(fmaxf(r0, r1), fmaxf(r2, r3));
             }
-            if (ks == 0 && lane == 0) hmax[wn] = am;
-            __syncthreads();
-            if (ks == 0) {
-                const int ex = pow2_exponent(fmaxf(hmax[0], hmax[1]));
-                const float up = ldexpf(1.0f, 15 - ex);
-                const int kk = wn * 16 + nl;                      // k of column n inside the group
+            const int ex = pow2_exponent(am);
+            const float up = ldexpf(1.0f, 15 - ex);
+#pragma unroll
+            for (int r = 0; r < 2; ++r) {
+                const int kk = 16 * r + nl;                       // k of this column inside the group
                 const int pos = 8 * (kk >> 3) + k_slot(FMT, kk & 7);
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     if (4 * h + i < rows_here) {
-                        const float sv = hv[i] * up;
+                        const float sv = hv[r][i] * up;
                         const _Float16 hh = (_Float16)sv;
-                        const size_t off = (size_t)(prow + i) * N + (size_t)tile * kGroup + pos;
+                        const size_t off = (size_t)(prow + i) * N + (size_t)tile[0] * kGroup + pos;
                         a.hhi[off] = hh;
                         a.hlo[off] = (_Float16)(sv - (float)hh);
                     }
                 }
-                if (wn == 0 && lane == 0) a.hpow[(size_t)tile * R + row_begin + mt] = ldexpf(1.0f, ex - 15);
             }
-            __syncthreads();
+            if (lane == 0) a.hpow[(size_t)(row_begin + mt) * n_tiles + tile[0]] = ldexpf(1.0f, ex - 15);
         } else {
-            if (ks == 0) {
 #pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    if (4 * h + i < rows_here) a.y[(size_t)(prow + i) * N + n] = acc[0][i];
+            for (int t = 0; t < 2; ++t) {
+                if (tile[t] >= n_tiles) continue;
+#pragma unroll
+                for (int r = 0; r < 2; ++r)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        if (4 * h + i < rows_here)
+                            a.y[(size_t)(prow + i) * N + tile[t] * kTile + 16 * r + nl] = acc[t][r][i];
             }
-            if constexpr (KS > 1) __syncthreads();
         }
     }
 }
 
-// K-split per block: enough waves to keep ~16 per CU busy, at least 4 groups per wave
-static int choose_ks(int slots, int tiles, int G) {
+// K-split per block: double it while the grid stays within ~12 waves per CU
+// (what fits at this kernel's register use) and every wave keeps at least two
+// pairs of groups
+static int choose_ks(int slots, int blocks_x, int P) {
     int ks = 1;
-    while (ks < 4 && (long)slots * tiles * 2 * ks < 4096 && G / (2 * ks) >= 4) ks *= 2;
+    while (ks < 8 && (long)slots * blocks_x * 2 * ks <= 3072 && P >= 4 * ks) ks *= 2;
     return ks;
 }
 
@@ -386,10 +431,10 @@ hipError_t launch_gemv(const moe_experts& routed, const moe_experts* shared, boo
     a.K = gateup ? d : I;
     a.N = gateup ? I : d;
     a.R = R;
-    const int G = a.K / kGroup;
-    const int64_t bpg = routed.format == MOE_W_INT8_G32 ? 32 : 16;
-    a.q_stride = (int64_t)a.N * G * bpg;
-    a.s_stride = (int64_t)a.N * G;
+    if (a.K / kGroup > kMaxGemvGroups) return hipErrorInvalidValue;
+    const int64_t codes = routed.format == MOE_W_INT8_G32 ? (int64_t)a.N * a.K : (int64_t)a.N * a.K / 2;
+    a.q_stride = codes;
+    a.s_stride = (int64_t)a.N * (a.K / kGroup);
     const moe_experts& sh = shared ? *shared : routed;
     if (gateup) {
         a.q[0] = (const uint8_t*)routed.gate_q; a.s[0] = routed.gate_s;
@@ -405,17 +450,19 @@ hipError_t launch_gemv(const moe_experts& routed, const moe_experts* shared, boo
     a.hpow = hpow;
     a.y = y;
     const int tiles = a.N / kTile;
-    const int ks = choose_ks(max_slots, tiles, G);
-    const dim3 grid(tiles, max_slots);
-#define MOE_GEMV(FMT, NM, KSV) hipLaunchKernelGGL((gemv_kernel<FMT, NM, KSV>), grid, dim3(128 * KSV), 0, st, a)
-#define MOE_GEMV_KS(FMT, NM)                \
-    if (ks == 1) MOE_GEMV(FMT, NM, 1);      \
-    else if (ks == 2) MOE_GEMV(FMT, NM, 2); \
-    else MOE_GEMV(FMT, NM, 4);
+    const int bx = gateup ? tiles : (tiles + 1) / 2;
+    const int ks = choose_ks(max_slots, bx, a.K / (2 * kGroup));
+    const dim3 grid(bx, max_slots);
+#define MOE_GEMV(FMT, GU, KSV) hipLaunchKernelGGL((gemv_kernel<FMT, GU, 2, KSV>), grid, dim3(64 * KSV), 0, st, a)
+#define MOE_GEMV_KS(FMT, GU)                \
+    if (ks == 1) MOE_GEMV(FMT, GU, 1);      \
+    else if (ks == 2) MOE_GEMV(FMT, GU, 2); \
+    else if (ks == 4) MOE_GEMV(FMT, GU, 4); \
+    else MOE_GEMV(FMT, GU, 8);
     if (routed.format == MOE_W_INT8_G32) {
-        if (gateup) { MOE_GEMV_KS(MOE_W_INT8_G32, 2) } else { MOE_GEMV_KS(MOE_W_INT8_G32, 1) }
+        if (gateup) { MOE_GEMV_KS(MOE_W_INT8_G32, true) } else { MOE_GEMV_KS(MOE_W_INT8_G32, false) }
     } else {
-        if (gateup) { MOE_GEMV_KS(MOE_W_INT4_G32, 2) } else { MOE_GEMV_KS(MOE_W_INT4_G32, 1) }
+        if (gateup) { MOE_GEMV_KS(MOE_W_INT4_G32, true) } else { MOE_GEMV_KS(MOE_W_INT4_G32, false) }
     }
 #undef MOE_GEMV_KS
 #undef MOE_GEMV

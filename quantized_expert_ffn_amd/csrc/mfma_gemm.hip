@@ -123,8 +123,6 @@ __global__ __launch_bounds__(256) void q8_mfma_kernel(const MfmaArgs a) {
             tile = n0 / kTile + bt;
         }
     };
-    constexpr int kBpg = FMT == MOE_W_INT8_G32 ? 32 : 16;   // code bytes per row per group
-
     constexpr int kBLoads = FMT == MOE_W_INT8_G32 ? 4 : 2;
     uint4 ra[2];
     uint4 rb[kBLoads];
@@ -143,32 +141,42 @@ __global__ __launch_bounds__(256) void q8_mfma_kernel(const MfmaArgs a) {
                        : make_uint4(0, 0, 0, 0);
         }
         rsa = (sa_ok && g0 + sa_g < G) ? a.a_s[(size_t)sa_src * G + g0 + sa_g] : 0.0f;
-        // one (tile, group) block of codes is contiguous: a wave reads it whole
+        // a 1 KB block of codes (int8: one tile x group, int4: one tile x
+        // pair of groups) is contiguous: a wave reads it whole
 #pragma unroll
         for (int r = 0; r < kBLoads; ++r) {
             const int li = tid + 256 * r;
-            const int lanes_per_block = FMT == MOE_W_INT8_G32 ? 64 : 32;
-            const int blk = li / lanes_per_block, j = li % lanes_per_block;
-            const int bt = blk >> 2, g = blk & 3;
+            const int blk = li >> 6, j = li & 63;
             const uint8_t* q;
             const float* sp;
             int tile;
-            b_tile(bt, q, sp, tile);
-            const bool ok = tile * kTile < N && g0 + g < G;
-            rb[r] = ok ? *reinterpret_cast<const uint4*>(q + ((size_t)tile * G + g0 + g) * (kTile * kBpg) + j * 16)
-                       : make_uint4(0, 0, 0, 0);
+            if constexpr (FMT == MOE_W_INT8_G32) {
+                const int bt = blk >> 2, g = blk & 3;
+                b_tile(bt, q, sp, tile);
+                const bool ok = tile * kTile < N && g0 + g < G;
+                rb[r] = ok ? *reinterpret_cast<const uint4*>(q + ((size_t)tile * G + g0 + g) * 1024 + j * 16)
+                           : make_uint4(0, 0, 0, 0);
+            } else {
+                const int bt = blk >> 1, pr = g0 / 2 + (blk & 1);
+                b_tile(bt, q, sp, tile);
+                const bool ok = tile * kTile < N && pr < G / 2;
+                rb[r] = ok ? *reinterpret_cast<const uint4*>(q + ((size_t)tile * (G / 2) + pr) * 1024 + j * 16)
+                           : make_uint4(0, 0, 0, 0);
+            }
         }
 #pragma unroll
         for (int r = 0; r < 2; ++r) {
             const int li = tid + 256 * r;
             const int blk = li >> 5, r32 = li & 31;
-            const int bt = blk >> 2, g = blk & 3;
+            const int bt = blk >> 2, g = g0 + (blk & 3);
             const uint8_t* q;
             const float* sp;
             int tile;
             b_tile(bt, q, sp, tile);
-            const bool ok = tile * kTile < N && g0 + g < G;
-            rsb[r] = ok ? sp[((size_t)tile * G + g0 + g) * kTile + r32] * kWScale : 0.0f;
+            const bool ok = tile * kTile < N && g < G;
+            rsb[r] = ok ? sp[((size_t)tile * (G / 2) + g / 2) * 64 + (r32 & 15) * 4 + (g & 1) * 2 + (r32 >> 4)] *
+                              kWScale
+                        : 0.0f;
         }
     };
 
@@ -184,28 +192,31 @@ __global__ __launch_bounds__(256) void q8_mfma_kernel(const MfmaArgs a) {
             *reinterpret_cast<uint4*>(A + (li >> 3) * kLdsRow + (li & 7) * 16) = ra[r];
         }
         SA[sa_row * kGroupsPerStage + sa_g] = rsa;
+        // lane j = nl + 16 h of a block holds k 8h .. 8h+7 of rows nl and 16 + nl
         if constexpr (FMT == MOE_W_INT8_G32) {
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int li = tid + 256 * r;
                 const int blk = li >> 6, j = li & 63;
-                const int brow = (blk >> 2) * kTile + (j >> 1), g = blk & 3, half = j & 1;
-                *reinterpret_cast<uint4*>(B + brow * kLdsRow + g * kGroup + half * 16) = rb[r];
+                const int brow = (blk >> 2) * kTile + (j & 15), g = blk & 3, h = j >> 4;
+                uint8_t* dst = B + brow * kLdsRow + g * kGroup + 8 * h;
+                *reinterpret_cast<uint2*>(dst) = make_uint2(rb[r].x, rb[r].y);
+                *reinterpret_cast<uint2*>(dst + 16 * kLdsRow) = make_uint2(rb[r].z, rb[r].w);
             }
         } else {
 #pragma unroll
             for (int r = 0; r < 2; ++r) {
                 const int li = tid + 256 * r;
-                const int blk = li >> 5, r32 = li & 31;
-                const int brow = (blk >> 2) * kTile + r32, g = blk & 3;
-                uint4 w0, w1;
-                widen_int4x8(rb[r].x, w0.x, w0.y);
-                widen_int4x8(rb[r].y, w0.z, w0.w);
-                widen_int4x8(rb[r].z, w1.x, w1.y);
-                widen_int4x8(rb[r].w, w1.z, w1.w);
-                uint8_t* dst = B + brow * kLdsRow + g * kGroup;
-                *reinterpret_cast<uint4*>(dst) = w0;
-                *reinterpret_cast<uint4*>(dst + 16) = w1;
+                const int blk = li >> 6, j = li & 63;
+                const int brow = (blk >> 1) * kTile + (j & 15), g = 2 * (blk & 1), h = j >> 4;
+                const uint32_t words[4] = {rb[r].x, rb[r].y, rb[r].z, rb[r].w};
+#pragma unroll
+                for (int qd = 0; qd < 4; ++qd) {
+                    uint2 w;
+                    widen_int4x8(words[qd], w.x, w.y);
+                    uint8_t* dst = B + (brow + 16 * (qd & 1)) * kLdsRow + (g + (qd >> 1)) * kGroup + 8 * h;
+                    *reinterpret_cast<uint2*>(dst) = w;
+                }
             }
         }
 #pragma unroll

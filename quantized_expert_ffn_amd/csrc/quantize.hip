@@ -12,7 +12,7 @@
 namespace moe {
 
 // One thread per group of 32 consecutive weights of one row; the codes and the
-// scale are stored in the 32-row tiled layout (common.h).
+// scale go to their places in the lane-ordered tile layout (common.h).
 template <int BITS>
 __global__ __launch_bounds__(256) void quantize_weights_kernel(const float* __restrict__ w,
                                                                int64_t n_groups, int G,
@@ -21,7 +21,7 @@ __global__ __launch_bounds__(256) void quantize_weights_kernel(const float* __re
     const int64_t gi = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (gi >= n_groups) return;
     const float4* src = reinterpret_cast<const float4*>(w + gi * kGroup);
-    const size_t g = tiled_index((size_t)(gi / G), (size_t)(gi % G), (size_t)G);
+    const size_t row = (size_t)(gi / G), g = (size_t)(gi % G);
     float v[kGroup];
 #pragma unroll
     for (int i = 0; i < kGroup / 4; ++i) {
@@ -43,26 +43,24 @@ __global__ __launch_bounds__(256) void quantize_weights_kernel(const float* __re
         r = fminf(fmaxf(r, -qmax), qmax);
         code[i] = (int)r;
     }
-    s[g] = sc;
-    if constexpr (BITS == 8) {
-        uint32_t packed[kGroup / 4];
+    s[scale_index(row, g, (size_t)G)] = sc;
 #pragma unroll
-        for (int i = 0; i < kGroup / 4; ++i)
-            packed[i] = (uint32_t)(code[4 * i] & 0xff) | ((uint32_t)(code[4 * i + 1] & 0xff) << 8) |
-                        ((uint32_t)(code[4 * i + 2] & 0xff) << 16) | ((uint32_t)(code[4 * i + 3] & 0xff) << 24);
-        uint4* dst = reinterpret_cast<uint4*>(q + g * kGroup);
-        dst[0] = make_uint4(packed[0], packed[1], packed[2], packed[3]);
-        dst[1] = make_uint4(packed[4], packed[5], packed[6], packed[7]);
-    } else {
-        uint32_t packed[kGroup / 8];
+    for (int h = 0; h < 4; ++h) {
+        const size_t k8 = 4 * g + h;
+        if constexpr (BITS == 8) {
+            uint32_t lo = 0, hi = 0;
 #pragma unroll
-        for (int i = 0; i < kGroup / 8; ++i) {
+            for (int j = 0; j < 4; ++j) {
+                lo |= (uint32_t)(code[8 * h + j] & 0xff) << (8 * j);
+                hi |= (uint32_t)(code[8 * h + 4 + j] & 0xff) << (8 * j);
+            }
+            *reinterpret_cast<uint2*>(q + int8_code_offset(row, k8, (size_t)G)) = make_uint2(lo, hi);
+        } else {
             uint32_t p = 0;
 #pragma unroll
-            for (int j = 0; j < 8; ++j) p |= (uint32_t)(code[8 * i + j] & 0xf) << (4 * j);
-            packed[i] = p;
+            for (int j = 0; j < 8; ++j) p |= (uint32_t)(code[8 * h + j] & 0xf) << (4 * j);
+            *reinterpret_cast<uint32_t*>(q + int4_code_offset(row, k8, (size_t)G)) = p;
         }
-        *reinterpret_cast<uint4*>(q + g * (kGroup / 2)) = make_uint4(packed[0], packed[1], packed[2], packed[3]);
     }
 }
 

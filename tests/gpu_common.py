@@ -63,16 +63,24 @@ def t2n(t: torch.Tensor) -> np.ndarray:
     return t.detach().cpu().numpy()
 
 
-def untile_codes(tiled: np.ndarray, n_rows: int, bytes_per_group: int) -> np.ndarray:
-    """Library weight codes (32-row tiles, group-major inside a tile:
-    [N/32][G][32][b]) back to row-major [N, G*b]."""
-    flat = np.asarray(tiled).reshape(-1)
-    g = flat.size // (n_rows * bytes_per_group)
-    return flat.reshape(n_rows // 32, g, 32, bytes_per_group).transpose(0, 2, 1, 3).reshape(n_rows, g * bytes_per_group)
+def untile_codes(tiled: np.ndarray, n_rows: int, n_cols: int, fmt: str) -> np.ndarray:
+    """Library weight codes (lane-tiled layout of include/moe.h) back to the
+    row-major storage the oracle keeps: int8 [N, K], or packed int4 [N, K/2]
+    (element 2i in the low nibble of byte i)."""
+    flat = np.asarray(tiled).reshape(-1).view(np.uint8)
+    nt, g = n_rows // 32, n_cols // 32
+    if fmt == "int8":
+        # (tile, group, h, nl, half, byte) -> row = 32 tile + 16 half + nl, k = 32 group + 8 h + byte
+        a = flat.reshape(nt, g, 4, 16, 2, 8).transpose(0, 4, 3, 1, 2, 5)
+        return a.reshape(n_rows, n_cols).view(np.int8)
+    # (tile, pair, h, nl, group of pair, half, byte) -> byte column 16 group + 4 h + byte
+    a = flat.reshape(nt, g // 2, 4, 16, 2, 2, 4).transpose(0, 5, 3, 1, 4, 2, 6)
+    return a.reshape(n_rows, n_cols // 2)
 
 
-def untile_scales(tiled: np.ndarray, n_rows: int) -> np.ndarray:
-    """Library group scales ([N/32][G][32]) back to row-major [N, G]."""
+def untile_scales(tiled: np.ndarray, n_rows: int, n_cols: int) -> np.ndarray:
+    """Library group scales (lane-tiled layout) back to row-major [N, K/32]."""
     flat = np.asarray(tiled).reshape(-1)
-    g = flat.size // n_rows
-    return flat.reshape(n_rows // 32, g, 32).transpose(0, 2, 1).reshape(n_rows, g)
+    nt, g = n_rows // 32, n_cols // 32
+    a = flat.reshape(nt, g // 2, 16, 2, 2).transpose(0, 4, 2, 1, 3)   # (tile, half, nl, pair, group of pair)
+    return a.reshape(n_rows, g)

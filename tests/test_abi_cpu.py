@@ -5,6 +5,7 @@ import ctypes
 import os
 import re
 
+import numpy as np
 import pytest
 
 from conftest import ROOT
@@ -93,6 +94,7 @@ def test_layer_forward_validation(lib):
     assert _fwd(lib, params=_params(n_experts=7)) == INVALID      # router E != experts E
     assert _fwd(lib, params=_params(mode=3)) == INVALID
     assert _fwd(lib, routed=_experts(d_model=65)) == UNSUPPORTED  # d % 32
+    assert _fwd(lib, routed=_experts(d_model=96)) == UNSUPPORTED  # d % 64 (pairs of groups)
     assert _fwd(lib, routed=_experts(d_ff=100)) == UNSUPPORTED    # I % 32
     assert _fwd(lib, routed=_experts(format=9)) == INVALID
     assert _fwd(lib, routed=_experts(up_s=None)) == INVALID
@@ -136,6 +138,7 @@ def test_route_dispatch_combine_validation(lib):
     assert lib.moe_combine(FAKE, FAKE, FAKE, None, 4, 2, 66, FAKE, None) == UNSUPPORTED
     assert lib.moe_combine(None, FAKE, FAKE, None, 4, 2, 64, FAKE, None) == INVALID
     assert lib.moe_quantize_weights(FAKE, 32, 48, 0, FAKE, FAKE, None) == UNSUPPORTED   # cols % 32
+    assert lib.moe_quantize_weights(FAKE, 32, 96, 1, FAKE, FAKE, None) == UNSUPPORTED   # cols % 64
     assert lib.moe_quantize_weights(FAKE, 40, 64, 0, FAKE, FAKE, None) == UNSUPPORTED   # rows % 32 (tiles)
     assert lib.moe_quantize_weights(FAKE, 32, 64, 3, FAKE, FAKE, None) == INVALID
     assert lib.moe_quantize_weights(FAKE, 0, 64, 1, FAKE, FAKE, None) == OK
@@ -156,3 +159,40 @@ def test_accounting_matches_page_figures():
     assert abs(payload / 1e6 - 19) < 0.5
     assert acc.expert_bytes(*glm, "int4") == payload + 3 * glm[0] * glm[1] // 32 * 4
     assert acc.useful_ops([2, 0, 1], 3, 64, 128, False) == 2 * 3 * 3 * 64 * 128
+
+
+@pytest.mark.parametrize("fmt", ["int8", "int4"])
+def test_untile_helpers_invert_the_documented_layout(fmt):
+    """The GPU tests read library weights back through untile_*; check those
+    against the layout formulas of include/moe.h, written out element by element."""
+    from gpu_common import untile_codes, untile_scales
+    rng = np.random.default_rng(3)
+    N, K = 64, 128
+    G, P = K // 32, K // 64
+    codes = rng.integers(-7 if fmt == "int4" else -127, 8 if fmt == "int4" else 128, (N, K))
+    scales = rng.standard_normal((N, G)).astype(np.float32)
+    sflat = np.zeros(N * G, np.float32)
+    if fmt == "int8":
+        qflat = np.zeros(N * K, np.int8)
+    else:
+        qflat = np.zeros(N * K // 8, np.uint32)
+    for row in range(N):
+        t, r = divmod(row, 32)
+        nl, half = r % 16, r // 16
+        for g in range(G):
+            sflat[(t * P + g // 2) * 64 + 4 * nl + 2 * (g % 2) + half] = scales[row, g]
+            for h in range(4):
+                lane = nl + 16 * h
+                ks = range(32 * g + 8 * h, 32 * g + 8 * h + 8)
+                if fmt == "int8":
+                    for k in ks:
+                        qflat[((t * G + g) * 64 + lane) * 16 + 8 * half + k % 8] = codes[row, k]
+                else:
+                    word = 0
+                    for k in ks:
+                        word |= (int(codes[row, k]) & 0xF) << (4 * (k % 8))
+                    qflat[((t * P + g // 2) * 64 + lane) * 4 + 2 * (g % 2) + half] = word
+    from oracle import quant as oquant
+    stored = codes.astype(np.int8) if fmt == "int8" else oquant.pack_int4(codes.astype(np.int8))
+    assert np.array_equal(untile_codes(qflat, N, K, fmt), stored)
+    assert np.array_equal(untile_scales(sflat, N, K), scales)

@@ -32,7 +32,7 @@ MARGIN_EPS = 1e-5      # logits closer than this may rank differently in fp32 vs
 def test_quantize_weights_bit_exact(fmt):
     need_gpu()
     rng = np.random.default_rng(21)
-    w = (rng.standard_normal((64, 96)) * rng.uniform(1e-4, 3, (64, 1))).astype(np.float32)
+    w = (rng.standard_normal((64, 192)) * rng.uniform(1e-4, 3, (64, 1))).astype(np.float32)
     w[3, 32:64] = 0.0
     w[4, :32] = 1e-30
     bits = 8 if fmt == "int8" else 4
@@ -42,8 +42,8 @@ def test_quantize_weights_bit_exact(fmt):
     s = torch.empty(s_ref.shape, dtype=torch.float32, device="cuda")
     qe.moe_quantize_weights(torch.from_numpy(w).cuda(), qe.FORMATS[fmt], q, s)
     torch.cuda.synchronize()
-    assert np.array_equal(untile_scales(t2n(s), 64), s_ref)
-    assert np.array_equal(untile_codes(t2n(q), 64, 32 if bits == 8 else 16), stored)
+    assert np.array_equal(untile_scales(t2n(s), 64, 192), s_ref)
+    assert np.array_equal(untile_codes(t2n(q), 64, 192, fmt), stored)
 
 
 def test_quantize_q8_0_bit_exact(golden_dir):
@@ -232,7 +232,7 @@ TINY_VARIANTS = {
     "tiny_int4": dict(wformat="int4"),
     "tiny_e1k1": dict(n_experts=1, top_k=1, renormalize=True),
     "tiny_kE": dict(top_k=8, renormalize=False),
-    "tiny_wide": dict(d_model=96, d_ff=160, n_experts=6, top_k=3),
+    "tiny_wide": dict(d_model=192, d_ff=320, n_experts=6, top_k=3),
 }
 
 
@@ -381,11 +381,13 @@ def test_layer_full_size(wname):
     assert_close_rel(got[rows], ref["out"], what=f"{wname} out")
     # the same weights, byte for byte, on both sides (a few experts)
     used = np.unique(ref["idx"])[:3]
-    bpg = 32 if shape.wformat == "int8" else 16
     for e in used:
         ox = oracle_expert(shape.name, int(e))
-        assert np.array_equal(untile_codes(t2n(dl.routed[0].gate_q[e]), shape.d_ff, bpg), ox.stored("gate"))
-        assert np.array_equal(untile_scales(t2n(dl.routed[0].down_s[e]), shape.d_model), ox.down_s)
+        assert np.array_equal(untile_codes(t2n(dl.routed[0].gate_q[e]), shape.d_ff, shape.d_model, shape.wformat),
+                              ox.stored("gate"))
+        assert np.array_equal(untile_codes(t2n(dl.routed[0].down_q[e]), shape.d_model, shape.d_ff, shape.wformat),
+                              ox.stored("down"))
+        assert np.array_equal(untile_scales(t2n(dl.routed[0].down_s[e]), shape.d_model, shape.d_ff), ox.down_s)
 
 
 @pytest.mark.parametrize("act_mode", ["f32", "q8_0"])
