@@ -47,14 +47,6 @@ def parse():
     return ap.parse_args()
 
 
-def source_digest(paths):
-    import hashlib
-    h = hashlib.sha256()
-    for p in paths:
-        h.update(open(p, "rb").read())
-    return h.hexdigest()[:16]
-
-
 def measured_traffic(kernel_key: str, sources):
     """HBM bytes per launch from committed rocprofv3 counter runs, if they were
     taken on the current kernel source; else None."""
@@ -62,6 +54,7 @@ def measured_traffic(kernel_key: str, sources):
         rec = json.load(open(TRAFFIC_FILE)).get(kernel_key)
     except (OSError, ValueError):
         return None
+    from quantized_expert_ffn_amd.profiling import source_digest
     if not rec or rec.get("source_digest") != source_digest(sources):
         return None
     return rec.get("bytes_per_launch")
@@ -144,15 +137,12 @@ def main():
     out = torch.empty((T, shape.d_model), dtype=torch.float32, device=dev)
     ws = qe.workspace(T, shape.top_k, shape.n_experts, shape.d_model, shape.d_ff, act, shape.shared_expert, dev)
     stream = torch.cuda.current_stream(dev)
-    G = qe.STAGES.index("gateup")
 
-    def step(i, ev_pair=None):
+    def step(i, evs=None):
         c = i % copies
-        if ev_pair is None:
+        if evs is None:
             qe.moe_layer_forward(x, layer.gate_w, layer.params, layer.routed[c], layer.shared[c], act, out, ws)
         else:
-            evs = [None] * (2 * qe.MOE_STAGE_COUNT)
-            evs[2 * G], evs[2 * G + 1] = ev_pair
             qe.moe_layer_forward_timed(x, layer.gate_w, layer.params, layer.routed[c], layer.shared[c], act, out,
                                        ws, evs)
 
@@ -161,17 +151,29 @@ def main():
     torch.cuda.synchronize(dev)
     print(f"[bench] warmup done ({args.warmup} steps)", file=sys.stderr, flush=True)
 
-    # (1) eager steps with HIP events around the gate/up kernel on the launch stream
-    pairs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    # (1) eager steps with HIP events on the launch stream: the gate/up and
+    # down kernels carry theirs on the dispatch itself, the other stages are
+    # bracketed by event records
+    stage_evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2 * qe.MOE_STAGE_COUNT)]
+                 for _ in range(args.steps)]
     torch.cuda.synchronize(dev)
     t0 = time.perf_counter()
     for i in range(args.steps):
-        step(args.warmup + i, pairs[i])
+        step(args.warmup + i, stage_evs[i])
     torch.cuda.synchronize(dev)
     eager_elapsed = time.perf_counter() - t0
-    kernel_ms = float(np.mean([a.elapsed_time(b) for a, b in pairs]))
-    print(f"[bench] eager {args.steps} steps: {eager_elapsed * 1e6 / args.steps:.1f} us/step, gate/up kernel "
-          f"{kernel_ms * 1e3:.1f} us", file=sys.stderr, flush=True)
+    stage_us = {}
+    for si, name in enumerate(qe.STAGES):
+        if name == "quant_x" and wl.act_mode == "f32":
+            name = "split_x"
+        if stage_evs[0][2 * si].query() and stage_evs[0][2 * si + 1].query():
+            try:
+                stage_us[name] = round(float(np.mean([e[2 * si].elapsed_time(e[2 * si + 1]) for e in stage_evs])) * 1e3, 2)
+            except RuntimeError:
+                pass
+    kernel_ms = stage_us["gateup"] * 1e-3
+    print(f"[bench] eager {args.steps} steps: {eager_elapsed * 1e6 / args.steps:.1f} us/step, stages (us) "
+          f"{stage_us}", file=sys.stderr, flush=True)
 
     # (2) the same step captured once per weight copy in a HIP graph and replayed
     elapsed = eager_elapsed
@@ -238,7 +240,8 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32 activations x int8 weights" if wl.act_mode == "f32" else "int8 x int8 -> int32, fp32 scales",
+        "dtype": (f"f32 (activations f32 as exact f16 pairs, {fmt} weights, f32 accumulate)" if wl.act_mode == "f32"
+                  else "i8 (int8 x int8 -> int32 group dots, f32 scales)"),
         "data": "synthetic (seeded N(0,1) activations, N(0,0.02) weights quantised on the GPU)",
         "config": {"workload": wl.name, "tokens": T, "d_model": d, "n_experts": shape.n_experts, "d_ff": I,
                    "top_k": shape.top_k, "router": shape.router, "weights": f"{fmt} group 32",
@@ -247,7 +250,9 @@ def main():
         "roofline": roof,
         "timing": {"launch": "eager" if args.no_graph else "hip_graph",
                    "eager_ms_per_step": round(eager_elapsed * 1e3 / args.steps, 5),
-                   "kernel_timing": "HIP events around the gate/up kernel in the eager steps"},
+                   "kernel_timing": "HIP events attached to the gate/up kernel dispatch (hipExtLaunchKernel), "
+                                    "mean over the eager steps",
+                   "eager_stage_us": stage_us},
     }
     if not args.no_cpu_baseline:
         print("[bench] oracle CPU baseline", file=sys.stderr, flush=True)

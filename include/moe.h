@@ -6,7 +6,7 @@
  *   - "I ran a 7B Mixture-of-Experts LLM in a language I built" (dev.to),
  *     section "Mixture-of-Experts": each token runs only its top-k experts
  *     (OLMoE: top 8 of 64 per layer), chosen by a softmax router.
- *   - "Show HN: colibri - GLM-5.2 on a slow computer" (note.crab.center),
+ *   - "Show HN: Getting GLM-5.2 running on my slow computer" (note.crab.center),
  *     section "What's implemented": a DeepSeek-V3-style sigmoid router
  *     (noaux_tc, routed_scaling_factor) and a shared expert; int8 / packed
  *     int4 weights dequantised on use; Q8_0-style int8 activations with
@@ -156,7 +156,7 @@ size_t moe_workspace_size(int32_t T, int32_t k, int32_t E, int32_t d, int32_t d_
                           int32_t act_mode, int32_t has_shared);
 
 /* Group-32 symmetric weight quantiser ("mtlm-7m-base", section "Files";
- * "Show HN: colibri", section "What's implemented": int8 / packed int4).
+ * "Show HN: Getting GLM-5.2 running on my slow computer", section "What's implemented": int8 / packed int4).
  *   w      device fp32 [rows, cols] row-major, rows % 32 == 0, cols % 64 == 0
  *          (a stack of matrices of the same cols, each with rows % 32 == 0,
  *          may be passed as one call)
@@ -171,7 +171,7 @@ size_t moe_workspace_size(int32_t T, int32_t k, int32_t E, int32_t d, int32_t d_
 moe_status moe_quantize_weights(const float* w, int64_t rows, int32_t cols, int32_t format,
                                 void* q, float* s, hipStream_t stream);
 
-/* Q8_0-style activation quantiser ("Show HN: colibri", section "What's
+/* Q8_0-style activation quantiser ("Show HN: Getting GLM-5.2 running on my slow computer", section "What's
  * implemented": Q8_0-style int8 activations).
  *   x [rows, cols] device fp32, cols % 32 == 0 -> q int8 [rows, cols],
  *   d fp32 [rows, cols/32]. Per group, in fp32: d = amax/127,
@@ -181,7 +181,7 @@ moe_status moe_quantize_q8_0(const float* x, int64_t rows, int32_t cols,
                              int8_t* q, float* d, hipStream_t stream);
 
 /* Router ("I ran a 7B Mixture-of-Experts LLM...", section
- * "Mixture-of-Experts": softmax top-k; "Show HN: colibri", section "What's
+ * "Mixture-of-Experts": softmax top-k; "Show HN: Getting GLM-5.2 running on my slow computer", section "What's
  * implemented": sigmoid noaux_tc with routed_scaling_factor).
  *   x        device fp32 [T, d];  gate_w device fp32 [E, d]
  *   topk_idx device int32 [T, k]: selected experts, larger selection key
@@ -196,7 +196,7 @@ moe_status moe_route(const float* x, int32_t T, int32_t d, const float* gate_w,
                      const moe_router_params* p, int32_t* topk_idx, float* topk_w,
                      void* ws, size_t ws_bytes, hipStream_t stream);
 
-/* Dispatch for batch-union ("Show HN: colibri", section "What's
+/* Dispatch for batch-union ("Show HN: Getting GLM-5.2 running on my slow computer", section "What's
  * implemented": each distinct expert is read once for all of its positions).
  *   topk_idx device int32 [T, k], values in [0, E).
  *   counts   device int32 [E]      assignments per expert
@@ -242,7 +242,7 @@ moe_status moe_combine(const float* y_perm, const float* topk_w, const int32_t* 
  *   x      device fp32 [T, d];  gate_w device fp32 [E, d]
  *   routed E routed experts; shared NULL or one expert (n_experts == 1) of
  *          the same d, format and d_ff, applied to every token with weight 1
- *          ("Show HN: colibri": shared expert).
+ *          ("Show HN: Getting GLM-5.2 running on my slow computer": shared expert).
  *   out    device fp32 [T, d]
  *   ws     device workspace of moe_workspace_size(T, k, E, d, d_ff,
  *          act_mode, shared != NULL) bytes.
@@ -256,6 +256,10 @@ moe_status moe_layer_forward(const float* x, int32_t T, const float* gate_w,
  * stage_events[2*s+1] after stage s (moe_stage) on `stream`. stage_events
  * is a host array of 2*MOE_STAGE_COUNT hipEvent_t created by the caller;
  * NULL entries are skipped. Stages that do not run are not recorded.
+ * The gate/up and down stages are one kernel each: their two events (both
+ * must be given) are attached to that kernel's dispatch (hipExtLaunchKernel),
+ * so the interval is the kernel's own execution time. The other stages are
+ * bracketed by event records.
  */
 moe_status moe_layer_forward_timed(const float* x, int32_t T, const float* gate_w,
                                    const moe_router_params* p, const moe_experts* routed,

@@ -17,7 +17,7 @@ Sources (the pages; cited by title and section):
   * "mtlm-7m-base" (huggingface.co), sections "Files" (int8 export with group
     size 32; max abs quantisation error 1.7e-3) and "What is and is not machin"
     (SwiGLU, SiLU; a float64 numpy oracle).
-  * "Show HN: colibri - GLM-5.2 on a slow computer" (note.crab.center), section
+  * "Show HN: Getting GLM-5.2 running on my slow computer" (note.crab.center), section
     "What's implemented": DeepSeek-V3-style sigmoid router (noaux_tc,
     routed_scaling_factor), shared expert, Q8_0-style int8 activations with
     integer dots, int8 / packed int4 weights dequantised on use, batch-union

@@ -2,7 +2,7 @@
 
 TEST INFRASTRUCTURE ONLY (see the package docstring).
 
-Batch-union ("Show HN: colibri", section "What's implemented"): in prefill and
+Batch-union ("Show HN: Getting GLM-5.2 running on my slow computer", section "What's implemented"): in prefill and
 verification each distinct expert of the batch is read once and applied to
 every position routed to it. That needs the positions grouped by expert.
 

@@ -3,7 +3,7 @@
 TEST INFRASTRUCTURE ONLY (see the package docstring).
 
 An expert is a SwiGLU FFN ("mtlm-7m-base": SwiGLU blocks, SiLU) whose three
-matrices are stored group-32 quantised ("Show HN: colibri", section "What's
+matrices are stored group-32 quantised ("Show HN: Getting GLM-5.2 running on my slow computer", section "What's
 implemented": int8 / packed int4, dequantised on use):
     gate, up: [I, d]    down: [d, I]
     G = X gate^T,  U = X up^T,  H = silu(G) * U,  Y = H down^T

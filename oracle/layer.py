@@ -3,12 +3,12 @@
 TEST INFRASTRUCTURE ONLY (see the package docstring).
 
 route -> dispatch -> each distinct expert applied once to all of its rows
-(batch-union; "Show HN: colibri", section "What's implemented") -> combine:
+(batch-union; "Show HN: Getting GLM-5.2 running on my slow computer", section "What's implemented") -> combine:
 
     out[t] = sum_j w[t, j] * Y[inv_perm[t*k + j]]  +  S[t]
 
 where Y holds the un-weighted expert outputs in permuted order and S is the
-shared expert ("Show HN: colibri": shared expert), an FFN of the same format
+shared expert ("Show HN: Getting GLM-5.2 running on my slow computer": shared expert), an FFN of the same format
 applied to every token with weight 1 (no gate on the shared expert: the pages
 name none).
 """

@@ -3,7 +3,7 @@
 TEST INFRASTRUCTURE ONLY (see the package docstring).
 
 Weights ("mtlm-7m-base", section "Files": int8 export with group size 32;
-"Show HN: colibri", section "What's implemented": int8 / packed int4
+"Show HN: Getting GLM-5.2 running on my slow computer", section "What's implemented": int8 / packed int4
 quantisation, dequantised on use). Each row of a matrix is cut into groups of
 32 consecutive elements along its input (reduction) axis; a group keeps one
 fp32 scale s and signed integer codes q with s*q approximating the weights:
@@ -22,7 +22,7 @@ Packed int4 ("two nibbles per byte", symmetric): element 2i sits in the low
 nibble of byte i and element 2i+1 in the high nibble, each as a 4-bit two's
 complement number.
 
-Activations ("Show HN: colibri", section "What's implemented": Q8_0-style int8
+Activations ("Show HN: Getting GLM-5.2 running on my slow computer", section "What's implemented": Q8_0-style int8
 activations). Each row is cut into groups of 32; a group keeps an fp32 scale d
 and int8 codes, all steps in fp32:
 

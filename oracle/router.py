@@ -9,7 +9,7 @@ softmax is monotone, so ranking logits ranks probabilities). A selected
 expert's weight is its softmax probability p = exp(L - max) / sum exp(L - max),
 divided by the sum of the selected probabilities when renormalising.
 
-Sigmoid noaux_tc ("Show HN: colibri", section "What's implemented": a
+Sigmoid noaux_tc ("Show HN: Getting GLM-5.2 running on my slow computer", section "What's implemented": a
 DeepSeek-V3-style sigmoid router with noaux_tc and routed_scaling_factor). The
 page names the router only; its steps are the DeepSeek-V3 ones:
     s = sigmoid(L);  c = s + b          (b: score-correction bias, selection only)

@@ -7,7 +7,7 @@ multiply-adds (2 ops each) of the expert matmuls, padding excluded.
 
 The pages give the same accounting for their GLM-5.2 layer: a routed expert is
 about 19 MB of int4 payload and a cold token reads about 11.4 GB of experts
-over 75 layers of 8 experts ("Show HN: colibri", sections "The idea" and "Got
+over 75 layers of 8 experts ("Show HN: Getting GLM-5.2 running on my slow computer", sections "The idea" and "Got
 a better machine?"). Group-32 fp32 scales add 4 bytes per 32 weights on top of
 that payload.
 """

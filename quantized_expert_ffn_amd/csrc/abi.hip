@@ -1,7 +1,7 @@
 // The C ABI of libmoe (declared in include/moe.h): argument validation,
 // workspace carving and kernel sequencing. Every check runs on the host
 // before anything is enqueued, so a rejected call leaves the stream untouched
-// ("Show HN: colibri", section "OpenAI-compatible API": unsupported requests
+// ("Show HN: Getting GLM-5.2 running on my slow computer", section "OpenAI-compatible API": unsupported requests
 // return an explicit error rather than being ignored; section "Experimental
 // resident CUDA backend": a request that cannot run fails instead of silently
 // falling back).
@@ -120,6 +120,8 @@ void record(const hipEvent_t* ev, int idx, hipStream_t st) {
     if (ev && ev[idx]) (void)hipEventRecord(ev[idx], st);
 }
 
+hipEvent_t stage_ev(const hipEvent_t* ev, int idx) { return ev ? ev[idx] : nullptr; }
+
 // The expert FFN over a prepared work list (slots / tiles / row_token in ws).
 moe_status run_experts(const float* x, int T, int k, const moe_experts& routed, const moe_experts* shared,
                        int act_mode, const moe::WsLayout& L, void* ws, float* y, int32_t* dots_gate,
@@ -146,16 +148,12 @@ moe_status run_experts(const float* x, int T, int k, const moe_experts& routed, 
         MOE_HIP(moe::launch_prep_act(fmt, x, row_token, slots, meta, max_slots, R, d, ahi, alo, apow, st),
                 "activation split");
         record(ev, 2 * MOE_STAGE_QUANT_X + 1, st);
-        record(ev, 2 * MOE_STAGE_GATEUP, st);
         MOE_HIP(moe::launch_gemv(routed, shared, true, ahi, alo, apow, R, slots, meta, max_slots, hhi, hlo, hpow,
-                                 nullptr, st),
+                                 nullptr, st, stage_ev(ev, 2 * MOE_STAGE_GATEUP), stage_ev(ev, 2 * MOE_STAGE_GATEUP + 1)),
                 "gate/up GEMV");
-        record(ev, 2 * MOE_STAGE_GATEUP + 1, st);
-        record(ev, 2 * MOE_STAGE_DOWN, st);
         MOE_HIP(moe::launch_gemv(routed, shared, false, hhi, hlo, hpow, R, slots, meta, max_slots, nullptr, nullptr,
-                                 nullptr, y, st),
+                                 nullptr, y, st, stage_ev(ev, 2 * MOE_STAGE_DOWN), stage_ev(ev, 2 * MOE_STAGE_DOWN + 1)),
                 "down GEMV");
-        record(ev, 2 * MOE_STAGE_DOWN + 1, st);
         return MOE_OK;
     }
     int8_t* xq = ws_at<int8_t>(ws, L.xq);
@@ -165,16 +163,14 @@ moe_status run_experts(const float* x, int T, int k, const moe_experts& routed, 
     record(ev, 2 * MOE_STAGE_QUANT_X, st);
     MOE_HIP(moe::launch_quantize_q8_0(x, T, d, xq, xd, st), "Q8_0 of x");
     record(ev, 2 * MOE_STAGE_QUANT_X + 1, st);
-    record(ev, 2 * MOE_STAGE_GATEUP, st);
     MOE_HIP(moe::launch_q8_mfma(routed, shared, true, xq, xd, row_token, tiles, meta, L.max_tiles, hq, hd, nullptr,
-                                dots_gate, dots_up, st),
+                                dots_gate, dots_up, st, stage_ev(ev, 2 * MOE_STAGE_GATEUP),
+                                stage_ev(ev, 2 * MOE_STAGE_GATEUP + 1)),
             "gate/up int8 MFMA");
-    record(ev, 2 * MOE_STAGE_GATEUP + 1, st);
-    record(ev, 2 * MOE_STAGE_DOWN, st);
     MOE_HIP(moe::launch_q8_mfma(routed, shared, false, hq, hd, nullptr, tiles, meta, L.max_tiles, nullptr, nullptr, y,
-                                dots_down, nullptr, st),
+                                dots_down, nullptr, st, stage_ev(ev, 2 * MOE_STAGE_DOWN),
+                                stage_ev(ev, 2 * MOE_STAGE_DOWN + 1)),
             "down int8 MFMA");
-    record(ev, 2 * MOE_STAGE_DOWN + 1, st);
     return MOE_OK;
 }
 

@@ -1,7 +1,7 @@
 // Combine: out[t] = sum_j w[t, j] * Y[inv_perm[t*k + j]] + S[t].
 //
 // The weighted sum of a token's k expert outputs plus the shared expert
-// ("Show HN: colibri", section "What's implemented": shared expert). Each
+// ("Show HN: Getting GLM-5.2 running on my slow computer", section "What's implemented": shared expert). Each
 // token gathers its own k rows in slot order, so no two threads ever add into
 // the same output and the result does not depend on scheduling (no atomics).
 #include "common.h"

@@ -1,6 +1,7 @@
 // Internal helpers shared by the libmoe HIP kernels (gfx950, wave64).
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -129,6 +130,17 @@ __host__ __device__ __forceinline__ size_t int4_code_offset(size_t row, size_t k
 __host__ __device__ __forceinline__ size_t scale_index(size_t row, size_t g, size_t G) {
     const size_t r = row % kTile;
     return ((row / kTile) * (G / 2) + (g >> 1)) * 64 + (r & 15) * 4 + (g & 1) * 2 + (r >> 4);
+}
+
+// Launch on `st`; with events, they are attached to the dispatch itself, so
+// their interval is the kernel's own execution (no separate marker packets).
+template <typename K, typename... Args>
+inline void launch_timed(K kernel, dim3 grid, dim3 block, hipStream_t st, hipEvent_t ev0, hipEvent_t ev1,
+                         Args... args) {
+    if (ev0 && ev1)
+        hipExtLaunchKernelGGL(kernel, grid, block, 0, st, ev0, ev1, 0, args...);
+    else
+        hipLaunchKernelGGL(kernel, grid, block, 0, st, args...);
 }
 
 // ---------------------------------------------------------------------------

@@ -1,4 +1,4 @@
-// Dispatch for batch-union MoE ("Show HN: colibri", section "What's
+// Dispatch for batch-union MoE ("Show HN: Getting GLM-5.2 running on my slow computer", section "What's
 // implemented": in prefill and verification each distinct expert is read once
 // and applied to every position routed to it).
 //

@@ -1,5 +1,5 @@
 // Decode path (fp32 activations): batch-union grouped GEMV on the f16 matrix
-// cores, weights dequantised on use ("Show HN: colibri", section "What's
+// cores, weights dequantised on use ("Show HN: Getting GLM-5.2 running on my slow computer", section "What's
 // implemented": int8 / packed int4 weights dequantised on use; batch-union
 // over the positions routed to one expert; a single row stays in f32).
 //
@@ -418,7 +418,8 @@ hipError_t launch_prep_act(int fmt, const float* x, const int* row_token, const 
 
 hipError_t launch_gemv(const moe_experts& routed, const moe_experts* shared, bool gateup, const _Float16* ahi,
                        const _Float16* alo, const float* apow, int R, const int* slots, const int* meta, int max_slots,
-                       _Float16* hhi, _Float16* hlo, float* hpow, float* y, hipStream_t st) {
+                       _Float16* hhi, _Float16* hlo, float* hpow, float* y, hipStream_t st, hipEvent_t ev0,
+                       hipEvent_t ev1) {
     if (max_slots == 0) return hipSuccess;
     GemvArgs a{};
     a.ahi = ahi;
@@ -453,7 +454,7 @@ hipError_t launch_gemv(const moe_experts& routed, const moe_experts* shared, boo
     const int bx = gateup ? tiles : (tiles + 1) / 2;
     const int ks = choose_ks(max_slots, bx, a.K / (2 * kGroup));
     const dim3 grid(bx, max_slots);
-#define MOE_GEMV(FMT, GU, KSV) hipLaunchKernelGGL((gemv_kernel<FMT, GU, 2, KSV>), grid, dim3(64 * KSV), 0, st, a)
+#define MOE_GEMV(FMT, GU, KSV) launch_timed(gemv_kernel<FMT, GU, 2, KSV>, grid, dim3(64 * KSV), st, ev0, ev1, a)
 #define MOE_GEMV_KS(FMT, GU)                \
     if (ks == 1) MOE_GEMV(FMT, GU, 1);      \
     else if (ks == 2) MOE_GEMV(FMT, GU, 2); \

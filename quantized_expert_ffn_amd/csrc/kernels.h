@@ -28,11 +28,13 @@ hipError_t launch_prep_act(int fmt, const float* x, const int* row_token, const 
                            int max_slots, int R, int K, _Float16* ahi, _Float16* alo, float* apow, hipStream_t st);
 hipError_t launch_gemv(const moe_experts& routed, const moe_experts* shared, bool gateup, const _Float16* ahi,
                        const _Float16* alo, const float* apow, int R, const int* slots, const int* meta, int max_slots,
-                       _Float16* hhi, _Float16* hlo, float* hpow, float* y, hipStream_t st);
+                       _Float16* hhi, _Float16* hlo, float* hpow, float* y, hipStream_t st,
+                       hipEvent_t ev_start = nullptr, hipEvent_t ev_stop = nullptr);
 
 hipError_t launch_q8_mfma(const moe_experts& routed, const moe_experts* shared, bool gateup, const int8_t* a_q,
                           const float* a_s, const int* row_token, const int* tiles, const int* meta, int max_tiles,
-                          int8_t* hq, float* hd, float* y, int32_t* dbg0, int32_t* dbg1, hipStream_t st);
+                          int8_t* hq, float* hd, float* y, int32_t* dbg0, int32_t* dbg1, hipStream_t st,
+                          hipEvent_t ev_start = nullptr, hipEvent_t ev_stop = nullptr);
 
 hipError_t launch_combine(const float* y, const float* w, const int* inv_perm, const float* shared_y, int T, int k,
                           int d, float* out, hipStream_t st);

@@ -1,5 +1,5 @@
 // Prefill / verification path: batch-union grouped GEMM on the int8 matrix
-// cores ("Show HN: colibri", section "What's implemented": integer-dot
+// cores ("Show HN: Getting GLM-5.2 running on my slow computer", section "What's implemented": integer-dot
 // kernels with Q8_0-style int8 activations, used in batch; batch-union MoE in
 // prefill and MTP verification).
 //
@@ -326,7 +326,8 @@ __global__ __launch_bounds__(256) void q8_mfma_kernel(const MfmaArgs a) {
 
 hipError_t launch_q8_mfma(const moe_experts& routed, const moe_experts* shared, bool gateup, const int8_t* a_q,
                           const float* a_s, const int* row_token, const int* tiles, const int* meta, int max_tiles,
-                          int8_t* hq, float* hd, float* y, int32_t* dbg0, int32_t* dbg1, hipStream_t st) {
+                          int8_t* hq, float* hd, float* y, int32_t* dbg0, int32_t* dbg1, hipStream_t st,
+                          hipEvent_t ev0, hipEvent_t ev1) {
     if (max_tiles == 0) return hipSuccess;
     MfmaArgs a{};
     a.a_q = a_q;
@@ -359,7 +360,7 @@ hipError_t launch_q8_mfma(const moe_experts& routed, const moe_experts* shared, 
     const int bn = gateup ? kBRows / 2 : kBRows;
     const dim3 grid((a.N + bn - 1) / bn, max_tiles);
     const bool dbg = dbg0 != nullptr;
-#define MOE_Q8(FMT, GU, DB) hipLaunchKernelGGL((q8_mfma_kernel<FMT, GU, DB>), grid, dim3(256), 0, st, a)
+#define MOE_Q8(FMT, GU, DB) launch_timed(q8_mfma_kernel<FMT, GU, DB>, grid, dim3(256), st, ev0, ev1, a)
     if (routed.format == MOE_W_INT8_G32) {
         if (gateup) { if (dbg) MOE_Q8(MOE_W_INT8_G32, true, true); else MOE_Q8(MOE_W_INT8_G32, true, false); }
         else { if (dbg) MOE_Q8(MOE_W_INT8_G32, false, true); else MOE_Q8(MOE_W_INT8_G32, false, false); }

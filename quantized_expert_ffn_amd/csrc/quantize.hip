@@ -1,7 +1,7 @@
 // Group-32 quantisers: weights (int8 / packed int4) and Q8_0 activations.
 //
 // Weights: "mtlm-7m-base" (huggingface.co), section "Files" (int8, group size
-// 32) and "Show HN: colibri", section "What's implemented" (int8 / packed
+// 32) and "Show HN: Getting GLM-5.2 running on my slow computer", section "What's implemented" (int8 / packed
 // int4 quantisation kernels). Activations: the same section's Q8_0-style int8
 // activations. Codes are decided in fp32 with IEEE division and
 // round-half-to-even, so a host implementation using the same fp32 steps

@@ -2,7 +2,7 @@
 //
 // Softmax top-k: "I ran a 7B Mixture-of-Experts LLM in a language I built"
 // (dev.to), section "Mixture-of-Experts" (OLMoE routes each token to its top 8
-// of 64 experts). Sigmoid noaux_tc: "Show HN: colibri", section "What's
+// of 64 experts). Sigmoid noaux_tc: "Show HN: Getting GLM-5.2 running on my slow computer", section "What's
 // implemented" (DeepSeek-V3-style sigmoid router, noaux_tc,
 // routed_scaling_factor); its steps are the DeepSeek-V3 ones: sigmoid scores,
 // selection on score + bias, groups ranked by the sum of their two best

@@ -13,7 +13,7 @@ Shapes follow the layers the pages run:
   * OLMoE-1B-7B, top-8 of 64 experts per layer (dev.to, "I ran a 7B
     Mixture-of-Experts LLM...", section "Mixture-of-Experts");
   * GLM-5.2 with a DeepSeek-V3-style sigmoid router and a shared expert
-    (note.crab.center, "Show HN: colibri", section "What's implemented");
+    (note.crab.center, "Show HN: Getting GLM-5.2 running on my slow computer", section "What's implemented");
   * a 512-expert Qwen-Next-class model (scholarbro.com, "FLE: Fast Local
     Experts", abstract).
 The pages run trained checkpoints on real prompts; none is available here, so

@@ -94,7 +94,7 @@ def test_int4_pack_matches_hand_worked_bytes(golden_dir):
 
 
 def test_int4_unpack_equals_int8_container():
-    # Show HN: colibri, section What's implemented: packing validated
+    # Show HN: Getting GLM-5.2 running on my slow computer, section What's implemented: packing validated
     # bit-identical to the int8 container. Every byte value round-trips.
     allbytes = np.arange(256, dtype=np.uint8)
     codes = quant.unpack_int4(allbytes)
@@ -137,7 +137,7 @@ def test_q8_0_bounds_and_zero_group():
 
 
 def test_page_byte_accounting(golden_dir):
-    # Show HN: colibri, section The idea: ~19 MB per routed expert at int4;
+    # Show HN: Getting GLM-5.2 running on my slow computer, section The idea: ~19 MB per routed expert at int4;
     # section Got a better machine?: ~11.4 GB of expert reads per cold token.
     pn = json.load(open(os.path.join(golden_dir, "page_numbers.json")))
     glm = synth.LAYERS["glm"]
