@@ -122,12 +122,29 @@ void record(const hipEvent_t* ev, int idx, hipStream_t st) {
 
 hipEvent_t stage_ev(const hipEvent_t* ev, int idx) { return ev ? ev[idx] : nullptr; }
 
-// The expert FFN over a prepared work list (slots / tiles / row_token in ws).
-moe_status run_experts(const float* x, int T, int k, const moe_experts& routed, const moe_experts* shared,
-                       int act_mode, const moe::WsLayout& L, void* ws, float* y, int32_t* dots_gate,
-                       int32_t* dots_up, int8_t* hq_out, float* hd_out, int32_t* dots_down,
-                       const hipEvent_t* ev, hipStream_t st) {
-    const int E = routed.n_experts, d = routed.d_model;
+// Where the prepared hidden states go in the workspace (f32 parts or Q8_0).
+moe::XPrep xprep_for(int act_mode, int fmt, const moe::WsLayout& L, void* ws) {
+    moe::XPrep xp;
+    if (act_mode == MOE_ACT_F32) {
+        xp.mode = moe::XPREP_SPLIT;
+        xp.fmt = fmt;
+        xp.hi = ws_at<_Float16>(ws, L.xq);
+        xp.lo = ws_at<_Float16>(ws, L.xd);
+        xp.pow = ws_at<float>(ws, L.xp);
+    } else {
+        xp.mode = moe::XPREP_Q8_0;
+        xp.q = ws_at<int8_t>(ws, L.xq);
+        xp.qd = ws_at<float>(ws, L.xd);
+    }
+    return xp;
+}
+
+// The expert FFN over a prepared work list (slots / tiles / row_token in ws)
+// and prepared hidden states (xprep_for).
+moe_status run_experts(int T, int k, const moe_experts& routed, const moe_experts* shared, int act_mode,
+                       const moe::WsLayout& L, void* ws, float* y, int32_t* dots_gate, int32_t* dots_up,
+                       int8_t* hq_out, float* hd_out, int32_t* dots_down, const hipEvent_t* ev, hipStream_t st) {
+    const int E = routed.n_experts;
     const int n = T * k;
     const int has_shared = shared != nullptr;
     const int* row_token = ws_at<int>(ws, L.row_token);
@@ -137,32 +154,26 @@ moe_status run_experts(const float* x, int T, int k, const moe_experts& routed, 
     if (act_mode == MOE_ACT_F32) {
         const int max_slots = (E < n ? E : n) + has_shared;
         const int R = n + (has_shared ? T : 0);
-        const int fmt = routed.format;
-        _Float16* ahi = ws_at<_Float16>(ws, L.xq);
-        _Float16* alo = ws_at<_Float16>(ws, L.xd);
-        float* apow = ws_at<float>(ws, L.xp);
+        const _Float16* ahi = ws_at<_Float16>(ws, L.xq);
+        const _Float16* alo = ws_at<_Float16>(ws, L.xd);
+        const float* apow = ws_at<float>(ws, L.xp);
         _Float16* hhi = ws_at<_Float16>(ws, L.h);
         _Float16* hlo = ws_at<_Float16>(ws, L.hd);
         float* hpow = ws_at<float>(ws, L.hp);
-        record(ev, 2 * MOE_STAGE_QUANT_X, st);
-        MOE_HIP(moe::launch_prep_act(fmt, x, row_token, slots, meta, max_slots, R, d, ahi, alo, apow, st),
-                "activation split");
-        record(ev, 2 * MOE_STAGE_QUANT_X + 1, st);
-        MOE_HIP(moe::launch_gemv(routed, shared, true, ahi, alo, apow, R, slots, meta, max_slots, hhi, hlo, hpow,
-                                 nullptr, st, stage_ev(ev, 2 * MOE_STAGE_GATEUP), stage_ev(ev, 2 * MOE_STAGE_GATEUP + 1)),
+        MOE_HIP(moe::launch_gemv(routed, shared, true, ahi, alo, apow, row_token, T, R, slots, meta, max_slots, hhi,
+                                 hlo, hpow, nullptr, st, stage_ev(ev, 2 * MOE_STAGE_GATEUP),
+                                 stage_ev(ev, 2 * MOE_STAGE_GATEUP + 1)),
                 "gate/up GEMV");
-        MOE_HIP(moe::launch_gemv(routed, shared, false, hhi, hlo, hpow, R, slots, meta, max_slots, nullptr, nullptr,
-                                 nullptr, y, st, stage_ev(ev, 2 * MOE_STAGE_DOWN), stage_ev(ev, 2 * MOE_STAGE_DOWN + 1)),
+        MOE_HIP(moe::launch_gemv(routed, shared, false, hhi, hlo, hpow, nullptr, R, R, slots, meta, max_slots, nullptr,
+                                 nullptr, nullptr, y, st, stage_ev(ev, 2 * MOE_STAGE_DOWN),
+                                 stage_ev(ev, 2 * MOE_STAGE_DOWN + 1)),
                 "down GEMV");
         return MOE_OK;
     }
-    int8_t* xq = ws_at<int8_t>(ws, L.xq);
-    float* xd = ws_at<float>(ws, L.xd);
+    const int8_t* xq = ws_at<int8_t>(ws, L.xq);
+    const float* xd = ws_at<float>(ws, L.xd);
     int8_t* hq = hq_out ? hq_out : ws_at<int8_t>(ws, L.h);
     float* hd = hd_out ? hd_out : ws_at<float>(ws, L.hd);
-    record(ev, 2 * MOE_STAGE_QUANT_X, st);
-    MOE_HIP(moe::launch_quantize_q8_0(x, T, d, xq, xd, st), "Q8_0 of x");
-    record(ev, 2 * MOE_STAGE_QUANT_X + 1, st);
     MOE_HIP(moe::launch_q8_mfma(routed, shared, true, xq, xd, row_token, tiles, meta, L.max_tiles, hq, hd, nullptr,
                                 dots_gate, dots_up, st, stage_ev(ev, 2 * MOE_STAGE_GATEUP),
                                 stage_ev(ev, 2 * MOE_STAGE_GATEUP + 1)),
@@ -196,8 +207,9 @@ moe_status expert_ffn_impl(const float* x, int32_t T, int32_t k, const moe_exper
     MOE_HIP(moe::launch_plan(counts, offsets, perm, T, k, ex->n_experts, 0, ws_at<int>(ws, L.row_token),
                              ws_at<int>(ws, L.slots), ws_at<int>(ws, L.tiles), ws_at<int>(ws, L.meta), st),
             "work-list kernel");
-    if ((s = run_experts(x, T, k, *ex, nullptr, act_mode, L, ws, y_perm, dots_gate, dots_up, hq, hd, dots_down,
-                         nullptr, st)) != MOE_OK)
+    MOE_HIP(moe::launch_xprep(x, T, ex->d_model, xprep_for(act_mode, ex->format, L, ws), st), "hidden states");
+    if ((s = run_experts(T, k, *ex, nullptr, act_mode, L, ws, y_perm, dots_gate, dots_up, hq, hd, dots_down, nullptr,
+                         st)) != MOE_OK)
         return s;
     return ok();
 }
@@ -233,18 +245,37 @@ moe_status layer_forward_impl(const float* x, int32_t T, const float* gate_w, co
     int* idx = ws_at<int>(ws, L.idx);
     float* w = ws_at<float>(ws, L.wts);
     int* inv_perm = ws_at<int>(ws, L.inv_perm);
+    float* logits = ws_at<float>(ws, L.logits);
+    const moe::XPrep xp = xprep_for(act_mode, routed->format, L, ws);
+    // small T: the logits kernel also prepares the hidden states, and top-k +
+    // dispatch are one block; larger T: each step is a kernel of its own
+    const bool small = moe::router_splits(T, E, d) == 0;
+    const bool fused = T <= moe::kFusedRouteT;
     record(ev, 2 * MOE_STAGE_ROUTE, st);
-    MOE_HIP(moe::launch_router(x, T, d, gate_w, *p, ws_at<float>(ws, L.logits), idx, w, st), "router");
+    MOE_HIP(moe::launch_router_logits(x, T, d, gate_w, E, logits, xp, st), "router logits");
+    if (!fused) MOE_HIP(moe::launch_router_topk(logits, T, d, *p, idx, w, st), "router top-k");
     record(ev, 2 * MOE_STAGE_ROUTE + 1, st);
+    if (!small) {
+        record(ev, 2 * MOE_STAGE_QUANT_X, st);
+        MOE_HIP(moe::launch_xprep(x, T, d, xp, st), "hidden states");
+        record(ev, 2 * MOE_STAGE_QUANT_X + 1, st);
+    }
     record(ev, 2 * MOE_STAGE_DISPATCH, st);
-    MOE_HIP(moe::launch_dispatch(idx, T, k, E, ws_at<int>(ws, L.counts), ws_at<int>(ws, L.offsets),
-                                 ws_at<int>(ws, L.perm), inv_perm, has_shared, ws_at<int>(ws, L.row_token),
-                                 ws_at<int>(ws, L.slots), ws_at<int>(ws, L.tiles), ws_at<int>(ws, L.meta), st),
-            "dispatch");
+    if (fused)
+        MOE_HIP(moe::launch_route_dispatch(logits, T, d, *p, idx, w, ws_at<int>(ws, L.counts),
+                                           ws_at<int>(ws, L.offsets), ws_at<int>(ws, L.perm), inv_perm, has_shared,
+                                           ws_at<int>(ws, L.row_token), ws_at<int>(ws, L.slots),
+                                           ws_at<int>(ws, L.tiles), ws_at<int>(ws, L.meta), st),
+                "router top-k + dispatch");
+    else
+        MOE_HIP(moe::launch_dispatch(idx, T, k, E, ws_at<int>(ws, L.counts), ws_at<int>(ws, L.offsets),
+                                     ws_at<int>(ws, L.perm), inv_perm, has_shared, ws_at<int>(ws, L.row_token),
+                                     ws_at<int>(ws, L.slots), ws_at<int>(ws, L.tiles), ws_at<int>(ws, L.meta), st),
+                "dispatch");
     record(ev, 2 * MOE_STAGE_DISPATCH + 1, st);
     float* y = ws_at<float>(ws, L.y);
-    if ((s = run_experts(x, T, k, *routed, shared, act_mode, L, ws, y, nullptr, nullptr, nullptr, nullptr, nullptr,
-                         ev, st)) != MOE_OK)
+    if ((s = run_experts(T, k, *routed, shared, act_mode, L, ws, y, nullptr, nullptr, nullptr, nullptr, nullptr, ev,
+                         st)) != MOE_OK)
         return s;
     record(ev, 2 * MOE_STAGE_COMBINE, st);
     MOE_HIP(moe::launch_combine(y, w, inv_perm, has_shared ? y + (size_t)T * k * d : nullptr, T, k, d, out, st),

@@ -30,9 +30,9 @@ struct WsLayout {
     size_t slots = 0;      // i32  [E + 1][4]  (expert, row_begin, n_rows, 0)
     size_t tiles = 0;      // i32  [max_tiles][4] (expert, row_begin, row_end, 0)
     size_t meta = 0;       // i32  [4]  n_slots, n_tiles, status, 0
-    size_t xq = 0;         // Q8_0: i8 [T, d]      F32: f16 hi parts [R, d]
-    size_t xd = 0;         // Q8_0: f32 [T, d/32]  F32: f16 lo parts [R, d]
-    size_t xp = 0;         //                      F32: f32 powers of two [R, d/32]
+    size_t xq = 0;         // Q8_0: i8 [T, d]      F32: f16 hi parts [T, d]
+    size_t xd = 0;         // Q8_0: f32 [T, d/32]  F32: f16 lo parts [T, d]
+    size_t xp = 0;         //                      F32: f32 powers of two [d/32]
     size_t h = 0;          // Q8_0: i8 [R, I]      F32: f16 hi parts [R, I];  R = T*k + T*shared
     size_t hd = 0;         // Q8_0: f32 [R, I/32]  F32: f16 lo parts [R, I]
     size_t hp = 0;         //                      F32: f32 powers of two [R, I/32]
@@ -83,9 +83,9 @@ inline WsLayout ws_layout(int T, int k, int E, int d, int I, int act_mode, int h
         L.h = take(R * I);
         L.hd = take(R * (I / kGroup) * 4);
     } else {
-        L.xq = take(R * d * 2);
-        L.xd = take(R * d * 2);
-        L.xp = take(R * (d / kGroup) * 4);
+        L.xq = take((size_t)T * d * 2);
+        L.xd = take((size_t)T * d * 2);
+        L.xp = take((size_t)(d / kGroup) * 4);
         L.h = take(R * I * 2);
         L.hd = take(R * I * 2);
         L.hp = take(R * (I / kGroup) * 4);
@@ -130,6 +130,32 @@ __host__ __device__ __forceinline__ size_t int4_code_offset(size_t row, size_t k
 __host__ __device__ __forceinline__ size_t scale_index(size_t row, size_t g, size_t G) {
     const size_t r = row % kTile;
     return ((row / kTile) * (G / 2) + (g >> 1)) * 64 + (r & 15) * 4 + (g & 1) * 2 + (r >> 4);
+}
+
+// ---------------------------------------------------------------------------
+// Activations of the f32 path on the f16 matrix cores. Per group of 32 along
+// the reduction axis, a power of two p = 2^(e-15) with max|x| < 2^e over the
+// rows that share an MFMA operand, and x/p split exactly into two f16 parts
+// (hi = f16(x/p), lo = f16(x/p - hi)). Inside each 8-wide slice the parts are
+// stored in the order in which the weight-code conversion produces its
+// operand slots (int8: bytes (0,2),(1,3) of a dword; int4: nibbles (0,4),
+// (1,5), (2,6), (3,7)).
+// ---------------------------------------------------------------------------
+// k offset (0..7) inside an 8-wide slice for operand slot j
+__host__ __device__ constexpr int slot_k(int fmt, int j) {
+    return fmt == MOE_W_INT8_G32 ? ((j & 4) | ((j & 1) << 1) | ((j >> 1) & 1)) : (((j & 1) << 2) | (j >> 1));
+}
+
+// operand slot holding k offset kin (0..7) of an 8-wide slice
+__host__ __device__ constexpr int k_slot(int fmt, int kin) {
+    return fmt == MOE_W_INT8_G32 ? ((kin & 4) | ((kin & 2) >> 1) | ((kin & 1) << 1)) : (((kin & 3) << 1) | (kin >> 2));
+}
+
+// exponent e with |x| < 2^e for x = amax (0 -> 0), clamped so 2^(15-e) stays finite
+__device__ __forceinline__ int pow2_exponent(float amax) {
+    int ex = 0;
+    if (amax > 0.0f) (void)frexpf(amax, &ex);
+    return min(max(ex, -100), 120);
 }
 
 // Launch on `st`; with events, they are attached to the dispatch itself, so

@@ -15,8 +15,12 @@
 // The same block then writes the work lists the expert kernels consume:
 // slots (one per expert with rows, then the shared expert), int8-MFMA tiles
 // of kTileRows rows, and the row -> token map.
+//
+// For small batches the router's top-k runs in the same block first (one wave
+// per token), so the routing reaches the dispatch through LDS.
 #include "common.h"
 #include "kernels.h"
+#include "topk.h"
 
 namespace moe {
 
@@ -25,7 +29,7 @@ constexpr int kDispWaves = kDispThreads / kWave;
 
 // Exclusive scan of one value per thread over the whole block. `tmp` holds at
 // least kDispWaves + 1 ints. Returns the exclusive prefix; *total gets the sum.
-__device__ int block_exclusive_scan(int v, int* tmp, int* total) {
+__device__ __forceinline__ int block_exclusive_scan(int v, int* tmp, int* total) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     int incl = v;
 #pragma unroll
@@ -52,7 +56,7 @@ __device__ int block_exclusive_scan(int v, int* tmp, int* total) {
 }
 
 // Work lists from counts/offsets (thread e < E holds counts[e], offsets[e]).
-__device__ void build_work_lists(int E, int cnt, int off, int n_rows_routed, int T, int has_shared,
+__device__ __forceinline__ void build_work_lists(int E, int cnt, int off, int n_rows_routed, int T, int has_shared,
                                  int tile_rows, int* scan_tmp, int* __restrict__ slots, int* __restrict__ tiles,
                                  int* __restrict__ meta) {
     const int e = threadIdx.x;
@@ -89,21 +93,18 @@ __device__ void build_work_lists(int E, int cnt, int off, int n_rows_routed, int
     }
 }
 
-__global__ __launch_bounds__(kDispThreads) void dispatch_kernel(const int* __restrict__ idx, int T, int k, int E,
-                                                                 int* __restrict__ counts, int* __restrict__ offsets,
-                                                                 int* __restrict__ perm, int* __restrict__ inv_perm,
-                                                                 int has_shared, int tile_rows,
-                                                                 int* __restrict__ row_token,
-                                                                 int* __restrict__ slots, int* __restrict__ tiles,
-                                                                 int* __restrict__ meta) {
-    extern __shared__ int lds[];
-    int* hist = lds;                                  // [kDispWaves][E]
-    int* scan_tmp = lds + kDispWaves * E;             // [kDispWaves + 1]
-    __shared__ int bad_flag;
+// The dispatch proper, by the whole block. idx: the T*k expert ids (global
+// or LDS); tmp: T*k ints for the ranks between the passes (LDS, or inv_perm
+// itself); hist: kDispWaves*E ints of LDS; scan_tmp: kDispWaves+1 ints of LDS.
+__device__ __forceinline__ void dispatch_block(const int* idx, int* tmp, int T, int k, int E, int* __restrict__ counts,
+                               int* __restrict__ offsets, int* __restrict__ perm, int* __restrict__ inv_perm,
+                               int has_shared, int tile_rows, int* __restrict__ row_token, int* __restrict__ slots,
+                               int* __restrict__ tiles, int* __restrict__ meta, int* hist, int* scan_tmp,
+                               int* bad_flag) {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int n = T * k;
     for (int i = tid; i < kDispWaves * E; i += kDispThreads) hist[i] = 0;
-    if (tid == 0) bad_flag = 0;
+    if (tid == 0) *bad_flag = 0;
     __syncthreads();
 
     const int chunk = (((n + kDispWaves - 1) / kDispWaves) + kWave - 1) / kWave * kWave;
@@ -115,7 +116,7 @@ __global__ __launch_bounds__(kDispThreads) void dispatch_kernel(const int* __res
 
     // pass 1: stable rank inside this wave's chunk; the expert ids of kPB
     // segments are fetched together so their loads overlap
-    constexpr int kPB = 8;
+    constexpr int kPB = 4;
     for (int base = begin; base < end; base += kPB * kWave) {
         int ev[kPB];
 #pragma unroll
@@ -129,7 +130,7 @@ __global__ __launch_bounds__(kDispThreads) void dispatch_kernel(const int* __res
             const bool valid = f < end;
             const int e = ev[u];
             const bool inr = valid && e >= 0 && e < E;
-            if (valid && !inr) bad_flag = 1;
+            if (valid && !inr) *bad_flag = 1;
             uint64_t peers = __ballot(inr);
             for (int b = 0; b < nbits; ++b) {
                 const bool bit = (e >> b) & 1;
@@ -141,7 +142,7 @@ __global__ __launch_bounds__(kDispThreads) void dispatch_kernel(const int* __res
             // the last lane of each peer set advances the histogram; every lane has
             // read it above, and a wave executes its LDS operations in order
             if (inr && rank == __popcll(peers) - 1) my_hist[e] = prior + __popcll(peers);
-            if (inr) inv_perm[f] = prior + rank;
+            if (inr) tmp[f] = prior + rank;
         }
     }
     __syncthreads();
@@ -174,7 +175,7 @@ __global__ __launch_bounds__(kDispThreads) void dispatch_kernel(const int* __res
         for (int u = 0; u < kPB; ++u) {
             const int f = base + u * kWave + lane;
             ev[u] = f < end ? idx[f] : -1;
-            rv[u] = (f < end && ev[u] >= 0 && ev[u] < E) ? inv_perm[f] : 0;
+            rv[u] = (f < end && ev[u] >= 0 && ev[u] < E) ? tmp[f] : 0;
         }
 #pragma unroll
         for (int u = 0; u < kPB; ++u) {
@@ -193,8 +194,58 @@ __global__ __launch_bounds__(kDispThreads) void dispatch_kernel(const int* __res
     if (slots) {
         build_work_lists(E, cnt, off, n, T, has_shared, tile_rows, scan_tmp, slots, tiles, meta);
         __syncthreads();
-        if (tid == 0) meta[2] = bad_flag;
+        if (tid == 0) meta[2] = *bad_flag;
     }
+}
+
+__global__ __launch_bounds__(kDispThreads) void dispatch_kernel(const int* __restrict__ idx, int T, int k, int E,
+                                                                 int* __restrict__ counts, int* __restrict__ offsets,
+                                                                 int* __restrict__ perm, int* __restrict__ inv_perm,
+                                                                 int has_shared, int tile_rows,
+                                                                 int* __restrict__ row_token,
+                                                                 int* __restrict__ slots, int* __restrict__ tiles,
+                                                                 int* __restrict__ meta) {
+    extern __shared__ __attribute__((aligned(16))) int lds[];
+    __shared__ int bad_flag;
+    dispatch_block(idx, inv_perm, T, k, E, counts, offsets, perm, inv_perm, has_shared, tile_rows, row_token, slots,
+                   tiles, meta, lds, lds + kDispWaves * E, &bad_flag);
+}
+
+// Top-k of T <= kDispWaves tokens (wave t takes token t), then the dispatch,
+// in one block; the expert ids and ranks stay in LDS.
+template <int EPL>
+__global__ __launch_bounds__(kDispThreads) void route_dispatch_kernel(const TopkArgs a, int* __restrict__ idx_out,
+                                                                       float* __restrict__ w_out,
+                                                                       int* __restrict__ counts,
+                                                                       int* __restrict__ offsets,
+                                                                       int* __restrict__ perm,
+                                                                       int* __restrict__ inv_perm, int has_shared,
+                                                                       int tile_rows, int* __restrict__ row_token,
+                                                                       int* __restrict__ slots,
+                                                                       int* __restrict__ tiles,
+                                                                       int* __restrict__ meta) {
+    extern __shared__ __attribute__((aligned(16))) int lds[];
+    __shared__ int bad_flag;
+    const int T = a.T, k = a.k, E = a.E, n = T * k;
+    const bool noaux = a.mode == MOE_ROUTER_SIGMOID_NOAUX_TC;
+    float* keybuf = reinterpret_cast<float*>(lds);           // [kDispWaves][E], noaux_tc only
+    int* idx_l = lds + (noaux ? kDispWaves * E : 0);         // [n]
+    int* rank_l = idx_l + n;                                 // [n]
+    int* hist = rank_l + n;                                  // [kDispWaves][E]
+    int* scan_tmp = hist + kDispWaves * E;                   // [kDispWaves + 1]
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const bool active = wave < T;
+    int my_e;
+    float my_w;
+    topk_token<EPL>(a, wave, active, keybuf + (noaux ? wave * E : 0), &my_e, &my_w);
+    if (active && lane < k) {
+        idx_out[wave * k + lane] = my_e;
+        w_out[wave * k + lane] = my_w;
+        idx_l[wave * k + lane] = my_e;
+    }
+    __syncthreads();
+    dispatch_block(idx_l, rank_l, T, k, E, counts, offsets, perm, inv_perm, has_shared, tile_rows, row_token, slots,
+                   tiles, meta, hist, scan_tmp, &bad_flag);
 }
 
 // Work lists for moe_expert_ffn from a caller's counts / offsets / perm.
@@ -224,6 +275,31 @@ __global__ __launch_bounds__(kDispThreads) void plan_kernel(const int* __restric
 }
 
 size_t dispatch_lds_bytes(int E) { return (size_t)(kDispWaves * E + kDispWaves + 1) * sizeof(int); }
+
+size_t route_dispatch_lds_bytes(int T, int k, int E, int mode) {
+    const size_t keybuf = mode == MOE_ROUTER_SIGMOID_NOAUX_TC ? (size_t)kDispWaves * E : 0;
+    return (keybuf + 2 * (size_t)T * k + dispatch_lds_bytes(E) / sizeof(int)) * sizeof(int);
+}
+
+hipError_t launch_route_dispatch(const float* logits, int T, int d, const moe_router_params& p, int* idx, float* w,
+                                 int* counts, int* offsets, int* perm, int* inv_perm, int has_shared,
+                                 int* row_token, int* slots, int* tiles, int* meta, hipStream_t st) {
+    if (T > kDispWaves) return hipErrorInvalidValue;
+    const TopkArgs a = topk_args(logits, T, d, p);
+    const size_t lds = route_dispatch_lds_bytes(T, p.top_k, p.n_experts, p.mode);
+#define MOE_RD(EPL)                                                                                              \
+    hipLaunchKernelGGL(route_dispatch_kernel<EPL>, dim3(1), dim3(kDispThreads), lds, st, a, idx, w, counts, offsets, \
+                       perm, inv_perm, has_shared, kTileRows, row_token, slots, tiles, meta)
+    switch (topk_epl(p.n_experts)) {
+        case 1: MOE_RD(1); break;
+        case 2: MOE_RD(2); break;
+        case 4: MOE_RD(4); break;
+        case 8: MOE_RD(8); break;
+        default: MOE_RD(16); break;
+    }
+#undef MOE_RD
+    return hipGetLastError();
+}
 
 hipError_t launch_dispatch(const int* idx, int T, int k, int E, int* counts, int* offsets, int* perm,
                            int* inv_perm, int has_shared, int* row_token, int* slots, int* tiles, int* meta,

@@ -12,12 +12,11 @@
 // = one quantisation group); the group's weight scale and p are applied once
 // per output per group.
 //
-// Three kernels:
-//   prep:    the activations of every permuted row (token of each routed
-//            assignment, then the shared expert's tokens) as hi/lo, with one
-//            p per (16-row tile of a slot, group).
+// Two kernels (the hidden states' f16 parts come from the router, one power
+// of two per 32-group over the batch):
 //   gate/up: per (expert, 32 weight rows): G and U for the expert's tokens,
-//            H = silu(G) * U written straight back as hi/lo + p per 32.
+//            H = silu(G) * U written straight back as hi/lo + p per (16-row
+//            tile, 32 columns), so the down kernel reads it as it is.
 //   down:    Y = H Wd^T, fp32, rows in permuted order.
 // Weight codes come straight from HBM into operand registers: in the
 // lane-tiled layout one 16-byte load per lane brings a wave the B operands of
@@ -45,15 +44,6 @@ typedef _Float16 v8h __attribute__((ext_vector_type(8)));
 typedef _Float16 v2h __attribute__((ext_vector_type(2)));
 typedef float v4f __attribute__((ext_vector_type(4)));
 
-// k offset (0..7) inside an 8-wide slice for operand slot j
-__host__ __device__ constexpr int slot_k(int fmt, int j) {
-    return fmt == MOE_W_INT8_G32 ? ((j & 4) | ((j & 1) << 1) | ((j >> 1) & 1)) : (((j & 1) << 2) | (j >> 1));
-}
-
-// operand slot holding k offset kin (0..7) of an 8-wide slice
-__host__ __device__ constexpr int k_slot(int fmt, int kin) {
-    return fmt == MOE_W_INT8_G32 ? ((kin & 4) | ((kin & 2) >> 1) | ((kin & 1) << 1)) : (((kin & 3) << 1) | (kin >> 2));
-}
 
 __device__ __forceinline__ uint32_t and_or(uint32_t a, uint32_t m, uint32_t o) { return (a & m) | o; }
 
@@ -87,80 +77,13 @@ __device__ __forceinline__ v8h codes_to_f16(uint32_t w0, uint32_t w1) {
     return r.h;
 }
 
-// exponent e with |x| < 2^e for x = amax (0 -> 0), clamped so 2^(15-e) stays finite
-__device__ __forceinline__ int pow2_exponent(float amax) {
-    int ex = 0;
-    if (amax > 0.0f) (void)frexpf(amax, &ex);
-    return min(max(ex, -100), 120);
-}
-
-// ---------------------------------------------------------------------------
-// prep: block (slot, 8 groups); each wave takes 2 groups of every 16-row tile
-// of the slot: lane -> (row r = lane % 16, group of the pair, half of 32)
-// ---------------------------------------------------------------------------
-template <int FMT>
-__global__ __launch_bounds__(256) void prep_act_kernel(const float* __restrict__ x, const int* __restrict__ row_token,
-                                                       const int4* __restrict__ slots, const int* __restrict__ meta,
-                                                       int R, int K, _Float16* __restrict__ ahi,
-                                                       _Float16* __restrict__ alo, float* __restrict__ apow) {
-    const int slot = blockIdx.y;
-    if (slot >= meta[0]) return;
-    const int4 sl = slots[slot];
-    const int row_begin = sl.y, n_rows = sl.z;
-    const int G = K / kGroup;
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int r = lane & 15, gsel = (lane >> 4) & 1, half = lane >> 5;
-    const int g = blockIdx.x * 8 + wave * 2 + gsel;
-    const bool g_ok = g < G;
-    for (int mt = 0; mt < n_rows; mt += 16) {
-        const bool ok = g_ok && r < n_rows - mt;
-        const int p = row_begin + mt + r;
-        float v[16];
-        const float4* src = reinterpret_cast<const float4*>(x + (size_t)(ok ? row_token[p] : 0) * K +
-                                                            (size_t)(g_ok ? g : 0) * kGroup + 16 * half);
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            const float4 f = ok ? src[q] : make_float4(0.f, 0.f, 0.f, 0.f);
-            v[4 * q] = f.x;
-            v[4 * q + 1] = f.y;
-            v[4 * q + 2] = f.z;
-            v[4 * q + 3] = f.w;
-        }
-        float amax = 0.0f;
-#pragma unroll
-        for (int j = 0; j < 16; ++j) amax = fmaxf(amax, fabsf(v[j]));
-        // max over the 16 rows (a DPP row) and the two halves (lanes l, l ^ 32)
-        amax = fmaxf(amax, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(amax), 0xB1, 0xF, 0xF, true)));
-        amax = fmaxf(amax, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(amax), 0x4E, 0xF, 0xF, true)));
-        amax = fmaxf(amax, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(amax), 0x141, 0xF, 0xF, true)));
-        amax = fmaxf(amax, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(amax), 0x140, 0xF, 0xF, true)));
-        amax = fmaxf(amax, __shfl_xor(amax, 32, kWave));
-        const int ex = pow2_exponent(amax);
-        const float up = ldexpf(1.0f, 15 - ex);
-        if (ok) {
-#pragma unroll
-            for (int s2 = 0; s2 < 2; ++s2) {
-                v8h hi, lo;
-#pragma unroll
-                for (int j = 0; j < 8; ++j) {
-                    const float sv = v[8 * s2 + slot_k(FMT, j)] * up;
-                    const _Float16 hv = (_Float16)sv;
-                    hi[j] = hv;
-                    lo[j] = (_Float16)(sv - (float)hv);
-                }
-                const size_t off = (size_t)p * K + (size_t)g * kGroup + 16 * half + 8 * s2;
-                *reinterpret_cast<v8h*>(ahi + off) = hi;
-                *reinterpret_cast<v8h*>(alo + off) = lo;
-            }
-        }
-        if (g_ok && r == 0 && half == 0) apow[(size_t)(row_begin + mt) * G + g] = ldexpf(1.0f, ex - 15);
-    }
-}
 
 struct GemvArgs {
-    const _Float16* ahi;    // activation parts [R, K] in slot order
+    const _Float16* ahi;    // activation parts in slot order: gate/up [T, K] token rows, down [R, K]
     const _Float16* alo;
-    const float* apow;      // [R, K/32]: row = first row of a 16-row tile
+    const float* apow;      // gate/up [K/32]; down [R, K/32] at the first row of each 16-row tile
+    const int* row_token;   // gate/up: permuted row -> token row of ahi / alo
+    int a_rows;             // rows of ahi / alo
     const int4* slots;      // (expert, row_begin, n_rows, 0)
     const int* meta;        // meta[0] = number of slots
     const uint8_t* q[2];    // routed codes: gate, up (gate/up) or down, down
@@ -219,19 +142,30 @@ __global__ __launch_bounds__(64 * KS) void gemv_kernel(const GemvArgs a) {
         q_voff[t] = tile[t] * (FMT == MOE_W_INT8_G32 ? G : P) * 1024 + lane * 16;
         s_voff[t] = (tile[t] * P * 64 + nl * 4) * 4;
     }
-    const __amdgpu_buffer_rsrc_t rah = __builtin_amdgcn_make_buffer_rsrc((void*)a.ahi, 0, R * K * 2, 0x00020000);
-    const __amdgpu_buffer_rsrc_t ral = __builtin_amdgcn_make_buffer_rsrc((void*)a.alo, 0, R * K * 2, 0x00020000);
+    const int a_bytes = a.a_rows * K * 2;
+    const __amdgpu_buffer_rsrc_t rah = __builtin_amdgcn_make_buffer_rsrc((void*)a.ahi, 0, a_bytes, 0x00020000);
+    const __amdgpu_buffer_rsrc_t ral = __builtin_amdgcn_make_buffer_rsrc((void*)a.alo, 0, a_bytes, 0x00020000);
     const int n_my = (P - ks + KS - 1) / KS;
+    if constexpr (GATEUP) {
+        for (int i = threadIdx.x; i < G; i += 64 * KS) pwtab[i] = a.apow[i];
+    }
 
     for (int mt = 0; mt < n_rows; mt += 16) {
         const int rows_here = min(16, n_rows - mt);
+        // this lane's operand row: a token (gate/up) or a permuted row (down);
         // rows past the expert's count read past the resource: zeros
-        const int a_voff = nl < rows_here ? ((row_begin + mt + nl) * K + 8 * h) * 2 : 0x7ffffff0;
-        const int prow = row_begin + mt + 4 * h;   // output rows (tokens) 4h .. 4h+3 of the tile
+        int a_voff = 0x7ffffff0;
+        if (nl < rows_here) {
+            const int ar = GATEUP ? a.row_token[row_begin + mt + nl] : row_begin + mt + nl;
+            a_voff = (ar * K + 8 * h) * 2;
+        }
+        const int prow = row_begin + mt + 4 * h;   // output rows 4h .. 4h+3 of the tile
 
-        __syncthreads();   // the previous tile's readers of pwtab / red are done
-        for (int i = threadIdx.x; i < G; i += 64 * KS) pwtab[i] = a.apow[(size_t)(row_begin + mt) * G + i];
-        __syncthreads();
+        __syncthreads();   // pwtab is written; the previous tile's readers of red are done
+        if constexpr (!GATEUP) {
+            for (int i = threadIdx.x; i < G; i += 64 * KS) pwtab[i] = a.apow[(size_t)(row_begin + mt) * G + i];
+            __syncthreads();
+        }
 
         v4f acc[2][2];
 #pragma unroll
@@ -402,29 +336,17 @@ static int choose_ks(int slots, int blocks_x, int P) {
     return ks;
 }
 
-hipError_t launch_prep_act(int fmt, const float* x, const int* row_token, const int* slots, const int* meta,
-                           int max_slots, int R, int K, _Float16* ahi, _Float16* alo, float* apow, hipStream_t st) {
-    if (max_slots == 0) return hipSuccess;
-    const dim3 grid((K / kGroup + 7) / 8, max_slots);
-    const int4* sl = reinterpret_cast<const int4*>(slots);
-    if (fmt == MOE_W_INT8_G32)
-        hipLaunchKernelGGL(prep_act_kernel<MOE_W_INT8_G32>, grid, dim3(256), 0, st, x, row_token, sl, meta, R, K, ahi,
-                           alo, apow);
-    else
-        hipLaunchKernelGGL(prep_act_kernel<MOE_W_INT4_G32>, grid, dim3(256), 0, st, x, row_token, sl, meta, R, K, ahi,
-                           alo, apow);
-    return hipGetLastError();
-}
-
 hipError_t launch_gemv(const moe_experts& routed, const moe_experts* shared, bool gateup, const _Float16* ahi,
-                       const _Float16* alo, const float* apow, int R, const int* slots, const int* meta, int max_slots,
-                       _Float16* hhi, _Float16* hlo, float* hpow, float* y, hipStream_t st, hipEvent_t ev0,
-                       hipEvent_t ev1) {
+                       const _Float16* alo, const float* apow, const int* row_token, int a_rows, int R,
+                       const int* slots, const int* meta, int max_slots, _Float16* hhi, _Float16* hlo, float* hpow,
+                       float* y, hipStream_t st, hipEvent_t ev0, hipEvent_t ev1) {
     if (max_slots == 0) return hipSuccess;
     GemvArgs a{};
     a.ahi = ahi;
     a.alo = alo;
     a.apow = apow;
+    a.row_token = row_token;
+    a.a_rows = a_rows;
     a.slots = reinterpret_cast<const int4*>(slots);
     a.meta = meta;
     a.E = routed.n_experts;

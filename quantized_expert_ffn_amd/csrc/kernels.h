@@ -10,8 +10,36 @@ hipError_t launch_quantize_weights(const float* w, int64_t rows, int cols, int b
                                    hipStream_t st);
 hipError_t launch_quantize_q8_0(const float* x, int64_t rows, int cols, int8_t* q, float* d, hipStream_t st);
 
+// Hidden-state preparation for the expert kernels, done by the router's
+// logits kernel at small T (else by a kernel of its own).
+enum { XPREP_NONE = 0, XPREP_SPLIT = 1, XPREP_Q8_0 = 2 };
+struct XPrep {
+    int mode = XPREP_NONE;
+    int fmt = MOE_W_INT8_G32;      // XPREP_SPLIT: the weight format (operand-slot order)
+    _Float16* hi = nullptr;        // XPREP_SPLIT: [T, d] f16 parts and one power of
+    _Float16* lo = nullptr;        //   two per 32-group over all rows, [d/32]
+    float* pow = nullptr;
+    int8_t* q = nullptr;           // XPREP_Q8_0: [T, d] codes, [T, d/32] scales
+    float* qd = nullptr;
+};
+
 hipError_t launch_router(const float* x, int T, int d, const float* wg, const moe_router_params& p, float* logits,
                          int* idx, float* w, hipStream_t st);
+// With router_splits(T, E, d) == 0 (small T) the logits kernel also does xp;
+// otherwise xp is ignored and the caller runs launch_xprep.
+hipError_t launch_router_logits(const float* x, int T, int d, const float* wg, int E, float* logits,
+                                const XPrep& xp, hipStream_t st);
+hipError_t launch_router_topk(const float* logits, int T, int d, const moe_router_params& p, int* idx, float* w,
+                              hipStream_t st);
+hipError_t launch_xprep(const float* x, int T, int d, const XPrep& xp, hipStream_t st);
+
+// Top-k and dispatch in one block for small batches (T <= kFusedRouteT):
+// routing results never leave LDS between the two.
+constexpr int kFusedRouteT = 16;
+size_t route_dispatch_lds_bytes(int T, int k, int E, int mode);
+hipError_t launch_route_dispatch(const float* logits, int T, int d, const moe_router_params& p, int* idx, float* w,
+                                 int* counts, int* offsets, int* perm, int* inv_perm, int has_shared,
+                                 int* row_token, int* slots, int* tiles, int* meta, hipStream_t st);
 
 size_t dispatch_lds_bytes(int E);
 hipError_t launch_dispatch(const int* idx, int T, int k, int E, int* counts, int* offsets, int* perm,
@@ -20,16 +48,14 @@ hipError_t launch_dispatch(const int* idx, int T, int k, int E, int* counts, int
 hipError_t launch_plan(const int* counts, const int* offsets, const int* perm, int T, int k, int E, int has_shared,
                        int* row_token, int* slots, int* tiles, int* meta, hipStream_t st);
 
-// Decode path (fp32 activations). prep writes the activations of every
-// permuted row as exact f16 hi/lo parts + a power of two per (16-row tile of
-// a slot, 32-group);
-// the GEMV runs gate/up (x parts -> H parts) or down (H parts -> Y fp32).
-hipError_t launch_prep_act(int fmt, const float* x, const int* row_token, const int* slots, const int* meta,
-                           int max_slots, int R, int K, _Float16* ahi, _Float16* alo, float* apow, hipStream_t st);
+// Decode path (fp32 activations). gate/up: A = the token rows' f16 parts
+// [T, d] (read through row_token) with one power of two per 32-group, [d/32];
+// it writes H's parts [R, I] with one power per (16-row tile of a slot,
+// 32-group), [R, I/32]. down: A = H's parts -> Y fp32 [R, d].
 hipError_t launch_gemv(const moe_experts& routed, const moe_experts* shared, bool gateup, const _Float16* ahi,
-                       const _Float16* alo, const float* apow, int R, const int* slots, const int* meta, int max_slots,
-                       _Float16* hhi, _Float16* hlo, float* hpow, float* y, hipStream_t st,
-                       hipEvent_t ev_start = nullptr, hipEvent_t ev_stop = nullptr);
+                       const _Float16* alo, const float* apow, const int* row_token, int a_rows, int R,
+                       const int* slots, const int* meta, int max_slots, _Float16* hhi, _Float16* hlo, float* hpow,
+                       float* y, hipStream_t st, hipEvent_t ev_start = nullptr, hipEvent_t ev_stop = nullptr);
 
 hipError_t launch_q8_mfma(const moe_experts& routed, const moe_experts* shared, bool gateup, const int8_t* a_q,
                           const float* a_s, const int* row_token, const int* tiles, const int* meta, int max_tiles,

@@ -1,101 +1,121 @@
-// Router: logits L = X Wg^T (fp32) and per-token top-k selection.
-//
-// Softmax top-k: "I ran a 7B Mixture-of-Experts LLM in a language I built"
-// (dev.to), section "Mixture-of-Experts" (OLMoE routes each token to its top 8
-// of 64 experts). Sigmoid noaux_tc: "Show HN: Getting GLM-5.2 running on my slow computer", section "What's
-// implemented" (DeepSeek-V3-style sigmoid router, noaux_tc,
-// routed_scaling_factor); its steps are the DeepSeek-V3 ones: sigmoid scores,
-// selection on score + bias, groups ranked by the sum of their two best
-// scores, top-k among the kept groups, weights = scores normalised and scaled.
-//
-// Ranking is by key descending, ties to the lower expert (group) id.
+// Router: logits L = X Wg^T (fp32) and per-token top-k selection (topk.h
+// gives the selection rules and their sources).
 //
 // Logits are written as S partial sums over contiguous slices of d
-// ([S, T, E]); the top-k kernel adds them in slice order, so the result is
+// ([S, T, E]); the top-k adds them in slice order, so the result is
 // deterministic whatever S the launcher picks for the shape.
-#include <float.h>
-
+//
+// The small-T logits kernel also prepares the hidden states for the expert
+// kernels while it has them in hand: the exact f16 hi/lo split of the f32
+// path, or the Q8_0 codes of the int8 path ("Show HN: Getting GLM-5.2 running
+// on my slow computer", section "What's implemented": Q8_0-style int8
+// activations in batch, a single row in f32).
 #include "common.h"
 #include "kernels.h"
+#include "topk.h"
 
 namespace moe {
 
 typedef float v16f __attribute__((ext_vector_type(16)));
+typedef _Float16 v8h __attribute__((ext_vector_type(8)));
 
-template <int CTRL>
-__device__ __forceinline__ float dppf(float v) {
-    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, true));
-}
-template <int CTRL>
-__device__ __forceinline__ int dppi(int v) {
-    return __builtin_amdgcn_update_dpp(0, v, CTRL, 0xF, 0xF, true);
-}
-
-// Full-wave sum, result in every lane (DPP inside rows of 16, then the four
-// row totals read back as uniform values and added in row order).
-__device__ __forceinline__ float wave_sum_all(float v) {
-    v += dppf<0xB1>(v);
-    v += dppf<0x4E>(v);
-    v += dppf<0x141>(v);
-    v += dppf<0x140>(v);
-    const float r0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
-    const float r1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16));
-    const float r2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
-    const float r3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48));
-    return (r0 + r1) + (r2 + r3);
-}
-
-__device__ __forceinline__ float wave_max_all(float v) {
-    v = fmaxf(v, dppf<0xB1>(v));
-    v = fmaxf(v, dppf<0x4E>(v));
-    v = fmaxf(v, dppf<0x141>(v));
-    v = fmaxf(v, dppf<0x140>(v));
-    const float r0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
-    const float r1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16));
-    const float r2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
-    const float r3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48));
-    return fmaxf(fmaxf(r0, r1), fmaxf(r2, r3));
-}
-
-// (key, id) ranking: larger key first, then lower id. id = INT_MAX means "none".
-__device__ __forceinline__ bool ranks_before(float ka, int ia, float kb, int ib) {
-    return ka > kb || (ka == kb && ia < ib);
-}
-
-template <int CTRL>
-__device__ __forceinline__ void argmax_step(float& k, int& id) {
-    const float ok = dppf<CTRL>(k);
-    const int oi = dppi<CTRL>(id);
-    if (ranks_before(ok, oi, k, id)) { k = ok; id = oi; }
-}
-
-// Wave argmax over (key, id); every lane gets the winner.
-__device__ __forceinline__ void wave_argmax(float& k, int& id) {
-    argmax_step<0xB1>(k, id);
-    argmax_step<0x4E>(k, id);
-    argmax_step<0x141>(k, id);
-    argmax_step<0x140>(k, id);
-    float bk = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(k), 0));
-    int bi = __builtin_amdgcn_readlane(id, 0);
-#pragma unroll
-    for (int r = 16; r < 64; r += 16) {
-        const float rk = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(k), r));
-        const int ri = __builtin_amdgcn_readlane(id, r);
-        if (ranks_before(rk, ri, bk, bi)) { bk = rk; bi = ri; }
+// ---------------------------------------------------------------------------
+// Hidden-state preparation
+// ---------------------------------------------------------------------------
+// f32 path, group g of every row, one wave: p = 2^(e-15) with max|x| < 2^e
+// over the T rows' 32 values, x/p split into f16 hi + lo in operand-slot order.
+template <int FMT>
+__device__ __forceinline__ void split_group(const float* __restrict__ x, int T, int d, int g, const XPrep& xp) {
+    const int lane = threadIdx.x & 63;
+    const int rsub = lane >> 2, q = lane & 3;   // 16 rows per pass, 8 values per lane
+    float amax = 0.0f;
+    for (int r0 = 0; r0 < T; r0 += 16) {
+        const int r = min(r0 + rsub, T - 1);
+        const float4* src = reinterpret_cast<const float4*>(x + (size_t)r * d + g * kGroup + 8 * q);
+        const float4 a = src[0], b = src[1];
+        amax = fmaxf(amax, fmaxf(fmaxf(fabsf(a.x), fabsf(a.y)), fmaxf(fabsf(a.z), fabsf(a.w))));
+        amax = fmaxf(amax, fmaxf(fmaxf(fabsf(b.x), fabsf(b.y)), fmaxf(fabsf(b.z), fabsf(b.w))));
     }
-    k = bk;
-    id = bi;
+    amax = wave_max_all(amax);
+    const int ex = pow2_exponent(amax);
+    const float up = ldexpf(1.0f, 15 - ex);
+    for (int r0 = 0; r0 < T; r0 += 16) {
+        const int r = r0 + rsub;
+        if (r >= T) break;
+        const float4* src = reinterpret_cast<const float4*>(x + (size_t)r * d + g * kGroup + 8 * q);
+        const float4 a = src[0], b = src[1];
+        const float v[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+        v8h hi, lo;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const float sv = v[slot_k(FMT, j)] * up;
+            const _Float16 hv = (_Float16)sv;
+            hi[j] = hv;
+            lo[j] = (_Float16)(sv - (float)hv);
+        }
+        const size_t off = (size_t)r * d + g * kGroup + 8 * q;
+        *reinterpret_cast<v8h*>(xp.hi + off) = hi;
+        *reinterpret_cast<v8h*>(xp.lo + off) = lo;
+    }
+    if (lane == 0) xp.pow[g] = ldexpf(1.0f, ex - 15);
+}
+
+// Q8_0 of one group of one row by 8 lanes (4 values each), in the fp32 steps
+// of quantize_q8_0_kernel: d = amax / 127, inv = 1 / d, q = rne(x * inv).
+__device__ __forceinline__ void q8_item(const float* __restrict__ x, int d, int G, int item, const XPrep& xp) {
+    const int sub = threadIdx.x & 7;
+    const int t = item / G, g = item - t * G;
+    const size_t off = (size_t)t * d + g * kGroup + 4 * sub;
+    const float4 v = *reinterpret_cast<const float4*>(x + off);
+    float amax = fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w)));
+    amax = fmaxf(amax, __shfl_xor(amax, 1, 8));
+    amax = fmaxf(amax, __shfl_xor(amax, 2, 8));
+    amax = fmaxf(amax, __shfl_xor(amax, 4, 8));
+    const float dd = __fdiv_rn(amax, 127.0f);
+    const float inv = dd != 0.0f ? __fdiv_rn(1.0f, dd) : 0.0f;
+    const float vals[4] = {v.x, v.y, v.z, v.w};
+    uint32_t packed = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        float r = rintf(__fmul_rn(vals[j], inv));
+        r = fminf(fmaxf(r, -127.0f), 127.0f);
+        packed |= ((uint32_t)((int)r & 0xff)) << (8 * j);
+    }
+    *reinterpret_cast<uint32_t*>(xp.q + off) = packed;
+    if (sub == 0) xp.qd[item] = dd;
+}
+
+// the preparation job, spread over every wave of the grid
+__device__ __forceinline__ void xprep_waves(const float* __restrict__ x, int T, int d, const XPrep& xp, int gw, int nw) {
+    const int G = d / kGroup;
+    if (xp.mode == XPREP_SPLIT) {
+        for (int g = gw; g < G; g += nw) {
+            if (xp.fmt == MOE_W_INT8_G32) split_group<MOE_W_INT8_G32>(x, T, d, g, xp);
+            else split_group<MOE_W_INT4_G32>(x, T, d, g, xp);
+        }
+    } else if (xp.mode == XPREP_Q8_0) {
+        const int items = T * G;
+        for (int base = gw * 8; base < items; base += nw * 8) {
+            const int item = base + ((threadIdx.x & 63) >> 3);
+            if (item < items) q8_item(x, d, G, item, xp);
+        }
+    }
+}
+
+__global__ __launch_bounds__(256) void xprep_kernel(const float* __restrict__ x, int T, int d, const XPrep xp) {
+    xprep_waves(x, T, d, xp, blockIdx.x * 4 + (threadIdx.x >> 6), gridDim.x * 4);
 }
 
 // ---------------------------------------------------------------------------
 // Logits, small T (decode): one block per expert; the 256 threads split d,
 // each keeps T partial sums, then a wave reduction and a fixed-order sum of
-// the four wave partials.
+// the four wave partials. The block's waves then take their share of the
+// hidden-state preparation.
 // ---------------------------------------------------------------------------
 template <int TB>
 __global__ __launch_bounds__(256) void router_logits_gemv_kernel(const float* __restrict__ x,
                                                                  const float* __restrict__ wg, int T, int d,
-                                                                 int E, float* __restrict__ L) {
+                                                                 int E, float* __restrict__ L, const XPrep xp) {
     __shared__ float part[4][TB];
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int e = blockIdx.x;
@@ -106,15 +126,15 @@ __global__ __launch_bounds__(256) void router_logits_gemv_kernel(const float* __
     const int n4 = d >> 2;
     for (int i = threadIdx.x; i < n4; i += 256) {
         const float4 w4 = wr[i];
+        // rows past T repeat the last row (unused sums): loads without
+        // conditions all go out together instead of one at a time
 #pragma unroll
         for (int t = 0; t < TB; ++t) {
-            if (t < T) {
-                const float4 x4 = reinterpret_cast<const float4*>(x + (size_t)t * d)[i];
-                acc[t] = fmaf(x4.x, w4.x, acc[t]);
-                acc[t] = fmaf(x4.y, w4.y, acc[t]);
-                acc[t] = fmaf(x4.z, w4.z, acc[t]);
-                acc[t] = fmaf(x4.w, w4.w, acc[t]);
-            }
+            const float4 x4 = reinterpret_cast<const float4*>(x + (size_t)min(t, T - 1) * d)[i];
+            acc[t] = fmaf(x4.x, w4.x, acc[t]);
+            acc[t] = fmaf(x4.y, w4.y, acc[t]);
+            acc[t] = fmaf(x4.z, w4.z, acc[t]);
+            acc[t] = fmaf(x4.w, w4.w, acc[t]);
         }
     }
 #pragma unroll
@@ -127,6 +147,7 @@ __global__ __launch_bounds__(256) void router_logits_gemv_kernel(const float* __
         const int t = threadIdx.x;
         L[(size_t)t * E + e] = (part[0][t] + part[1][t]) + (part[2][t] + part[3][t]);
     }
+    xprep_waves(x, T, d, xp, blockIdx.x * 4 + wave, gridDim.x * 4);
 }
 
 // ---------------------------------------------------------------------------
@@ -169,159 +190,93 @@ __global__ __launch_bounds__(256) void router_logits_mfma_kernel(const float* __
 }
 
 // ---------------------------------------------------------------------------
-// Top-k: one wave per token. Lane l owns experts [l*EPL, l*EPL + EPL).
+// Top-k: one wave per token.
 // ---------------------------------------------------------------------------
 template <int EPL>
-__global__ __launch_bounds__(256) void router_topk_kernel(const float* __restrict__ L, int S, int T, int E, int k,
-                                                          int mode, int renorm, int n_group, int topk_group,
-                                                          float rsf, const float* __restrict__ bias,
-                                                          int* __restrict__ idx_out, float* __restrict__ w_out) {
-    __shared__ float keybuf[4][kMaxExperts];
+__global__ __launch_bounds__(256) void router_topk_kernel(const TopkArgs a, int* __restrict__ idx_out,
+                                                          float* __restrict__ w_out) {
+    __shared__ __attribute__((aligned(16))) float keybuf[4][kMaxExperts];
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int t = blockIdx.x * 4 + wave;
-    const bool active = t < T;
-    constexpr float NEG_INF = -INFINITY;
+    const bool active = t < a.T;
+    int my_e;
+    float my_w;
+    topk_token<EPL>(a, t, active, keybuf[wave], &my_e, &my_w);
+    if (active && lane < a.k) {
+        idx_out[(size_t)t * a.k + lane] = my_e;
+        w_out[(size_t)t * a.k + lane] = my_w;
+    }
+}
 
-    float key[EPL], val[EPL];
-#pragma unroll
-    for (int i = 0; i < EPL; ++i) {
-        const int e = lane * EPL + i;
-        float l = NEG_INF;
-        if (active && e < E) {
-            l = L[(size_t)t * E + e];
-            for (int s = 1; s < S; ++s) l += L[((size_t)s * T + t) * E + e];
-        }
-        if (mode == MOE_ROUTER_SOFTMAX_TOPK) {
-            key[i] = l;
-            val[i] = l;
-        } else {
-            const float sg = (e < E) ? 1.0f / (1.0f + expf(-l)) : 0.0f;
-            val[i] = sg;
-            key[i] = (e < E) ? sg + (bias ? bias[e] : 0.0f) : NEG_INF;
-        }
-    }
+TopkArgs topk_args(const float* logits, int T, int d, const moe_router_params& p) {
+    const int S = router_splits(T, p.n_experts, d);
+    TopkArgs a;
+    a.L = logits;
+    a.S = S == 0 ? 1 : S;
+    a.T = T;
+    a.E = p.n_experts;
+    a.k = p.top_k;
+    a.mode = p.mode;
+    a.renorm = p.renormalize;
+    a.n_group = p.n_group;
+    a.topk_group = p.topk_group;
+    a.rsf = p.routed_scaling_factor;
+    a.bias = p.score_bias;
+    return a;
+}
 
-    float lmax = 0.0f, denom = 1.0f;
-    if (mode == MOE_ROUTER_SOFTMAX_TOPK) {
-        float m = NEG_INF;
-#pragma unroll
-        for (int i = 0; i < EPL; ++i) m = fmaxf(m, val[i]);
-        lmax = wave_max_all(m);
-        float s = 0.0f;
-#pragma unroll
-        for (int i = 0; i < EPL; ++i)
-            if (lane * EPL + i < E) s += expf(val[i] - lmax);
-        denom = wave_sum_all(s);
-    } else {
-        // group-limited selection: group score = sum of the two best keys
-#pragma unroll
-        for (int i = 0; i < EPL; ++i)
-            if (lane * EPL + i < E) keybuf[wave][lane * EPL + i] = key[i];
-        __syncthreads();
-        const int gs = E / n_group;
-        float gscore = NEG_INF;
-        if (lane < n_group) {
-            float m1 = NEG_INF, m2 = NEG_INF;
-            for (int e = lane * gs; e < (lane + 1) * gs; ++e) {
-                const float c = keybuf[wave][e];
-                if (c > m1) { m2 = m1; m1 = c; }
-                else if (c > m2) { m2 = c; }
-            }
-            gscore = gs >= 2 ? m1 + m2 : m1;
-        }
-        uint64_t kept = 0;
-        for (int r = 0; r < topk_group; ++r) {
-            const bool taken = lane < n_group && ((kept >> lane) & 1ull);
-            float kk = (lane < n_group && !taken) ? gscore : NEG_INF;
-            int id = (lane < n_group && !taken) ? lane : INT_MAX;
-            wave_argmax(kk, id);
-            if (id != INT_MAX) kept |= 1ull << id;
-        }
-#pragma unroll
-        for (int i = 0; i < EPL; ++i) {
-            const int e = lane * EPL + i;
-            if (e < E && !((kept >> (e / gs)) & 1ull)) key[i] = NEG_INF;
-        }
+hipError_t launch_router_logits(const float* x, int T, int d, const float* wg, int E, float* logits,
+                                const XPrep& xp, hipStream_t st) {
+    if (T == 0) return hipSuccess;
+    const int S = router_splits(T, E, d);
+    if (S == 0) {
+        const dim3 grid(E);
+#define MOE_RL(TB) hipLaunchKernelGGL(router_logits_gemv_kernel<TB>, grid, dim3(256), 0, st, x, wg, T, d, E, logits, xp)
+        if (T == 1) MOE_RL(1);
+        else if (T <= 2) MOE_RL(2);
+        else if (T <= 4) MOE_RL(4);
+        else if (T <= 8) MOE_RL(8);
+        else MOE_RL(16);
+#undef MOE_RL
+        return hipGetLastError();
     }
+    // larger T: the preparation is the caller's own launch (launch_xprep)
+    const int kslice = router_kslice(d, S);
+    const dim3 grid((E + 63) / 64, (T + 63) / 64, S);
+    hipLaunchKernelGGL(router_logits_mfma_kernel, grid, dim3(256), 0, st, x, wg, T, d, E, kslice, logits);
+    return hipGetLastError();
+}
 
-    // k rounds of wave argmax; lane j keeps slot j's expert and value
-    uint32_t taken = 0;
-    int my_e = -1;
-    float my_v = 0.0f;
-    for (int j = 0; j < k; ++j) {
-        float bk = NEG_INF;
-        int be = INT_MAX;
-#pragma unroll
-        for (int i = 0; i < EPL; ++i) {
-            const int e = lane * EPL + i;
-            const bool cand = e < E && !((taken >> i) & 1u) && key[i] != NEG_INF;
-            if (cand && ranks_before(key[i], e, bk, be)) { bk = key[i]; be = e; }
-        }
-        wave_argmax(bk, be);
-        if (be == INT_MAX) break;                 // cannot happen for validated k
-        float v = 0.0f;
-        const int owner = be / EPL;
-        if (lane == owner) {
-#pragma unroll
-            for (int i = 0; i < EPL; ++i)
-                if (i == be - owner * EPL) { v = val[i]; taken |= 1u << i; }
-        }
-        v = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), owner));
-        if (lane == j) { my_e = be; my_v = v; }
-    }
+hipError_t launch_xprep(const float* x, int T, int d, const XPrep& xp, hipStream_t st) {
+    if (T == 0 || xp.mode == XPREP_NONE) return hipSuccess;
+    const int G = d / kGroup;
+    const int waves = xp.mode == XPREP_SPLIT ? G : (T * G + 7) / 8;
+    hipLaunchKernelGGL(xprep_kernel, dim3((waves + 3) / 4), dim3(256), 0, st, x, T, d, xp);
+    return hipGetLastError();
+}
 
-    float wj = 0.0f;
-    if (lane < k) {
-        if (mode == MOE_ROUTER_SOFTMAX_TOPK) wj = expf(my_v - lmax) / denom;
-        else wj = my_v;
+hipError_t launch_router_topk(const float* logits, int T, int d, const moe_router_params& p, int* idx, float* w,
+                              hipStream_t st) {
+    if (T == 0) return hipSuccess;
+    const TopkArgs a = topk_args(logits, T, d, p);
+    const dim3 grid((T + 3) / 4);
+#define MOE_TOPK(EPL) hipLaunchKernelGGL(router_topk_kernel<EPL>, grid, dim3(256), 0, st, a, idx, w)
+    switch (topk_epl(p.n_experts)) {
+        case 1: MOE_TOPK(1); break;
+        case 2: MOE_TOPK(2); break;
+        case 4: MOE_TOPK(4); break;
+        case 8: MOE_TOPK(8); break;
+        default: MOE_TOPK(16); break;
     }
-    if (mode == MOE_ROUTER_SOFTMAX_TOPK) {
-        if (renorm) {
-            const float tot = wave_sum_all(lane < k ? wj : 0.0f);
-            wj = wj / tot;
-        }
-    } else {
-        const float tot = wave_sum_all(lane < k ? wj : 0.0f);
-        wj = wj / tot * rsf;
-    }
-    if (active && lane < k) {
-        idx_out[(size_t)t * k + lane] = my_e;
-        w_out[(size_t)t * k + lane] = wj;
-    }
+#undef MOE_TOPK
+    return hipGetLastError();
 }
 
 hipError_t launch_router(const float* x, int T, int d, const float* wg, const moe_router_params& p,
                          float* logits, int* idx, float* w, hipStream_t st) {
-    if (T == 0) return hipSuccess;
-    const int E = p.n_experts;
-    const int S = router_splits(T, E, d);
-    if (S == 0) {
-        const dim3 grid(E);
-        if (T == 1) hipLaunchKernelGGL(router_logits_gemv_kernel<1>, grid, dim3(256), 0, st, x, wg, T, d, E, logits);
-        else if (T <= 2) hipLaunchKernelGGL(router_logits_gemv_kernel<2>, grid, dim3(256), 0, st, x, wg, T, d, E, logits);
-        else if (T <= 4) hipLaunchKernelGGL(router_logits_gemv_kernel<4>, grid, dim3(256), 0, st, x, wg, T, d, E, logits);
-        else if (T <= 8) hipLaunchKernelGGL(router_logits_gemv_kernel<8>, grid, dim3(256), 0, st, x, wg, T, d, E, logits);
-        else hipLaunchKernelGGL(router_logits_gemv_kernel<16>, grid, dim3(256), 0, st, x, wg, T, d, E, logits);
-    } else {
-        const int kslice = router_kslice(d, S);
-        const dim3 grid((E + 63) / 64, (T + 63) / 64, S);
-        hipLaunchKernelGGL(router_logits_mfma_kernel, grid, dim3(256), 0, st, x, wg, T, d, E, kslice, logits);
-    }
-    hipError_t err = hipGetLastError();
+    hipError_t err = launch_router_logits(x, T, d, wg, p.n_experts, logits, XPrep{}, st);
     if (err != hipSuccess) return err;
-    const int Ssum = S == 0 ? 1 : S;
-    const dim3 grid((T + 3) / 4);
-    const float rsf = p.routed_scaling_factor;
-#define MOE_TOPK(EPL)                                                                                          \
-    hipLaunchKernelGGL(router_topk_kernel<EPL>, grid, dim3(256), 0, st, logits, Ssum, T, E, p.top_k, p.mode,  \
-                       p.renormalize, p.n_group, p.topk_group, rsf, p.score_bias, idx, w)
-    if (E <= 64) MOE_TOPK(1);
-    else if (E <= 128) MOE_TOPK(2);
-    else if (E <= 256) MOE_TOPK(4);
-    else if (E <= 512) MOE_TOPK(8);
-    else MOE_TOPK(16);
-#undef MOE_TOPK
-    return hipGetLastError();
+    return launch_router_topk(logits, T, d, p, idx, w, st);
 }
 
 }  // namespace moe

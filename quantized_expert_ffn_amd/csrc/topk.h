@@ -1,0 +1,245 @@
+// Wave-level reductions and the per-token top-k selection of the router.
+//
+// Softmax top-k: "I ran a 7B Mixture-of-Experts LLM in a language I built"
+// (dev.to), section "Mixture-of-Experts" (each token goes to its top 8 of 64
+// experts). Sigmoid noaux_tc: "Show HN: Getting GLM-5.2 running on my slow
+// computer", section "What's implemented" (DeepSeek-V3-style sigmoid router,
+// noaux_tc, routed_scaling_factor); its steps are the DeepSeek-V3 ones:
+// sigmoid scores, selection on score + bias, groups ranked by the sum of
+// their two best keys, top-k among the kept groups, weights = the chosen
+// scores normalised to sum 1 and scaled.
+//
+// Ranking is by key descending, ties to the lower expert (group) id; the
+// output slot order is the selection order.
+#pragma once
+
+#include <float.h>
+
+#include "common.h"
+
+namespace moe {
+
+template <int CTRL>
+__device__ __forceinline__ float dppf(float v) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, true));
+}
+template <int CTRL>
+__device__ __forceinline__ int dppi(int v) {
+    return __builtin_amdgcn_update_dpp(0, v, CTRL, 0xF, 0xF, true);
+}
+
+// Full-wave sum, result in every lane (DPP inside rows of 16, then the four
+// row totals read back as uniform values and added in row order).
+__device__ __forceinline__ float wave_sum_all(float v) {
+    v += dppf<0xB1>(v);
+    v += dppf<0x4E>(v);
+    v += dppf<0x141>(v);
+    v += dppf<0x140>(v);
+    const float r0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
+    const float r1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16));
+    const float r2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
+    const float r3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48));
+    return (r0 + r1) + (r2 + r3);
+}
+
+__device__ __forceinline__ float wave_max_all(float v) {
+    v = fmaxf(v, dppf<0xB1>(v));
+    v = fmaxf(v, dppf<0x4E>(v));
+    v = fmaxf(v, dppf<0x141>(v));
+    v = fmaxf(v, dppf<0x140>(v));
+    const float r0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
+    const float r1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16));
+    const float r2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
+    const float r3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48));
+    return fmaxf(fmaxf(r0, r1), fmaxf(r2, r3));
+}
+
+// (key, id) ranking: larger key first, then lower id. id = INT_MAX means "none".
+__device__ __forceinline__ bool ranks_before(float ka, int ia, float kb, int ib) {
+    return ka > kb || (ka == kb && ia < ib);
+}
+
+template <int CTRL>
+__device__ __forceinline__ void argmax_step(float& k, int& id) {
+    const float ok = dppf<CTRL>(k);
+    const int oi = dppi<CTRL>(id);
+    if (ranks_before(ok, oi, k, id)) { k = ok; id = oi; }
+}
+
+// Wave argmax over (key, id); every lane gets the winner.
+__device__ __forceinline__ void wave_argmax(float& k, int& id) {
+    argmax_step<0xB1>(k, id);
+    argmax_step<0x4E>(k, id);
+    argmax_step<0x141>(k, id);
+    argmax_step<0x140>(k, id);
+    float bk = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(k), 0));
+    int bi = __builtin_amdgcn_readlane(id, 0);
+#pragma unroll
+    for (int r = 16; r < 64; r += 16) {
+        const float rk = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(k), r));
+        const int ri = __builtin_amdgcn_readlane(id, r);
+        if (ranks_before(rk, ri, bk, bi)) { bk = rk; bi = ri; }
+    }
+    // the winner is the same in every lane; say so, so that lane selects
+    // and shifts on it stay scalar
+    k = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(bk)));
+    id = __builtin_amdgcn_readfirstlane(bi);
+}
+
+struct TopkArgs {
+    const float* L;      // logits as S partial sums [S, T, E]
+    int S, T, E, k;
+    int mode, renorm, n_group, topk_group;
+    float rsf;
+    const float* bias;   // [E] or null
+};
+
+TopkArgs topk_args(const float* logits, int T, int d, const moe_router_params& p);
+
+// Top-k of token t by one wave (lane l owns experts l*EPL .. l*EPL+EPL-1).
+// Lane j < k returns slot j's expert and weight. keybuf: E floats of LDS
+// private to this wave (noaux_tc only). A wave with nothing to do (active
+// false) returns at once; no block-wide barrier is involved.
+template <int EPL>
+__device__ __forceinline__ void topk_token(const TopkArgs& a, int t, bool active, float* keybuf, int* out_e, float* out_w) {
+    const int lane = threadIdx.x & 63;
+    *out_e = -1;
+    *out_w = 0.0f;
+    if (!active) return;
+    const int E = a.E, k = a.k;
+    constexpr float NEG_INF = -INFINITY;
+
+    // every load goes out at once (clamped indices, masked afterwards): a load
+    // under its own condition would wait for the one before it
+    const int tc = active ? t : 0;
+    float lv[EPL], bv[EPL];
+#pragma unroll
+    for (int i = 0; i < EPL; ++i) {
+        const int ec = min(lane * EPL + i, E - 1);
+        lv[i] = a.L[(size_t)tc * E + ec];
+        bv[i] = a.bias ? a.bias[ec] : 0.0f;
+    }
+    for (int s = 1; s < a.S; ++s)
+#pragma unroll
+        for (int i = 0; i < EPL; ++i) lv[i] += a.L[((size_t)s * a.T + tc) * E + min(lane * EPL + i, E - 1)];
+
+    float key[EPL], val[EPL];
+#pragma unroll
+    for (int i = 0; i < EPL; ++i) {
+        const int e = lane * EPL + i;
+        const float l = (active && e < E) ? lv[i] : NEG_INF;
+        if (a.mode == MOE_ROUTER_SOFTMAX_TOPK) {
+            key[i] = l;
+            val[i] = l;
+        } else {
+            const float sg = (e < E) ? 1.0f / (1.0f + expf(-l)) : 0.0f;
+            val[i] = sg;
+            key[i] = (e < E) ? sg + bv[i] : NEG_INF;
+        }
+    }
+
+    float lmax = 0.0f, denom = 1.0f;
+    if (a.mode == MOE_ROUTER_SOFTMAX_TOPK) {
+        float m = NEG_INF;
+#pragma unroll
+        for (int i = 0; i < EPL; ++i) m = fmaxf(m, val[i]);
+        lmax = wave_max_all(m);
+        float s = 0.0f;
+#pragma unroll
+        for (int i = 0; i < EPL; ++i)
+            if (lane * EPL + i < E) s += expf(val[i] - lmax);
+        denom = wave_sum_all(s);
+    } else {
+        // group-limited selection: group score = sum of the two best keys
+#pragma unroll
+        for (int i = 0; i < EPL; ++i)
+            if (lane * EPL + i < E) keybuf[lane * EPL + i] = key[i];
+        // the keys are this wave's own: a wave-level barrier orders them
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        const int gs = E / a.n_group;
+        float gscore = NEG_INF;
+        if (lane < a.n_group) {
+            // the two largest keys of the group, branch-free (m1 >= m2)
+            float m1 = NEG_INF, m2 = NEG_INF;
+            auto take = [&](float c) {
+                m2 = fmaxf(m2, fminf(m1, c));
+                m1 = fmaxf(m1, c);
+            };
+            const float* grp = keybuf + lane * gs;
+            int e = 0;
+            if ((gs & 3) == 0)
+                for (; e < gs; e += 4) {
+                    const float4 c = *reinterpret_cast<const float4*>(grp + e);
+                    take(c.x);
+                    take(c.y);
+                    take(c.z);
+                    take(c.w);
+                }
+            for (; e < gs; ++e) take(grp[e]);
+            gscore = gs >= 2 ? m1 + m2 : m1;
+        }
+        uint64_t kept = 0;
+        for (int r = 0; r < a.topk_group; ++r) {
+            const bool taken = lane < a.n_group && ((kept >> lane) & 1ull);
+            float kk = (lane < a.n_group && !taken) ? gscore : NEG_INF;
+            int id = (lane < a.n_group && !taken) ? lane : INT_MAX;
+            wave_argmax(kk, id);
+            if (id != INT_MAX) kept |= 1ull << id;
+        }
+#pragma unroll
+        for (int i = 0; i < EPL; ++i) {
+            const int e = lane * EPL + i;
+            if (e < E && !((kept >> (e / gs)) & 1ull)) key[i] = NEG_INF;
+        }
+    }
+
+    // k rounds of wave argmax; lane j keeps slot j's expert and value
+    uint32_t taken = 0;
+    int my_e = -1;
+    float my_v = 0.0f;
+    for (int j = 0; j < k; ++j) {
+        float bk = NEG_INF;
+        int be = INT_MAX;
+#pragma unroll
+        for (int i = 0; i < EPL; ++i) {
+            const int e = lane * EPL + i;
+            const bool cand = e < E && !((taken >> i) & 1u) && key[i] != NEG_INF;
+            if (cand && ranks_before(key[i], e, bk, be)) { bk = key[i]; be = e; }
+        }
+        wave_argmax(bk, be);
+        if (be == INT_MAX) break;                 // cannot happen for validated k
+        float v = 0.0f;
+        const int owner = be / EPL;
+        if (lane == owner) {
+#pragma unroll
+            for (int i = 0; i < EPL; ++i)
+                if (i == be - owner * EPL) { v = val[i]; taken |= 1u << i; }
+        }
+        v = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), owner));
+        if (lane == j) { my_e = be; my_v = v; }
+    }
+
+    float wj = 0.0f;
+    if (lane < k) {
+        if (a.mode == MOE_ROUTER_SOFTMAX_TOPK) wj = expf(my_v - lmax) / denom;
+        else wj = my_v;
+    }
+    if (a.mode == MOE_ROUTER_SOFTMAX_TOPK) {
+        if (a.renorm) {
+            const float tot = wave_sum_all(lane < k ? wj : 0.0f);
+            wj = wj / tot;
+        }
+    } else {
+        const float tot = wave_sum_all(lane < k ? wj : 0.0f);
+        wj = wj / tot * a.rsf;
+    }
+    *out_e = my_e;
+    *out_w = wj;
+}
+
+// experts per lane for the top-k wave: the smallest power of two with 64*EPL >= E
+inline int topk_epl(int E) { return E <= 64 ? 1 : E <= 128 ? 2 : E <= 256 ? 4 : E <= 512 ? 8 : 16; }
+
+}  // namespace moe
