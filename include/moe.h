@@ -38,18 +38,21 @@
  *     weights are scale * code.
  *   - Weight layout ("lane-tiled"; written by moe_quantize_weights, read by
  *     every expert kernel). A matrix of N rows (outputs) and K columns
- *     (inputs), N % 32 == 0, K % 64 == 0, is cut into 32-row tiles, tile t
- *     holding rows 32t .. 32t+31. Inside a tile, "lane" l = nl + 16h
- *     (0 <= nl < 16, 0 <= h < 4) owns, for each group g, the codes of
- *     k = 32g + 8h .. 32g + 8h + 7 of rows 32t + nl and 32t + 16 + nl:
- *       int8 codes   byte ((t*G + g)*64 + l)*16 + 8*(row >= 16) + (k % 8),
- *                    G = K/32 (row = row % 32; K*N bytes in all);
- *       int4 codes   dword ((t*P + g/2)*64 + l)*4 + 2*(g % 2) + (row >= 16),
- *                    P = K/64, nibble k % 8 (K*N/2 bytes in all);
- *       scales fp32  float (t*P + g/2)*64 + 4*nl + 2*(g % 2) + (row >= 16)
+ *     (inputs), N % 32 == 0, K % 64 == 0, is cut into NT = N/32 tiles of 32
+ *     rows, tile t holding rows 32t .. 32t+31. Inside a tile, "lane"
+ *     l = nl + 16h (0 <= nl < 16, 0 <= h < 4) owns, for each group g, the
+ *     codes of k = 32g + 8h .. 32g + 8h + 7 of rows 32t + nl and
+ *     32t + 16 + nl. With G = K/32, P = K/64 and r = row % 32:
+ *       int8 codes   byte ((g*NT + t)*64 + l)*16 + 8*(r >= 16) + (k % 8)
+ *                    (K*N bytes in all);
+ *       int4 codes   dword ((g/2*NT + t)*64 + l)*4 + 2*(g % 2) + (r >= 16),
+ *                    nibble k % 8 (K*N/2 bytes in all);
+ *       scales fp32  float (t*P + g/2)*64 + 4*nl + 2*(g % 2) + (r >= 16)
  *                    (K*N/32 floats in all).
- *     A wave thus reads 1 KB of operands per 16-byte load, and one scale load
- *     covers two groups.
+ *     Codes are group-major, so the waves that stream the tiles of a matrix
+ *     side by side read neighbouring kilobytes; scales are tile-major, so one
+ *     16-byte load per lane brings a wave the scales of four group pairs. A
+ *     wave reads 1 KB of operands per 16-byte load.
  *   - Results are deterministic: the same inputs give bitwise equal outputs
  *     (no floating-point atomics anywhere).
  */
@@ -158,9 +161,10 @@ size_t moe_workspace_size(int32_t T, int32_t k, int32_t E, int32_t d, int32_t d_
 
 /* Group-32 symmetric weight quantiser ("mtlm-7m-base", section "Files";
  * "Show HN: Getting GLM-5.2 running on my slow computer", section "What's implemented": int8 / packed int4).
- *   w      device fp32 [rows, cols] row-major, rows % 32 == 0, cols % 64 == 0
- *          (a stack of matrices of the same cols, each with rows % 32 == 0,
- *          may be passed as one call)
+ *   w      device fp32 [rows, cols] row-major, cols % 64 == 0: a stack of
+ *          rows / matrix_rows matrices of matrix_rows rows each
+ *          (matrix_rows % 32 == 0, rows % matrix_rows == 0), each written
+ *          in the layout above, one after the other
  *   format MOE_W_INT8_G32 -> q holds rows*cols bytes;
  *          MOE_W_INT4_G32 -> q holds rows*cols/2 bytes
  *   s      device fp32, rows*cols/32 floats
@@ -169,8 +173,8 @@ size_t moe_workspace_size(int32_t T, int32_t k, int32_t E, int32_t d, int32_t d_
  * clamp(round_half_even(w/s), -qmax, qmax) (fp32 divide); amax == 0 gives
  * s = 0 and codes 0.
  */
-moe_status moe_quantize_weights(const float* w, int64_t rows, int32_t cols, int32_t format,
-                                void* q, float* s, hipStream_t stream);
+moe_status moe_quantize_weights(const float* w, int64_t rows, int32_t cols, int32_t matrix_rows,
+                                int32_t format, void* q, float* s, hipStream_t stream);
 
 /* Q8_0-style activation quantiser ("Show HN: Getting GLM-5.2 running on my slow computer", section "What's
  * implemented": Q8_0-style int8 activations).

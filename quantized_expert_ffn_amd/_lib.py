@@ -64,7 +64,7 @@ _SZ = ctypes.c_size_t
 
 _SIGNATURES = {
     "moe_workspace_size": (_SZ, [_I32, _I32, _I32, _I32, _I32, _I32, _I32]),
-    "moe_quantize_weights": (_I32, [_P, _I64, _I32, _I32, _P, _P, _P]),
+    "moe_quantize_weights": (_I32, [_P, _I64, _I32, _I32, _I32, _P, _P, _P]),
     "moe_quantize_q8_0": (_I32, [_P, _I64, _I32, _P, _P, _P]),
     "moe_route": (_I32, [_P, _I32, _I32, _P, ctypes.POINTER(RouterParams), _P, _P, _P, _SZ, _P]),
     "moe_dispatch": (_I32, [_P, _I32, _I32, _I32, _P, _P, _P, _P, _P, _SZ, _P]),
@@ -206,9 +206,13 @@ def moe_workspace_size(T: int, k: int, E: int, d: int, d_ff: int, act_mode: int,
     return int(load().moe_workspace_size(T, k, E, d, d_ff, act_mode, int(bool(has_shared))))
 
 
-def moe_quantize_weights(w: torch.Tensor, fmt: int, q: torch.Tensor, s: torch.Tensor, stream=None) -> None:
+def moe_quantize_weights(w: torch.Tensor, fmt: int, q: torch.Tensor, s: torch.Tensor, stream=None,
+                         matrix_rows: Optional[int] = None) -> None:
+    """w: one matrix [N, K] or a stack [..., N, K]; each N-row matrix is
+    written in the lane-tiled layout, one after the other."""
     rows = w.numel() // w.shape[-1]
-    _check(load().moe_quantize_weights(_ptr(w, torch.float32, "w"), rows, w.shape[-1], fmt, _ptr(q, None, "q"),
+    mr = int(matrix_rows) if matrix_rows is not None else w.shape[-2]
+    _check(load().moe_quantize_weights(_ptr(w, torch.float32, "w"), rows, w.shape[-1], mr, fmt, _ptr(q, None, "q"),
                                        _ptr(s, torch.float32, "s"), _stream(stream)), "moe_quantize_weights")
 
 

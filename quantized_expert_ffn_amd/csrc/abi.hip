@@ -295,19 +295,21 @@ size_t moe_workspace_size(int32_t T, int32_t k, int32_t E, int32_t d, int32_t d_
     return moe::ws_layout(T, k, E, d, d_ff, act_mode, has_shared ? 1 : 0).total;
 }
 
-moe_status moe_quantize_weights(const float* w, int64_t rows, int32_t cols, int32_t format, void* q, float* s,
-                                hipStream_t stream) {
+moe_status moe_quantize_weights(const float* w, int64_t rows, int32_t cols, int32_t matrix_rows, int32_t format,
+                                void* q, float* s, hipStream_t stream) {
     MOE_REQUIRE(rows >= 0 && cols > 0, MOE_ERR_INVALID_ARG, "bad shape [%lld, %d]", (long long)rows, cols);
+    MOE_REQUIRE(matrix_rows > 0 && rows % matrix_rows == 0, MOE_ERR_INVALID_ARG,
+                "rows = %lld is not a whole number of matrices of %d rows", (long long)rows, matrix_rows);
     MOE_REQUIRE(cols % (2 * moe::kGroup) == 0, MOE_ERR_UNSUPPORTED,
                 "cols = %d is not a multiple of 64 (pairs of groups)", cols);
-    MOE_REQUIRE(rows % moe::kTile == 0, MOE_ERR_UNSUPPORTED, "rows = %lld is not a multiple of 32 (tiled layout)",
-                (long long)rows);
+    MOE_REQUIRE(matrix_rows % moe::kTile == 0, MOE_ERR_UNSUPPORTED,
+                "matrix_rows = %d is not a multiple of 32 (tiled layout)", matrix_rows);
     MOE_REQUIRE(format == MOE_W_INT8_G32 || format == MOE_W_INT4_G32, MOE_ERR_INVALID_ARG, "unknown format %d",
                 format);
     if (rows == 0) return ok();
     MOE_REQUIRE(w && q && s, MOE_ERR_INVALID_ARG, "NULL tensor argument");
     MOE_REQUIRE(aligned16(w) && aligned16(q), MOE_ERR_INVALID_ARG, "w and q must be 16-byte aligned");
-    MOE_HIP(moe::launch_quantize_weights(w, rows, cols, format == MOE_W_INT8_G32 ? 8 : 4, q, s, stream),
+    MOE_HIP(moe::launch_quantize_weights(w, rows, cols, matrix_rows, format == MOE_W_INT8_G32 ? 8 : 4, q, s, stream),
             "weight quantiser");
     return ok();
 }

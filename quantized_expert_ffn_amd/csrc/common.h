@@ -97,36 +97,43 @@ inline WsLayout ws_layout(int T, int k, int E, int d, int I, int act_mode, int h
 
 // ---------------------------------------------------------------------------
 // Weight layout in HBM. A matrix of N rows (outputs) and K columns (reduction
-// axis), N % 32 == 0 and K % 64 == 0, is cut into 32-row tiles; G = K / 32
-// groups, P = G / 2 group pairs. Inside a tile the data is ordered by lane of
-// a 64-lane wave: lane l = nl + 16 h (nl < 16, h < 4) holds, for one group,
-// the 8 codes k = 8h .. 8h+7 of rows nl and 16 + nl -- exactly its part of
-// the B operands of two 16x16x32 matrix-core products (rows 0-15, 16-31).
-//   int8 codes:  block (tile, group) of 1 KB; lane l's 16 bytes at l*16:
-//                [row nl: 8 codes][row 16+nl: 8 codes]
-//   int4 codes:  block (tile, pair) of 1 KB; lane l's 16 bytes at l*16, four
-//                dwords of 8 nibbles (low nibble = lower k):
+// axis), N % 32 == 0 and K % 64 == 0, is cut into NT = N/32 tiles of 32
+// rows; G = K / 32 groups, P = G / 2 group pairs. Inside a tile the data is
+// ordered by lane of a 64-lane wave: lane l = nl + 16 h (nl < 16, h < 4)
+// holds, for one group, the 8 codes k = 8h .. 8h+7 of rows nl and 16 + nl --
+// exactly its part of the B operands of two 16x16x32 matrix-core products
+// (rows 0-15, 16-31).
+//   int8 codes:  1 KB blocks, block (group g, tile t) at (g*NT + t) KB; lane
+//                l's 16 bytes at l*16: [row nl: 8 codes][row 16+nl: 8 codes]
+//   int4 codes:  1 KB blocks, block (pair p, tile t) at (p*NT + t) KB; lane
+//                l's 16 bytes at l*16, four dwords of 8 nibbles (low nibble =
+//                lower k): [row nl, g0][row 16+nl, g0][row nl, g1][row 16+nl, g1]
+//   scales fp32: 64-float blocks, block (tile t, pair p) at (t*P + p)*64;
+//                lane quad nl at nl*4:
 //                [row nl, g0][row 16+nl, g0][row nl, g1][row 16+nl, g1]
-//   scales fp32: block (tile, pair) of 64 floats; lane quad nl at nl*4:
-//                [row nl, g0][row 16+nl, g0][row nl, g1][row 16+nl, g1]
-// (g0 = 2p, g1 = 2p + 1.) One 16-byte load per lane thus moves 1 KB of a
-// wave's operands, and one scale load covers two groups.
+// (g0 = 2p, g1 = 2p + 1.) Codes are group- (pair-) major, so the waves
+// streaming the tiles of one matrix side by side read neighbouring
+// kilobytes; scales are tile-major, so one 16-byte load per lane brings a
+// wave the scales of four consecutive pairs. A stack of matrices of the same
+// shape is stored matrix after matrix.
 // ---------------------------------------------------------------------------
 constexpr int kTile = 32;
 
-// byte offset of the 8 int8 codes (row, k = 8*(k8) .. +7), k8 = k / 8 in 0..K/8
-__host__ __device__ __forceinline__ size_t int8_code_offset(size_t row, size_t k8, size_t G) {
+// byte offset, inside one matrix of NT tiles, of the 8 int8 codes (row,
+// k = 8*k8 .. +7)
+__host__ __device__ __forceinline__ size_t int8_code_offset(size_t row, size_t k8, size_t NT) {
     const size_t g = k8 >> 2, h = k8 & 3, r = row % kTile;
-    return ((row / kTile) * G + g) * 1024 + ((r & 15) + 16 * h) * 16 + (r >> 4) * 8;
+    return (g * NT + row / kTile) * 1024 + ((r & 15) + 16 * h) * 16 + (r >> 4) * 8;
 }
 
-// byte offset of the dword holding the 8 int4 codes (row, k = 8*k8 .. +7)
-__host__ __device__ __forceinline__ size_t int4_code_offset(size_t row, size_t k8, size_t G) {
+// byte offset, inside one matrix of NT tiles, of the dword holding the 8 int4
+// codes (row, k = 8*k8 .. +7)
+__host__ __device__ __forceinline__ size_t int4_code_offset(size_t row, size_t k8, size_t NT) {
     const size_t g = k8 >> 2, h = k8 & 3, r = row % kTile;
-    return ((row / kTile) * (G / 2) + (g >> 1)) * 1024 + ((r & 15) + 16 * h) * 16 + ((g & 1) * 2 + (r >> 4)) * 4;
+    return ((g >> 1) * NT + row / kTile) * 1024 + ((r & 15) + 16 * h) * 16 + ((g & 1) * 2 + (r >> 4)) * 4;
 }
 
-// float index of the scale of (row, group g)
+// float index, inside one matrix, of the scale of (row, group g)
 __host__ __device__ __forceinline__ size_t scale_index(size_t row, size_t g, size_t G) {
     const size_t r = row % kTile;
     return ((row / kTile) * (G / 2) + (g >> 1)) * 64 + (r & 15) * 4 + (g & 1) * 2 + (r >> 4);

@@ -102,13 +102,14 @@ struct GemvArgs {
 
 constexpr int kMaxGemvGroups = 256;   // K <= 8192
 
-// Block: KS waves splitting the group pairs of the reduction axis (wave ks:
-// pairs ks, ks + KS, ...). Each wave covers two 32-row matrix tiles: gate and
-// up of tile blockIdx.x (GATEUP), or down tiles 2 blockIdx.x and +1. NB pairs
-// of groups are in flight per wave: weight codes (HBM), scales and
-// activation fragments (L2) alike; loads retire in order, so every stream
-// keeps the same depth.
-template <int FMT, bool GATEUP, int NB, int KS>
+// Block: KS waves splitting the group pairs of the reduction axis into
+// contiguous runs. Each wave covers two 32-row matrix tiles: gate and up of
+// tile blockIdx.x (GATEUP), or down tiles 2 blockIdx.x and +1. Two pairs of
+// groups are in flight per wave, weight codes (HBM) and activation
+// fragments (L2) alike; loads retire in order, so both streams keep the same
+// depth. Scales come four pairs per load and reach their lanes through
+// ds_bpermute.
+template <int FMT, bool GATEUP, int KS>
 __global__ __launch_bounds__(64 * KS) void gemv_kernel(const GemvArgs a) {
     constexpr int kCL = FMT == MOE_W_INT8_G32 ? 2 : 1;   // 16-byte code loads per tile per pair
     __shared__ float pwtab[kMaxGemvGroups];
@@ -139,13 +140,17 @@ __global__ __launch_bounds__(64 * KS) void gemv_kernel(const GemvArgs a) {
         const float* sbase = (is_shared ? a.ss[m] : a.s[m]) + eo * a.s_stride;
         rq[t] = __builtin_amdgcn_make_buffer_rsrc((void*)qbase, 0, (int)a.q_stride, 0x00020000);
         rs[t] = __builtin_amdgcn_make_buffer_rsrc((void*)sbase, 0, (int)(a.s_stride * 4), 0x00020000);
-        q_voff[t] = tile[t] * (FMT == MOE_W_INT8_G32 ? G : P) * 1024 + lane * 16;
-        s_voff[t] = (tile[t] * P * 64 + nl * 4) * 4;
+        q_voff[t] = tile[t] * 1024 + lane * 16;
+        // four consecutive pairs' scale blocks are 1 KB: lane nl + 16q reads
+        // pair q's 16 bytes for rows nl, 16 + nl
+        s_voff[t] = tile[t] * P * 256 + lane * 16;
     }
     const int a_bytes = a.a_rows * K * 2;
     const __amdgpu_buffer_rsrc_t rah = __builtin_amdgcn_make_buffer_rsrc((void*)a.ahi, 0, a_bytes, 0x00020000);
     const __amdgpu_buffer_rsrc_t ral = __builtin_amdgcn_make_buffer_rsrc((void*)a.alo, 0, a_bytes, 0x00020000);
-    const int n_my = (P - ks + KS - 1) / KS;
+    // wave ks takes a contiguous run of pairs [c0, c0 + n_my)
+    const int c0 = ks * P / KS;
+    const int n_my = (ks + 1) * P / KS - c0;
     if constexpr (GATEUP) {
         for (int i = threadIdx.x; i < G; i += 64 * KS) pwtab[i] = a.apow[i];
     }
@@ -173,30 +178,48 @@ __global__ __launch_bounds__(64 * KS) void gemv_kernel(const GemvArgs a) {
 #pragma unroll
             for (int r = 0; r < 2; ++r) acc[t][r] = v4f{0.f, 0.f, 0.f, 0.f};
 
-        uint4 wq[NB][2][kCL];
-        uint4 wsc[NB][2];
-        v8h xh[NB][2], xl[NB][2];
+        // ring of NB = 2 pairs (codes, activation parts) and of two scale
+        // quads (four pairs each: the current one and the next)
+        uint4 wq[2][2][kCL];
+        v8h xh[2][2], xl[2][2];
+        uint4 sq_cur[2], sq_next[2];
         auto load = [&](int sp, int j) {
             // past the end: the last pair again (L2-resident), so that every
             // step issues the same loads and waits stay counted
-            const int p = ks + KS * (j < n_my ? j : n_my - 1);
+            const int p = c0 + (j < n_my ? j : n_my - 1);
 #pragma unroll
-            for (int t = 0; t < 2; ++t) {
+            for (int t = 0; t < 2; ++t)
 #pragma unroll
                 for (int c = 0; c < kCL; ++c)
                     wq[sp][t][c] = __builtin_bit_cast(
-                        uint4, __builtin_amdgcn_raw_buffer_load_b128(rq[t], q_voff[t], (kCL * p + c) * 1024, 0));
-                wsc[sp][t] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rs[t], s_voff[t], p * 256, 0));
-            }
+                        uint4, __builtin_amdgcn_raw_buffer_load_b128(rq[t], q_voff[t], (kCL * p + c) * n_tiles * 1024, 0));
 #pragma unroll
             for (int gi = 0; gi < 2; ++gi) {
                 xh[sp][gi] = __builtin_bit_cast(v8h, __builtin_amdgcn_raw_buffer_load_b128(rah, a_voff, (2 * p + gi) * 64, 0));
                 xl[sp][gi] = __builtin_bit_cast(v8h, __builtin_amdgcn_raw_buffer_load_b128(ral, a_voff, (2 * p + gi) * 64, 0));
             }
         };
-        auto step = [&](int jj, int j) {
-            const int p = ks + KS * j;
+        // scales of pairs c0 + 4q .. + 3 (those past the run are read but unused)
+        auto load_quad = [&](int q) {
+#pragma unroll
+            for (int t = 0; t < 2; ++t)
+                sq_next[t] = __builtin_bit_cast(
+                    uint4, __builtin_amdgcn_raw_buffer_load_b128(rs[t], s_voff[t], (c0 + 4 * q) * 256, 0));
+        };
+        // pair j of the run, from ring slot jj; its scales sit in lane row r
+        // (= j % 4) of the current quad
+        auto step = [&](int jj, int j, int r) {
+            const int p = c0 + j;
             const float pw0 = pwtab[2 * p], pw1 = pwtab[2 * p + 1];
+            const int src = (nl + 16 * r) * 4;
+            float sc[2][4];
+#pragma unroll
+            for (int t = 0; t < 2; ++t) {
+                sc[t][0] = __int_as_float(__builtin_amdgcn_ds_bpermute(src, (int)sq_cur[t].x));
+                sc[t][1] = __int_as_float(__builtin_amdgcn_ds_bpermute(src, (int)sq_cur[t].y));
+                sc[t][2] = __int_as_float(__builtin_amdgcn_ds_bpermute(src, (int)sq_cur[t].z));
+                sc[t][3] = __int_as_float(__builtin_amdgcn_ds_bpermute(src, (int)sq_cur[t].w));
+            }
 #pragma unroll
             for (int gi = 0; gi < 2; ++gi) {
                 const float pw = gi ? pw1 : pw0;
@@ -216,9 +239,8 @@ __global__ __launch_bounds__(64 * KS) void gemv_kernel(const GemvArgs a) {
                     v4f d1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(xh[jj][gi], b1, v4f{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
                     d0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(xl[jj][gi], b0, d0, 0, 0, 0);
                     d1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(xl[jj][gi], b1, d1, 0, 0, 0);
-                    const uint4 sc = wsc[jj][t];
-                    const float f0 = __builtin_bit_cast(float, gi ? sc.z : sc.x) * pw;
-                    const float f1 = __builtin_bit_cast(float, gi ? sc.w : sc.y) * pw;
+                    const float f0 = sc[t][2 * gi] * pw;
+                    const float f1 = sc[t][2 * gi + 1] * pw;
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
                         acc[t][0][i] = fmaf(d0[i], f0, acc[t][0][i]);
@@ -227,25 +249,38 @@ __global__ __launch_bounds__(64 * KS) void gemv_kernel(const GemvArgs a) {
                 }
             }
         };
-        // whole rounds of NB steps: every step computes its ring slot and
-        // refills it NB pairs ahead; then the last n_my % NB steps, no loads
-#pragma unroll
-        for (int jj = 0; jj < NB; ++jj) load(jj, jj);
+        // rounds of four pairs: each step computes its ring slot and refills
+        // it two pairs ahead; the scale quad of the next round is issued at
+        // the start of this one. The refills stay where they are: issued
+        // later, their waits would cover the younger loads too (loads retire
+        // in order).
+        // the first quad goes out first: at the top of every round the quad
+        // it waits for is then older than at least two pairs of loads
+        load_quad(0);
+        load(0, 0);
+        load(1, 1);
         int j0 = 0;
-        for (; j0 + NB <= n_my; j0 += NB) {
+        for (; j0 + 4 <= n_my; j0 += 4) {
+            sq_cur[0] = sq_next[0];
+            sq_cur[1] = sq_next[1];
+            __builtin_amdgcn_sched_barrier(0);
+            load_quad(j0 / 4 + 1);
 #pragma unroll
-            for (int jj = 0; jj < NB; ++jj) {
-                step(jj, j0 + jj);
-                // keep the refill here: issued later, its wait would cover
-                // the younger slots' loads too (they retire in order)
+            for (int r = 0; r < 4; ++r) {
                 __builtin_amdgcn_sched_barrier(0);
-                load(jj, j0 + jj + NB);
+                step(r & 1, j0 + r, r);
                 __builtin_amdgcn_sched_barrier(0);
+                load(r & 1, j0 + r + 2);
             }
         }
-#pragma unroll
-        for (int jj = 0; jj < NB - 1; ++jj)
-            if (j0 + jj < n_my) step(jj, j0 + jj);
+        // the last n_my % 4 pairs
+        sq_cur[0] = sq_next[0];
+        sq_cur[1] = sq_next[1];
+        const int rest = n_my - j0;
+        if (rest > 0) step(0, j0, 0);
+        if (rest > 2) load(0, j0 + 2);
+        if (rest > 1) step(1, j0 + 1, 1);
+        if (rest > 2) step(0, j0 + 2, 2);
 
         // sum the KS partial results of each output in wave order
         if constexpr (KS > 1) {
@@ -376,7 +411,7 @@ hipError_t launch_gemv(const moe_experts& routed, const moe_experts* shared, boo
     const int bx = gateup ? tiles : (tiles + 1) / 2;
     const int ks = choose_ks(max_slots, bx, a.K / (2 * kGroup));
     const dim3 grid(bx, max_slots);
-#define MOE_GEMV(FMT, GU, KSV) launch_timed(gemv_kernel<FMT, GU, 2, KSV>, grid, dim3(64 * KSV), st, ev0, ev1, a)
+#define MOE_GEMV(FMT, GU, KSV) launch_timed(gemv_kernel<FMT, GU, KSV>, grid, dim3(64 * KSV), st, ev0, ev1, a)
 #define MOE_GEMV_KS(FMT, GU)                \
     if (ks == 1) MOE_GEMV(FMT, GU, 1);      \
     else if (ks == 2) MOE_GEMV(FMT, GU, 2); \

@@ -88,7 +88,7 @@ __global__ __launch_bounds__(256) void q8_mfma_kernel(const MfmaArgs a) {
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wm = wave & 1, wn = wave >> 1;
-    const int K = a.K, N = a.N, G = K / kGroup;
+    const int K = a.K, N = a.N, G = K / kGroup, NT = N / kTile;
     const int n0 = blockIdx.x * (GATEUP ? kBRows / 2 : kBRows);
     const int row_bytes = FMT == MOE_W_INT8_G32 ? K : K / 2;
     constexpr float kWScale = FMT == MOE_W_INT8_G32 ? 1.0f : 0.0625f;
@@ -154,13 +154,13 @@ __global__ __launch_bounds__(256) void q8_mfma_kernel(const MfmaArgs a) {
                 const int bt = blk >> 2, g = blk & 3;
                 b_tile(bt, q, sp, tile);
                 const bool ok = tile * kTile < N && g0 + g < G;
-                rb[r] = ok ? *reinterpret_cast<const uint4*>(q + ((size_t)tile * G + g0 + g) * 1024 + j * 16)
+                rb[r] = ok ? *reinterpret_cast<const uint4*>(q + ((size_t)(g0 + g) * NT + tile) * 1024 + j * 16)
                            : make_uint4(0, 0, 0, 0);
             } else {
                 const int bt = blk >> 1, pr = g0 / 2 + (blk & 1);
                 b_tile(bt, q, sp, tile);
                 const bool ok = tile * kTile < N && pr < G / 2;
-                rb[r] = ok ? *reinterpret_cast<const uint4*>(q + ((size_t)tile * (G / 2) + pr) * 1024 + j * 16)
+                rb[r] = ok ? *reinterpret_cast<const uint4*>(q + ((size_t)pr * NT + tile) * 1024 + j * 16)
                            : make_uint4(0, 0, 0, 0);
             }
         }

@@ -12,16 +12,21 @@
 namespace moe {
 
 // One thread per group of 32 consecutive weights of one row; the codes and the
-// scale go to their places in the lane-ordered tile layout (common.h).
+// scale go to their places in the lane-tiled layout (common.h) of the row's
+// matrix (a stack of matrices of matrix_rows rows each).
 template <int BITS>
 __global__ __launch_bounds__(256) void quantize_weights_kernel(const float* __restrict__ w,
-                                                               int64_t n_groups, int G,
+                                                               int64_t n_groups, int G, int matrix_rows,
                                                                uint8_t* __restrict__ q,
                                                                float* __restrict__ s) {
     const int64_t gi = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (gi >= n_groups) return;
     const float4* src = reinterpret_cast<const float4*>(w + gi * kGroup);
-    const size_t row = (size_t)(gi / G), g = (size_t)(gi % G);
+    const size_t grow = (size_t)(gi / G), g = (size_t)(gi % G);
+    const size_t mat = grow / matrix_rows, row = grow % matrix_rows, NT = matrix_rows / kTile;
+    const size_t mat_elems = (size_t)matrix_rows * G * kGroup;
+    q += mat * (BITS == 8 ? mat_elems : mat_elems / 2);
+    s += mat * (size_t)matrix_rows * G;
     float v[kGroup];
 #pragma unroll
     for (int i = 0; i < kGroup / 4; ++i) {
@@ -54,12 +59,12 @@ __global__ __launch_bounds__(256) void quantize_weights_kernel(const float* __re
                 lo |= (uint32_t)(code[8 * h + j] & 0xff) << (8 * j);
                 hi |= (uint32_t)(code[8 * h + 4 + j] & 0xff) << (8 * j);
             }
-            *reinterpret_cast<uint2*>(q + int8_code_offset(row, k8, (size_t)G)) = make_uint2(lo, hi);
+            *reinterpret_cast<uint2*>(q + int8_code_offset(row, k8, NT)) = make_uint2(lo, hi);
         } else {
             uint32_t p = 0;
 #pragma unroll
             for (int j = 0; j < 8; ++j) p |= (uint32_t)(code[8 * h + j] & 0xf) << (4 * j);
-            *reinterpret_cast<uint32_t*>(q + int4_code_offset(row, k8, (size_t)G)) = p;
+            *reinterpret_cast<uint32_t*>(q + int4_code_offset(row, k8, NT)) = p;
         }
     }
 }
@@ -102,16 +107,18 @@ __global__ __launch_bounds__(256) void quantize_q8_0_kernel(const float* __restr
     dst[1] = make_uint4(packed[4], packed[5], packed[6], packed[7]);
 }
 
-hipError_t launch_quantize_weights(const float* w, int64_t rows, int cols, int bits, void* q, float* s,
-                                   hipStream_t st) {
+hipError_t launch_quantize_weights(const float* w, int64_t rows, int cols, int matrix_rows, int bits, void* q,
+                                   float* s, hipStream_t st) {
     const int G = cols / kGroup;
     const int64_t n_groups = rows * G;
     if (n_groups == 0) return hipSuccess;
     const dim3 grid((unsigned)((n_groups + 255) / 256));
     if (bits == 8)
-        hipLaunchKernelGGL(quantize_weights_kernel<8>, grid, dim3(256), 0, st, w, n_groups, G, (uint8_t*)q, s);
+        hipLaunchKernelGGL(quantize_weights_kernel<8>, grid, dim3(256), 0, st, w, n_groups, G, matrix_rows,
+                           (uint8_t*)q, s);
     else
-        hipLaunchKernelGGL(quantize_weights_kernel<4>, grid, dim3(256), 0, st, w, n_groups, G, (uint8_t*)q, s);
+        hipLaunchKernelGGL(quantize_weights_kernel<4>, grid, dim3(256), 0, st, w, n_groups, G, matrix_rows,
+                           (uint8_t*)q, s);
     return hipGetLastError();
 }
 

@@ -137,11 +137,13 @@ def test_route_dispatch_combine_validation(lib):
     assert lib.moe_combine(FAKE, FAKE, FAKE, None, 0, 2, 64, FAKE, None) == OK
     assert lib.moe_combine(FAKE, FAKE, FAKE, None, 4, 2, 66, FAKE, None) == UNSUPPORTED
     assert lib.moe_combine(None, FAKE, FAKE, None, 4, 2, 64, FAKE, None) == INVALID
-    assert lib.moe_quantize_weights(FAKE, 32, 48, 0, FAKE, FAKE, None) == UNSUPPORTED   # cols % 32
-    assert lib.moe_quantize_weights(FAKE, 32, 96, 1, FAKE, FAKE, None) == UNSUPPORTED   # cols % 64
-    assert lib.moe_quantize_weights(FAKE, 40, 64, 0, FAKE, FAKE, None) == UNSUPPORTED   # rows % 32 (tiles)
-    assert lib.moe_quantize_weights(FAKE, 32, 64, 3, FAKE, FAKE, None) == INVALID
-    assert lib.moe_quantize_weights(FAKE, 0, 64, 1, FAKE, FAKE, None) == OK
+    assert lib.moe_quantize_weights(FAKE, 32, 48, 32, 0, FAKE, FAKE, None) == UNSUPPORTED   # cols % 32
+    assert lib.moe_quantize_weights(FAKE, 32, 96, 32, 1, FAKE, FAKE, None) == UNSUPPORTED   # cols % 64
+    assert lib.moe_quantize_weights(FAKE, 40, 64, 40, 0, FAKE, FAKE, None) == UNSUPPORTED   # matrix rows % 32
+    assert lib.moe_quantize_weights(FAKE, 96, 64, 64, 0, FAKE, FAKE, None) == INVALID       # not whole matrices
+    assert lib.moe_quantize_weights(FAKE, 64, 64, 0, 0, FAKE, FAKE, None) == INVALID
+    assert lib.moe_quantize_weights(FAKE, 32, 64, 32, 3, FAKE, FAKE, None) == INVALID
+    assert lib.moe_quantize_weights(FAKE, 0, 64, 32, 1, FAKE, FAKE, None) == OK
     assert lib.moe_quantize_q8_0(FAKE, 4, 40, FAKE, FAKE, None) == UNSUPPORTED
     e = _experts()
     assert lib.moe_expert_ffn(FAKE, 4, 9, ctypes.byref(e), FAKE, FAKE, FAKE, 0, FAKE, FAKE, 1 << 30, None) == INVALID
@@ -167,8 +169,8 @@ def test_untile_helpers_invert_the_documented_layout(fmt):
     against the layout formulas of include/moe.h, written out element by element."""
     from gpu_common import untile_codes, untile_scales
     rng = np.random.default_rng(3)
-    N, K = 64, 128
-    G, P = K // 32, K // 64
+    N, K = 96, 128
+    G, P, NT = K // 32, K // 64, N // 32
     codes = rng.integers(-7 if fmt == "int4" else -127, 8 if fmt == "int4" else 128, (N, K))
     scales = rng.standard_normal((N, G)).astype(np.float32)
     sflat = np.zeros(N * G, np.float32)
@@ -186,12 +188,12 @@ def test_untile_helpers_invert_the_documented_layout(fmt):
                 ks = range(32 * g + 8 * h, 32 * g + 8 * h + 8)
                 if fmt == "int8":
                     for k in ks:
-                        qflat[((t * G + g) * 64 + lane) * 16 + 8 * half + k % 8] = codes[row, k]
+                        qflat[((g * NT + t) * 64 + lane) * 16 + 8 * half + k % 8] = codes[row, k]
                 else:
                     word = 0
                     for k in ks:
                         word |= (int(codes[row, k]) & 0xF) << (4 * (k % 8))
-                    qflat[((t * P + g // 2) * 64 + lane) * 4 + 2 * (g % 2) + half] = word
+                    qflat[((g // 2 * NT + t) * 64 + lane) * 4 + 2 * (g % 2) + half] = word
     from oracle import quant as oquant
     stored = codes.astype(np.int8) if fmt == "int8" else oquant.pack_int4(codes.astype(np.int8))
     assert np.array_equal(untile_codes(qflat, N, K, fmt), stored)
