@@ -23,8 +23,10 @@ LIBDIR = os.path.join(PKG, "lib")
 LIB = os.path.join(LIBDIR, "libmoe.so")
 
 ARCH = "gfx950"
-# Packed fp32 vector instructions are kept out of every kernel.
-DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+# Packed fp32 vector instructions are kept out of every kernel; matrix-core
+# results go to ordinary VGPRs (the epilogues consume them with VALU ops,
+# which would otherwise first copy them out of AGPRs).
+DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", "-mllvm", "-amdgpu-mfma-vgpr-form=1"]
 CFLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-I", INCLUDE, "-I", CSRC,
           "-Wall", "-Wno-unused-function", "-Wno-unused-variable"] + DEVICE_FLAGS
 

@@ -11,9 +11,11 @@
 // the high half of the byte), so the matrix core sees int8 codes; the factor
 // 16 is removed exactly by folding 1/16 into the weight scale.
 //
-// Block tile: 64 rows (tokens of one expert) x 128 weight rows, staged
-// through LDS in steps of 4 groups (128 k), double buffered. Four waves in
-// 2 x 2; each wave owns 32 rows and two 32-column MFMA tiles.
+// Block tile: 64 rows (tokens of one expert) x 128 weight rows (four 32-row
+// tiles), staged through LDS in steps of 4 groups (128 k), double buffered,
+// by direct global -> LDS loads: no staging registers, the weight blocks land
+// exactly as they are stored. Four waves in 2 x 2; each wave owns 32 rows
+// and two 32-column MFMA tiles.
 //   gate/up kernel: the two tiles are gate and up of the same 32 outputs, so
 //     SwiGLU and the Q8_0 quantisation of H (32 outputs = one group) happen
 //     in registers; H leaves as int8 codes + one fp32 scale per 32.
@@ -28,16 +30,24 @@ namespace moe {
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef int v16i __attribute__((ext_vector_type(16)));
 
-constexpr int kBM = kTileRows;       // 64 rows per tile
-constexpr int kBRows = 128;          // weight rows per block
-constexpr int kGroupsPerStage = 4;   // 128 k per LDS stage
-constexpr int kStageK = kGroupsPerStage * kGroup;
-constexpr int kLdsRow = kStageK + 16;              // padded row pitch in bytes
-constexpr int kLdsA = kBM * kLdsRow;               // 9216
-constexpr int kLdsB = kBRows * kLdsRow;            // 18432
-constexpr int kLdsSA = kBM * kGroupsPerStage * 4;  // 1024
-constexpr int kLdsSB = kBRows * kGroupsPerStage * 4;
-constexpr int kLdsStage = kLdsA + kLdsB + kLdsSA + kLdsSB;
+constexpr int kBM = kTileRows;       // 64 token rows per block
+constexpr int kSG = 4;               // groups per LDS stage (128 k)
+
+// One LDS stage (bytes), filled by direct global -> LDS loads (each wave
+// load writes 64 lanes x 16 (or 4) bytes contiguously):
+//   A  [kSG groups][2 halves][64 rows][16 B]   activation codes; a wave's
+//      MFMA A operand (row l%32, k 16(l/32) .. +15) is one conflict-free read
+//   B  int8: [4 tiles][kSG groups][1 KB]  weight blocks exactly as in HBM
+//      int4: [4 tiles][kSG/2 pairs][1 KB]
+//   SX [kSG groups][64 rows] fp32   activation scales (4 rows per 16-byte read)
+//   SW [4 tiles][kSG/2 pairs][64] fp32  weight scale blocks as in HBM
+constexpr int kLdsA = kSG * 2 * kBM * 16;        // 8192
+constexpr int kLdsSX = kSG * kBM * 4;            // 1024
+constexpr int kLdsSW = 4 * (kSG / 2) * 64 * 4;   // 2048
+template <int FMT>
+constexpr int lds_b_bytes() { return FMT == MOE_W_INT8_G32 ? 4 * kSG * 1024 : 4 * (kSG / 2) * 1024; }
+template <int FMT>
+constexpr int lds_stage_bytes() { return kLdsA + lds_b_bytes<FMT>() + kLdsSX + kLdsSW; }
 
 struct MfmaMat {
     const uint8_t* q;
@@ -71,231 +81,188 @@ __device__ __forceinline__ void widen_int4x8(uint32_t p, uint32_t& out_lo, uint3
     out_hi = __builtin_amdgcn_perm(odd, even, 0x07030602u);
 }
 
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
+// one wave's direct load of 64 x BYTES from per-lane global addresses into
+// LDS at `dst` (wave-uniform), lane L at dst + L * BYTES
+template <int BYTES>
+__device__ __forceinline__ void wave_load_lds(const void* src, uint8_t* dst) {
+    if constexpr (BYTES == 16)
+        __builtin_amdgcn_global_load_lds(src, (lds_ptr_t)dst, 16, 0, 0);
+    else
+        __builtin_amdgcn_global_load_lds(src, (lds_ptr_t)dst, 4, 0, 0);
+}
+
 template <int FMT, bool GATEUP, bool DBG>
 __global__ __launch_bounds__(256) void q8_mfma_kernel(const MfmaArgs a) {
-    __shared__ __attribute__((aligned(16))) uint8_t lds[2 * kLdsStage];
-    const int tile = blockIdx.y;
-    if (tile >= a.meta[1]) return;
-    const int4 td = a.tiles[tile];
+    constexpr int kStage = lds_stage_bytes<FMT>();
+    __shared__ __attribute__((aligned(1024))) uint8_t lds[2 * kStage];
+    const int tile_id = blockIdx.y;
+    if (tile_id >= a.meta[1]) return;
+    const int4 td = a.tiles[tile_id];
     const int e = td.x, row_begin = td.y, rows = td.z - td.y;
     const bool is_shared = e == a.E;
     const MfmaMat* M = is_shared ? a.shared : a.routed;
     const int64_t eo = is_shared ? 0 : e;
-    const uint8_t* wq0 = M[0].q + eo * M[0].q_stride;
-    const uint8_t* wq1 = M[1].q + eo * M[1].q_stride;
-    const float* ws0 = M[0].s + eo * M[0].s_stride;
-    const float* ws1 = M[1].s + eo * M[1].s_stride;
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave & 1, wn = wave >> 1;
-    const int K = a.K, N = a.N, G = K / kGroup, NT = N / kTile;
-    const int n0 = blockIdx.x * (GATEUP ? kBRows / 2 : kBRows);
-    const int row_bytes = FMT == MOE_W_INT8_G32 ? K : K / 2;
+    const int K = a.K, N = a.N, G = K / kGroup, P = G / 2, NT = N / kTile;
+    const int T0 = blockIdx.x * (GATEUP ? 2 : 4);      // first 32-row weight tile of the block
     constexpr float kWScale = FMT == MOE_W_INT8_G32 ? 1.0f : 0.0625f;
 
-    // ---- per-thread global load assignments (fixed over the K loop) ----
-    // A codes: 2 x 16 B per thread: row = li / 8, chunk = li % 8
-    int a_row_src[2];
-    bool a_row_ok[2];
+    // block tile j (0..3) -> matrix and tile index (clamped to the matrix:
+    // loads stay inside it; results of a clamped tile are not stored)
+    auto tile_of = [&](int j) { return min(T0 + (GATEUP ? (j & 1) : j), NT - 1); };
+    auto mat_of = [&](int j) { return GATEUP ? (j >> 1) : 0; };
+    const uint8_t* wq[2];
+    const float* wsb[2];
 #pragma unroll
-    for (int r = 0; r < 2; ++r) {
-        const int li = tid + 256 * r;
-        const int row = li >> 3;
-        a_row_ok[r] = row < rows;
-        const int prow = row_begin + (a_row_ok[r] ? row : 0);
-        a_row_src[r] = a.row_token ? a.row_token[prow] : prow;
+    for (int m = 0; m < 2; ++m) {
+        wq[m] = M[m].q + eo * M[m].q_stride;
+        wsb[m] = M[m].s + eo * M[m].s_stride;
     }
-    // A scales: thread -> (row = tid / 4, group = tid % 4)
-    const int sa_row = tid >> 2, sa_g = tid & 3;
-    const bool sa_ok = sa_row < rows;
-    const int sa_src = a.row_token ? a.row_token[row_begin + (sa_ok ? sa_row : 0)] : row_begin + (sa_ok ? sa_row : 0);
-    // B: 4 tiles of 32 weight rows per block (gate/up: 2 gate + 2 up tiles;
-    // down: 4 down tiles). Tile bt of the block -> matrix codes/scales + tile row.
-    auto b_tile = [&](int bt, const uint8_t*& q, const float*& s, int& tile) {
-        if (GATEUP) {
-            const bool up = bt >= 2;
-            q = up ? wq1 : wq0;
-            s = up ? ws1 : ws0;
-            tile = n0 / kTile + (up ? bt - 2 : bt);
-        } else {
-            q = wq0;
-            s = ws0;
-            tile = n0 / kTile + bt;
-        }
-    };
-    constexpr int kBLoads = FMT == MOE_W_INT8_G32 ? 4 : 2;
-    uint4 ra[2];
-    uint4 rb[kBLoads];
-    float rsa;
-    float rsb[2];
+    // this lane's activation row for the stage loads (row L of the tile,
+    // clamped to the tile's rows: rows past it are computed, never stored)
+    const int arow = row_begin + min(lane, rows - 1);
+    const int asrc = a.row_token ? a.row_token[arow] : arow;
+    const int8_t* arow_ptr = a.a_q + (size_t)asrc * K;
+    const float* srow_ptr = a.a_s + (size_t)asrc * G;
 
-    auto load_stage = [&](int stage) {
-        const int k0 = stage * kStageK;
-        const int g0 = stage * kGroupsPerStage;
-#pragma unroll
-        for (int r = 0; r < 2; ++r) {
-            const int li = tid + 256 * r;
-            const int chunk = li & 7;
-            const bool ok = a_row_ok[r] && (k0 + chunk * 16) < K;
-            ra[r] = ok ? *reinterpret_cast<const uint4*>(a.a_q + (size_t)a_row_src[r] * K + k0 + chunk * 16)
-                       : make_uint4(0, 0, 0, 0);
-        }
-        rsa = (sa_ok && g0 + sa_g < G) ? a.a_s[(size_t)sa_src * G + g0 + sa_g] : 0.0f;
-        // a 1 KB block of codes (int8: one tile x group, int4: one tile x
-        // pair of groups) is contiguous: a wave reads it whole
-#pragma unroll
-        for (int r = 0; r < kBLoads; ++r) {
-            const int li = tid + 256 * r;
-            const int blk = li >> 6, j = li & 63;
-            const uint8_t* q;
-            const float* sp;
-            int tile;
-            if constexpr (FMT == MOE_W_INT8_G32) {
-                const int bt = blk >> 2, g = blk & 3;
-                b_tile(bt, q, sp, tile);
-                const bool ok = tile * kTile < N && g0 + g < G;
-                rb[r] = ok ? *reinterpret_cast<const uint4*>(q + ((size_t)(g0 + g) * NT + tile) * 1024 + j * 16)
-                           : make_uint4(0, 0, 0, 0);
-            } else {
-                const int bt = blk >> 1, pr = g0 / 2 + (blk & 1);
-                b_tile(bt, q, sp, tile);
-                const bool ok = tile * kTile < N && pr < G / 2;
-                rb[r] = ok ? *reinterpret_cast<const uint4*>(q + ((size_t)pr * NT + tile) * 1024 + j * 16)
-                           : make_uint4(0, 0, 0, 0);
-            }
-        }
-#pragma unroll
-        for (int r = 0; r < 2; ++r) {
-            const int li = tid + 256 * r;
-            const int blk = li >> 5, r32 = li & 31;
-            const int bt = blk >> 2, g = g0 + (blk & 3);
-            const uint8_t* q;
-            const float* sp;
-            int tile;
-            b_tile(bt, q, sp, tile);
-            const bool ok = tile * kTile < N && g < G;
-            rsb[r] = ok ? sp[((size_t)tile * (G / 2) + g / 2) * 64 + (r32 & 15) * 4 + (g & 1) * 2 + (r32 >> 4)] *
-                              kWScale
-                        : 0.0f;
-        }
-    };
-
-    auto store_stage = [&](int buf) {
-        uint8_t* base = lds + buf * kLdsStage;
+    // stage loads: every wave takes every fourth job
+    auto issue_stage = [&](int st, int buf) {
+        uint8_t* base = lds + buf * kStage;
         uint8_t* A = base;
         uint8_t* B = base + kLdsA;
-        float* SA = reinterpret_cast<float*>(base + kLdsA + kLdsB);
-        float* SB = reinterpret_cast<float*>(base + kLdsA + kLdsB + kLdsSA);
+        uint8_t* SX = B + lds_b_bytes<FMT>();
+        uint8_t* SW = SX + kLdsSX;
+        const int g0 = st * kSG;
+        constexpr int nA = kSG * 2;
+        constexpr int nB = FMT == MOE_W_INT8_G32 ? 4 * kSG : 4 * (kSG / 2);
+        constexpr int nSX = kSG;
+        constexpr int nSW = 2;
+        constexpr int nJobs = nA + nB + nSX + nSW;
 #pragma unroll
-        for (int r = 0; r < 2; ++r) {
-            const int li = tid + 256 * r;
-            *reinterpret_cast<uint4*>(A + (li >> 3) * kLdsRow + (li & 7) * 16) = ra[r];
-        }
-        SA[sa_row * kGroupsPerStage + sa_g] = rsa;
-        // lane j = nl + 16 h of a block holds k 8h .. 8h+7 of rows nl and 16 + nl
-        if constexpr (FMT == MOE_W_INT8_G32) {
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int li = tid + 256 * r;
-                const int blk = li >> 6, j = li & 63;
-                const int brow = (blk >> 2) * kTile + (j & 15), g = blk & 3, h = j >> 4;
-                uint8_t* dst = B + brow * kLdsRow + g * kGroup + 8 * h;
-                *reinterpret_cast<uint2*>(dst) = make_uint2(rb[r].x, rb[r].y);
-                *reinterpret_cast<uint2*>(dst + 16 * kLdsRow) = make_uint2(rb[r].z, rb[r].w);
-            }
-        } else {
-#pragma unroll
-            for (int r = 0; r < 2; ++r) {
-                const int li = tid + 256 * r;
-                const int blk = li >> 6, j = li & 63;
-                const int brow = (blk >> 1) * kTile + (j & 15), g = 2 * (blk & 1), h = j >> 4;
-                const uint32_t words[4] = {rb[r].x, rb[r].y, rb[r].z, rb[r].w};
-#pragma unroll
-                for (int qd = 0; qd < 4; ++qd) {
-                    uint2 w;
-                    widen_int4x8(words[qd], w.x, w.y);
-                    uint8_t* dst = B + (brow + 16 * (qd & 1)) * kLdsRow + (g + (qd >> 1)) * kGroup + 8 * h;
-                    *reinterpret_cast<uint2*>(dst) = w;
+        for (int job = wave; job < nJobs; job += 4) {
+            if (job < nA) {
+                const int g = job >> 1, half = job & 1;
+                const int gc = min(g0 + g, G - 1);
+                wave_load_lds<16>(arow_ptr + gc * kGroup + half * 16, A + (g * 2 + half) * kBM * 16);
+            } else if (job < nA + nB) {
+                const int b = job - nA;
+                if constexpr (FMT == MOE_W_INT8_G32) {
+                    const int j = b / kSG, g = b % kSG;
+                    const int gc = min(g0 + g, G - 1);
+                    wave_load_lds<16>(wq[mat_of(j)] + ((size_t)gc * NT + tile_of(j)) * 1024 + lane * 16,
+                                      B + (j * kSG + g) * 1024);
+                } else {
+                    const int j = b / (kSG / 2), pp = b % (kSG / 2);
+                    const int pc = min(g0 / 2 + pp, P - 1);
+                    wave_load_lds<16>(wq[mat_of(j)] + ((size_t)pc * NT + tile_of(j)) * 1024 + lane * 16,
+                                      B + (j * (kSG / 2) + pp) * 1024);
                 }
+            } else if (job < nA + nB + nSX) {
+                const int g = job - nA - nB;
+                wave_load_lds<4>(srow_ptr + min(g0 + g, G - 1), SX + g * kBM * 4);
+            } else {
+                // two tiles' scale blocks for this stage's two pairs, 512 B each
+                const int q = job - nA - nB - nSX;
+                const int j = 2 * q + (lane >> 5);
+                const int pc = min(g0 / 2 + ((lane & 31) >> 4), P - 1);
+                wave_load_lds<16>(wsb[mat_of(j)] + ((size_t)tile_of(j) * P + pc) * 64 + (lane & 15) * 4,
+                                  SW + q * 1024);
             }
-        }
-#pragma unroll
-        for (int r = 0; r < 2; ++r) {
-            const int li = tid + 256 * r;
-            const int blk = li >> 5, r32 = li & 31;
-            SB[((blk >> 2) * kTile + r32) * kGroupsPerStage + (blk & 3)] = rsb[r];
         }
     };
 
-    // wave's operand rows inside the block tile
-    const int a_lrow = wm * 32 + (lane & 31);
-    const int b_lrow0 = GATEUP ? wn * 32 + (lane & 31) : wn * 64 + (lane & 31);
-    const int b_lrow1 = GATEUP ? kBRows / 2 + wn * 32 + (lane & 31) : wn * 64 + 32 + (lane & 31);
-    const int khalf = (lane >> 5) * 16;
-    // output row of accumulator register i: 8*(i/4) + 4*(lane/32) + i%4
-    int m_of[16];
-#pragma unroll
-    for (int i = 0; i < 16; ++i) m_of[i] = 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
+    // output rows of accumulator register i: 8*(i/4) + 4*(lane/32) + i%4
+    const int khalf = lane >> 5, ncol = lane & 31;
+    // wave's two MFMA tiles (block tile index j)
+    const int jt0 = GATEUP ? wn : 2 * wn;
+    const int jt1 = GATEUP ? 2 + wn : 2 * wn + 1;
 
-    float acc0[16], acc1[16];
+    float acc[2][16];
 #pragma unroll
-    for (int i = 0; i < 16; ++i) { acc0[i] = 0.0f; acc1[i] = 0.0f; }
+    for (int i = 0; i < 16; ++i) { acc[0][i] = 0.0f; acc[1][i] = 0.0f; }
 
-    const int n_stages = (G + kGroupsPerStage - 1) / kGroupsPerStage;
-    load_stage(0);
-    store_stage(0);
+    const int n_stages = (G + kSG - 1) / kSG;
+    issue_stage(0, 0);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
     for (int st = 0; st < n_stages; ++st) {
-        if (st + 1 < n_stages) load_stage(st + 1);
-        const uint8_t* base = lds + (st & 1) * kLdsStage;
+        if (st + 1 < n_stages) issue_stage(st + 1, (st + 1) & 1);
+        const uint8_t* base = lds + (st & 1) * kStage;
         const uint8_t* A = base;
         const uint8_t* B = base + kLdsA;
-        const float* SA = reinterpret_cast<const float*>(base + kLdsA + kLdsB);
-        const float* SB = reinterpret_cast<const float*>(base + kLdsA + kLdsB + kLdsSA);
-        const int g_here = min(kGroupsPerStage, G - st * kGroupsPerStage);
-        for (int g = 0; g < g_here; ++g) {
-            const v4i af = *reinterpret_cast<const v4i*>(A + a_lrow * kLdsRow + g * kGroup + khalf);
-            const v4i bf0 = *reinterpret_cast<const v4i*>(B + b_lrow0 * kLdsRow + g * kGroup + khalf);
-            const v4i bf1 = *reinterpret_cast<const v4i*>(B + b_lrow1 * kLdsRow + g * kGroup + khalf);
-            const v16i zero = {};
-            const v16i d0 = __builtin_amdgcn_mfma_i32_32x32x32_i8(af, bf0, zero, 0, 0, 0);
-            const v16i d1 = __builtin_amdgcn_mfma_i32_32x32x32_i8(af, bf1, zero, 0, 0, 0);
-            const float sw0 = SB[b_lrow0 * kGroupsPerStage + g];
-            const float sw1 = SB[b_lrow1 * kGroupsPerStage + g];
+        const float* SX = reinterpret_cast<const float*>(B + lds_b_bytes<FMT>());
+        const float* SW = SX + kSG * kBM;
+        const int g_here = min(kSG, G - st * kSG);
 #pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                const float sx = SA[(wm * 32 + m_of[i]) * kGroupsPerStage + g];
-                acc0[i] = fmaf((float)d0[i] * sw0, sx, acc0[i]);
-                acc1[i] = fmaf((float)d1[i] * sw1, sx, acc1[i]);
+        for (int g = 0; g < kSG; ++g) {
+            if (g >= g_here) break;
+            const v4i af = *reinterpret_cast<const v4i*>(A + ((g * 2 + khalf) * kBM + wm * 32 + ncol) * 16);
+            float sx[16];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const float4 v = *reinterpret_cast<const float4*>(SX + g * kBM + wm * 32 + 8 * q + 4 * khalf);
+                sx[4 * q] = v.x;
+                sx[4 * q + 1] = v.y;
+                sx[4 * q + 2] = v.z;
+                sx[4 * q + 3] = v.w;
             }
-            if constexpr (DBG) {
-                const int gg = st * kGroupsPerStage + g;
-                const int c0 = GATEUP ? n0 + wn * 32 + (lane & 31) : n0 + wn * 64 + (lane & 31);
-                const int c1 = GATEUP ? c0 : c0 + 32;
 #pragma unroll
-                for (int i = 0; i < 16; ++i) {
-                    const int row = wm * 32 + m_of[i];
-                    if (row >= rows) continue;
-                    const size_t r = (size_t)(row_begin + row);
-                    const int v0 = FMT == MOE_W_INT8_G32 ? d0[i] : (d0[i] >> 4);
-                    const int v1 = FMT == MOE_W_INT8_G32 ? d1[i] : (d1[i] >> 4);
-                    if (c0 < N) a.dbg0[(r * N + c0) * G + gg] = v0;
-                    if (c1 < N) (GATEUP ? a.dbg1 : a.dbg0)[(r * N + c1) * G + gg] = v1;
+            for (int tt = 0; tt < 2; ++tt) {
+                const int j = tt ? jt1 : jt0;
+                v4i bf;
+                if constexpr (FMT == MOE_W_INT8_G32) {
+                    // row ncol, k 16 khalf .. +15: lanes (ncol%16) + 32 khalf (+16) of the block
+                    const uint8_t* blk = B + (j * kSG + g) * 1024 + ((ncol & 15) + 32 * khalf) * 16 + (ncol >> 4) * 8;
+                    const uint2 p0 = *reinterpret_cast<const uint2*>(blk);
+                    const uint2 p1 = *reinterpret_cast<const uint2*>(blk + 256);
+                    bf = v4i{(int)p0.x, (int)p0.y, (int)p1.x, (int)p1.y};
+                } else {
+                    const uint8_t* blk = B + (j * (kSG / 2) + (g >> 1)) * 1024 + ((ncol & 15) + 32 * khalf) * 16 +
+                                         ((g & 1) * 2 + (ncol >> 4)) * 4;
+                    const uint32_t d0 = *reinterpret_cast<const uint32_t*>(blk);
+                    const uint32_t d1 = *reinterpret_cast<const uint32_t*>(blk + 256);
+                    uint32_t w0, w1, w2, w3;
+                    widen_int4x8(d0, w0, w1);
+                    widen_int4x8(d1, w2, w3);
+                    bf = v4i{(int)w0, (int)w1, (int)w2, (int)w3};
+                }
+                const v16i zero = {};
+                const v16i d = __builtin_amdgcn_mfma_i32_32x32x32_i8(af, bf, zero, 0, 0, 0);
+                const float sw = SW[(j * (kSG / 2) + (g >> 1)) * 64 + (ncol & 15) * 4 + (g & 1) * 2 + (ncol >> 4)] *
+                                 kWScale;
+#pragma unroll
+                for (int i = 0; i < 16; ++i) acc[tt][i] = fmaf((float)d[i] * sw, sx[i], acc[tt][i]);
+                if constexpr (DBG) {
+                    const int gg = st * kSG + g;
+                    const int col = GATEUP ? T0 * kTile + 32 * wn + ncol : (T0 + j) * kTile + ncol;
+                    int32_t* dst = (GATEUP && tt == 1) ? a.dbg1 : a.dbg0;
+#pragma unroll
+                    for (int i = 0; i < 16; ++i) {
+                        const int row = wm * 32 + 8 * (i >> 2) + 4 * khalf + (i & 3);
+                        if (row >= rows || col >= N) continue;
+                        const int v = FMT == MOE_W_INT8_G32 ? d[i] : (d[i] >> 4);
+                        dst[((size_t)(row_begin + row) * N + col) * G + gg] = v;
+                    }
                 }
             }
         }
-        if (st + 1 < n_stages) store_stage((st + 1) & 1);
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         __syncthreads();
     }
 
     // ---- epilogue ----
     if constexpr (GATEUP) {
-        const int col = n0 + wn * 32 + (lane & 31);
-        const bool col_ok = n0 + wn * 32 < N;
+        const int col = T0 * kTile + 32 * wn + ncol;
+        const bool col_ok = T0 + wn < NT;
         const int GN = N / kGroup;
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-            const float h = silu(acc0[i]) * acc1[i];
+            const float h = silu(acc[0][i]) * acc[1][i];
             float amax = fabsf(h);
 #pragma unroll
             for (int off = 16; off > 0; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off, kWave));
@@ -303,23 +270,24 @@ __global__ __launch_bounds__(256) void q8_mfma_kernel(const MfmaArgs a) {
             const float inv = dd != 0.0f ? __fdiv_rn(1.0f, dd) : 0.0f;
             float q = rintf(__fmul_rn(h, inv));
             q = fminf(fmaxf(q, -127.0f), 127.0f);
-            const int row = wm * 32 + m_of[i];
+            const int row = wm * 32 + 8 * (i >> 2) + 4 * khalf + (i & 3);
             if (row < rows && col_ok) {
                 const size_t r = (size_t)(row_begin + row);
                 a.hq[r * N + col] = (int8_t)(int)q;
-                if ((lane & 31) == 0) a.hd[r * GN + (n0 + wn * 32) / kGroup] = dd;
+                if (ncol == 0) a.hd[r * GN + T0 + wn] = dd;
             }
         }
     } else {
-        const int c0 = n0 + wn * 64 + (lane & 31);
-        const int c1 = c0 + 32;
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            const int row = wm * 32 + m_of[i];
-            if (row >= rows) continue;
-            const size_t r = (size_t)(row_begin + row);
-            if (c0 < N) a.y[r * N + c0] = acc0[i];
-            if (c1 < N) a.y[r * N + c1] = acc1[i];
+        for (int tt = 0; tt < 2; ++tt) {
+            const int t = T0 + (tt ? jt1 : jt0);
+            if (t >= NT) continue;
+            const int col = t * kTile + ncol;
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                const int row = wm * 32 + 8 * (i >> 2) + 4 * khalf + (i & 3);
+                if (row < rows) a.y[(size_t)(row_begin + row) * N + col] = acc[tt][i];
+            }
         }
     }
 }
@@ -357,7 +325,7 @@ hipError_t launch_q8_mfma(const moe_experts& routed, const moe_experts* shared, 
     };
     fill(a.routed, routed);
     fill(a.shared, shared ? *shared : routed);
-    const int bn = gateup ? kBRows / 2 : kBRows;
+    const int bn = gateup ? 2 * kTile : 4 * kTile;   // output columns per block
     const dim3 grid((a.N + bn - 1) / bn, max_tiles);
     const bool dbg = dbg0 != nullptr;
 #define MOE_Q8(FMT, GU, DB) launch_timed(q8_mfma_kernel<FMT, GU, DB>, grid, dim3(256), st, ev0, ev1, a)
