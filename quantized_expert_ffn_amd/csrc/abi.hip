@@ -102,12 +102,13 @@ moe_status check_act_mode(int act_mode) {
 
 // The f32 path addresses its activation parts ([R, max(d, I)] f16, R = T*k
 // rows plus T for a shared expert) with 32-bit offsets.
-moe_status check_f32_rows(int act_mode, int T, int k, int has_shared, const moe_experts* ex) {
-    if (act_mode != MOE_ACT_F32) return MOE_OK;
+// The expert kernels address their f16 activation rows with 32-bit byte
+// offsets: R rows of max(d, d_ff) values, 2 bytes each (both modes).
+moe_status check_rows(int T, int k, int has_shared, const moe_experts* ex) {
     const int64_t R = (int64_t)T * k + (has_shared ? T : 0);
     const int64_t K = ex->d_model > ex->d_ff ? ex->d_model : ex->d_ff;
     MOE_REQUIRE(R * K * 2 < ((int64_t)1 << 31), MOE_ERR_UNSUPPORTED,
-                "the f32 path takes up to 2^30 activation values (T*k rows of max(d, d_ff)); use MOE_ACT_Q8_0");
+                "up to 2^30 routed activation values (T*k rows of max(d, d_ff)) per call");
     return MOE_OK;
 }
 
@@ -125,15 +126,15 @@ hipEvent_t stage_ev(const hipEvent_t* ev, int idx) { return ev ? ev[idx] : nullp
 // Where the prepared hidden states go in the workspace (f32 parts or Q8_0).
 moe::XPrep xprep_for(int act_mode, int fmt, const moe::WsLayout& L, void* ws) {
     moe::XPrep xp;
+    xp.fmt = fmt;
     if (act_mode == MOE_ACT_F32) {
         xp.mode = moe::XPREP_SPLIT;
-        xp.fmt = fmt;
         xp.hi = ws_at<_Float16>(ws, L.xq);
         xp.lo = ws_at<_Float16>(ws, L.xd);
         xp.pow = ws_at<float>(ws, L.xp);
     } else {
         xp.mode = moe::XPREP_Q8_0;
-        xp.q = ws_at<int8_t>(ws, L.xq);
+        xp.q = ws_at<_Float16>(ws, L.xq);
         xp.qd = ws_at<float>(ws, L.xd);
     }
     return xp;
@@ -170,18 +171,19 @@ moe_status run_experts(int T, int k, const moe_experts& routed, const moe_expert
                 "down GEMV");
         return MOE_OK;
     }
-    const int8_t* xq = ws_at<int8_t>(ws, L.xq);
+    const _Float16* xq = ws_at<_Float16>(ws, L.xq);
     const float* xd = ws_at<float>(ws, L.xd);
-    int8_t* hq = hq_out ? hq_out : ws_at<int8_t>(ws, L.h);
+    _Float16* hq = ws_at<_Float16>(ws, L.h);
     float* hd = hd_out ? hd_out : ws_at<float>(ws, L.hd);
-    MOE_HIP(moe::launch_q8_mfma(routed, shared, true, xq, xd, row_token, tiles, meta, L.max_tiles, hq, hd, nullptr,
-                                dots_gate, dots_up, st, stage_ev(ev, 2 * MOE_STAGE_GATEUP),
+    const int R = n + (has_shared ? T : 0);
+    MOE_HIP(moe::launch_q8_mfma(routed, shared, true, xq, xd, T, row_token, tiles, meta, L.max_tiles, hq, hd, nullptr,
+                                dots_gate, dots_up, hq_out, st, stage_ev(ev, 2 * MOE_STAGE_GATEUP),
                                 stage_ev(ev, 2 * MOE_STAGE_GATEUP + 1)),
-            "gate/up int8 MFMA");
-    MOE_HIP(moe::launch_q8_mfma(routed, shared, false, hq, hd, nullptr, tiles, meta, L.max_tiles, nullptr, nullptr, y,
-                                dots_down, nullptr, st, stage_ev(ev, 2 * MOE_STAGE_DOWN),
+            "gate/up matrix-core GEMM");
+    MOE_HIP(moe::launch_q8_mfma(routed, shared, false, hq, hd, R, nullptr, tiles, meta, L.max_tiles, nullptr, nullptr, y,
+                                dots_down, nullptr, nullptr, st, stage_ev(ev, 2 * MOE_STAGE_DOWN),
                                 stage_ev(ev, 2 * MOE_STAGE_DOWN + 1)),
-            "down int8 MFMA");
+            "down matrix-core GEMM");
     return MOE_OK;
 }
 
@@ -197,7 +199,7 @@ moe_status expert_ffn_impl(const float* x, int32_t T, int32_t k, const moe_exper
     MOE_REQUIRE(ex->n_experts <= moe::kMaxExperts, MOE_ERR_UNSUPPORTED, "n_experts = %d > %d", ex->n_experts,
                 moe::kMaxExperts);
     if (T == 0) return ok();
-    if ((s = check_f32_rows(act_mode, T, k, 0, ex)) != MOE_OK) return s;
+    if ((s = check_rows(T, k, 0, ex)) != MOE_OK) return s;
     MOE_REQUIRE(x && counts && offsets && perm && y_perm, MOE_ERR_INVALID_ARG, "NULL tensor argument");
     MOE_REQUIRE(aligned16(x) && aligned16(y_perm), MOE_ERR_INVALID_ARG, "x and y_perm must be 16-byte aligned");
     const moe::WsLayout L = moe::ws_layout(T, k, ex->n_experts, ex->d_model, ex->d_ff, act_mode, 0);
@@ -231,7 +233,7 @@ moe_status layer_forward_impl(const float* x, int32_t T, const float* gate_w, co
     }
     MOE_REQUIRE(T >= 0, MOE_ERR_INVALID_ARG, "T = %d < 0", T);
     if (T == 0) return ok();
-    if ((s = check_f32_rows(act_mode, T, p->top_k, shared != nullptr, routed)) != MOE_OK) return s;
+    if ((s = check_rows(T, p->top_k, shared != nullptr, routed)) != MOE_OK) return s;
     MOE_REQUIRE(x && gate_w && out, MOE_ERR_INVALID_ARG, "NULL tensor argument");
     MOE_REQUIRE(aligned16(x) && aligned16(gate_w) && aligned16(out), MOE_ERR_INVALID_ARG,
                 "x, gate_w and out must be 16-byte aligned");

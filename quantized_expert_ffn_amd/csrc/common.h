@@ -30,10 +30,10 @@ struct WsLayout {
     size_t slots = 0;      // i32  [E + 1][4]  (expert, row_begin, n_rows, 0)
     size_t tiles = 0;      // i32  [max_tiles][4] (expert, row_begin, row_end, 0)
     size_t meta = 0;       // i32  [4]  n_slots, n_tiles, status, 0
-    size_t xq = 0;         // Q8_0: i8 [T, d]      F32: f16 hi parts [T, d]
+    size_t xq = 0;         // Q8_0: f16 codes [T, d]  F32: f16 hi parts [T, d]
     size_t xd = 0;         // Q8_0: f32 [T, d/32]  F32: f16 lo parts [T, d]
     size_t xp = 0;         //                      F32: f32 powers of two [d/32]
-    size_t h = 0;          // Q8_0: i8 [R, I]      F32: f16 hi parts [R, I];  R = T*k + T*shared
+    size_t h = 0;          // Q8_0: f16 codes [R, I]  F32: f16 hi parts [R, I];  R = T*k + T*shared
     size_t hd = 0;         // Q8_0: f32 [R, I/32]  F32: f16 lo parts [R, I]
     size_t hp = 0;         //                      F32: f32 powers of two [R, I/32]
     size_t y = 0;          // f32  [R, d]
@@ -41,7 +41,7 @@ struct WsLayout {
     int max_tiles = 0;
 };
 
-constexpr int kTileRows = 64;         // rows (tokens) per int8-MFMA tile
+constexpr int kTileRows = 128;        // rows (tokens) per prefill matrix-core tile
 
 // Router logits: 0 = one block per expert (small T); S >= 1 = fp32 matrix-core
 // tiles of 64 x 64 with d cut into S slices, enough to give ~512 blocks.
@@ -78,9 +78,9 @@ inline WsLayout ws_layout(int T, int k, int E, int d, int I, int act_mode, int h
     L.tiles = take((size_t)(L.max_tiles > 0 ? L.max_tiles : 1) * 16);
     L.meta = take(16);
     if (act_mode == MOE_ACT_Q8_0) {
-        L.xq = take((size_t)T * d);
+        L.xq = take((size_t)T * d * 2);
         L.xd = take((size_t)T * (d / kGroup) * 4);
-        L.h = take(R * I);
+        L.h = take(R * I * 2);
         L.hd = take(R * (I / kGroup) * 4);
     } else {
         L.xq = take((size_t)T * d * 2);
@@ -191,7 +191,9 @@ __device__ __forceinline__ float wave_max(float v) {
     return v;
 }
 
-__device__ __forceinline__ float silu(float g) { return g / (1.0f + __expf(-g)); }
+// SiLU with the hardware reciprocal (about 1 ulp) in place of a rounded
+// division; large negative g gives exp -> inf, reciprocal 0, result -0.
+__device__ __forceinline__ float silu(float g) { return g * __builtin_amdgcn_rcpf(1.0f + __expf(-g)); }
 
 __device__ __forceinline__ uint64_t lanemask_lt() {
     const int lane = threadIdx.x & (kWave - 1);

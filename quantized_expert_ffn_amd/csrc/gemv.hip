@@ -3,10 +3,12 @@
 // implemented": int8 / packed int4 weights dequantised on use; batch-union
 // over the positions routed to one expert; a single row stays in f32).
 //
-// Exact fp32-level activations on f16 matrix cores. For every tile of up to 16
-// activation rows of one expert and group of 32, a power of two p = 2^(e-15)
-// with max|x| < 2^e is chosen and x/p (exact) is split into hi = f16(x/p) and
-// lo = f16(x/p - hi): together 22 significant bits. Weight codes are small integers, exact in f16. So
+// Exact fp32-level activations on f16 matrix cores. For every group of 32
+// along the reduction axis, a power of two p = 2^(e-15) with max|x| < 2^e over
+// the rows that share it (the whole batch for X, a 16-row tile for H) is
+// chosen and x/p (exact) is split into hi = f16(x/p) and lo = f16(x/p - hi):
+// together 22 significant bits. Weight codes are small integers, exact in f16
+// (f16codes.h). So
 //     sum_k x_k q_k = p * (MFMA(hi, q) + MFMA(lo, q))
 // with exact products and fp32 accumulation (v_mfma_f32_16x16x32_f16, K = 32
 // = one quantisation group); the group's weight scale and p are applied once
@@ -21,62 +23,18 @@
 // Weight codes come straight from HBM into operand registers: in the
 // lane-tiled layout one 16-byte load per lane brings a wave the B operands of
 // both 16-row halves of a 32-row tile for one group (int8) or two groups
-// (int4), and one more brings the scales of two groups. Every vector memory
-// instruction costs the CU's address unit about the same time whatever its
-// width, so the kernel issues few, wide ones: per pair of groups and 32-row
-// tile of two matrices, 4 (int8) or 2 (int4) code loads, 2 scale loads and 4
-// activation loads (hi/lo of two groups), the activations serving 64 weight
-// rows. Activation fragments come from L2; token rows past an expert's count
-// read as zeros.
-//
-// Codes to f16 without a conversion instruction: an unsigned byte u ORed
-// into 0x6400 is the f16 number 1024 + u; a packed f16 subtract of 1152
-// (int8 after XOR 0x80) or 1032 (int4 after XOR 0x8) leaves the signed code.
-// That pairs bytes (0,2),(1,3) of an int8 dword and nibbles (0,4),(1,5),
-// (2,6),(3,7) of an int4 dword; activations are stored in the same k order
-// inside every 8-wide slice, and a dot product ignores the order of terms.
+// (int4), and one more brings the scales of four group pairs of the tile.
+// Every vector memory instruction costs the CU's address unit about the same
+// time whatever its width, so the kernel issues few, wide ones: per pair of
+// groups and 32-row tile of two matrices, 4 (int8) or 2 (int4) code loads,
+// half a scale load and 4 activation loads (hi/lo of two groups), the
+// activations serving 64 weight rows. Activation fragments come from L2;
+// token rows past an expert's count read as zeros.
 #include "common.h"
+#include "f16codes.h"
 #include "kernels.h"
 
 namespace moe {
-
-typedef _Float16 v8h __attribute__((ext_vector_type(8)));
-typedef _Float16 v2h __attribute__((ext_vector_type(2)));
-typedef float v4f __attribute__((ext_vector_type(4)));
-
-
-__device__ __forceinline__ uint32_t and_or(uint32_t a, uint32_t m, uint32_t o) { return (a & m) | o; }
-
-// 8 codes of one lane slice -> 8 f16 in slot order
-template <int FMT>
-__device__ __forceinline__ v8h codes_to_f16(uint32_t w0, uint32_t w1) {
-    union {
-        uint32_t u[4];
-        v8h h;
-    } r;
-    v2h off;
-    if constexpr (FMT == MOE_W_INT8_G32) {
-        // byte pick: (code byte 0 or 1, 0x64) and (code byte 2 or 3, 0x64)
-        const uint32_t a = w0 ^ 0x80808080u, b = w1 ^ 0x80808080u;
-        r.u[0] = __builtin_amdgcn_perm(a, 0x64646464u, 0x00060004u);
-        r.u[1] = __builtin_amdgcn_perm(a, 0x64646464u, 0x00070005u);
-        r.u[2] = __builtin_amdgcn_perm(b, 0x64646464u, 0x00060004u);
-        r.u[3] = __builtin_amdgcn_perm(b, 0x64646464u, 0x00070005u);
-        off = v2h{(_Float16)-1152.0f, (_Float16)-1152.0f};
-    } else {
-        const uint32_t a = w0 ^ 0x88888888u;
-        r.u[0] = and_or(a, 0x000f000fu, 0x64006400u);
-        r.u[1] = and_or(a >> 4, 0x000f000fu, 0x64006400u);
-        r.u[2] = and_or(a >> 8, 0x000f000fu, 0x64006400u);
-        r.u[3] = and_or(a >> 12, 0x000f000fu, 0x64006400u);
-        off = v2h{(_Float16)-1032.0f, (_Float16)-1032.0f};
-        (void)w1;
-    }
-#pragma unroll
-    for (int i = 0; i < 4; ++i) r.u[i] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(v2h, r.u[i]) + off);
-    return r.h;
-}
-
 
 struct GemvArgs {
     const _Float16* ahi;    // activation parts in slot order: gate/up [T, K] token rows, down [R, K]

@@ -15,11 +15,11 @@ hipError_t launch_quantize_q8_0(const float* x, int64_t rows, int cols, int8_t* 
 enum { XPREP_NONE = 0, XPREP_SPLIT = 1, XPREP_Q8_0 = 2 };
 struct XPrep {
     int mode = XPREP_NONE;
-    int fmt = MOE_W_INT8_G32;      // XPREP_SPLIT: the weight format (operand-slot order)
+    int fmt = MOE_W_INT8_G32;      // the weight format (operand-slot order of the f16 outputs)
     _Float16* hi = nullptr;        // XPREP_SPLIT: [T, d] f16 parts and one power of
     _Float16* lo = nullptr;        //   two per 32-group over all rows, [d/32]
     float* pow = nullptr;
-    int8_t* q = nullptr;           // XPREP_Q8_0: [T, d] codes, [T, d/32] scales
+    _Float16* q = nullptr;         // XPREP_Q8_0: [T, d] codes as f16 in slot order, [T, d/32] scales
     float* qd = nullptr;
 };
 
@@ -57,10 +57,16 @@ hipError_t launch_gemv(const moe_experts& routed, const moe_experts* shared, boo
                        const int* slots, const int* meta, int max_slots, _Float16* hhi, _Float16* hlo, float* hpow,
                        float* y, hipStream_t st, hipEvent_t ev_start = nullptr, hipEvent_t ev_stop = nullptr);
 
-hipError_t launch_q8_mfma(const moe_experts& routed, const moe_experts* shared, bool gateup, const int8_t* a_q,
-                          const float* a_s, const int* row_token, const int* tiles, const int* meta, int max_tiles,
-                          int8_t* hq, float* hd, float* y, int32_t* dbg0, int32_t* dbg1, hipStream_t st,
-                          hipEvent_t ev_start = nullptr, hipEvent_t ev_stop = nullptr);
+// Prefill path (Q8_0 activations). gate/up: A = the token rows' Q8_0 codes
+// as f16 in slot order [a_rows = T, d] (read through row_token) + scales
+// [T, d/32]; it writes H's Q8_0 codes the same way, [R, I] + [R, I/32].
+// down: A = those (a_rows = R) -> Y fp32 [R, d]. The dbg pointers (all or
+// none) receive the exact group dots and H's int8 codes in natural order.
+hipError_t launch_q8_mfma(const moe_experts& routed, const moe_experts* shared, bool gateup, const _Float16* a_q,
+                          const float* a_s, int a_rows, const int* row_token, const int* tiles, const int* meta,
+                          int max_tiles, _Float16* hq, float* hd, float* y, int32_t* dbg0, int32_t* dbg1,
+                          int8_t* dbg_hq,
+                          hipStream_t st, hipEvent_t ev_start = nullptr, hipEvent_t ev_stop = nullptr);
 
 hipError_t launch_combine(const float* y, const float* w, const int* inv_perm, const float* shared_y, int T, int k,
                           int d, float* out, hipStream_t st);

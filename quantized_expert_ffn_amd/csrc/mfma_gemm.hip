@@ -1,51 +1,63 @@
-// Prefill / verification path: batch-union grouped GEMM on the int8 matrix
-// cores ("Show HN: Getting GLM-5.2 running on my slow computer", section "What's implemented": integer-dot
+// Prefill / verification path: batch-union grouped GEMM with Q8_0
+// activations and exact integer group dots ("Show HN: Getting GLM-5.2
+// running on my slow computer", section "What's implemented": integer-dot
 // kernels with Q8_0-style int8 activations, used in batch; batch-union MoE in
 // prefill and MTP verification).
 //
-// Each 32-deep quantisation group is one v_mfma_i32_32x32x32_i8, whose int32
-// result is exact; the group's two fp32 scales (activation row, weight
-// column) are applied to it before it joins the fp32 accumulator:
-//     acc[m][n] += sx[m, g] * sw[n, g] * I_g[m, n].
-// Packed int4 weights are widened to int8 bytes holding 16*q (the nibble in
-// the high half of the byte), so the matrix core sees int8 codes; the factor
-// 16 is removed exactly by folding 1/16 into the weight scale.
+// Each 32-deep quantisation group is one v_mfma_f32_16x16x32_f16 per 16 x 16
+// output tile, fed with the integer codes themselves: activation and weight
+// codes are exact in f16, their products are exact, and the group's sum
+// (|sum| <= 32 * 127 * 127 < 2^24) is exact in the fp32 result, so the matrix
+// core returns the exact integer group dot I_g, already as a float. The
+// group's two fp32 scales (activation row, weight row) are then applied
+// before it joins the fp32 accumulator:
+//     acc[m][n] += I_g[m, n] * (sx[m, g] * sw[n, g])
+// which is two VALU operations per output and group (an int8 matrix-core
+// product would need a third, the int -> float conversion, and the VALU work
+// is what bounds this kernel).
 //
-// Block tile: 64 rows (tokens of one expert) x 128 weight rows (four 32-row
-// tiles), staged through LDS in steps of 4 groups (128 k), double buffered,
-// by direct global -> LDS loads: no staging registers, the weight blocks land
-// exactly as they are stored. Four waves in 2 x 2; each wave owns 32 rows
-// and two 32-column MFMA tiles.
-//   gate/up kernel: the two tiles are gate and up of the same 32 outputs, so
-//     SwiGLU and the Q8_0 quantisation of H (32 outputs = one group) happen
-//     in registers; H leaves as int8 codes + one fp32 scale per 32.
-//   down kernel: two adjacent 32-column tiles of the output; Y leaves fp32.
-// Work list: one tile per (expert, 64-row block) from the dispatch kernel;
+// Block tile: 128 rows (tokens of one expert) x 128 weight rows (four 32-row
+// tiles), staged through LDS one group pair (64 k) at a time, double
+// buffered, by direct global -> LDS loads: no staging registers; weight
+// blocks land exactly as they are stored. Four waves in 2 x 2; each wave owns
+// 64 rows (four 16-row tiles) and two weight tiles (four 16-row halves), 16
+// matrix-core products per group. 16-row tiles past the tile's row count
+// are neither loaded nor multiplied (wave-uniform), so a short tile costs
+// little more than its rows.
+//   gate/up kernel: the wave's two weight tiles are gate and up of the same 32
+//     outputs, so SwiGLU and the Q8_0 quantisation of H (32 outputs = one
+//     group) happen in registers; H leaves as f16 codes in operand-slot
+//     order + one fp32 scale per 32, ready to be the down kernel's A operand.
+//   down kernel: two adjacent 32-row weight tiles; Y leaves fp32.
+// Work list: one tile per (expert, 128-row block) from the dispatch kernel;
 // blocks past the live tile count exit at once (no host read-back).
+#include <type_traits>
+
 #include "common.h"
+#include "f16codes.h"
 #include "kernels.h"
 
 namespace moe {
 
-typedef int v4i __attribute__((ext_vector_type(4)));
-typedef int v16i __attribute__((ext_vector_type(16)));
-
-constexpr int kBM = kTileRows;       // 64 token rows per block
-constexpr int kSG = 4;               // groups per LDS stage (128 k)
+constexpr int kBM = kTileRows;       // 128 token rows per block
+constexpr int kSG = 2;               // groups per LDS stage (one pair, 64 k)
+constexpr int kM16 = kBM / 16;       // 16-row tiles per block
 
 // One LDS stage (bytes), filled by direct global -> LDS loads (each wave
 // load writes 64 lanes x 16 (or 4) bytes contiguously):
-//   A  [kSG groups][2 halves][64 rows][16 B]   activation codes; a wave's
-//      MFMA A operand (row l%32, k 16(l/32) .. +15) is one conflict-free read
+//   A  [kSG groups][kM16 tiles][64 lanes][16 B]  f16 activation codes; block
+//      (g, i) is the MFMA A operand of 16-row tile i, lane l = r + 16 h
+//      holding row 16 i + r, slice h (k 8h .. 8h+7 in slot order): one
+//      contiguous 1 KB read per operand
 //   B  int8: [4 tiles][kSG groups][1 KB]  weight blocks exactly as in HBM
-//      int4: [4 tiles][kSG/2 pairs][1 KB]
-//   SX [kSG groups][64 rows] fp32   activation scales (4 rows per 16-byte read)
-//   SW [4 tiles][kSG/2 pairs][64] fp32  weight scale blocks as in HBM
-constexpr int kLdsA = kSG * 2 * kBM * 16;        // 8192
-constexpr int kLdsSX = kSG * kBM * 4;            // 1024
-constexpr int kLdsSW = 4 * (kSG / 2) * 64 * 4;   // 2048
+//      int4: [4 tiles][1 KB]              (one block holds the pair)
+//   SX [kSG groups][kBM rows] fp32        activation scales
+//   SW [4 tiles][64] fp32                 the tiles' scale blocks of the pair
+constexpr int kLdsA = kSG * kM16 * 1024;   // 16384
+constexpr int kLdsSX = kSG * kBM * 4;      // 1024
+constexpr int kLdsSW = 4 * 64 * 4;         // 1024
 template <int FMT>
-constexpr int lds_b_bytes() { return FMT == MOE_W_INT8_G32 ? 4 * kSG * 1024 : 4 * (kSG / 2) * 1024; }
+constexpr int lds_b_bytes() { return FMT == MOE_W_INT8_G32 ? 4 * kSG * 1024 : 4 * 1024; }
 template <int FMT>
 constexpr int lds_stage_bytes() { return kLdsA + lds_b_bytes<FMT>() + kLdsSX + kLdsSW; }
 
@@ -57,46 +69,78 @@ struct MfmaMat {
 };
 
 struct MfmaArgs {
-    const int8_t* a_q;      // activation codes, rows of K
+    const _Float16* a_q;    // activation codes as f16, rows of K, slot order
     const float* a_s;       // activation scales, rows of K/32
+    uint32_t a_bytes;       // sizes of the two (rows * K * 2, rows * K/32 * 4)
+    uint32_t s_bytes;
     const int* row_token;   // permuted row -> activation row (nullptr: identity)
     const int4* tiles;      // (expert, row_begin, row_end, 0)
     const int* meta;        // meta[1] = live tile count
     MfmaMat routed[2];      // gate, up (or down, down)
     MfmaMat shared[2];
     int E, K, N;
-    int8_t* hq;             // gate/up output codes  [R, N]
+    _Float16* hq;           // gate/up output codes  [R, N], f16, slot order
     float* hd;              // gate/up output scales [R, N/32]
     float* y;               // down output           [R, N]
     int32_t* dbg0;          // optional exact group dots [R, N, K/32]
     int32_t* dbg1;
+    int8_t* dbg_hq;         // optional int8 H codes [R, N], natural order
 };
 
-// Widen 8 packed int4 codes (one dword) to 8 bytes of 16*q, natural order.
-__device__ __forceinline__ void widen_int4x8(uint32_t p, uint32_t& out_lo, uint32_t& out_hi) {
-    const uint32_t even = (p << 4) & 0xf0f0f0f0u;   // elements 0,2,4,6 as 16*q
-    const uint32_t odd = p & 0xf0f0f0f0u;           // elements 1,3,5,7 as 16*q
-    // byte i of the 8-byte {odd:even} pair: 0..3 -> even, 4..7 -> odd
-    out_lo = __builtin_amdgcn_perm(odd, even, 0x05010400u);
-    out_hi = __builtin_amdgcn_perm(odd, even, 0x07030602u);
-}
-
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
+typedef __attribute__((address_space(3))) uint8_t lds_byte;
+
+typedef uint32_t v4u __attribute__((ext_vector_type(4)));
+
+// 16-byte LDS read of any 16-byte type
+template <typename T>
+__device__ __forceinline__ T lds_read(const lds_byte* p) {
+    static_assert(sizeof(T) == 16, "16-byte reads only");
+    const v4u v = *reinterpret_cast<const __attribute__((address_space(3))) v4u*>(p);
+    return __builtin_bit_cast(T, v);
+}
 
 // one wave's direct load of 64 x BYTES from per-lane global addresses into
 // LDS at `dst` (wave-uniform), lane L at dst + L * BYTES
 template <int BYTES>
-__device__ __forceinline__ void wave_load_lds(const void* src, uint8_t* dst) {
+__device__ __forceinline__ void wave_load_lds(const void* src, lds_byte* dst) {
     if constexpr (BYTES == 16)
         __builtin_amdgcn_global_load_lds(src, (lds_ptr_t)dst, 16, 0, 0);
     else
         __builtin_amdgcn_global_load_lds(src, (lds_ptr_t)dst, 4, 0, 0);
 }
 
+// the same through a buffer resource: lane L reads BYTES at voff + soff
+template <int BYTES>
+__device__ __forceinline__ void buffer_load_lds(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff, lds_byte* dst) {
+    const uint32_t so = __builtin_amdgcn_readfirstlane(soff);
+    if constexpr (BYTES == 16)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr_t)dst, 16, voff, so, 0, 0);
+    else
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr_t)dst, 4, voff, so, 0, 0);
+}
+
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float v) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, true));
+}
+
+// max over the 16 lanes of a DPP row, result in every lane of the row
+__device__ __forceinline__ float row16_max(float v) {
+    v = fmaxf(v, dpp_f32<0xB1>(v));    // quad_perm [1,0,3,2]
+    v = fmaxf(v, dpp_f32<0x4E>(v));    // quad_perm [2,3,0,1]
+    v = fmaxf(v, dpp_f32<0x141>(v));   // row_half_mirror
+    v = fmaxf(v, dpp_f32<0x140>(v));   // row_mirror
+    return v;
+}
+
 template <int FMT, bool GATEUP, bool DBG>
 __global__ __launch_bounds__(256) void q8_mfma_kernel(const MfmaArgs a) {
     constexpr int kStage = lds_stage_bytes<FMT>();
-    __shared__ __attribute__((aligned(1024))) uint8_t lds[2 * kStage];
+    // the two stage buffers are separate objects, so the compiler can tell
+    // that reading one does not wait for the direct loads into the other
+    __shared__ __attribute__((aligned(1024))) uint8_t lds0[kStage];
+    __shared__ __attribute__((aligned(1024))) uint8_t lds1[kStage];
     const int tile_id = blockIdx.y;
     if (tile_id >= a.meta[1]) return;
     const int4 td = a.tiles[tile_id];
@@ -110,10 +154,11 @@ __global__ __launch_bounds__(256) void q8_mfma_kernel(const MfmaArgs a) {
     const int wm = wave & 1, wn = wave >> 1;
     const int K = a.K, N = a.N, G = K / kGroup, P = G / 2, NT = N / kTile;
     const int T0 = blockIdx.x * (GATEUP ? 2 : 4);      // first 32-row weight tile of the block
-    constexpr float kWScale = FMT == MOE_W_INT8_G32 ? 1.0f : 0.0625f;
+    const int m16_live = (rows + 15) >> 4;               // 16-row tiles holding rows (1 .. 8)
+    const int my_live = min(max(m16_live - 4 * wm, 0), 4);
 
-    // block tile j (0..3) -> matrix and tile index (clamped to the matrix:
-    // loads stay inside it; results of a clamped tile are not stored)
+    // block weight tile j (0..3) -> matrix and tile index (clamped to the
+    // matrix: loads stay inside it; results of a clamped tile are not stored)
     auto tile_of = [&](int j) { return min(T0 + (GATEUP ? (j & 1) : j), NT - 1); };
     auto mat_of = [&](int j) { return GATEUP ? (j >> 1) : 0; };
     const uint8_t* wq[2];
@@ -123,179 +168,248 @@ __global__ __launch_bounds__(256) void q8_mfma_kernel(const MfmaArgs a) {
         wq[m] = M[m].q + eo * M[m].q_stride;
         wsb[m] = M[m].s + eo * M[m].s_stride;
     }
-    // this lane's activation row for the stage loads (row L of the tile,
-    // clamped to the tile's rows: rows past it are computed, never stored)
-    const int arow = row_begin + min(lane, rows - 1);
-    const int asrc = a.row_token ? a.row_token[arow] : arow;
-    const int8_t* arow_ptr = a.a_q + (size_t)asrc * K;
-    const float* srow_ptr = a.a_s + (size_t)asrc * G;
-
-    // stage loads: every wave takes every fourth job
-    auto issue_stage = [&](int st, int buf) {
-        uint8_t* base = lds + buf * kStage;
-        uint8_t* A = base;
-        uint8_t* B = base + kLdsA;
-        uint8_t* SX = B + lds_b_bytes<FMT>();
-        uint8_t* SW = SX + kLdsSX;
-        const int g0 = st * kSG;
-        constexpr int nA = kSG * 2;
-        constexpr int nB = FMT == MOE_W_INT8_G32 ? 4 * kSG : 4 * (kSG / 2);
-        constexpr int nSX = kSG;
-        constexpr int nSW = 2;
-        constexpr int nJobs = nA + nB + nSX + nSW;
+    // activation row of a block row (clamped to the tile's rows: rows past it
+    // are loaded only inside a live 16-row tile and never stored)
+    auto src_row = [&](int r) {
+        const int pr = row_begin + min(r, rows - 1);
+        return a.row_token ? a.row_token[pr] : pr;
+    };
+    // this wave's stage jobs are fixed (job index % 4 == wave): A tiles
+    // i = wave and wave + 4 of both groups, and the scale job of (group
+    // wave / 2, rows 64 * (wave % 2) ..). Activation rows, their scales and
+    // the weight codes are read through buffer resources: the per-lane byte
+    // offset stays in a register for the whole kernel and the stage's offset
+    // goes in a scalar register, so issuing a stage costs no vector ALU work
+    // (and a read past a resource's end returns zeros).
+    uint32_t a_off[2];
 #pragma unroll
-        for (int job = wave; job < nJobs; job += 4) {
+    for (int s = 0; s < 2; ++s)
+        a_off[s] = ((uint32_t)src_row(16 * (wave + 4 * s) + (lane & 15)) * K + 8 * (lane >> 4)) * 2;
+    const uint32_t s_off = (uint32_t)src_row(64 * (wave & 1) + lane) * G * 4;
+    const uint32_t l_off = lane * 16;
+    const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc((void*)a.a_q, 0, a.a_bytes, 0x00020000);
+    const __amdgpu_buffer_rsrc_t rsx = __builtin_amdgcn_make_buffer_rsrc((void*)a.a_s, 0, a.s_bytes, 0x00020000);
+    __amdgpu_buffer_rsrc_t rw[2];
+#pragma unroll
+    for (int m = 0; m < 2; ++m)
+        rw[m] = __builtin_amdgcn_make_buffer_rsrc((void*)wq[m], 0, (int)M[m].q_stride, 0x00020000);
+
+    auto issue_stage = [&](int st, lds_byte* base) __attribute__((always_inline)) {
+        lds_byte* A = base;
+        lds_byte* B = base + kLdsA;
+        lds_byte* SX = B + lds_b_bytes<FMT>();
+        lds_byte* SW = SX + kLdsSX;
+        const int pc = min(st, P - 1);
+        constexpr int nA = kSG * kM16;
+        constexpr int nB = FMT == MOE_W_INT8_G32 ? 4 * kSG : 4;
+        constexpr int nSX = kSG * 2;
+        constexpr int nJobs = nA + nB + nSX + 1;
+        static_assert((nA + nB) % 4 == 0, "scale jobs must start on wave 0");
+#pragma unroll
+        for (int job = 0; job < nJobs; ++job) {
+            if (job % 4 != (wave & 3)) continue;   // wave-uniform
             if (job < nA) {
-                const int g = job >> 1, half = job & 1;
-                const int gc = min(g0 + g, G - 1);
-                wave_load_lds<16>(arow_ptr + gc * kGroup + half * 16, A + (g * 2 + half) * kBM * 16);
+                const int g = job / kM16, i = job % kM16;
+                if (i < m16_live) buffer_load_lds<16>(ra, a_off[i >= 4], (2 * pc + g) * kGroup * 2, A + (g * kM16 + i) * 1024);
             } else if (job < nA + nB) {
                 const int b = job - nA;
                 if constexpr (FMT == MOE_W_INT8_G32) {
                     const int j = b / kSG, g = b % kSG;
-                    const int gc = min(g0 + g, G - 1);
-                    wave_load_lds<16>(wq[mat_of(j)] + ((size_t)gc * NT + tile_of(j)) * 1024 + lane * 16,
-                                      B + (j * kSG + g) * 1024);
+                    buffer_load_lds<16>(rw[mat_of(j)], l_off, ((2 * pc + g) * NT + tile_of(j)) * 1024,
+                                        B + (j * kSG + g) * 1024);
                 } else {
-                    const int j = b / (kSG / 2), pp = b % (kSG / 2);
-                    const int pc = min(g0 / 2 + pp, P - 1);
-                    wave_load_lds<16>(wq[mat_of(j)] + ((size_t)pc * NT + tile_of(j)) * 1024 + lane * 16,
-                                      B + (j * (kSG / 2) + pp) * 1024);
+                    const int j = b;
+                    buffer_load_lds<16>(rw[mat_of(j)], l_off, (pc * NT + tile_of(j)) * 1024, B + j * 1024);
                 }
             } else if (job < nA + nB + nSX) {
-                const int g = job - nA - nB;
-                wave_load_lds<4>(srow_ptr + min(g0 + g, G - 1), SX + g * kBM * 4);
+                // job q = wave: group q / 2, rows 64 * (q % 2) + lane
+                const int q = job - nA - nB;
+                buffer_load_lds<4>(rsx, s_off, (2 * pc + (q >> 1)) * 4, SX + ((q >> 1) * kBM + 64 * (q & 1)) * 4);
             } else {
-                // two tiles' scale blocks for this stage's two pairs, 512 B each
-                const int q = job - nA - nB - nSX;
-                const int j = 2 * q + (lane >> 5);
-                const int pc = min(g0 / 2 + ((lane & 31) >> 4), P - 1);
-                wave_load_lds<16>(wsb[mat_of(j)] + ((size_t)tile_of(j) * P + pc) * 64 + (lane & 15) * 4,
-                                  SW + q * 1024);
+                // the four tiles' scale blocks of pair pc, 256 B each
+                const int j = lane >> 4;
+                wave_load_lds<16>(wsb[mat_of(j)] + ((size_t)tile_of(j) * P + pc) * 64 + (lane & 15) * 4, SW);
             }
         }
     };
 
-    // output rows of accumulator register i: 8*(i/4) + 4*(lane/32) + i%4
-    const int khalf = lane >> 5, ncol = lane & 31;
-    // wave's two MFMA tiles (block tile index j)
-    const int jt0 = GATEUP ? wn : 2 * wn;
+    // output (i, n, r): row 64 wm + 16 i + 4 (lane / 16) + r of the block,
+    // weight row 16 (n % 2) + lane % 16 of the wave's weight tile n / 2
+    const int nl = lane & 15, rq = lane >> 4;
+    const int jt0 = GATEUP ? wn : 2 * wn;       // block weight tiles of the wave
     const int jt1 = GATEUP ? 2 + wn : 2 * wn + 1;
 
-    float acc[2][16];
+    v4f acc[4][4];
 #pragma unroll
-    for (int i = 0; i < 16; ++i) { acc[0][i] = 0.0f; acc[1][i] = 0.0f; }
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int n = 0; n < 4; ++n) acc[i][n] = v4f{0.f, 0.f, 0.f, 0.f};
 
-    const int n_stages = (G + kSG - 1) / kSG;
-    issue_stage(0, 0);
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
-    for (int st = 0; st < n_stages; ++st) {
-        if (st + 1 < n_stages) issue_stage(st + 1, (st + 1) & 1);
-        const uint8_t* base = lds + (st & 1) * kStage;
-        const uint8_t* A = base;
-        const uint8_t* B = base + kLdsA;
-        const float* SX = reinterpret_cast<const float*>(B + lds_b_bytes<FMT>());
-        const float* SW = SX + kSG * kBM;
-        const int g_here = min(kSG, G - st * kSG);
+    // Per-lane LDS byte offsets of the operands inside a stage buffer, kept
+    // opaque to the optimiser: every LDS read is then the buffer plus one
+    // offset plus a constant. The compiler proves that a read of one buffer
+    // does not alias the direct loads into the other only for addresses it
+    // can trace back to the buffer in a few steps; a longer chain makes it
+    // wait for every load in flight.
+    auto opaque = [](int v) __attribute__((always_inline)) {
+        asm volatile("" : "+v"(v));
+        return v;
+    };
+    const int oA = opaque((4 * wm * 64 + lane) * 16);
+    const int oB0 = opaque(kLdsA + (FMT == MOE_W_INT8_G32 ? jt0 * kSG : jt0) * 1024 + lane * 16);
+    const int oB1 = opaque(kLdsA + (FMT == MOE_W_INT8_G32 ? jt1 * kSG : jt1) * 1024 + lane * 16);
+    const int oSX = opaque(kLdsA + lds_b_bytes<FMT>() + (64 * wm + 4 * rq) * 4);
+    const int oSW0 = opaque(kLdsA + lds_b_bytes<FMT>() + kLdsSX + (jt0 * 64 + nl * 4) * 4);
+    const int oSW1 = opaque(kLdsA + lds_b_bytes<FMT>() + kLdsSX + (jt1 * 64 + nl * 4) * 4);
+
+    auto compute = [&](const lds_byte* base, int st) __attribute__((always_inline)) {
+        // [row nl, g0][row 16+nl, g0][row nl, g1][row 16+nl, g1] of each tile
+        // (zero for the padding stage past the last pair)
+        const bool real = st < P;
+        float4 sw0 = lds_read<float4>(base + oSW0);
+        float4 sw1 = lds_read<float4>(base + oSW1);
+        if (!real) sw0 = sw1 = make_float4(0.f, 0.f, 0.f, 0.f);
+        uint4 c4[2];
+        if constexpr (FMT == MOE_W_INT4_G32) {
+            c4[0] = lds_read<uint4>(base + oB0);
+            c4[1] = lds_read<uint4>(base + oB1);
+        }
+        // One group for a wave with LIVE live 16-row tiles. The count is a
+        // compile-time constant inside, so no branch separates a product from
+        // the instructions that read it (the compiler's wait-state insertion
+        // does not cover a matrix-core result read across a branch).
+        auto group = [&](auto live_c, int g) __attribute__((always_inline)) {
+            constexpr int LIVE = decltype(live_c)::value;
+            v8h af[LIVE];
+            float4 sx[LIVE];
 #pragma unroll
-        for (int g = 0; g < kSG; ++g) {
-            if (g >= g_here) break;
-            const v4i af = *reinterpret_cast<const v4i*>(A + ((g * 2 + khalf) * kBM + wm * 32 + ncol) * 16);
-            float sx[16];
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const float4 v = *reinterpret_cast<const float4*>(SX + g * kBM + wm * 32 + 8 * q + 4 * khalf);
-                sx[4 * q] = v.x;
-                sx[4 * q + 1] = v.y;
-                sx[4 * q + 2] = v.z;
-                sx[4 * q + 3] = v.w;
+            for (int i = 0; i < LIVE; ++i) {
+                af[i] = lds_read<v8h>(base + oA + (g * kM16 + i) * 1024);
+                sx[i] = lds_read<float4>(base + oSX + (g * kBM + 16 * i) * 4);
             }
+            // one weight half-tile (16 rows) at a time: convert its codes,
+            // then its products with every live 16-row tile
 #pragma unroll
-            for (int tt = 0; tt < 2; ++tt) {
-                const int j = tt ? jt1 : jt0;
-                v4i bf;
+            for (int n = 0; n < 4; ++n) {
+                const int t = n >> 1, hh = n & 1;
+                v8h bf;
                 if constexpr (FMT == MOE_W_INT8_G32) {
-                    // row ncol, k 16 khalf .. +15: lanes (ncol%16) + 32 khalf (+16) of the block
-                    const uint8_t* blk = B + (j * kSG + g) * 1024 + ((ncol & 15) + 32 * khalf) * 16 + (ncol >> 4) * 8;
-                    const uint2 p0 = *reinterpret_cast<const uint2*>(blk);
-                    const uint2 p1 = *reinterpret_cast<const uint2*>(blk + 256);
-                    bf = v4i{(int)p0.x, (int)p0.y, (int)p1.x, (int)p1.y};
+                    const uint4 c = lds_read<uint4>(base + (t ? oB1 : oB0) + g * 1024);
+                    bf = hh ? codes_to_f16<FMT>(c.z, c.w) : codes_to_f16<FMT>(c.x, c.y);
                 } else {
-                    const uint8_t* blk = B + (j * (kSG / 2) + (g >> 1)) * 1024 + ((ncol & 15) + 32 * khalf) * 16 +
-                                         ((g & 1) * 2 + (ncol >> 4)) * 4;
-                    const uint32_t d0 = *reinterpret_cast<const uint32_t*>(blk);
-                    const uint32_t d1 = *reinterpret_cast<const uint32_t*>(blk + 256);
-                    uint32_t w0, w1, w2, w3;
-                    widen_int4x8(d0, w0, w1);
-                    widen_int4x8(d1, w2, w3);
-                    bf = v4i{(int)w0, (int)w1, (int)w2, (int)w3};
+                    const uint4 c = c4[t];
+                    bf = codes_to_f16<FMT>(g ? (hh ? c.w : c.z) : (hh ? c.y : c.x), 0u);
                 }
-                const v16i zero = {};
-                const v16i d = __builtin_amdgcn_mfma_i32_32x32x32_i8(af, bf, zero, 0, 0, 0);
-                const float sw = SW[(j * (kSG / 2) + (g >> 1)) * 64 + (ncol & 15) * 4 + (g & 1) * 2 + (ncol >> 4)] *
-                                 kWScale;
+                const float4 swt = t ? sw1 : sw0;
+                const float sw = g ? (hh ? swt.w : swt.z) : (hh ? swt.y : swt.x);
 #pragma unroll
-                for (int i = 0; i < 16; ++i) acc[tt][i] = fmaf((float)d[i] * sw, sx[i], acc[tt][i]);
-                if constexpr (DBG) {
-                    const int gg = st * kSG + g;
-                    const int col = GATEUP ? T0 * kTile + 32 * wn + ncol : (T0 + j) * kTile + ncol;
-                    int32_t* dst = (GATEUP && tt == 1) ? a.dbg1 : a.dbg0;
+                for (int i = 0; i < LIVE; ++i) {
+                    const v4f d = __builtin_amdgcn_mfma_f32_16x16x32_f16(af[i], bf, v4f{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+                    acc[i][n][0] = fmaf(d[0], sx[i].x * sw, acc[i][n][0]);
+                    acc[i][n][1] = fmaf(d[1], sx[i].y * sw, acc[i][n][1]);
+                    acc[i][n][2] = fmaf(d[2], sx[i].z * sw, acc[i][n][2]);
+                    acc[i][n][3] = fmaf(d[3], sx[i].w * sw, acc[i][n][3]);
+                    if constexpr (DBG) {
+                        const int jt = t ? jt1 : jt0;
+                        const int wt = T0 + (GATEUP ? (jt & 1) : jt);
+                        const int col = wt * kTile + 16 * hh + nl;
+                        int32_t* dst = (GATEUP && t) ? a.dbg1 : a.dbg0;
 #pragma unroll
-                    for (int i = 0; i < 16; ++i) {
-                        const int row = wm * 32 + 8 * (i >> 2) + 4 * khalf + (i & 3);
-                        if (row >= rows || col >= N) continue;
-                        const int v = FMT == MOE_W_INT8_G32 ? d[i] : (d[i] >> 4);
-                        dst[((size_t)(row_begin + row) * N + col) * G + gg] = v;
+                        for (int r = 0; r < 4; ++r) {
+                            const int row = 64 * wm + 16 * i + 4 * rq + r;
+                            if (row < rows && wt < NT && real)
+                                dst[((size_t)(row_begin + row) * N + col) * G + 2 * st + g] = (int32_t)d[r];
+                        }
                     }
                 }
             }
+        };
+#pragma unroll
+        for (int g = 0; g < kSG; ++g) {
+            // wave-uniform: a wave with 2 or 3 live tiles computes all four
+            // (the rows of a dead tile are never stored)
+            if (my_live >= 2) group(std::integral_constant<int, 4>{}, g);
+            else if (my_live == 1) group(std::integral_constant<int, 1>{}, g);
         }
+    };
+
+    lds_byte* const buf0 = (lds_byte*)lds0;
+    lds_byte* const buf1 = (lds_byte*)lds1;
+    issue_stage(0, buf0);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    // Stages alternate between the buffers; each stage's direct loads for the
+    // next one are in flight while it is multiplied. An odd stage count runs
+    // one more stage whose weight scales are taken as zero (its loads repeat
+    // the last pair), so the loop body has no exit in its middle.
+    const int P2 = (P + 1) & ~1;
+    for (int st = 0; st < P2; st += 2) {
+        issue_stage(st + 1, buf1);
+        compute(buf0, st);
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __syncthreads();
+        if (st + 2 < P2) issue_stage(st + 2, buf0);
+        compute(buf1, st + 1);
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         __syncthreads();
     }
 
     // ---- epilogue ----
     if constexpr (GATEUP) {
-        const int col = T0 * kTile + 32 * wn + ncol;
-        const bool col_ok = T0 + wn < NT;
+        const int t = T0 + wn;                  // weight tile = group of H's columns
         const int GN = N / kGroup;
+        // H column 32 t + kk sits at slot position (kk & ~7) + k_slot(kk & 7)
+        const int pos0 = (nl & 8) + k_slot(FMT, nl & 7);
+        const int pos1 = 16 + pos0;
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            const float h = silu(acc[0][i]) * acc[1][i];
-            float amax = fabsf(h);
+        for (int i = 0; i < 4; ++i) {
+            if (i >= my_live) continue;
 #pragma unroll
-            for (int off = 16; off > 0; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off, kWave));
-            const float dd = __fdiv_rn(amax, 127.0f);
-            const float inv = dd != 0.0f ? __fdiv_rn(1.0f, dd) : 0.0f;
-            float q = rintf(__fmul_rn(h, inv));
-            q = fminf(fmaxf(q, -127.0f), 127.0f);
-            const int row = wm * 32 + 8 * (i >> 2) + 4 * khalf + (i & 3);
-            if (row < rows && col_ok) {
-                const size_t r = (size_t)(row_begin + row);
-                a.hq[r * N + col] = (int8_t)(int)q;
-                if (ncol == 0) a.hd[r * GN + T0 + wn] = dd;
+            for (int r = 0; r < 4; ++r) {
+                const float h0 = silu(acc[i][0][r]) * acc[i][2][r];   // H column 32 t + nl
+                const float h1 = silu(acc[i][1][r]) * acc[i][3][r];   // H column 32 t + 16 + nl
+                const float amax = row16_max(fmaxf(fabsf(h0), fabsf(h1)));
+                const float dd = __fdiv_rn(amax, 127.0f);
+                const float inv = dd != 0.0f ? __fdiv_rn(1.0f, dd) : 0.0f;
+                const float q0 = fminf(fmaxf(rintf(__fmul_rn(h0, inv)), -127.0f), 127.0f);
+                const float q1 = fminf(fmaxf(rintf(__fmul_rn(h1, inv)), -127.0f), 127.0f);
+                const int row = 64 * wm + 16 * i + 4 * rq + r;
+                if (row < rows) {
+                    const size_t R = (size_t)(row_begin + row);
+                    _Float16* hrow = a.hq + R * N + t * kTile;
+                    hrow[pos0] = (_Float16)q0;
+                    hrow[pos1] = (_Float16)q1;
+                    if (nl == 0) a.hd[R * GN + t] = dd;
+                    if constexpr (DBG) {
+                        a.dbg_hq[R * N + t * kTile + nl] = (int8_t)(int)q0;
+                        a.dbg_hq[R * N + t * kTile + 16 + nl] = (int8_t)(int)q1;
+                    }
+                }
             }
         }
     } else {
 #pragma unroll
-        for (int tt = 0; tt < 2; ++tt) {
-            const int t = T0 + (tt ? jt1 : jt0);
+        for (int n = 0; n < 4; ++n) {
+            const int t = T0 + (n < 2 ? jt0 : jt1);
             if (t >= NT) continue;
-            const int col = t * kTile + ncol;
+            const int col = t * kTile + 16 * (n & 1) + nl;
 #pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                const int row = wm * 32 + 8 * (i >> 2) + 4 * khalf + (i & 3);
-                if (row < rows) a.y[(size_t)(row_begin + row) * N + col] = acc[tt][i];
+            for (int i = 0; i < 4; ++i) {
+                if (i >= my_live) continue;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int row = 64 * wm + 16 * i + 4 * rq + r;
+                    if (row < rows) a.y[(size_t)(row_begin + row) * N + col] = acc[i][n][r];
+                }
             }
         }
     }
 }
 
-hipError_t launch_q8_mfma(const moe_experts& routed, const moe_experts* shared, bool gateup, const int8_t* a_q,
-                          const float* a_s, const int* row_token, const int* tiles, const int* meta, int max_tiles,
-                          int8_t* hq, float* hd, float* y, int32_t* dbg0, int32_t* dbg1, hipStream_t st,
-                          hipEvent_t ev0, hipEvent_t ev1) {
+hipError_t launch_q8_mfma(const moe_experts& routed, const moe_experts* shared, bool gateup, const _Float16* a_q,
+                          const float* a_s, int a_rows, const int* row_token, const int* tiles, const int* meta,
+                          int max_tiles, _Float16* hq, float* hd, float* y, int32_t* dbg0, int32_t* dbg1, int8_t* dbg_hq,
+                          hipStream_t st, hipEvent_t ev0, hipEvent_t ev1) {
     if (max_tiles == 0) return hipSuccess;
     MfmaArgs a{};
     a.a_q = a_q;
@@ -307,11 +421,14 @@ hipError_t launch_q8_mfma(const moe_experts& routed, const moe_experts* shared, 
     const int d = routed.d_model, I = routed.d_ff;
     a.K = gateup ? d : I;
     a.N = gateup ? I : d;
+    a.a_bytes = (uint32_t)((size_t)a_rows * a.K * 2);
+    a.s_bytes = (uint32_t)((size_t)a_rows * (a.K / kGroup) * 4);
     a.hq = hq;
     a.hd = hd;
     a.y = y;
     a.dbg0 = dbg0;
     a.dbg1 = dbg1;
+    a.dbg_hq = dbg_hq;
     auto fill = [&](MfmaMat* dst, const moe_experts& ev) {
         const int64_t rowb = ev.format == MOE_W_INT8_G32 ? a.K : a.K / 2;
         const int64_t qs = (int64_t)a.N * rowb, ss = (int64_t)a.N * (a.K / kGroup);

@@ -60,28 +60,32 @@ __device__ __forceinline__ void split_group(const float* __restrict__ x, int T, 
     if (lane == 0) xp.pow[g] = ldexpf(1.0f, ex - 15);
 }
 
-// Q8_0 of one group of one row by 8 lanes (4 values each), in the fp32 steps
-// of quantize_q8_0_kernel: d = amax / 127, inv = 1 / d, q = rne(x * inv).
+// Q8_0 of one group of one row by 4 lanes (one 8-wide slice each), in the
+// fp32 steps of quantize_q8_0_kernel: d = amax / 127, inv = 1 / d,
+// q = rne(x * inv). The codes leave as f16 (exact) in operand-slot order,
+// ready to be a matrix-core operand.
+template <int FMT>
 __device__ __forceinline__ void q8_item(const float* __restrict__ x, int d, int G, int item, const XPrep& xp) {
-    const int sub = threadIdx.x & 7;
+    const int sub = threadIdx.x & 3;
     const int t = item / G, g = item - t * G;
-    const size_t off = (size_t)t * d + g * kGroup + 4 * sub;
-    const float4 v = *reinterpret_cast<const float4*>(x + off);
-    float amax = fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w)));
-    amax = fmaxf(amax, __shfl_xor(amax, 1, 8));
-    amax = fmaxf(amax, __shfl_xor(amax, 2, 8));
-    amax = fmaxf(amax, __shfl_xor(amax, 4, 8));
+    const size_t off = (size_t)t * d + g * kGroup + 8 * sub;
+    const float4 a = *reinterpret_cast<const float4*>(x + off);
+    const float4 b = *reinterpret_cast<const float4*>(x + off + 4);
+    const float v[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+    float amax = 0.0f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) amax = fmaxf(amax, fabsf(v[j]));
+    amax = fmaxf(amax, __shfl_xor(amax, 1, 4));
+    amax = fmaxf(amax, __shfl_xor(amax, 2, 4));
     const float dd = __fdiv_rn(amax, 127.0f);
     const float inv = dd != 0.0f ? __fdiv_rn(1.0f, dd) : 0.0f;
-    const float vals[4] = {v.x, v.y, v.z, v.w};
-    uint32_t packed = 0;
+    v8h q;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        float r = rintf(__fmul_rn(vals[j], inv));
-        r = fminf(fmaxf(r, -127.0f), 127.0f);
-        packed |= ((uint32_t)((int)r & 0xff)) << (8 * j);
+    for (int j = 0; j < 8; ++j) {
+        const float r = rintf(__fmul_rn(v[slot_k(FMT, j)], inv));
+        q[j] = (_Float16)fminf(fmaxf(r, -127.0f), 127.0f);
     }
-    *reinterpret_cast<uint32_t*>(xp.q + off) = packed;
+    *reinterpret_cast<v8h*>(xp.q + off) = q;
     if (sub == 0) xp.qd[item] = dd;
 }
 
@@ -95,9 +99,11 @@ __device__ __forceinline__ void xprep_waves(const float* __restrict__ x, int T, 
         }
     } else if (xp.mode == XPREP_Q8_0) {
         const int items = T * G;
-        for (int base = gw * 8; base < items; base += nw * 8) {
-            const int item = base + ((threadIdx.x & 63) >> 3);
-            if (item < items) q8_item(x, d, G, item, xp);
+        for (int base = gw * 16; base < items; base += nw * 16) {
+            const int item = base + ((threadIdx.x & 63) >> 2);
+            if (item >= items) continue;
+            if (xp.fmt == MOE_W_INT8_G32) q8_item<MOE_W_INT8_G32>(x, d, G, item, xp);
+            else q8_item<MOE_W_INT4_G32>(x, d, G, item, xp);
         }
     }
 }
@@ -250,7 +256,7 @@ hipError_t launch_router_logits(const float* x, int T, int d, const float* wg, i
 hipError_t launch_xprep(const float* x, int T, int d, const XPrep& xp, hipStream_t st) {
     if (T == 0 || xp.mode == XPREP_NONE) return hipSuccess;
     const int G = d / kGroup;
-    const int waves = xp.mode == XPREP_SPLIT ? G : (T * G + 7) / 8;
+    const int waves = xp.mode == XPREP_SPLIT ? G : (T * G + 15) / 16;
     hipLaunchKernelGGL(xprep_kernel, dim3((waves + 3) / 4), dim3(256), 0, st, x, T, d, xp);
     return hipGetLastError();
 }
