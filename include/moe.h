@@ -87,7 +87,7 @@ typedef enum {
 
 typedef enum {
     MOE_ACT_F32 = 0,   /* fp32 activations x dequantised weights (decode GEMV path) */
-    MOE_ACT_Q8_0 = 1   /* Q8_0 int8 activations, int8 matrix-core dots (prefill / verify path) */
+    MOE_ACT_Q8_0 = 1   /* Q8_0 int8 activations, exact integer dots on the matrix cores (prefill / verify path) */
 } moe_act_mode;
 
 /* Timed stages of moe_layer_forward_timed. */
@@ -222,7 +222,8 @@ moe_status moe_dispatch(const int32_t* topk_idx, int32_t T, int32_t k, int32_t E
  *   counts, offsets, perm   as produced by moe_dispatch for (T, k, E)
  *   act_mode MOE_ACT_F32: fp32 activations times dequantised weights, fp32
  *            accumulation. MOE_ACT_Q8_0: x is Q8_0-quantised per token, each
- *            32-group gives an exact int32 dot on the int8 matrix cores,
+ *            32-group gives an exact integer dot (int8 x int8 or int4 codes,
+ *            summed exactly on the matrix cores),
  *            rescaled by both group scales; H = silu(G)*U is Q8_0-quantised
  *            again before the down projection.
  *   y_perm  device fp32 [T*k, d]: row p is expert e's output for token
@@ -272,7 +273,7 @@ moe_status moe_layer_forward_timed(const float* x, int32_t T, const float* gate_
                                    void* ws, size_t ws_bytes, const hipEvent_t* stage_events,
                                    hipStream_t stream);
 
-/* Test hook for the Q8_0 path: runs the production int8 matrix-core kernels
+/* Test hook for the Q8_0 path: runs the production matrix-core kernels
  * of moe_expert_ffn(act_mode = MOE_ACT_Q8_0) and also writes their exact
  * int32 per-group dots and the Q8_0 codes of H. With R = T*k rows in
  * permuted order:
