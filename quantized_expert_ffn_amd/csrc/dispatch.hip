@@ -2,19 +2,21 @@
 // implemented": in prefill and verification each distinct expert is read once
 // and applied to every position routed to it).
 //
-// One block of 1024 threads does the whole job in LDS, with no atomics and no
-// host round trip:
-//   1. each of the 16 waves takes a contiguous chunk of the flat assignments
-//      f = t*k + j and walks it 64 at a time; lanes with the same expert find
-//      each other with one ballot per bit of the expert id, which gives every
-//      assignment its rank among equal experts earlier in the chunk, and a
-//      per-wave histogram row;
-//   2. the per-wave histograms are scanned (over waves, then over experts)
-//      into counts, offsets and each wave's starting position per expert;
-//   3. position = start + rank, so the permutation is stable by construction.
-// The same block then writes the work lists the expert kernels consume:
-// slots (one per expert with rows, then the shared expert), int8-MFMA tiles
-// of kTileRows rows, and the row -> token map.
+// All of it runs in one block, in LDS, with no atomics and no host round
+// trip. Small batches (up to kWaveDispatchMax assignments, the decode case)
+// take a single wave and never touch a block barrier:
+//   1. it walks the flat assignments f = t*k + j 64 at a time; lanes with the
+//      same expert find each other with one ballot per bit of the expert id,
+//      which ranks every assignment among equal experts of the pass, and a
+//      running count per expert in LDS carries the rank across passes;
+//   2. each lane scans a run of experts and the runs are scanned across the
+//      wave into counts, offsets, slot and tile positions;
+//   3. position = offset + rank, so the permutation is stable by construction.
+// Large batches spread step 1 over the 16 waves of a 1024-thread block (a
+// histogram row per wave, scanned over waves and then over experts).
+// Both then write the work lists the expert kernels consume: slots (one per
+// expert with rows, then the shared expert), prefill tiles of kTileRows rows,
+// and the row -> token map.
 //
 // For small batches the router's top-k runs in the same block first (one wave
 // per token), so the routing reaches the dispatch through LDS.
@@ -198,6 +200,115 @@ __device__ __forceinline__ void dispatch_block(const int* idx, int* tmp, int T, 
     }
 }
 
+// Wave-wide exclusive scan of one value per lane; *total gets the sum.
+__device__ __forceinline__ int wave_exclusive_scan(int v, int* total) {
+    const int lane = threadIdx.x & 63;
+    int incl = v;
+#pragma unroll
+    for (int off = 1; off < kWave; off <<= 1) {
+        const int o = __shfl_up(incl, off, kWave);
+        if (lane >= off) incl += o;
+    }
+    *total = __shfl(incl, kWave - 1, kWave);
+    return incl - v;
+}
+
+// The same dispatch by one wave, for small batches (the decode case): no
+// block barrier anywhere, every LDS access is the wave's own and in order.
+// cnt_l, off_l: E ints of LDS each; rank_l: n ints (LDS or global).
+constexpr int kWaveDispatchMax = 2048;   // assignments (32 passes of 64)
+__device__ __forceinline__ void dispatch_wave(const int* idx, int* rank_l, int T, int k, int E,
+                                              int* __restrict__ counts, int* __restrict__ offsets,
+                                              int* __restrict__ perm, int* __restrict__ inv_perm, int has_shared,
+                                              int tile_rows, int* __restrict__ row_token, int* __restrict__ slots,
+                                              int* __restrict__ tiles, int* __restrict__ meta, int* cnt_l,
+                                              int* off_l) {
+    const int lane = threadIdx.x & 63;
+    const int n = T * k;
+    const int nbits = E > 1 ? 32 - __clz(E - 1) : 0;
+    const uint64_t lt = lanemask_lt();
+    for (int e = lane; e < E; e += kWave) cnt_l[e] = 0;
+    bool bad = false;
+    // stable rank among equal experts: earlier passes through the running
+    // count, earlier lanes of this pass through the ballots
+    for (int base = 0; base < n; base += kWave) {
+        const int f = base + lane;
+        const bool valid = f < n;
+        const int e = valid ? idx[f] : 0;
+        const bool inr = valid && e >= 0 && e < E;
+        bad |= valid && !inr;
+        uint64_t peers = __ballot(inr);
+        for (int b = 0; b < nbits; ++b) {
+            const bool bit = (e >> b) & 1;
+            const uint64_t m = __ballot(inr && bit);
+            peers &= bit ? m : ~m;
+        }
+        const int rank = __popcll(peers & lt);
+        const int prior = inr ? cnt_l[e] : 0;
+        if (inr && rank == __popcll(peers) - 1) cnt_l[e] = prior + __popcll(peers);
+        if (inr) rank_l[f] = prior + rank;
+    }
+    // offsets: each lane scans a contiguous run of experts, the runs are
+    // scanned across the wave
+    const int epl = (E + kWave - 1) / kWave;
+    const int e0 = min(lane * epl, E), e1 = min(e0 + epl, E);
+    int run = 0, act = 0, ntl = 0;
+    for (int e = e0; e < e1; ++e) {
+        const int c = cnt_l[e];
+        run += c;
+        act += c > 0;
+        ntl += (c + tile_rows - 1) / tile_rows;
+    }
+    int total = 0, n_active = 0, n_tiles = 0;
+    int off = wave_exclusive_scan(run, &total);
+    int slot = wave_exclusive_scan(act, &n_active);
+    int tile = wave_exclusive_scan(ntl, &n_tiles);
+    for (int e = e0; e < e1; ++e) {
+        const int c = cnt_l[e];
+        counts[e] = c;
+        offsets[e] = off;
+        off_l[e] = off;
+        if (slots && c > 0) {
+            reinterpret_cast<int4*>(slots)[slot++] = make_int4(e, off, c, 0);
+            for (int rb = off; rb < off + c; rb += tile_rows)
+                reinterpret_cast<int4*>(tiles)[tile++] = make_int4(e, rb, min(off + c, rb + tile_rows), 0);
+        }
+        off += c;
+    }
+    if (lane == 0) offsets[E] = total;
+    // final positions
+    for (int base = 0; base < n; base += kWave) {
+        const int f = base + lane;
+        if (f >= n) break;
+        const int e = idx[f];
+        if (e < 0 || e >= E) continue;
+        const int pos = off_l[e] + rank_l[f];
+        perm[pos] = f;
+        inv_perm[f] = pos;
+        if (row_token) row_token[pos] = f / k;
+    }
+    if (row_token && has_shared)
+        for (int t = lane; t < T; t += kWave) row_token[n + t] = t;
+    if (slots) {
+        if (has_shared) {
+            const int shared_tiles = (T + tile_rows - 1) / tile_rows;
+            for (int i = lane; i < shared_tiles; i += kWave) {
+                const int rb = n + i * tile_rows;
+                reinterpret_cast<int4*>(tiles)[n_tiles + i] = make_int4(E, rb, min(n + T, rb + tile_rows), 0);
+            }
+            if (lane == 0) reinterpret_cast<int4*>(slots)[n_active] = make_int4(E, n, T, 0);
+            n_tiles += shared_tiles;
+            n_active += 1;
+        }
+        const bool any_bad = __ballot(bad) != 0;
+        if (lane == 0) {
+            meta[0] = n_active;
+            meta[1] = n_tiles;
+            meta[2] = any_bad ? 1 : 0;
+        }
+    }
+}
+
 __global__ __launch_bounds__(kDispThreads) void dispatch_kernel(const int* __restrict__ idx, int T, int k, int E,
                                                                  int* __restrict__ counts, int* __restrict__ offsets,
                                                                  int* __restrict__ perm, int* __restrict__ inv_perm,
@@ -207,6 +318,13 @@ __global__ __launch_bounds__(kDispThreads) void dispatch_kernel(const int* __res
                                                                  int* __restrict__ meta) {
     extern __shared__ __attribute__((aligned(16))) int lds[];
     __shared__ int bad_flag;
+    if (T * k <= kWaveDispatchMax) {
+        // ranks between the passes go through inv_perm itself
+        if (threadIdx.x < kWave)
+            dispatch_wave(idx, inv_perm, T, k, E, counts, offsets, perm, inv_perm, has_shared, tile_rows, row_token,
+                          slots, tiles, meta, lds, lds + E);
+        return;
+    }
     dispatch_block(idx, inv_perm, T, k, E, counts, offsets, perm, inv_perm, has_shared, tile_rows, row_token, slots,
                    tiles, meta, lds, lds + kDispWaves * E, &bad_flag);
 }
@@ -244,8 +362,11 @@ __global__ __launch_bounds__(kDispThreads) void route_dispatch_kernel(const Topk
         idx_l[wave * k + lane] = my_e;
     }
     __syncthreads();
-    dispatch_block(idx_l, rank_l, T, k, E, counts, offsets, perm, inv_perm, has_shared, tile_rows, row_token, slots,
-                   tiles, meta, hist, scan_tmp, &bad_flag);
+    (void)scan_tmp;
+    (void)bad_flag;
+    if (wave == 0)
+        dispatch_wave(idx_l, rank_l, T, k, E, counts, offsets, perm, inv_perm, has_shared, tile_rows, row_token, slots,
+                      tiles, meta, hist, hist + E);
 }
 
 // Work lists for moe_expert_ffn from a caller's counts / offsets / perm.
@@ -287,8 +408,9 @@ hipError_t launch_route_dispatch(const float* logits, int T, int d, const moe_ro
     if (T > kDispWaves) return hipErrorInvalidValue;
     const TopkArgs a = topk_args(logits, T, d, p);
     const size_t lds = route_dispatch_lds_bytes(T, p.top_k, p.n_experts, p.mode);
+    const int threads = (T > 0 ? T : 1) * kWave;   // one wave per token; wave 0 then dispatches
 #define MOE_RD(EPL)                                                                                              \
-    hipLaunchKernelGGL(route_dispatch_kernel<EPL>, dim3(1), dim3(kDispThreads), lds, st, a, idx, w, counts, offsets, \
+    hipLaunchKernelGGL(route_dispatch_kernel<EPL>, dim3(1), dim3(threads), lds, st, a, idx, w, counts, offsets,     \
                        perm, inv_perm, has_shared, kTileRows, row_token, slots, tiles, meta)
     switch (topk_epl(p.n_experts)) {
         case 1: MOE_RD(1); break;
@@ -304,8 +426,10 @@ hipError_t launch_route_dispatch(const float* logits, int T, int d, const moe_ro
 hipError_t launch_dispatch(const int* idx, int T, int k, int E, int* counts, int* offsets, int* perm,
                            int* inv_perm, int has_shared, int* row_token, int* slots, int* tiles, int* meta,
                            hipStream_t st) {
-    hipLaunchKernelGGL(dispatch_kernel, dim3(1), dim3(kDispThreads), dispatch_lds_bytes(E), st, idx, T, k, E,
-                       counts, offsets, perm, inv_perm, has_shared, kTileRows, row_token, slots, tiles, meta);
+    // small batches: one wave does it all (dispatch_wave)
+    const int threads = (int64_t)T * k <= kWaveDispatchMax ? kWave : kDispThreads;
+    hipLaunchKernelGGL(dispatch_kernel, dim3(1), dim3(threads), dispatch_lds_bytes(E), st, idx, T, k, E, counts,
+                       offsets, perm, inv_perm, has_shared, kTileRows, row_token, slots, tiles, meta);
     return hipGetLastError();
 }
 
