@@ -30,6 +30,7 @@ if ROOT not in sys.path:
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 INT8_PEAK_TOPS = 5000.0        # MI355X dense int8 matrix cores (5.0 POPS)
+GEMV_MAX_T = 16               # Q8_0 batches up to this many tokens run on the GEMV
 F16_PEAK_TFLOPS = 2500.0       # MI355X dense f16 matrix cores (2.5 PFLOP/s): the prefill products run here
 MALL_DEFEAT_BYTES = 2 << 30    # rotate through at least this much weight memory
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
@@ -209,14 +210,17 @@ def main():
     counts_h = counts.cpu().numpy()
 
     d, I, fmt = shape.d_model, shape.d_ff, shape.wformat
-    # the kernel the library launches for the gate/up stage of this workload
-    if wl.act_mode == "f32":
-        kfile, kname = ("gemv.hip", "gateup_gemv")
+    # the kernel the library launches for the gate/up stage of this workload:
+    # the GEMV for decode and for Q8_0 batches of up to 16 tokens (HBM bound),
+    # the tiled matrix-core GEMM for prefill (matrix-core bound)
+    gemv = wl.act_mode == "f32" or T <= GEMV_MAX_T
+    if gemv:
+        kfile, kname = "gemv.hip", ("gateup_gemv" if wl.act_mode == "f32" else "gateup_gemv_q8")
     else:
         kfile, kname = "mfma_gemm.hip", "gateup_q8_mfma"
     kernel_sources = [os.path.join(ROOT, "quantized_expert_ffn_amd", "csrc", kfile)]
-    if wl.act_mode == "f32":
-        algo = acc.gateup_kernel_bytes(counts_h, T, shape.top_k, d, I, fmt, shape.shared_expert, "f32")
+    if gemv:
+        algo = acc.gateup_kernel_bytes(counts_h, T, shape.top_k, d, I, fmt, shape.shared_expert, wl.act_mode)
         achieved = algo / (kernel_ms * 1e-3) / 1e9
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4)}

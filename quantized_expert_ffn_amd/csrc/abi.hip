@@ -152,30 +152,47 @@ moe_status run_experts(int T, int k, const moe_experts& routed, const moe_expert
     const int* slots = ws_at<int>(ws, L.slots);
     const int* tiles = ws_at<int>(ws, L.tiles);
     const int* meta = ws_at<int>(ws, L.meta);
+    const int max_slots = (E < n ? E : n) + has_shared;
+    const int R = n + (has_shared ? T : 0);
     if (act_mode == MOE_ACT_F32) {
-        const int max_slots = (E < n ? E : n) + has_shared;
-        const int R = n + (has_shared ? T : 0);
         const _Float16* ahi = ws_at<_Float16>(ws, L.xq);
         const _Float16* alo = ws_at<_Float16>(ws, L.xd);
         const float* apow = ws_at<float>(ws, L.xp);
         _Float16* hhi = ws_at<_Float16>(ws, L.h);
         _Float16* hlo = ws_at<_Float16>(ws, L.hd);
         float* hpow = ws_at<float>(ws, L.hp);
-        MOE_HIP(moe::launch_gemv(routed, shared, true, ahi, alo, apow, row_token, T, R, slots, meta, max_slots, hhi,
-                                 hlo, hpow, nullptr, st, stage_ev(ev, 2 * MOE_STAGE_GATEUP),
+        MOE_HIP(moe::launch_gemv(routed, shared, true, false, ahi, alo, apow, row_token, T, R, slots, meta, max_slots,
+                                 hhi, hlo, hpow, nullptr, st, stage_ev(ev, 2 * MOE_STAGE_GATEUP),
                                  stage_ev(ev, 2 * MOE_STAGE_GATEUP + 1)),
                 "gate/up GEMV");
-        MOE_HIP(moe::launch_gemv(routed, shared, false, hhi, hlo, hpow, nullptr, R, R, slots, meta, max_slots, nullptr,
-                                 nullptr, nullptr, y, st, stage_ev(ev, 2 * MOE_STAGE_DOWN),
+        MOE_HIP(moe::launch_gemv(routed, shared, false, false, hhi, hlo, hpow, nullptr, R, R, slots, meta, max_slots,
+                                 nullptr, nullptr, nullptr, y, st, stage_ev(ev, 2 * MOE_STAGE_DOWN),
                                  stage_ev(ev, 2 * MOE_STAGE_DOWN + 1)),
                 "down GEMV");
+        return MOE_OK;
+    }
+    if (T <= moe::kGemvMaxT && dots_gate == nullptr) {
+        // Q8_0 with a handful of tokens (verification): every slot holds at
+        // most T <= 16 rows, so the GEMV reads each weight once, with the
+        // same exact integer group dots as the tiled kernel
+        _Float16* xq = ws_at<_Float16>(ws, L.xq);
+        float* xd = ws_at<float>(ws, L.xd);
+        _Float16* hq = ws_at<_Float16>(ws, L.h);
+        float* hd = ws_at<float>(ws, L.hd);
+        MOE_HIP(moe::launch_gemv(routed, shared, true, true, xq, nullptr, xd, row_token, T, R, slots, meta, max_slots,
+                                 hq, nullptr, hd, nullptr, st, stage_ev(ev, 2 * MOE_STAGE_GATEUP),
+                                 stage_ev(ev, 2 * MOE_STAGE_GATEUP + 1)),
+                "gate/up GEMV (Q8_0)");
+        MOE_HIP(moe::launch_gemv(routed, shared, false, true, hq, nullptr, hd, nullptr, R, R, slots, meta, max_slots,
+                                 nullptr, nullptr, nullptr, y, st, stage_ev(ev, 2 * MOE_STAGE_DOWN),
+                                 stage_ev(ev, 2 * MOE_STAGE_DOWN + 1)),
+                "down GEMV (Q8_0)");
         return MOE_OK;
     }
     const _Float16* xq = ws_at<_Float16>(ws, L.xq);
     const float* xd = ws_at<float>(ws, L.xd);
     _Float16* hq = ws_at<_Float16>(ws, L.h);
     float* hd = hd_out ? hd_out : ws_at<float>(ws, L.hd);
-    const int R = n + (has_shared ? T : 0);
     MOE_HIP(moe::launch_q8_mfma(routed, shared, true, xq, xd, T, row_token, tiles, meta, L.max_tiles, hq, hd, nullptr,
                                 dots_gate, dots_up, hq_out, st, stage_ev(ev, 2 * MOE_STAGE_GATEUP),
                                 stage_ev(ev, 2 * MOE_STAGE_GATEUP + 1)),

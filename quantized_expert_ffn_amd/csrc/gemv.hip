@@ -37,9 +37,14 @@
 namespace moe {
 
 struct GemvArgs {
-    const _Float16* ahi;    // activation parts in slot order: gate/up [T, K] token rows, down [R, K]
+    // f32 path: activation parts in slot order (gate/up [T, K] token rows,
+    // down [R, K]) and powers of two (gate/up [K/32]; down [R, K/32] at the
+    // first row of each 16-row tile). Q8_0 path: ahi holds the Q8_0 codes as
+    // f16 in slot order, alo is unused and apow holds the per-row scales
+    // [rows, K/32].
+    const _Float16* ahi;
     const _Float16* alo;
-    const float* apow;      // gate/up [K/32]; down [R, K/32] at the first row of each 16-row tile
+    const float* apow;
     const int* row_token;   // gate/up: permuted row -> token row of ahi / alo
     int a_rows;             // rows of ahi / alo
     const int4* slots;      // (expert, row_begin, n_rows, 0)
@@ -50,10 +55,12 @@ struct GemvArgs {
     const float* ss[2];
     int64_t q_stride, s_stride;   // per expert (bytes, floats)
     int E, K, N, R;
-    // gate/up output: H as parts + powers of two for the down kernel
+    // gate/up output, as the down kernel reads it: f32 path H as parts +
+    // powers of two ([R, N/32] at the first row of each 16-row tile); Q8_0
+    // path H's codes as f16 in hhi and its per-row scales in hpow [R, N/32]
     _Float16* hhi;
     _Float16* hlo;
-    float* hpow;            // [R, N/32]: row = first row of a 16-row tile
+    float* hpow;
     // down output
     float* y;               // [R, N]
 };
@@ -67,10 +74,16 @@ constexpr int kMaxGemvGroups = 256;   // K <= 8192
 // fragments (L2) alike; loads retire in order, so both streams keep the same
 // depth. Scales come four pairs per load and reach their lanes through
 // ds_bpermute.
-template <int FMT, bool GATEUP, int KS>
+//
+// Q8 (Q8_0 activations, the small-batch verification case): the activation
+// operand is the codes themselves, exact in f16 like the weight codes, so one
+// product per group gives the exact integer group dot and no lo part is
+// needed; both group scales are applied to it per output (the activation
+// scale varies by row, from an LDS table of the tile's 16 rows).
+template <int FMT, bool GATEUP, int KS, bool Q8>
 __global__ __launch_bounds__(64 * KS) void gemv_kernel(const GemvArgs a) {
     constexpr int kCL = FMT == MOE_W_INT8_G32 ? 2 : 1;   // 16-byte code loads per tile per pair
-    __shared__ float pwtab[kMaxGemvGroups];
+    __shared__ float pwtab[Q8 ? 16 * kMaxGemvGroups : kMaxGemvGroups];   // Q8: [group][16 rows]
     __shared__ float red[KS > 1 ? KS - 1 : 1][2][2][4][64];
 
     const int slot = blockIdx.y;
@@ -109,7 +122,7 @@ __global__ __launch_bounds__(64 * KS) void gemv_kernel(const GemvArgs a) {
     // wave ks takes a contiguous run of pairs [c0, c0 + n_my)
     const int c0 = ks * P / KS;
     const int n_my = (ks + 1) * P / KS - c0;
-    if constexpr (GATEUP) {
+    if constexpr (GATEUP && !Q8) {
         for (int i = threadIdx.x; i < G; i += 64 * KS) pwtab[i] = a.apow[i];
     }
 
@@ -125,7 +138,18 @@ __global__ __launch_bounds__(64 * KS) void gemv_kernel(const GemvArgs a) {
         const int prow = row_begin + mt + 4 * h;   // output rows 4h .. 4h+3 of the tile
 
         __syncthreads();   // pwtab is written; the previous tile's readers of red are done
-        if constexpr (!GATEUP) {
+        if constexpr (Q8) {
+            for (int i = threadIdx.x; i < 16 * G; i += 64 * KS) {
+                const int g = i >> 4, rr = i & 15;
+                float v = 0.0f;
+                if (rr < rows_here) {
+                    const int ar = GATEUP ? a.row_token[row_begin + mt + rr] : row_begin + mt + rr;
+                    v = a.apow[(size_t)ar * G + g];
+                }
+                pwtab[i] = v;
+            }
+            __syncthreads();
+        } else if constexpr (!GATEUP) {
             for (int i = threadIdx.x; i < G; i += 64 * KS) pwtab[i] = a.apow[(size_t)(row_begin + mt) * G + i];
             __syncthreads();
         }
@@ -154,7 +178,9 @@ __global__ __launch_bounds__(64 * KS) void gemv_kernel(const GemvArgs a) {
 #pragma unroll
             for (int gi = 0; gi < 2; ++gi) {
                 xh[sp][gi] = __builtin_bit_cast(v8h, __builtin_amdgcn_raw_buffer_load_b128(rah, a_voff, (2 * p + gi) * 64, 0));
-                xl[sp][gi] = __builtin_bit_cast(v8h, __builtin_amdgcn_raw_buffer_load_b128(ral, a_voff, (2 * p + gi) * 64, 0));
+                if constexpr (!Q8)
+                    xl[sp][gi] =
+                        __builtin_bit_cast(v8h, __builtin_amdgcn_raw_buffer_load_b128(ral, a_voff, (2 * p + gi) * 64, 0));
             }
         };
         // scales of pairs c0 + 4q .. + 3 (those past the run are read but unused)
@@ -168,7 +194,16 @@ __global__ __launch_bounds__(64 * KS) void gemv_kernel(const GemvArgs a) {
         // (= j % 4) of the current quad
         auto step = [&](int jj, int j, int r) {
             const int p = c0 + j;
-            const float pw0 = pwtab[2 * p], pw1 = pwtab[2 * p + 1];
+            float pw0 = 0.0f, pw1 = 0.0f;
+            float4 sx[2];
+            if constexpr (Q8) {
+                // activation scales of the lane's rows 4h .. 4h+3, both groups
+                sx[0] = *reinterpret_cast<const float4*>(&pwtab[(2 * p) * 16 + 4 * h]);
+                sx[1] = *reinterpret_cast<const float4*>(&pwtab[(2 * p + 1) * 16 + 4 * h]);
+            } else {
+                pw0 = pwtab[2 * p];
+                pw1 = pwtab[2 * p + 1];
+            }
             const int src = (nl + 16 * r) * 4;
             float sc[2][4];
 #pragma unroll
@@ -195,14 +230,27 @@ __global__ __launch_bounds__(64 * KS) void gemv_kernel(const GemvArgs a) {
                     }
                     v4f d0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(xh[jj][gi], b0, v4f{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
                     v4f d1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(xh[jj][gi], b1, v4f{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
-                    d0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(xl[jj][gi], b0, d0, 0, 0, 0);
-                    d1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(xl[jj][gi], b1, d1, 0, 0, 0);
-                    const float f0 = sc[t][2 * gi] * pw;
-                    const float f1 = sc[t][2 * gi + 1] * pw;
+                    if constexpr (Q8) {
+                        const float s0 = sc[t][2 * gi], s1 = sc[t][2 * gi + 1];
+                        const float4 x = sx[gi];
+                        acc[t][0][0] = fmaf(d0[0], s0 * x.x, acc[t][0][0]);
+                        acc[t][0][1] = fmaf(d0[1], s0 * x.y, acc[t][0][1]);
+                        acc[t][0][2] = fmaf(d0[2], s0 * x.z, acc[t][0][2]);
+                        acc[t][0][3] = fmaf(d0[3], s0 * x.w, acc[t][0][3]);
+                        acc[t][1][0] = fmaf(d1[0], s1 * x.x, acc[t][1][0]);
+                        acc[t][1][1] = fmaf(d1[1], s1 * x.y, acc[t][1][1]);
+                        acc[t][1][2] = fmaf(d1[2], s1 * x.z, acc[t][1][2]);
+                        acc[t][1][3] = fmaf(d1[3], s1 * x.w, acc[t][1][3]);
+                    } else {
+                        d0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(xl[jj][gi], b0, d0, 0, 0, 0);
+                        d1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(xl[jj][gi], b1, d1, 0, 0, 0);
+                        const float f0 = sc[t][2 * gi] * pw;
+                        const float f1 = sc[t][2 * gi + 1] * pw;
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        acc[t][0][i] = fmaf(d0[i], f0, acc[t][0][i]);
-                        acc[t][1][i] = fmaf(d1[i], f1, acc[t][1][i]);
+                        for (int i = 0; i < 4; ++i) {
+                            acc[t][0][i] = fmaf(d0[i], f0, acc[t][0][i]);
+                            acc[t][1][i] = fmaf(d1[i], f1, acc[t][1][i]);
+                        }
                     }
                 }
             }
@@ -264,7 +312,35 @@ __global__ __launch_bounds__(64 * KS) void gemv_kernel(const GemvArgs a) {
         }
         if (ks != 0) continue;
 
-        if constexpr (GATEUP) {
+        if constexpr (GATEUP && Q8) {
+            // H = silu(G) * U, then Q8_0 of each token's 32 columns (one group
+            // of the down projection's reduction axis) in the fp32 steps of the
+            // quantiser: d = amax / 127, q = rne(h * (1 / d))
+            const int GN = N / kGroup;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const float h0 = silu(acc[0][0][i]) * acc[1][0][i];   // column nl
+                const float h1 = silu(acc[0][1][i]) * acc[1][1][i];   // column 16 + nl
+                float am = fmaxf(fabsf(h0), fabsf(h1));
+                am = fmaxf(am, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(am), 0xB1, 0xF, 0xF, true)));
+                am = fmaxf(am, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(am), 0x4E, 0xF, 0xF, true)));
+                am = fmaxf(am, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(am), 0x141, 0xF, 0xF, true)));
+                am = fmaxf(am, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(am), 0x140, 0xF, 0xF, true)));
+                const float dd = __fdiv_rn(am, 127.0f);
+                const float inv = dd != 0.0f ? __fdiv_rn(1.0f, dd) : 0.0f;
+                if (4 * h + i < rows_here) {
+                    const size_t row = (size_t)(prow + i);
+#pragma unroll
+                    for (int r = 0; r < 2; ++r) {
+                        const int kk = 16 * r + nl;
+                        const int pos = 8 * (kk >> 3) + k_slot(FMT, kk & 7);
+                        const float q = fminf(fmaxf(rintf(__fmul_rn(r ? h1 : h0, inv)), -127.0f), 127.0f);
+                        a.hhi[row * N + (size_t)tile[0] * kGroup + pos] = (_Float16)q;
+                    }
+                    if (nl == 0) a.hpow[row * GN + tile[0]] = dd;
+                }
+            }
+        } else if constexpr (GATEUP) {
             // H = silu(G) * U for tokens 4h + i and columns nl, 16 + nl of the
             // tile: 16 tokens x 32 columns, one group of the down projection's
             // reduction axis, one power of two for all of it
@@ -329,7 +405,7 @@ static int choose_ks(int slots, int blocks_x, int P) {
     return ks;
 }
 
-hipError_t launch_gemv(const moe_experts& routed, const moe_experts* shared, bool gateup, const _Float16* ahi,
+hipError_t launch_gemv(const moe_experts& routed, const moe_experts* shared, bool gateup, bool q8, const _Float16* ahi,
                        const _Float16* alo, const float* apow, const int* row_token, int a_rows, int R,
                        const int* slots, const int* meta, int max_slots, _Float16* hhi, _Float16* hlo, float* hpow,
                        float* y, hipStream_t st, hipEvent_t ev0, hipEvent_t ev1) {
@@ -369,7 +445,11 @@ hipError_t launch_gemv(const moe_experts& routed, const moe_experts* shared, boo
     const int bx = gateup ? tiles : (tiles + 1) / 2;
     const int ks = choose_ks(max_slots, bx, a.K / (2 * kGroup));
     const dim3 grid(bx, max_slots);
-#define MOE_GEMV(FMT, GU, KSV) launch_timed(gemv_kernel<FMT, GU, KSV>, grid, dim3(64 * KSV), st, ev0, ev1, a)
+#define MOE_GEMV(FMT, GU, KSV)                                                                           \
+    do {                                                                                                 \
+        if (q8) launch_timed(gemv_kernel<FMT, GU, KSV, true>, grid, dim3(64 * KSV), st, ev0, ev1, a);    \
+        else launch_timed(gemv_kernel<FMT, GU, KSV, false>, grid, dim3(64 * KSV), st, ev0, ev1, a);      \
+    } while (0)
 #define MOE_GEMV_KS(FMT, GU)                \
     if (ks == 1) MOE_GEMV(FMT, GU, 1);      \
     else if (ks == 2) MOE_GEMV(FMT, GU, 2); \

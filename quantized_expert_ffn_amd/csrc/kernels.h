@@ -52,7 +52,12 @@ hipError_t launch_plan(const int* counts, const int* offsets, const int* perm, i
 // [T, d] (read through row_token) with one power of two per 32-group, [d/32];
 // it writes H's parts [R, I] with one power per (16-row tile of a slot,
 // 32-group), [R, I/32]. down: A = H's parts -> Y fp32 [R, d].
-hipError_t launch_gemv(const moe_experts& routed, const moe_experts* shared, bool gateup, const _Float16* ahi,
+// q8 (small-batch Q8_0 path): A = Q8_0 codes as f16 in slot order with
+// per-row scales in apow ([rows, K/32]); gate/up writes H's Q8_0 codes to hhi
+// and its per-row scales to hpow; alo and hlo are unused. Every slot must
+// hold at most 16 rows for the weights to be read once (T <= 16).
+constexpr int kGemvMaxT = 16;   // the Q8_0 path takes the GEMV up to this many tokens
+hipError_t launch_gemv(const moe_experts& routed, const moe_experts* shared, bool gateup, bool q8, const _Float16* ahi,
                        const _Float16* alo, const float* apow, const int* row_token, int a_rows, int R,
                        const int* slots, const int* meta, int max_slots, _Float16* hhi, _Float16* hlo, float* hpow,
                        float* y, hipStream_t st, hipEvent_t ev_start = nullptr, hipEvent_t ev_stop = nullptr);
