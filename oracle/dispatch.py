@@ -14,6 +14,10 @@ idx[t, j]. The dispatch is:
     inv_perm   = the inverse permutation: inv_perm[perm[p]] = p
 Rows offsets[e] .. offsets[e+1]-1 of the permuted order belong to expert e,
 in increasing f (so in increasing token) order.
+
+An assignment to expert -1 is a slot dropped by the adaptive expert top-p: it
+is not counted, its inv_perm entry is -1, and perm lists the kept assignments
+only, followed by -1 up to T*k entries.
 """
 from __future__ import annotations
 
@@ -23,12 +27,15 @@ import numpy as np
 def dispatch(idx: np.ndarray, n_experts: int):
     """Returns (counts, offsets, perm, inv_perm), all int32."""
     flat = np.asarray(idx).reshape(-1).astype(np.int64)
-    if flat.size and (flat.min() < 0 or flat.max() >= n_experts):
+    if flat.size and (flat.min() < -1 or flat.max() >= n_experts):
         raise ValueError("expert index out of range")
-    counts = np.bincount(flat, minlength=n_experts)
+    kept = np.nonzero(flat >= 0)[0]
+    counts = np.bincount(flat[kept], minlength=n_experts)
     offsets = np.concatenate([[0], np.cumsum(counts)])
-    perm = np.argsort(flat, kind="stable")
-    inv = np.empty_like(perm)
-    inv[perm] = np.arange(perm.size)
+    order = kept[np.argsort(flat[kept], kind="stable")]
+    perm = np.full(flat.size, -1, dtype=np.int64)
+    perm[:order.size] = order
+    inv = np.full(flat.size, -1, dtype=np.int64)
+    inv[order] = np.arange(order.size)
     return (counts.astype(np.int32), offsets.astype(np.int32),
             perm.astype(np.int32), inv.astype(np.int32))

@@ -32,15 +32,19 @@ class RouterSpec:
     topk_group: int = 1
     routed_scaling_factor: float = 1.0
     bias: Optional[np.ndarray] = None
+    top_p: float = 0.0           # adaptive expert top-p; 0 (or >= 1) keeps all k
 
 
 def route(x, wg, spec: RouterSpec):
     if spec.mode == "softmax":
-        return router.route_softmax(x, wg, spec.top_k, spec.renormalize)
-    if spec.mode == "noaux_tc":
-        return router.route_noaux_tc(x, wg, spec.bias, spec.top_k, spec.n_group,
-                                     spec.topk_group, spec.routed_scaling_factor)
-    raise ValueError(f"unknown router mode {spec.mode}")
+        idx, w, l = router.route_softmax(x, wg, spec.top_k, spec.renormalize)
+    elif spec.mode == "noaux_tc":
+        idx, w, l = router.route_noaux_tc(x, wg, spec.bias, spec.top_k, spec.n_group,
+                                          spec.topk_group, spec.routed_scaling_factor)
+    else:
+        raise ValueError(f"unknown router mode {spec.mode}")
+    idx, w = router.apply_top_p(idx, w, spec.top_p)
+    return idx, w, l
 
 
 def expert_rows(x, ex: ffn.QuantExpert, act_mode: str):
@@ -53,8 +57,10 @@ def expert_rows(x, ex: ffn.QuantExpert, act_mode: str):
 
 def combine(y_perm, w, inv_perm, shared_y=None):
     t, k = w.shape
-    gathered = y_perm[np.asarray(inv_perm).reshape(t, k)]        # [T, k, d]
-    out = np.einsum("tk,tkd->td", np.asarray(w, np.float64), gathered)
+    inv = np.asarray(inv_perm).reshape(t, k)
+    gathered = y_perm[np.maximum(inv, 0)]                         # [T, k, d]
+    wk = np.where(inv >= 0, np.asarray(w, np.float64), 0.0)       # dropped slots add nothing
+    out = np.einsum("tk,tkd->td", wk, gathered)
     if shared_y is not None:
         out = out + shared_y
     return out

@@ -161,3 +161,70 @@ def test_dispatch_invariants_and_brute_force():
         for ex in range(e):
             seg = perm[offsets[ex]:offsets[ex + 1]]
             assert np.all(flat[seg] == ex) and np.all(np.diff(seg) > 0)
+
+
+# ---------------------------------------------------------------------------
+# adaptive expert top-p (the reading: shortest prefix in selection order whose
+# mass reaches top_p of the selected total, kept weights rescaled to that total)
+# ---------------------------------------------------------------------------
+def test_top_p_off_keeps_everything():
+    rng = np.random.default_rng(5)
+    idx = rng.integers(0, 64, size=(7, 8)).astype(np.int32)
+    w = rng.random((7, 8))
+    for p in (0.0, 1.0, 1.5):
+        i2, w2 = router.apply_top_p(idx, w, p)
+        assert np.array_equal(i2, idx) and np.array_equal(w2, w)
+
+
+def test_top_p_hand_worked_example():
+    # weights 0.5, 0.3, 0.2 (sum 1), top_p 0.7: the mass before the slots is
+    # 0, 0.5, 0.8, so slots 0 and 1 stay (0.5 < 0.7) and slot 2 goes; the kept
+    # 0.8 is rescaled to 1: 0.625, 0.375
+    idx = np.array([[11, 4, 9]], dtype=np.int32)
+    w = np.array([[0.5, 0.3, 0.2]])
+    i2, w2 = router.apply_top_p(idx, w, 0.7)
+    assert i2.tolist() == [[11, 4, -1]]
+    assert np.allclose(w2, [[0.625, 0.375, 0.0]], rtol=0, atol=1e-15)
+
+
+@pytest.mark.parametrize("k,p", [(8, 0.7), (8, 0.3), (10, 0.55), (4, 0.9), (6, 0.01)])
+def test_top_p_equal_weights_keep_ceil_pk(k, p):
+    # equal weights: the mass before slot j is j/k of the total, so slot j
+    # stays iff j < p*k, which keeps ceil(p*k) slots (p*k not an integer)
+    w = np.full((3, k), 2.5 / k)
+    idx = np.tile(np.arange(k, dtype=np.int32), (3, 1))
+    i2, w2 = router.apply_top_p(idx, w, p)
+    n_keep = int(np.ceil(p * k))
+    assert (i2 >= 0).sum(axis=1).tolist() == [n_keep] * 3
+    assert np.allclose(w2[:, :n_keep], 2.5 / n_keep) and np.all(w2[:, n_keep:] == 0)
+
+
+def test_top_p_dominant_first_slot_and_invariants():
+    rng = np.random.default_rng(9)
+    w = rng.random((200, 8)) + 0.01
+    w[0] = [0.9, 0.05, 0.02, 0.01, 0.01, 0.005, 0.003, 0.002]      # slot 0 alone reaches 0.7
+    w = -np.sort(-w, axis=1) * 2.5 / w.sum(axis=1, keepdims=True)  # selection order, sum 2.5
+    idx = np.tile(np.arange(8, dtype=np.int32), (200, 1))
+    i2, w2 = router.apply_top_p(idx, w, 0.7)
+    assert i2[0].tolist() == [0, -1, -1, -1, -1, -1, -1, -1] and np.isclose(w2[0, 0], 2.5)
+    assert np.allclose(w2.sum(axis=1), 2.5)                        # total mass kept
+    kept = i2 >= 0
+    assert np.all(kept[:, 0])                                      # at least one slot
+    assert np.all(kept[:, :-1] >= kept[:, 1:])                     # dropped slots form a suffix
+    # a larger top_p never keeps fewer slots
+    for p_lo, p_hi in ((0.3, 0.5), (0.5, 0.7), (0.7, 0.95)):
+        a, _ = router.apply_top_p(idx, w, p_lo)
+        b, _ = router.apply_top_p(idx, w, p_hi)
+        assert np.all((a >= 0).sum(axis=1) <= (b >= 0).sum(axis=1))
+
+
+def test_dispatch_skips_dropped_slots():
+    idx = np.array([[3, 1, -1], [1, -1, -1], [0, 3, 2]], dtype=np.int32)
+    counts, offsets, perm, inv = dispatch.dispatch(idx, 4)
+    assert counts.tolist() == [1, 2, 1, 2]
+    assert offsets.tolist() == [0, 1, 3, 4, 6]
+    # kept flat assignments sorted by (expert, f): e0: 6; e1: 1, 3; e2: 8; e3: 0, 7
+    assert perm.tolist() == [6, 1, 3, 8, 0, 7, -1, -1, -1]
+    assert inv.tolist() == [4, 1, -1, 2, -1, -1, 0, 5, 3]
+    with pytest.raises(ValueError):
+        dispatch.dispatch(np.array([[4, -2]]), 4)
