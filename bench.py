@@ -88,7 +88,8 @@ def cpu_baseline(wl, target_s: float):
 
     spec = olayer.RouterSpec(mode=shape.router, top_k=shape.top_k, renormalize=shape.renormalize,
                              n_group=shape.n_group, topk_group=shape.topk_group,
-                             routed_scaling_factor=shape.routed_scaling_factor, bias=synth.score_bias(shape))
+                             routed_scaling_factor=shape.routed_scaling_factor, bias=synth.score_bias(shape),
+                             top_p=wl.top_p or shape.top_p)
     wg = synth.gate_weight(shape)
     shared = expert(shape.n_experts) if shape.shared_expert else None
     # sample: the whole batch for decode; a prefix of tokens for prefill
@@ -134,6 +135,7 @@ def main():
     print(f"[bench] {wl.name}: building {copies} device copies of the layer "
           f"({per_copy / 1e6:.1f} MB each)", file=sys.stderr, flush=True)
     layer = dl.build(shape, dev, copies=copies)
+    params = qe.with_top_p(layer.params, wl.top_p) if wl.top_p else layer.params
     T = wl.tokens
     x = dl.activations(shape, T, dev)
     out = torch.empty((T, shape.d_model), dtype=torch.float32, device=dev)
@@ -143,9 +145,9 @@ def main():
     def step(i, evs=None):
         c = i % copies
         if evs is None:
-            qe.moe_layer_forward(x, layer.gate_w, layer.params, layer.routed[c], layer.shared[c], act, out, ws)
+            qe.moe_layer_forward(x, layer.gate_w, params, layer.routed[c], layer.shared[c], act, out, ws)
         else:
-            qe.moe_layer_forward_timed(x, layer.gate_w, layer.params, layer.routed[c], layer.shared[c], act, out,
+            qe.moe_layer_forward_timed(x, layer.gate_w, params, layer.routed[c], layer.shared[c], act, out,
                                        ws, evs)
 
     for i in range(args.warmup):
@@ -201,7 +203,7 @@ def main():
     # the routing of this batch (identical every step): distinct experts for the byte count
     idx = torch.empty((T, shape.top_k), dtype=torch.int32, device=dev)
     wts = torch.empty((T, shape.top_k), dtype=torch.float32, device=dev)
-    qe.moe_route(x, layer.gate_w, layer.params, idx, wts, ws)
+    qe.moe_route(x, layer.gate_w, params, idx, wts, ws)
     counts = torch.empty(shape.n_experts, dtype=torch.int32, device=dev)
     offsets = torch.empty(shape.n_experts + 1, dtype=torch.int32, device=dev)
     perm = torch.empty(T * shape.top_k, dtype=torch.int32, device=dev)
@@ -254,7 +256,8 @@ def main():
         "config": {"workload": wl.name, "tokens": T, "d_model": d, "n_experts": shape.n_experts, "d_ff": I,
                    "top_k": shape.top_k, "router": shape.router, "weights": f"{fmt} group 32",
                    "act_mode": wl.act_mode, "shared_expert": shape.shared_expert,
-                   "distinct_experts": int((counts_h > 0).sum()), "device_copies": copies},
+                   "distinct_experts": int((counts_h > 0).sum()), "routed_rows": int(counts_h.sum()),
+                   "top_p": wl.top_p or shape.top_p, "device_copies": copies},
         "roofline": roof,
         "timing": {"launch": "eager" if args.no_graph else "hip_graph",
                    "eager_ms_per_step": round(eager_elapsed * 1e3 / args.steps, 5),

@@ -116,6 +116,15 @@ typedef enum {
  *   routed_scaling_factor noaux_tc: multiplies the normalised weights.
  *   score_bias  noaux_tc: device fp32 [E] added to the sigmoid scores for
  *               selection only (NULL = zero). Ignored by softmax mode.
+ *   top_p       adaptive expert top-p ("Show HN: Getting GLM-5.2 running on
+ *               my slow computer", section "Useful knobs"), both modes. With S
+ *               the sum of a token's k weights, slot j is kept when j == 0 or
+ *               the weights of slots 0 .. j-1 sum to less than top_p * S; the
+ *               kept weights are rescaled to sum to S, and a dropped slot
+ *               gets expert -1 and weight 0 (dropped slots are always the
+ *               last ones). 0, or any value >= 1, keeps all k slots; a
+ *               negative or NaN value is MOE_ERR_INVALID_ARG. The keep
+ *               decisions are taken in fp32.
  */
 typedef struct {
     int32_t n_experts;
@@ -126,6 +135,7 @@ typedef struct {
     int32_t topk_group;
     float routed_scaling_factor;
     const float* score_bias;
+    float top_p;
 } moe_router_params;
 
 /* A stack of n_experts quantised SwiGLU experts (device pointers), each
@@ -193,6 +203,7 @@ moe_status moe_quantize_q8_0(const float* x, int64_t rows, int32_t cols,
  *            first (logit in softmax mode, sigmoid + bias in noaux_tc mode),
  *            equal keys to the lower expert id.
  *   topk_w   device fp32 [T, k]: the weight of each selected expert.
+ *            With top_p, dropped slots hold -1 and 0.
  *   ws       device workspace (moe_workspace_size with this T, k, E, d).
  * Logits are fp32 on the GPU; a selection whose margin lies within fp32
  * rounding of the logits may differ from an exact-arithmetic ranking.
@@ -203,14 +214,17 @@ moe_status moe_route(const float* x, int32_t T, int32_t d, const float* gate_w,
 
 /* Dispatch for batch-union ("Show HN: Getting GLM-5.2 running on my slow computer", section "What's
  * implemented": each distinct expert is read once for all of its positions).
- *   topk_idx device int32 [T, k], values in [0, E).
+ *   topk_idx device int32 [T, k], values in [0, E), or -1 for a slot
+ *            dropped by top_p.
  *   counts   device int32 [E]      assignments per expert
  *   offsets  device int32 [E + 1]  exclusive prefix sum of counts
  *   perm     device int32 [T*k]    flat assignments f = t*k + j, stably
- *                                  sorted by expert (so by f within one)
- *   inv_perm device int32 [T*k]    inv_perm[perm[p]] = p
- * Entries of topk_idx outside [0, E) are skipped (not counted), leaving
- * the permutation incomplete; they never cause an out-of-bounds access.
+ *                                  sorted by expert (so by f within one);
+ *                                  entries past offsets[E] are -1
+ *   inv_perm device int32 [T*k]    inv_perm[perm[p]] = p; -1 for a slot
+ *                                  that is not dispatched
+ * A -1 entry is a dropped slot (not counted). Other entries outside [0, E)
+ * are skipped the same way; they never cause an out-of-bounds access.
  */
 moe_status moe_dispatch(const int32_t* topk_idx, int32_t T, int32_t k, int32_t E,
                         int32_t* counts, int32_t* offsets, int32_t* perm, int32_t* inv_perm,

@@ -46,7 +46,8 @@ class MoeError(RuntimeError):
 class RouterParams(ctypes.Structure):
     _fields_ = [("n_experts", ctypes.c_int32), ("top_k", ctypes.c_int32), ("mode", ctypes.c_int32),
                 ("renormalize", ctypes.c_int32), ("n_group", ctypes.c_int32), ("topk_group", ctypes.c_int32),
-                ("routed_scaling_factor", ctypes.c_float), ("score_bias", ctypes.c_void_p)]
+                ("routed_scaling_factor", ctypes.c_float), ("score_bias", ctypes.c_void_p),
+                ("top_p", ctypes.c_float)]
 
 
 class Experts(ctypes.Structure):
@@ -136,7 +137,7 @@ def _stream(stream) -> Optional[int]:
 
 def router_params(n_experts: int, top_k: int, mode: str = "softmax", renormalize: bool = False,
                   n_group: int = 1, topk_group: int = 1, routed_scaling_factor: float = 1.0,
-                  score_bias: Optional[torch.Tensor] = None) -> RouterParams:
+                  score_bias: Optional[torch.Tensor] = None, top_p: float = 0.0) -> RouterParams:
     p = RouterParams()
     p.n_experts = n_experts
     p.top_k = top_k
@@ -146,8 +147,18 @@ def router_params(n_experts: int, top_k: int, mode: str = "softmax", renormalize
     p.topk_group = topk_group
     p.routed_scaling_factor = routed_scaling_factor
     p.score_bias = _ptr(score_bias, torch.float32, "score_bias")
+    p.top_p = top_p
     p._keep = score_bias      # keep the bias tensor alive with the struct
     return p
+
+
+def with_top_p(params: RouterParams, top_p: float) -> RouterParams:
+    """A copy of a router parameter set with another adaptive expert top-p."""
+    q = RouterParams()
+    ctypes.memmove(ctypes.addressof(q), ctypes.addressof(params), ctypes.sizeof(RouterParams))
+    q.top_p = top_p
+    q._keep = getattr(params, "_keep", None)
+    return q
 
 
 class QuantExperts:

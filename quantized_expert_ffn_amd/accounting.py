@@ -54,7 +54,7 @@ def gateup_kernel_bytes(counts: Sequence[int], T: int, k: int, d: int, d_ff: int
     """Algorithmic bytes of the gate/up kernel: distinct experts' gate and up
     weights once, the activations once, H written once."""
     n = distinct_experts(counts) + (1 if has_shared else 0)
-    rows = T * k + (T if has_shared else 0)
+    rows = int(sum(counts)) + (T if has_shared else 0)     # routed rows (T*k unless top-p dropped some)
     if act_mode == "f32":
         x_bytes = T * d * 4
         h_bytes = rows * d_ff * 4

@@ -58,6 +58,8 @@ moe_status check_router(const moe_router_params* p, int E_expected) {
     MOE_REQUIRE(E <= moe::kMaxExperts, MOE_ERR_UNSUPPORTED, "n_experts = %d > %d", E, moe::kMaxExperts);
     MOE_REQUIRE(k >= 1 && k <= E, MOE_ERR_INVALID_ARG, "top_k = %d outside [1, n_experts = %d]", k, E);
     MOE_REQUIRE(k <= 64, MOE_ERR_UNSUPPORTED, "top_k = %d > 64", k);
+    MOE_REQUIRE(p->top_p >= 0.0f, MOE_ERR_INVALID_ARG, "top_p = %g must be >= 0 (0 keeps every slot)",
+                (double)p->top_p);   // also rejects NaN
     if (p->mode == MOE_ROUTER_SOFTMAX_TOPK) return MOE_OK;
     MOE_REQUIRE(p->mode == MOE_ROUTER_SIGMOID_NOAUX_TC, MOE_ERR_INVALID_ARG, "unknown router mode %d", p->mode);
     MOE_REQUIRE(p->n_group >= 1, MOE_ERR_INVALID_ARG, "n_group = %d must be >= 1", p->n_group);

@@ -1,4 +1,5 @@
-// Combine: out[t] = sum_j w[t, j] * Y[inv_perm[t*k + j]] + S[t].
+// Combine: out[t] = sum_j w[t, j] * Y[inv_perm[t*k + j]] + S[t], over the
+// dispatched slots (inv_perm >= 0; a slot dropped by top-p adds nothing).
 //
 // The weighted sum of a token's k expert outputs plus the shared expert
 // ("Show HN: Getting GLM-5.2 running on my slow computer", section "What's implemented": shared expert). Each
@@ -22,6 +23,7 @@ __global__ __launch_bounds__(64) void combine_kernel(const float* __restrict__ y
     for (int j = 0; j < k; ++j) {
         const float wj = w[(size_t)t * k + j];
         const int row = inv_perm[(size_t)t * k + j];
+        if (row < 0) continue;   // a slot dropped by top-p (uniform across the block)
         const float4 v = reinterpret_cast<const float4*>(y + (size_t)row * d)[c];
         acc.x = fmaf(wj, v.x, acc.x);
         acc.y = fmaf(wj, v.y, acc.y);

@@ -132,7 +132,7 @@ __device__ __forceinline__ void dispatch_block(const int* idx, int* tmp, int T, 
             const bool valid = f < end;
             const int e = ev[u];
             const bool inr = valid && e >= 0 && e < E;
-            if (valid && !inr) *bad_flag = 1;
+            if (valid && !inr && e != -1) *bad_flag = 1;   // -1: a slot dropped by top-p
             uint64_t peers = __ballot(inr);
             for (int b = 0; b < nbits; ++b) {
                 const bool bit = (e >> b) & 1;
@@ -183,13 +183,18 @@ __device__ __forceinline__ void dispatch_block(const int* idx, int* tmp, int T, 
         for (int u = 0; u < kPB; ++u) {
             const int f = base + u * kWave + lane;
             const int e = ev[u];
-            if (f >= end || e < 0 || e >= E) continue;
+            if (f >= end) continue;
+            if (e < 0 || e >= E) {
+                inv_perm[f] = -1;
+                continue;
+            }
             const int pos = my_hist[e] + rv[u];
             perm[pos] = f;
             inv_perm[f] = pos;
             if (row_token) row_token[pos] = f / k;
         }
     }
+    for (int p = total + tid; p < n; p += kDispThreads) perm[p] = -1;
     if (row_token && has_shared)
         for (int t = tid; t < T; t += kDispThreads) row_token[n + t] = t;
 
@@ -236,7 +241,7 @@ __device__ __forceinline__ void dispatch_wave(const int* idx, int* rank_l, int T
         const bool valid = f < n;
         const int e = valid ? idx[f] : 0;
         const bool inr = valid && e >= 0 && e < E;
-        bad |= valid && !inr;
+        bad |= valid && !inr && e != -1;   // -1: a slot dropped by top-p
         uint64_t peers = __ballot(inr);
         for (int b = 0; b < nbits; ++b) {
             const bool bit = (e >> b) & 1;
@@ -276,17 +281,22 @@ __device__ __forceinline__ void dispatch_wave(const int* idx, int* rank_l, int T
         off += c;
     }
     if (lane == 0) offsets[E] = total;
-    // final positions
+    // final positions; assignments not dispatched get inv_perm -1 and the
+    // permutation's unused tail is -1
     for (int base = 0; base < n; base += kWave) {
         const int f = base + lane;
         if (f >= n) break;
         const int e = idx[f];
-        if (e < 0 || e >= E) continue;
+        if (e < 0 || e >= E) {
+            inv_perm[f] = -1;
+            continue;
+        }
         const int pos = off_l[e] + rank_l[f];
         perm[pos] = f;
         inv_perm[f] = pos;
         if (row_token) row_token[pos] = f / k;
     }
+    for (int p = total + lane; p < n; p += kWave) perm[p] = -1;
     if (row_token && has_shared)
         for (int t = lane; t < T; t += kWave) row_token[n + t] = t;
     if (slots) {

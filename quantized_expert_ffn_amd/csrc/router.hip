@@ -228,6 +228,7 @@ TopkArgs topk_args(const float* logits, int T, int d, const moe_router_params& p
     a.topk_group = p.topk_group;
     a.rsf = p.routed_scaling_factor;
     a.bias = p.score_bias;
+    a.top_p = (p.top_p > 0.0f && p.top_p < 1.0f) ? p.top_p : 0.0f;
     return a;
 }
 

@@ -92,6 +92,7 @@ struct TopkArgs {
     int mode, renorm, n_group, topk_group;
     float rsf;
     const float* bias;   // [E] or null
+    float top_p;         // adaptive expert top-p in (0, 1), or 0 = off
 };
 
 TopkArgs topk_args(const float* logits, int T, int d, const moe_router_params& p);
@@ -234,6 +235,22 @@ __device__ __forceinline__ void topk_token(const TopkArgs& a, int t, bool active
     } else {
         const float tot = wave_sum_all(lane < k ? wj : 0.0f);
         wj = wj / tot * a.rsf;
+    }
+    if (a.top_p > 0.0f) {
+        // adaptive expert top-p: keep slot j while the slots before it hold
+        // less than top_p of the total, then rescale the kept ones to the total
+        const float w_in = lane < k ? wj : 0.0f;
+        float incl = w_in;
+#pragma unroll
+        for (int off = 1; off < kWave; off <<= 1) {
+            const float o = __shfl_up(incl, off, kWave);
+            if (lane >= off) incl += o;
+        }
+        const float tot = __shfl(incl, kWave - 1, kWave);
+        const bool keep = lane < k && (lane == 0 || incl - w_in < a.top_p * tot);
+        const float kept = wave_sum_all(keep ? wj : 0.0f);
+        wj = keep ? wj * (tot / kept) : 0.0f;
+        if (!keep) my_e = -1;
     }
     *out_e = my_e;
     *out_w = wj;

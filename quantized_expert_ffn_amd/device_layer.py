@@ -68,7 +68,7 @@ def build(shape: synth.LayerShape, device="cuda", copies: int = 1, chunk: Option
     b = synth.score_bias(shape)
     bias = torch.from_numpy(b).to(device) if b is not None else None
     params = _lib.router_params(E, shape.top_k, shape.router, shape.renormalize, shape.n_group,
-                                shape.topk_group, shape.routed_scaling_factor, bias)
+                                shape.topk_group, shape.routed_scaling_factor, bias, shape.top_p)
     return DeviceLayer(shape, gate_w, bias, routed_list, shared_list, params)
 
 

@@ -59,6 +59,7 @@ class LayerShape:
     shared_expert: bool = False
     wformat: str = "int8"       # "int8" | "int4"  (group 32, fp32 scales)
     zipf_s: float = 0.0         # > 0: Zipf(s) log-prior on the router logits
+    top_p: float = 0.0          # adaptive expert top-p (0: keep all k)
 
 
 @dataclasses.dataclass(frozen=True)
@@ -67,7 +68,8 @@ class Workload:
     name: str
     layer: LayerShape
     tokens: int
-    act_mode: str               # "f32" (decode GEMV) | "q8_0" (int8 MFMA)
+    act_mode: str               # "f32" (decode GEMV) | "q8_0" (integer-dot path)
+    top_p: float = 0.0          # > 0: adaptive expert top-p for this workload
 
 
 LAYERS = {
@@ -95,6 +97,9 @@ WORKLOADS = {
     "glm_b1": Workload("glm_b1", LAYERS["glm"], 1, "f32"),
     "glm_verify4": Workload("glm_verify4", LAYERS["glm"], 4, "q8_0"),
     "qwen_prefill": Workload("qwen_prefill", LAYERS["qwen"], 4096, "q8_0"),
+    # the pages' decode knob: adaptive expert top-p 0.7
+    "glm_b1_topp": Workload("glm_b1_topp", LAYERS["glm"], 1, "f32", top_p=0.7),
+    "olmoe_b16_topp": Workload("olmoe_b16_topp", LAYERS["olmoe"], 16, "f32", top_p=0.7),
 }
 
 

@@ -198,3 +198,12 @@ def test_untile_helpers_invert_the_documented_layout(fmt):
     stored = codes.astype(np.int8) if fmt == "int8" else oquant.pack_int4(codes.astype(np.int8))
     assert np.array_equal(untile_codes(qflat, N, K, fmt), stored)
     assert np.array_equal(untile_scales(sflat, N, K), scales)
+
+
+def test_router_top_p_validation(lib):
+    for bad in (-0.1, float("nan")):
+        p = _params(top_p=bad)
+        assert lib.moe_route(FAKE, 4, 64, FAKE, ctypes.byref(p), FAKE, FAKE, FAKE, 1 << 30, None) == INVALID
+        assert _fwd(lib, params=p) == INVALID
+    # a struct built field by field leaves top_p at 0: every slot kept
+    assert _params().top_p == 0.0

@@ -5,6 +5,8 @@ indices (tokens whose selection margin is wider than fp32 logit rounding),
 counts, offsets, the permutation and its inverse, int32 group dots.
 Tolerance: every floating-point output tensor within 2e-3 * max|ref|.
 """
+import dataclasses
+
 import numpy as np
 import pytest
 import torch
@@ -23,6 +25,7 @@ from gpu_common import (REL_TOL, assert_close_rel, device_layer, need_gpu, oracl
 pytestmark = pytest.mark.gpu
 
 MARGIN_EPS = 1e-5      # logits closer than this may rank differently in fp32 vs fp64
+TOPP_EPS = 1e-5        # top-p mass this close (relative) to the threshold may decide differently
 
 
 # ---------------------------------------------------------------------------
@@ -81,24 +84,34 @@ def check_route(x, wg, spec: olayer.RouterSpec, bias=None):
     E = wg.shape[0]
     bias_d = torch.from_numpy(bias).cuda() if bias is not None else None
     params = qe.router_params(E, spec.top_k, spec.mode, spec.renormalize, spec.n_group, spec.topk_group,
-                              spec.routed_scaling_factor, bias_d)
+                              spec.routed_scaling_factor, bias_d, spec.top_p)
     gi, gw = gpu_route(x, wg, params, spec.top_k)
-    ri, rw, l = olayer.route(x, wg, spec)
+    ri0, rw0, l = olayer.route(x, wg, dataclasses.replace(spec, top_p=0.0))
+    ri, rw = orouter.apply_top_p(ri0, rw0, spec.top_p)
     keys = orouter.selection_keys(l, spec.mode, spec.bias, spec.n_group, spec.topk_group)
     margin = orouter.boundary_margin(keys, spec.top_k)
     if spec.mode == "noaux_tc":
         margin = np.minimum(margin, orouter.group_margin(l, spec.bias, spec.n_group, spec.topk_group))
     near = margin < MARGIN_EPS
-    say(f"[route] T={x.shape[0]} E={E} k={spec.top_k} mode={spec.mode}: min margin {margin.min():.3e}, "
-        f"near-ties {int(near.sum())}")
+    # top-p: a token whose kept mass lies within fp32 rounding of the threshold
+    near_p = orouter.top_p_margin(rw0, spec.top_p) < TOPP_EPS
+    say(f"[route] T={x.shape[0]} E={E} k={spec.top_k} mode={spec.mode} top_p={spec.top_p}: "
+        f"min margin {margin.min():.3e}, near-ties {int(near.sum())}, near top-p {int(near_p.sum())}")
     # bit-exact wherever fp32 rounding cannot reorder the boundary
-    assert np.array_equal(gi[~near], ri[~near])
+    ok = ~near & ~near_p
+    assert np.array_equal(gi[ok], ri[ok])
     # near-tie tokens: the GPU choice must be a valid top-k within the margin
     for t in np.nonzero(near)[0]:
-        sel = keys[t, gi[t]]
-        rest = np.delete(keys[t], gi[t])
-        assert sel.min() >= rest.max() - MARGIN_EPS
-    ok = ~near
+        kept = gi[t][gi[t] >= 0]
+        rest = np.setdiff1d(np.arange(E), kept)
+        if rest.size:
+            assert keys[t, kept].min() >= keys[t, rest].max() - MARGIN_EPS
+    # near top-p tokens: the kept slots are a prefix of the oracle's selection,
+    # one slot longer or shorter at most
+    for t in np.nonzero(near_p & ~near)[0]:
+        n_gpu, n_ref = int((gi[t] >= 0).sum()), int((ri[t] >= 0).sum())
+        assert abs(n_gpu - n_ref) <= 1 and np.array_equal(gi[t][:n_gpu], ri0[t][:n_gpu])
+    assert np.all(gi[:, 0] >= 0)
     assert np.allclose(gw[ok], rw[ok], rtol=1e-5, atol=1e-7)
     return gi, gw
 
@@ -136,6 +149,22 @@ def test_route_noaux_tc_variants(e, n_group, topk_group, k):
     wg = (synth.gate_weight(lay) * 15).astype(np.float32)      # logits of order 1
     spec = router_spec(lay)
     check_route(x, wg, spec, synth.score_bias(lay))
+
+
+@pytest.mark.parametrize("mode", ["softmax", "noaux_tc"])
+@pytest.mark.parametrize("top_p", [0.3, 0.7, 0.95])
+def test_route_top_p(mode, top_p):
+    need_gpu()
+    if mode == "softmax":
+        lay = synth.variant(synth.LAYERS["tiny"], n_experts=64, top_k=8, renormalize=False, top_p=top_p)
+    else:
+        lay = synth.variant(synth.LAYERS["tiny"], router="noaux_tc", n_experts=64, n_group=8, topk_group=4,
+                            top_k=8, has_bias=True, routed_scaling_factor=2.5, top_p=top_p)
+    x = synth.activations(lay, 300)
+    wg = (synth.gate_weight(lay) * 15).astype(np.float32)
+    gi, gw = check_route(x, wg, router_spec(lay), synth.score_bias(lay))
+    kept = (gi >= 0).sum(axis=1)
+    say(f"[route] top_p {top_p} {mode}: mean kept slots {kept.mean():.2f} of {lay.top_k}")
 
 
 def test_route_max_experts_and_k():
@@ -200,16 +229,17 @@ def test_dispatch_empty_and_out_of_range():
 # ---------------------------------------------------------------------------
 # whole layer, small shapes (every output element)
 # ---------------------------------------------------------------------------
-def run_layer(dl, x_np, act_mode, copy=0, timed=False):
+def run_layer(dl, x_np, act_mode, copy=0, timed=False, top_p=None):
     T = x_np.shape[0]
     lay = dl.shape
+    params = dl.params if top_p is None else qe.with_top_p(dl.params, top_p)
     x = torch.from_numpy(np.ascontiguousarray(x_np)).cuda()
     out = torch.empty((T, lay.d_model), dtype=torch.float32, device="cuda")
     ws = qe.workspace(T, lay.top_k, lay.n_experts, lay.d_model, lay.d_ff, qe.ACT_MODES[act_mode],
                       dl.shared[copy] is not None)
     if timed:
         evs = [torch.cuda.Event(enable_timing=True) for _ in range(2 * qe.MOE_STAGE_COUNT)]
-        qe.moe_layer_forward_timed(x, dl.gate_w, dl.params, dl.routed[copy], dl.shared[copy],
+        qe.moe_layer_forward_timed(x, dl.gate_w, params, dl.routed[copy], dl.shared[copy],
                                    qe.ACT_MODES[act_mode], out, ws, evs)
         torch.cuda.synchronize()
         for s in range(qe.MOE_STAGE_COUNT):      # every stage that runs as its own launch was timed
@@ -218,17 +248,28 @@ def run_layer(dl, x_np, act_mode, copy=0, timed=False):
             ms = evs[2 * s].elapsed_time(evs[2 * s + 1])
             assert 0.0 < ms < 1000.0, (qe.STAGES[s], ms)
     else:
-        qe.moe_layer_forward(x, dl.gate_w, dl.params, dl.routed[copy], dl.shared[copy], qe.ACT_MODES[act_mode],
+        qe.moe_layer_forward(x, dl.gate_w, params, dl.routed[copy], dl.shared[copy], qe.ACT_MODES[act_mode],
                              out, ws)
     torch.cuda.synchronize()
     return t2n(out)
 
 
-def oracle_layer(shape, x, act_mode, name=None):
+def oracle_layer(shape, x, act_mode, name=None, top_p=None):
     key = name or shape
     shared = oracle_expert(key, shape.n_experts) if shape.shared_expert else None
     wg = synth.gate_weight(shape)
-    return olayer.layer_forward(x, wg, router_spec(shape), lambda e: oracle_expert(key, e), shared, act_mode)
+    return olayer.layer_forward(x, wg, router_spec(shape, top_p), lambda e: oracle_expert(key, e), shared,
+                                act_mode)
+
+
+def top_p_settled(shape, x, top_p=None):
+    """Tokens whose top-p keep decisions are far from the threshold (fp32 and
+    fp64 decide them alike); all tokens when top-p is off."""
+    spec = router_spec(shape, top_p)
+    if not 0.0 < spec.top_p < 1.0:
+        return np.ones(x.shape[0], dtype=bool)
+    _, w0, _ = olayer.route(x, synth.gate_weight(shape), dataclasses.replace(spec, top_p=0.0))
+    return orouter.top_p_margin(w0, spec.top_p) >= TOPP_EPS
 
 
 TINY_VARIANTS = {
@@ -239,6 +280,9 @@ TINY_VARIANTS = {
     "tiny_e1k1": dict(n_experts=1, top_k=1, renormalize=True),
     "tiny_kE": dict(top_k=8, renormalize=False),
     "tiny_wide": dict(d_model=192, d_ff=320, n_experts=6, top_k=3),
+    "tiny_topp": dict(n_experts=16, top_k=6, renormalize=False, top_p=0.6),
+    "tiny_noaux_topp": dict(router="noaux_tc", n_experts=16, n_group=4, topk_group=2, top_k=4, has_bias=True,
+                            routed_scaling_factor=2.5, shared_expert=True, top_p=0.7),
 }
 
 
@@ -263,7 +307,9 @@ def test_layer_tiny(variant, act_mode):
         x = synth.activations(shape, T)
         got = run_layer(dl, x, act_mode)
         ref = oracle_layer(shape, x, act_mode)
-        assert_close_rel(got, ref["out"], what=f"{variant}/{act_mode}/T={T} out")
+        ok = top_p_settled(shape, x)
+        assert ok.sum() >= 0.98 * T
+        assert_close_rel(got[ok], ref["out"][ok], what=f"{variant}/{act_mode}/T={T} out")
 
 
 def test_layer_zero_tokens_is_noop():
@@ -371,7 +417,7 @@ SAMPLE = 48
 
 
 @pytest.mark.parametrize("wname", ["olmoe_b1", "olmoe_b16", "glm_b1", "glm_verify4", "olmoe_int4_prefill",
-                                   "qwen_prefill"])
+                                   "qwen_prefill", "glm_b1_topp", "olmoe_b16_topp"])
 def test_layer_full_size(wname):
     need_gpu()
     wl = synth.workload(wname)
@@ -379,15 +425,19 @@ def test_layer_full_size(wname):
     dl = device_layer(shape.name)
     x = synth.activations(shape, wl.tokens)
     say(f"[gpu] {wname}: running the layer on T={wl.tokens}")
-    got = run_layer(dl, x, wl.act_mode)
+    top_p = wl.top_p or None
+    got = run_layer(dl, x, wl.act_mode, top_p=top_p)
     rows = np.arange(wl.tokens)
     if wl.tokens > SAMPLE:
         rows = np.sort(np.random.default_rng(5).choice(wl.tokens, SAMPLE, replace=False))
+    rows = rows[top_p_settled(shape, x[rows], top_p)]
     say(f"[oracle] {wname}: {len(rows)} tokens")
-    ref = oracle_layer(shape, x[rows], wl.act_mode, name=shape.name)
+    ref = oracle_layer(shape, x[rows], wl.act_mode, name=shape.name, top_p=top_p)
+    if top_p:
+        say(f"[gpu] {wname}: top-p {top_p} keeps {(ref['idx'] >= 0).sum()} of {ref['idx'].size} slots")
     assert_close_rel(got[rows], ref["out"], what=f"{wname} out")
     # the same weights, byte for byte, on both sides (a few experts)
-    used = np.unique(ref["idx"])[:3]
+    used = np.unique(ref["idx"][ref["idx"] >= 0])[:3]
     for e in used:
         ox = oracle_expert(shape.name, int(e))
         assert np.array_equal(untile_codes(t2n(dl.routed[0].gate_q[e]), shape.d_ff, shape.d_model, shape.wformat),
