@@ -35,6 +35,18 @@ class RouterSpec:
     top_p: float = 0.0           # adaptive expert top-p; 0 (or >= 1) keeps all k
 
 
+def rmsnorm(x, gamma, eps: float):
+    """RMSNorm of each row, in fp64: x / sqrt(mean(x^2) + eps) * gamma.
+
+    The hidden states the layer takes are "after RMSNorm"; the normalisation
+    itself is the transformer block's (the mtlm-7m-base page lists RMSNorm
+    among the model's layers, section "What is and is not machin").
+    """
+    x = np.asarray(x, np.float64)
+    inv = 1.0 / np.sqrt((x * x).mean(axis=1, keepdims=True) + eps)
+    return x * inv * np.asarray(gamma, np.float64)[None, :]
+
+
 def route(x, wg, spec: RouterSpec):
     if spec.mode == "softmax":
         idx, w, l = router.route_softmax(x, wg, spec.top_k, spec.renormalize)
@@ -85,3 +97,19 @@ def layer_forward(x, wg, spec: RouterSpec, get_expert: Callable[[int], ffn.Quant
     out = combine(y_perm, w, inv, shared_y)
     return dict(idx=idx, w=w, logits=l, counts=counts, offsets=offsets, perm=perm,
                 inv_perm=inv, y_perm=y_perm, shared_y=shared_y, out=out)
+
+
+def block_forward(x, gamma, eps: float, wg, spec: RouterSpec, get_expert: Callable[[int], ffn.QuantExpert],
+                  shared: Optional[ffn.QuantExpert], act_mode: str):
+    """The layer between its neighbours: out = x + layer(RMSNorm(x)).
+
+    The normalised states enter the layer in fp32 (the layer's input type);
+    gamma = None skips the normalisation. Returns layer_forward's dict with
+    out replaced by the residual sum and x_norm added.
+    """
+    x = np.asarray(x, np.float32)
+    xn = x if gamma is None else rmsnorm(x, gamma, eps).astype(np.float32)
+    res = layer_forward(xn, wg, spec, get_expert, shared, act_mode)
+    res["x_norm"] = xn
+    res["out"] = np.asarray(x, np.float64) + res["out"]
+    return res

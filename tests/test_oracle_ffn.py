@@ -168,3 +168,49 @@ def test_layer_noaux_tc_weights_sum_to_scaling_factor():
     exps = _tiny_experts(lay)
     r = layer.layer_forward(x, wg, _spec(lay), lambda e: exps[e], None, "f32")
     assert np.allclose(r["w"].sum(1), 2.5, rtol=1e-12)
+
+
+# ---------------------------------------------------------------------------
+# the neighbours of the layer: RMSNorm before it, the residual after it
+# ---------------------------------------------------------------------------
+def test_rmsnorm_closed_forms():
+    d = 64
+    gamma = np.linspace(0.5, 1.5, d)
+    # a constant row c: mean(x^2) = c^2, so x_norm = sign(c) * gamma / sqrt(1 + eps / c^2)
+    for c, eps in ((3.0, 0.0), (-0.25, 1e-6), (2.0, 1e-2)):
+        got = layer.rmsnorm(np.full((1, d), c), gamma, eps)[0]
+        assert np.allclose(got, np.sign(c) * gamma / math.sqrt(1.0 + eps / c ** 2), rtol=1e-14, atol=0)
+    # a row of one +a and (d-1) zeros: mean(x^2) = a^2/d, x_norm[0] = sqrt(d) * gamma[0]
+    x = np.zeros((1, d))
+    x[0, 0] = 7.0
+    got = layer.rmsnorm(x, gamma, 0.0)[0]
+    assert math.isclose(got[0], math.sqrt(d) * gamma[0], rel_tol=1e-14) and np.all(got[1:] == 0)
+    # with eps = 0: invariant to a positive scale of the row, unit root-mean-square before gamma
+    rng = np.random.default_rng(2)
+    x = rng.standard_normal((5, d))
+    a = layer.rmsnorm(x, np.ones(d), 0.0)
+    assert np.allclose(layer.rmsnorm(37.5 * x, np.ones(d), 0.0), a, rtol=1e-13, atol=0)
+    assert np.allclose(np.sqrt((a * a).mean(axis=1)), 1.0, rtol=1e-13)
+
+
+def test_block_residual_only_when_the_norm_gain_is_zero():
+    # gamma = 0: the layer sees zero states, every logit is 0 (experts 0..k-1
+    # by the tie rule), every expert output is 0, so out is the residual x
+    lay = synth.variant(synth.LAYERS["tiny"], shared_expert=True)
+    x = synth.activations(lay, 9)
+    exps = _tiny_experts(lay)
+    for act in ("f32", "q8_0"):
+        r = layer.block_forward(x, np.zeros(lay.d_model), 1e-6, synth.gate_weight(lay), _spec(lay),
+                                lambda e: exps[e], exps[lay.n_experts], act)
+        assert np.array_equal(r["out"], x.astype(np.float64))
+        assert np.all(r["idx"] == np.arange(lay.top_k))
+
+
+def test_block_without_norm_is_residual_plus_layer():
+    lay = synth.variant(synth.LAYERS["tiny"], shared_expert=True)
+    x = synth.activations(lay, 9)
+    exps = _tiny_experts(lay)
+    wg = synth.gate_weight(lay)
+    r = layer.block_forward(x, None, 0.0, wg, _spec(lay), lambda e: exps[e], exps[lay.n_experts], "f32")
+    base = layer.layer_forward(x, wg, _spec(lay), lambda e: exps[e], exps[lay.n_experts], "f32")
+    assert np.array_equal(r["out"], x.astype(np.float64) + base["out"])
