@@ -287,6 +287,30 @@ moe_status moe_layer_forward_timed(const float* x, int32_t T, const float* gate_
                                    void* ws, size_t ws_bytes, const hipEvent_t* stage_events,
                                    hipStream_t stream);
 
+/* The layer between its neighbours in a transformer block:
+ *   out = x + moe_layer_forward(RMSNorm(x))
+ * with RMSNorm(x)[t] = x[t] / sqrt(mean_c(x[t][c]^2) + eps) * norm_w, the
+ * normalisation the layer's input has been through ("mtlm-7m-base",
+ * section "What is and is not machin": RMSNorm, SwiGLU) and the residual
+ * connection around it.
+ *   x        device fp32 [T, d], the block's hidden states before the norm.
+ *   norm_w   device fp32 [d], the norm's gain; NULL skips the normalisation
+ *            (out = x + layer(x)).
+ *   eps      finite, >= 0.
+ *   out      device fp32 [T, d]; may be the same buffer as x (each element
+ *            of x is read before the same element of out is written).
+ *   stage_events  as moe_layer_forward_timed, or NULL. The normalisation is
+ *            part of the route stage.
+ * Up to 16 tokens the normalisation happens inside the router's logits
+ * kernel (no extra pass over x); above that, once into the workspace.
+ * Everything else as moe_layer_forward (same workspace size).
+ */
+moe_status moe_block_forward(const float* x, int32_t T, const float* norm_w, float eps,
+                             const float* gate_w, const moe_router_params* p,
+                             const moe_experts* routed, const moe_experts* shared,
+                             int32_t act_mode, float* out, void* ws, size_t ws_bytes,
+                             const hipEvent_t* stage_events, hipStream_t stream);
+
 /* Test hook for the Q8_0 path: runs the production matrix-core kernels
  * of moe_expert_ffn(act_mode = MOE_ACT_Q8_0) and also writes their exact
  * int32 per-group dots and the Q8_0 codes of H. With R = T*k rows in

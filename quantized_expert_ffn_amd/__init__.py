@@ -12,5 +12,6 @@ from ._lib import (  # noqa: F401
     load, exported_names, router_params, with_top_p, quantize_experts, workspace,
     moe_workspace_size, moe_quantize_weights, moe_quantize_q8_0, moe_route, moe_dispatch,
     moe_expert_ffn, moe_debug_q8_expert_ffn, moe_combine, moe_layer_forward, moe_layer_forward_timed,
+    moe_block_forward,
     moe_status_string, moe_last_error_detail,
 )

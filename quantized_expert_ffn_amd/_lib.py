@@ -75,6 +75,8 @@ _SIGNATURES = {
                                  ctypes.POINTER(Experts), _I32, _P, _P, _SZ, _P]),
     "moe_layer_forward_timed": (_I32, [_P, _I32, _P, ctypes.POINTER(RouterParams), ctypes.POINTER(Experts),
                                        ctypes.POINTER(Experts), _I32, _P, _P, _SZ, _P, _P]),
+    "moe_block_forward": (_I32, [_P, _I32, _P, ctypes.c_float, _P, ctypes.POINTER(RouterParams),
+                                 ctypes.POINTER(Experts), ctypes.POINTER(Experts), _I32, _P, _P, _SZ, _P, _P]),
     "moe_debug_q8_expert_ffn": (_I32, [_P, _I32, _I32, ctypes.POINTER(Experts), _P, _P, _P, _P, _P, _P, _P, _P,
                                        _P, _P, _SZ, _P]),
     "moe_status_string": (ctypes.c_char_p, [_I32]),
@@ -313,6 +315,34 @@ def moe_layer_forward_timed(x, gate_w, params: RouterParams, routed: QuantExpert
         _ptr(x, torch.float32, "x"), x.shape[0], _ptr(gate_w, torch.float32, "gate_w"), ctypes.byref(params),
         ctypes.byref(r), ctypes.byref(s) if s is not None else None, act_mode, _ptr(out, torch.float32, "out"),
         _ptr(ws, None, "ws"), ws.numel() * ws.element_size(), arr, _stream(stream)), "moe_layer_forward_timed")
+
+
+def _event_array(events):
+    if len(events) != 2 * MOE_STAGE_COUNT:
+        raise ValueError(f"need {2 * MOE_STAGE_COUNT} events")
+    handles = []
+    for ev in events:
+        if ev is None:
+            handles.append(None)
+            continue
+        if not ev.cuda_event:
+            ev.record()        # torch creates the HIP event on its first record
+        handles.append(ev.cuda_event)
+    return (ctypes.c_void_p * len(events))(*handles)
+
+
+def moe_block_forward(x, norm_w: Optional[torch.Tensor], eps: float, gate_w, params: RouterParams,
+                      routed: QuantExperts, shared: Optional[QuantExperts], act_mode: int, out, ws,
+                      events: Optional[Sequence[Optional[torch.cuda.Event]]] = None, stream=None) -> None:
+    """out = x + layer(RMSNorm(x)) (norm_w None: out = x + layer(x)); out may be x."""
+    arr = _event_array(events) if events is not None else None
+    r = routed.abi()
+    s = shared.abi() if shared is not None else None
+    _check(load().moe_block_forward(
+        _ptr(x, torch.float32, "x"), x.shape[0], _ptr(norm_w, torch.float32, "norm_w"), eps,
+        _ptr(gate_w, torch.float32, "gate_w"), ctypes.byref(params), ctypes.byref(r),
+        ctypes.byref(s) if s is not None else None, act_mode, _ptr(out, torch.float32, "out"),
+        _ptr(ws, None, "ws"), ws.numel() * ws.element_size(), arr, _stream(stream)), "moe_block_forward")
 
 
 def quantize_experts(gate: torch.Tensor, up: torch.Tensor, down: torch.Tensor, fmt: str, stream=None) -> QuantExperts:

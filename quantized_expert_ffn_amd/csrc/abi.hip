@@ -235,9 +235,12 @@ moe_status expert_ffn_impl(const float* x, int32_t T, int32_t k, const moe_exper
     return ok();
 }
 
+// The layer; with `block`, between its neighbours: out = x + layer(RMSNorm(x))
+// (norm_w null: no normalisation, the residual is still added).
 moe_status layer_forward_impl(const float* x, int32_t T, const float* gate_w, const moe_router_params* p,
                               const moe_experts* routed, const moe_experts* shared, int32_t act_mode, float* out,
-                              void* ws, size_t ws_bytes, const hipEvent_t* ev, hipStream_t st) {
+                              void* ws, size_t ws_bytes, const hipEvent_t* ev, hipStream_t st, bool block = false,
+                              const float* norm_w = nullptr, float eps = 0.0f) {
     moe_status s;
     if ((s = check_act_mode(act_mode)) != MOE_OK) return s;
     if ((s = check_experts(routed, "routed", act_mode)) != MOE_OK) return s;
@@ -256,6 +259,9 @@ moe_status layer_forward_impl(const float* x, int32_t T, const float* gate_w, co
     MOE_REQUIRE(x && gate_w && out, MOE_ERR_INVALID_ARG, "NULL tensor argument");
     MOE_REQUIRE(aligned16(x) && aligned16(gate_w) && aligned16(out), MOE_ERR_INVALID_ARG,
                 "x, gate_w and out must be 16-byte aligned");
+    MOE_REQUIRE(norm_w == nullptr || aligned16(norm_w), MOE_ERR_INVALID_ARG, "norm_w must be 16-byte aligned");
+    MOE_REQUIRE(std::isfinite(eps) && eps >= 0.0f, MOE_ERR_INVALID_ARG, "eps = %g must be finite and >= 0",
+                (double)eps);
     const int E = routed->n_experts, k = p->top_k, d = routed->d_model;
     const int has_shared = shared != nullptr;
     const moe::WsLayout L = moe::ws_layout(T, k, E, d, routed->d_ff, act_mode, has_shared);
@@ -272,13 +278,23 @@ moe_status layer_forward_impl(const float* x, int32_t T, const float* gate_w, co
     // dispatch are one block; larger T: each step is a kernel of its own
     const bool small = moe::router_splits(T, E, d) == 0;
     const bool fused = T <= moe::kFusedRouteT;
+    const bool norm = block && norm_w != nullptr;
+    // the layer's input: x, or RMSNorm(x) (inside the router kernel for small
+    // T; larger T normalises once into the workspace)
+    const float* xl = x;
     record(ev, 2 * MOE_STAGE_ROUTE, st);
-    MOE_HIP(moe::launch_router_logits(x, T, d, gate_w, E, logits, xp, st), "router logits");
+    if (norm && !small) {
+        float* xn = ws_at<float>(ws, L.xn);
+        MOE_HIP(moe::launch_rmsnorm(x, T, d, norm_w, eps, xn, st), "RMSNorm");
+        xl = xn;
+    }
+    MOE_HIP(moe::launch_router_logits(xl, T, d, gate_w, E, logits, xp, (norm && small) ? norm_w : nullptr, eps, st),
+            "router logits");
     if (!fused) MOE_HIP(moe::launch_router_topk(logits, T, d, *p, idx, w, st), "router top-k");
     record(ev, 2 * MOE_STAGE_ROUTE + 1, st);
     if (!small) {
         record(ev, 2 * MOE_STAGE_QUANT_X, st);
-        MOE_HIP(moe::launch_xprep(x, T, d, xp, st), "hidden states");
+        MOE_HIP(moe::launch_xprep(xl, T, d, xp, st), "hidden states");
         record(ev, 2 * MOE_STAGE_QUANT_X + 1, st);
     }
     record(ev, 2 * MOE_STAGE_DISPATCH, st);
@@ -299,7 +315,8 @@ moe_status layer_forward_impl(const float* x, int32_t T, const float* gate_w, co
                          st)) != MOE_OK)
         return s;
     record(ev, 2 * MOE_STAGE_COMBINE, st);
-    MOE_HIP(moe::launch_combine(y, w, inv_perm, has_shared ? y + (size_t)T * k * d : nullptr, T, k, d, out, st),
+    MOE_HIP(moe::launch_combine(y, w, inv_perm, has_shared ? y + (size_t)T * k * d : nullptr, block ? x : nullptr, T, k,
+                                d, out, st),
             "combine");
     record(ev, 2 * MOE_STAGE_COMBINE + 1, st);
     return ok();
@@ -403,7 +420,7 @@ moe_status moe_combine(const float* y_perm, const float* topk_w, const int32_t* 
     MOE_REQUIRE(y_perm && topk_w && inv_perm && out, MOE_ERR_INVALID_ARG, "NULL tensor argument");
     MOE_REQUIRE(aligned16(y_perm) && aligned16(out) && (shared_y == nullptr || aligned16(shared_y)),
                 MOE_ERR_INVALID_ARG, "y_perm, shared_y and out must be 16-byte aligned");
-    MOE_HIP(moe::launch_combine(y_perm, topk_w, inv_perm, shared_y, T, k, d, out, stream), "combine");
+    MOE_HIP(moe::launch_combine(y_perm, topk_w, inv_perm, shared_y, nullptr, T, k, d, out, stream), "combine");
     return ok();
 }
 
@@ -417,6 +434,14 @@ moe_status moe_layer_forward_timed(const float* x, int32_t T, const float* gate_
                                    const moe_experts* routed, const moe_experts* shared, int32_t act_mode, float* out,
                                    void* ws, size_t ws_bytes, const hipEvent_t* stage_events, hipStream_t stream) {
     return layer_forward_impl(x, T, gate_w, p, routed, shared, act_mode, out, ws, ws_bytes, stage_events, stream);
+}
+
+moe_status moe_block_forward(const float* x, int32_t T, const float* norm_w, float eps, const float* gate_w,
+                             const moe_router_params* p, const moe_experts* routed, const moe_experts* shared,
+                             int32_t act_mode, float* out, void* ws, size_t ws_bytes,
+                             const hipEvent_t* stage_events, hipStream_t stream) {
+    return layer_forward_impl(x, T, gate_w, p, routed, shared, act_mode, out, ws, ws_bytes, stage_events, stream, true,
+                              norm_w, eps);
 }
 
 const char* moe_status_string(moe_status st) {

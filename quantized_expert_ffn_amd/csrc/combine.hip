@@ -1,5 +1,6 @@
 // Combine: out[t] = sum_j w[t, j] * Y[inv_perm[t*k + j]] + S[t], over the
-// dispatched slots (inv_perm >= 0; a slot dropped by top-p adds nothing).
+// dispatched slots (inv_perm >= 0; a slot dropped by top-p adds nothing),
+// plus the block's residual when the layer runs between its neighbours.
 //
 // The weighted sum of a token's k expert outputs plus the shared expert
 // ("Show HN: Getting GLM-5.2 running on my slow computer", section "What's implemented": shared expert). Each
@@ -14,7 +15,8 @@ namespace moe {
 // column per lane. The token's weights and row indices are uniform loads.
 __global__ __launch_bounds__(64) void combine_kernel(const float* __restrict__ y, const float* __restrict__ w,
                                                      const int* __restrict__ inv_perm,
-                                                     const float* __restrict__ shared_y, int T, int k, int d,
+                                                     const float* __restrict__ shared_y,
+                                                     const float* __restrict__ residual, int T, int k, int d,
                                                      float* __restrict__ out) {
     const int t = blockIdx.y;
     const int c = blockIdx.x * 64 + threadIdx.x;
@@ -37,14 +39,22 @@ __global__ __launch_bounds__(64) void combine_kernel(const float* __restrict__ y
         acc.z += s.z;
         acc.w += s.w;
     }
+    if (residual) {
+        // read before the store of the same element: out may alias residual
+        const float4 r = reinterpret_cast<const float4*>(residual + (size_t)t * d)[c];
+        acc.x += r.x;
+        acc.y += r.y;
+        acc.z += r.z;
+        acc.w += r.w;
+    }
     reinterpret_cast<float4*>(out + (size_t)t * d)[c] = acc;
 }
 
-hipError_t launch_combine(const float* y, const float* w, const int* inv_perm, const float* shared_y, int T, int k,
-                          int d, float* out, hipStream_t st) {
+hipError_t launch_combine(const float* y, const float* w, const int* inv_perm, const float* shared_y,
+                          const float* residual, int T, int k, int d, float* out, hipStream_t st) {
     if (T == 0) return hipSuccess;
     const dim3 grid((d / 4 + 63) / 64, T);
-    hipLaunchKernelGGL(combine_kernel, grid, dim3(64), 0, st, y, w, inv_perm, shared_y, T, k, d, out);
+    hipLaunchKernelGGL(combine_kernel, grid, dim3(64), 0, st, y, w, inv_perm, shared_y, residual, T, k, d, out);
     return hipGetLastError();
 }
 

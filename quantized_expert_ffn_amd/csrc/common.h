@@ -37,6 +37,7 @@ struct WsLayout {
     size_t hd = 0;         // Q8_0: f32 [R, I/32]  F32: f16 lo parts [R, I]
     size_t hp = 0;         //                      F32: f32 powers of two [R, I/32]
     size_t y = 0;          // f32  [R, d]
+    size_t xn = 0;         // f32  [T, d]  RMSNorm(x) for the block entry point, T > 16 only
     size_t total = 0;
     int max_tiles = 0;
 };
@@ -91,6 +92,7 @@ inline WsLayout ws_layout(int T, int k, int E, int d, int I, int act_mode, int h
         L.hp = take(R * (I / kGroup) * 4);
     }
     L.y = take(R * d * 4);
+    if (S > 0) L.xn = take((size_t)T * d * 4);
     L.total = off;
     return L;
 }

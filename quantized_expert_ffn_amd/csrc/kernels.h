@@ -21,14 +21,21 @@ struct XPrep {
     float* pow = nullptr;
     _Float16* q = nullptr;         // XPREP_Q8_0: [T, d] codes as f16 in slot order, [T, d/32] scales
     float* qd = nullptr;
+    // RMSNorm applied on the way in (the small-T router kernel only): the
+    // prepared value of x[t][c] is x[t][c] * gamma[c] * inv_rms[t]
+    const float* gamma = nullptr;  // [d] or null (no normalisation)
+    const float* inv_rms = nullptr;
 };
 
 hipError_t launch_router(const float* x, int T, int d, const float* wg, const moe_router_params& p, float* logits,
                          int* idx, float* w, hipStream_t st);
 // With router_splits(T, E, d) == 0 (small T) the logits kernel also does xp;
-// otherwise xp is ignored and the caller runs launch_xprep.
+// otherwise xp is ignored and the caller runs launch_xprep. norm_w (small T
+// only, else null): the logits and xp see RMSNorm(x) with gain norm_w and eps.
 hipError_t launch_router_logits(const float* x, int T, int d, const float* wg, int E, float* logits,
-                                const XPrep& xp, hipStream_t st);
+                                const XPrep& xp, const float* norm_w, float eps, hipStream_t st);
+// RMSNorm of T rows into xn [T, d] (the larger-T path)
+hipError_t launch_rmsnorm(const float* x, int T, int d, const float* norm_w, float eps, float* xn, hipStream_t st);
 hipError_t launch_router_topk(const float* logits, int T, int d, const moe_router_params& p, int* idx, float* w,
                               hipStream_t st);
 hipError_t launch_xprep(const float* x, int T, int d, const XPrep& xp, hipStream_t st);
@@ -73,7 +80,8 @@ hipError_t launch_q8_mfma(const moe_experts& routed, const moe_experts* shared, 
                           int8_t* dbg_hq,
                           hipStream_t st, hipEvent_t ev_start = nullptr, hipEvent_t ev_stop = nullptr);
 
-hipError_t launch_combine(const float* y, const float* w, const int* inv_perm, const float* shared_y, int T, int k,
-                          int d, float* out, hipStream_t st);
+// residual: [T, d] added last, or null
+hipError_t launch_combine(const float* y, const float* w, const int* inv_perm, const float* shared_y,
+                          const float* residual, int T, int k, int d, float* out, hipStream_t st);
 
 }  // namespace moe

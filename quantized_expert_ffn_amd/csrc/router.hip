@@ -22,6 +22,21 @@ typedef _Float16 v8h __attribute__((ext_vector_type(8)));
 // ---------------------------------------------------------------------------
 // Hidden-state preparation
 // ---------------------------------------------------------------------------
+// 8 consecutive values x[r][c .. c+7], normalised when xp carries an RMSNorm
+__device__ __forceinline__ void load8(const float* __restrict__ x, int r, int d, int c, const XPrep& xp, float4& a,
+                                      float4& b) {
+    const float4* src = reinterpret_cast<const float4*>(x + (size_t)r * d + c);
+    a = src[0];
+    b = src[1];
+    if (xp.gamma) {
+        const float s = xp.inv_rms[r];
+        const float4 ga = *reinterpret_cast<const float4*>(xp.gamma + c);
+        const float4 gb = *reinterpret_cast<const float4*>(xp.gamma + c + 4);
+        a = make_float4(a.x * ga.x * s, a.y * ga.y * s, a.z * ga.z * s, a.w * ga.w * s);
+        b = make_float4(b.x * gb.x * s, b.y * gb.y * s, b.z * gb.z * s, b.w * gb.w * s);
+    }
+}
+
 // f32 path, group g of every row, one wave: p = 2^(e-15) with max|x| < 2^e
 // over the T rows' 32 values, x/p split into f16 hi + lo in operand-slot order.
 template <int FMT>
@@ -31,8 +46,8 @@ __device__ __forceinline__ void split_group(const float* __restrict__ x, int T, 
     float amax = 0.0f;
     for (int r0 = 0; r0 < T; r0 += 16) {
         const int r = min(r0 + rsub, T - 1);
-        const float4* src = reinterpret_cast<const float4*>(x + (size_t)r * d + g * kGroup + 8 * q);
-        const float4 a = src[0], b = src[1];
+        float4 a, b;
+        load8(x, r, d, g * kGroup + 8 * q, xp, a, b);
         amax = fmaxf(amax, fmaxf(fmaxf(fabsf(a.x), fabsf(a.y)), fmaxf(fabsf(a.z), fabsf(a.w))));
         amax = fmaxf(amax, fmaxf(fmaxf(fabsf(b.x), fabsf(b.y)), fmaxf(fabsf(b.z), fabsf(b.w))));
     }
@@ -42,8 +57,8 @@ __device__ __forceinline__ void split_group(const float* __restrict__ x, int T, 
     for (int r0 = 0; r0 < T; r0 += 16) {
         const int r = r0 + rsub;
         if (r >= T) break;
-        const float4* src = reinterpret_cast<const float4*>(x + (size_t)r * d + g * kGroup + 8 * q);
-        const float4 a = src[0], b = src[1];
+        float4 a, b;
+        load8(x, r, d, g * kGroup + 8 * q, xp, a, b);
         const float v[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
         v8h hi, lo;
 #pragma unroll
@@ -69,8 +84,8 @@ __device__ __forceinline__ void q8_item(const float* __restrict__ x, int d, int 
     const int sub = threadIdx.x & 3;
     const int t = item / G, g = item - t * G;
     const size_t off = (size_t)t * d + g * kGroup + 8 * sub;
-    const float4 a = *reinterpret_cast<const float4*>(x + off);
-    const float4 b = *reinterpret_cast<const float4*>(x + off + 4);
+    float4 a, b;
+    load8(x, t, d, g * kGroup + 8 * sub, xp, a, b);
     const float v[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
     float amax = 0.0f;
 #pragma unroll
@@ -121,17 +136,26 @@ __global__ __launch_bounds__(256) void xprep_kernel(const float* __restrict__ x,
 template <int TB>
 __global__ __launch_bounds__(256) void router_logits_gemv_kernel(const float* __restrict__ x,
                                                                  const float* __restrict__ wg, int T, int d,
-                                                                 int E, float* __restrict__ L, const XPrep xp) {
+                                                                 int E, float* __restrict__ L, XPrep xp,
+                                                                 const float* __restrict__ gamma, float eps) {
     __shared__ float part[4][TB];
+    __shared__ float sq[4][TB];
+    __shared__ float inv_rms[TB];
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int e = blockIdx.x;
-    float acc[TB];
+    float acc[TB], ss[TB];
 #pragma unroll
-    for (int t = 0; t < TB; ++t) acc[t] = 0.0f;
+    for (int t = 0; t < TB; ++t) acc[t] = ss[t] = 0.0f;
     const float4* wr = reinterpret_cast<const float4*>(wg + (size_t)e * d);
     const int n4 = d >> 2;
     for (int i = threadIdx.x; i < n4; i += 256) {
-        const float4 w4 = wr[i];
+        float4 w4 = wr[i];
+        if (gamma) {
+            // RMSNorm(x) . w = inv_rms * sum x (gamma w); the sums of squares
+            // come from the same loads
+            const float4 g4 = reinterpret_cast<const float4*>(gamma)[i];
+            w4 = make_float4(w4.x * g4.x, w4.y * g4.y, w4.z * g4.z, w4.w * g4.w);
+        }
         // rows past T repeat the last row (unused sums): loads without
         // conditions all go out together instead of one at a time
 #pragma unroll
@@ -141,19 +165,67 @@ __global__ __launch_bounds__(256) void router_logits_gemv_kernel(const float* __
             acc[t] = fmaf(x4.y, w4.y, acc[t]);
             acc[t] = fmaf(x4.z, w4.z, acc[t]);
             acc[t] = fmaf(x4.w, w4.w, acc[t]);
+            if (gamma) {
+                ss[t] = fmaf(x4.x, x4.x, ss[t]);
+                ss[t] = fmaf(x4.y, x4.y, ss[t]);
+                ss[t] = fmaf(x4.z, x4.z, ss[t]);
+                ss[t] = fmaf(x4.w, x4.w, ss[t]);
+            }
         }
     }
 #pragma unroll
     for (int t = 0; t < TB; ++t) {
         const float s = wave_sum_all(acc[t]);
         if (lane == 0) part[wave][t] = s;
+        if (gamma) {
+            const float q = wave_sum_all(ss[t]);
+            if (lane == 0) sq[wave][t] = q;
+        }
+    }
+    __syncthreads();
+    if (gamma && threadIdx.x < TB) {
+        const int t = threadIdx.x;
+        const float tot = (sq[0][t] + sq[1][t]) + (sq[2][t] + sq[3][t]);
+        inv_rms[t] = 1.0f / sqrtf(tot / (float)d + eps);
     }
     __syncthreads();
     if (threadIdx.x < T) {
         const int t = threadIdx.x;
-        L[(size_t)t * E + e] = (part[0][t] + part[1][t]) + (part[2][t] + part[3][t]);
+        const float l = (part[0][t] + part[1][t]) + (part[2][t] + part[3][t]);
+        L[(size_t)t * E + e] = gamma ? l * inv_rms[t] : l;
+    }
+    if (gamma) {
+        xp.gamma = gamma;
+        xp.inv_rms = inv_rms;
     }
     xprep_waves(x, T, d, xp, blockIdx.x * 4 + wave, gridDim.x * 4);
+}
+
+// RMSNorm of one row per block (the larger-T path writes the normalised rows
+// once; every later stage reads them)
+__global__ __launch_bounds__(256) void rmsnorm_kernel(const float* __restrict__ x, int d,
+                                                      const float* __restrict__ gamma, float eps,
+                                                      float* __restrict__ xn) {
+    __shared__ float part[4];
+    const int t = blockIdx.x, wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const float4* xr = reinterpret_cast<const float4*>(x + (size_t)t * d);
+    float ss = 0.0f;
+    for (int i = threadIdx.x; i < (d >> 2); i += 256) {
+        const float4 v = xr[i];
+        ss = fmaf(v.x, v.x, ss);
+        ss = fmaf(v.y, v.y, ss);
+        ss = fmaf(v.z, v.z, ss);
+        ss = fmaf(v.w, v.w, ss);
+    }
+    ss = wave_sum_all(ss);
+    if (lane == 0) part[wave] = ss;
+    __syncthreads();
+    const float inv = 1.0f / sqrtf(((part[0] + part[1]) + (part[2] + part[3])) / (float)d + eps);
+    float4* dst = reinterpret_cast<float4*>(xn + (size_t)t * d);
+    for (int i = threadIdx.x; i < (d >> 2); i += 256) {
+        const float4 v = xr[i], g = reinterpret_cast<const float4*>(gamma)[i];
+        dst[i] = make_float4(v.x * g.x * inv, v.y * g.y * inv, v.z * g.z * inv, v.w * g.w * inv);
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -233,12 +305,14 @@ TopkArgs topk_args(const float* logits, int T, int d, const moe_router_params& p
 }
 
 hipError_t launch_router_logits(const float* x, int T, int d, const float* wg, int E, float* logits,
-                                const XPrep& xp, hipStream_t st) {
+                                const XPrep& xp, const float* norm_w, float eps, hipStream_t st) {
     if (T == 0) return hipSuccess;
     const int S = router_splits(T, E, d);
     if (S == 0) {
         const dim3 grid(E);
-#define MOE_RL(TB) hipLaunchKernelGGL(router_logits_gemv_kernel<TB>, grid, dim3(256), 0, st, x, wg, T, d, E, logits, xp)
+#define MOE_RL(TB)                                                                                            \
+    hipLaunchKernelGGL(router_logits_gemv_kernel<TB>, grid, dim3(256), 0, st, x, wg, T, d, E, logits, xp, norm_w, \
+                       eps)
         if (T == 1) MOE_RL(1);
         else if (T <= 2) MOE_RL(2);
         else if (T <= 4) MOE_RL(4);
@@ -251,6 +325,12 @@ hipError_t launch_router_logits(const float* x, int T, int d, const float* wg, i
     const int kslice = router_kslice(d, S);
     const dim3 grid((E + 63) / 64, (T + 63) / 64, S);
     hipLaunchKernelGGL(router_logits_mfma_kernel, grid, dim3(256), 0, st, x, wg, T, d, E, kslice, logits);
+    return hipGetLastError();
+}
+
+hipError_t launch_rmsnorm(const float* x, int T, int d, const float* norm_w, float eps, float* xn, hipStream_t st) {
+    if (T == 0) return hipSuccess;
+    hipLaunchKernelGGL(rmsnorm_kernel, dim3(T), dim3(256), 0, st, x, d, norm_w, eps, xn);
     return hipGetLastError();
 }
 
@@ -281,7 +361,7 @@ hipError_t launch_router_topk(const float* logits, int T, int d, const moe_route
 
 hipError_t launch_router(const float* x, int T, int d, const float* wg, const moe_router_params& p,
                          float* logits, int* idx, float* w, hipStream_t st) {
-    hipError_t err = launch_router_logits(x, T, d, wg, p.n_experts, logits, XPrep{}, st);
+    hipError_t err = launch_router_logits(x, T, d, wg, p.n_experts, logits, XPrep{}, nullptr, 0.0f, st);
     if (err != hipSuccess) return err;
     return launch_router_topk(logits, T, d, p, idx, w, st);
 }

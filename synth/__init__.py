@@ -33,6 +33,8 @@ TAG_X = 1
 TAG_GATE_W = 2
 TAG_BIAS = 3
 TAG_ZIPF_RANK = 4
+TAG_NORM_W = 5
+TAG_RESID = 6
 TAG_W_GATE = 10
 TAG_W_UP = 11
 TAG_W_DOWN = 12
@@ -129,6 +131,20 @@ def activations(layer: LayerShape, tokens: int) -> np.ndarray:
     if layer.zipf_s > 0:
         x[:, -1] = 1.0
     return x
+
+
+def block_states(layer: LayerShape, tokens: int) -> np.ndarray:
+    """Hidden states before the block's RMSNorm [T, d] fp32: N(0, 1) rows with
+    a per-row scale in [0.25, 4) (the norm removes it); row t does not depend
+    on T."""
+    x = _normal(layer.seed, TAG_RESID, 0, (tokens, layer.d_model), 1.0)
+    scale = np.exp2(_rng(layer.seed, TAG_RESID, 1).uniform(-2.0, 2.0, size=(65536,)))[:tokens]
+    return (x * scale[:, None].astype(np.float32)).astype(np.float32)
+
+
+def norm_weight(layer: LayerShape) -> np.ndarray:
+    """The RMSNorm gain [d] fp32 ~ 1 + N(0, 0.1)."""
+    return (1.0 + _normal(layer.seed, TAG_NORM_W, 0, (layer.d_model,), 0.1)).astype(np.float32)
 
 
 def gate_weight(layer: LayerShape) -> np.ndarray:

@@ -207,3 +207,18 @@ def test_router_top_p_validation(lib):
         assert _fwd(lib, params=p) == INVALID
     # a struct built field by field leaves top_p at 0: every slot kept
     assert _params().top_p == 0.0
+
+
+def test_block_forward_validation(lib):
+    p = _params()
+    e = _experts()
+    def blk(eps=1e-6, norm=FAKE, x=FAKE):
+        return lib.moe_block_forward(x, 4, norm, ctypes.c_float(eps), FAKE, ctypes.byref(p), ctypes.byref(e), None, 0,
+                                     FAKE, FAKE, 1 << 30, None, None)
+    assert blk(eps=-1.0) == INVALID
+    assert blk(eps=float("nan")) == INVALID
+    assert blk(eps=float("inf")) == INVALID
+    assert blk(x=None) == INVALID
+    assert blk(norm=FAKE + 4) == INVALID        # norm_w not 16-byte aligned
+    assert lib.moe_block_forward(FAKE, 0, None, ctypes.c_float(0.0), FAKE, ctypes.byref(p), ctypes.byref(e), None, 0,
+                                 FAKE, FAKE, 0, None, None) == OK      # T = 0

@@ -471,3 +471,60 @@ def test_layer_hip_graph_replay(act_mode):
         g.replay()
         torch.cuda.synchronize()
         assert torch.equal(out, eager), f"replay {r} differs"
+
+
+# ---------------------------------------------------------------------------
+# the layer between its neighbours: RMSNorm before, residual after
+# ---------------------------------------------------------------------------
+def run_block(dl, x_np, act_mode, norm_w, eps, in_place=False):
+    T = x_np.shape[0]
+    lay = dl.shape
+    x = torch.from_numpy(np.ascontiguousarray(x_np)).cuda()
+    out = x if in_place else torch.empty_like(x)
+    g = torch.from_numpy(norm_w).cuda() if norm_w is not None else None
+    ws = qe.workspace(T, lay.top_k, lay.n_experts, lay.d_model, lay.d_ff, qe.ACT_MODES[act_mode],
+                      dl.shared[0] is not None)
+    qe.moe_block_forward(x, g, eps, dl.gate_w, dl.params, dl.routed[0], dl.shared[0], qe.ACT_MODES[act_mode], out, ws)
+    torch.cuda.synchronize()
+    return t2n(out)
+
+
+def oracle_block(shape, x, act_mode, norm_w, eps, name=None):
+    key = name or shape
+    shared = oracle_expert(key, shape.n_experts) if shape.shared_expert else None
+    return olayer.block_forward(x, norm_w, eps, synth.gate_weight(shape), router_spec(shape),
+                                lambda e: oracle_expert(key, e), shared, act_mode)
+
+
+@pytest.mark.parametrize("act_mode", ["f32", "q8_0"])
+@pytest.mark.parametrize("variant", ["tiny", "tiny_shared_noaux", "tiny_int4", "tiny_topp"])
+def test_block_forward_tiny(variant, act_mode):
+    need_gpu()
+    shape, dl = tiny_layer(variant)
+    gamma = synth.norm_weight(shape)
+    for T, norm, in_place in ((16, True, False), (67, True, True), (16, False, True), (67, False, False), (1, True, False)):
+        x = synth.block_states(shape, T)
+        g = gamma if norm else None
+        got = run_block(dl, x, act_mode, g, 1e-6, in_place)
+        ref = oracle_block(shape, x, act_mode, g, 1e-6)
+        ok = top_p_settled(shape, ref["x_norm"])
+        assert_close_rel(got[ok], ref["out"][ok], what=f"{variant}/{act_mode}/T={T}/norm={norm} block out")
+        # the layer's own part, against the same tolerance (the residual is exact)
+        assert_close_rel(got[ok] - x[ok], ref["out"][ok] - x[ok].astype(np.float64),
+                         what=f"{variant}/{act_mode}/T={T} layer part")
+
+
+@pytest.mark.parametrize("wname", ["olmoe_b16", "glm_verify4", "olmoe_int4_prefill"])
+def test_block_forward_full_size(wname):
+    need_gpu()
+    wl = synth.workload(wname)
+    shape = wl.layer
+    dl = device_layer(shape.name)
+    x = synth.block_states(shape, wl.tokens)
+    gamma = synth.norm_weight(shape)
+    got = run_block(dl, x, wl.act_mode, gamma, 1e-5)
+    rows = np.arange(wl.tokens)
+    if wl.tokens > SAMPLE:
+        rows = np.sort(np.random.default_rng(6).choice(wl.tokens, SAMPLE, replace=False))
+    ref = oracle_block(shape, x[rows], wl.act_mode, gamma, 1e-5, name=shape.name)
+    assert_close_rel(got[rows] - x[rows], ref["out"] - x[rows].astype(np.float64), what=f"{wname} block layer part")
