@@ -94,13 +94,19 @@ def cpu_baseline(wl, target_s: float):
     shared = expert(shape.n_experts) if shape.shared_expert else None
     # sample: the whole batch for decode; a prefix of tokens for prefill
     n_tok = wl.tokens if wl.tokens <= 16 else 64
-    x = synth.activations(shape, wl.tokens)[:n_tok]
+    if wl.block:
+        x = synth.block_states(shape, wl.tokens)[:n_tok]
+        gamma = synth.norm_weight(shape)
+        run = lambda: olayer.block_forward(x, gamma, 1e-5, wg, spec, expert, shared, wl.act_mode)  # noqa: E731
+    else:
+        x = synth.activations(shape, wl.tokens)[:n_tok]
+        run = lambda: olayer.layer_forward(x, wg, spec, expert, shared, wl.act_mode)  # noqa: E731
     # untimed pass to quantise the experts the sample needs (weight preparation, not the layer)
-    olayer.layer_forward(x, wg, spec, expert, shared, wl.act_mode)
+    run()
     runs, elapsed = 0, 0.0
     while elapsed < target_s and runs < 50:
         t0 = time.perf_counter()
-        olayer.layer_forward(x, wg, spec, expert, shared, wl.act_mode)
+        run()
         elapsed += time.perf_counter() - t0
         runs += 1
     if ctl is not None:
@@ -137,13 +143,21 @@ def main():
     layer = dl.build(shape, dev, copies=copies)
     params = qe.with_top_p(layer.params, wl.top_p) if wl.top_p else layer.params
     T = wl.tokens
-    x = dl.activations(shape, T, dev)
+    if wl.block:
+        x = torch.from_numpy(synth.block_states(shape, T)).to(dev)
+        norm_w = torch.from_numpy(synth.norm_weight(shape)).to(dev)
+    else:
+        x = dl.activations(shape, T, dev)
     out = torch.empty((T, shape.d_model), dtype=torch.float32, device=dev)
     ws = qe.workspace(T, shape.top_k, shape.n_experts, shape.d_model, shape.d_ff, act, shape.shared_expert, dev)
     stream = torch.cuda.current_stream(dev)
 
     def step(i, evs=None):
         c = i % copies
+        if wl.block:
+            qe.moe_block_forward(x, norm_w, 1e-5, layer.gate_w, params, layer.routed[c], layer.shared[c], act, out, ws,
+                                 evs)
+            return
         if evs is None:
             qe.moe_layer_forward(x, layer.gate_w, params, layer.routed[c], layer.shared[c], act, out, ws)
         else:
@@ -203,7 +217,12 @@ def main():
     # the routing of this batch (identical every step): distinct experts for the byte count
     idx = torch.empty((T, shape.top_k), dtype=torch.int32, device=dev)
     wts = torch.empty((T, shape.top_k), dtype=torch.float32, device=dev)
-    qe.moe_route(x, layer.gate_w, params, idx, wts, ws)
+    # (a block routes its normalised states; torch recomputes them here only
+    # to count the experts the timed steps read)
+    x_route = x
+    if wl.block:
+        x_route = (x * torch.rsqrt((x * x).mean(dim=1, keepdim=True) + 1e-5) * norm_w).contiguous()
+    qe.moe_route(x_route, layer.gate_w, params, idx, wts, ws)
     counts = torch.empty(shape.n_experts, dtype=torch.int32, device=dev)
     offsets = torch.empty(shape.n_experts + 1, dtype=torch.int32, device=dev)
     perm = torch.empty(T * shape.top_k, dtype=torch.int32, device=dev)
@@ -257,7 +276,7 @@ def main():
                    "top_k": shape.top_k, "router": shape.router, "weights": f"{fmt} group 32",
                    "act_mode": wl.act_mode, "shared_expert": shape.shared_expert,
                    "distinct_experts": int((counts_h > 0).sum()), "routed_rows": int(counts_h.sum()),
-                   "top_p": wl.top_p or shape.top_p, "device_copies": copies},
+                   "top_p": wl.top_p or shape.top_p, "block": wl.block, "device_copies": copies},
         "roofline": roof,
         "timing": {"launch": "eager" if args.no_graph else "hip_graph",
                    "eager_ms_per_step": round(eager_elapsed * 1e3 / args.steps, 5),

@@ -72,6 +72,7 @@ class Workload:
     tokens: int
     act_mode: str               # "f32" (decode GEMV) | "q8_0" (integer-dot path)
     top_p: float = 0.0          # > 0: adaptive expert top-p for this workload
+    block: bool = False         # run as a block: out = x + layer(RMSNorm(x))
 
 
 LAYERS = {
@@ -102,6 +103,9 @@ WORKLOADS = {
     # the pages' decode knob: adaptive expert top-p 0.7
     "glm_b1_topp": Workload("glm_b1_topp", LAYERS["glm"], 1, "f32", top_p=0.7),
     "olmoe_b16_topp": Workload("olmoe_b16_topp", LAYERS["olmoe"], 16, "f32", top_p=0.7),
+    # the layer with its neighbours fused in: RMSNorm before, residual after
+    "olmoe_b16_block": Workload("olmoe_b16_block", LAYERS["olmoe"], 16, "f32", block=True),
+    "olmoe_int4_prefill_block": Workload("olmoe_int4_prefill_block", LAYERS["olmoe_int4"], 2048, "q8_0", block=True),
 }
 
 
