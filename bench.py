@@ -76,14 +76,15 @@ def cpu_baseline(wl, target_s: float):
     except Exception:           # threadpoolctl missing: numpy's own default
         ctl, cores = None, os.cpu_count() or 1
     shape = wl.layer
-    bits = 8 if shape.wformat == "int8" else 4
+    bits = 8 if shape.wformat.startswith("int8") else 4
     cache = {}
 
     def expert(e):
         if e not in cache:
             cache[e] = offn.QuantExpert.from_fp32(synth.expert_weight(shape, e, "gate"),
                                                   synth.expert_weight(shape, e, "up"),
-                                                  synth.expert_weight(shape, e, "down"), bits)
+                                                  synth.expert_weight(shape, e, "down"), bits,
+                                                  shape.wformat.endswith("_row"))
         return cache[e]
 
     spec = olayer.RouterSpec(mode=shape.router, top_k=shape.top_k, renormalize=shape.renormalize,

@@ -35,7 +35,8 @@ class QuantExpert:
     """One expert's quantised matrices as integer codes plus fp32 scales.
 
     bits = 8: codes in [-127, 127]; bits = 4: codes in [-7, 7].
-    gate_q, up_q [I, d]; down_q [d, I]; *_s the matching group scales.
+    gate_q, up_q [I, d]; down_q [d, I]; *_s the matching group scales, or one
+    scale per row ([rows, 1]) when per_row.
     """
     bits: int
     gate_q: np.ndarray
@@ -44,13 +45,15 @@ class QuantExpert:
     up_s: np.ndarray
     down_q: np.ndarray
     down_s: np.ndarray
+    per_row: bool = False
 
     @classmethod
-    def from_fp32(cls, gate, up, down, bits: int) -> "QuantExpert":
-        gq, gs = quant.quantize_weights(gate, bits)
-        uq, us = quant.quantize_weights(up, bits)
-        dq, ds = quant.quantize_weights(down, bits)
-        return cls(bits, gq, gs, uq, us, dq, ds)
+    def from_fp32(cls, gate, up, down, bits: int, per_row: bool = False) -> "QuantExpert":
+        qz = quant.quantize_rows if per_row else quant.quantize_weights
+        gq, gs = qz(gate, bits)
+        uq, us = qz(up, bits)
+        dq, ds = qz(down, bits)
+        return cls(bits, gq, gs, uq, us, dq, ds, per_row)
 
     def dequantized(self):
         return (quant.dequantize(self.gate_q, self.gate_s),

@@ -69,8 +69,30 @@ def quantize_weights(w: np.ndarray, bits: int):
     return q.astype(np.int8).reshape(w.shape), s
 
 
+def quantize_rows(w: np.ndarray, bits: int):
+    """Per-row symmetric quantisation ("Show HN: Getting GLM-5.2 running on my
+    slow computer", section "What's implemented": int8 / packed int4 kernels
+    with per-row scales): one fp32 scale per row over the whole last axis,
+    s = amax / qmax, q = clamp(round_half_even(w / s), -qmax, qmax), in the
+    same fp32 steps as the group quantiser.
+
+    Returns (q, s): q int8 codes with the shape of w, s fp32 [..., 1] (the
+    shape dequantize broadcasts over the groups of a row).
+    """
+    w = np.asarray(w, dtype=np.float32)
+    qmax = np.float32(qmax_for_bits(bits))
+    amax = np.max(np.abs(w), axis=-1, keepdims=True)
+    s = (amax / qmax).astype(np.float32)
+    q = np.zeros(w.shape, dtype=np.float32)
+    nz = (s > 0)[..., 0]
+    if np.any(nz):
+        q[nz] = np.clip(np.rint(w[nz] / s[nz]), -qmax, qmax)
+    return q.astype(np.int8), s
+
+
 def dequantize(q: np.ndarray, s: np.ndarray) -> np.ndarray:
-    """s * q in fp64 (exact: an fp32 scale times a small integer)."""
+    """s * q in fp64 (exact: an fp32 scale times a small integer). s holds one
+    scale per group, or one per row as [..., 1]."""
     g = _groups(np.asarray(q).astype(np.float64))
     return (g * np.asarray(s, dtype=np.float64)[..., None]).reshape(np.shape(q))
 

@@ -59,7 +59,7 @@ class LayerShape:
     routed_scaling_factor: float = 1.0
     has_bias: bool = False
     shared_expert: bool = False
-    wformat: str = "int8"       # "int8" | "int4"  (group 32, fp32 scales)
+    wformat: str = "int8"       # "int8" | "int4" (group 32, fp32 scales) | "int8_row" | "int4_row" (per row)
     zipf_s: float = 0.0         # > 0: Zipf(s) log-prior on the router logits
     top_p: float = 0.0          # adaptive expert top-p (0: keep all k)
 

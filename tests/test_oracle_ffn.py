@@ -15,10 +15,10 @@ import synth
 
 
 def _tiny_experts(lay, bits=None):
-    bits = bits or (8 if lay.wformat == "int8" else 4)
+    bits = bits or (8 if lay.wformat.startswith("int8") else 4)
     return [ffn.QuantExpert.from_fp32(synth.expert_weight(lay, e, "gate"),
                                       synth.expert_weight(lay, e, "up"),
-                                      synth.expert_weight(lay, e, "down"), bits)
+                                      synth.expert_weight(lay, e, "down"), bits, lay.wformat.endswith("_row"))
             for e in range(lay.n_experts + (1 if lay.shared_expert else 0))]
 
 

@@ -147,3 +147,45 @@ def test_page_byte_accounting(golden_dir):
     assert abs(payload / 1e6 - pn["glm_routed_expert_mb_int4"]["value"]) < 0.5
     cold = pn["glm_moe_layers"]["value"] * pn["glm_experts_per_token"]["value"] * payload
     assert abs(cold / 1e9 - pn["glm_cold_token_gb"]["value"]) / pn["glm_cold_token_gb"]["value"] < 0.02
+
+
+# ---------------------------------------------------------------------------
+# per-row scales (the GLM engine's kernels: one scale per row)
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("bits", [8, 4])
+def test_per_row_on_one_group_rows_equals_group_32(bits):
+    # a row of exactly 32 values is one group: both quantisers must agree
+    w = (np.random.default_rng(11).standard_normal((40, 32)) * 0.02).astype(np.float32)
+    qr, sr = quant.quantize_rows(w, bits)
+    qg, sg = quant.quantize_weights(w, bits)
+    assert np.array_equal(qr, qg) and np.array_equal(sr[:, 0], sg[:, 0])
+
+
+@pytest.mark.parametrize("bits", [8, 4])
+def test_per_row_round_trip_and_amax(bits):
+    rng = np.random.default_rng(12)
+    w = (rng.standard_normal((33, 256)) * 0.02).astype(np.float32)
+    w[5] = 0.0                                                   # an all-zero row: scale 0, codes 0
+    q, s = quant.quantize_rows(w, bits)
+    qmax = 127 if bits == 8 else 7
+    assert s.shape == (33, 1) and s[5, 0] == 0 and np.all(q[5] == 0)
+    err = np.abs(quant.dequantize(q, s) - w.astype(np.float64))
+    assert np.all(err <= s.astype(np.float64) / 2 * (1 + 1e-6))  # nearest code
+    rows = [r for r in range(33) if r != 5]
+    am = np.argmax(np.abs(w[rows]), axis=1)
+    assert np.all(np.abs(q[rows, am]) == qmax)                   # the row's amax maps to +-qmax
+    # one scale per row: the error of a per-row code can exceed the group
+    # quantiser's, never its own half step
+    qg, sg = quant.quantize_weights(w, bits)
+    assert np.abs(quant.dequantize(qg, sg) - w).max() <= np.abs(quant.dequantize(q, s) - w).max()
+
+
+def test_per_row_hand_worked():
+    # row [0.7, -0.35, 0.1, ...zeros]: amax 0.7, int4 scale 0.1: codes 7, -3.5 -> -4 (half to even), 1
+    w = np.zeros((1, 64), np.float32)
+    w[0, :3] = [0.7, -0.35, 0.1]
+    q, s = quant.quantize_rows(w, 4)
+    assert np.isclose(s[0, 0], np.float32(0.7) / np.float32(7))
+    assert q[0, :3].tolist() == [7, -4, 1] and np.all(q[0, 3:] == 0)
+    # int4 packing of per-row codes unpacks to the same int8 container
+    assert np.array_equal(quant.unpack_int4(quant.pack_int4(q)), q)
