@@ -26,13 +26,15 @@ MOE_ROUTER_SOFTMAX_TOPK = 0
 MOE_ROUTER_SIGMOID_NOAUX_TC = 1
 MOE_W_INT8_G32 = 0
 MOE_W_INT4_G32 = 1
+MOE_W_INT8_ROW = 2
+MOE_W_INT4_ROW = 3
 MOE_ACT_F32 = 0
 MOE_ACT_Q8_0 = 1
 
 STAGES = ("route", "dispatch", "quant_x", "gateup", "down", "combine")
 MOE_STAGE_COUNT = len(STAGES)
 
-FORMATS = {"int8": MOE_W_INT8_G32, "int4": MOE_W_INT4_G32}
+FORMATS = {"int8": MOE_W_INT8_G32, "int4": MOE_W_INT4_G32, "int8_row": MOE_W_INT8_ROW, "int4_row": MOE_W_INT4_ROW}
 ACT_MODES = {"f32": MOE_ACT_F32, "q8_0": MOE_ACT_Q8_0}
 ROUTERS = {"softmax": MOE_ROUTER_SOFTMAX_TOPK, "noaux_tc": MOE_ROUTER_SIGMOID_NOAUX_TC}
 
@@ -168,9 +170,11 @@ class QuantExperts:
 
     Tensor shapes give the per-expert storage size only: gate_q / up_q hold
     I*d bytes (int8) or I*d/2 (packed int4) per expert, shaped [E, I, d] or
-    [E, I, d/2]; scales I*d/32 floats, shaped [E, I, d/32]; down_q / down_s
-    likewise with d and I swapped. The bytes inside are in the lane-tiled
-    layout of include/moe.h (32-row tiles, lane-ordered), not row-major.
+    [E, I, d/2]; scales I*d/32 floats, shaped [E, I, d/32] (the per-row
+    formats: I floats, shaped [E, I, 1]); down_q / down_s likewise with d and
+    I swapped. The bytes inside are in the lane-tiled layout of
+    include/moe.h (32-row tiles, lane-ordered), not row-major; per-row scales
+    are in row order.
     """
 
     def __init__(self, fmt: str, gate_q, gate_s, up_q, up_s, down_q, down_s):
@@ -183,15 +187,21 @@ class QuantExperts:
 
     @classmethod
     def empty(cls, n_experts: int, d_model: int, d_ff: int, fmt: str, device="cuda"):
-        div = 1 if fmt == "int8" else 2
-        qdt = torch.int8 if fmt == "int8" else torch.uint8
+        if fmt not in FORMATS:
+            raise ValueError(f"unknown weight format {fmt!r}")
+        int8 = fmt.startswith("int8")
+        div = 1 if int8 else 2
+        qdt = torch.int8 if int8 else torch.uint8
+        per_row = fmt.endswith("_row")
+        sg_d = 1 if per_row else d_model // 32    # scales per gate / up row
+        sg_i = 1 if per_row else d_ff // 32       # scales per down row
         return cls(fmt,
                    torch.empty((n_experts, d_ff, d_model // div), dtype=qdt, device=device),
-                   torch.empty((n_experts, d_ff, d_model // 32), dtype=torch.float32, device=device),
+                   torch.empty((n_experts, d_ff, sg_d), dtype=torch.float32, device=device),
                    torch.empty((n_experts, d_ff, d_model // div), dtype=qdt, device=device),
-                   torch.empty((n_experts, d_ff, d_model // 32), dtype=torch.float32, device=device),
+                   torch.empty((n_experts, d_ff, sg_d), dtype=torch.float32, device=device),
                    torch.empty((n_experts, d_model, d_ff // div), dtype=qdt, device=device),
-                   torch.empty((n_experts, d_model, d_ff // 32), dtype=torch.float32, device=device))
+                   torch.empty((n_experts, d_model, sg_i), dtype=torch.float32, device=device))
 
     def abi(self) -> Experts:
         ex = Experts()

@@ -9,7 +9,7 @@ The pages give the same accounting for their GLM-5.2 layer: a routed expert is
 about 19 MB of int4 payload and a cold token reads about 11.4 GB of experts
 over 75 layers of 8 experts ("Show HN: Getting GLM-5.2 running on my slow computer", sections "The idea" and "Got
 a better machine?"). Group-32 fp32 scales add 4 bytes per 32 weights on top of
-that payload.
+that payload; per-row scales add 4 bytes per matrix row.
 """
 from __future__ import annotations
 
@@ -19,9 +19,11 @@ GROUP = 32
 
 
 def matrix_bytes(rows: int, cols: int, fmt: str) -> int:
-    """Quantised codes + fp32 group scales of one [rows, cols] matrix."""
-    payload = rows * cols if fmt == "int8" else rows * cols // 2
-    return payload + rows * (cols // GROUP) * 4
+    """Quantised codes + fp32 scales (per group of 32, or per row for the
+    "_row" formats) of one [rows, cols] matrix."""
+    payload = rows * cols if fmt.startswith("int8") else rows * cols // 2
+    scales = rows if fmt.endswith("_row") else rows * (cols // GROUP)
+    return payload + scales * 4
 
 
 def expert_bytes(d: int, d_ff: int, fmt: str) -> int:

@@ -82,8 +82,7 @@ moe_status check_experts(const moe_experts* ex, const char* name, int act_mode) 
                 ex->d_model, ex->d_ff);
     MOE_REQUIRE(ex->d_model % (2 * moe::kGroup) == 0 && ex->d_ff % (2 * moe::kGroup) == 0, MOE_ERR_UNSUPPORTED,
                 "%s d_model %d and d_ff %d must be multiples of 64 (pairs of groups)", name, ex->d_model, ex->d_ff);
-    MOE_REQUIRE(ex->format == MOE_W_INT8_G32 || ex->format == MOE_W_INT4_G32, MOE_ERR_INVALID_ARG,
-                "%s unknown weight format %d", name, ex->format);
+    MOE_REQUIRE(moe::fmt_valid(ex->format), MOE_ERR_INVALID_ARG, "%s unknown weight format %d", name, ex->format);
     MOE_REQUIRE(ex->gate_q && ex->gate_s && ex->up_q && ex->up_s && ex->down_q && ex->down_s, MOE_ERR_INVALID_ARG,
                 "%s has a NULL weight or scale pointer", name);
     MOE_REQUIRE(aligned16(ex->gate_q) && aligned16(ex->up_q) && aligned16(ex->down_q), MOE_ERR_INVALID_ARG,
@@ -128,7 +127,7 @@ hipEvent_t stage_ev(const hipEvent_t* ev, int idx) { return ev ? ev[idx] : nullp
 // Where the prepared hidden states go in the workspace (f32 parts or Q8_0).
 moe::XPrep xprep_for(int act_mode, int fmt, const moe::WsLayout& L, void* ws) {
     moe::XPrep xp;
-    xp.fmt = fmt;
+    xp.fmt = moe::fmt_codes(fmt);
     if (act_mode == MOE_ACT_F32) {
         xp.mode = moe::XPREP_SPLIT;
         xp.hi = ws_at<_Float16>(ws, L.xq);
@@ -342,13 +341,11 @@ moe_status moe_quantize_weights(const float* w, int64_t rows, int32_t cols, int3
                 "cols = %d is not a multiple of 64 (pairs of groups)", cols);
     MOE_REQUIRE(matrix_rows % moe::kTile == 0, MOE_ERR_UNSUPPORTED,
                 "matrix_rows = %d is not a multiple of 32 (tiled layout)", matrix_rows);
-    MOE_REQUIRE(format == MOE_W_INT8_G32 || format == MOE_W_INT4_G32, MOE_ERR_INVALID_ARG, "unknown format %d",
-                format);
+    MOE_REQUIRE(moe::fmt_valid(format), MOE_ERR_INVALID_ARG, "unknown format %d", format);
     if (rows == 0) return ok();
     MOE_REQUIRE(w && q && s, MOE_ERR_INVALID_ARG, "NULL tensor argument");
     MOE_REQUIRE(aligned16(w) && aligned16(q), MOE_ERR_INVALID_ARG, "w and q must be 16-byte aligned");
-    MOE_HIP(moe::launch_quantize_weights(w, rows, cols, matrix_rows, format == MOE_W_INT8_G32 ? 8 : 4, q, s, stream),
-            "weight quantiser");
+    MOE_HIP(moe::launch_quantize_weights(w, rows, cols, matrix_rows, format, q, s, stream), "weight quantiser");
     return ok();
 }
 

@@ -121,6 +121,17 @@ inline WsLayout ws_layout(int T, int k, int E, int d, int I, int act_mode, int h
 // ---------------------------------------------------------------------------
 constexpr int kTile = 32;
 
+// Weight formats: the code layout (int8 or packed int4, both described
+// above) and where the scales live (per group as above, or per row: one float
+// per matrix row, in row order).
+__host__ __device__ constexpr bool fmt_int8(int fmt) { return fmt == MOE_W_INT8_G32 || fmt == MOE_W_INT8_ROW; }
+__host__ __device__ constexpr int fmt_codes(int fmt) { return fmt_int8(fmt) ? MOE_W_INT8_G32 : MOE_W_INT4_G32; }
+__host__ __device__ constexpr bool fmt_per_row(int fmt) { return fmt == MOE_W_INT8_ROW || fmt == MOE_W_INT4_ROW; }
+inline bool fmt_valid(int fmt) { return fmt >= MOE_W_INT8_G32 && fmt <= MOE_W_INT4_ROW; }
+// bytes of codes and floats of scales of one N x K matrix
+inline int64_t fmt_code_bytes(int fmt, int64_t N, int64_t K) { return fmt_int8(fmt) ? N * K : N * K / 2; }
+inline int64_t fmt_scale_floats(int fmt, int64_t N, int64_t K) { return fmt_per_row(fmt) ? N : N * (K / kGroup); }
+
 // byte offset, inside one matrix of NT tiles, of the 8 int8 codes (row,
 // k = 8*k8 .. +7)
 __host__ __device__ __forceinline__ size_t int8_code_offset(size_t row, size_t k8, size_t NT) {

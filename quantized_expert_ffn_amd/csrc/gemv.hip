@@ -80,7 +80,11 @@ constexpr int kMaxGemvGroups = 256;   // K <= 8192
 // product per group gives the exact integer group dot and no lo part is
 // needed; both group scales are applied to it per output (the activation
 // scale varies by row, from an LDS table of the tile's 16 rows).
-template <int FMT, bool GATEUP, int KS, bool Q8>
+//
+// ROW (a scale per weight row): no scale loads in the loop; only the
+// activation side's per-group factor joins each group's product, and the
+// row's scale multiplies the finished sum once.
+template <int FMT, bool GATEUP, int KS, bool Q8, bool ROW>
 __global__ __launch_bounds__(64 * KS) void gemv_kernel(const GemvArgs a) {
     constexpr int kCL = FMT == MOE_W_INT8_G32 ? 2 : 1;   // 16-byte code loads per tile per pair
     __shared__ float pwtab[Q8 ? 16 * kMaxGemvGroups : kMaxGemvGroups];   // Q8: [group][16 rows]
@@ -115,6 +119,17 @@ __global__ __launch_bounds__(64 * KS) void gemv_kernel(const GemvArgs a) {
         // four consecutive pairs' scale blocks are 1 KB: lane nl + 16q reads
         // pair q's 16 bytes for rows nl, 16 + nl
         s_voff[t] = tile[t] * P * 256 + lane * 16;
+    }
+    // ROW: the scales of this lane's output rows (a tile past the matrix
+    // reads zeros)
+    float srow[2][2];
+    if constexpr (ROW) {
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+            for (int r = 0; r < 2; ++r)
+                srow[t][r] = __builtin_bit_cast(
+                    float, __builtin_amdgcn_raw_buffer_load_b32(rs[t], (tile[t] * kTile + 16 * r + nl) * 4, 0, 0));
     }
     const int a_bytes = a.a_rows * K * 2;
     const __amdgpu_buffer_rsrc_t rah = __builtin_amdgcn_make_buffer_rsrc((void*)a.ahi, 0, a_bytes, 0x00020000);
@@ -164,7 +179,7 @@ __global__ __launch_bounds__(64 * KS) void gemv_kernel(const GemvArgs a) {
         // quads (four pairs each: the current one and the next)
         uint4 wq[2][2][kCL];
         v8h xh[2][2], xl[2][2];
-        uint4 sq_cur[2], sq_next[2];
+        uint4 sq_cur[2] = {}, sq_next[2] = {};
         auto load = [&](int sp, int j) {
             // past the end: the last pair again (L2-resident), so that every
             // step issues the same loads and waits stay counted
@@ -185,6 +200,7 @@ __global__ __launch_bounds__(64 * KS) void gemv_kernel(const GemvArgs a) {
         };
         // scales of pairs c0 + 4q .. + 3 (those past the run are read but unused)
         auto load_quad = [&](int q) {
+            if constexpr (ROW) return;
 #pragma unroll
             for (int t = 0; t < 2; ++t)
                 sq_next[t] = __builtin_bit_cast(
@@ -205,13 +221,15 @@ __global__ __launch_bounds__(64 * KS) void gemv_kernel(const GemvArgs a) {
                 pw1 = pwtab[2 * p + 1];
             }
             const int src = (nl + 16 * r) * 4;
-            float sc[2][4];
+            float sc[2][4] = {};
+            if constexpr (!ROW) {
 #pragma unroll
-            for (int t = 0; t < 2; ++t) {
-                sc[t][0] = __int_as_float(__builtin_amdgcn_ds_bpermute(src, (int)sq_cur[t].x));
-                sc[t][1] = __int_as_float(__builtin_amdgcn_ds_bpermute(src, (int)sq_cur[t].y));
-                sc[t][2] = __int_as_float(__builtin_amdgcn_ds_bpermute(src, (int)sq_cur[t].z));
-                sc[t][3] = __int_as_float(__builtin_amdgcn_ds_bpermute(src, (int)sq_cur[t].w));
+                for (int t = 0; t < 2; ++t) {
+                    sc[t][0] = __int_as_float(__builtin_amdgcn_ds_bpermute(src, (int)sq_cur[t].x));
+                    sc[t][1] = __int_as_float(__builtin_amdgcn_ds_bpermute(src, (int)sq_cur[t].y));
+                    sc[t][2] = __int_as_float(__builtin_amdgcn_ds_bpermute(src, (int)sq_cur[t].z));
+                    sc[t][3] = __int_as_float(__builtin_amdgcn_ds_bpermute(src, (int)sq_cur[t].w));
+                }
             }
 #pragma unroll
             for (int gi = 0; gi < 2; ++gi) {
@@ -230,7 +248,17 @@ __global__ __launch_bounds__(64 * KS) void gemv_kernel(const GemvArgs a) {
                     }
                     v4f d0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(xh[jj][gi], b0, v4f{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
                     v4f d1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(xh[jj][gi], b1, v4f{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
-                    if constexpr (Q8) {
+                    if constexpr (Q8 && ROW) {
+                        const float4 x = sx[gi];
+                        acc[t][0][0] = fmaf(d0[0], x.x, acc[t][0][0]);
+                        acc[t][0][1] = fmaf(d0[1], x.y, acc[t][0][1]);
+                        acc[t][0][2] = fmaf(d0[2], x.z, acc[t][0][2]);
+                        acc[t][0][3] = fmaf(d0[3], x.w, acc[t][0][3]);
+                        acc[t][1][0] = fmaf(d1[0], x.x, acc[t][1][0]);
+                        acc[t][1][1] = fmaf(d1[1], x.y, acc[t][1][1]);
+                        acc[t][1][2] = fmaf(d1[2], x.z, acc[t][1][2]);
+                        acc[t][1][3] = fmaf(d1[3], x.w, acc[t][1][3]);
+                    } else if constexpr (Q8) {
                         const float s0 = sc[t][2 * gi], s1 = sc[t][2 * gi + 1];
                         const float4 x = sx[gi];
                         acc[t][0][0] = fmaf(d0[0], s0 * x.x, acc[t][0][0]);
@@ -244,8 +272,8 @@ __global__ __launch_bounds__(64 * KS) void gemv_kernel(const GemvArgs a) {
                     } else {
                         d0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(xl[jj][gi], b0, d0, 0, 0, 0);
                         d1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(xl[jj][gi], b1, d1, 0, 0, 0);
-                        const float f0 = sc[t][2 * gi] * pw;
-                        const float f1 = sc[t][2 * gi + 1] * pw;
+                        const float f0 = ROW ? pw : sc[t][2 * gi] * pw;
+                        const float f1 = ROW ? pw : sc[t][2 * gi + 1] * pw;
 #pragma unroll
                         for (int i = 0; i < 4; ++i) {
                             acc[t][0][i] = fmaf(d0[i], f0, acc[t][0][i]);
@@ -311,6 +339,14 @@ __global__ __launch_bounds__(64 * KS) void gemv_kernel(const GemvArgs a) {
             }
         }
         if (ks != 0) continue;
+        if constexpr (ROW) {
+#pragma unroll
+            for (int t = 0; t < 2; ++t)
+#pragma unroll
+                for (int r = 0; r < 2; ++r)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) acc[t][r][i] *= srow[t][r];
+        }
 
         if constexpr (GATEUP && Q8) {
             // H = silu(G) * U, then Q8_0 of each token's 32 columns (one group
@@ -424,9 +460,8 @@ hipError_t launch_gemv(const moe_experts& routed, const moe_experts* shared, boo
     a.N = gateup ? I : d;
     a.R = R;
     if (a.K / kGroup > kMaxGemvGroups) return hipErrorInvalidValue;
-    const int64_t codes = routed.format == MOE_W_INT8_G32 ? (int64_t)a.N * a.K : (int64_t)a.N * a.K / 2;
-    a.q_stride = codes;
-    a.s_stride = (int64_t)a.N * (a.K / kGroup);
+    a.q_stride = fmt_code_bytes(routed.format, a.N, a.K);
+    a.s_stride = fmt_scale_floats(routed.format, a.N, a.K);
     const moe_experts& sh = shared ? *shared : routed;
     if (gateup) {
         a.q[0] = (const uint8_t*)routed.gate_q; a.s[0] = routed.gate_s;
@@ -445,21 +480,25 @@ hipError_t launch_gemv(const moe_experts& routed, const moe_experts* shared, boo
     const int bx = gateup ? tiles : (tiles + 1) / 2;
     const int ks = choose_ks(max_slots, bx, a.K / (2 * kGroup));
     const dim3 grid(bx, max_slots);
-#define MOE_GEMV(FMT, GU, KSV)                                                                           \
-    do {                                                                                                 \
-        if (q8) launch_timed(gemv_kernel<FMT, GU, KSV, true>, grid, dim3(64 * KSV), st, ev0, ev1, a);    \
-        else launch_timed(gemv_kernel<FMT, GU, KSV, false>, grid, dim3(64 * KSV), st, ev0, ev1, a);      \
+#define MOE_GEMV(FMT, RW, GU, KSV)                                                                        \
+    do {                                                                                                  \
+        if (q8) launch_timed(gemv_kernel<FMT, GU, KSV, true, RW>, grid, dim3(64 * KSV), st, ev0, ev1, a); \
+        else launch_timed(gemv_kernel<FMT, GU, KSV, false, RW>, grid, dim3(64 * KSV), st, ev0, ev1, a);   \
     } while (0)
-#define MOE_GEMV_KS(FMT, GU)                \
-    if (ks == 1) MOE_GEMV(FMT, GU, 1);      \
-    else if (ks == 2) MOE_GEMV(FMT, GU, 2); \
-    else if (ks == 4) MOE_GEMV(FMT, GU, 4); \
-    else MOE_GEMV(FMT, GU, 8);
-    if (routed.format == MOE_W_INT8_G32) {
-        if (gateup) { MOE_GEMV_KS(MOE_W_INT8_G32, true) } else { MOE_GEMV_KS(MOE_W_INT8_G32, false) }
-    } else {
-        if (gateup) { MOE_GEMV_KS(MOE_W_INT4_G32, true) } else { MOE_GEMV_KS(MOE_W_INT4_G32, false) }
+#define MOE_GEMV_KS(FMT, RW, GU)                \
+    if (ks == 1) MOE_GEMV(FMT, RW, GU, 1);      \
+    else if (ks == 2) MOE_GEMV(FMT, RW, GU, 2); \
+    else if (ks == 4) MOE_GEMV(FMT, RW, GU, 4); \
+    else MOE_GEMV(FMT, RW, GU, 8);
+#define MOE_GEMV_GU(FMT, RW) \
+    if (gateup) { MOE_GEMV_KS(FMT, RW, true) } else { MOE_GEMV_KS(FMT, RW, false) }
+    switch (routed.format) {
+        case MOE_W_INT8_G32: MOE_GEMV_GU(MOE_W_INT8_G32, false) break;
+        case MOE_W_INT4_G32: MOE_GEMV_GU(MOE_W_INT4_G32, false) break;
+        case MOE_W_INT8_ROW: MOE_GEMV_GU(MOE_W_INT8_G32, true) break;
+        default: MOE_GEMV_GU(MOE_W_INT4_G32, true) break;
     }
+#undef MOE_GEMV_GU
 #undef MOE_GEMV_KS
 #undef MOE_GEMV
     return hipGetLastError();

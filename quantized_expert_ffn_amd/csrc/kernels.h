@@ -6,7 +6,7 @@
 
 namespace moe {
 
-hipError_t launch_quantize_weights(const float* w, int64_t rows, int cols, int matrix_rows, int bits, void* q,
+hipError_t launch_quantize_weights(const float* w, int64_t rows, int cols, int matrix_rows, int format, void* q,
                                    float* s, hipStream_t st);
 hipError_t launch_quantize_q8_0(const float* x, int64_t rows, int cols, int8_t* q, float* d, hipStream_t st);
 

@@ -14,7 +14,10 @@
 //     acc[m][n] += I_g[m, n] * (sx[m, g] * sw[n, g])
 // which is two VALU operations per output and group (an int8 matrix-core
 // product would need a third, the int -> float conversion, and the VALU work
-// is what bounds this kernel).
+// is what bounds this kernel). With one scale per weight row (the per-row
+// formats) the group's factor is sx alone, one VALU operation per output and
+// group, and the row's scale multiplies the finished sum:
+//     acc[m][n] = sw[n] * sum_g I_g[m, n] * sx[m, g]
 //
 // Block tile: 128 rows (tokens of one expert) x 128 weight rows (four 32-row
 // tiles), staged through LDS one group pair (64 k) at a time, double
@@ -53,6 +56,7 @@ constexpr int kM16 = kBM / 16;       // 16-row tiles per block
 //      int4: [4 tiles][1 KB]              (one block holds the pair)
 //   SX [kSG groups][kBM rows] fp32        activation scales
 //   SW [4 tiles][64] fp32                 the tiles' scale blocks of the pair
+//                                         (group-scale formats only)
 constexpr int kLdsA = kSG * kM16 * 1024;   // 16384
 constexpr int kLdsSX = kSG * kBM * 4;      // 1024
 constexpr int kLdsSW = 4 * 64 * 4;         // 1024
@@ -134,7 +138,7 @@ __device__ __forceinline__ float row16_max(float v) {
     return v;
 }
 
-template <int FMT, bool GATEUP, bool DBG>
+template <int FMT, bool GATEUP, bool DBG, bool ROW>
 __global__ __launch_bounds__(256) void q8_mfma_kernel(const MfmaArgs a) {
     constexpr int kStage = lds_stage_bytes<FMT>();
     // the two stage buffers are separate objects, so the compiler can tell
@@ -203,7 +207,7 @@ __global__ __launch_bounds__(256) void q8_mfma_kernel(const MfmaArgs a) {
         constexpr int nA = kSG * kM16;
         constexpr int nB = FMT == MOE_W_INT8_G32 ? 4 * kSG : 4;
         constexpr int nSX = kSG * 2;
-        constexpr int nJobs = nA + nB + nSX + 1;
+        constexpr int nJobs = nA + nB + nSX + (ROW ? 0 : 1);
         static_assert((nA + nB) % 4 == 0, "scale jobs must start on wave 0");
 #pragma unroll
         for (int job = 0; job < nJobs; ++job) {
@@ -262,13 +266,26 @@ __global__ __launch_bounds__(256) void q8_mfma_kernel(const MfmaArgs a) {
     const int oSW0 = opaque(kLdsA + lds_b_bytes<FMT>() + kLdsSX + (jt0 * 64 + nl * 4) * 4);
     const int oSW1 = opaque(kLdsA + lds_b_bytes<FMT>() + kLdsSX + (jt1 * 64 + nl * 4) * 4);
 
+    // ROW: the scales of the wave's four 16-row weight halves, lane row nl
+    float srow[4];
+    if constexpr (ROW) {
+#pragma unroll
+        for (int n = 0; n < 4; ++n) {
+            const int jt = n < 2 ? jt0 : jt1;
+            srow[n] = wsb[mat_of(jt)][tile_of(jt) * kTile + 16 * (n & 1) + nl];
+        }
+    }
+
     auto compute = [&](const lds_byte* base, int st) __attribute__((always_inline)) {
         // [row nl, g0][row 16+nl, g0][row nl, g1][row 16+nl, g1] of each tile
         // (zero for the padding stage past the last pair)
         const bool real = st < P;
-        float4 sw0 = lds_read<float4>(base + oSW0);
-        float4 sw1 = lds_read<float4>(base + oSW1);
-        if (!real) sw0 = sw1 = make_float4(0.f, 0.f, 0.f, 0.f);
+        float4 sw0 = make_float4(0.f, 0.f, 0.f, 0.f), sw1 = sw0;
+        if constexpr (!ROW) {
+            sw0 = lds_read<float4>(base + oSW0);
+            sw1 = lds_read<float4>(base + oSW1);
+            if (!real) sw0 = sw1 = make_float4(0.f, 0.f, 0.f, 0.f);
+        }
         uint4 c4[2];
         if constexpr (FMT == MOE_W_INT4_G32) {
             c4[0] = lds_read<uint4>(base + oB0);
@@ -305,10 +322,17 @@ __global__ __launch_bounds__(256) void q8_mfma_kernel(const MfmaArgs a) {
 #pragma unroll
                 for (int i = 0; i < LIVE; ++i) {
                     const v4f d = __builtin_amdgcn_mfma_f32_16x16x32_f16(af[i], bf, v4f{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
-                    acc[i][n][0] = fmaf(d[0], sx[i].x * sw, acc[i][n][0]);
-                    acc[i][n][1] = fmaf(d[1], sx[i].y * sw, acc[i][n][1]);
-                    acc[i][n][2] = fmaf(d[2], sx[i].z * sw, acc[i][n][2]);
-                    acc[i][n][3] = fmaf(d[3], sx[i].w * sw, acc[i][n][3]);
+                    if constexpr (ROW) {
+                        acc[i][n][0] = fmaf(d[0], sx[i].x, acc[i][n][0]);
+                        acc[i][n][1] = fmaf(d[1], sx[i].y, acc[i][n][1]);
+                        acc[i][n][2] = fmaf(d[2], sx[i].z, acc[i][n][2]);
+                        acc[i][n][3] = fmaf(d[3], sx[i].w, acc[i][n][3]);
+                    } else {
+                        acc[i][n][0] = fmaf(d[0], sx[i].x * sw, acc[i][n][0]);
+                        acc[i][n][1] = fmaf(d[1], sx[i].y * sw, acc[i][n][1]);
+                        acc[i][n][2] = fmaf(d[2], sx[i].z * sw, acc[i][n][2]);
+                        acc[i][n][3] = fmaf(d[3], sx[i].w * sw, acc[i][n][3]);
+                    }
                     if constexpr (DBG) {
                         const int jt = t ? jt1 : jt0;
                         const int wt = T0 + (GATEUP ? (jt & 1) : jt);
@@ -349,12 +373,22 @@ __global__ __launch_bounds__(256) void q8_mfma_kernel(const MfmaArgs a) {
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         __syncthreads();
         if (st + 2 < P2) issue_stage(st + 2, buf0);
-        compute(buf1, st + 1);
+        // per-row formats have no weight scale to zero: they skip the
+        // padding stage's products
+        if (!ROW || st + 1 < P) compute(buf1, st + 1);
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         __syncthreads();
     }
 
     // ---- epilogue ----
+    if constexpr (ROW) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int n = 0; n < 4; ++n)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) acc[i][n][r] *= srow[n];
+    }
     if constexpr (GATEUP) {
         const int t = T0 + wn;                  // weight tile = group of H's columns
         const int GN = N / kGroup;
@@ -430,8 +464,7 @@ hipError_t launch_q8_mfma(const moe_experts& routed, const moe_experts* shared, 
     a.dbg1 = dbg1;
     a.dbg_hq = dbg_hq;
     auto fill = [&](MfmaMat* dst, const moe_experts& ev) {
-        const int64_t rowb = ev.format == MOE_W_INT8_G32 ? a.K : a.K / 2;
-        const int64_t qs = (int64_t)a.N * rowb, ss = (int64_t)a.N * (a.K / kGroup);
+        const int64_t qs = fmt_code_bytes(ev.format, a.N, a.K), ss = fmt_scale_floats(ev.format, a.N, a.K);
         if (gateup) {
             dst[0] = MfmaMat{(const uint8_t*)ev.gate_q, ev.gate_s, qs, ss};
             dst[1] = MfmaMat{(const uint8_t*)ev.up_q, ev.up_s, qs, ss};
@@ -445,14 +478,17 @@ hipError_t launch_q8_mfma(const moe_experts& routed, const moe_experts* shared, 
     const int bn = gateup ? 2 * kTile : 4 * kTile;   // output columns per block
     const dim3 grid((a.N + bn - 1) / bn, max_tiles);
     const bool dbg = dbg0 != nullptr;
-#define MOE_Q8(FMT, GU, DB) launch_timed(q8_mfma_kernel<FMT, GU, DB>, grid, dim3(256), st, ev0, ev1, a)
-    if (routed.format == MOE_W_INT8_G32) {
-        if (gateup) { if (dbg) MOE_Q8(MOE_W_INT8_G32, true, true); else MOE_Q8(MOE_W_INT8_G32, true, false); }
-        else { if (dbg) MOE_Q8(MOE_W_INT8_G32, false, true); else MOE_Q8(MOE_W_INT8_G32, false, false); }
-    } else {
-        if (gateup) { if (dbg) MOE_Q8(MOE_W_INT4_G32, true, true); else MOE_Q8(MOE_W_INT4_G32, true, false); }
-        else { if (dbg) MOE_Q8(MOE_W_INT4_G32, false, true); else MOE_Q8(MOE_W_INT4_G32, false, false); }
+#define MOE_Q8(FMT, GU, DB, RW) launch_timed(q8_mfma_kernel<FMT, GU, DB, RW>, grid, dim3(256), st, ev0, ev1, a)
+#define MOE_Q8_GU(FMT, RW)                                                              \
+    if (gateup) { if (dbg) MOE_Q8(FMT, true, true, RW); else MOE_Q8(FMT, true, false, RW); } \
+    else { if (dbg) MOE_Q8(FMT, false, true, RW); else MOE_Q8(FMT, false, false, RW); }
+    switch (routed.format) {
+        case MOE_W_INT8_G32: MOE_Q8_GU(MOE_W_INT8_G32, false) break;
+        case MOE_W_INT4_G32: MOE_Q8_GU(MOE_W_INT4_G32, false) break;
+        case MOE_W_INT8_ROW: MOE_Q8_GU(MOE_W_INT8_G32, true) break;
+        default: MOE_Q8_GU(MOE_W_INT4_G32, true) break;
     }
+#undef MOE_Q8_GU
 #undef MOE_Q8
     return hipGetLastError();
 }

@@ -86,6 +86,9 @@ LAYERS = {
                       router="noaux_tc", n_group=8, topk_group=4,
                       routed_scaling_factor=2.5, has_bias=True, shared_expert=True,
                       wformat="int4"),
+    # per-row scales: the OLMoE shape with one fp32 scale per matrix row
+    "olmoe_int4_row": LayerShape("olmoe_int4_row", 1006, d_model=2048, n_experts=64, d_ff=1024,
+                                 top_k=8, router="softmax", renormalize=False, wformat="int4_row"),
     "qwen": LayerShape("qwen", 1005, d_model=2048, n_experts=512, d_ff=512, top_k=10,
                        router="softmax", renormalize=True, shared_expert=True,
                        wformat="int4", zipf_s=1.1),
@@ -103,6 +106,10 @@ WORKLOADS = {
     # the pages' decode knob: adaptive expert top-p 0.7
     "glm_b1_topp": Workload("glm_b1_topp", LAYERS["glm"], 1, "f32", top_p=0.7),
     "olmoe_b16_topp": Workload("olmoe_b16_topp", LAYERS["olmoe"], 16, "f32", top_p=0.7),
+    "olmoe_b16_int4": Workload("olmoe_b16_int4", LAYERS["olmoe_int4"], 16, "f32"),
+    # per-row weight scales (decode and prefill)
+    "olmoe_b16_int4_row": Workload("olmoe_b16_int4_row", LAYERS["olmoe_int4_row"], 16, "f32"),
+    "olmoe_int4_row_prefill": Workload("olmoe_int4_row_prefill", LAYERS["olmoe_int4_row"], 2048, "q8_0"),
     # the layer with its neighbours fused in: RMSNorm before, residual after
     "olmoe_b16_block": Workload("olmoe_b16_block", LAYERS["olmoe"], 16, "f32", block=True),
     "olmoe_int4_prefill_block": Workload("olmoe_int4_prefill_block", LAYERS["olmoe_int4"], 2048, "q8_0", block=True),

@@ -70,7 +70,7 @@ def untile_codes(tiled: np.ndarray, n_rows: int, n_cols: int, fmt: str) -> np.nd
     (element 2i in the low nibble of byte i)."""
     flat = np.asarray(tiled).reshape(-1).view(np.uint8)
     nt, g = n_rows // 32, n_cols // 32
-    if fmt == "int8":
+    if fmt.startswith("int8"):
         # (group, tile, h, nl, half, byte) -> row = 32 tile + 16 half + nl, k = 32 group + 8 h + byte
         a = flat.reshape(g, nt, 4, 16, 2, 8).transpose(1, 4, 3, 0, 2, 5)
         return a.reshape(n_rows, n_cols).view(np.int8)
@@ -79,9 +79,12 @@ def untile_codes(tiled: np.ndarray, n_rows: int, n_cols: int, fmt: str) -> np.nd
     return a.reshape(n_rows, n_cols // 2)
 
 
-def untile_scales(tiled: np.ndarray, n_rows: int, n_cols: int) -> np.ndarray:
-    """Library group scales (lane-tiled layout) back to row-major [N, K/32]."""
+def untile_scales(tiled: np.ndarray, n_rows: int, n_cols: int, fmt: str = "int8") -> np.ndarray:
+    """Library scales back to the oracle's shape: group scales (lane-tiled
+    layout) to row-major [N, K/32]; per-row scales (row order) to [N, 1]."""
     flat = np.asarray(tiled).reshape(-1)
+    if fmt.endswith("_row"):
+        return flat.reshape(n_rows, 1)
     nt, g = n_rows // 32, n_cols // 32
     a = flat.reshape(nt, g // 2, 16, 2, 2).transpose(0, 4, 2, 1, 3)   # (tile, half, nl, pair, group of pair)
     return a.reshape(n_rows, g)

@@ -97,6 +97,9 @@ def test_layer_forward_validation(lib):
     assert _fwd(lib, routed=_experts(d_model=96)) == UNSUPPORTED  # d % 64 (pairs of groups)
     assert _fwd(lib, routed=_experts(d_ff=100)) == UNSUPPORTED    # I % 32
     assert _fwd(lib, routed=_experts(format=9)) == INVALID
+    assert _fwd(lib, routed=_experts(format=4)) == INVALID
+    assert _fwd(lib, T=0, routed=_experts(format=3)) == OK        # the per-row formats are valid
+    assert _fwd(lib, shared=_experts(n_experts=1, format=2)) == UNSUPPORTED   # shared format != routed
     assert _fwd(lib, routed=_experts(up_s=None)) == INVALID
     assert _fwd(lib, routed=_experts(gate_q=FAKE + 4)) == INVALID  # misaligned codes
     assert _fwd(lib, shared=_experts(n_experts=2)) == INVALID
@@ -142,8 +145,11 @@ def test_route_dispatch_combine_validation(lib):
     assert lib.moe_quantize_weights(FAKE, 40, 64, 40, 0, FAKE, FAKE, None) == UNSUPPORTED   # matrix rows % 32
     assert lib.moe_quantize_weights(FAKE, 96, 64, 64, 0, FAKE, FAKE, None) == INVALID       # not whole matrices
     assert lib.moe_quantize_weights(FAKE, 64, 64, 0, 0, FAKE, FAKE, None) == INVALID
-    assert lib.moe_quantize_weights(FAKE, 32, 64, 32, 3, FAKE, FAKE, None) == INVALID
+    assert lib.moe_quantize_weights(FAKE, 32, 64, 32, 4, FAKE, FAKE, None) == INVALID      # unknown format
+    assert lib.moe_quantize_weights(FAKE, 32, 64, 32, -1, FAKE, FAKE, None) == INVALID
+    assert lib.moe_quantize_weights(FAKE, 40, 64, 40, 3, FAKE, FAKE, None) == UNSUPPORTED  # per-row: same layout
     assert lib.moe_quantize_weights(FAKE, 0, 64, 32, 1, FAKE, FAKE, None) == OK
+    assert lib.moe_quantize_weights(FAKE, 0, 64, 32, 3, FAKE, FAKE, None) == OK
     assert lib.moe_quantize_q8_0(FAKE, 4, 40, FAKE, FAKE, None) == UNSUPPORTED
     e = _experts()
     assert lib.moe_expert_ffn(FAKE, 4, 9, ctypes.byref(e), FAKE, FAKE, FAKE, 0, FAKE, FAKE, 1 << 30, None) == INVALID
@@ -161,6 +167,9 @@ def test_accounting_matches_page_figures():
     assert abs(payload / 1e6 - 19) < 0.5
     assert acc.expert_bytes(*glm, "int4") == payload + 3 * glm[0] * glm[1] // 32 * 4
     assert acc.useful_ops([2, 0, 1], 3, 64, 128, False) == 2 * 3 * 3 * 64 * 128
+    # per-row scales: one float per matrix row
+    assert acc.expert_bytes(*glm, "int4_row") == payload + (2 * glm[1] + glm[0]) * 4
+    assert acc.expert_bytes(*glm, "int8_row") == 2 * payload + (2 * glm[1] + glm[0]) * 4
 
 
 @pytest.mark.parametrize("fmt", ["int8", "int4"])

@@ -31,22 +31,28 @@ TOPP_EPS = 1e-5        # top-p mass this close (relative) to the threshold may d
 # ---------------------------------------------------------------------------
 # quantisers
 # ---------------------------------------------------------------------------
-@pytest.mark.parametrize("fmt", ["int8", "int4"])
+@pytest.mark.parametrize("fmt", ["int8", "int4", "int8_row", "int4_row"])
 def test_quantize_weights_bit_exact(fmt):
+    """A stack of two 64 x 192 matrices, with rows scaled over eight decades,
+    an all-zero group and row, and a group of tiny values."""
     need_gpu()
     rng = np.random.default_rng(21)
-    w = (rng.standard_normal((64, 192)) * rng.uniform(1e-4, 3, (64, 1))).astype(np.float32)
-    w[3, 32:64] = 0.0
-    w[4, :32] = 1e-30
-    bits = 8 if fmt == "int8" else 4
-    q_ref, s_ref = oquant.quantize_weights(w, bits)
-    stored = q_ref if bits == 8 else oquant.pack_int4(q_ref)
-    q = torch.empty(stored.shape, dtype=torch.int8 if bits == 8 else torch.uint8, device="cuda")
-    s = torch.empty(s_ref.shape, dtype=torch.float32, device="cuda")
+    w = (rng.standard_normal((2, 64, 192)) * rng.uniform(1e-4, 3, (2, 64, 1))).astype(np.float32)
+    w[0, 3, 32:64] = 0.0
+    w[0, 4, :32] = 1e-30
+    w[1, 5, :] = 0.0
+    bits = 8 if fmt.startswith("int8") else 4
+    per_row = fmt.endswith("_row")
+    qz = oquant.quantize_rows if per_row else oquant.quantize_weights
+    refs = [qz(w[m], bits) for m in range(2)]
+    stored = [q if bits == 8 else oquant.pack_int4(q) for q, _ in refs]
+    q = torch.empty((2,) + stored[0].shape, dtype=torch.int8 if bits == 8 else torch.uint8, device="cuda")
+    s = torch.empty((2,) + refs[0][1].shape, dtype=torch.float32, device="cuda")
     qe.moe_quantize_weights(torch.from_numpy(w).cuda(), qe.FORMATS[fmt], q, s)
     torch.cuda.synchronize()
-    assert np.array_equal(untile_scales(t2n(s), 64, 192), s_ref)
-    assert np.array_equal(untile_codes(t2n(q), 64, 192, fmt), stored)
+    for m in range(2):
+        assert np.array_equal(untile_scales(t2n(s[m]), 64, 192, fmt), refs[m][1])
+        assert np.array_equal(untile_codes(t2n(q[m]), 64, 192, fmt), stored[m])
 
 
 def test_quantize_q8_0_bit_exact(golden_dir):
@@ -283,6 +289,9 @@ TINY_VARIANTS = {
     "tiny_topp": dict(n_experts=16, top_k=6, renormalize=False, top_p=0.6),
     "tiny_noaux_topp": dict(router="noaux_tc", n_experts=16, n_group=4, topk_group=2, top_k=4, has_bias=True,
                             routed_scaling_factor=2.5, shared_expert=True, top_p=0.7),
+    # per-row scales; the wide one has odd group-pair counts on both axes
+    "tiny_int8_row": dict(wformat="int8_row", shared_expert=True),
+    "tiny_int4_row_wide": dict(wformat="int4_row", d_model=192, d_ff=320, n_experts=6, top_k=3),
 }
 
 
@@ -365,7 +374,7 @@ def test_expert_ffn_and_combine_pieces(act_mode):
     assert_close_rel(t2n(out), ref["out"], what="out")
 
 
-@pytest.mark.parametrize("variant", ["tiny", "tiny_int4", "tiny_wide"])
+@pytest.mark.parametrize("variant", ["tiny", "tiny_int4", "tiny_wide", "tiny_int4_row_wide"])
 def test_q8_group_dots_bit_exact(variant):
     """The production int8-MFMA kernels' exact int32 group dots, Q8_0(H) codes
     and the down projection's dots fed the GPU's own H codes."""
@@ -417,7 +426,8 @@ SAMPLE = 48
 
 
 @pytest.mark.parametrize("wname", ["olmoe_b1", "olmoe_b16", "glm_b1", "glm_verify4", "olmoe_int4_prefill",
-                                   "qwen_prefill", "glm_b1_topp", "olmoe_b16_topp"])
+                                   "qwen_prefill", "glm_b1_topp", "olmoe_b16_topp", "olmoe_b16_int4_row",
+                                   "olmoe_int4_row_prefill"])
 def test_layer_full_size(wname):
     need_gpu()
     wl = synth.workload(wname)
@@ -444,7 +454,8 @@ def test_layer_full_size(wname):
                               ox.stored("gate"))
         assert np.array_equal(untile_codes(t2n(dl.routed[0].down_q[e]), shape.d_model, shape.d_ff, shape.wformat),
                               ox.stored("down"))
-        assert np.array_equal(untile_scales(t2n(dl.routed[0].down_s[e]), shape.d_model, shape.d_ff), ox.down_s)
+        assert np.array_equal(untile_scales(t2n(dl.routed[0].down_s[e]), shape.d_model, shape.d_ff, shape.wformat),
+                              ox.down_s)
 
 
 @pytest.mark.parametrize("act_mode", ["f32", "q8_0"])
