@@ -90,7 +90,7 @@ def cpu_baseline(wl, target_s: float):
     spec = olayer.RouterSpec(mode=shape.router, top_k=shape.top_k, renormalize=shape.renormalize,
                              n_group=shape.n_group, topk_group=shape.topk_group,
                              routed_scaling_factor=shape.routed_scaling_factor, bias=synth.score_bias(shape),
-                             top_p=wl.top_p or shape.top_p)
+                             top_p=wl.top_p or shape.top_p, shared_gate=synth.shared_gate_weight(shape))
     wg = synth.gate_weight(shape)
     shared = expert(shape.n_experts) if shape.shared_expert else None
     # sample: the whole batch for decode; a prefix of tokens for prefill

@@ -9,8 +9,16 @@ route -> dispatch -> each distinct expert applied once to all of its rows
 
 where Y holds the un-weighted expert outputs in permuted order and S is the
 shared expert ("Show HN: Getting GLM-5.2 running on my slow computer": shared expert), an FFN of the same format
-applied to every token with weight 1 (no gate on the shared expert: the pages
-name none).
+applied to every token with weight 1: the pages name no gate on it.
+
+Gated shared expert (an option, off by default): some model families scale
+the shared expert's output per token by a learned scalar gate, the sigmoid of
+one more linear projection of the hidden state. With that vector u [d]:
+
+    S[t] = sigmoid(x[t] . u) * FFN_shared(x[t])
+
+The pages do not describe it; this is the plain form of the option, taken in
+fp64 on the layer's input rows (the same rows the router sees).
 """
 from __future__ import annotations
 
@@ -33,6 +41,7 @@ class RouterSpec:
     routed_scaling_factor: float = 1.0
     bias: Optional[np.ndarray] = None
     top_p: float = 0.0           # adaptive expert top-p; 0 (or >= 1) keeps all k
+    shared_gate: Optional[np.ndarray] = None   # [d]: gate the shared expert by sigmoid(x . u)
 
 
 def rmsnorm(x, gamma, eps: float):
@@ -67,6 +76,12 @@ def expert_rows(x, ex: ffn.QuantExpert, act_mode: str):
     raise ValueError(f"unknown act_mode {act_mode}")
 
 
+def shared_gate_values(x, u) -> np.ndarray:
+    """sigmoid(x[t] . u) per row, fp64 [T]."""
+    z = np.asarray(x, np.float64) @ np.asarray(u, np.float64)
+    return 1.0 / (1.0 + np.exp(-z))
+
+
 def combine(y_perm, w, inv_perm, shared_y=None):
     t, k = w.shape
     inv = np.asarray(inv_perm).reshape(t, k)
@@ -94,9 +109,13 @@ def layer_forward(x, wg, spec: RouterSpec, get_expert: Callable[[int], ffn.Quant
         tokens = perm[lo:hi] // k
         y_perm[lo:hi] = expert_rows(x[tokens], get_expert(int(e)), act_mode)
     shared_y = expert_rows(x, shared, act_mode) if shared is not None else None
+    gate = None
+    if shared_y is not None and spec.shared_gate is not None:
+        gate = shared_gate_values(x, spec.shared_gate)
+        shared_y = gate[:, None] * shared_y
     out = combine(y_perm, w, inv, shared_y)
     return dict(idx=idx, w=w, logits=l, counts=counts, offsets=offsets, perm=perm,
-                inv_perm=inv, y_perm=y_perm, shared_y=shared_y, out=out)
+                inv_perm=inv, y_perm=y_perm, shared_y=shared_y, shared_gate=gate, out=out)
 
 
 def block_forward(x, gamma, eps: float, wg, spec: RouterSpec, get_expert: Callable[[int], ffn.QuantExpert],

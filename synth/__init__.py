@@ -35,6 +35,7 @@ TAG_BIAS = 3
 TAG_ZIPF_RANK = 4
 TAG_NORM_W = 5
 TAG_RESID = 6
+TAG_SHARED_GATE = 7
 TAG_W_GATE = 10
 TAG_W_UP = 11
 TAG_W_DOWN = 12
@@ -59,6 +60,7 @@ class LayerShape:
     routed_scaling_factor: float = 1.0
     has_bias: bool = False
     shared_expert: bool = False
+    shared_gate: bool = False   # shared expert scaled by sigmoid(x . u) per token
     wformat: str = "int8"       # "int8" | "int4" (group 32, fp32 scales) | "int8_row" | "int4_row" (per row)
     zipf_s: float = 0.0         # > 0: Zipf(s) log-prior on the router logits
     top_p: float = 0.0          # adaptive expert top-p (0: keep all k)
@@ -169,6 +171,14 @@ def gate_weight(layer: LayerShape) -> np.ndarray:
         ranks = zipf_ranks(layer).astype(np.float64)
         wg[:, -1] = (-layer.zipf_s * np.log(ranks)).astype(np.float32)
     return wg
+
+
+def shared_gate_weight(layer: LayerShape) -> Optional[np.ndarray]:
+    """The shared expert's gate vector u [d] fp32 ~ N(0, 0.02), or None
+    (ungated, or no shared expert)."""
+    if not (layer.shared_expert and layer.shared_gate):
+        return None
+    return _normal(layer.seed, TAG_SHARED_GATE, 0, (layer.d_model,), WEIGHT_STD)
 
 
 def score_bias(layer: LayerShape) -> Optional[np.ndarray]:

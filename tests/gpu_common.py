@@ -46,7 +46,8 @@ def router_spec(shape, top_p=None) -> olayer.RouterSpec:
     return olayer.RouterSpec(mode=shape.router, top_k=shape.top_k, renormalize=shape.renormalize,
                              n_group=shape.n_group, topk_group=shape.topk_group,
                              routed_scaling_factor=shape.routed_scaling_factor, bias=synth.score_bias(shape),
-                             top_p=shape.top_p if top_p is None else top_p)
+                             top_p=shape.top_p if top_p is None else top_p,
+                             shared_gate=synth.shared_gate_weight(shape))
 
 
 def assert_close_rel(gpu: np.ndarray, ref: np.ndarray, tol: float = REL_TOL, what: str = "output"):

@@ -120,6 +120,38 @@ def test_shared_expert_adds_with_weight_one():
     assert np.allclose(withs["out"] - base["out"], s, rtol=1e-12, atol=1e-15)
 
 
+@pytest.mark.parametrize("act_mode", ["f32", "q8_0"])
+def test_gated_shared_expert_closed_forms(act_mode):
+    """A zero gate vector halves the shared expert (sigmoid(0) = 1/2); a gate
+    vector along token 0's hidden state gives that token sigmoid(alpha)."""
+    lay = synth.variant(synth.LAYERS["tiny"], shared_expert=True)
+    x = synth.activations(lay, 5)
+    wg = synth.gate_weight(lay)
+    exps = _tiny_experts(lay)
+    sh = exps[lay.n_experts]
+    routed = layer.layer_forward(x, wg, _spec(lay), lambda e: exps[e], None, act_mode)["out"]
+    full = layer.layer_forward(x, wg, _spec(lay), lambda e: exps[e], sh, act_mode)["out"]
+    s = full - routed
+    half = layer.layer_forward(x, wg, _spec(lay, shared_gate=np.zeros(lay.d_model)), lambda e: exps[e], sh,
+                               act_mode)
+    assert np.allclose(half["out"] - routed, 0.5 * s, rtol=1e-12, atol=1e-15)
+    assert np.all(half["shared_gate"] == 0.5)
+    alpha = 1.7
+    x0 = x[0].astype(np.float64)
+    u = alpha * x0 / (x0 @ x0)
+    r = layer.layer_forward(x, wg, _spec(lay, shared_gate=u), lambda e: exps[e], sh, act_mode)
+    g0 = 1.0 / (1.0 + math.exp(-alpha))
+    assert abs(r["shared_gate"][0] - g0) < 1e-12
+    assert np.allclose(r["out"][0] - routed[0], g0 * s[0], rtol=1e-10, atol=1e-15)
+    # the gate is per token: x[t] . u for the other rows too, and never enters the routing
+    z = x.astype(np.float64) @ u
+    assert np.allclose(r["shared_gate"], 1.0 / (1.0 + np.exp(-z)), rtol=1e-14)
+    assert np.array_equal(r["idx"], half["idx"])
+    # without a shared expert the gate is ignored
+    assert np.array_equal(layer.layer_forward(x, wg, _spec(lay, shared_gate=u), lambda e: exps[e], None,
+                                              act_mode)["out"], routed)
+
+
 def test_group_dots_brute_force_python_ints():
     rng = np.random.default_rng(4)
     a = rng.integers(-127, 128, size=(3, 64)).astype(np.int8)
