@@ -275,7 +275,7 @@ def main():
         "data": "synthetic (seeded N(0,1) activations, N(0,0.02) weights quantised on the GPU)",
         "config": {"workload": wl.name, "tokens": T, "d_model": d, "n_experts": shape.n_experts, "d_ff": I,
                    "top_k": shape.top_k, "router": shape.router, "weights": (f"{fmt[:4]} per-row scales" if fmt.endswith("_row") else f"{fmt} group 32"),
-                   "act_mode": wl.act_mode, "shared_expert": shape.shared_expert,
+                   "act_mode": wl.act_mode, "shared_expert": shape.shared_expert, "shared_gate": shape.shared_gate,
                    "distinct_experts": int((counts_h > 0).sum()), "routed_rows": int(counts_h.sum()),
                    "top_p": wl.top_p or shape.top_p, "block": wl.block, "device_copies": copies},
         "roofline": roof,

@@ -133,6 +133,14 @@ typedef enum {
  *               last ones). 0, or any value >= 1, keeps all k slots; a
  *               negative or NaN value is MOE_ERR_INVALID_ARG. The keep
  *               decisions are taken in fp32.
+ *   shared_gate device fp32 [d], or NULL: gates the shared expert. When a
+ *               shared expert is passed to moe_layer_forward(_timed) or
+ *               moe_block_forward, its output for token t is multiplied by
+ *               sigmoid(x[t] . shared_gate), x[t] being the layer's input row
+ *               (after the RMSNorm of moe_block_forward), the dot taken in
+ *               fp32. The pages name no such gate; it is an option for model
+ *               families that have one (off when NULL). Ignored without a
+ *               shared expert, and by moe_route.
  */
 typedef struct {
     int32_t n_experts;
@@ -144,6 +152,7 @@ typedef struct {
     float routed_scaling_factor;
     const float* score_bias;
     float top_p;
+    const float* shared_gate;
 } moe_router_params;
 
 /* A stack of n_experts quantised SwiGLU experts (device pointers), each
@@ -263,6 +272,8 @@ moe_status moe_expert_ffn(const float* x, int32_t T, int32_t k, const moe_expert
  *   y_perm device fp32 [T*k, d]; topk_w device fp32 [T, k];
  *   inv_perm device int32 [T*k]; shared_y device fp32 [T, d] or NULL;
  *   out device fp32 [T, d].
+ * A gated shared expert is the caller's to scale here: pass shared_y
+ * already multiplied by its gate.
  */
 moe_status moe_combine(const float* y_perm, const float* topk_w, const int32_t* inv_perm,
                        const float* shared_y, int32_t T, int32_t k, int32_t d, float* out,

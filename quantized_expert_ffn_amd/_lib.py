@@ -49,7 +49,7 @@ class RouterParams(ctypes.Structure):
     _fields_ = [("n_experts", ctypes.c_int32), ("top_k", ctypes.c_int32), ("mode", ctypes.c_int32),
                 ("renormalize", ctypes.c_int32), ("n_group", ctypes.c_int32), ("topk_group", ctypes.c_int32),
                 ("routed_scaling_factor", ctypes.c_float), ("score_bias", ctypes.c_void_p),
-                ("top_p", ctypes.c_float)]
+                ("top_p", ctypes.c_float), ("shared_gate", ctypes.c_void_p)]
 
 
 class Experts(ctypes.Structure):
@@ -141,7 +141,10 @@ def _stream(stream) -> Optional[int]:
 
 def router_params(n_experts: int, top_k: int, mode: str = "softmax", renormalize: bool = False,
                   n_group: int = 1, topk_group: int = 1, routed_scaling_factor: float = 1.0,
-                  score_bias: Optional[torch.Tensor] = None, top_p: float = 0.0) -> RouterParams:
+                  score_bias: Optional[torch.Tensor] = None, top_p: float = 0.0,
+                  shared_gate: Optional[torch.Tensor] = None) -> RouterParams:
+    """shared_gate: [d] fp32 device vector gating the shared expert by
+    sigmoid(x . shared_gate), or None."""
     p = RouterParams()
     p.n_experts = n_experts
     p.top_k = top_k
@@ -152,7 +155,8 @@ def router_params(n_experts: int, top_k: int, mode: str = "softmax", renormalize
     p.routed_scaling_factor = routed_scaling_factor
     p.score_bias = _ptr(score_bias, torch.float32, "score_bias")
     p.top_p = top_p
-    p._keep = score_bias      # keep the bias tensor alive with the struct
+    p.shared_gate = _ptr(shared_gate, torch.float32, "shared_gate")
+    p._keep = (score_bias, shared_gate)   # keep the tensors alive with the struct
     return p
 
 

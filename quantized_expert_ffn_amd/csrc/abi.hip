@@ -251,6 +251,8 @@ moe_status layer_forward_impl(const float* x, int32_t T, const float* gate_w, co
         MOE_REQUIRE(shared->d_model == routed->d_model && shared->d_ff == routed->d_ff &&
                         shared->format == routed->format,
                     MOE_ERR_UNSUPPORTED, "shared expert must match the routed d_model, d_ff and format");
+        MOE_REQUIRE(p->shared_gate == nullptr || aligned16(p->shared_gate), MOE_ERR_INVALID_ARG,
+                    "shared_gate must be 16-byte aligned");
     }
     MOE_REQUIRE(T >= 0, MOE_ERR_INVALID_ARG, "T = %d < 0", T);
     if (T == 0) return ok();
@@ -287,7 +289,11 @@ moe_status layer_forward_impl(const float* x, int32_t T, const float* gate_w, co
         MOE_HIP(moe::launch_rmsnorm(x, T, d, norm_w, eps, xn, st), "RMSNorm");
         xl = xn;
     }
-    MOE_HIP(moe::launch_router_logits(xl, T, d, gate_w, E, logits, xp, (norm && small) ? norm_w : nullptr, eps, st),
+    // the shared expert's gate logit rides along as one more router row
+    const float* sg = has_shared ? p->shared_gate : nullptr;
+    float* sgl = sg ? ws_at<float>(ws, L.sgl) : nullptr;
+    MOE_HIP(moe::launch_router_logits(xl, T, d, gate_w, E, logits, xp, (norm && small) ? norm_w : nullptr, eps, sg,
+                                      sgl, st),
             "router logits");
     if (!fused) MOE_HIP(moe::launch_router_topk(logits, T, d, *p, idx, w, st), "router top-k");
     record(ev, 2 * MOE_STAGE_ROUTE + 1, st);
@@ -314,8 +320,9 @@ moe_status layer_forward_impl(const float* x, int32_t T, const float* gate_w, co
                          st)) != MOE_OK)
         return s;
     record(ev, 2 * MOE_STAGE_COMBINE, st);
-    MOE_HIP(moe::launch_combine(y, w, inv_perm, has_shared ? y + (size_t)T * k * d : nullptr, block ? x : nullptr, T, k,
-                                d, out, st),
+    const int S = moe::router_splits(T, E, d);
+    MOE_HIP(moe::launch_combine(y, w, inv_perm, has_shared ? y + (size_t)T * k * d : nullptr, sgl, S > 0 ? S : 1,
+                                block ? x : nullptr, T, k, d, out, st),
             "combine");
     record(ev, 2 * MOE_STAGE_COMBINE + 1, st);
     return ok();
@@ -417,7 +424,8 @@ moe_status moe_combine(const float* y_perm, const float* topk_w, const int32_t* 
     MOE_REQUIRE(y_perm && topk_w && inv_perm && out, MOE_ERR_INVALID_ARG, "NULL tensor argument");
     MOE_REQUIRE(aligned16(y_perm) && aligned16(out) && (shared_y == nullptr || aligned16(shared_y)),
                 MOE_ERR_INVALID_ARG, "y_perm, shared_y and out must be 16-byte aligned");
-    MOE_HIP(moe::launch_combine(y_perm, topk_w, inv_perm, shared_y, nullptr, T, k, d, out, stream), "combine");
+    MOE_HIP(moe::launch_combine(y_perm, topk_w, inv_perm, shared_y, nullptr, 0, nullptr, T, k, d, out, stream),
+            "combine");
     return ok();
 }
 

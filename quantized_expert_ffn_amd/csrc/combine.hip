@@ -1,6 +1,8 @@
-// Combine: out[t] = sum_j w[t, j] * Y[inv_perm[t*k + j]] + S[t], over the
-// dispatched slots (inv_perm >= 0; a slot dropped by top-p adds nothing),
+// Combine: out[t] = sum_j w[t, j] * Y[inv_perm[t*k + j]] + g[t] * S[t], over
+// the dispatched slots (inv_perm >= 0; a slot dropped by top-p adds nothing),
 // plus the block's residual when the layer runs between its neighbours.
+// g[t] = 1, or for a gated shared expert sigmoid of the gate logit, whose
+// slice sums the router left in sgl [slices, T] (added here in slice order).
 //
 // The weighted sum of a token's k expert outputs plus the shared expert
 // ("Show HN: Getting GLM-5.2 running on my slow computer", section "What's implemented": shared expert). Each
@@ -16,6 +18,7 @@ namespace moe {
 __global__ __launch_bounds__(64) void combine_kernel(const float* __restrict__ y, const float* __restrict__ w,
                                                      const int* __restrict__ inv_perm,
                                                      const float* __restrict__ shared_y,
+                                                     const float* __restrict__ sgl, int sgl_slices,
                                                      const float* __restrict__ residual, int T, int k, int d,
                                                      float* __restrict__ out) {
     const int t = blockIdx.y;
@@ -34,10 +37,20 @@ __global__ __launch_bounds__(64) void combine_kernel(const float* __restrict__ y
     }
     if (shared_y) {
         const float4 s = reinterpret_cast<const float4*>(shared_y + (size_t)t * d)[c];
-        acc.x += s.x;
-        acc.y += s.y;
-        acc.z += s.z;
-        acc.w += s.w;
+        if (sgl) {
+            float z = 0.0f;
+            for (int i = 0; i < sgl_slices; ++i) z += sgl[(size_t)i * T + t];
+            const float g = 1.0f / (1.0f + __expf(-z));
+            acc.x = fmaf(g, s.x, acc.x);
+            acc.y = fmaf(g, s.y, acc.y);
+            acc.z = fmaf(g, s.z, acc.z);
+            acc.w = fmaf(g, s.w, acc.w);
+        } else {
+            acc.x += s.x;
+            acc.y += s.y;
+            acc.z += s.z;
+            acc.w += s.w;
+        }
     }
     if (residual) {
         // read before the store of the same element: out may alias residual
@@ -51,10 +64,12 @@ __global__ __launch_bounds__(64) void combine_kernel(const float* __restrict__ y
 }
 
 hipError_t launch_combine(const float* y, const float* w, const int* inv_perm, const float* shared_y,
-                          const float* residual, int T, int k, int d, float* out, hipStream_t st) {
+                          const float* sgl, int sgl_slices, const float* residual, int T, int k, int d, float* out,
+                          hipStream_t st) {
     if (T == 0) return hipSuccess;
     const dim3 grid((d / 4 + 63) / 64, T);
-    hipLaunchKernelGGL(combine_kernel, grid, dim3(64), 0, st, y, w, inv_perm, shared_y, residual, T, k, d, out);
+    hipLaunchKernelGGL(combine_kernel, grid, dim3(64), 0, st, y, w, inv_perm, shared_y, sgl, sgl_slices, residual, T,
+                       k, d, out);
     return hipGetLastError();
 }
 

@@ -38,6 +38,7 @@ struct WsLayout {
     size_t hp = 0;         //                      F32: f32 powers of two [R, I/32]
     size_t y = 0;          // f32  [R, d]
     size_t xn = 0;         // f32  [T, d]  RMSNorm(x) for the block entry point, T > 16 only
+    size_t sgl = 0;        // f32  [max(S, 1), T]  shared-expert gate logits per d slice (with a shared expert)
     size_t total = 0;
     int max_tiles = 0;
 };
@@ -93,6 +94,7 @@ inline WsLayout ws_layout(int T, int k, int E, int d, int I, int act_mode, int h
     }
     L.y = take(R * d * 4);
     if (S > 0) L.xn = take((size_t)T * d * 4);
+    if (has_shared) L.sgl = take((size_t)(S > 0 ? S : 1) * T * 4);
     L.total = off;
     return L;
 }

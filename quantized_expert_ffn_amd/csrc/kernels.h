@@ -32,8 +32,11 @@ hipError_t launch_router(const float* x, int T, int d, const float* wg, const mo
 // With router_splits(T, E, d) == 0 (small T) the logits kernel also does xp;
 // otherwise xp is ignored and the caller runs launch_xprep. norm_w (small T
 // only, else null): the logits and xp see RMSNorm(x) with gain norm_w and eps.
+// sg (or null): the shared-expert gate vector, whose logit x . sg goes to sgl
+// as max(S, 1) slice sums [S, T] (S = router_splits).
 hipError_t launch_router_logits(const float* x, int T, int d, const float* wg, int E, float* logits,
-                                const XPrep& xp, const float* norm_w, float eps, hipStream_t st);
+                                const XPrep& xp, const float* norm_w, float eps, const float* sg, float* sgl,
+                                hipStream_t st);
 // RMSNorm of T rows into xn [T, d] (the larger-T path)
 hipError_t launch_rmsnorm(const float* x, int T, int d, const float* norm_w, float eps, float* xn, hipStream_t st);
 hipError_t launch_router_topk(const float* logits, int T, int d, const moe_router_params& p, int* idx, float* w,
@@ -82,6 +85,7 @@ hipError_t launch_q8_mfma(const moe_experts& routed, const moe_experts* shared, 
 
 // residual: [T, d] added last, or null
 hipError_t launch_combine(const float* y, const float* w, const int* inv_perm, const float* shared_y,
-                          const float* residual, int T, int k, int d, float* out, hipStream_t st);
+                          const float* sgl, int sgl_slices, const float* residual, int T, int k, int d, float* out,
+                          hipStream_t st);
 
 }  // namespace moe

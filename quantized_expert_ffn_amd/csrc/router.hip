@@ -131,13 +131,16 @@ __global__ __launch_bounds__(256) void xprep_kernel(const float* __restrict__ x,
 // Logits, small T (decode): one block per expert; the 256 threads split d,
 // each keeps T partial sums, then a wave reduction and a fixed-order sum of
 // the four wave partials. The block's waves then take their share of the
-// hidden-state preparation.
+// hidden-state preparation. With a shared-expert gate vector sg, block E
+// computes x . sg the same way into sgl [T].
 // ---------------------------------------------------------------------------
 template <int TB>
 __global__ __launch_bounds__(256) void router_logits_gemv_kernel(const float* __restrict__ x,
                                                                  const float* __restrict__ wg, int T, int d,
                                                                  int E, float* __restrict__ L, XPrep xp,
-                                                                 const float* __restrict__ gamma, float eps) {
+                                                                 const float* __restrict__ gamma, float eps,
+                                                                 const float* __restrict__ sg,
+                                                                 float* __restrict__ sgl) {
     __shared__ float part[4][TB];
     __shared__ float sq[4][TB];
     __shared__ float inv_rms[TB];
@@ -146,7 +149,7 @@ __global__ __launch_bounds__(256) void router_logits_gemv_kernel(const float* __
     float acc[TB], ss[TB];
 #pragma unroll
     for (int t = 0; t < TB; ++t) acc[t] = ss[t] = 0.0f;
-    const float4* wr = reinterpret_cast<const float4*>(wg + (size_t)e * d);
+    const float4* wr = reinterpret_cast<const float4*>(e < E ? wg + (size_t)e * d : sg);
     const int n4 = d >> 2;
     for (int i = threadIdx.x; i < n4; i += 256) {
         float4 w4 = wr[i];
@@ -192,7 +195,9 @@ __global__ __launch_bounds__(256) void router_logits_gemv_kernel(const float* __
     if (threadIdx.x < T) {
         const int t = threadIdx.x;
         const float l = (part[0][t] + part[1][t]) + (part[2][t] + part[3][t]);
-        L[(size_t)t * E + e] = gamma ? l * inv_rms[t] : l;
+        const float v = gamma ? l * inv_rms[t] : l;
+        if (e < E) L[(size_t)t * E + e] = v;
+        else sgl[t] = v;
     }
     if (gamma) {
         xp.gamma = gamma;
@@ -234,19 +239,24 @@ __global__ __launch_bounds__(256) void rmsnorm_kernel(const float* __restrict__ 
 // Each lane loads 4 consecutive k of its token row and its expert row; the
 // four MFMAs of a step each take one of them (the two lane halves cover
 // k..k+3 and k+4..k+7), so every (token, expert, k) product enters once.
+// A shared-expert gate vector sg is expert row E; its slice sums go to
+// sgl [S, T].
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void router_logits_mfma_kernel(const float* __restrict__ x,
                                                                  const float* __restrict__ wg, int T, int d,
-                                                                 int E, int kslice, float* __restrict__ L) {
+                                                                 int E, int kslice, float* __restrict__ L,
+                                                                 const float* __restrict__ sg,
+                                                                 float* __restrict__ sgl) {
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int t0 = blockIdx.y * 64 + (wave & 1) * 32;
     const int e0 = blockIdx.x * 64 + (wave >> 1) * 32;
     const int ks = blockIdx.z;
     const int kbeg = ks * kslice, kend = min(d, kbeg + kslice);
     const int row = lane & 31, h = lane >> 5;
-    const bool tok_ok = t0 + row < T, exp_ok = e0 + row < E;
+    const bool is_sg = sg != nullptr && e0 + row == E;
+    const bool tok_ok = t0 + row < T, exp_ok = e0 + row < E || is_sg;
     const float* xr = x + (size_t)(tok_ok ? t0 + row : 0) * d;
-    const float* wr = wg + (size_t)(exp_ok ? e0 + row : 0) * d;
+    const float* wr = is_sg ? sg : wg + (size_t)(exp_ok ? e0 + row : 0) * d;
     v16f acc = {};
     for (int k = kbeg; k < kend; k += 8) {
         const int kk = k + 4 * h;
@@ -264,6 +274,7 @@ __global__ __launch_bounds__(256) void router_logits_mfma_kernel(const float* __
     for (int i = 0; i < 16; ++i) {
         const int t = t0 + 8 * (i >> 2) + 4 * h + (i & 3);
         if (t < T && e < E) out[(size_t)t * E + e] = acc[i];
+        if (t < T && is_sg) sgl[(size_t)ks * T + t] = acc[i];
     }
 }
 
@@ -305,14 +316,16 @@ TopkArgs topk_args(const float* logits, int T, int d, const moe_router_params& p
 }
 
 hipError_t launch_router_logits(const float* x, int T, int d, const float* wg, int E, float* logits,
-                                const XPrep& xp, const float* norm_w, float eps, hipStream_t st) {
+                                const XPrep& xp, const float* norm_w, float eps, const float* sg, float* sgl,
+                                hipStream_t st) {
     if (T == 0) return hipSuccess;
     const int S = router_splits(T, E, d);
+    const int rows = E + (sg ? 1 : 0);   // experts, then the shared-expert gate
     if (S == 0) {
-        const dim3 grid(E);
+        const dim3 grid(rows);
 #define MOE_RL(TB)                                                                                            \
     hipLaunchKernelGGL(router_logits_gemv_kernel<TB>, grid, dim3(256), 0, st, x, wg, T, d, E, logits, xp, norm_w, \
-                       eps)
+                       eps, sg, sgl)
         if (T == 1) MOE_RL(1);
         else if (T <= 2) MOE_RL(2);
         else if (T <= 4) MOE_RL(4);
@@ -323,8 +336,8 @@ hipError_t launch_router_logits(const float* x, int T, int d, const float* wg, i
     }
     // larger T: the preparation is the caller's own launch (launch_xprep)
     const int kslice = router_kslice(d, S);
-    const dim3 grid((E + 63) / 64, (T + 63) / 64, S);
-    hipLaunchKernelGGL(router_logits_mfma_kernel, grid, dim3(256), 0, st, x, wg, T, d, E, kslice, logits);
+    const dim3 grid((rows + 63) / 64, (T + 63) / 64, S);
+    hipLaunchKernelGGL(router_logits_mfma_kernel, grid, dim3(256), 0, st, x, wg, T, d, E, kslice, logits, sg, sgl);
     return hipGetLastError();
 }
 
@@ -361,7 +374,7 @@ hipError_t launch_router_topk(const float* logits, int T, int d, const moe_route
 
 hipError_t launch_router(const float* x, int T, int d, const float* wg, const moe_router_params& p,
                          float* logits, int* idx, float* w, hipStream_t st) {
-    hipError_t err = launch_router_logits(x, T, d, wg, p.n_experts, logits, XPrep{}, nullptr, 0.0f, st);
+    hipError_t err = launch_router_logits(x, T, d, wg, p.n_experts, logits, XPrep{}, nullptr, 0.0f, nullptr, nullptr, st);
     if (err != hipSuccess) return err;
     return launch_router_topk(logits, T, d, p, idx, w, st);
 }

@@ -21,6 +21,7 @@ class DeviceLayer:
     shape: synth.LayerShape
     gate_w: torch.Tensor                  # [E, d] fp32
     bias: Optional[torch.Tensor]          # [E] fp32 or None
+    shared_gate: Optional[torch.Tensor]   # [d] fp32 or None
     routed: List[_lib.QuantExperts]       # one or more copies of the routed stack
     shared: List[Optional[_lib.QuantExperts]]
     params: _lib.RouterParams
@@ -67,9 +68,11 @@ def build(shape: synth.LayerShape, device="cuda", copies: int = 1, chunk: Option
     gate_w = torch.from_numpy(synth.gate_weight(shape)).to(device)
     b = synth.score_bias(shape)
     bias = torch.from_numpy(b).to(device) if b is not None else None
+    u = synth.shared_gate_weight(shape)
+    sg = torch.from_numpy(u).to(device) if u is not None else None
     params = _lib.router_params(E, shape.top_k, shape.router, shape.renormalize, shape.n_group,
-                                shape.topk_group, shape.routed_scaling_factor, bias, shape.top_p)
-    return DeviceLayer(shape, gate_w, bias, routed_list, shared_list, params)
+                                shape.topk_group, shape.routed_scaling_factor, bias, shape.top_p, sg)
+    return DeviceLayer(shape, gate_w, bias, sg, routed_list, shared_list, params)
 
 
 def activations(shape: synth.LayerShape, tokens: int, device="cuda") -> torch.Tensor:

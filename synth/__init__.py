@@ -92,7 +92,7 @@ LAYERS = {
     "olmoe_int4_row": LayerShape("olmoe_int4_row", 1006, d_model=2048, n_experts=64, d_ff=1024,
                                  top_k=8, router="softmax", renormalize=False, wformat="int4_row"),
     "qwen": LayerShape("qwen", 1005, d_model=2048, n_experts=512, d_ff=512, top_k=10,
-                       router="softmax", renormalize=True, shared_expert=True,
+                       router="softmax", renormalize=True, shared_expert=True, shared_gate=True,
                        wformat="int4", zipf_s=1.1),
 }
 

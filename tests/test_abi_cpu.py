@@ -100,6 +100,7 @@ def test_layer_forward_validation(lib):
     assert _fwd(lib, routed=_experts(format=4)) == INVALID
     assert _fwd(lib, T=0, routed=_experts(format=3)) == OK        # the per-row formats are valid
     assert _fwd(lib, shared=_experts(n_experts=1, format=2)) == UNSUPPORTED   # shared format != routed
+    assert _fwd(lib, params=_params(shared_gate=FAKE + 4), shared=_experts(n_experts=1)) == INVALID  # misaligned
     assert _fwd(lib, routed=_experts(up_s=None)) == INVALID
     assert _fwd(lib, routed=_experts(gate_q=FAKE + 4)) == INVALID  # misaligned codes
     assert _fwd(lib, shared=_experts(n_experts=2)) == INVALID

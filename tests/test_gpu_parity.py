@@ -292,6 +292,8 @@ TINY_VARIANTS = {
     # per-row scales; the wide one has odd group-pair counts on both axes
     "tiny_int8_row": dict(wformat="int8_row", shared_expert=True),
     "tiny_int4_row_wide": dict(wformat="int4_row", d_model=192, d_ff=320, n_experts=6, top_k=3),
+    # a shared expert gated by sigmoid(x . u)
+    "tiny_gated": dict(shared_expert=True, shared_gate=True),
 }
 
 
@@ -508,7 +510,7 @@ def oracle_block(shape, x, act_mode, norm_w, eps, name=None):
 
 
 @pytest.mark.parametrize("act_mode", ["f32", "q8_0"])
-@pytest.mark.parametrize("variant", ["tiny", "tiny_shared_noaux", "tiny_int4", "tiny_topp"])
+@pytest.mark.parametrize("variant", ["tiny", "tiny_shared_noaux", "tiny_int4", "tiny_topp", "tiny_gated"])
 def test_block_forward_tiny(variant, act_mode):
     need_gpu()
     shape, dl = tiny_layer(variant)
