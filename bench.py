@@ -76,7 +76,7 @@ def cpu_baseline(wl, target_s: float):
     except Exception:           # threadpoolctl missing: numpy's own default
         ctl, cores = None, os.cpu_count() or 1
     shape = wl.layer
-    bits = 8 if shape.wformat.startswith("int8") else 4
+    bits = synth.weight_bits(shape)
     cache = {}
 
     def expert(e):
@@ -84,7 +84,7 @@ def cpu_baseline(wl, target_s: float):
             cache[e] = offn.QuantExpert.from_fp32(synth.expert_weight(shape, e, "gate"),
                                                   synth.expert_weight(shape, e, "up"),
                                                   synth.expert_weight(shape, e, "down"), bits,
-                                                  shape.wformat.endswith("_row"))
+                                                  synth.weight_per_row(shape))
         return cache[e]
 
     spec = olayer.RouterSpec(mode=shape.router, top_k=shape.top_k, renormalize=shape.renormalize,

@@ -34,7 +34,8 @@ from . import quant
 class QuantExpert:
     """One expert's quantised matrices as integer codes plus fp32 scales.
 
-    bits = 8: codes in [-127, 127]; bits = 4: codes in [-7, 7].
+    bits = 8: codes in [-127, 127]; bits = 4: codes in [-7, 7]; bits = 2:
+    codes in [-1, 1].
     gate_q, up_q [I, d]; down_q [d, I]; *_s the matching group scales, or one
     scale per row ([rows, 1]) when per_row.
     """
@@ -61,9 +62,8 @@ class QuantExpert:
                 quant.dequantize(self.down_q, self.down_s))
 
     def stored(self, which: str) -> np.ndarray:
-        """Bytes as the library stores them: int8 codes, or packed int4."""
-        q = getattr(self, which + "_q")
-        return q if self.bits == 8 else quant.pack_int4(q)
+        """Bytes as the library stores them: int8 codes, or packed int4 / int2."""
+        return quant.pack_codes(getattr(self, which + "_q"), self.bits)
 
 
 def silu(g: np.ndarray) -> np.ndarray:

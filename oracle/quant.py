@@ -9,7 +9,8 @@ quantisation, dequantised on use). Each row of a matrix is cut into groups of
 fp32 scale s and signed integer codes q with s*q approximating the weights:
 
     amax = max |w| over the group
-    s    = amax / qmax            (qmax = 127 for int8, 7 for int4; fp32 divide)
+    s    = amax / qmax            (qmax = 127 for int8, 7 for int4, 1 for int2;
+                                   fp32 divide)
     q    = clamp(rne(w / s), -qmax, qmax)   (fp32 divide, round half to even)
     amax == 0  ->  s = 0, q = 0
 
@@ -21,6 +22,12 @@ for bit.
 Packed int4 ("two nibbles per byte", symmetric): element 2i sits in the low
 nibble of byte i and element 2i+1 in the high nibble, each as a 4-bit two's
 complement number.
+
+Packed int2 (same section: "packed int2", next to int4 and validated against
+the int8 container): four 2-bit two's complement codes per byte, element
+4i + j in bits 2j, 2j+1 of byte i. Symmetric like the other widths, so
+qmax = 2^(bits-1) - 1 = 1: the codes are -1, 0 and 1 (the pattern of -2 is
+never produced by the quantiser, though unpacking reads it).
 
 Activations ("Show HN: Getting GLM-5.2 running on my slow computer", section "What's implemented": Q8_0-style int8
 activations). Each row is cut into groups of 32; a group keeps an fp32 scale d
@@ -47,6 +54,8 @@ def qmax_for_bits(bits: int) -> int:
         return 127
     if bits == 4:
         return 7
+    if bits == 2:
+        return 1
     raise ValueError(f"unsupported weight bits {bits}")
 
 
@@ -121,6 +130,40 @@ def unpack_int4(b: np.ndarray) -> np.ndarray:
     out[..., 0::2] = lo
     out[..., 1::2] = hi
     return out
+
+
+def pack_int2(q: np.ndarray) -> np.ndarray:
+    """Pack int2 codes (int8 array, values in [-2, 1]) four per byte."""
+    q = np.asarray(q)
+    if q.shape[-1] % 4:
+        raise ValueError("int2 packing needs a last dimension divisible by 4")
+    if q.min(initial=0) < -2 or q.max(initial=0) > 1:
+        raise ValueError("int2 code out of range")
+    u = q.astype(np.int16) & 0x3
+    out = u[..., 0::4] | (u[..., 1::4] << 2) | (u[..., 2::4] << 4) | (u[..., 3::4] << 6)
+    return out.astype(np.uint8)
+
+
+def unpack_int2(b: np.ndarray) -> np.ndarray:
+    """Inverse of pack_int2: bytes -> int8 codes (sign-extended 2-bit fields)."""
+    b = np.asarray(b, dtype=np.uint8).astype(np.int16)
+    out = np.empty(b.shape[:-1] + (b.shape[-1] * 4,), dtype=np.int8)
+    for j in range(4):
+        f = (b >> (2 * j)) & 0x3
+        out[..., j::4] = np.where(f >= 2, f - 4, f)
+    return out
+
+
+def pack_codes(q: np.ndarray, bits: int) -> np.ndarray:
+    """The stored bytes of int8 codes at a weight width: int8 as is, int4 and
+    int2 packed."""
+    if bits == 8:
+        return np.asarray(q, np.int8)
+    if bits == 4:
+        return pack_int4(q)
+    if bits == 2:
+        return pack_int2(q)
+    raise ValueError(f"unsupported weight bits {bits}")
 
 
 def quantize_q8_0(x: np.ndarray):

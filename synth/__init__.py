@@ -61,7 +61,7 @@ class LayerShape:
     has_bias: bool = False
     shared_expert: bool = False
     shared_gate: bool = False   # shared expert scaled by sigmoid(x . u) per token
-    wformat: str = "int8"       # "int8" | "int4" (group 32, fp32 scales) | "int8_row" | "int4_row" (per row)
+    wformat: str = "int8"       # "int8" | "int4" | "int2" (group 32, fp32 scales); "..._row": a scale per row
     zipf_s: float = 0.0         # > 0: Zipf(s) log-prior on the router logits
     top_p: float = 0.0          # adaptive expert top-p (0: keep all k)
 
@@ -116,6 +116,16 @@ WORKLOADS = {
     "olmoe_b16_block": Workload("olmoe_b16_block", LAYERS["olmoe"], 16, "f32", block=True),
     "olmoe_int4_prefill_block": Workload("olmoe_int4_prefill_block", LAYERS["olmoe_int4"], 2048, "q8_0", block=True),
 }
+
+
+def weight_bits(layer: LayerShape) -> int:
+    """Code width of the layer's weight format: 8, 4 or 2."""
+    return {"int8": 8, "int4": 4, "int2": 2}[layer.wformat.split("_")[0]]
+
+
+def weight_per_row(layer: LayerShape) -> bool:
+    """True for the per-row-scale formats ("..._row")."""
+    return layer.wformat.endswith("_row")
 
 
 def _rng(seed: int, tag: int, index: int = 0) -> np.random.Generator:

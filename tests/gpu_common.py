@@ -37,9 +37,9 @@ def device_layer(name: str):
 @functools.lru_cache(maxsize=2048)
 def oracle_expert(name: str, e: int) -> offn.QuantExpert:
     shape = synth.LAYERS[name] if isinstance(name, str) else name
-    bits = 8 if shape.wformat.startswith("int8") else 4
+    bits = synth.weight_bits(shape)
     return offn.QuantExpert.from_fp32(synth.expert_weight(shape, e, "gate"), synth.expert_weight(shape, e, "up"),
-                                      synth.expert_weight(shape, e, "down"), bits, shape.wformat.endswith("_row"))
+                                      synth.expert_weight(shape, e, "down"), bits, synth.weight_per_row(shape))
 
 
 def router_spec(shape, top_p=None) -> olayer.RouterSpec:

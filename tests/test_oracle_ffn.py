@@ -15,10 +15,10 @@ import synth
 
 
 def _tiny_experts(lay, bits=None):
-    bits = bits or (8 if lay.wformat.startswith("int8") else 4)
+    bits = bits or (synth.weight_bits(lay))
     return [ffn.QuantExpert.from_fp32(synth.expert_weight(lay, e, "gate"),
                                       synth.expert_weight(lay, e, "up"),
-                                      synth.expert_weight(lay, e, "down"), bits, lay.wformat.endswith("_row"))
+                                      synth.expert_weight(lay, e, "down"), bits, synth.weight_per_row(lay))
             for e in range(lay.n_experts + (1 if lay.shared_expert else 0))]
 
 
@@ -80,8 +80,9 @@ def test_dense_masked_equals_sparse_tiny(act_mode):
     assert np.allclose(r["out"], dense, rtol=0, atol=1e-12 * np.abs(dense).max())
 
 
-def test_single_expert_is_dense_swiglu():
-    lay = synth.variant(synth.LAYERS["tiny"], n_experts=1, top_k=1, renormalize=True)
+@pytest.mark.parametrize("wformat", ["int8", "int4", "int2", "int2_row"])
+def test_single_expert_is_dense_swiglu(wformat):
+    lay = synth.variant(synth.LAYERS["tiny"], n_experts=1, top_k=1, renormalize=True, wformat=wformat)
     x = synth.activations(lay, 16)
     wg = synth.gate_weight(lay)
     exps = _tiny_experts(lay)

@@ -26,13 +26,13 @@ def test_int8_g32_error_within_page_bound(golden_dir):
     assert err <= 0.5 * s.max() * (1 + 1e-5)
 
 
-@pytest.mark.parametrize("bits", [8, 4])
+@pytest.mark.parametrize("bits", [8, 4, 2])
 def test_round_trip_half_step_and_amax(bits):
     rng = np.random.default_rng(7)
     w = (rng.standard_normal((37, 96)) * rng.uniform(1e-4, 3, (37, 1))).astype(np.float32)
     w[3, 32:64] = 0.0                                   # an all-zero group
     q, s = quant.quantize_weights(w, bits)
-    qmax = 127 if bits == 8 else 7
+    qmax = {8: 127, 4: 7, 2: 1}[bits]
     assert q.dtype == np.int8 and s.dtype == np.float32
     assert q.min() >= -qmax and q.max() <= qmax
     deq = quant.dequantize(q, s)
@@ -52,13 +52,13 @@ def test_round_trip_half_step_and_amax(bits):
     assert s[3, 1] == 0 and np.all(q[3, 32:64] == 0)
 
 
-@pytest.mark.parametrize("bits", [8, 4])
+@pytest.mark.parametrize("bits", [8, 4, 2])
 def test_codes_are_nearest_integers_brute_force(bits):
     # brute force: for each element, no other code in range lands closer to w/s
     rng = np.random.default_rng(11)
     w = (rng.standard_normal((4, 64)) * 0.02).astype(np.float32)
     q, s = quant.quantize_weights(w, bits)
-    qmax = 127 if bits == 8 else 7
+    qmax = {8: 127, 4: 7, 2: 1}[bits]
     codes = np.arange(-qmax, qmax + 1)
     for r in range(4):
         for c in range(64):
@@ -103,6 +103,46 @@ def test_int4_unpack_equals_int8_container():
     w = (np.random.default_rng(3).standard_normal((16, 128)) * 0.02).astype(np.float32)
     q, _ = quant.quantize_weights(w, 4)
     assert np.array_equal(quant.unpack_int4(quant.pack_int4(q)), q)
+
+
+def test_int2_pack_matches_hand_worked_bytes(golden_dir):
+    for line in open(os.path.join(golden_dir, "int2_fields.txt")):
+        if line.startswith("#") or not line.strip():
+            continue
+        left, right = line.split("|")
+        codes = np.array([int(v) for v in left.split()], dtype=np.int8)
+        want = np.array([int(v, 16) for v in right.split()], dtype=np.uint8)
+        assert np.array_equal(quant.pack_int2(codes), want)
+        assert np.array_equal(quant.unpack_int2(want), codes)
+
+
+def test_int2_unpack_equals_int8_container():
+    # every byte value round-trips; quantised codes survive packing unchanged
+    allbytes = np.arange(256, dtype=np.uint8)
+    codes = quant.unpack_int2(allbytes)
+    assert codes.min() == -2 and codes.max() == 1
+    assert np.array_equal(quant.pack_int2(codes), allbytes)
+    w = (np.random.default_rng(3).standard_normal((16, 128)) * 0.02).astype(np.float32)
+    for qz in (quant.quantize_weights, quant.quantize_rows):
+        q, _ = qz(w, 2)
+        assert set(np.unique(q).tolist()) <= {-1, 0, 1}
+        assert np.array_equal(quant.unpack_int2(quant.pack_int2(q)), q)
+
+
+def test_int2_hand_worked():
+    # group [0.8, -0.8, 0.4, 0.41, -0.39, 0...]: s = amax / 1 = 0.8; 0.4 / 0.8 is
+    # exactly 1/2 in fp32 -> 0 (half to even); 0.41 -> 1; -0.39 -> -0
+    w = np.zeros((1, 32), np.float32)
+    w[0, :5] = [0.8, -0.8, 0.4, 0.41, -0.39]
+    q, s = quant.quantize_weights(w, 2)
+    assert s[0, 0] == np.float32(0.8)
+    assert q[0, :5].tolist() == [1, -1, 0, 1, 0] and np.all(q[0, 5:] == 0)
+    # the mean absolute error of ternary codes on a Gaussian group is far from
+    # zero but below half the scale
+    g = (np.random.default_rng(9).standard_normal((64, 32)) * 0.02).astype(np.float32)
+    qg, sg = quant.quantize_weights(g, 2)
+    err = np.abs(quant.dequantize(qg, sg) - g)
+    assert np.all(err <= 0.5 * np.repeat(sg, 32, axis=1) * (1 + 1e-6))
 
 
 def test_q8_0_hand_worked_rounding(golden_dir):
@@ -152,7 +192,7 @@ def test_page_byte_accounting(golden_dir):
 # ---------------------------------------------------------------------------
 # per-row scales (the GLM engine's kernels: one scale per row)
 # ---------------------------------------------------------------------------
-@pytest.mark.parametrize("bits", [8, 4])
+@pytest.mark.parametrize("bits", [8, 4, 2])
 def test_per_row_on_one_group_rows_equals_group_32(bits):
     # a row of exactly 32 values is one group: both quantisers must agree
     w = (np.random.default_rng(11).standard_normal((40, 32)) * 0.02).astype(np.float32)
@@ -161,13 +201,13 @@ def test_per_row_on_one_group_rows_equals_group_32(bits):
     assert np.array_equal(qr, qg) and np.array_equal(sr[:, 0], sg[:, 0])
 
 
-@pytest.mark.parametrize("bits", [8, 4])
+@pytest.mark.parametrize("bits", [8, 4, 2])
 def test_per_row_round_trip_and_amax(bits):
     rng = np.random.default_rng(12)
     w = (rng.standard_normal((33, 256)) * 0.02).astype(np.float32)
     w[5] = 0.0                                                   # an all-zero row: scale 0, codes 0
     q, s = quant.quantize_rows(w, bits)
-    qmax = 127 if bits == 8 else 7
+    qmax = {8: 127, 4: 7, 2: 1}[bits]
     assert s.shape == (33, 1) and s[5, 0] == 0 and np.all(q[5] == 0)
     err = np.abs(quant.dequantize(q, s) - w.astype(np.float64))
     assert np.all(err <= s.astype(np.float64) / 2 * (1 + 1e-6))  # nearest code
