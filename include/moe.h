@@ -34,13 +34,16 @@
  *   - Weight formats (symmetric): MOE_W_INT8_G32 stores int8 codes in
  *     [-127, 127]; MOE_W_INT4_G32 stores codes in [-7, 7] as 4-bit two's
  *     complement, eight to a little-endian dword, the lower k in the lower
- *     nibble. Both carry one fp32 scale per group of 32 along each matrix's
- *     input axis, and a group's weights are scale * code. MOE_W_INT8_ROW and
- *     MOE_W_INT4_ROW store the same codes in the same layout with one fp32
- *     scale per matrix row (output) instead ("Show HN: Getting GLM-5.2
- *     running on my slow computer", section "What's implemented": per-row
- *     scales), row n's weights being scale[n] * code; their scales are N
- *     floats per matrix in row order.
+ *     nibble; MOE_W_INT2_G32 stores codes in [-1, 1] as 2-bit two's
+ *     complement, eight to a little-endian 16-bit word, the lower k in the
+ *     lower bits. All carry one fp32 scale per group of 32 along each
+ *     matrix's input axis, and a group's weights are scale * code.
+ *     MOE_W_INT8_ROW, MOE_W_INT4_ROW and MOE_W_INT2_ROW store the same codes
+ *     in the same layout with one fp32 scale per matrix row (output) instead
+ *     ("Show HN: Getting GLM-5.2 running on my slow computer", section
+ *     "What's implemented": packed int2, per-row scales), row n's weights
+ *     being scale[n] * code; their scales are N floats per matrix in row
+ *     order. The int2 formats need K % 128 == 0.
  *   - Weight layout ("lane-tiled"; written by moe_quantize_weights, read by
  *     every expert kernel). A matrix of N rows (outputs) and K columns
  *     (inputs), N % 32 == 0, K % 64 == 0, is cut into NT = N/32 tiles of 32
@@ -52,6 +55,8 @@
  *                    (K*N bytes in all);
  *       int4 codes   dword ((g/2*NT + t)*64 + l)*4 + 2*(g % 2) + (r >= 16),
  *                    nibble k % 8 (K*N/2 bytes in all);
+ *       int2 codes   16-bit word ((g/4*NT + t)*64 + l)*8 + 2*(g % 4) + (r >= 16),
+ *                    bits 2*(k % 8), +1 (K*N/4 bytes in all);
  *       scales fp32  float (t*P + g/2)*64 + 4*nl + 2*(g % 2) + (r >= 16)
  *                    (K*N/32 floats in all; per-row formats: float n of
  *                    row n, N floats in all).
@@ -90,7 +95,9 @@ typedef enum {
     MOE_W_INT8_G32 = 0,   /* int8 codes, fp32 scale per group of 32 */
     MOE_W_INT4_G32 = 1,   /* packed int4 codes, fp32 scale per group of 32 */
     MOE_W_INT8_ROW = 2,   /* int8 codes, fp32 scale per matrix row */
-    MOE_W_INT4_ROW = 3    /* packed int4 codes, fp32 scale per matrix row */
+    MOE_W_INT4_ROW = 3,   /* packed int4 codes, fp32 scale per matrix row */
+    MOE_W_INT2_G32 = 4,   /* packed int2 codes, fp32 scale per group of 32 */
+    MOE_W_INT2_ROW = 5    /* packed int2 codes, fp32 scale per matrix row */
 } moe_weight_format;
 
 typedef enum {
@@ -157,12 +164,13 @@ typedef struct {
 
 /* A stack of n_experts quantised SwiGLU experts (device pointers), each
  * matrix in the lane-tiled layout above, experts back to back:
- *   gate_q, up_q : per expert an [I x d] matrix: I*d bytes (int8) or I*d/2 (int4)
+ *   gate_q, up_q : per expert an [I x d] matrix: I*d bytes (int8), I*d/2 (int4) or I*d/4 (int2)
  *   gate_s, up_s : per expert I*d/32 fp32 (per-row formats: I fp32)
- *   down_q       : per expert a [d x I] matrix: d*I bytes (int8) or d*I/2 (int4)
+ *   down_q       : per expert a [d x I] matrix: d*I bytes (int8), d*I/2 (int4) or d*I/4 (int2)
  *   down_s       : per expert d*I/32 fp32 (per-row formats: d fp32)
  * Expert e computes  y = (silu(x Wg^T) * (x Wu^T)) Wd^T  with W = scale*code.
- * d % 64 == 0 and I % 64 == 0 are required (MOE_ERR_UNSUPPORTED otherwise).
+ * d % 64 == 0 and I % 64 == 0 are required, d % 128 == 0 and I % 128 == 0
+ * for the int2 formats (MOE_ERR_UNSUPPORTED otherwise).
  */
 typedef struct {
     int32_t n_experts;
@@ -194,12 +202,14 @@ size_t moe_workspace_size(int32_t T, int32_t k, int32_t E, int32_t d, int32_t d_
  *          (matrix_rows % 32 == 0, rows % matrix_rows == 0), each written
  *          in the layout above, one after the other
  *   format MOE_W_INT8_G32 / MOE_W_INT8_ROW -> q holds rows*cols bytes;
- *          MOE_W_INT4_G32 / MOE_W_INT4_ROW -> q holds rows*cols/2 bytes
+ *          MOE_W_INT4_G32 / MOE_W_INT4_ROW -> q holds rows*cols/2 bytes;
+ *          MOE_W_INT2_G32 / MOE_W_INT2_ROW -> q holds rows*cols/4 bytes
+ *          (cols % 128 == 0)
  *   s      device fp32: rows*cols/32 floats (group formats) or rows floats
  *          (per-row formats, s[i] the scale of row i of w)
  *   q and s are written in the lane-tiled layout described at the top.
- * Per group (per row for the per-row formats): s = amax/qmax (qmax 127 or
- * 7, fp32 divide), code = clamp(round_half_even(w/s), -qmax, qmax) (fp32
+ * Per group (per row for the per-row formats): s = amax/qmax (qmax 127, 7
+ * or 1, fp32 divide), code = clamp(round_half_even(w/s), -qmax, qmax) (fp32
  * divide); amax == 0 gives s = 0 and codes 0.
  */
 moe_status moe_quantize_weights(const float* w, int64_t rows, int32_t cols, int32_t matrix_rows,

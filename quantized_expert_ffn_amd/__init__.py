@@ -6,7 +6,8 @@ the byte / op accounting used to price a run against the chip's roofline.
 """
 from ._lib import (  # noqa: F401
     ACT_MODES, FORMATS, ROUTERS, STAGES, MOE_STAGE_COUNT,
-    MOE_ACT_F32, MOE_ACT_Q8_0, MOE_W_INT4_G32, MOE_W_INT8_G32, MOE_W_INT4_ROW, MOE_W_INT8_ROW,
+    MOE_ACT_F32, MOE_ACT_Q8_0, MOE_W_INT4_G32, MOE_W_INT8_G32, MOE_W_INT2_G32, MOE_W_INT4_ROW, MOE_W_INT8_ROW,
+    MOE_W_INT2_ROW,
     MOE_ROUTER_SOFTMAX_TOPK, MOE_ROUTER_SIGMOID_NOAUX_TC,
     MoeError, QuantExperts, RouterParams, Experts,
     load, exported_names, router_params, with_top_p, quantize_experts, workspace,

@@ -28,13 +28,16 @@ MOE_W_INT8_G32 = 0
 MOE_W_INT4_G32 = 1
 MOE_W_INT8_ROW = 2
 MOE_W_INT4_ROW = 3
+MOE_W_INT2_G32 = 4
+MOE_W_INT2_ROW = 5
 MOE_ACT_F32 = 0
 MOE_ACT_Q8_0 = 1
 
 STAGES = ("route", "dispatch", "quant_x", "gateup", "down", "combine")
 MOE_STAGE_COUNT = len(STAGES)
 
-FORMATS = {"int8": MOE_W_INT8_G32, "int4": MOE_W_INT4_G32, "int8_row": MOE_W_INT8_ROW, "int4_row": MOE_W_INT4_ROW}
+FORMATS = {"int8": MOE_W_INT8_G32, "int4": MOE_W_INT4_G32, "int2": MOE_W_INT2_G32,
+           "int8_row": MOE_W_INT8_ROW, "int4_row": MOE_W_INT4_ROW, "int2_row": MOE_W_INT2_ROW}
 ACT_MODES = {"f32": MOE_ACT_F32, "q8_0": MOE_ACT_Q8_0}
 ROUTERS = {"softmax": MOE_ROUTER_SOFTMAX_TOPK, "noaux_tc": MOE_ROUTER_SIGMOID_NOAUX_TC}
 
@@ -173,8 +176,8 @@ class QuantExperts:
     """A stack of quantised SwiGLU experts in the library's layout (GPU tensors).
 
     Tensor shapes give the per-expert storage size only: gate_q / up_q hold
-    I*d bytes (int8) or I*d/2 (packed int4) per expert, shaped [E, I, d] or
-    [E, I, d/2]; scales I*d/32 floats, shaped [E, I, d/32] (the per-row
+    I*d bytes (int8), I*d/2 (packed int4) or I*d/4 (packed int2) per expert,
+    shaped [E, I, d], [E, I, d/2] or [E, I, d/4]; scales I*d/32 floats, shaped [E, I, d/32] (the per-row
     formats: I floats, shaped [E, I, 1]); down_q / down_s likewise with d and
     I swapped. The bytes inside are in the lane-tiled layout of
     include/moe.h (32-row tiles, lane-ordered), not row-major; per-row scales
@@ -194,7 +197,7 @@ class QuantExperts:
         if fmt not in FORMATS:
             raise ValueError(f"unknown weight format {fmt!r}")
         int8 = fmt.startswith("int8")
-        div = 1 if int8 else 2
+        div = {"int8": 1, "int4": 2, "int2": 4}[fmt.split("_")[0]]
         qdt = torch.int8 if int8 else torch.uint8
         per_row = fmt.endswith("_row")
         sg_d = 1 if per_row else d_model // 32    # scales per gate / up row

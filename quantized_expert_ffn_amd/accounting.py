@@ -21,7 +21,7 @@ GROUP = 32
 def matrix_bytes(rows: int, cols: int, fmt: str) -> int:
     """Quantised codes + fp32 scales (per group of 32, or per row for the
     "_row" formats) of one [rows, cols] matrix."""
-    payload = rows * cols if fmt.startswith("int8") else rows * cols // 2
+    payload = rows * cols * {"int8": 8, "int4": 4, "int2": 2}[fmt.split("_")[0]] // 8
     scales = rows if fmt.endswith("_row") else rows * (cols // GROUP)
     return payload + scales * 4
 

@@ -83,6 +83,10 @@ moe_status check_experts(const moe_experts* ex, const char* name, int act_mode) 
     MOE_REQUIRE(ex->d_model % (2 * moe::kGroup) == 0 && ex->d_ff % (2 * moe::kGroup) == 0, MOE_ERR_UNSUPPORTED,
                 "%s d_model %d and d_ff %d must be multiples of 64 (pairs of groups)", name, ex->d_model, ex->d_ff);
     MOE_REQUIRE(moe::fmt_valid(ex->format), MOE_ERR_INVALID_ARG, "%s unknown weight format %d", name, ex->format);
+    const int km = moe::fmt_k_multiple(ex->format);
+    MOE_REQUIRE(ex->d_model % km == 0 && ex->d_ff % km == 0, MOE_ERR_UNSUPPORTED,
+                "%s d_model %d and d_ff %d must be multiples of %d for weight format %d", name, ex->d_model,
+                ex->d_ff, km, ex->format);
     MOE_REQUIRE(ex->gate_q && ex->gate_s && ex->up_q && ex->up_s && ex->down_q && ex->down_s, MOE_ERR_INVALID_ARG,
                 "%s has a NULL weight or scale pointer", name);
     MOE_REQUIRE(aligned16(ex->gate_q) && aligned16(ex->up_q) && aligned16(ex->down_q), MOE_ERR_INVALID_ARG,
@@ -349,6 +353,9 @@ moe_status moe_quantize_weights(const float* w, int64_t rows, int32_t cols, int3
     MOE_REQUIRE(matrix_rows % moe::kTile == 0, MOE_ERR_UNSUPPORTED,
                 "matrix_rows = %d is not a multiple of 32 (tiled layout)", matrix_rows);
     MOE_REQUIRE(moe::fmt_valid(format), MOE_ERR_INVALID_ARG, "unknown format %d", format);
+    MOE_REQUIRE(cols % moe::fmt_k_multiple(format) == 0, MOE_ERR_UNSUPPORTED,
+                "cols = %d is not a multiple of %d (whole code blocks of format %d)", cols,
+                moe::fmt_k_multiple(format), format);
     if (rows == 0) return ok();
     MOE_REQUIRE(w && q && s, MOE_ERR_INVALID_ARG, "NULL tensor argument");
     MOE_REQUIRE(aligned16(w) && aligned16(q), MOE_ERR_INVALID_ARG, "w and q must be 16-byte aligned");

@@ -112,6 +112,10 @@ inline WsLayout ws_layout(int T, int k, int E, int d, int I, int act_mode, int h
 //   int4 codes:  1 KB blocks, block (pair p, tile t) at (p*NT + t) KB; lane
 //                l's 16 bytes at l*16, four dwords of 8 nibbles (low nibble =
 //                lower k): [row nl, g0][row 16+nl, g0][row nl, g1][row 16+nl, g1]
+//   int2 codes:  1 KB blocks, block (quad q of groups 4q .. 4q+3, tile t) at
+//                (q*NT + t) KB; lane l's 16 bytes at l*16, one dword per group
+//                of the quad, each two 16-bit words of 8 two-bit codes (low
+//                bits = lower k): [row nl][row 16+nl]
 //   scales fp32: 64-float blocks, block (tile t, pair p) at (t*P + p)*64;
 //                lane quad nl at nl*4:
 //                [row nl, g0][row 16+nl, g0][row nl, g1][row 16+nl, g1]
@@ -123,15 +127,26 @@ inline WsLayout ws_layout(int T, int k, int E, int d, int I, int act_mode, int h
 // ---------------------------------------------------------------------------
 constexpr int kTile = 32;
 
-// Weight formats: the code layout (int8 or packed int4, both described
-// above) and where the scales live (per group as above, or per row: one float
-// per matrix row, in row order).
-__host__ __device__ constexpr bool fmt_int8(int fmt) { return fmt == MOE_W_INT8_G32 || fmt == MOE_W_INT8_ROW; }
-__host__ __device__ constexpr int fmt_codes(int fmt) { return fmt_int8(fmt) ? MOE_W_INT8_G32 : MOE_W_INT4_G32; }
-__host__ __device__ constexpr bool fmt_per_row(int fmt) { return fmt == MOE_W_INT8_ROW || fmt == MOE_W_INT4_ROW; }
-inline bool fmt_valid(int fmt) { return fmt >= MOE_W_INT8_G32 && fmt <= MOE_W_INT4_ROW; }
+// Weight formats: the code layout (int8, packed int4 or packed int2, all
+// described above) and where the scales live (per group as above, or per row:
+// one float per matrix row, in row order).
+__host__ __device__ constexpr bool fmt_per_row(int fmt) {
+    return fmt == MOE_W_INT8_ROW || fmt == MOE_W_INT4_ROW || fmt == MOE_W_INT2_ROW;
+}
+// the group-scale format with the same codes (what the kernels' code paths
+// are keyed on)
+__host__ __device__ constexpr int fmt_codes(int fmt) {
+    return fmt == MOE_W_INT8_ROW ? MOE_W_INT8_G32 : fmt == MOE_W_INT4_ROW ? MOE_W_INT4_G32
+                                                  : fmt == MOE_W_INT2_ROW ? MOE_W_INT2_G32 : fmt;
+}
+__host__ __device__ constexpr int fmt_bits(int fmt) {
+    return fmt_codes(fmt) == MOE_W_INT8_G32 ? 8 : fmt_codes(fmt) == MOE_W_INT4_G32 ? 4 : 2;
+}
+inline bool fmt_valid(int fmt) { return fmt >= MOE_W_INT8_G32 && fmt <= MOE_W_INT2_ROW; }
+// the reduction length K must be a multiple of this (whole code blocks)
+inline int fmt_k_multiple(int fmt) { return fmt_bits(fmt) == 2 ? 4 * kGroup : 2 * kGroup; }
 // bytes of codes and floats of scales of one N x K matrix
-inline int64_t fmt_code_bytes(int fmt, int64_t N, int64_t K) { return fmt_int8(fmt) ? N * K : N * K / 2; }
+inline int64_t fmt_code_bytes(int fmt, int64_t N, int64_t K) { return N * K * fmt_bits(fmt) / 8; }
 inline int64_t fmt_scale_floats(int fmt, int64_t N, int64_t K) { return fmt_per_row(fmt) ? N : N * (K / kGroup); }
 
 // byte offset, inside one matrix of NT tiles, of the 8 int8 codes (row,
@@ -148,6 +163,13 @@ __host__ __device__ __forceinline__ size_t int4_code_offset(size_t row, size_t k
     return ((g >> 1) * NT + row / kTile) * 1024 + ((r & 15) + 16 * h) * 16 + ((g & 1) * 2 + (r >> 4)) * 4;
 }
 
+// byte offset, inside one matrix of NT tiles, of the 16-bit word holding the
+// 8 int2 codes (row, k = 8*k8 .. +7)
+__host__ __device__ __forceinline__ size_t int2_code_offset(size_t row, size_t k8, size_t NT) {
+    const size_t g = k8 >> 2, h = k8 & 3, r = row % kTile;
+    return ((g >> 2) * NT + row / kTile) * 1024 + ((r & 15) + 16 * h) * 16 + (g & 3) * 4 + (r >> 4) * 2;
+}
+
 // float index, inside one matrix, of the scale of (row, group g)
 __host__ __device__ __forceinline__ size_t scale_index(size_t row, size_t g, size_t G) {
     const size_t r = row % kTile;
@@ -161,16 +183,20 @@ __host__ __device__ __forceinline__ size_t scale_index(size_t row, size_t g, siz
 // (hi = f16(x/p), lo = f16(x/p - hi)). Inside each 8-wide slice the parts are
 // stored in the order in which the weight-code conversion produces its
 // operand slots (int8: bytes (0,2),(1,3) of a dword; int4: nibbles (0,4),
-// (1,5), (2,6), (3,7)).
+// (1,5), (2,6), (3,7); int2: k order).
 // ---------------------------------------------------------------------------
 // k offset (0..7) inside an 8-wide slice for operand slot j
 __host__ __device__ constexpr int slot_k(int fmt, int j) {
-    return fmt == MOE_W_INT8_G32 ? ((j & 4) | ((j & 1) << 1) | ((j >> 1) & 1)) : (((j & 1) << 2) | (j >> 1));
+    return fmt == MOE_W_INT8_G32   ? ((j & 4) | ((j & 1) << 1) | ((j >> 1) & 1))
+           : fmt == MOE_W_INT4_G32 ? (((j & 1) << 2) | (j >> 1))
+                                   : j;
 }
 
 // operand slot holding k offset kin (0..7) of an 8-wide slice
 __host__ __device__ constexpr int k_slot(int fmt, int kin) {
-    return fmt == MOE_W_INT8_G32 ? ((kin & 4) | ((kin & 2) >> 1) | ((kin & 1) << 1)) : (((kin & 3) << 1) | (kin >> 2));
+    return fmt == MOE_W_INT8_G32   ? ((kin & 4) | ((kin & 2) >> 1) | ((kin & 1) << 1))
+           : fmt == MOE_W_INT4_G32 ? (((kin & 3) << 1) | (kin >> 2))
+                                   : kin;
 }
 
 // exponent e with |x| < 2^e for x = amax (0 -> 0), clamped so 2^(15-e) stays finite

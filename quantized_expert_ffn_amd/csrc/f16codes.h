@@ -16,6 +16,12 @@
 // nibbles (0,4),(1,5),(2,6),(3,7) of an int4 dword, so the eight operand
 // slots of a lane hold the k offsets slot_k(fmt, 0..7) of its 8-wide slice
 // (common.h); the other operand is stored in the same order.
+//
+// An int2 code (|q| <= 1) is a 2-bit field u (after XOR 0b10, u = q + 2). The
+// 16-bit word of a lane's 8 codes is copied into both halves of a dword; a
+// mask then leaves one field in each half at bit 0, 2, 4 or 6, giving
+// 1024 + u * 2^b, and a packed fused multiply-add by 2^-b less (1024 / 2^b +
+// 2) leaves q. Eight codes take four such pairs, in k order.
 #pragma once
 
 #include "common.h"
@@ -69,6 +75,32 @@ __device__ __forceinline__ v8h codes_to_f16(uint32_t w0, uint32_t w1) {
         (void)w1;
         return r.h;
     }
+}
+
+// 8 int2 codes (one 16-bit word of dword w: rows nl (HALF 0) or 16 + nl
+// (HALF 1)) -> 8 f16 in k order
+template <int HALF>
+__device__ __forceinline__ v8h int2_codes_to_f16(uint32_t w) {
+    union {
+        uint32_t u[4];
+        v8h h;
+    } r;
+    const uint32_t a = w ^ 0xAAAAAAAAu;
+    // the word in both halves: k0..k7 at bits 0..15 and 16..31
+    const uint32_t y = __builtin_amdgcn_perm(a, a, HALF ? 0x03020302u : 0x01000100u);
+    // k4..k7 at bits 0..7 of the low half and of the high half
+    const uint32_t z = y >> 8;
+    r.u[0] = and_or(y, 0x000C0003u, 0x64006400u);   // k0 at bit 0, k1 at bit 2 (of its half)
+    r.u[1] = and_or(y, 0x00C00030u, 0x64006400u);   // k2 at bit 4, k3 at bit 6
+    r.u[2] = and_or(z, 0x000C0003u, 0x64006400u);   // k4, k5
+    r.u[3] = and_or(z, 0x00C00030u, 0x64006400u);   // k6, k7
+    const v2h m01 = v2h{(_Float16)1.0f, (_Float16)0.25f}, o01 = v2h{(_Float16)-1026.0f, (_Float16)-258.0f};
+    const v2h m23 = v2h{(_Float16)0.0625f, (_Float16)0.015625f}, o23 = v2h{(_Float16)-66.0f, (_Float16)-18.0f};
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+        r.u[i] = __builtin_bit_cast(uint32_t, __builtin_elementwise_fma(__builtin_bit_cast(v2h, r.u[i]),
+                                                                        (i & 1) ? m23 : m01, (i & 1) ? o23 : o01));
+    return r.h;
 }
 
 }  // namespace moe

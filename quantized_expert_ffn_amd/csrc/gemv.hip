@@ -86,7 +86,9 @@ constexpr int kMaxGemvGroups = 256;   // K <= 8192
 // row's scale multiplies the finished sum once.
 template <int FMT, bool GATEUP, int KS, bool Q8, bool ROW>
 __global__ __launch_bounds__(64 * KS) void gemv_kernel(const GemvArgs a) {
-    constexpr int kCL = FMT == MOE_W_INT8_G32 ? 2 : 1;   // 16-byte code loads per tile per pair
+    // 16-byte code loads per tile per pair (int2: one per two pairs)
+    constexpr int kCL = FMT == MOE_W_INT8_G32 ? 2 : 1;
+    constexpr bool I2 = FMT == MOE_W_INT2_G32;
     __shared__ float pwtab[Q8 ? 16 * kMaxGemvGroups : kMaxGemvGroups];   // Q8: [group][16 rows]
     __shared__ float red[KS > 1 ? KS - 1 : 1][2][2][4][64];
 
@@ -134,9 +136,17 @@ __global__ __launch_bounds__(64 * KS) void gemv_kernel(const GemvArgs a) {
     const int a_bytes = a.a_rows * K * 2;
     const __amdgpu_buffer_rsrc_t rah = __builtin_amdgcn_make_buffer_rsrc((void*)a.ahi, 0, a_bytes, 0x00020000);
     const __amdgpu_buffer_rsrc_t ral = __builtin_amdgcn_make_buffer_rsrc((void*)a.alo, 0, a_bytes, 0x00020000);
-    // wave ks takes a contiguous run of pairs [c0, c0 + n_my)
-    const int c0 = ks * P / KS;
-    const int n_my = (ks + 1) * P / KS - c0;
+    // wave ks takes a contiguous run of pairs [c0, c0 + n_my) (int2: whole
+    // quads of groups, as its code blocks hold them)
+    int c0, n_my;
+    if constexpr (I2) {
+        const int Q = P / 2;
+        c0 = 2 * (ks * Q / KS);
+        n_my = 2 * ((ks + 1) * Q / KS) - c0;
+    } else {
+        c0 = ks * P / KS;
+        n_my = (ks + 1) * P / KS - c0;
+    }
     if constexpr (GATEUP && !Q8) {
         for (int i = threadIdx.x; i < G; i += 64 * KS) pwtab[i] = a.apow[i];
     }
@@ -176,20 +186,33 @@ __global__ __launch_bounds__(64 * KS) void gemv_kernel(const GemvArgs a) {
             for (int r = 0; r < 2; ++r) acc[t][r] = v4f{0.f, 0.f, 0.f, 0.f};
 
         // ring of NB = 2 pairs (codes, activation parts) and of two scale
-        // quads (four pairs each: the current one and the next)
+        // quads (four pairs each: the current one and the next). int2: the
+        // code ring holds two quads of groups, slot (j / 2) % 2, each loaded
+        // by its even pair for itself and the odd one after it.
         uint4 wq[2][2][kCL];
         v8h xh[2][2], xl[2][2];
         uint4 sq_cur[2] = {}, sq_next[2] = {};
-        auto load = [&](int sp, int j) {
+        // pair j of the run into ring slot sp; rr = j % 4 (a constant at every
+        // call: runs start on an even pair and rounds hold four)
+        auto load = [&](int sp, int j, int rr) {
             // past the end: the last pair again (L2-resident), so that every
             // step issues the same loads and waits stay counted
             const int p = c0 + (j < n_my ? j : n_my - 1);
+            if constexpr (I2) {
+                if ((rr & 1) == 0) {
 #pragma unroll
-            for (int t = 0; t < 2; ++t)
+                    for (int t = 0; t < 2; ++t)
+                        wq[(rr >> 1) & 1][t][0] = __builtin_bit_cast(
+                            uint4, __builtin_amdgcn_raw_buffer_load_b128(rq[t], q_voff[t], (p >> 1) * n_tiles * 1024, 0));
+                }
+            } else {
 #pragma unroll
-                for (int c = 0; c < kCL; ++c)
-                    wq[sp][t][c] = __builtin_bit_cast(
-                        uint4, __builtin_amdgcn_raw_buffer_load_b128(rq[t], q_voff[t], (kCL * p + c) * n_tiles * 1024, 0));
+                for (int t = 0; t < 2; ++t)
+#pragma unroll
+                    for (int c = 0; c < kCL; ++c)
+                        wq[sp][t][c] = __builtin_bit_cast(
+                            uint4, __builtin_amdgcn_raw_buffer_load_b128(rq[t], q_voff[t], (kCL * p + c) * n_tiles * 1024, 0));
+            }
 #pragma unroll
             for (int gi = 0; gi < 2; ++gi) {
                 xh[sp][gi] = __builtin_bit_cast(v8h, __builtin_amdgcn_raw_buffer_load_b128(rah, a_voff, (2 * p + gi) * 64, 0));
@@ -237,7 +260,13 @@ __global__ __launch_bounds__(64 * KS) void gemv_kernel(const GemvArgs a) {
 #pragma unroll
                 for (int t = 0; t < 2; ++t) {
                     v8h b0, b1;
-                    if constexpr (FMT == MOE_W_INT8_G32) {
+                    if constexpr (I2) {
+                        // dword 2 (j % 2) + gi of the quad: both 16-row halves
+                        const uint4 c = wq[(r >> 1) & 1][t][0];
+                        const uint32_t dw = (r & 1) ? (gi ? c.w : c.z) : (gi ? c.y : c.x);
+                        b0 = int2_codes_to_f16<0>(dw);
+                        b1 = int2_codes_to_f16<1>(dw);
+                    } else if constexpr (FMT == MOE_W_INT8_G32) {
                         const uint4 c = wq[jj][t][gi];
                         b0 = codes_to_f16<FMT>(c.x, c.y);
                         b1 = codes_to_f16<FMT>(c.z, c.w);
@@ -291,8 +320,8 @@ __global__ __launch_bounds__(64 * KS) void gemv_kernel(const GemvArgs a) {
         // the first quad goes out first: at the top of every round the quad
         // it waits for is then older than at least two pairs of loads
         load_quad(0);
-        load(0, 0);
-        load(1, 1);
+        load(0, 0, 0);
+        load(1, 1, 1);
         int j0 = 0;
         for (; j0 + 4 <= n_my; j0 += 4) {
             sq_cur[0] = sq_next[0];
@@ -304,7 +333,7 @@ __global__ __launch_bounds__(64 * KS) void gemv_kernel(const GemvArgs a) {
                 __builtin_amdgcn_sched_barrier(0);
                 step(r & 1, j0 + r, r);
                 __builtin_amdgcn_sched_barrier(0);
-                load(r & 1, j0 + r + 2);
+                load(r & 1, j0 + r + 2, (r + 2) & 3);
             }
         }
         // the last n_my % 4 pairs
@@ -312,7 +341,7 @@ __global__ __launch_bounds__(64 * KS) void gemv_kernel(const GemvArgs a) {
         sq_cur[1] = sq_next[1];
         const int rest = n_my - j0;
         if (rest > 0) step(0, j0, 0);
-        if (rest > 2) load(0, j0 + 2);
+        if (rest > 2) load(0, j0 + 2, 2);
         if (rest > 1) step(1, j0 + 1, 1);
         if (rest > 2) step(0, j0 + 2, 2);
 
@@ -495,8 +524,10 @@ hipError_t launch_gemv(const moe_experts& routed, const moe_experts* shared, boo
     switch (routed.format) {
         case MOE_W_INT8_G32: MOE_GEMV_GU(MOE_W_INT8_G32, false) break;
         case MOE_W_INT4_G32: MOE_GEMV_GU(MOE_W_INT4_G32, false) break;
+        case MOE_W_INT2_G32: MOE_GEMV_GU(MOE_W_INT2_G32, false) break;
         case MOE_W_INT8_ROW: MOE_GEMV_GU(MOE_W_INT8_G32, true) break;
-        default: MOE_GEMV_GU(MOE_W_INT4_G32, true) break;
+        case MOE_W_INT4_ROW: MOE_GEMV_GU(MOE_W_INT4_G32, true) break;
+        default: MOE_GEMV_GU(MOE_W_INT2_G32, true) break;
     }
 #undef MOE_GEMV_GU
 #undef MOE_GEMV_KS

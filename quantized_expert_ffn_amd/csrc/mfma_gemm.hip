@@ -54,6 +54,8 @@ constexpr int kM16 = kBM / 16;       // 16-row tiles per block
 //      contiguous 1 KB read per operand
 //   B  int8: [4 tiles][kSG groups][1 KB]  weight blocks exactly as in HBM
 //      int4: [4 tiles][1 KB]              (one block holds the pair)
+//      int2: [4 tiles][kSG groups][256 B] the pair's dwords of each lane (a
+//                                         block holds two pairs)
 //   SX [kSG groups][kBM rows] fp32        activation scales
 //   SW [4 tiles][64] fp32                 the tiles' scale blocks of the pair
 //                                         (group-scale formats only)
@@ -61,7 +63,9 @@ constexpr int kLdsA = kSG * kM16 * 1024;   // 16384
 constexpr int kLdsSX = kSG * kBM * 4;      // 1024
 constexpr int kLdsSW = 4 * 64 * 4;         // 1024
 template <int FMT>
-constexpr int lds_b_bytes() { return FMT == MOE_W_INT8_G32 ? 4 * kSG * 1024 : 4 * 1024; }
+constexpr int lds_b_bytes() {
+    return FMT == MOE_W_INT8_G32 ? 4 * kSG * 1024 : FMT == MOE_W_INT4_G32 ? 4 * 1024 : 4 * kSG * 256;
+}
 template <int FMT>
 constexpr int lds_stage_bytes() { return kLdsA + lds_b_bytes<FMT>() + kLdsSX + kLdsSW; }
 
@@ -122,6 +126,10 @@ __device__ __forceinline__ void buffer_load_lds(__amdgpu_buffer_rsrc_t r, uint32
         __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr_t)dst, 16, voff, so, 0, 0);
     else
         __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr_t)dst, 4, voff, so, 0, 0);
+}
+
+__device__ __forceinline__ uint32_t lds_read_u32(const lds_byte* p) {
+    return *reinterpret_cast<const __attribute__((address_space(3))) uint32_t*>(p);
 }
 
 template <int CTRL>
@@ -205,7 +213,7 @@ __global__ __launch_bounds__(256) void q8_mfma_kernel(const MfmaArgs a) {
         lds_byte* SW = SX + kLdsSX;
         const int pc = min(st, P - 1);
         constexpr int nA = kSG * kM16;
-        constexpr int nB = FMT == MOE_W_INT8_G32 ? 4 * kSG : 4;
+        constexpr int nB = FMT == MOE_W_INT4_G32 ? 4 : 4 * kSG;
         constexpr int nSX = kSG * 2;
         constexpr int nJobs = nA + nB + nSX + (ROW ? 0 : 1);
         static_assert((nA + nB) % 4 == 0, "scale jobs must start on wave 0");
@@ -221,6 +229,11 @@ __global__ __launch_bounds__(256) void q8_mfma_kernel(const MfmaArgs a) {
                     const int j = b / kSG, g = b % kSG;
                     buffer_load_lds<16>(rw[mat_of(j)], l_off, ((2 * pc + g) * NT + tile_of(j)) * 1024,
                                         B + (j * kSG + g) * 1024);
+                } else if constexpr (FMT == MOE_W_INT2_G32) {
+                    // dword 2 (pc % 2) + g of each lane's 16 bytes in the quad block
+                    const int j = b / kSG, g = b % kSG;
+                    buffer_load_lds<4>(rw[mat_of(j)], l_off, ((pc >> 1) * NT + tile_of(j)) * 1024 + (2 * (pc & 1) + g) * 4,
+                                       B + (j * kSG + g) * 256);
                 } else {
                     const int j = b;
                     buffer_load_lds<16>(rw[mat_of(j)], l_off, (pc * NT + tile_of(j)) * 1024, B + j * 1024);
@@ -260,8 +273,10 @@ __global__ __launch_bounds__(256) void q8_mfma_kernel(const MfmaArgs a) {
         return v;
     };
     const int oA = opaque((4 * wm * 64 + lane) * 16);
-    const int oB0 = opaque(kLdsA + (FMT == MOE_W_INT8_G32 ? jt0 * kSG : jt0) * 1024 + lane * 16);
-    const int oB1 = opaque(kLdsA + (FMT == MOE_W_INT8_G32 ? jt1 * kSG : jt1) * 1024 + lane * 16);
+    const int oB0 = opaque(kLdsA + (FMT == MOE_W_INT2_G32 ? jt0 * kSG * 256 + lane * 4
+                                                          : (FMT == MOE_W_INT8_G32 ? jt0 * kSG : jt0) * 1024 + lane * 16));
+    const int oB1 = opaque(kLdsA + (FMT == MOE_W_INT2_G32 ? jt1 * kSG * 256 + lane * 4
+                                                          : (FMT == MOE_W_INT8_G32 ? jt1 * kSG : jt1) * 1024 + lane * 16));
     const int oSX = opaque(kLdsA + lds_b_bytes<FMT>() + (64 * wm + 4 * rq) * 4);
     const int oSW0 = opaque(kLdsA + lds_b_bytes<FMT>() + kLdsSX + (jt0 * 64 + nl * 4) * 4);
     const int oSW1 = opaque(kLdsA + lds_b_bytes<FMT>() + kLdsSX + (jt1 * 64 + nl * 4) * 4);
@@ -313,6 +328,9 @@ __global__ __launch_bounds__(256) void q8_mfma_kernel(const MfmaArgs a) {
                 if constexpr (FMT == MOE_W_INT8_G32) {
                     const uint4 c = lds_read<uint4>(base + (t ? oB1 : oB0) + g * 1024);
                     bf = hh ? codes_to_f16<FMT>(c.z, c.w) : codes_to_f16<FMT>(c.x, c.y);
+                } else if constexpr (FMT == MOE_W_INT2_G32) {
+                    const uint32_t c = lds_read_u32(base + (t ? oB1 : oB0) + g * 256);
+                    bf = hh ? int2_codes_to_f16<1>(c) : int2_codes_to_f16<0>(c);
                 } else {
                     const uint4 c = c4[t];
                     bf = codes_to_f16<FMT>(g ? (hh ? c.w : c.z) : (hh ? c.y : c.x), 0u);
@@ -485,8 +503,10 @@ hipError_t launch_q8_mfma(const moe_experts& routed, const moe_experts* shared, 
     switch (routed.format) {
         case MOE_W_INT8_G32: MOE_Q8_GU(MOE_W_INT8_G32, false) break;
         case MOE_W_INT4_G32: MOE_Q8_GU(MOE_W_INT4_G32, false) break;
+        case MOE_W_INT2_G32: MOE_Q8_GU(MOE_W_INT2_G32, false) break;
         case MOE_W_INT8_ROW: MOE_Q8_GU(MOE_W_INT8_G32, true) break;
-        default: MOE_Q8_GU(MOE_W_INT4_G32, true) break;
+        case MOE_W_INT4_ROW: MOE_Q8_GU(MOE_W_INT4_G32, true) break;
+        default: MOE_Q8_GU(MOE_W_INT2_G32, true) break;
     }
 #undef MOE_Q8_GU
 #undef MOE_Q8

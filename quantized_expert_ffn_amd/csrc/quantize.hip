@@ -1,5 +1,5 @@
-// Quantisers: weights (int8 / packed int4, a scale per group of 32 or per
-// row) and Q8_0 activations.
+// Quantisers: weights (int8 / packed int4 / packed int2, a scale per group of
+// 32 or per row) and Q8_0 activations.
 //
 // Weights: "mtlm-7m-base" (huggingface.co), section "Files" (int8, group size
 // 32) and "Show HN: Getting GLM-5.2 running on my slow computer", section "What's implemented" (int8 / packed
@@ -17,7 +17,7 @@ namespace moe {
 template <int BITS>
 __device__ __forceinline__ void encode_group(const float (&v)[kGroup], float sc, size_t row, size_t g, size_t NT,
                                              uint8_t* __restrict__ q) {
-    constexpr float qmax = BITS == 8 ? 127.0f : 7.0f;
+    constexpr float qmax = BITS == 8 ? 127.0f : BITS == 4 ? 7.0f : 1.0f;
     int code[kGroup];
 #pragma unroll
     for (int i = 0; i < kGroup; ++i) {
@@ -36,11 +36,16 @@ __device__ __forceinline__ void encode_group(const float (&v)[kGroup], float sc,
                 hi |= (uint32_t)(code[8 * h + 4 + j] & 0xff) << (8 * j);
             }
             *reinterpret_cast<uint2*>(q + int8_code_offset(row, k8, NT)) = make_uint2(lo, hi);
-        } else {
+        } else if constexpr (BITS == 4) {
             uint32_t p = 0;
 #pragma unroll
             for (int j = 0; j < 8; ++j) p |= (uint32_t)(code[8 * h + j] & 0xf) << (4 * j);
             *reinterpret_cast<uint32_t*>(q + int4_code_offset(row, k8, NT)) = p;
+        } else {
+            uint32_t p = 0;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) p |= (uint32_t)(code[8 * h + j] & 0x3) << (2 * j);
+            *reinterpret_cast<uint16_t*>(q + int2_code_offset(row, k8, NT)) = (uint16_t)p;
         }
     }
 }
@@ -70,14 +75,14 @@ __global__ __launch_bounds__(256) void quantize_weights_kernel(const float* __re
     const size_t grow = (size_t)(gi / G), g = (size_t)(gi % G);
     const size_t mat = grow / matrix_rows, row = grow % matrix_rows, NT = matrix_rows / kTile;
     const size_t mat_elems = (size_t)matrix_rows * G * kGroup;
-    q += mat * (BITS == 8 ? mat_elems : mat_elems / 2);
+    q += mat * mat_elems * BITS / 8;
     s += mat * (size_t)matrix_rows * G;
     float v[kGroup];
     load_group(w + gi * kGroup, v);
     float amax = 0.0f;
 #pragma unroll
     for (int i = 0; i < kGroup; ++i) amax = fmaxf(amax, fabsf(v[i]));
-    const float sc = __fdiv_rn(amax, BITS == 8 ? 127.0f : 7.0f);
+    const float sc = __fdiv_rn(amax, BITS == 8 ? 127.0f : BITS == 4 ? 7.0f : 1.0f);
     s[scale_index(row, g, (size_t)G)] = sc;
     encode_group<BITS>(v, sc, row, g, NT, q);
 }
@@ -100,10 +105,10 @@ __global__ __launch_bounds__(256) void quantize_rows_kernel(const float* __restr
         amax = fmaxf(amax, fmaxf(fmaxf(fabsf(f.x), fabsf(f.y)), fmaxf(fabsf(f.z), fabsf(f.w))));
     }
     amax = wave_max(amax);
-    const float sc = __fdiv_rn(amax, BITS == 8 ? 127.0f : 7.0f);
+    const float sc = __fdiv_rn(amax, BITS == 8 ? 127.0f : BITS == 4 ? 7.0f : 1.0f);
     const size_t mat = (size_t)grow / matrix_rows, row = (size_t)grow % matrix_rows, NT = matrix_rows / kTile;
     const size_t mat_elems = (size_t)matrix_rows * cols;
-    q += mat * (BITS == 8 ? mat_elems : mat_elems / 2);
+    q += mat * mat_elems * BITS / 8;
     if (lane == 0) s[grow] = sc;
     for (int g = lane; g < G; g += kWave) {
         float v[kGroup];
@@ -147,22 +152,23 @@ hipError_t launch_quantize_weights(const float* w, int64_t rows, int cols, int m
     const int G = cols / kGroup;
     const int64_t n_groups = rows * G;
     if (n_groups == 0) return hipSuccess;
-    const bool int8 = fmt_int8(format);
+    const int bits = fmt_bits(format);
     if (fmt_per_row(format)) {
         const dim3 grid((unsigned)((rows + 3) / 4));
-        if (int8)
-            hipLaunchKernelGGL(quantize_rows_kernel<8>, grid, dim3(256), 0, st, w, rows, G, matrix_rows, (uint8_t*)q, s);
-        else
-            hipLaunchKernelGGL(quantize_rows_kernel<4>, grid, dim3(256), 0, st, w, rows, G, matrix_rows, (uint8_t*)q, s);
+#define MOE_QR(B) hipLaunchKernelGGL(quantize_rows_kernel<B>, grid, dim3(256), 0, st, w, rows, G, matrix_rows, (uint8_t*)q, s)
+        if (bits == 8) MOE_QR(8);
+        else if (bits == 4) MOE_QR(4);
+        else MOE_QR(2);
+#undef MOE_QR
         return hipGetLastError();
     }
     const dim3 grid((unsigned)((n_groups + 255) / 256));
-    if (int8)
-        hipLaunchKernelGGL(quantize_weights_kernel<8>, grid, dim3(256), 0, st, w, n_groups, G, matrix_rows,
-                           (uint8_t*)q, s);
-    else
-        hipLaunchKernelGGL(quantize_weights_kernel<4>, grid, dim3(256), 0, st, w, n_groups, G, matrix_rows,
-                           (uint8_t*)q, s);
+#define MOE_QW(B) \
+    hipLaunchKernelGGL(quantize_weights_kernel<B>, grid, dim3(256), 0, st, w, n_groups, G, matrix_rows, (uint8_t*)q, s)
+    if (bits == 8) MOE_QW(8);
+    else if (bits == 4) MOE_QW(4);
+    else MOE_QW(2);
+#undef MOE_QW
     return hipGetLastError();
 }
 

@@ -110,7 +110,8 @@ __device__ __forceinline__ void xprep_waves(const float* __restrict__ x, int T, 
     if (xp.mode == XPREP_SPLIT) {
         for (int g = gw; g < G; g += nw) {
             if (xp.fmt == MOE_W_INT8_G32) split_group<MOE_W_INT8_G32>(x, T, d, g, xp);
-            else split_group<MOE_W_INT4_G32>(x, T, d, g, xp);
+            else if (xp.fmt == MOE_W_INT4_G32) split_group<MOE_W_INT4_G32>(x, T, d, g, xp);
+            else split_group<MOE_W_INT2_G32>(x, T, d, g, xp);
         }
     } else if (xp.mode == XPREP_Q8_0) {
         const int items = T * G;
@@ -118,7 +119,8 @@ __device__ __forceinline__ void xprep_waves(const float* __restrict__ x, int T, 
             const int item = base + ((threadIdx.x & 63) >> 2);
             if (item >= items) continue;
             if (xp.fmt == MOE_W_INT8_G32) q8_item<MOE_W_INT8_G32>(x, d, G, item, xp);
-            else q8_item<MOE_W_INT4_G32>(x, d, G, item, xp);
+            else if (xp.fmt == MOE_W_INT4_G32) q8_item<MOE_W_INT4_G32>(x, d, G, item, xp);
+            else q8_item<MOE_W_INT2_G32>(x, d, G, item, xp);
         }
     }
 }

@@ -91,6 +91,13 @@ LAYERS = {
     # per-row scales: the OLMoE shape with one fp32 scale per matrix row
     "olmoe_int4_row": LayerShape("olmoe_int4_row", 1006, d_model=2048, n_experts=64, d_ff=1024,
                                  top_k=8, router="softmax", renormalize=False, wformat="int4_row"),
+    # packed int2 (ternary codes): the OLMoE shape and the GLM shape
+    "olmoe_int2": LayerShape("olmoe_int2", 1007, d_model=2048, n_experts=64, d_ff=1024,
+                             top_k=8, router="softmax", renormalize=False, wformat="int2"),
+    "glm_int2": LayerShape("glm_int2", 1008, d_model=6144, n_experts=256, d_ff=2048, top_k=8,
+                           router="noaux_tc", n_group=8, topk_group=4,
+                           routed_scaling_factor=2.5, has_bias=True, shared_expert=True,
+                           wformat="int2"),
     "qwen": LayerShape("qwen", 1005, d_model=2048, n_experts=512, d_ff=512, top_k=10,
                        router="softmax", renormalize=True, shared_expert=True, shared_gate=True,
                        wformat="int4", zipf_s=1.1),
@@ -112,6 +119,10 @@ WORKLOADS = {
     # per-row weight scales (decode and prefill)
     "olmoe_b16_int4_row": Workload("olmoe_b16_int4_row", LAYERS["olmoe_int4_row"], 16, "f32"),
     "olmoe_int4_row_prefill": Workload("olmoe_int4_row_prefill", LAYERS["olmoe_int4_row"], 2048, "q8_0"),
+    # packed int2 weights
+    "olmoe_b16_int2": Workload("olmoe_b16_int2", LAYERS["olmoe_int2"], 16, "f32"),
+    "olmoe_int2_prefill": Workload("olmoe_int2_prefill", LAYERS["olmoe_int2"], 2048, "q8_0"),
+    "glm_b1_int2": Workload("glm_b1_int2", LAYERS["glm_int2"], 1, "f32"),
     # the layer with its neighbours fused in: RMSNorm before, residual after
     "olmoe_b16_block": Workload("olmoe_b16_block", LAYERS["olmoe"], 16, "f32", block=True),
     "olmoe_int4_prefill_block": Workload("olmoe_int4_prefill_block", LAYERS["olmoe_int4"], 2048, "q8_0", block=True),

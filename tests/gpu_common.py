@@ -67,14 +67,19 @@ def t2n(t: torch.Tensor) -> np.ndarray:
 
 def untile_codes(tiled: np.ndarray, n_rows: int, n_cols: int, fmt: str) -> np.ndarray:
     """Library weight codes (lane-tiled, group-major layout of include/moe.h) back to the
-    row-major storage the oracle keeps: int8 [N, K], or packed int4 [N, K/2]
-    (element 2i in the low nibble of byte i)."""
+    row-major storage the oracle keeps: int8 [N, K], packed int4 [N, K/2]
+    (element 2i in the low nibble of byte i) or packed int2 [N, K/4] (element
+    4i + j in bits 2j of byte i)."""
     flat = np.asarray(tiled).reshape(-1).view(np.uint8)
     nt, g = n_rows // 32, n_cols // 32
     if fmt.startswith("int8"):
         # (group, tile, h, nl, half, byte) -> row = 32 tile + 16 half + nl, k = 32 group + 8 h + byte
         a = flat.reshape(g, nt, 4, 16, 2, 8).transpose(1, 4, 3, 0, 2, 5)
         return a.reshape(n_rows, n_cols).view(np.int8)
+    if fmt.startswith("int2"):
+        # (quad, tile, h, nl, group of quad, half, byte) -> byte column 8 group + 2 h + byte
+        a = flat.reshape(g // 4, nt, 4, 16, 4, 2, 2).transpose(1, 5, 3, 0, 4, 2, 6)
+        return a.reshape(n_rows, n_cols // 4)
     # (pair, tile, h, nl, group of pair, half, byte) -> byte column 16 group + 4 h + byte
     a = flat.reshape(g // 2, nt, 4, 16, 2, 2, 4).transpose(1, 5, 3, 0, 4, 2, 6)
     return a.reshape(n_rows, n_cols // 2)

@@ -97,7 +97,9 @@ def test_layer_forward_validation(lib):
     assert _fwd(lib, routed=_experts(d_model=96)) == UNSUPPORTED  # d % 64 (pairs of groups)
     assert _fwd(lib, routed=_experts(d_ff=100)) == UNSUPPORTED    # I % 32
     assert _fwd(lib, routed=_experts(format=9)) == INVALID
-    assert _fwd(lib, routed=_experts(format=4)) == INVALID
+    assert _fwd(lib, routed=_experts(format=6)) == INVALID
+    assert _fwd(lib, routed=_experts(format=4)) == UNSUPPORTED   # int2 needs d % 128
+    assert _fwd(lib, T=0, routed=_experts(format=4, d_model=128, d_ff=256)) == OK
     assert _fwd(lib, T=0, routed=_experts(format=3)) == OK        # the per-row formats are valid
     assert _fwd(lib, shared=_experts(n_experts=1, format=2)) == UNSUPPORTED   # shared format != routed
     assert _fwd(lib, params=_params(shared_gate=FAKE + 4), shared=_experts(n_experts=1)) == INVALID  # misaligned
@@ -146,7 +148,9 @@ def test_route_dispatch_combine_validation(lib):
     assert lib.moe_quantize_weights(FAKE, 40, 64, 40, 0, FAKE, FAKE, None) == UNSUPPORTED   # matrix rows % 32
     assert lib.moe_quantize_weights(FAKE, 96, 64, 64, 0, FAKE, FAKE, None) == INVALID       # not whole matrices
     assert lib.moe_quantize_weights(FAKE, 64, 64, 0, 0, FAKE, FAKE, None) == INVALID
-    assert lib.moe_quantize_weights(FAKE, 32, 64, 32, 4, FAKE, FAKE, None) == INVALID      # unknown format
+    assert lib.moe_quantize_weights(FAKE, 32, 64, 32, 6, FAKE, FAKE, None) == INVALID      # unknown format
+    assert lib.moe_quantize_weights(FAKE, 32, 64, 32, 4, FAKE, FAKE, None) == UNSUPPORTED  # int2: cols % 128
+    assert lib.moe_quantize_weights(FAKE, 0, 128, 32, 5, FAKE, FAKE, None) == OK
     assert lib.moe_quantize_weights(FAKE, 32, 64, 32, -1, FAKE, FAKE, None) == INVALID
     assert lib.moe_quantize_weights(FAKE, 40, 64, 40, 3, FAKE, FAKE, None) == UNSUPPORTED  # per-row: same layout
     assert lib.moe_quantize_weights(FAKE, 0, 64, 32, 1, FAKE, FAKE, None) == OK
@@ -171,23 +175,28 @@ def test_accounting_matches_page_figures():
     # per-row scales: one float per matrix row
     assert acc.expert_bytes(*glm, "int4_row") == payload + (2 * glm[1] + glm[0]) * 4
     assert acc.expert_bytes(*glm, "int8_row") == 2 * payload + (2 * glm[1] + glm[0]) * 4
+    assert acc.expert_bytes(*glm, "int2") == payload // 2 + 3 * glm[0] * glm[1] // 32 * 4
+    assert acc.expert_bytes(*glm, "int2_row") == payload // 2 + (2 * glm[1] + glm[0]) * 4
 
 
-@pytest.mark.parametrize("fmt", ["int8", "int4"])
+@pytest.mark.parametrize("fmt", ["int8", "int4", "int2"])
 def test_untile_helpers_invert_the_documented_layout(fmt):
     """The GPU tests read library weights back through untile_*; check those
     against the layout formulas of include/moe.h, written out element by element."""
     from gpu_common import untile_codes, untile_scales
     rng = np.random.default_rng(3)
-    N, K = 96, 128
+    N, K = 96, 256
     G, P, NT = K // 32, K // 64, N // 32
-    codes = rng.integers(-7 if fmt == "int4" else -127, 8 if fmt == "int4" else 128, (N, K))
+    qmax = {"int8": 127, "int4": 7, "int2": 1}[fmt]
+    codes = rng.integers(-qmax, qmax + 1, (N, K))
     scales = rng.standard_normal((N, G)).astype(np.float32)
     sflat = np.zeros(N * G, np.float32)
     if fmt == "int8":
         qflat = np.zeros(N * K, np.int8)
-    else:
+    elif fmt == "int4":
         qflat = np.zeros(N * K // 8, np.uint32)
+    else:
+        qflat = np.zeros(N * K // 8, np.uint16)
     for row in range(N):
         t, r = divmod(row, 32)
         nl, half = r % 16, r // 16
@@ -199,13 +208,18 @@ def test_untile_helpers_invert_the_documented_layout(fmt):
                 if fmt == "int8":
                     for k in ks:
                         qflat[((g * NT + t) * 64 + lane) * 16 + 8 * half + k % 8] = codes[row, k]
-                else:
+                elif fmt == "int4":
                     word = 0
                     for k in ks:
                         word |= (int(codes[row, k]) & 0xF) << (4 * (k % 8))
                     qflat[((g // 2 * NT + t) * 64 + lane) * 4 + 2 * (g % 2) + half] = word
+                else:
+                    word = 0
+                    for k in ks:
+                        word |= (int(codes[row, k]) & 0x3) << (2 * (k % 8))
+                    qflat[((g // 4 * NT + t) * 64 + lane) * 8 + 2 * (g % 4) + half] = word
     from oracle import quant as oquant
-    stored = codes.astype(np.int8) if fmt == "int8" else oquant.pack_int4(codes.astype(np.int8))
+    stored = oquant.pack_codes(codes.astype(np.int8), {"int8": 8, "int4": 4, "int2": 2}[fmt])
     assert np.array_equal(untile_codes(qflat, N, K, fmt), stored)
     assert np.array_equal(untile_scales(sflat, N, K), scales)
 

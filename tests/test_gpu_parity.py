@@ -31,28 +31,28 @@ TOPP_EPS = 1e-5        # top-p mass this close (relative) to the threshold may d
 # ---------------------------------------------------------------------------
 # quantisers
 # ---------------------------------------------------------------------------
-@pytest.mark.parametrize("fmt", ["int8", "int4", "int8_row", "int4_row"])
+@pytest.mark.parametrize("fmt", ["int8", "int4", "int2", "int8_row", "int4_row", "int2_row"])
 def test_quantize_weights_bit_exact(fmt):
-    """A stack of two 64 x 192 matrices, with rows scaled over eight decades,
+    """A stack of two 64 x 256 matrices, with rows scaled over eight decades,
     an all-zero group and row, and a group of tiny values."""
     need_gpu()
     rng = np.random.default_rng(21)
-    w = (rng.standard_normal((2, 64, 192)) * rng.uniform(1e-4, 3, (2, 64, 1))).astype(np.float32)
+    w = (rng.standard_normal((2, 64, 256)) * rng.uniform(1e-4, 3, (2, 64, 1))).astype(np.float32)
     w[0, 3, 32:64] = 0.0
     w[0, 4, :32] = 1e-30
     w[1, 5, :] = 0.0
-    bits = 8 if fmt.startswith("int8") else 4
+    bits = {"int8": 8, "int4": 4, "int2": 2}[fmt.split("_")[0]]
     per_row = fmt.endswith("_row")
     qz = oquant.quantize_rows if per_row else oquant.quantize_weights
     refs = [qz(w[m], bits) for m in range(2)]
-    stored = [q if bits == 8 else oquant.pack_int4(q) for q, _ in refs]
+    stored = [oquant.pack_codes(q, bits) for q, _ in refs]
     q = torch.empty((2,) + stored[0].shape, dtype=torch.int8 if bits == 8 else torch.uint8, device="cuda")
     s = torch.empty((2,) + refs[0][1].shape, dtype=torch.float32, device="cuda")
     qe.moe_quantize_weights(torch.from_numpy(w).cuda(), qe.FORMATS[fmt], q, s)
     torch.cuda.synchronize()
     for m in range(2):
-        assert np.array_equal(untile_scales(t2n(s[m]), 64, 192, fmt), refs[m][1])
-        assert np.array_equal(untile_codes(t2n(q[m]), 64, 192, fmt), stored[m])
+        assert np.array_equal(untile_scales(t2n(s[m]), 64, 256, fmt), refs[m][1])
+        assert np.array_equal(untile_codes(t2n(q[m]), 64, 256, fmt), stored[m])
 
 
 def test_quantize_q8_0_bit_exact(golden_dir):
@@ -294,6 +294,10 @@ TINY_VARIANTS = {
     "tiny_int4_row_wide": dict(wformat="int4_row", d_model=192, d_ff=320, n_experts=6, top_k=3),
     # a shared expert gated by sigmoid(x . u)
     "tiny_gated": dict(shared_expert=True, shared_gate=True),
+    # packed int2 (K % 128 == 0 on both axes); the second has odd quad counts
+    # along d_ff and a K-split along d_model in the decode kernel
+    "tiny_int2": dict(wformat="int2", d_model=128, d_ff=256, shared_expert=True),
+    "tiny_int2_row": dict(wformat="int2_row", d_model=512, d_ff=384, n_experts=6, top_k=3),
 }
 
 
@@ -376,7 +380,8 @@ def test_expert_ffn_and_combine_pieces(act_mode):
     assert_close_rel(t2n(out), ref["out"], what="out")
 
 
-@pytest.mark.parametrize("variant", ["tiny", "tiny_int4", "tiny_wide", "tiny_int4_row_wide"])
+@pytest.mark.parametrize("variant", ["tiny", "tiny_int4", "tiny_wide", "tiny_int4_row_wide", "tiny_int2",
+                                     "tiny_int2_row"])
 def test_q8_group_dots_bit_exact(variant):
     """The production int8-MFMA kernels' exact int32 group dots, Q8_0(H) codes
     and the down projection's dots fed the GPU's own H codes."""
@@ -429,7 +434,8 @@ SAMPLE = 48
 
 @pytest.mark.parametrize("wname", ["olmoe_b1", "olmoe_b16", "glm_b1", "glm_verify4", "olmoe_int4_prefill",
                                    "qwen_prefill", "glm_b1_topp", "olmoe_b16_topp", "olmoe_b16_int4_row",
-                                   "olmoe_int4_row_prefill"])
+                                   "olmoe_int4_row_prefill", "olmoe_b16_int2", "olmoe_int2_prefill",
+                                   "glm_b1_int2"])
 def test_layer_full_size(wname):
     need_gpu()
     wl = synth.workload(wname)
