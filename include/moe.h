@@ -254,6 +254,10 @@ moe_status moe_route(const float* x, int32_t T, int32_t d, const float* gate_w,
  *                                  that is not dispatched
  * A -1 entry is a dropped slot (not counted). Other entries outside [0, E)
  * are skipped the same way; they never cause an out-of-bounds access.
+ *   ws, ws_bytes  optional scratch (device, 16-byte aligned, or NULL): with
+ *            T*k > 2048 and at least moe_workspace_size(T, k, E, 64, 64,
+ *            MOE_ACT_Q8_0, 0) bytes the dispatch spreads over many blocks;
+ *            otherwise it runs in one block. The result is the same.
  */
 moe_status moe_dispatch(const int32_t* topk_idx, int32_t T, int32_t k, int32_t E,
                         int32_t* counts, int32_t* offsets, int32_t* perm, int32_t* inv_perm,

@@ -262,11 +262,15 @@ def moe_route(x: torch.Tensor, gate_w: torch.Tensor, params: RouterParams, topk_
 
 
 def moe_dispatch(topk_idx: torch.Tensor, E: int, counts: torch.Tensor, offsets: torch.Tensor,
-                 perm: torch.Tensor, inv_perm: torch.Tensor, stream=None) -> None:
+                 perm: torch.Tensor, inv_perm: torch.Tensor, ws: Optional[torch.Tensor] = None,
+                 stream=None) -> None:
+    """ws (optional): scratch that lets large batches dispatch over many blocks."""
     T, k = topk_idx.shape
+    nbytes = ws.numel() * ws.element_size() if ws is not None else 0
     _check(load().moe_dispatch(_ptr(topk_idx, torch.int32, "topk_idx"), T, k, E, _ptr(counts, torch.int32, "counts"),
                                _ptr(offsets, torch.int32, "offsets"), _ptr(perm, torch.int32, "perm"),
-                               _ptr(inv_perm, torch.int32, "inv_perm"), None, 0, _stream(stream)), "moe_dispatch")
+                               _ptr(inv_perm, torch.int32, "inv_perm"), _ptr(ws, None, "ws"), nbytes,
+                               _stream(stream)), "moe_dispatch")
 
 
 def moe_expert_ffn(x: torch.Tensor, k: int, experts: QuantExperts, counts: torch.Tensor, offsets: torch.Tensor,

@@ -316,7 +316,8 @@ moe_status layer_forward_impl(const float* x, int32_t T, const float* gate_w, co
     else
         MOE_HIP(moe::launch_dispatch(idx, T, k, E, ws_at<int>(ws, L.counts), ws_at<int>(ws, L.offsets),
                                      ws_at<int>(ws, L.perm), inv_perm, has_shared, ws_at<int>(ws, L.row_token),
-                                     ws_at<int>(ws, L.slots), ws_at<int>(ws, L.tiles), ws_at<int>(ws, L.meta), st),
+                                     ws_at<int>(ws, L.slots), ws_at<int>(ws, L.tiles), ws_at<int>(ws, L.meta),
+                                     L.dhist ? ws_at<int>(ws, L.dhist) : nullptr, L.dbad ? ws_at<int>(ws, L.dbad) : nullptr, st),
                 "dispatch");
     record(ev, 2 * MOE_STAGE_DISPATCH + 1, st);
     float* y = ws_at<float>(ws, L.y);
@@ -393,16 +394,26 @@ moe_status moe_route(const float* x, int32_t T, int32_t d, const float* gate_w, 
 moe_status moe_dispatch(const int32_t* topk_idx, int32_t T, int32_t k, int32_t E, int32_t* counts,
                         int32_t* offsets, int32_t* perm, int32_t* inv_perm, void* ws, size_t ws_bytes,
                         hipStream_t stream) {
-    (void)ws;
-    (void)ws_bytes;
     MOE_REQUIRE(T >= 0 && k >= 1 && E >= 1 && k <= E, MOE_ERR_INVALID_ARG, "bad sizes T = %d, k = %d, E = %d", T,
                 k, E);
     MOE_REQUIRE(E <= moe::kMaxExperts, MOE_ERR_UNSUPPORTED, "E = %d > %d", E, moe::kMaxExperts);
     MOE_REQUIRE((int64_t)T * k <= (int64_t)1 << 30, MOE_ERR_UNSUPPORTED, "T*k too large");
     MOE_REQUIRE(counts && offsets, MOE_ERR_INVALID_ARG, "NULL tensor argument");
     if (T > 0) MOE_REQUIRE(topk_idx && perm && inv_perm, MOE_ERR_INVALID_ARG, "NULL tensor argument");
+    // scratch for the multi-block dispatch when the caller's workspace holds it
+    const int64_t n = (int64_t)T * k;
+    int* chunk_hist = nullptr;
+    int* chunk_bad = nullptr;
+    if (n > moe::kDispatchWaveMax && ws && aligned16(ws)) {
+        const size_t nch = (size_t)moe::dispatch_chunk_count(n);
+        const size_t hb = moe::align256(nch * E * sizeof(int));
+        if (ws_bytes >= hb + nch * sizeof(int)) {
+            chunk_hist = static_cast<int*>(ws);
+            chunk_bad = ws_at<int>(ws, hb);
+        }
+    }
     MOE_HIP(moe::launch_dispatch(topk_idx, T, k, E, counts, offsets, perm, inv_perm, 0, nullptr, nullptr, nullptr,
-                                 nullptr, stream),
+                                 nullptr, chunk_hist, chunk_bad, stream),
             "dispatch");
     return ok();
 }

@@ -39,23 +39,30 @@ struct WsLayout {
     size_t y = 0;          // f32  [R, d]
     size_t xn = 0;         // f32  [T, d]  RMSNorm(x) for the block entry point, T > 16 only
     size_t sgl = 0;        // f32  [max(S, 1), T]  shared-expert gate logits per d slice (with a shared expert)
+    size_t dhist = 0;      // i32  [chunks, E]  multi-block dispatch histograms (T*k > kDispatchWaveMax)
+    size_t dbad = 0;       // i32  [chunks]
     size_t total = 0;
     int max_tiles = 0;
 };
 
 constexpr int kTileRows = 128;        // rows (tokens) per prefill matrix-core tile
+constexpr int kDispatchWaveMax = 2048;   // assignments a single-wave dispatch takes
+constexpr int kDispatchChunk = 1024;     // assignments per block of the multi-block dispatch
+inline int dispatch_chunk_count(int64_t n) { return (int)((n + kDispatchChunk - 1) / kDispatchChunk); }
 
 // Router logits: 0 = one block per expert (small T); S >= 1 = fp32 matrix-core
-// tiles of 64 x 64 with d cut into S slices, enough to give ~512 blocks.
+// tiles of 128 tokens x 64 experts with d cut into S slices, enough to give
+// ~512 blocks.
 inline int router_splits(int T, int E, int d) {
     if (T <= 16) return 0;
-    const int tiles = ((T + 63) / 64) * ((E + 63) / 64);
+    const int tiles = ((T + 127) / 128) * ((E + 63) / 64);
     int s = (512 + tiles - 1) / tiles;
     const int smax = d / 128 > 0 ? d / 128 : 1;
     if (s > smax) s = smax;
     return s < 1 ? 1 : s;
 }
-inline int router_kslice(int d, int S) { return ((d + S - 1) / S + 7) / 8 * 8; }
+// d-slice length: a multiple of 64 (the last slice takes what is left)
+inline int router_kslice(int d, int S) { return ((d + S - 1) / S + 63) / 64 * 64; }
 
 inline size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
 
@@ -95,6 +102,10 @@ inline WsLayout ws_layout(int T, int k, int E, int d, int I, int act_mode, int h
     L.y = take(R * d * 4);
     if (S > 0) L.xn = take((size_t)T * d * 4);
     if (has_shared) L.sgl = take((size_t)(S > 0 ? S : 1) * T * 4);
+    if (n > (size_t)kDispatchWaveMax) {
+        L.dhist = take((size_t)dispatch_chunk_count((int64_t)n) * E * 4);
+        L.dbad = take((size_t)dispatch_chunk_count((int64_t)n) * 4);
+    }
     L.total = off;
     return L;
 }

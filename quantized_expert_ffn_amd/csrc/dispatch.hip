@@ -12,8 +12,11 @@
 //   2. each lane scans a run of experts and the runs are scanned across the
 //      wave into counts, offsets, slot and tile positions;
 //   3. position = offset + rank, so the permutation is stable by construction.
-// Large batches spread step 1 over the 16 waves of a 1024-thread block (a
-// histogram row per wave, scanned over waves and then over experts).
+// Large batches rank over many blocks of kRankChunk assignments each (a
+// histogram per chunk), one block scans the chunk histograms per expert and
+// then over experts, and many blocks place every assignment; without the
+// chunk scratch (moe_dispatch called with no workspace) the same steps run
+// in one 1024-thread block, a histogram row per wave.
 // Both then write the work lists the expert kernels consume: slots (one per
 // expert with rows, then the shared expert), prefill tiles of kTileRows rows,
 // and the row -> token map.
@@ -221,7 +224,7 @@ __device__ __forceinline__ int wave_exclusive_scan(int v, int* total) {
 // The same dispatch by one wave, for small batches (the decode case): no
 // block barrier anywhere, every LDS access is the wave's own and in order.
 // cnt_l, off_l: E ints of LDS each; rank_l: n ints (LDS or global).
-constexpr int kWaveDispatchMax = 2048;   // assignments (32 passes of 64)
+constexpr int kWaveDispatchMax = kDispatchWaveMax;   // assignments (32 passes of 64)
 __device__ __forceinline__ void dispatch_wave(const int* idx, int* rank_l, int T, int k, int E,
                                               int* __restrict__ counts, int* __restrict__ offsets,
                                               int* __restrict__ perm, int* __restrict__ inv_perm, int has_shared,
@@ -339,6 +342,153 @@ __global__ __launch_bounds__(kDispThreads) void dispatch_kernel(const int* __res
                    tiles, meta, lds, lds + kDispWaves * E, &bad_flag);
 }
 
+// ---------------------------------------------------------------------------
+// Multi-block dispatch for large batches. Chunk c = assignments
+// [c * kRankChunk, (c + 1) * kRankChunk); each of a block's four waves ranks
+// a quarter of it, 64 at a time. The three kernels run in stream order.
+// ---------------------------------------------------------------------------
+constexpr int kRankChunk = kDispatchChunk;
+constexpr int kRankPasses = kRankChunk / (4 * kWave);   // passes of 64 per wave
+
+int dispatch_chunks(int64_t n) { return dispatch_chunk_count(n); }
+
+// 1. ranks: tmp[f] = rank of f among the chunk's assignments to its expert;
+//    chunk_hist[c][e] = the chunk's count of expert e; chunk_bad[c] = 1 when
+//    the chunk holds an id outside [0, E) other than -1.
+__global__ __launch_bounds__(256) void dispatch_rank_kernel(const int* __restrict__ idx, int n, int E,
+                                                            int* __restrict__ tmp, int* __restrict__ chunk_hist,
+                                                            int* __restrict__ chunk_bad) {
+    extern __shared__ __attribute__((aligned(16))) int hist[];   // [4][E]
+    __shared__ int bad_any;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int c = blockIdx.x;
+    for (int i = tid; i < 4 * E; i += 256) hist[i] = 0;
+    if (tid == 0) bad_any = 0;
+    __syncthreads();
+    const int nbits = E > 1 ? 32 - __clz(E - 1) : 0;
+    const uint64_t lt = lanemask_lt();
+    int* my_hist = hist + wave * E;
+    const int base = c * kRankChunk + wave * (kRankPasses * kWave);
+    int ev[kRankPasses], rv[kRankPasses];
+#pragma unroll
+    for (int u = 0; u < kRankPasses; ++u) {
+        const int f = base + u * kWave + lane;
+        ev[u] = f < n ? idx[f] : -1;
+    }
+    bool bad = false;
+#pragma unroll
+    for (int u = 0; u < kRankPasses; ++u) {
+        const int f = base + u * kWave + lane;
+        const int e = ev[u];
+        const bool inr = f < n && e >= 0 && e < E;
+        bad |= f < n && !inr && e != -1;   // -1: a slot dropped by top-p
+        uint64_t peers = __ballot(inr);
+        for (int b = 0; b < nbits; ++b) {
+            const bool bit = (e >> b) & 1;
+            const uint64_t m = __ballot(inr && bit);
+            peers &= bit ? m : ~m;
+        }
+        const int rank = __popcll(peers & lt);
+        const int prior = inr ? my_hist[e] : 0;
+        // the last lane of each peer set advances the count; every lane has
+        // read it above, and a wave executes its LDS operations in order
+        if (inr && rank == __popcll(peers) - 1) my_hist[e] = prior + __popcll(peers);
+        rv[u] = prior + rank;
+        ev[u] = inr ? e : -1;
+    }
+    if (bad) bad_any = 1;
+    __syncthreads();
+    // per expert: the waves' counts become wave offsets inside the chunk
+    for (int e = tid; e < E; e += 256) {
+        int run = 0;
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+            const int v = hist[w * E + e];
+            hist[w * E + e] = run;
+            run += v;
+        }
+        chunk_hist[(size_t)c * E + e] = run;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int u = 0; u < kRankPasses; ++u) {
+        const int f = base + u * kWave + lane;
+        if (ev[u] >= 0) tmp[f] = my_hist[ev[u]] + rv[u];
+    }
+    if (tid == 0) chunk_bad[c] = bad_any;
+}
+
+// 2. one block: per expert, chunk offsets (exclusive over chunks, in place;
+//    8 chunks' loads at a time) and the count; offsets over experts. Then the
+//    perm tail, the shared rows of row_token and the work lists.
+__global__ __launch_bounds__(kDispThreads) void dispatch_scan_kernel(int* __restrict__ chunk_hist,
+                                                                     const int* __restrict__ chunk_bad, int nch,
+                                                                     int T, int k, int E, int* __restrict__ counts,
+                                                                     int* __restrict__ offsets,
+                                                                     int* __restrict__ perm, int has_shared,
+                                                                     int tile_rows, int* __restrict__ row_token,
+                                                                     int* __restrict__ slots, int* __restrict__ tiles,
+                                                                     int* __restrict__ meta) {
+    __shared__ int scan_tmp[kDispWaves + 1];
+    const int tid = threadIdx.x;
+    const int n = T * k;
+    int cnt = 0;
+    if (tid < E) {
+        for (int c0 = 0; c0 < nch; c0 += 8) {
+            int v[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) v[u] = c0 + u < nch ? chunk_hist[(size_t)(c0 + u) * E + tid] : 0;
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                if (c0 + u < nch) chunk_hist[(size_t)(c0 + u) * E + tid] = cnt;
+                cnt += v[u];
+            }
+        }
+    }
+    int total = 0;
+    const int off = block_exclusive_scan(tid < E ? cnt : 0, scan_tmp, &total);
+    if (tid < E) {
+        counts[tid] = cnt;
+        offsets[tid] = off;
+    }
+    if (tid == 0) offsets[E] = total;
+    for (int p = total + tid; p < n; p += kDispThreads) perm[p] = -1;
+    if (row_token && has_shared)
+        for (int t = tid; t < T; t += kDispThreads) row_token[n + t] = t;
+    if (slots) {
+        build_work_lists(E, cnt, off, n, T, has_shared, tile_rows, scan_tmp, slots, tiles, meta);
+        if (tid == 0) {
+            int bad = 0;
+            for (int c = 0; c < nch; ++c) bad |= chunk_bad[c];
+            meta[2] = bad;
+        }
+    }
+}
+
+// 3. positions: pos = offsets[e] + rows of e in earlier chunks + rank in the
+//    chunk
+__global__ __launch_bounds__(256) void dispatch_place_kernel(const int* __restrict__ idx, int n, int k, int E,
+                                                             const int* __restrict__ offsets,
+                                                             const int* __restrict__ chunk_hist,
+                                                             int* __restrict__ perm, int* __restrict__ inv_perm,
+                                                             int* __restrict__ row_token) {
+    const int c = blockIdx.x;
+#pragma unroll
+    for (int u = 0; u < kRankChunk / 256; ++u) {
+        const int f = c * kRankChunk + u * 256 + threadIdx.x;
+        if (f >= n) break;
+        const int e = idx[f];
+        if (e < 0 || e >= E) {
+            inv_perm[f] = -1;
+            continue;
+        }
+        const int pos = offsets[e] + chunk_hist[(size_t)c * E + e] + inv_perm[f];   // inv_perm holds the rank here
+        perm[pos] = f;
+        inv_perm[f] = pos;
+        if (row_token) row_token[pos] = f / k;
+    }
+}
+
 // Top-k of T <= kDispWaves tokens (wave t takes token t), then the dispatch,
 // in one block; the expert ids and ranks stay in LDS.
 template <int EPL>
@@ -435,9 +585,20 @@ hipError_t launch_route_dispatch(const float* logits, int T, int d, const moe_ro
 
 hipError_t launch_dispatch(const int* idx, int T, int k, int E, int* counts, int* offsets, int* perm,
                            int* inv_perm, int has_shared, int* row_token, int* slots, int* tiles, int* meta,
-                           hipStream_t st) {
+                           int* chunk_hist, int* chunk_bad, hipStream_t st) {
+    const int64_t n = (int64_t)T * k;
+    if (n > kWaveDispatchMax && chunk_hist && chunk_bad) {
+        const int nch = dispatch_chunks(n);
+        hipLaunchKernelGGL(dispatch_rank_kernel, dim3(nch), dim3(256), (size_t)4 * E * sizeof(int), st, idx, (int)n,
+                           E, inv_perm, chunk_hist, chunk_bad);
+        hipLaunchKernelGGL(dispatch_scan_kernel, dim3(1), dim3(kDispThreads), 0, st, chunk_hist, chunk_bad, nch, T, k,
+                           E, counts, offsets, perm, has_shared, kTileRows, row_token, slots, tiles, meta);
+        hipLaunchKernelGGL(dispatch_place_kernel, dim3(nch), dim3(256), 0, st, idx, (int)n, k, E, offsets, chunk_hist,
+                           perm, inv_perm, row_token);
+        return hipGetLastError();
+    }
     // small batches: one wave does it all (dispatch_wave)
-    const int threads = (int64_t)T * k <= kWaveDispatchMax ? kWave : kDispThreads;
+    const int threads = n <= kWaveDispatchMax ? kWave : kDispThreads;
     hipLaunchKernelGGL(dispatch_kernel, dim3(1), dim3(threads), dispatch_lds_bytes(E), st, idx, T, k, E, counts,
                        offsets, perm, inv_perm, has_shared, kTileRows, row_token, slots, tiles, meta);
     return hipGetLastError();

@@ -52,9 +52,13 @@ hipError_t launch_route_dispatch(const float* logits, int T, int d, const moe_ro
                                  int* row_token, int* slots, int* tiles, int* meta, hipStream_t st);
 
 size_t dispatch_lds_bytes(int E);
+// chunks of the multi-block dispatch for n assignments (its scratch: a
+// histogram [chunks, E] and a flag per chunk, ints)
+int dispatch_chunks(int64_t n);
+// chunk_hist / chunk_bad null: the single-block dispatch for any size
 hipError_t launch_dispatch(const int* idx, int T, int k, int E, int* counts, int* offsets, int* perm,
                            int* inv_perm, int has_shared, int* row_token, int* slots, int* tiles, int* meta,
-                           hipStream_t st);
+                           int* chunk_hist, int* chunk_bad, hipStream_t st);
 hipError_t launch_plan(const int* counts, const int* offsets, const int* perm, int T, int k, int E, int has_shared,
                        int* row_token, int* slots, int* tiles, int* meta, hipStream_t st);
 

@@ -237,47 +237,88 @@ __global__ __launch_bounds__(256) void rmsnorm_kernel(const float* __restrict__ 
 
 // ---------------------------------------------------------------------------
 // Logits, larger T: fp32 matrix cores (v_mfma_f32_32x32x2_f32), split over d.
-// Block: 64 tokens x 64 experts, four waves of 32 x 32; blockIdx.z = slice.
-// Each lane loads 4 consecutive k of its token row and its expert row; the
-// four MFMAs of a step each take one of them (the two lane halves cover
+// Block: kRBM tokens x kRBN experts, four waves of 64 x 32 (two 32 x 32
+// products each); blockIdx.z = slice. The slice goes through LDS kRKC k at a
+// time: each row's chunk is one 128-byte line, read by 8 neighbouring lanes,
+// and the next chunk's loads are in flight while the current one is
+// multiplied. From LDS each lane takes 4 consecutive k of its row; the four
+// products of a step each take one of them (the two lane halves cover
 // k..k+3 and k+4..k+7), so every (token, expert, k) product enters once.
-// A shared-expert gate vector sg is expert row E; its slice sums go to
-// sgl [S, T].
+// Rows past T or E read a valid row and are never stored. A shared-expert
+// gate vector sg is expert row E; its slice sums go to sgl [S, T].
 // ---------------------------------------------------------------------------
+constexpr int kRBM = 128, kRBN = 64, kRKC = 32;
+constexpr int kRPad = kRKC + 4;   // LDS row stride (floats): 16-byte reads of 16 rows hit distinct banks
+
 __global__ __launch_bounds__(256) void router_logits_mfma_kernel(const float* __restrict__ x,
                                                                  const float* __restrict__ wg, int T, int d,
                                                                  int E, int kslice, float* __restrict__ L,
                                                                  const float* __restrict__ sg,
                                                                  float* __restrict__ sgl) {
-    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    const int t0 = blockIdx.y * 64 + (wave & 1) * 32;
-    const int e0 = blockIdx.x * 64 + (wave >> 1) * 32;
+    __shared__ __attribute__((aligned(16))) float xs[kRBM * kRPad];
+    __shared__ __attribute__((aligned(16))) float wsh[kRBN * kRPad];
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int wm = wave & 1, wn = wave >> 1;
+    const int tb = blockIdx.y * kRBM, eb = blockIdx.x * kRBN;
     const int ks = blockIdx.z;
     const int kbeg = ks * kslice, kend = min(d, kbeg + kslice);
+    // loads: rows lr + 32 j, k quad lq of each chunk
+    const int lr = tid >> 3, lq = (tid & 7) * 4;
+    const float* xsrc[kRBM / 32];
+    const float* wsrc[kRBN / 32];
+#pragma unroll
+    for (int j = 0; j < kRBM / 32; ++j) xsrc[j] = x + (size_t)min(tb + lr + 32 * j, T - 1) * d + lq;
+#pragma unroll
+    for (int j = 0; j < kRBN / 32; ++j) {
+        const int e = eb + lr + 32 * j;
+        wsrc[j] = (sg != nullptr && e == E) ? sg + lq : wg + (size_t)min(e, E - 1) * d + lq;
+    }
+    float4 xr[kRBM / 32], wr[kRBN / 32];
+    auto gload = [&](int k0) {
+        const bool ok = k0 + lq < kend;   // d % 4 == 0: a quad is all in or all out
+#pragma unroll
+        for (int j = 0; j < kRBM / 32; ++j)
+            xr[j] = ok ? *reinterpret_cast<const float4*>(xsrc[j] + k0) : make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+        for (int j = 0; j < kRBN / 32; ++j)
+            wr[j] = ok ? *reinterpret_cast<const float4*>(wsrc[j] + k0) : make_float4(0.f, 0.f, 0.f, 0.f);
+    };
     const int row = lane & 31, h = lane >> 5;
-    const bool is_sg = sg != nullptr && e0 + row == E;
-    const bool tok_ok = t0 + row < T, exp_ok = e0 + row < E || is_sg;
-    const float* xr = x + (size_t)(tok_ok ? t0 + row : 0) * d;
-    const float* wr = is_sg ? sg : wg + (size_t)(exp_ok ? e0 + row : 0) * d;
-    v16f acc = {};
-    for (int k = kbeg; k < kend; k += 8) {
-        const int kk = k + 4 * h;
-        const bool kok = kk < kend;
-        const float4 a = (tok_ok && kok) ? *reinterpret_cast<const float4*>(xr + kk) : make_float4(0.f, 0.f, 0.f, 0.f);
-        const float4 b = (exp_ok && kok) ? *reinterpret_cast<const float4*>(wr + kk) : make_float4(0.f, 0.f, 0.f, 0.f);
-        acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a.x, b.x, acc, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a.y, b.y, acc, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a.z, b.z, acc, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a.w, b.w, acc, 0, 0, 0);
+    v16f acc[2] = {};
+    if (kbeg < kend) gload(kbeg);
+    for (int k0 = kbeg; k0 < kend; k0 += kRKC) {
+        __syncthreads();   // the previous chunk's readers are done
+#pragma unroll
+        for (int j = 0; j < kRBM / 32; ++j) *reinterpret_cast<float4*>(&xs[(lr + 32 * j) * kRPad + lq]) = xr[j];
+#pragma unroll
+        for (int j = 0; j < kRBN / 32; ++j) *reinterpret_cast<float4*>(&wsh[(lr + 32 * j) * kRPad + lq]) = wr[j];
+        __syncthreads();
+        if (k0 + kRKC < kend) gload(k0 + kRKC);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int s = 0; s < kRKC / 8; ++s) {
+            const float4 b = *reinterpret_cast<const float4*>(&wsh[(32 * wn + row) * kRPad + 8 * s + 4 * h]);
+#pragma unroll
+            for (int i = 0; i < 2; ++i) {
+                const float4 a = *reinterpret_cast<const float4*>(&xs[(64 * wm + 32 * i + row) * kRPad + 8 * s + 4 * h]);
+                acc[i] = __builtin_amdgcn_mfma_f32_32x32x2f32(a.x, b.x, acc[i], 0, 0, 0);
+                acc[i] = __builtin_amdgcn_mfma_f32_32x32x2f32(a.y, b.y, acc[i], 0, 0, 0);
+                acc[i] = __builtin_amdgcn_mfma_f32_32x32x2f32(a.z, b.z, acc[i], 0, 0, 0);
+                acc[i] = __builtin_amdgcn_mfma_f32_32x32x2f32(a.w, b.w, acc[i], 0, 0, 0);
+            }
+        }
     }
     float* out = L + (size_t)ks * T * E;
-    const int e = e0 + row;
+    const int e = eb + 32 * wn + row;
+    const bool is_sg = sg != nullptr && e == E;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-        const int t = t0 + 8 * (i >> 2) + 4 * h + (i & 3);
-        if (t < T && e < E) out[(size_t)t * E + e] = acc[i];
-        if (t < T && is_sg) sgl[(size_t)ks * T + t] = acc[i];
-    }
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int q = 0; q < 16; ++q) {
+            const int t = tb + 64 * wm + 32 * i + 8 * (q >> 2) + 4 * h + (q & 3);
+            if (t < T && e < E) out[(size_t)t * E + e] = acc[i][q];
+            if (t < T && is_sg) sgl[(size_t)ks * T + t] = acc[i][q];
+        }
 }
 
 // ---------------------------------------------------------------------------
@@ -338,7 +379,7 @@ hipError_t launch_router_logits(const float* x, int T, int d, const float* wg, i
     }
     // larger T: the preparation is the caller's own launch (launch_xprep)
     const int kslice = router_kslice(d, S);
-    const dim3 grid((rows + 63) / 64, (T + 63) / 64, S);
+    const dim3 grid((rows + kRBN - 1) / kRBN, (T + kRBM - 1) / kRBM, S);
     hipLaunchKernelGGL(router_logits_mfma_kernel, grid, dim3(256), 0, st, x, wg, T, d, E, kslice, logits, sg, sgl);
     return hipGetLastError();
 }

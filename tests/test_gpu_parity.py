@@ -191,23 +191,28 @@ def test_route_full_size(name, tokens):
 # ---------------------------------------------------------------------------
 # dispatch
 # ---------------------------------------------------------------------------
-def gpu_dispatch(idx, E):
+def gpu_dispatch(idx, E, scratch=True):
+    """scratch: pass a workspace (large batches then dispatch over many
+    blocks); without one the single-block dispatch runs."""
     T, k = idx.shape
     n = max(1, T * k)
+    ws = qe.workspace(T, k, E, 64, 64, qe.MOE_ACT_Q8_0, False) if scratch else None
     counts = torch.empty(E, dtype=torch.int32, device="cuda")
     offsets = torch.empty(E + 1, dtype=torch.int32, device="cuda")
     perm = torch.empty(n, dtype=torch.int32, device="cuda")
     inv = torch.empty(n, dtype=torch.int32, device="cuda")
     qe.moe_dispatch(torch.from_numpy(np.ascontiguousarray(idx, dtype=np.int32)).cuda(), E, counts, offsets,
-                    perm, inv)
+                    perm, inv, ws)
     torch.cuda.synchronize()
     return t2n(counts), t2n(offsets), t2n(perm)[:T * k], t2n(inv)[:T * k]
 
 
+@pytest.mark.parametrize("scratch", [True, False])
 @pytest.mark.parametrize("T,k,E,zipf", [(16, 2, 8, False), (1, 8, 64, False), (16, 8, 64, False),
                                         (2048, 8, 64, False), (4, 8, 256, False), (4096, 10, 512, True),
-                                        (64, 64, 1024, False), (3, 1, 1, False), (777, 3, 5, True)])
-def test_dispatch_bit_exact(T, k, E, zipf):
+                                        (64, 64, 1024, False), (3, 1, 1, False), (777, 3, 5, True),
+                                        (2049, 1, 3, False), (1000, 9, 1024, True)])
+def test_dispatch_bit_exact(T, k, E, zipf, scratch):
     need_gpu()
     rng = np.random.default_rng(T * 31 + k * 7 + E)
     if zipf:
@@ -216,7 +221,7 @@ def test_dispatch_bit_exact(T, k, E, zipf):
         idx = np.stack([rng.choice(E, size=k, replace=False, p=p) for _ in range(T)])
     else:
         idx = np.stack([rng.choice(E, size=k, replace=False) for _ in range(T)])
-    got = gpu_dispatch(idx, E)
+    got = gpu_dispatch(idx, E, scratch)
     want = odispatch.dispatch(idx, E)
     for g, w, nm in zip(got, want, ("counts", "offsets", "perm", "inv_perm")):
         assert np.array_equal(g, w), nm
@@ -230,6 +235,17 @@ def test_dispatch_empty_and_out_of_range():
     c, o, perm, inv = gpu_dispatch(idx, 8)
     assert c.tolist() == [1, 0, 0, 2, 0, 0, 0, 1] and o[-1] == 4
     assert sorted(perm[:4].tolist()) == [0, 1, 2, 5]
+    # a large batch (the multi-block dispatch) with dropped and out-of-range ids
+    rng = np.random.default_rng(8)
+    idx = rng.integers(0, 8, size=(1500, 3)).astype(np.int32)
+    idx[::7, 2] = -1
+    idx[5, 0], idx[901, 1], idx[1499, 2] = 8, 1 << 20, -5
+    for scratch in (True, False):
+        c, o, perm, inv = gpu_dispatch(idx, 8, scratch)
+        # ids outside [0, E) are skipped like -1
+        wc, wo, wp, wi = odispatch.dispatch(np.where((idx >= 0) & (idx < 8), idx, -1), 8)
+        assert np.array_equal(c, wc) and np.array_equal(o, wo)
+        assert np.array_equal(perm, wp) and np.array_equal(inv, wi)
 
 
 # ---------------------------------------------------------------------------
