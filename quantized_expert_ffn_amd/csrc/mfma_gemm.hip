@@ -153,7 +153,17 @@ __global__ __launch_bounds__(256) void q8_mfma_kernel(const MfmaArgs a) {
     // that reading one does not wait for the direct loads into the other
     __shared__ __attribute__((aligned(1024))) uint8_t lds0[kStage];
     __shared__ __attribute__((aligned(1024))) uint8_t lds1[kStage];
-    const int tile_id = blockIdx.y;
+    // XCD-aware order: the hardware deals blocks to the 8 XCDs in turn by
+    // linear id, so linear id L runs on XCD L % 8. Block L takes column block
+    // (L / 8) % ncol of row tile ((L / 8) / ncol) * 8 + L % 8: all column
+    // blocks of one row tile share an XCD, and its activation rows are
+    // fetched into that XCD's L2 once (the grid's tile count is a multiple
+    // of 8, so this is a bijection).
+    const int ncol = gridDim.x;
+    const int lin = blockIdx.y * ncol + blockIdx.x;
+    const int xcd = lin & 7, sl = lin >> 3;
+    const int col_blk = sl % ncol;
+    const int tile_id = (sl / ncol) * 8 + xcd;
     if (tile_id >= a.meta[1]) return;
     const int4 td = a.tiles[tile_id];
     const int e = td.x, row_begin = td.y, rows = td.z - td.y;
@@ -165,7 +175,7 @@ __global__ __launch_bounds__(256) void q8_mfma_kernel(const MfmaArgs a) {
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave & 1, wn = wave >> 1;
     const int K = a.K, N = a.N, G = K / kGroup, P = G / 2, NT = N / kTile;
-    const int T0 = blockIdx.x * (GATEUP ? 2 : 4);      // first 32-row weight tile of the block
+    const int T0 = col_blk * (GATEUP ? 2 : 4);         // first 32-row weight tile of the block
     const int m16_live = (rows + 15) >> 4;               // 16-row tiles holding rows (1 .. 8)
     const int my_live = min(max(m16_live - 4 * wm, 0), 4);
 
@@ -494,7 +504,7 @@ hipError_t launch_q8_mfma(const moe_experts& routed, const moe_experts* shared, 
     fill(a.routed, routed);
     fill(a.shared, shared ? *shared : routed);
     const int bn = gateup ? 2 * kTile : 4 * kTile;   // output columns per block
-    const dim3 grid((a.N + bn - 1) / bn, max_tiles);
+    const dim3 grid((a.N + bn - 1) / bn, (max_tiles + 7) / 8 * 8);   // tile count padded for the XCD order
     const bool dbg = dbg0 != nullptr;
 #define MOE_Q8(FMT, GU, DB, RW) launch_timed(q8_mfma_kernel<FMT, GU, DB, RW>, grid, dim3(256), st, ev0, ev1, a)
 #define MOE_Q8_GU(FMT, RW)                                                              \
