@@ -16,7 +16,7 @@
 
 namespace moe {
 
-typedef float v16f __attribute__((ext_vector_type(16)));
+typedef float v4f __attribute__((ext_vector_type(4)));
 typedef _Float16 v8h __attribute__((ext_vector_type(8)));
 
 // ---------------------------------------------------------------------------
@@ -236,31 +236,73 @@ __global__ __launch_bounds__(256) void rmsnorm_kernel(const float* __restrict__ 
 }
 
 // ---------------------------------------------------------------------------
-// Logits, larger T: fp32 matrix cores (v_mfma_f32_32x32x2_f32), split over d.
-// Block: kRBM tokens x kRBN experts, four waves of 64 x 32 (two 32 x 32
-// products each); blockIdx.z = slice. The slice goes through LDS kRKC k at a
-// time: each row's chunk is one 128-byte line, read by 8 neighbouring lanes,
-// and the next chunk's loads are in flight while the current one is
-// multiplied. From LDS each lane takes 4 consecutive k of its row; the four
-// products of a step each take one of them (the two lane halves cover
-// k..k+3 and k+4..k+7), so every (token, expert, k) product enters once.
-// Rows past T or E read a valid row and are never stored. A shared-expert
-// gate vector sg is expert row E; its slice sums go to sgl [S, T].
+// Logits, larger T: fp32-level products on the bf16 matrix cores
+// (v_mfma_f32_16x16x32_bf16), split over d.
+//
+// Each fp32 value v is split into three bf16 parts, v = h + m + l exactly
+// (h = bf16(v), m = bf16(v - h), l = bf16(v - h - m): 8 significant bits
+// each, and bf16 has the fp32 exponent range, so no scaling is needed). A
+// product of two parts is exact in fp32, and the six products
+//     hh + hm + mh + hl + lh + mm
+// are the fp32 product up to terms of 2^-24 relative; the matrix core adds
+// them in fp32. Six bf16 products take a third of the time of the same MACs
+// on the fp32 matrix cores.
+//
+// Block: kRBM tokens x kRBN experts, four waves of 64 tokens x 32 experts
+// (4 x 2 products of 16 x 16 per part pair); blockIdx.z = slice. The slice
+// goes through LDS kRKC = 32 k (one product) at a time: each row's chunk is
+// one 128-byte line read by 8 neighbouring lanes, split into its parts on the
+// way in, and the next chunk's loads are in flight while the current one is
+// multiplied. Rows past T or E read a valid row and are never stored. A
+// shared-expert gate vector sg is expert row E; its slice sums go to
+// sgl [S, T].
 // ---------------------------------------------------------------------------
 constexpr int kRBM = 128, kRBN = 64, kRKC = 32;
-constexpr int kRPad = kRKC + 4;   // LDS row stride (floats): 16-byte reads of 16 rows hit distinct banks
+constexpr int kRPad = kRKC + 8;   // LDS row stride (bf16): 16-byte reads of 16 rows hit distinct banks
+
+typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+
+// v = h + m + l, each part bf16 (round to nearest even), packed two per dword
+__device__ __forceinline__ void split3_bf16(float4 v, uint2& h, uint2& m, uint2& l) {
+    const float a[4] = {v.x, v.y, v.z, v.w};
+    uint16_t ph[4], pm[4], pl[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const __bf16 bh = (__bf16)a[i];
+        const float r1 = a[i] - (float)bh;
+        const __bf16 bm = (__bf16)r1;
+        const float r2 = r1 - (float)bm;
+        const __bf16 bl = (__bf16)r2;
+        ph[i] = __builtin_bit_cast(uint16_t, bh);
+        pm[i] = __builtin_bit_cast(uint16_t, bm);
+        pl[i] = __builtin_bit_cast(uint16_t, bl);
+    }
+    h = make_uint2(ph[0] | ((uint32_t)ph[1] << 16), ph[2] | ((uint32_t)ph[3] << 16));
+    m = make_uint2(pm[0] | ((uint32_t)pm[1] << 16), pm[2] | ((uint32_t)pm[3] << 16));
+    l = make_uint2(pl[0] | ((uint32_t)pl[1] << 16), pl[2] | ((uint32_t)pl[3] << 16));
+}
 
 __global__ __launch_bounds__(256) void router_logits_mfma_kernel(const float* __restrict__ x,
                                                                  const float* __restrict__ wg, int T, int d,
                                                                  int E, int kslice, float* __restrict__ L,
                                                                  const float* __restrict__ sg,
                                                                  float* __restrict__ sgl) {
-    __shared__ __attribute__((aligned(16))) float xs[kRBM * kRPad];
-    __shared__ __attribute__((aligned(16))) float wsh[kRBN * kRPad];
+    // [part][row][k], parts h, m, l
+    __shared__ __attribute__((aligned(16))) uint16_t xs[3][kRBM * kRPad];
+    __shared__ __attribute__((aligned(16))) uint16_t wsh[3][kRBN * kRPad];
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int wm = wave & 1, wn = wave >> 1;
-    const int tb = blockIdx.y * kRBM, eb = blockIdx.x * kRBN;
-    const int ks = blockIdx.z;
+    // XCD-aware order (blocks go to the 8 XCDs in turn by linear id): every
+    // (expert tile, slice) block of one token tile runs on the same XCD, so
+    // the token rows come into that XCD's L2 once. The grid's token-tile
+    // count is padded to a multiple of 8; padding tiles exit here.
+    const int ncol = gridDim.x * gridDim.z;
+    const int lin = blockIdx.x + gridDim.x * (blockIdx.y + gridDim.y * blockIdx.z);
+    const int sl = lin >> 3, col = sl % ncol;
+    const int tb = ((sl / ncol) * 8 + (lin & 7)) * kRBM;
+    if (tb >= T) return;
+    const int eb = (col % gridDim.x) * kRBN;
+    const int ks = col / gridDim.x;
     const int kbeg = ks * kslice, kend = min(d, kbeg + kslice);
     // loads: rows lr + 32 j, k quad lq of each chunk
     const int lr = tid >> 3, lq = (tid & 7) * 4;
@@ -283,42 +325,78 @@ __global__ __launch_bounds__(256) void router_logits_mfma_kernel(const float* __
         for (int j = 0; j < kRBN / 32; ++j)
             wr[j] = ok ? *reinterpret_cast<const float4*>(wsrc[j] + k0) : make_float4(0.f, 0.f, 0.f, 0.f);
     };
-    const int row = lane & 31, h = lane >> 5;
-    v16f acc[2] = {};
+    // operand rows of this lane: tokens 64 wm + 16 i + (lane % 16), experts
+    // 32 wn + 16 j + (lane % 16); k 8 (lane / 16) .. + 7 of the chunk
+    const int orow = lane & 15, ok8 = (lane >> 4) * 8;
+    v4f acc[4][2];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
     if (kbeg < kend) gload(kbeg);
     for (int k0 = kbeg; k0 < kend; k0 += kRKC) {
         __syncthreads();   // the previous chunk's readers are done
 #pragma unroll
-        for (int j = 0; j < kRBM / 32; ++j) *reinterpret_cast<float4*>(&xs[(lr + 32 * j) * kRPad + lq]) = xr[j];
+        for (int j = 0; j < kRBM / 32; ++j) {
+            uint2 h, m, l;
+            split3_bf16(xr[j], h, m, l);
+            const int o = (lr + 32 * j) * kRPad + lq;
+            *reinterpret_cast<uint2*>(&xs[0][o]) = h;
+            *reinterpret_cast<uint2*>(&xs[1][o]) = m;
+            *reinterpret_cast<uint2*>(&xs[2][o]) = l;
+        }
 #pragma unroll
-        for (int j = 0; j < kRBN / 32; ++j) *reinterpret_cast<float4*>(&wsh[(lr + 32 * j) * kRPad + lq]) = wr[j];
+        for (int j = 0; j < kRBN / 32; ++j) {
+            uint2 h, m, l;
+            split3_bf16(wr[j], h, m, l);
+            const int o = (lr + 32 * j) * kRPad + lq;
+            *reinterpret_cast<uint2*>(&wsh[0][o]) = h;
+            *reinterpret_cast<uint2*>(&wsh[1][o]) = m;
+            *reinterpret_cast<uint2*>(&wsh[2][o]) = l;
+        }
         __syncthreads();
         if (k0 + kRKC < kend) gload(k0 + kRKC);
         __builtin_amdgcn_sched_barrier(0);
+        v8bf b[2][3];
 #pragma unroll
-        for (int s = 0; s < kRKC / 8; ++s) {
-            const float4 b = *reinterpret_cast<const float4*>(&wsh[(32 * wn + row) * kRPad + 8 * s + 4 * h]);
+        for (int j = 0; j < 2; ++j)
 #pragma unroll
-            for (int i = 0; i < 2; ++i) {
-                const float4 a = *reinterpret_cast<const float4*>(&xs[(64 * wm + 32 * i + row) * kRPad + 8 * s + 4 * h]);
-                acc[i] = __builtin_amdgcn_mfma_f32_32x32x2f32(a.x, b.x, acc[i], 0, 0, 0);
-                acc[i] = __builtin_amdgcn_mfma_f32_32x32x2f32(a.y, b.y, acc[i], 0, 0, 0);
-                acc[i] = __builtin_amdgcn_mfma_f32_32x32x2f32(a.z, b.z, acc[i], 0, 0, 0);
-                acc[i] = __builtin_amdgcn_mfma_f32_32x32x2f32(a.w, b.w, acc[i], 0, 0, 0);
+            for (int p = 0; p < 3; ++p)
+                b[j][p] = __builtin_bit_cast(v8bf, *reinterpret_cast<const uint4*>(
+                                                        &wsh[p][(32 * wn + 16 * j + orow) * kRPad + ok8]));
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            v8bf a[3];
+#pragma unroll
+            for (int p = 0; p < 3; ++p)
+                a[p] = __builtin_bit_cast(v8bf, *reinterpret_cast<const uint4*>(
+                                                    &xs[p][(64 * wm + 16 * i + orow) * kRPad + ok8]));
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+                // the small terms first
+                acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[1], b[j][1], acc[i][j], 0, 0, 0);
+                acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[0], b[j][2], acc[i][j], 0, 0, 0);
+                acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[2], b[j][0], acc[i][j], 0, 0, 0);
+                acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[0], b[j][1], acc[i][j], 0, 0, 0);
+                acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[1], b[j][0], acc[i][j], 0, 0, 0);
+                acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[0], b[j][0], acc[i][j], 0, 0, 0);
             }
         }
     }
     float* out = L + (size_t)ks * T * E;
-    const int e = eb + 32 * wn + row;
-    const bool is_sg = sg != nullptr && e == E;
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int j = 0; j < 2; ++j) {
+        const int e = eb + 32 * wn + 16 * j + orow;
+        const bool is_sg = sg != nullptr && e == E;
 #pragma unroll
-        for (int q = 0; q < 16; ++q) {
-            const int t = tb + 64 * wm + 32 * i + 8 * (q >> 2) + 4 * h + (q & 3);
-            if (t < T && e < E) out[(size_t)t * E + e] = acc[i][q];
-            if (t < T && is_sg) sgl[(size_t)ks * T + t] = acc[i][q];
-        }
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int t = tb + 64 * wm + 16 * i + 4 * (lane >> 4) + r;
+                if (t < T && e < E) out[(size_t)t * E + e] = acc[i][j][r];
+                if (t < T && is_sg) sgl[(size_t)ks * T + t] = acc[i][j][r];
+            }
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -379,7 +457,7 @@ hipError_t launch_router_logits(const float* x, int T, int d, const float* wg, i
     }
     // larger T: the preparation is the caller's own launch (launch_xprep)
     const int kslice = router_kslice(d, S);
-    const dim3 grid((rows + kRBN - 1) / kRBN, (T + kRBM - 1) / kRBM, S);
+    const dim3 grid((rows + kRBN - 1) / kRBN, ((T + kRBM - 1) / kRBM + 7) / 8 * 8, S);
     hipLaunchKernelGGL(router_logits_mfma_kernel, grid, dim3(256), 0, st, x, wg, T, d, E, kslice, logits, sg, sgl);
     return hipGetLastError();
 }
