@@ -365,11 +365,12 @@ def test_layer_deterministic(act_mode):
 
 
 @pytest.mark.parametrize("act_mode", ["f32", "q8_0"])
-def test_expert_ffn_and_combine_pieces(act_mode):
+@pytest.mark.parametrize("variant", ["tiny_wide", "tiny_int4_row_wide", "tiny_int2_row"])
+def test_expert_ffn_and_combine_pieces(act_mode, variant):
     """moe_route -> moe_dispatch -> moe_expert_ffn -> moe_combine against the oracle's
     y_perm and out (routed only)."""
     need_gpu()
-    shape, dl = tiny_layer("tiny_wide")
+    shape, dl = tiny_layer(variant)
     T = 41
     x = synth.activations(shape, T)
     ref = oracle_layer(synth.variant(shape, shared_expert=False), x, act_mode, name=shape)
@@ -483,12 +484,14 @@ def test_layer_full_size(wname):
 
 
 @pytest.mark.parametrize("act_mode", ["f32", "q8_0"])
-def test_layer_hip_graph_replay(act_mode):
+@pytest.mark.parametrize("variant,T", [("tiny_shared_noaux", 67), ("tiny_gated", 1100)])
+def test_layer_hip_graph_replay(act_mode, variant, T):
     """The layer captured in a HIP graph: every replay, with eager work and
-    synchronisation between replays, equals the eager result bit for bit."""
+    synchronisation between replays, equals the eager result bit for bit.
+    1100 tokens x top-2 take the multi-block dispatch and the tiled router
+    (with the shared-expert gate row)."""
     need_gpu()
-    shape, dl = tiny_layer("tiny_shared_noaux")
-    T = 67
+    shape, dl = tiny_layer(variant)
     x = torch.from_numpy(synth.activations(shape, T)).cuda()
     am = qe.ACT_MODES[act_mode]
     ws = qe.workspace(T, shape.top_k, shape.n_experts, shape.d_model, shape.d_ff, am, True)
