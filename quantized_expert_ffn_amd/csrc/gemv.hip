@@ -461,12 +461,15 @@ __global__ __launch_bounds__(64 * KS) void gemv_kernel(const GemvArgs a) {
     }
 }
 
-// K-split per block: double it while the grid stays within ~12 waves per CU
-// (what fits at this kernel's register use) and every wave keeps at least two
-// pairs of groups
-static int choose_ks(int slots, int blocks_x, int P) {
+// K-split per block: double it while the grid stays within a wave budget and
+// every wave keeps at least two pairs of groups. The budgets were measured:
+// the f32 path is fastest at ~6 waves per CU (more waves thrash the caches
+// between the activation parts and the code streams), the Q8_0 path, which
+// reads half the activation bytes, at ~4 times that.
+static int choose_ks(int slots, int blocks_x, int P, bool q8) {
+    const long budget = q8 ? 12288 : 3072;   // waves x 2
     int ks = 1;
-    while (ks < 8 && (long)slots * blocks_x * 2 * ks <= 3072 && P >= 4 * ks) ks *= 2;
+    while (ks < 8 && (long)slots * blocks_x * 2 * ks <= budget && P >= 4 * ks) ks *= 2;
     return ks;
 }
 
@@ -507,7 +510,7 @@ hipError_t launch_gemv(const moe_experts& routed, const moe_experts* shared, boo
     a.y = y;
     const int tiles = a.N / kTile;
     const int bx = gateup ? tiles : (tiles + 1) / 2;
-    const int ks = choose_ks(max_slots, bx, a.K / (2 * kGroup));
+    const int ks = choose_ks(max_slots, bx, a.K / (2 * kGroup), q8);
     const dim3 grid(bx, max_slots);
 #define MOE_GEMV(FMT, RW, GU, KSV)                                                                        \
     do {                                                                                                  \
