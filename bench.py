@@ -215,6 +215,21 @@ def main():
               flush=True)
     ms_per_step = elapsed * 1e3 / args.steps
 
+    # (3) the per-step spread: the same steps once more, each between two
+    # events on the launch stream (not part of the timed region above)
+    step_evs = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+    torch.cuda.synchronize(dev)
+    step_evs[0].record()
+    for i in range(args.steps):
+        if args.no_graph:
+            step(args.warmup + i)
+        else:
+            graphs[i % copies].replay()
+        step_evs[i + 1].record()
+    torch.cuda.synchronize(dev)
+    per_step = np.array([step_evs[i].elapsed_time(step_evs[i + 1]) * 1e3 for i in range(args.steps)])
+    step_pct = {q: round(float(np.percentile(per_step, v)), 2) for q, v in (("p10", 10), ("p50", 50), ("p90", 90))}
+
     # the routing of this batch (identical every step): distinct experts for the byte count
     idx = torch.empty((T, shape.top_k), dtype=torch.int32, device=dev)
     wts = torch.empty((T, shape.top_k), dtype=torch.float32, device=dev)
@@ -252,8 +267,12 @@ def main():
         achieved = ops / (kernel_ms * 1e-3) / 1e12
         # the integer codes are multiplied on the f16 matrix cores (exactly), so
         # the peak of that unit bounds the kernel; the int8 figure is given too
+        # attainable = min(int8 peak, the kernel's intensity x HBM peak)
+        kbytes = acc.gateup_kernel_bytes(counts_h, T, shape.top_k, d, I, fmt, shape.shared_expert, wl.act_mode)
+        attainable = min(INT8_PEAK_TOPS, ops / kbytes * HBM_PEAK_GBS / 1e3)
         roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": F16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                "frac": round(achieved / F16_PEAK_TFLOPS, 4), "frac_of_int8_peak": round(achieved / INT8_PEAK_TOPS, 4)}
+                "frac": round(achieved / F16_PEAK_TFLOPS, 4), "frac_of_int8_peak": round(achieved / INT8_PEAK_TOPS, 4),
+                "attainable_int8": round(attainable, 1), "frac_of_attainable": round(achieved / attainable, 4)}
         kkey = f"{kname}_{wl.name}"
     roof["kernel"] = kkey
     roof["traffic"] = measured_traffic(kkey, kernel_sources)
@@ -280,6 +299,7 @@ def main():
                    "top_p": wl.top_p or shape.top_p, "block": wl.block, "device_copies": copies},
         "roofline": roof,
         "timing": {"launch": "eager" if args.no_graph else "hip_graph",
+                   "step_us": step_pct,
                    "eager_ms_per_step": round(eager_elapsed * 1e3 / args.steps, 5),
                    "kernel_timing": "HIP events attached to the gate/up kernel dispatch (hipExtLaunchKernel), "
                                     "mean over the eager steps",
