@@ -7,12 +7,12 @@
  *     section "Mixture-of-Experts": each token runs only its top-k experts
  *     (OLMoE: top 8 of 64 per layer), chosen by a softmax router.
  *   - "Show HN: Getting GLM-5.2 running on my slow computer" (note.crab.center),
- *     section "What's implemented": a DeepSeek-V3-style sigmoid router
- *     (noaux_tc, routed_scaling_factor) and a shared expert; int8 / packed
- *     int4 weights dequantised on use; Q8_0-style int8 activations with
- *     integer dot products, used in batch while a single row stays in f32;
- *     batch-union MoE, where each distinct expert of a batch is read once
- *     and applied to every position routed to it.
+ *     section "What's implemented": a sigmoid router of the DeepSeek-V3 kind
+ *     (noaux_tc selection, a routed scaling factor) and a shared expert; int8
+ *     and packed int4 weights dequantised on use; batches take integer dot
+ *     products on int8 activations quantised the Q8_0 way, while a single
+ *     row keeps f32 activations; batch-union MoE, where a batch loads every
+ *     expert it selects one time, for all of the positions that chose it.
  *   - "mtlm-7m-base" (huggingface.co), section "Files": int8 weights with a
  *     scale per group of 32; "What is and is not machin": SwiGLU with SiLU.
  *
@@ -81,7 +81,7 @@ extern "C" {
 typedef enum {
     MOE_OK = 0,
     MOE_ERR_INVALID_ARG = -1,   /* null pointer, negative size, inconsistent shapes */
-    MOE_ERR_UNSUPPORTED = -2,   /* a valid request this build does not run */
+    MOE_ERR_UNSUPPORTED = -2,   /* a valid request the library does not support */
     MOE_ERR_WORKSPACE = -3,     /* workspace missing or smaller than moe_workspace_size() */
     MOE_ERR_HIP = -4            /* a HIP launch or runtime call failed */
 } moe_status;

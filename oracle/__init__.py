@@ -18,10 +18,11 @@ Sources (the pages; cited by title and section):
     size 32; max abs quantisation error 1.7e-3) and "What is and is not machin"
     (SwiGLU, SiLU; a float64 numpy oracle).
   * "Show HN: Getting GLM-5.2 running on my slow computer" (note.crab.center), section
-    "What's implemented": DeepSeek-V3-style sigmoid router (noaux_tc,
-    routed_scaling_factor), shared expert, Q8_0-style int8 activations with
-    integer dots, int8 / packed int4 weights dequantised on use, batch-union
-    MoE in prefill and verification.
+    "What's implemented": a sigmoid router of the DeepSeek-V3 kind
+    (noaux_tc selection, a routed scaling factor), a shared expert, integer
+    dots on int8 activations quantised the Q8_0 way, int8 and packed int4
+    weights dequantised on use, one read of each selected expert per batch
+    in prefill and verification.
 
 Modules:
   quant     group-32 weight quantiser, int4 packing, Q8_0 activations

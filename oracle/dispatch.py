@@ -2,9 +2,9 @@
 
 TEST INFRASTRUCTURE ONLY (see the package docstring).
 
-Batch-union ("Show HN: Getting GLM-5.2 running on my slow computer", section "What's implemented"): in prefill and
-verification each distinct expert of the batch is read once and applied to
-every position routed to it. That needs the positions grouped by expert.
+Batch-union ("Show HN: Getting GLM-5.2 running on my slow computer", section "What's implemented"): a prefill
+or verification batch loads every expert it selects one time, for all of the
+positions that chose it. That needs the positions grouped by expert.
 
 The routing gives idx [T, k]; assignment f = t*k + j sends token t to expert
 idx[t, j]. The dispatch is:

@@ -9,8 +9,8 @@ implemented": int8 / packed int4, dequantised on use):
     G = X gate^T,  U = X up^T,  H = silu(G) * U,  Y = H down^T
 with silu(g) = g * sigmoid(g).
 
-Two activation modes, after the same page ("integer-dot kernels, Q8_0-style
-int8 activations ... int4 single-row stays f32"):
+Two activation modes, after the same page (batches take integer dots on
+Q8_0-quantised activations, while a single int4 row keeps f32 activations):
   * "f32": activations stay fp32 and meet the dequantised weights s*q. The
     oracle evaluates every product and sum in fp64.
   * "q8_0": activations are Q8_0-quantised per 32 (see oracle.quant). Per

@@ -1,10 +1,9 @@
 // The C ABI of libmoe (declared in include/moe.h): argument validation,
 // workspace carving and kernel sequencing. Every check runs on the host
 // before anything is enqueued, so a rejected call leaves the stream untouched
-// ("Show HN: Getting GLM-5.2 running on my slow computer", section "OpenAI-compatible API": unsupported requests
-// return an explicit error rather than being ignored; section "Experimental
-// resident CUDA backend": a request that cannot run fails instead of silently
-// falling back).
+// ("Show HN: Getting GLM-5.2 running on my slow computer", section "OpenAI-compatible API": a request the
+// server cannot honour gets an error back; section "Experimental resident
+// CUDA backend": a path that cannot run reports it, with no quiet fallback).
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>

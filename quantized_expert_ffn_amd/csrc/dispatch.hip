@@ -1,6 +1,6 @@
 // Dispatch for batch-union MoE ("Show HN: Getting GLM-5.2 running on my slow computer", section "What's
-// implemented": in prefill and verification each distinct expert is read once
-// and applied to every position routed to it).
+// implemented": a prefill or verification batch loads every expert it selects
+// one time, for all of the positions that chose it).
 //
 // All of it runs in one block, in LDS, with no atomics and no host round
 // trip. Small batches (up to kWaveDispatchMax assignments, the decode case)

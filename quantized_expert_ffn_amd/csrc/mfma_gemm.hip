@@ -1,8 +1,9 @@
 // Prefill / verification path: batch-union grouped GEMM with Q8_0
 // activations and exact integer group dots ("Show HN: Getting GLM-5.2
-// running on my slow computer", section "What's implemented": integer-dot
-// kernels with Q8_0-style int8 activations, used in batch; batch-union MoE in
-// prefill and MTP verification).
+// running on my slow computer", section "What's implemented": batches take
+// integer dot products on int8 activations quantised the Q8_0 way, and in
+// prefill as in multi-token verification every selected expert is read once
+// per batch).
 //
 // Each 32-deep quantisation group is one v_mfma_f32_16x16x32_f16 per 16 x 16
 // output tile, fed with the integer codes themselves: activation and weight

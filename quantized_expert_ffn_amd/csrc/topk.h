@@ -3,8 +3,9 @@
 // Softmax top-k: "I ran a 7B Mixture-of-Experts LLM in a language I built"
 // (dev.to), section "Mixture-of-Experts" (each token goes to its top 8 of 64
 // experts). Sigmoid noaux_tc: "Show HN: Getting GLM-5.2 running on my slow
-// computer", section "What's implemented" (DeepSeek-V3-style sigmoid router,
-// noaux_tc, routed_scaling_factor); its steps are the DeepSeek-V3 ones:
+// computer", section "What's implemented" (a sigmoid router of the
+// DeepSeek-V3 kind: noaux_tc selection and a routed scaling factor); its
+// steps are the DeepSeek-V3 ones:
 // sigmoid scores, selection on score + bias, groups ranked by the sum of
 // their two best keys, top-k among the kept groups, weights = the chosen
 // scores normalised to sum 1 and scaled.

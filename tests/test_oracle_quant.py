@@ -16,7 +16,7 @@ import synth
 
 
 def test_int8_g32_error_within_page_bound(golden_dir):
-    # mtlm-7m-base, section Files: int8 group-32 export, max abs error 1.7e-3.
+    # mtlm-7m-base, section Files: the int8 export in groups of 32 reports a largest absolute error of 1.7e-3.
     bound = json.load(open(os.path.join(golden_dir, "page_numbers.json")))["int8_g32_max_abs_error"]["value"]
     w = synth.expert_weight(synth.LAYERS["olmoe"], 0, "gate")
     q, s = quant.quantize_weights(w, 8)
@@ -94,8 +94,8 @@ def test_int4_pack_matches_hand_worked_bytes(golden_dir):
 
 
 def test_int4_unpack_equals_int8_container():
-    # Show HN: Getting GLM-5.2 running on my slow computer, section What's implemented: packing validated
-    # bit-identical to the int8 container. Every byte value round-trips.
+    # Show HN: Getting GLM-5.2 running on my slow computer, section What's implemented: the page checks
+    # that packed codes unpack to exactly the int8 codes. Every byte value round-trips.
     allbytes = np.arange(256, dtype=np.uint8)
     codes = quant.unpack_int4(allbytes)
     assert codes.min() == -8 and codes.max() == 7
@@ -178,7 +178,7 @@ def test_q8_0_bounds_and_zero_group():
 
 def test_page_byte_accounting(golden_dir):
     # Show HN: Getting GLM-5.2 running on my slow computer, section The idea: ~19 MB per routed expert at int4;
-    # section Got a better machine?: ~11.4 GB of expert reads per cold token.
+    # section Got a better machine?: a cold token reads about 11.4 GB of experts.
     pn = json.load(open(os.path.join(golden_dir, "page_numbers.json")))
     glm = synth.LAYERS["glm"]
     payload = 0
