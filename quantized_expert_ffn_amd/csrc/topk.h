@@ -24,10 +24,6 @@ template <int CTRL>
 __device__ __forceinline__ float dppf(float v) {
     return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, true));
 }
-template <int CTRL>
-__device__ __forceinline__ int dppi(int v) {
-    return __builtin_amdgcn_update_dpp(0, v, CTRL, 0xF, 0xF, true);
-}
 
 // Full-wave sum, result in every lane (DPP inside rows of 16, then the four
 // row totals read back as uniform values and added in row order).
@@ -60,31 +56,17 @@ __device__ __forceinline__ bool ranks_before(float ka, int ia, float kb, int ib)
     return ka > kb || (ka == kb && ia < ib);
 }
 
-template <int CTRL>
-__device__ __forceinline__ void argmax_step(float& k, int& id) {
-    const float ok = dppf<CTRL>(k);
-    const int oi = dppi<CTRL>(id);
-    if (ranks_before(ok, oi, k, id)) { k = ok; id = oi; }
-}
-
-// Wave argmax over (key, id); every lane gets the winner.
+// Wave argmax over (key, id); every lane gets the winner. Lanes hold
+// increasing ids (a lane's candidate being its own best, ties to its lower
+// id), so the first lane that holds the largest key holds the winner: one
+// wave max, one ballot and one read, instead of a compare-exchange per step.
 __device__ __forceinline__ void wave_argmax(float& k, int& id) {
-    argmax_step<0xB1>(k, id);
-    argmax_step<0x4E>(k, id);
-    argmax_step<0x141>(k, id);
-    argmax_step<0x140>(k, id);
-    float bk = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(k), 0));
-    int bi = __builtin_amdgcn_readlane(id, 0);
-#pragma unroll
-    for (int r = 16; r < 64; r += 16) {
-        const float rk = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(k), r));
-        const int ri = __builtin_amdgcn_readlane(id, r);
-        if (ranks_before(rk, ri, bk, bi)) { bk = rk; bi = ri; }
-    }
-    // the winner is the same in every lane; say so, so that lane selects
-    // and shifts on it stay scalar
-    k = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(bk)));
-    id = __builtin_amdgcn_readfirstlane(bi);
+    const float m = wave_max_all(k);
+    const uint64_t b = __ballot(k == m);
+    const int src = b ? __builtin_ctzll(b) : 0;   // no lane equal: only NaN keys
+    id = __builtin_amdgcn_readlane(id, src);
+    k = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(m)));
+    id = __builtin_amdgcn_readfirstlane(id);
 }
 
 struct TopkArgs {
