@@ -283,6 +283,7 @@ moe_status layer_forward_impl(const float* x, int32_t T, const float* gate_w, co
     const bool small = moe::router_splits(T, E, d) == 0;
     const bool fused = T <= moe::kFusedRouteT;
     const bool norm = block && norm_w != nullptr;
+    const int S = moe::router_slices(T, E, d, norm && small);   // logits slices
     // the layer's input: x, or RMSNorm(x) (inside the router kernel for small
     // T; larger T normalises once into the workspace)
     const float* xl = x;
@@ -298,7 +299,7 @@ moe_status layer_forward_impl(const float* x, int32_t T, const float* gate_w, co
     MOE_HIP(moe::launch_router_logits(xl, T, d, gate_w, E, logits, xp, (norm && small) ? norm_w : nullptr, eps, sg,
                                       sgl, st),
             "router logits");
-    if (!fused) MOE_HIP(moe::launch_router_topk(logits, T, d, *p, idx, w, st), "router top-k");
+    if (!fused) MOE_HIP(moe::launch_router_topk(logits, T, S, *p, idx, w, st), "router top-k");
     record(ev, 2 * MOE_STAGE_ROUTE + 1, st);
     if (!small) {
         record(ev, 2 * MOE_STAGE_QUANT_X, st);
@@ -307,7 +308,7 @@ moe_status layer_forward_impl(const float* x, int32_t T, const float* gate_w, co
     }
     record(ev, 2 * MOE_STAGE_DISPATCH, st);
     if (fused)
-        MOE_HIP(moe::launch_route_dispatch(logits, T, d, *p, idx, w, ws_at<int>(ws, L.counts),
+        MOE_HIP(moe::launch_route_dispatch(logits, T, S, *p, idx, w, ws_at<int>(ws, L.counts),
                                            ws_at<int>(ws, L.offsets), ws_at<int>(ws, L.perm), inv_perm, has_shared,
                                            ws_at<int>(ws, L.row_token), ws_at<int>(ws, L.slots),
                                            ws_at<int>(ws, L.tiles), ws_at<int>(ws, L.meta), st),
@@ -324,8 +325,7 @@ moe_status layer_forward_impl(const float* x, int32_t T, const float* gate_w, co
                          st)) != MOE_OK)
         return s;
     record(ev, 2 * MOE_STAGE_COMBINE, st);
-    const int S = moe::router_splits(T, E, d);
-    MOE_HIP(moe::launch_combine(y, w, inv_perm, has_shared ? y + (size_t)T * k * d : nullptr, sgl, S > 0 ? S : 1,
+    MOE_HIP(moe::launch_combine(y, w, inv_perm, has_shared ? y + (size_t)T * k * d : nullptr, sgl, S,
                                 block ? x : nullptr, T, k, d, out, st),
             "combine");
     record(ev, 2 * MOE_STAGE_COMBINE + 1, st);
@@ -382,8 +382,7 @@ moe_status moe_route(const float* x, int32_t T, int32_t d, const float* gate_w, 
     if (T == 0) return ok();
     MOE_REQUIRE(x && gate_w && topk_idx && topk_w, MOE_ERR_INVALID_ARG, "NULL tensor argument");
     MOE_REQUIRE(aligned16(x) && aligned16(gate_w), MOE_ERR_INVALID_ARG, "x and gate_w must be 16-byte aligned");
-    const int S = moe::router_splits(T, p->n_experts, d);
-    const size_t need = (size_t)(S > 0 ? S : 1) * T * p->n_experts * sizeof(float);
+    const size_t need = (size_t)moe::router_slices(T, p->n_experts, d, false) * T * p->n_experts * sizeof(float);
     MOE_REQUIRE(ws != nullptr && ws_bytes >= need, MOE_ERR_WORKSPACE, "workspace %zu bytes < %zu needed",
                 ws ? ws_bytes : 0, need);
     MOE_HIP(moe::launch_router(x, T, d, gate_w, *p, static_cast<float*>(ws), topk_idx, topk_w, stream), "router");

@@ -38,7 +38,7 @@ struct WsLayout {
     size_t hp = 0;         //                      F32: f32 powers of two [R, I/32]
     size_t y = 0;          // f32  [R, d]
     size_t xn = 0;         // f32  [T, d]  RMSNorm(x) for the block entry point, T > 16 only
-    size_t sgl = 0;        // f32  [max(S, 1), T]  shared-expert gate logits per d slice (with a shared expert)
+    size_t sgl = 0;        // f32  [S, T]  shared-expert gate logits per d slice (with a shared expert)
     size_t dhist = 0;      // i32  [chunks, E]  multi-block dispatch histograms (T*k > kDispatchWaveMax)
     size_t dbad = 0;       // i32  [chunks]
     size_t total = 0;
@@ -64,6 +64,27 @@ inline int router_splits(int T, int E, int d) {
 // d-slice length: a multiple of 64 (the last slice takes what is left)
 inline int router_kslice(int d, int S) { return ((d + S - 1) / S + 63) / 64 * 64; }
 
+// Router logits leave as S partial sums over slices of d ([S, T, E]; the
+// shared-expert gate logit as [S, T]); the top-k and the combine add them in
+// slice order. T > 16: the matrix-core kernel's router_splits slices;
+// T <= kSmallSplitMinT, or T <= 16 with the RMSNorm fused in: one slice (one
+// block per router row reads whole rows; the norm needs them); other T <= 16:
+// at most kSmallSlicesMax slices of router_small_units units of kSmallUnit
+// values each (split over d, so that no block reads all of X).
+constexpr int kSmallUnit = 256;
+constexpr int kSmallSlicesMax = 8;
+constexpr int kSmallSplitMinT = 4;
+inline int router_small_units(int d) {
+    const int u = (d + kSmallUnit - 1) / kSmallUnit;
+    return (u + kSmallSlicesMax - 1) / kSmallSlicesMax;
+}
+inline int router_slices(int T, int E, int d, bool norm) {
+    if (router_splits(T, E, d) > 0) return router_splits(T, E, d);
+    if (norm || T <= kSmallSplitMinT) return 1;
+    const int u = (d + kSmallUnit - 1) / kSmallUnit, pu = router_small_units(d);
+    return (u + pu - 1) / pu;
+}
+
 inline size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
 
 inline WsLayout ws_layout(int T, int k, int E, int d, int I, int act_mode, int has_shared) {
@@ -75,7 +96,8 @@ inline WsLayout ws_layout(int T, int k, int E, int d, int I, int act_mode, int h
     L.max_tiles = (int)((n + kTileRows - 1) / kTileRows + (size_t)(E < (long long)n ? E : n) +
                         (has_shared ? (T + kTileRows - 1) / kTileRows : 0));
     const int S = router_splits(T, E, d);
-    L.logits = take((size_t)(S > 0 ? S : 1) * T * E * 4);
+    const int SL = router_slices(T, E, d, false);   // the most slices any path writes
+    L.logits = take((size_t)SL * T * E * 4);
     L.idx = take(n * 4);
     L.wts = take(n * 4);
     L.counts = take((size_t)E * 4);
@@ -101,7 +123,7 @@ inline WsLayout ws_layout(int T, int k, int E, int d, int I, int act_mode, int h
     }
     L.y = take(R * d * 4);
     if (S > 0) L.xn = take((size_t)T * d * 4);
-    if (has_shared) L.sgl = take((size_t)(S > 0 ? S : 1) * T * 4);
+    if (has_shared) L.sgl = take((size_t)SL * T * 4);
     if (n > (size_t)kDispatchWaveMax) {
         L.dhist = take((size_t)dispatch_chunk_count((int64_t)n) * E * 4);
         L.dbad = take((size_t)dispatch_chunk_count((int64_t)n) * 4);

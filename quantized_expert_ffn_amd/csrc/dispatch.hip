@@ -208,17 +208,26 @@ __device__ __forceinline__ void dispatch_block(const int* idx, int* tmp, int T, 
     }
 }
 
-// Wave-wide exclusive scan of one value per lane; *total gets the sum.
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ int dpp_or_zero(int v) {
+    return __builtin_amdgcn_update_dpp(0, v, CTRL, ROW_MASK, 0xF, false);
+}
+
+// Wave-wide exclusive scan of one value per lane (all 64 lanes active);
+// *total gets the sum. Inside each row of 16 lanes, shifted copies (row_shr
+// 1, 2, 4, 8; zeros shift in) are added; then the last lane of row 0 (row 2)
+// is broadcast to row 1 (row 3) and the last lane of row 1 to rows 2 and 3
+// (row_bcast 15 and 31, the other rows adding zero).
 __device__ __forceinline__ int wave_exclusive_scan(int v, int* total) {
-    const int lane = threadIdx.x & 63;
-    int incl = v;
-#pragma unroll
-    for (int off = 1; off < kWave; off <<= 1) {
-        const int o = __shfl_up(incl, off, kWave);
-        if (lane >= off) incl += o;
-    }
-    *total = __shfl(incl, kWave - 1, kWave);
-    return incl - v;
+    int x = v;
+    x += dpp_or_zero<0x111, 0xF>(x);   // row_shr:1
+    x += dpp_or_zero<0x112, 0xF>(x);   // row_shr:2
+    x += dpp_or_zero<0x114, 0xF>(x);   // row_shr:4
+    x += dpp_or_zero<0x118, 0xF>(x);   // row_shr:8
+    x += dpp_or_zero<0x142, 0xA>(x);   // row_bcast:15 into rows 1 and 3
+    x += dpp_or_zero<0x143, 0xC>(x);   // row_bcast:31 into rows 2 and 3
+    *total = __builtin_amdgcn_readlane(x, kWave - 1);
+    return x - v;
 }
 
 // The same dispatch by one wave, for small batches (the decode case): no
@@ -562,11 +571,11 @@ size_t route_dispatch_lds_bytes(int T, int k, int E, int mode) {
     return (keybuf + 2 * (size_t)T * k + dispatch_lds_bytes(E) / sizeof(int)) * sizeof(int);
 }
 
-hipError_t launch_route_dispatch(const float* logits, int T, int d, const moe_router_params& p, int* idx, float* w,
+hipError_t launch_route_dispatch(const float* logits, int T, int S, const moe_router_params& p, int* idx, float* w,
                                  int* counts, int* offsets, int* perm, int* inv_perm, int has_shared,
                                  int* row_token, int* slots, int* tiles, int* meta, hipStream_t st) {
     if (T > kDispWaves) return hipErrorInvalidValue;
-    const TopkArgs a = topk_args(logits, T, d, p);
+    const TopkArgs a = topk_args(logits, T, S, p);
     const size_t lds = route_dispatch_lds_bytes(T, p.top_k, p.n_experts, p.mode);
     const int threads = (T > 0 ? T : 1) * kWave;   // one wave per token; wave 0 then dispatches
 #define MOE_RD(EPL)                                                                                              \

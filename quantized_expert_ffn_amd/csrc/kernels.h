@@ -32,14 +32,15 @@ hipError_t launch_router(const float* x, int T, int d, const float* wg, const mo
 // With router_splits(T, E, d) == 0 (small T) the logits kernel also does xp;
 // otherwise xp is ignored and the caller runs launch_xprep. norm_w (small T
 // only, else null): the logits and xp see RMSNorm(x) with gain norm_w and eps.
-// sg (or null): the shared-expert gate vector, whose logit x . sg goes to sgl
-// as max(S, 1) slice sums [S, T] (S = router_splits).
+// The logits leave as S = router_slices(T, E, d, norm_w != null) slice sums
+// [S, T, E]; sg (or null): the shared-expert gate vector, whose logit x . sg
+// goes to sgl as slice sums [S, T].
 hipError_t launch_router_logits(const float* x, int T, int d, const float* wg, int E, float* logits,
                                 const XPrep& xp, const float* norm_w, float eps, const float* sg, float* sgl,
                                 hipStream_t st);
 // RMSNorm of T rows into xn [T, d] (the larger-T path)
 hipError_t launch_rmsnorm(const float* x, int T, int d, const float* norm_w, float eps, float* xn, hipStream_t st);
-hipError_t launch_router_topk(const float* logits, int T, int d, const moe_router_params& p, int* idx, float* w,
+hipError_t launch_router_topk(const float* logits, int T, int S, const moe_router_params& p, int* idx, float* w,
                               hipStream_t st);
 hipError_t launch_xprep(const float* x, int T, int d, const XPrep& xp, hipStream_t st);
 
@@ -47,7 +48,7 @@ hipError_t launch_xprep(const float* x, int T, int d, const XPrep& xp, hipStream
 // routing results never leave LDS between the two.
 constexpr int kFusedRouteT = 16;
 size_t route_dispatch_lds_bytes(int T, int k, int E, int mode);
-hipError_t launch_route_dispatch(const float* logits, int T, int d, const moe_router_params& p, int* idx, float* w,
+hipError_t launch_route_dispatch(const float* logits, int T, int S, const moe_router_params& p, int* idx, float* w,
                                  int* counts, int* offsets, int* perm, int* inv_perm, int has_shared,
                                  int* row_token, int* slots, int* tiles, int* meta, hipStream_t st);
 

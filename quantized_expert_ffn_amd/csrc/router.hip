@@ -208,6 +208,84 @@ __global__ __launch_bounds__(256) void router_logits_gemv_kernel(const float* __
     xprep_waves(x, T, d, xp, blockIdx.x * 4 + wave, gridDim.x * 4);
 }
 
+// ---------------------------------------------------------------------------
+// Logits, small T without a fused norm: fp32 matrix-core products
+// (v_mfma_f32_16x16x4_f32), d cut into slices of PU * kSmallUnit values.
+// Block (r, s) computes router rows 16 r .. 16 r + 15 (the experts, then the
+// shared-expert gate as row E) for every token of slice s: no block reads
+// more of X and of the router weights than its slice. Wave w takes a quarter
+// of the slice in steps of 16 values; in a step lane l (m = l % 16,
+// q = l / 16) holds the four values k = 4 q .. 4 q + 3 of token m (the A
+// operand) and of router row 16 r + m (B), and four products take one value
+// each, so A and B use the same k in every lane. The next four steps' loads
+// are in flight during a group's products. Output lane l, register i: token
+// 4 q + i, row 16 r + m. The four waves' tiles are added in wave order
+// through LDS. With a hidden-state preparation job, nprep more blocks do that
+// job alone, alongside the products (grid: nrb * S product blocks, block b
+// taking rows 16 (b % nrb) .. of slice b / nrb, then the nprep).
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void router_logits_small_kernel(const float* __restrict__ x,
+                                                                  const float* __restrict__ wg, int T, int d, int E,
+                                                                  int PU, int nrb, int S, float* __restrict__ L,
+                                                                  XPrep xp, const float* __restrict__ sg,
+                                                                  float* __restrict__ sgl) {
+    __shared__ float part[4][256];
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int b = blockIdx.x;
+    if (b >= nrb * S) {
+        const int pb = b - nrb * S;
+        xprep_waves(x, T, d, xp, pb * 4 + wave, (gridDim.x - nrb * S) * 4);
+        return;
+    }
+    const int m = lane & 15, q = lane >> 4;
+    const int r0 = (b % nrb) * 16, slice = b / nrb;
+    const int row = r0 + m;
+    const float* wrow = row < E ? wg + (size_t)row * d : (row == E ? sg : nullptr);
+    const float* xrow = x + (size_t)min(m, T - 1) * d;   // rows past T repeat the last (unused)
+    const int steps = 4 * PU;                             // steps of 16 values per wave
+    const int k0 = (slice * 4 + wave) * 16 * steps + 4 * q;
+    auto load4 = [&](int j0, float4 (&xa)[4], float4 (&wb)[4]) __attribute__((always_inline)) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int k = k0 + 16 * (j0 + j);
+            const bool in = j0 + j < steps && k < d;   // d % 4 == 0: a float4 is wholly in or out
+            xa[j] = in ? *reinterpret_cast<const float4*>(xrow + k) : make_float4(0.f, 0.f, 0.f, 0.f);
+            wb[j] = (in && wrow) ? *reinterpret_cast<const float4*>(wrow + k) : make_float4(0.f, 0.f, 0.f, 0.f);
+        }
+    };
+    auto mfma4 = [&](const float4 (&xa)[4], const float4 (&wb)[4], v4f acc) __attribute__((always_inline)) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            acc = __builtin_amdgcn_mfma_f32_16x16x4f32(xa[j].x, wb[j].x, acc, 0, 0, 0);
+            acc = __builtin_amdgcn_mfma_f32_16x16x4f32(xa[j].y, wb[j].y, acc, 0, 0, 0);
+            acc = __builtin_amdgcn_mfma_f32_16x16x4f32(xa[j].z, wb[j].z, acc, 0, 0, 0);
+            acc = __builtin_amdgcn_mfma_f32_16x16x4f32(xa[j].w, wb[j].w, acc, 0, 0, 0);
+        }
+        return acc;
+    };
+    v4f acc = v4f{0.f, 0.f, 0.f, 0.f};
+    float4 xa[4], wb[4], xb[4], wc[4];
+    load4(0, xa, wb);
+    for (int j = 0; j < steps; j += 8) {
+        load4(j + 4, xb, wc);   // zeros past the slice
+        acc = mfma4(xa, wb, acc);
+        if (j + 8 < steps) load4(j + 8, xa, wb);
+        if (j + 4 < steps) acc = mfma4(xb, wc, acc);
+    }
+    *reinterpret_cast<float4*>(&part[wave][lane * 4]) = make_float4(acc[0], acc[1], acc[2], acc[3]);
+    __syncthreads();
+    {
+        // thread o: lane o / 4 of the tiles, register o % 4
+        const int o = threadIdx.x, ol = o >> 2;
+        const int t = 4 * (ol >> 4) + (o & 3), n = r0 + (ol & 15);
+        const float v = (part[0][o] + part[1][o]) + (part[2][o] + part[3][o]);
+        if (t < T) {
+            if (n < E) L[((size_t)slice * T + t) * E + n] = v;
+            else if (n == E && sg) sgl[(size_t)slice * T + t] = v;
+        }
+    }
+}
+
 // RMSNorm of one row per block (the larger-T path writes the normalised rows
 // once; every later stage reads them)
 __global__ __launch_bounds__(256) void rmsnorm_kernel(const float* __restrict__ x, int d,
@@ -418,11 +496,10 @@ __global__ __launch_bounds__(256) void router_topk_kernel(const TopkArgs a, int*
     }
 }
 
-TopkArgs topk_args(const float* logits, int T, int d, const moe_router_params& p) {
-    const int S = router_splits(T, p.n_experts, d);
+TopkArgs topk_args(const float* logits, int T, int S, const moe_router_params& p) {
     TopkArgs a;
     a.L = logits;
-    a.S = S == 0 ? 1 : S;
+    a.S = S;
     a.T = T;
     a.E = p.n_experts;
     a.k = p.top_k;
@@ -442,6 +519,16 @@ hipError_t launch_router_logits(const float* x, int T, int d, const float* wg, i
     if (T == 0) return hipSuccess;
     const int S = router_splits(T, E, d);
     const int rows = E + (sg ? 1 : 0);   // experts, then the shared-expert gate
+    if (S == 0 && !norm_w && T > kSmallSplitMinT) {
+        const int nrb = (rows + 15) / 16, SS = router_slices(T, E, d, false);
+        // preparation blocks: enough waves for one pass over the job
+        const int G = d / kGroup;
+        const int prep_waves = xp.mode == XPREP_SPLIT ? G : xp.mode == XPREP_Q8_0 ? (T * G + 15) / 16 : 0;
+        const int nprep = (prep_waves + 3) / 4;
+        hipLaunchKernelGGL(router_logits_small_kernel, dim3(nrb * SS + nprep), dim3(256), 0, st, x, wg, T, d, E,
+                           router_small_units(d), nrb, SS, logits, xp, sg, sgl);
+        return hipGetLastError();
+    }
     if (S == 0) {
         const dim3 grid(rows);
 #define MOE_RL(TB)                                                                                            \
@@ -476,10 +563,10 @@ hipError_t launch_xprep(const float* x, int T, int d, const XPrep& xp, hipStream
     return hipGetLastError();
 }
 
-hipError_t launch_router_topk(const float* logits, int T, int d, const moe_router_params& p, int* idx, float* w,
+hipError_t launch_router_topk(const float* logits, int T, int S, const moe_router_params& p, int* idx, float* w,
                               hipStream_t st) {
     if (T == 0) return hipSuccess;
-    const TopkArgs a = topk_args(logits, T, d, p);
+    const TopkArgs a = topk_args(logits, T, S, p);
     const dim3 grid((T + 3) / 4);
 #define MOE_TOPK(EPL) hipLaunchKernelGGL(router_topk_kernel<EPL>, grid, dim3(256), 0, st, a, idx, w)
     switch (topk_epl(p.n_experts)) {
@@ -497,7 +584,7 @@ hipError_t launch_router(const float* x, int T, int d, const float* wg, const mo
                          float* logits, int* idx, float* w, hipStream_t st) {
     hipError_t err = launch_router_logits(x, T, d, wg, p.n_experts, logits, XPrep{}, nullptr, 0.0f, nullptr, nullptr, st);
     if (err != hipSuccess) return err;
-    return launch_router_topk(logits, T, d, p, idx, w, st);
+    return launch_router_topk(logits, T, router_slices(T, p.n_experts, d, false), p, idx, w, st);
 }
 
 }  // namespace moe

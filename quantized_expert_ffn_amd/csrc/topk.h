@@ -78,7 +78,8 @@ struct TopkArgs {
     float top_p;         // adaptive expert top-p in (0, 1), or 0 = off
 };
 
-TopkArgs topk_args(const float* logits, int T, int d, const moe_router_params& p);
+// S: the number of partial-sum slices the logits kernel wrote (router_slices)
+TopkArgs topk_args(const float* logits, int T, int S, const moe_router_params& p);
 
 // Top-k of token t by one wave (lane l owns experts l*EPL .. l*EPL+EPL-1).
 // Lane j < k returns slot j's expert and weight. keybuf: E floats of LDS
@@ -100,12 +101,26 @@ __device__ __forceinline__ void topk_token(const TopkArgs& a, int t, bool active
 #pragma unroll
     for (int i = 0; i < EPL; ++i) {
         const int ec = min(lane * EPL + i, E - 1);
-        lv[i] = a.L[(size_t)tc * E + ec];
+        lv[i] = 0.0f;
         bv[i] = a.bias ? a.bias[ec] : 0.0f;
     }
-    for (int s = 1; s < a.S; ++s)
+    // the slices' partial sums, added in slice order; a batch of slices is
+    // loaded before any of it is added, so the loads overlap
+    constexpr int SB = EPL >= 16 ? 2 : EPL >= 8 ? 4 : 8;
+    for (int s0 = 0; s0 < a.S; s0 += SB) {
+        float pv[SB][EPL];
 #pragma unroll
-        for (int i = 0; i < EPL; ++i) lv[i] += a.L[((size_t)s * a.T + tc) * E + min(lane * EPL + i, E - 1)];
+        for (int u = 0; u < SB; ++u) {
+            const int s = min(s0 + u, a.S - 1);
+#pragma unroll
+            for (int i = 0; i < EPL; ++i) pv[u][i] = a.L[((size_t)s * a.T + tc) * E + min(lane * EPL + i, E - 1)];
+        }
+#pragma unroll
+        for (int u = 0; u < SB; ++u)
+            if (s0 + u < a.S)
+#pragma unroll
+                for (int i = 0; i < EPL; ++i) lv[i] = u == 0 && s0 == 0 ? pv[0][i] : lv[i] + pv[u][i];
+    }
 
     float key[EPL], val[EPL];
 #pragma unroll

@@ -173,9 +173,13 @@ def test_route_top_p(mode, top_p):
     say(f"[route] top_p {top_p} {mode}: mean kept slots {kept.mean():.2f} of {lay.top_k}")
 
 
-def test_route_max_experts_and_k():
+@pytest.mark.parametrize("e,k", [(1024, 64), (1024, 8), (128, 6), (100, 7), (40, 40), (512, 16)])
+def test_route_max_experts_and_k(e, k):
+    """Expert counts and k around the selection's limits: 64 lanes of 1..16
+    experts each, k * experts-per-lane candidates up to 128 (ranked) and
+    beyond (arg-max rounds), E not a multiple of 64, k = E."""
     need_gpu()
-    lay = synth.variant(synth.LAYERS["tiny"], n_experts=1024, top_k=64, renormalize=True)
+    lay = synth.variant(synth.LAYERS["tiny"], n_experts=e, top_k=k, renormalize=True)
     x = synth.activations(lay, 37)
     wg = (synth.gate_weight(lay) * 15).astype(np.float32)
     check_route(x, wg, router_spec(lay))
