@@ -15,6 +15,9 @@ namespace moe {
 
 // Grid (column blocks of 256 floats, tokens); one wave per block, one float4
 // column per lane. The token's weights and row indices are uniform loads.
+// Slots go in batches of 8 whose rows are all loaded before the first is
+// added (a dropped slot loads row 0 and adds nothing), so the loads overlap;
+// the sum still runs in slot order.
 __global__ __launch_bounds__(64) void combine_kernel(const float* __restrict__ y, const float* __restrict__ w,
                                                      const int* __restrict__ inv_perm,
                                                      const float* __restrict__ shared_y,
@@ -22,18 +25,38 @@ __global__ __launch_bounds__(64) void combine_kernel(const float* __restrict__ y
                                                      const float* __restrict__ residual, int T, int k, int d,
                                                      float* __restrict__ out) {
     const int t = blockIdx.y;
-    const int c = blockIdx.x * 64 + threadIdx.x;
-    if (t >= T || c >= (d >> 2)) return;
+    const int c0 = blockIdx.x * 64 + threadIdx.x;
+    if (t >= T) return;
+    // lanes past the row's end take part in the slot loads (all 64 lanes are
+    // needed there) and store nothing
+    const bool col_in = c0 < (d >> 2);
+    const int c = col_in ? c0 : 0;
     float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-    for (int j = 0; j < k; ++j) {
-        const float wj = w[(size_t)t * k + j];
-        const int row = inv_perm[(size_t)t * k + j];
-        if (row < 0) continue;   // a slot dropped by top-p (uniform across the block)
-        const float4 v = reinterpret_cast<const float4*>(y + (size_t)row * d)[c];
-        acc.x = fmaf(wj, v.x, acc.x);
-        acc.y = fmaf(wj, v.y, acc.y);
-        acc.z = fmaf(wj, v.z, acc.z);
-        acc.w = fmaf(wj, v.w, acc.w);
+    constexpr int kB = 8;
+    for (int j0 = 0; j0 < k; j0 += kB) {
+        // lane u < kB fetches slot j0 + u's row and weight (clamped index),
+        // then every lane reads them from lane u: one load each for the batch
+        const int jl = min(j0 + (int)(threadIdx.x % kB), k - 1);
+        const int rl = inv_perm[(size_t)t * k + jl];   // -1: dropped by top-p
+        const float wl = w[(size_t)t * k + jl];
+        float4 v[kB];
+        float wv[kB];
+        bool use[kB];
+#pragma unroll
+        for (int u = 0; u < kB; ++u) {
+            const int row = __builtin_amdgcn_readlane(rl, u);
+            use[u] = j0 + u < k && row >= 0;
+            wv[u] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wl), u));
+            v[u] = reinterpret_cast<const float4*>(y + (size_t)(use[u] ? row : 0) * d)[c];
+        }
+#pragma unroll
+        for (int u = 0; u < kB; ++u) {
+            if (!use[u]) continue;   // uniform across the block
+            acc.x = fmaf(wv[u], v[u].x, acc.x);
+            acc.y = fmaf(wv[u], v[u].y, acc.y);
+            acc.z = fmaf(wv[u], v[u].z, acc.z);
+            acc.w = fmaf(wv[u], v[u].w, acc.w);
+        }
     }
     if (shared_y) {
         const float4 s = reinterpret_cast<const float4*>(shared_y + (size_t)t * d)[c];
@@ -60,7 +83,7 @@ __global__ __launch_bounds__(64) void combine_kernel(const float* __restrict__ y
         acc.z += r.z;
         acc.w += r.w;
     }
-    reinterpret_cast<float4*>(out + (size_t)t * d)[c] = acc;
+    if (col_in) reinterpret_cast<float4*>(out + (size_t)t * d)[c] = acc;
 }
 
 hipError_t launch_combine(const float* y, const float* w, const int* inv_perm, const float* shared_y,
