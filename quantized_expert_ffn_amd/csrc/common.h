@@ -46,6 +46,11 @@ struct WsLayout {
 };
 
 constexpr int kTileRows = 128;        // rows (tokens) per prefill matrix-core tile
+// Cache policy of a buffer load (its last argument) for data read once per
+// call, such as the decode path's weight codes and scales: non-temporal. On a
+// 2 GiB stream of 16-byte buffer loads this policy read at ~7.0 TB/s against
+// ~6.1 TB/s for the default one.
+constexpr int kStreamed = 2;
 constexpr int kDispatchWaveMax = 2048;   // assignments a single-wave dispatch takes
 constexpr int kDispatchChunk = 1024;     // assignments per block of the multi-block dispatch
 inline int dispatch_chunk_count(int64_t n) { return (int)((n + kDispatchChunk - 1) / kDispatchChunk); }

@@ -88,6 +88,11 @@ template <int FMT, bool GATEUP, int KS, bool Q8, bool ROW>
 __global__ __launch_bounds__(64 * KS) void gemv_kernel(const GemvArgs a) {
     // 16-byte code loads per tile per pair (int2: one per two pairs)
     constexpr int kCL = FMT == MOE_W_INT8_G32 ? 2 : 1;
+    // cache policy of the code loads: non-temporal where it measured faster
+    // (one wave per tile, or Q8_0 activations: OLMoE int8 / int4 at 16 tokens
+    // and GLM verification gained 5-10%); the f32 path's K-split waves at one
+    // token measured ~3% slower with it, so they keep the default policy
+    constexpr int kCodePolicy = (Q8 || KS == 1) ? kStreamed : 0;
     constexpr bool I2 = FMT == MOE_W_INT2_G32;
     __shared__ float pwtab[Q8 ? 16 * kMaxGemvGroups : kMaxGemvGroups];   // Q8: [group][16 rows]
     __shared__ float red[KS > 1 ? KS - 1 : 1][2][2][4][64];
@@ -108,7 +113,8 @@ __global__ __launch_bounds__(64 * KS) void gemv_kernel(const GemvArgs a) {
 
     // operands through buffer resources: a lane offset per stream, the pair
     // step in a uniform register; offsets past a resource's end read as 0
-    __amdgpu_buffer_rsrc_t rq[2], rs[2];
+    // (rq0: the same codes with no records, every read a zero)
+    __amdgpu_buffer_rsrc_t rq[2], rq0[2], rs[2];
     int q_voff[2], s_voff[2];
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
@@ -116,6 +122,7 @@ __global__ __launch_bounds__(64 * KS) void gemv_kernel(const GemvArgs a) {
         const uint8_t* qbase = (is_shared ? a.sq[m] : a.q[m]) + eo * a.q_stride;
         const float* sbase = (is_shared ? a.ss[m] : a.s[m]) + eo * a.s_stride;
         rq[t] = __builtin_amdgcn_make_buffer_rsrc((void*)qbase, 0, (int)a.q_stride, 0x00020000);
+        rq0[t] = __builtin_amdgcn_make_buffer_rsrc((void*)qbase, 0, 0, 0x00020000);
         rs[t] = __builtin_amdgcn_make_buffer_rsrc((void*)sbase, 0, (int)(a.s_stride * 4), 0x00020000);
         q_voff[t] = tile[t] * 1024 + lane * 16;
         // four consecutive pairs' scale blocks are 1 KB: lane nl + 16q reads
@@ -195,15 +202,21 @@ __global__ __launch_bounds__(64 * KS) void gemv_kernel(const GemvArgs a) {
         // pair j of the run into ring slot sp; rr = j % 4 (a constant at every
         // call: runs start on an even pair and rounds hold four)
         auto load = [&](int sp, int j, int rr) {
-            // past the end: the last pair again (L2-resident), so that every
-            // step issues the same loads and waits stay counted
-            const int p = c0 + (j < n_my ? j : n_my - 1);
+            // past the end of the run every step still issues the same loads,
+            // so that waits stay counted: the activations of the last pair
+            // again (L2-resident), and code loads through a resource with no
+            // records, which return zeros without touching memory (codes
+            // streamed with the non-temporal policy would otherwise be read
+            // from HBM again)
+            const bool past = j >= n_my;
+            const int p = c0 + (past ? n_my - 1 : j);
             if constexpr (I2) {
                 if ((rr & 1) == 0) {
 #pragma unroll
                     for (int t = 0; t < 2; ++t)
                         wq[(rr >> 1) & 1][t][0] = __builtin_bit_cast(
-                            uint4, __builtin_amdgcn_raw_buffer_load_b128(rq[t], q_voff[t], (p >> 1) * n_tiles * 1024, 0));
+                            uint4, __builtin_amdgcn_raw_buffer_load_b128(past ? rq0[t] : rq[t], q_voff[t],
+                                                                         (p >> 1) * n_tiles * 1024, kCodePolicy));
                 }
             } else {
 #pragma unroll
@@ -211,7 +224,8 @@ __global__ __launch_bounds__(64 * KS) void gemv_kernel(const GemvArgs a) {
 #pragma unroll
                     for (int c = 0; c < kCL; ++c)
                         wq[sp][t][c] = __builtin_bit_cast(
-                            uint4, __builtin_amdgcn_raw_buffer_load_b128(rq[t], q_voff[t], (kCL * p + c) * n_tiles * 1024, 0));
+                            uint4, __builtin_amdgcn_raw_buffer_load_b128(past ? rq0[t] : rq[t], q_voff[t],
+                                                                         (kCL * p + c) * n_tiles * 1024, kCodePolicy));
             }
 #pragma unroll
             for (int gi = 0; gi < 2; ++gi) {
