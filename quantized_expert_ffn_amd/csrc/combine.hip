@@ -13,6 +13,8 @@
 
 namespace moe {
 
+typedef float v4f_t __attribute__((ext_vector_type(4)));
+
 // Grid (column blocks of 256 floats, tokens); one wave per block, one float4
 // column per lane. The token's weights and row indices are uniform loads.
 // Slots go in batches of 8 whose rows are all loaded before the first is
@@ -47,7 +49,9 @@ __global__ __launch_bounds__(64) void combine_kernel(const float* __restrict__ y
             const int row = __builtin_amdgcn_readlane(rl, u);
             use[u] = j0 + u < k && row >= 0;
             wv[u] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wl), u));
-            v[u] = reinterpret_cast<const float4*>(y + (size_t)(use[u] ? row : 0) * d)[c];
+            // expert outputs are read once: non-temporal loads
+            const v4f_t nv = __builtin_nontemporal_load(reinterpret_cast<const v4f_t*>(y + (size_t)(use[u] ? row : 0) * d) + c);
+            v[u] = make_float4(nv[0], nv[1], nv[2], nv[3]);
         }
 #pragma unroll
         for (int u = 0; u < kB; ++u) {
