@@ -55,13 +55,13 @@ constexpr int kDispatchWaveMax = 2048;   // assignments a single-wave dispatch t
 constexpr int kDispatchChunk = 1024;     // assignments per block of the multi-block dispatch
 inline int dispatch_chunk_count(int64_t n) { return (int)((n + kDispatchChunk - 1) / kDispatchChunk); }
 
-// Router logits: 0 = one block per expert (small T); S >= 1 = fp32 matrix-core
-// tiles of 128 tokens x 64 experts with d cut into S slices, enough to give
-// ~512 blocks.
+// Router logits: 0 = the small-T kernels; S >= 1 = matrix-core tiles of 128
+// tokens x 64 experts with d cut into S slices, enough to give ~1024 blocks
+// (measured on Qwen prefill: 512, 1024, 2048 blocks took 110, 100, 109 us).
 inline int router_splits(int T, int E, int d) {
     if (T <= 16) return 0;
     const int tiles = ((T + 127) / 128) * ((E + 63) / 64);
-    int s = (512 + tiles - 1) / tiles;
+    int s = (1024 + tiles - 1) / tiles;
     const int smax = d / 128 > 0 ? d / 128 : 1;
     if (s > smax) s = smax;
     return s < 1 ? 1 : s;
