@@ -32,16 +32,40 @@ namespace moe {
 constexpr int kDispThreads = 1024;
 constexpr int kDispWaves = kDispThreads / kWave;
 
-// Exclusive scan of one value per thread over the whole block. `tmp` holds at
-// least kDispWaves + 1 ints. Returns the exclusive prefix; *total gets the sum.
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ int dpp_or_zero(int v) {
+    return __builtin_amdgcn_update_dpp(0, v, CTRL, ROW_MASK, 0xF, false);
+}
+
+// Wave-wide inclusive scan of one value per lane (all 64 lanes active).
+// Inside each row of 16 lanes, shifted copies (row_shr 1, 2, 4, 8; zeros
+// shift in) are added; then the last lane of row 0 (row 2) is broadcast to
+// row 1 (row 3) and the last lane of row 1 to rows 2 and 3 (row_bcast 15 and
+// 31, the other rows adding zero).
+__device__ __forceinline__ int wave_inclusive_scan(int v) {
+    int x = v;
+    x += dpp_or_zero<0x111, 0xF>(x);   // row_shr:1
+    x += dpp_or_zero<0x112, 0xF>(x);   // row_shr:2
+    x += dpp_or_zero<0x114, 0xF>(x);   // row_shr:4
+    x += dpp_or_zero<0x118, 0xF>(x);   // row_shr:8
+    x += dpp_or_zero<0x142, 0xA>(x);   // row_bcast:15 into rows 1 and 3
+    x += dpp_or_zero<0x143, 0xC>(x);   // row_bcast:31 into rows 2 and 3
+    return x;
+}
+
+// Wave-wide exclusive scan (all 64 lanes active); *total gets the sum.
+__device__ __forceinline__ int wave_exclusive_scan(int v, int* total) {
+    const int x = wave_inclusive_scan(v);
+    *total = __builtin_amdgcn_readlane(x, kWave - 1);
+    return x - v;
+}
+
+// Exclusive scan of one value per thread over the whole block (every thread
+// of the kDispThreads present). `tmp` holds at least kDispWaves + 1 ints.
+// Returns the exclusive prefix; *total gets the sum.
 __device__ __forceinline__ int block_exclusive_scan(int v, int* tmp, int* total) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    int incl = v;
-#pragma unroll
-    for (int off = 1; off < kWave; off <<= 1) {
-        const int o = __shfl_up(incl, off, kWave);
-        if (lane >= off) incl += o;
-    }
+    const int incl = wave_inclusive_scan(v);
     if (lane == kWave - 1) tmp[wave] = incl;
     __syncthreads();
     if (threadIdx.x == 0) {
@@ -208,27 +232,6 @@ __device__ __forceinline__ void dispatch_block(const int* idx, int* tmp, int T, 
     }
 }
 
-template <int CTRL, int ROW_MASK>
-__device__ __forceinline__ int dpp_or_zero(int v) {
-    return __builtin_amdgcn_update_dpp(0, v, CTRL, ROW_MASK, 0xF, false);
-}
-
-// Wave-wide exclusive scan of one value per lane (all 64 lanes active);
-// *total gets the sum. Inside each row of 16 lanes, shifted copies (row_shr
-// 1, 2, 4, 8; zeros shift in) are added; then the last lane of row 0 (row 2)
-// is broadcast to row 1 (row 3) and the last lane of row 1 to rows 2 and 3
-// (row_bcast 15 and 31, the other rows adding zero).
-__device__ __forceinline__ int wave_exclusive_scan(int v, int* total) {
-    int x = v;
-    x += dpp_or_zero<0x111, 0xF>(x);   // row_shr:1
-    x += dpp_or_zero<0x112, 0xF>(x);   // row_shr:2
-    x += dpp_or_zero<0x114, 0xF>(x);   // row_shr:4
-    x += dpp_or_zero<0x118, 0xF>(x);   // row_shr:8
-    x += dpp_or_zero<0x142, 0xA>(x);   // row_bcast:15 into rows 1 and 3
-    x += dpp_or_zero<0x143, 0xC>(x);   // row_bcast:31 into rows 2 and 3
-    *total = __builtin_amdgcn_readlane(x, kWave - 1);
-    return x - v;
-}
 
 // The same dispatch by one wave, for small batches (the decode case): no
 // block barrier anywhere, every LDS access is the wave's own and in order.
