@@ -247,3 +247,125 @@ def test_block_without_norm_is_residual_plus_layer():
     r = layer.block_forward(x, None, 0.0, wg, _spec(lay), lambda e: exps[e], exps[lay.n_experts], "f32")
     base = layer.layer_forward(x, wg, _spec(lay), lambda e: exps[e], exps[lay.n_experts], "f32")
     assert np.array_equal(r["out"], x.astype(np.float64) + base["out"])
+
+
+# ---------------------------------------------------------------------------
+# the Q8_0 path's second half, worked with exact integers
+# ---------------------------------------------------------------------------
+def _round_binary(q, mant_bits: int):
+    """Round a rational to the nearest binary floating-point number with
+    mant_bits significant bits, ties to the even mantissa (IEEE round to
+    nearest in the normal range; the values used here are all normal)."""
+    from fractions import Fraction
+    q = Fraction(q)
+    if q == 0:
+        return Fraction(0)
+    sign = -1 if q < 0 else 1
+    a = abs(q)
+    e = a.numerator.bit_length() - a.denominator.bit_length()
+    if Fraction(2) ** e > a:
+        e -= 1
+    ulp = Fraction(2) ** (e - mant_bits + 1)
+    m = a / ulp
+    whole = m.numerator // m.denominator
+    rest = m - whole
+    if rest > Fraction(1, 2) or (rest == Fraction(1, 2) and whole % 2 == 1):
+        whole += 1
+    return sign * whole * ulp
+
+
+def _rne_int(q) -> int:
+    from fractions import Fraction
+    q = Fraction(q)
+    whole = q.numerator // q.denominator
+    rest = q - whole
+    if rest > Fraction(1, 2) or (rest == Fraction(1, 2) and whole % 2 == 1):
+        whole += 1
+    return whole
+
+
+def _q8_0_exact(row):
+    """Q8_0 of one group of 32 exact rationals in the quantiser's fp32 steps
+    ("Show HN: Getting GLM-5.2 running on my slow computer", section "What's
+    implemented": Q8_0-style int8 activations), each step rounded to fp32 by
+    _round_binary: d = fp32(amax / 127), id = fp32(1 / d), q = rne(fp32(v * id))."""
+    from fractions import Fraction
+    f32 = lambda v: _round_binary(v, 24)  # noqa: E731
+    amax = max(abs(v) for v in row)
+    d = f32(amax / 127)
+    idv = f32(Fraction(1) / d) if d != 0 else Fraction(0)
+    return [max(-127, min(127, _rne_int(f32(v * idv)))) for v in row], d
+
+
+def test_q8_second_half_hand_worked_exact_integers():
+    """d = I = 32, two tokens, one int8 expert with dyadic weights chosen by
+    hand. Every quantity of the Q8_0 path is recomputed here with Python
+    integers and exact fractions (no numpy arithmetic): the Q8_0 codes of X,
+    the integer group dots and G, U; H = silu(G) * U taken in fp64 and then
+    rounded to fp32 (silu(G) = G exactly: every G here is either 0 or >= 38,
+    where 1 + e^-G rounds to 1 in fp64); the Q8_0 codes and scale of that fp32
+    H; the down projection's integer dots over those codes and Y = hd * sw * dot.
+    The oracle must reproduce each one bit for bit."""
+    from fractions import Fraction as Fr
+    d = i_ff = 32
+    x = np.zeros((2, d), np.float32)
+    x[0, :3] = [100.0, -37.25, 3.0]      # amax 100: a scale that is no power of two
+    x[1, 3:5] = [50.0, 50.0]
+    # gate row n: code 127 at k = 0 (the group's largest, so the scale is 2^-1),
+    # codes g1 at k = 1 and g3 at k = 3 (g3 = 0 or >= 2 keeps token 1's G at 0 or >= 38)
+    g1 = [(-1) ** n * (7 * n % 120) for n in range(i_ff)]
+    g3 = [0 if n % 5 == 0 else 2 + (11 * n) % 100 for n in range(i_ff)]
+    gate = np.zeros((i_ff, d), np.float32)
+    gate[:, 0] = 127 * 0.5
+    gate[:, 1] = np.array(g1, np.float32) * 0.5
+    gate[:, 3] = np.array(g3, np.float32) * 0.5
+    # up row n: codes on k = 0..4 and the largest code, 127, at k = 31 (where
+    # both tokens are 0), so the scale is 2^-6
+    u_codes = [[(5 * n + 3 * j) % 255 - 127 for j in range(5)] for n in range(i_ff)]
+    up = np.zeros((i_ff, d), np.float32)
+    up[:, :5] = np.array(u_codes, np.float32) * 2.0 ** -6
+    up[:, 31] = 127 * 2.0 ** -6
+    # down row j: scale 2^-(7 + j % 3), codes spread over [-127, 127], 127 at n = j
+    down = np.zeros((d, i_ff), np.float32)
+    for j in range(d):
+        c = [((13 * j + 29 * n) % 255) - 127 for n in range(i_ff)]
+        c[j] = 127
+        down[j] = np.array(c, np.float32) * 2.0 ** -(7 + j % 3)
+    ex = ffn.QuantExpert.from_fp32(gate, up, down, 8)
+    y, parts = ffn.ffn_q8(x, ex)
+
+    f32 = lambda v: _round_binary(v, 24)  # noqa: E731
+    f64 = lambda v: _round_binary(v, 53)  # noqa: E731
+    gq = [[int(round(float(gate[n, k]) * 2)) for k in range(d)] for n in range(i_ff)]
+    uq = [[int(round(float(up[n, k]) * 64)) for k in range(d)] for n in range(i_ff)]
+    dq = [[int(round(float(down[j, n]) * 2 ** (7 + j % 3))) for n in range(i_ff)] for j in range(d)]
+    assert ex.gate_q.tolist() == gq and ex.up_q.tolist() == uq and ex.down_q.tolist() == dq
+    sw_gate, sw_up = Fr(1, 2), Fr(1, 64)
+    sw_down = [Fr(1, 2 ** (7 + j % 3)) for j in range(d)]
+    n_diff_fp32_arith = 0
+    for t in range(2):
+        xq, dx = _q8_0_exact([Fr(float(v)) for v in x[t]])
+        assert parts["xq"][t].tolist() == xq and Fr(float(parts["xd"][t, 0])) == dx
+        h32 = []
+        for n in range(i_ff):
+            dot_g = sum(a * b for a, b in zip(xq, gq[n]))         # integer group dots
+            dot_u = sum(a * b for a, b in zip(xq, uq[n]))
+            G = dx * sw_gate * dot_g                              # exact rationals
+            U = dx * sw_up * dot_u
+            assert G == 0 or G >= 38
+            assert Fr(float(parts["g"][t, n])) == G and Fr(float(parts["u"][t, n])) == U
+            h = f32(f64(G * U))                                   # silu(G) = G; fp64 product, then fp32
+            h32.append(h)
+            assert Fr(float(parts["h32"][t, n])) == h, (t, n)
+            # a quantiser fed H computed in fp32 arithmetic instead would see another value here
+            n_diff_fp32_arith += f32(f32(G) * f32(U)) != h
+        hq, hd = _q8_0_exact(h32)
+        assert parts["hq"][t].tolist() == hq
+        assert parts["hd"].dtype == np.float32 and Fr(float(parts["hd"][t, 0])) == hd
+        for j in range(d):
+            dot_d = sum(a * b for a, b in zip(hq, dq[j]))         # down integer dots over H's codes
+            assert Fr(float(y[t, j])) == hd * sw_down[j] * dot_d, (t, j)
+        # the activation scale in the down projection's place would move Y
+        assert any(dx * sw_down[j] * sum(a * b for a, b in zip(hq, dq[j])) != Fr(float(y[t, j])) for j in range(d))
+    assert n_diff_fp32_arith > 0
+    assert set(g3) >= {0} and parts["h32"].dtype == np.float32
