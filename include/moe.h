@@ -346,10 +346,11 @@ moe_status moe_block_forward(const float* x, int32_t T, const float* norm_w, flo
                              int32_t act_mode, float* out, void* ws, size_t ws_bytes,
                              const hipEvent_t* stage_events, hipStream_t stream);
 
-/* Test hook for the Q8_0 path: runs the production matrix-core kernels
- * of moe_expert_ffn(act_mode = MOE_ACT_Q8_0) and also writes their exact
- * int32 per-group dots and the Q8_0 codes of H. With R = T*k rows in
- * permuted order:
+/* Test hook for the Q8_0 path: runs the kernels moe_expert_ffn(act_mode =
+ * MOE_ACT_Q8_0) runs for the same T (the small-batch GEMV up to 16 tokens,
+ * the tiled matrix-core GEMM above that) and also writes their exact int32
+ * per-group dots and the Q8_0 codes of H. With R = T*k rows in permuted
+ * order:
  *   dots_gate, dots_up  device int32 [R, I, d/32]  sum over a 32-group of
  *                       xq * wq for gate and up
  *   hq, hd              device int8 [R, I], fp32 [R, I/32]  Q8_0 of H
@@ -363,6 +364,43 @@ moe_status moe_debug_q8_expert_ffn(const float* x, int32_t T, int32_t k, const m
                                    const int32_t* perm, int32_t* dots_gate, int32_t* dots_up,
                                    int8_t* hq, float* hd, int32_t* dots_down, float* y_perm,
                                    void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* Test hook: where moe_layer_forward, moe_layer_forward_timed and
+ * moe_block_forward leave their intermediate results inside the workspace
+ * (a buffer of moe_workspace_size(T, k, E, d, d_ff, act_mode, has_shared)
+ * bytes), so that a test can read them back after the call. offsets_out
+ * (host, MOE_WS_SECTION_COUNT entries) receives byte offsets from the start
+ * of the workspace:
+ *   MOE_WS_TOPK_IDX   int32 [T, k]    the router's selection (as moe_route)
+ *   MOE_WS_TOPK_W     fp32  [T, k]    its weights
+ *   MOE_WS_COUNTS     int32 [E]       as moe_dispatch
+ *   MOE_WS_OFFSETS    int32 [E + 1]
+ *   MOE_WS_PERM       int32 [T*k]
+ *   MOE_WS_INV_PERM   int32 [T*k]
+ *   MOE_WS_H_CODES    Q8_0 mode: H's codes as fp16 [R, d_ff] (R = T*k, plus T
+ *                     rows of the shared expert after them), row p of the
+ *                     permuted order; inside each 8-wide slice of a row the
+ *                     codes sit in the operand order of the weight format (for
+ *                     int8: k offsets 0, 2, 1, 3, 4, 6, 5, 7; int4: 0, 4, 1, 5,
+ *                     2, 6, 3, 7; int2: 0 .. 7). -1 in F32 mode.
+ *   MOE_WS_H_SCALES   Q8_0 mode: fp32 [R, d_ff/32], H's Q8_0 scales. -1 in
+ *                     F32 mode.
+ * Returns MOE_ERR_INVALID_ARG for sizes moe_workspace_size rejects.
+ */
+typedef enum {
+    MOE_WS_TOPK_IDX = 0,
+    MOE_WS_TOPK_W = 1,
+    MOE_WS_COUNTS = 2,
+    MOE_WS_OFFSETS = 3,
+    MOE_WS_PERM = 4,
+    MOE_WS_INV_PERM = 5,
+    MOE_WS_H_CODES = 6,
+    MOE_WS_H_SCALES = 7,
+    MOE_WS_SECTION_COUNT = 8
+} moe_ws_section;
+
+moe_status moe_debug_workspace_sections(int32_t T, int32_t k, int32_t E, int32_t d, int32_t d_ff, int32_t act_mode,
+                                        int32_t has_shared, int64_t* offsets_out);
 
 /* Static text for a status code. */
 const char* moe_status_string(moe_status st);

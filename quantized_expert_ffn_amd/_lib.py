@@ -34,6 +34,8 @@ MOE_ACT_F32 = 0
 MOE_ACT_Q8_0 = 1
 
 STAGES = ("route", "dispatch", "quant_x", "gateup", "down", "combine")
+# workspace sections the test hook moe_debug_workspace_sections locates
+WS_SECTIONS = ("topk_idx", "topk_w", "counts", "offsets", "perm", "inv_perm", "h_codes", "h_scales")
 MOE_STAGE_COUNT = len(STAGES)
 
 FORMATS = {"int8": MOE_W_INT8_G32, "int4": MOE_W_INT4_G32, "int2": MOE_W_INT2_G32,
@@ -84,7 +86,10 @@ _SIGNATURES = {
                                  ctypes.POINTER(Experts), ctypes.POINTER(Experts), _I32, _P, _P, _SZ, _P, _P]),
     "moe_debug_q8_expert_ffn": (_I32, [_P, _I32, _I32, ctypes.POINTER(Experts), _P, _P, _P, _P, _P, _P, _P, _P,
                                        _P, _P, _SZ, _P]),
+    "moe_debug_workspace_sections": (_I32, [_I32, _I32, _I32, _I32, _I32, _I32, _I32, _P]),
     "moe_status_string": (ctypes.c_char_p, [_I32]),
+    # include/moe_calib.h: measurement references
+    "moe_calib_stream_read": (_I32, [_P, ctypes.c_uint64, _P, _I32, _P]),
     "moe_last_error_detail": (ctypes.c_char_p, []),
 }
 
@@ -293,6 +298,24 @@ def moe_debug_q8_expert_ffn(x, k, experts: QuantExperts, counts, offsets, perm, 
         _ptr(hq, torch.int8, "hq"), _ptr(hd, torch.float32, "hd"), _ptr(dots_down, torch.int32, "dots_down"),
         _ptr(y_perm, torch.float32, "y_perm"), _ptr(ws, None, "ws"), ws.numel() * ws.element_size(),
         _stream(stream)), "moe_debug_q8_expert_ffn")
+
+
+def moe_debug_workspace_sections(T: int, k: int, E: int, d: int, d_ff: int, act_mode: int,
+                                 has_shared: bool) -> dict:
+    """Byte offsets inside the layer's workspace where moe_layer_forward leaves
+    its routing results and (Q8_0 mode) H's codes and scales: a dict keyed by
+    WS_SECTIONS (-1 for a section the mode does not have)."""
+    arr = (ctypes.c_int64 * len(WS_SECTIONS))()
+    _check(load().moe_debug_workspace_sections(T, k, E, d, d_ff, act_mode, int(bool(has_shared)), arr),
+           "moe_debug_workspace_sections")
+    return dict(zip(WS_SECTIONS, (int(v) for v in arr)))
+
+
+def moe_calib_stream_read(buf: torch.Tensor, sink: torch.Tensor, blocks: int, stream=None) -> None:
+    """Reference streaming read of every byte of buf (include/moe_calib.h);
+    sink: uint32-sized [blocks] device tensor."""
+    _check(load().moe_calib_stream_read(_ptr(buf, None, "buf"), buf.numel() * buf.element_size(),
+                                        _ptr(sink, None, "sink"), blocks, _stream(stream)), "moe_calib_stream_read")
 
 
 def moe_combine(y_perm: torch.Tensor, topk_w: torch.Tensor, inv_perm: torch.Tensor,

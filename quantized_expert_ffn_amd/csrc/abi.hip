@@ -74,7 +74,8 @@ moe_status check_router(const moe_router_params* p, int E_expected) {
     return MOE_OK;
 }
 
-moe_status check_experts(const moe_experts* ex, const char* name, int act_mode) {
+// T: the call's token count (the GEMV paths bound the reduction length)
+moe_status check_experts(const moe_experts* ex, const char* name, int act_mode, int T) {
     MOE_REQUIRE(ex != nullptr, MOE_ERR_INVALID_ARG, "%s experts is NULL", name);
     MOE_REQUIRE(ex->n_experts >= 1, MOE_ERR_INVALID_ARG, "%s n_experts = %d", name, ex->n_experts);
     MOE_REQUIRE(ex->d_model > 0 && ex->d_ff > 0, MOE_ERR_INVALID_ARG, "%s d_model %d / d_ff %d must be > 0", name,
@@ -92,9 +93,12 @@ moe_status check_experts(const moe_experts* ex, const char* name, int act_mode) 
                 "%s weight codes must be 16-byte aligned", name);
     MOE_REQUIRE(aligned16(ex->gate_s) && aligned16(ex->up_s) && aligned16(ex->down_s), MOE_ERR_INVALID_ARG,
                 "%s scales must be 16-byte aligned", name);
-    if (act_mode == MOE_ACT_F32)
+    // the decode GEMV (f32 activations, or Q8_0 up to kGemvMaxT tokens) keeps
+    // one activation scale per group in LDS: K / 32 <= 256 groups
+    if (act_mode == MOE_ACT_F32 || T <= moe::kGemvMaxT)
         MOE_REQUIRE(ex->d_model <= 8192 && ex->d_ff <= 8192, MOE_ERR_UNSUPPORTED,
-                    "%s: the f32 path supports d_model and d_ff up to 8192", name);
+                    "%s: the f32 path, and the Q8_0 path up to %d tokens, support d_model and d_ff up to 8192", name,
+                    moe::kGemvMaxT);
     return MOE_OK;
 }
 
@@ -175,21 +179,22 @@ moe_status run_experts(int T, int k, const moe_experts& routed, const moe_expert
                 "down GEMV");
         return MOE_OK;
     }
-    if (T <= moe::kGemvMaxT && dots_gate == nullptr) {
+    if (T <= moe::kGemvMaxT) {
         // Q8_0 with a handful of tokens (verification): every slot holds at
         // most T <= 16 rows, so the GEMV reads each weight once, with the
-        // same exact integer group dots as the tiled kernel
+        // same exact integer group dots as the tiled kernel (the test hook's
+        // dots come from these same kernels)
         _Float16* xq = ws_at<_Float16>(ws, L.xq);
         float* xd = ws_at<float>(ws, L.xd);
         _Float16* hq = ws_at<_Float16>(ws, L.h);
-        float* hd = ws_at<float>(ws, L.hd);
+        float* hd = hd_out ? hd_out : ws_at<float>(ws, L.hd);
         MOE_HIP(moe::launch_gemv(routed, shared, true, true, xq, nullptr, xd, row_token, T, R, slots, meta, max_slots,
                                  hq, nullptr, hd, nullptr, st, stage_ev(ev, 2 * MOE_STAGE_GATEUP),
-                                 stage_ev(ev, 2 * MOE_STAGE_GATEUP + 1)),
+                                 stage_ev(ev, 2 * MOE_STAGE_GATEUP + 1), dots_gate, dots_up, hq_out),
                 "gate/up GEMV (Q8_0)");
         MOE_HIP(moe::launch_gemv(routed, shared, false, true, hq, nullptr, hd, nullptr, R, R, slots, meta, max_slots,
                                  nullptr, nullptr, nullptr, y, st, stage_ev(ev, 2 * MOE_STAGE_DOWN),
-                                 stage_ev(ev, 2 * MOE_STAGE_DOWN + 1)),
+                                 stage_ev(ev, 2 * MOE_STAGE_DOWN + 1), dots_down, dots_down, nullptr),
                 "down GEMV (Q8_0)");
         return MOE_OK;
     }
@@ -214,7 +219,7 @@ moe_status expert_ffn_impl(const float* x, int32_t T, int32_t k, const moe_exper
                            void* ws, size_t ws_bytes, hipStream_t st) {
     moe_status s;
     if ((s = check_act_mode(act_mode)) != MOE_OK) return s;
-    if ((s = check_experts(ex, "routed", act_mode)) != MOE_OK) return s;
+    if ((s = check_experts(ex, "routed", act_mode, T)) != MOE_OK) return s;
     MOE_REQUIRE(T >= 0, MOE_ERR_INVALID_ARG, "T = %d < 0", T);
     MOE_REQUIRE(k >= 1 && k <= ex->n_experts, MOE_ERR_INVALID_ARG, "k = %d outside [1, %d]", k, ex->n_experts);
     MOE_REQUIRE(ex->n_experts <= moe::kMaxExperts, MOE_ERR_UNSUPPORTED, "n_experts = %d > %d", ex->n_experts,
@@ -245,10 +250,10 @@ moe_status layer_forward_impl(const float* x, int32_t T, const float* gate_w, co
                               const float* norm_w = nullptr, float eps = 0.0f) {
     moe_status s;
     if ((s = check_act_mode(act_mode)) != MOE_OK) return s;
-    if ((s = check_experts(routed, "routed", act_mode)) != MOE_OK) return s;
+    if ((s = check_experts(routed, "routed", act_mode, T)) != MOE_OK) return s;
     if ((s = check_router(p, routed->n_experts)) != MOE_OK) return s;
     if (shared) {
-        if ((s = check_experts(shared, "shared", act_mode)) != MOE_OK) return s;
+        if ((s = check_experts(shared, "shared", act_mode, T)) != MOE_OK) return s;
         MOE_REQUIRE(shared->n_experts == 1, MOE_ERR_INVALID_ARG, "shared expert set must hold 1 expert, not %d",
                     shared->n_experts);
         MOE_REQUIRE(shared->d_model == routed->d_model && shared->d_ff == routed->d_ff &&
@@ -463,6 +468,23 @@ moe_status moe_block_forward(const float* x, int32_t T, const float* norm_w, flo
                              const hipEvent_t* stage_events, hipStream_t stream) {
     return layer_forward_impl(x, T, gate_w, p, routed, shared, act_mode, out, ws, ws_bytes, stage_events, stream, true,
                               norm_w, eps);
+}
+
+moe_status moe_debug_workspace_sections(int32_t T, int32_t k, int32_t E, int32_t d, int32_t d_ff, int32_t act_mode,
+                                        int32_t has_shared, int64_t* offsets_out) {
+    MOE_REQUIRE(offsets_out != nullptr, MOE_ERR_INVALID_ARG, "offsets_out is NULL");
+    MOE_REQUIRE(moe_workspace_size(T, k, E, d, d_ff, act_mode, has_shared) > 0, MOE_ERR_INVALID_ARG,
+                "invalid sizes T = %d, k = %d, E = %d, d = %d, d_ff = %d, act_mode = %d", T, k, E, d, d_ff, act_mode);
+    const moe::WsLayout L = moe::ws_layout(T, k, E, d, d_ff, act_mode, has_shared ? 1 : 0);
+    offsets_out[MOE_WS_TOPK_IDX] = (int64_t)L.idx;
+    offsets_out[MOE_WS_TOPK_W] = (int64_t)L.wts;
+    offsets_out[MOE_WS_COUNTS] = (int64_t)L.counts;
+    offsets_out[MOE_WS_OFFSETS] = (int64_t)L.offsets;
+    offsets_out[MOE_WS_PERM] = (int64_t)L.perm;
+    offsets_out[MOE_WS_INV_PERM] = (int64_t)L.inv_perm;
+    offsets_out[MOE_WS_H_CODES] = act_mode == MOE_ACT_Q8_0 ? (int64_t)L.h : -1;
+    offsets_out[MOE_WS_H_SCALES] = act_mode == MOE_ACT_Q8_0 ? (int64_t)L.hd : -1;
+    return ok();
 }
 
 const char* moe_status_string(moe_status st) {

@@ -557,14 +557,23 @@ __global__ __launch_bounds__(kDispThreads) void plan_kernel(const int* __restric
     }
     if (has_shared)
         for (int t = tid; t < T; t += kDispThreads) row_token[n + t] = t;
-    // a caller's counts / offsets are clamped into [0, T*k) so that rows never
-    // leave the permuted range, whatever they hold
-    int off = tid < E ? offsets[tid] : 0;
-    off = min(max(off, 0), n);
-    int cnt = tid < E ? counts[tid] : 0;
-    cnt = min(max(cnt, 0), n - off);
+    // A caller's counts / offsets are clamped so that every row stays inside
+    // the permuted range [0, T*k) and the counts sum to at most T*k: then
+    // the tiles number at most ceil(T*k / tile_rows) + min(E, T*k) (plus the
+    // shared expert's), the size of the tile list. Counts and offsets that
+    // are not the exclusive prefix sum of each other set the status flag
+    // meta[2] (the results are then unspecified, but every access stays in
+    // bounds).
+    const int off_in = tid < E ? offsets[tid] : 0;
+    const int cnt_in = tid < E ? counts[tid] : 0;
+    const int off = min(max(off_in, 0), n);
+    int cnt = min(max(cnt_in, 0), n - off);
+    int total = 0;
+    const int before = block_exclusive_scan(cnt, scan_tmp, &total);
+    cnt = min(cnt, max(n - before, 0));
+    const int bad = __syncthreads_or(tid < E && (off_in != before || cnt != cnt_in));
     build_work_lists(E, cnt, off, n, T, has_shared, tile_rows, scan_tmp, slots, tiles, meta);
-    if (tid == 0) meta[2] = 0;
+    if (tid == 0) meta[2] = bad;
 }
 
 size_t dispatch_lds_bytes(int E) { return (size_t)(kDispWaves * E + kDispWaves + 1) * sizeof(int); }

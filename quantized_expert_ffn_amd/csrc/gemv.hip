@@ -63,6 +63,12 @@ struct GemvArgs {
     float* hpow;
     // down output
     float* y;               // [R, N]
+    // debug (Q8_0 path only, all or none): the exact group dots [R, N, K/32]
+    // of the first and second matrix (gate, up; down: both tiles to dbg0),
+    // and H's int8 codes in natural order [R, N]
+    int32_t* dbg0;
+    int32_t* dbg1;
+    int8_t* dbg_hq;
 };
 
 constexpr int kMaxGemvGroups = 256;   // K <= 8192
@@ -84,8 +90,12 @@ constexpr int kMaxGemvGroups = 256;   // K <= 8192
 // ROW (a scale per weight row): no scale loads in the loop; only the
 // activation side's per-group factor joins each group's product, and the
 // row's scale multiplies the finished sum once.
-template <int FMT, bool GATEUP, int KS, bool Q8, bool ROW>
+//
+// DBG (Q8 only, the test hook): also writes every exact group dot and H's
+// int8 codes, from the same products the outputs are made of.
+template <int FMT, bool GATEUP, int KS, bool Q8, bool ROW, bool DBG = false>
 __global__ __launch_bounds__(64 * KS) void gemv_kernel(const GemvArgs a) {
+    static_assert(Q8 || !DBG, "group dots exist on the Q8_0 path only");
     // 16-byte code loads per tile per pair (int2: one per two pairs)
     constexpr int kCL = FMT == MOE_W_INT8_G32 ? 2 : 1;
     // cache policy of the code loads: non-temporal where it measured faster
@@ -291,6 +301,20 @@ __global__ __launch_bounds__(64 * KS) void gemv_kernel(const GemvArgs a) {
                     }
                     v4f d0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(xh[jj][gi], b0, v4f{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
                     v4f d1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(xh[jj][gi], b1, v4f{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+                    if constexpr (DBG) {
+                        // rows 4h + i of this 16-row tile, columns nl and 16 + nl of
+                        // weight tile t, group 2p + gi
+                        if (tile[t] < n_tiles) {
+                            int32_t* dst = (GATEUP && t) ? a.dbg1 : a.dbg0;
+#pragma unroll
+                            for (int i = 0; i < 4; ++i) {
+                                if (4 * h + i >= rows_here) continue;
+                                const size_t o = ((size_t)(prow + i) * N + tile[t] * kTile + nl) * G + 2 * p + gi;
+                                dst[o] = (int32_t)d0[i];
+                                dst[o + (size_t)16 * G] = (int32_t)d1[i];
+                            }
+                        }
+                    }
                     if constexpr (Q8 && ROW) {
                         const float4 x = sx[gi];
                         acc[t][0][0] = fmaf(d0[0], x.x, acc[t][0][0]);
@@ -415,6 +439,7 @@ __global__ __launch_bounds__(64 * KS) void gemv_kernel(const GemvArgs a) {
                         const int pos = 8 * (kk >> 3) + k_slot(FMT, kk & 7);
                         const float q = fminf(fmaxf(rintf(__fmul_rn(r ? h1 : h0, inv)), -127.0f), 127.0f);
                         a.hhi[row * N + (size_t)tile[0] * kGroup + pos] = (_Float16)q;
+                        if constexpr (DBG) a.dbg_hq[row * N + (size_t)tile[0] * kGroup + kk] = (int8_t)(int)q;
                     }
                     if (nl == 0) a.hpow[row * GN + tile[0]] = dd;
                 }
@@ -490,8 +515,10 @@ static int choose_ks(int slots, int blocks_x, int P, bool q8) {
 hipError_t launch_gemv(const moe_experts& routed, const moe_experts* shared, bool gateup, bool q8, const _Float16* ahi,
                        const _Float16* alo, const float* apow, const int* row_token, int a_rows, int R,
                        const int* slots, const int* meta, int max_slots, _Float16* hhi, _Float16* hlo, float* hpow,
-                       float* y, hipStream_t st, hipEvent_t ev0, hipEvent_t ev1) {
+                       float* y, hipStream_t st, hipEvent_t ev0, hipEvent_t ev1, int32_t* dbg0, int32_t* dbg1,
+                       int8_t* dbg_hq) {
     if (max_slots == 0) return hipSuccess;
+    if (dbg0 && !q8) return hipErrorInvalidValue;
     GemvArgs a{};
     a.ahi = ahi;
     a.alo = alo;
@@ -522,14 +549,19 @@ hipError_t launch_gemv(const moe_experts& routed, const moe_experts* shared, boo
     a.hlo = hlo;
     a.hpow = hpow;
     a.y = y;
+    a.dbg0 = dbg0;
+    a.dbg1 = dbg1;
+    a.dbg_hq = dbg_hq;
+    const bool dbg = dbg0 != nullptr;
     const int tiles = a.N / kTile;
     const int bx = gateup ? tiles : (tiles + 1) / 2;
     const int ks = choose_ks(max_slots, bx, a.K / (2 * kGroup), q8);
     const dim3 grid(bx, max_slots);
-#define MOE_GEMV(FMT, RW, GU, KSV)                                                                        \
-    do {                                                                                                  \
-        if (q8) launch_timed(gemv_kernel<FMT, GU, KSV, true, RW>, grid, dim3(64 * KSV), st, ev0, ev1, a); \
-        else launch_timed(gemv_kernel<FMT, GU, KSV, false, RW>, grid, dim3(64 * KSV), st, ev0, ev1, a);   \
+#define MOE_GEMV(FMT, RW, GU, KSV)                                                                              \
+    do {                                                                                                        \
+        if (q8 && dbg) launch_timed(gemv_kernel<FMT, GU, KSV, true, RW, true>, grid, dim3(64 * KSV), st, ev0, ev1, a); \
+        else if (q8) launch_timed(gemv_kernel<FMT, GU, KSV, true, RW>, grid, dim3(64 * KSV), st, ev0, ev1, a);  \
+        else launch_timed(gemv_kernel<FMT, GU, KSV, false, RW>, grid, dim3(64 * KSV), st, ev0, ev1, a);         \
     } while (0)
 #define MOE_GEMV_KS(FMT, RW, GU)                \
     if (ks == 1) MOE_GEMV(FMT, RW, GU, 1);      \

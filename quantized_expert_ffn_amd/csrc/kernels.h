@@ -70,12 +70,16 @@ hipError_t launch_plan(const int* counts, const int* offsets, const int* perm, i
 // q8 (small-batch Q8_0 path): A = Q8_0 codes as f16 in slot order with
 // per-row scales in apow ([rows, K/32]); gate/up writes H's Q8_0 codes to hhi
 // and its per-row scales to hpow; alo and hlo are unused. Every slot must
-// hold at most 16 rows for the weights to be read once (T <= 16).
+// hold at most 16 rows for the weights to be read once (T <= 16). The dbg
+// pointers (q8 only; all or none) receive the exact group dots, [R, N, K/32]
+// (gate/up: gate to dbg0, up to dbg1; down: dbg0), and H's int8 codes in
+// natural order [R, N] (gate/up).
 constexpr int kGemvMaxT = 16;   // the Q8_0 path takes the GEMV up to this many tokens
 hipError_t launch_gemv(const moe_experts& routed, const moe_experts* shared, bool gateup, bool q8, const _Float16* ahi,
                        const _Float16* alo, const float* apow, const int* row_token, int a_rows, int R,
                        const int* slots, const int* meta, int max_slots, _Float16* hhi, _Float16* hlo, float* hpow,
-                       float* y, hipStream_t st, hipEvent_t ev_start = nullptr, hipEvent_t ev_stop = nullptr);
+                       float* y, hipStream_t st, hipEvent_t ev_start = nullptr, hipEvent_t ev_stop = nullptr,
+                       int32_t* dbg0 = nullptr, int32_t* dbg1 = nullptr, int8_t* dbg_hq = nullptr);
 
 // Prefill path (Q8_0 activations). gate/up: A = the token rows' Q8_0 codes
 // as f16 in slot order [a_rows = T, d] (read through row_token) + scales

@@ -75,6 +75,17 @@ def build(shape: synth.LayerShape, device="cuda", copies: int = 1, chunk: Option
     return DeviceLayer(shape, gate_w, bias, sg, routed_list, shared_list, params)
 
 
+def add_copies(layer: DeviceLayer, total: int) -> None:
+    """Grow the layer to `total` device copies of its experts (device-to-device
+    clones of the first copy)."""
+    r0, s0 = layer.routed[0], layer.shared[0]
+    while len(layer.routed) < total:
+        layer.routed.append(_lib.QuantExperts(r0.fmt, *(t.clone() for t in (
+            r0.gate_q, r0.gate_s, r0.up_q, r0.up_s, r0.down_q, r0.down_s))))
+        layer.shared.append(None if s0 is None else _lib.QuantExperts(s0.fmt, *(t.clone() for t in (
+            s0.gate_q, s0.gate_s, s0.up_q, s0.up_s, s0.down_q, s0.down_s))))
+
+
 def activations(shape: synth.LayerShape, tokens: int, device="cuda") -> torch.Tensor:
     return torch.from_numpy(synth.activations(shape, tokens)).to(device)
 

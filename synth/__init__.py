@@ -98,9 +98,14 @@ LAYERS = {
                            router="noaux_tc", n_group=8, topk_group=4,
                            routed_scaling_factor=2.5, has_bias=True, shared_expert=True,
                            wformat="int2"),
+    # the 512-expert layer as its configuration states it: one ungated shared expert
     "qwen": LayerShape("qwen", 1005, d_model=2048, n_experts=512, d_ff=512, top_k=10,
-                       router="softmax", renormalize=True, shared_expert=True, shared_gate=True,
+                       router="softmax", renormalize=True, shared_expert=True,
                        wformat="int4", zipf_s=1.1),
+    # the same weights with the shared expert scaled by sigmoid(x . u) per token
+    "qwen_gated": LayerShape("qwen_gated", 1005, d_model=2048, n_experts=512, d_ff=512, top_k=10,
+                             router="softmax", renormalize=True, shared_expert=True, shared_gate=True,
+                             wformat="int4", zipf_s=1.1),
 }
 
 WORKLOADS = {
@@ -112,6 +117,7 @@ WORKLOADS = {
     "glm_b1": Workload("glm_b1", LAYERS["glm"], 1, "f32"),
     "glm_verify4": Workload("glm_verify4", LAYERS["glm"], 4, "q8_0"),
     "qwen_prefill": Workload("qwen_prefill", LAYERS["qwen"], 4096, "q8_0"),
+    "qwen_gated_prefill": Workload("qwen_gated_prefill", LAYERS["qwen_gated"], 4096, "q8_0"),
     # the pages' decode knob: adaptive expert top-p 0.7
     "glm_b1_topp": Workload("glm_b1_topp", LAYERS["glm"], 1, "f32", top_p=0.7),
     "olmoe_b16_topp": Workload("olmoe_b16_topp", LAYERS["olmoe"], 16, "f32", top_p=0.7),

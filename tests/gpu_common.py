@@ -94,3 +94,63 @@ def untile_scales(tiled: np.ndarray, n_rows: int, n_cols: int, fmt: str = "int8"
     nt, g = n_rows // 32, n_cols // 32
     a = flat.reshape(nt, g // 2, 16, 2, 2).transpose(0, 4, 2, 1, 3)   # (tile, half, nl, pair, group of pair)
     return a.reshape(n_rows, g)
+
+
+# operand-slot order of H's codes in the workspace (include/moe.h,
+# MOE_WS_H_CODES): slot j of each 8-wide slice holds k offset SLOT_K[codes][j]
+SLOT_K = {"int8": [0, 2, 1, 3, 4, 6, 5, 7], "int4": [0, 4, 1, 5, 2, 6, 3, 7], "int2": list(range(8))}
+
+
+def workspace_sections(ws: torch.Tensor, T: int, shape, act_mode: str, has_shared: bool):
+    """The routing results (and, in Q8_0 mode, H's codes and scales) a layer
+    call left in its workspace, as numpy arrays."""
+    import quantized_expert_ffn_amd as qe
+    k, E, d, I = shape.top_k, shape.n_experts, shape.d_model, shape.d_ff
+    off = qe.moe_debug_workspace_sections(T, k, E, d, I, qe.ACT_MODES[act_mode], has_shared)
+    raw = ws.detach().cpu().numpy().view(np.uint8)
+
+    def take(name, dtype, count):
+        o = off[name]
+        return raw[o:o + count * np.dtype(dtype).itemsize].view(dtype).copy()
+
+    n = T * k
+    out = dict(idx=take("topk_idx", np.int32, n).reshape(T, k), w=take("topk_w", np.float32, n).reshape(T, k),
+               counts=take("counts", np.int32, E), offsets=take("offsets", np.int32, E + 1),
+               perm=take("perm", np.int32, n), inv_perm=take("inv_perm", np.int32, n))
+    if act_mode == "q8_0":
+        R = n + (T if has_shared else 0)
+        codes = take("h_codes", np.float16, R * I).reshape(R, I // 8, 8)
+        order = SLOT_K[shape.wformat.split("_")[0]]
+        nat = np.empty_like(codes)
+        nat[:, :, order] = codes
+        out["hq"] = nat.reshape(R, I).astype(np.int64)
+        out["hd"] = take("h_scales", np.float32, R * (I // 32)).reshape(R, I // 32)
+    return out
+
+
+def h_code_flips(sec, shape, x, rows, oracle_expert_fn, shared_expert=None):
+    """H's Q8_0 codes the GPU left for the given token rows against the
+    oracle's, per routed slot (and the shared expert): returns (flips, total);
+    asserts that no code differs by more than one step."""
+    from oracle import ffn as offn
+    k = shape.top_k
+    T = sec["idx"].shape[0]
+    flips = total = 0
+    for t in rows:
+        for j in range(k):
+            e = int(sec["idx"][t, j])
+            if e < 0:
+                continue
+            p = int(sec["inv_perm"][t * k + j])
+            _, parts = offn.ffn_q8(x[t:t + 1], oracle_expert_fn(e))
+            diff = sec["hq"][p] - parts["hq"][0].astype(np.int64)
+            assert np.abs(diff).max() <= 1, f"token {t} slot {j}: H code off by {np.abs(diff).max()}"
+            flips += int(np.count_nonzero(diff))
+            total += diff.size
+        if shared_expert is not None:
+            _, parts = offn.ffn_q8(x[t:t + 1], shared_expert)
+            diff = sec["hq"][T * k + t] - parts["hq"][0].astype(np.int64)
+            assert np.abs(diff).max() <= 1, f"token {t} shared expert: H code off by {np.abs(diff).max()}"
+            flips += int(np.count_nonzero(diff))
+            total += diff.size
+    return flips, total

@@ -13,14 +13,15 @@ from conftest import ROOT
 import quantized_expert_ffn_amd as qe
 from quantized_expert_ffn_amd import _lib
 
-HEADER = os.path.join(ROOT, "include", "moe.h")
+HEADERS = sorted(os.path.join(ROOT, "include", f) for f in os.listdir(os.path.join(ROOT, "include"))
+                 if f.endswith(".h"))
 
 OK, INVALID, UNSUPPORTED, WORKSPACE = 0, -1, -2, -3
 FAKE = 0x10000          # an aligned, never dereferenced address
 
 
 def declared_functions():
-    text = open(HEADER).read()
+    text = "\n".join(open(h).read() for h in HEADERS)
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     return sorted(set(re.findall(r"^\s*(?:const\s+)?[\w]+\s*\*?\s*(moe_\w+)\s*\(", text, flags=re.M)))
 
@@ -36,7 +37,7 @@ def test_exports_every_declared_symbol(lib):
     names = declared_functions()
     assert len(names) >= 12
     for n in names:
-        assert hasattr(lib, n), f"{n} declared in moe.h but not exported"
+        assert hasattr(lib, n), f"{n} declared in include/ but not exported"
     assert set(names) == set(_lib.exported_names()), "binding and header disagree"
 
 
@@ -246,3 +247,37 @@ def test_block_forward_validation(lib):
     assert blk(norm=FAKE + 4) == INVALID        # norm_w not 16-byte aligned
     assert lib.moe_block_forward(FAKE, 0, None, ctypes.c_float(0.0), FAKE, ctypes.byref(p), ctypes.byref(e), None, 0,
                                  FAKE, FAKE, 0, None, None) == OK      # T = 0
+
+
+def test_workspace_sections_inside_the_workspace(lib):
+    """The test hook's section offsets: 256-byte aligned, in bounds, the
+    routing sections large enough and disjoint; H's sections only in Q8_0
+    mode; sizes the workspace rejects are rejected too."""
+    for act, shared in ((0, False), (1, False), (1, True)):
+        T, k, E, d, I = 16, 2, 8, 64, 128
+        size = qe.moe_workspace_size(T, k, E, d, I, act, shared)
+        sec = qe.moe_debug_workspace_sections(T, k, E, d, I, act, shared)
+        need = {"topk_idx": T * k * 4, "topk_w": T * k * 4, "counts": E * 4, "offsets": (E + 1) * 4,
+                "perm": T * k * 4, "inv_perm": T * k * 4}
+        if act == 1:
+            R = T * k + (T if shared else 0)
+            need.update(h_codes=R * I * 2, h_scales=R * (I // 32) * 4)
+        else:
+            assert sec["h_codes"] == -1 and sec["h_scales"] == -1
+        spans = sorted((sec[n], sec[n] + b) for n, b in need.items())
+        for (a0, a1), (b0, _) in zip(spans, spans[1:]):
+            assert a1 <= b0
+        assert all(o % 256 == 0 for o, _ in spans) and spans[-1][1] <= size
+    with pytest.raises(qe.MoeError) as e:
+        qe.moe_debug_workspace_sections(16, 9, 8, 64, 128, 0, False)        # k > E
+    assert e.value.status == INVALID
+
+
+def test_calib_stream_read_rejects_bad_arguments(lib):
+    f = lib.moe_calib_stream_read
+    assert f(None, 1 << 20, FAKE, 64, None) == INVALID
+    assert f(FAKE, 1 << 20, None, 64, None) == INVALID
+    assert f(FAKE + 4, 1 << 20, FAKE, 64, None) == INVALID            # unaligned
+    assert f(FAKE, 1000, FAKE, 64, None) == INVALID                   # not a multiple of 16
+    assert f(FAKE, 0, FAKE, 64, None) == INVALID
+    assert f(FAKE, 1 << 20, FAKE, 0, None) == INVALID

@@ -19,8 +19,8 @@ from oracle import layer as olayer
 from oracle import quant as oquant
 from oracle import router as orouter
 
-from gpu_common import (REL_TOL, assert_close_rel, device_layer, need_gpu, oracle_expert, router_spec, say, t2n,
-                        untile_codes, untile_scales)
+from gpu_common import (REL_TOL, assert_close_rel, device_layer, h_code_flips, need_gpu, oracle_expert, router_spec,
+                        say, t2n, untile_codes, untile_scales, workspace_sections)
 
 pytestmark = pytest.mark.gpu
 
@@ -255,7 +255,7 @@ def test_dispatch_empty_and_out_of_range():
 # ---------------------------------------------------------------------------
 # whole layer, small shapes (every output element)
 # ---------------------------------------------------------------------------
-def run_layer(dl, x_np, act_mode, copy=0, timed=False, top_p=None):
+def run_layer(dl, x_np, act_mode, copy=0, timed=False, top_p=None, return_ws=False):
     T = x_np.shape[0]
     lay = dl.shape
     params = dl.params if top_p is None else qe.with_top_p(dl.params, top_p)
@@ -277,6 +277,8 @@ def run_layer(dl, x_np, act_mode, copy=0, timed=False, top_p=None):
         qe.moe_layer_forward(x, dl.gate_w, params, dl.routed[copy], dl.shared[copy], qe.ACT_MODES[act_mode],
                              out, ws)
     torch.cuda.synchronize()
+    if return_ws:
+        return t2n(out), ws
     return t2n(out)
 
 
@@ -286,6 +288,17 @@ def oracle_layer(shape, x, act_mode, name=None, top_p=None):
     wg = synth.gate_weight(shape)
     return olayer.layer_forward(x, wg, router_spec(shape, top_p), lambda e: oracle_expert(key, e), shared,
                                 act_mode)
+
+
+def report_h_flips(ws, shape, x, rows, what, key):
+    """H's Q8_0 codes the layer left in its workspace against the oracle's, for
+    the given tokens: every code within one step, and the count of one-step
+    differences (the fp32 H on the GPU against fp64 in the oracle) reported."""
+    sec = workspace_sections(ws, x.shape[0], shape, "q8_0", shape.shared_expert)
+    shared = oracle_expert(key, shape.n_experts) if shape.shared_expert else None
+    flips, total = h_code_flips(sec, shape, x, rows, lambda e: oracle_expert(key, e), shared)
+    say(f"[q8] {what}: {flips} of {total} H codes differ by one step from the oracle's ({flips / max(total, 1):.2e})")
+    assert flips <= max(2, total // 100)
 
 
 def top_p_settled(shape, x, top_p=None):
@@ -340,11 +353,13 @@ def test_layer_tiny(variant, act_mode):
     # 600 tokens: experts span several 128-row prefill tiles, the last one short
     for T in (16, 1, 67, 600):
         x = synth.activations(shape, T)
-        got = run_layer(dl, x, act_mode)
+        got, ws = run_layer(dl, x, act_mode, return_ws=True)
         ref = oracle_layer(shape, x, act_mode)
         ok = top_p_settled(shape, x)
         assert ok.sum() >= 0.98 * T
         assert_close_rel(got[ok], ref["out"][ok], what=f"{variant}/{act_mode}/T={T} out")
+        if act_mode == "q8_0":
+            report_h_flips(ws, shape, x, np.nonzero(ok)[0], f"{variant}/T={T}", shape)
 
 
 def test_layer_zero_tokens_is_noop():
@@ -401,14 +416,17 @@ def test_expert_ffn_and_combine_pieces(act_mode, variant):
     assert_close_rel(t2n(out), ref["out"], what="out")
 
 
+@pytest.mark.parametrize("T", [29, 1, 4, 16])
 @pytest.mark.parametrize("variant", ["tiny", "tiny_int4", "tiny_wide", "tiny_int4_row_wide", "tiny_int2",
                                      "tiny_int2_row"])
-def test_q8_group_dots_bit_exact(variant):
-    """The production int8-MFMA kernels' exact int32 group dots, Q8_0(H) codes
-    and the down projection's dots fed the GPU's own H codes."""
+def test_q8_group_dots_bit_exact(variant, T):
+    """The production Q8_0 kernels' exact int32 group dots, Q8_0(H) codes
+    and the down projection's dots fed the GPU's own H codes: the tiled
+    matrix-core GEMM above 16 tokens (T = 29), the small-batch GEMV up to 16
+    (T = 1, 4, 16: the verification batches)."""
     need_gpu()
     shape, dl = tiny_layer(variant)
-    T, k, E, d, I = 29, shape.top_k, shape.n_experts, shape.d_model, shape.d_ff
+    k, E, d, I = shape.top_k, shape.n_experts, shape.d_model, shape.d_ff
     x = synth.activations(shape, T)
     ref = oracle_layer(shape, x, "q8_0")
     R = T * k
@@ -443,7 +461,7 @@ def test_q8_group_dots_bit_exact(variant):
         n_diff += int(np.count_nonzero(diff))
         y_ref, _ = offn.ffn_q8(x[toks], ex, hq_override=(hq[lo:hi], hd[lo:hi]))
         assert_close_rel(y[lo:hi], y_ref, what=f"y e={e} (GPU H codes)")
-    say(f"[q8] {variant}: {n_diff} of {hq.size} H codes differ by 1 from the oracle's")
+    say(f"[q8] {variant} T={T}: {n_diff} of {hq.size} H codes differ by 1 from the oracle's")
     assert n_diff <= max(2, hq.size // 100)
 
 
@@ -454,7 +472,7 @@ SAMPLE = 48
 
 
 @pytest.mark.parametrize("wname", ["olmoe_b1", "olmoe_b16", "glm_b1", "glm_verify4", "olmoe_int4_prefill",
-                                   "qwen_prefill", "glm_b1_topp", "olmoe_b16_topp", "olmoe_b16_int4_row",
+                                   "qwen_prefill", "qwen_gated_prefill", "glm_b1_topp", "olmoe_b16_topp", "olmoe_b16_int4_row",
                                    "olmoe_int4_row_prefill", "olmoe_b16_int2", "olmoe_int2_prefill",
                                    "glm_b1_int2"])
 def test_layer_full_size(wname):
@@ -465,7 +483,7 @@ def test_layer_full_size(wname):
     x = synth.activations(shape, wl.tokens)
     say(f"[gpu] {wname}: running the layer on T={wl.tokens}")
     top_p = wl.top_p or None
-    got = run_layer(dl, x, wl.act_mode, top_p=top_p)
+    got, ws = run_layer(dl, x, wl.act_mode, top_p=top_p, return_ws=True)
     rows = np.arange(wl.tokens)
     if wl.tokens > SAMPLE:
         rows = np.sort(np.random.default_rng(5).choice(wl.tokens, SAMPLE, replace=False))
@@ -475,6 +493,8 @@ def test_layer_full_size(wname):
     if top_p:
         say(f"[gpu] {wname}: top-p {top_p} keeps {(ref['idx'] >= 0).sum()} of {ref['idx'].size} slots")
     assert_close_rel(got[rows], ref["out"], what=f"{wname} out")
+    if wl.act_mode == "q8_0":
+        report_h_flips(ws, shape, x, rows, wname, shape.name)
     # the same weights, byte for byte, on both sides (a few experts)
     used = np.unique(ref["idx"][ref["idx"] >= 0])[:3]
     for e in used:
@@ -485,6 +505,67 @@ def test_layer_full_size(wname):
                               ox.stored("down"))
         assert np.array_equal(untile_scales(t2n(dl.routed[0].down_s[e]), shape.d_model, shape.d_ff, shape.wformat),
                               ox.down_s)
+
+
+def check_layer_routing(sec, shape, x, top_p=None):
+    """The routing a layer call left in its workspace against the oracle's:
+    expert ids bit for bit wherever the selection margin exceeds fp32 logit
+    rounding (and top-p keep decisions are settled), weights to fp32
+    rounding, and counts / offsets / perm / inv_perm bit for bit (equal to
+    the oracle's dispatch of the GPU's own ids, and to the oracle's routing
+    where no token is near a tie)."""
+    spec = router_spec(shape, top_p)
+    ri0, rw0, l = olayer.route(x, synth.gate_weight(shape), dataclasses.replace(spec, top_p=0.0))
+    ri, rw = orouter.apply_top_p(ri0, rw0, spec.top_p)
+    keys = orouter.selection_keys(l, spec.mode, spec.bias, spec.n_group, spec.topk_group)
+    margin = orouter.boundary_margin(keys, spec.top_k)
+    if spec.mode == "noaux_tc":
+        margin = np.minimum(margin, orouter.group_margin(l, spec.bias, spec.n_group, spec.topk_group))
+    ok = (margin >= MARGIN_EPS) & (orouter.top_p_margin(rw0, spec.top_p) >= TOPP_EPS)
+    gi, gw = sec["idx"], sec["w"]
+    assert np.array_equal(gi[ok], ri[ok])
+    assert np.allclose(gw[ok], rw[ok], rtol=1e-5, atol=1e-7)
+    mine = odispatch.dispatch(gi, shape.n_experts)
+    for g, w, nm in zip((sec["counts"], sec["offsets"], sec["perm"], sec["inv_perm"]), mine,
+                        ("counts", "offsets", "perm", "inv_perm")):
+        assert np.array_equal(g, w), nm
+    if ok.all():
+        ref = odispatch.dispatch(ri, shape.n_experts)
+        for g, w, nm in zip((sec["counts"], sec["offsets"], sec["perm"], sec["inv_perm"]), ref,
+                            ("counts", "offsets", "perm", "inv_perm")):
+            assert np.array_equal(g, w), nm
+    return int((~ok).sum()), float(margin.min())
+
+
+@pytest.mark.parametrize("wname,tokens", [("olmoe_b1", 1), ("olmoe_b16", 4), ("olmoe_b16", 16), ("glm_b1", 1),
+                                          ("glm_verify4", 4), ("glm_verify4", 16), ("olmoe_b16_topp", 16),
+                                          ("qwen_gated_prefill", 16)])
+def test_layer_fused_routing_bit_exact(wname, tokens):
+    """Up to 16 tokens the layer's top-k and dispatch run as one fused kernel
+    whose results never leave the workspace: read them back after the call
+    (include/moe.h, moe_debug_workspace_sections) and compare with the
+    oracle's routing and dispatch."""
+    need_gpu()
+    wl = synth.workload(wname)
+    shape = wl.layer
+    dl = device_layer(shape.name)
+    x = synth.activations(shape, tokens)
+    _, ws = run_layer(dl, x, wl.act_mode, top_p=wl.top_p or None, return_ws=True)
+    sec = workspace_sections(ws, tokens, shape, wl.act_mode, shape.shared_expert)
+    near, margin = check_layer_routing(sec, shape, x, wl.top_p or None)
+    say(f"[route] {wname} T={tokens}: fused routing read back, min margin {margin:.3e}, unsettled tokens {near}")
+
+
+@pytest.mark.parametrize("act_mode", ["f32", "q8_0"])
+@pytest.mark.parametrize("variant", ["tiny_noaux_topp", "tiny_shared_noaux", "tiny_topp", "tiny_kE", "tiny_e1k1"])
+def test_layer_fused_routing_tiny(variant, act_mode):
+    need_gpu()
+    shape, dl = tiny_layer(variant)
+    for T in (1, 4, 16, 67):
+        x = synth.activations(shape, T)
+        _, ws = run_layer(dl, x, act_mode, return_ws=True)
+        sec = workspace_sections(ws, T, shape, act_mode, shape.shared_expert)
+        check_layer_routing(sec, shape, x)
 
 
 @pytest.mark.parametrize("act_mode", ["f32", "q8_0"])
