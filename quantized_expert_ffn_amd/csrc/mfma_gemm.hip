@@ -10,29 +10,38 @@
 // codes are exact in f16, their products are exact, and the group's sum
 // (|sum| <= 32 * 127 * 127 < 2^24) is exact in the fp32 result, so the matrix
 // core returns the exact integer group dot I_g, already as a float. The
-// group's two fp32 scales (activation row, weight row) are then applied
+// group's two fp32 scales (weight row, activation row) are then applied
 // before it joins the fp32 accumulator:
-//     acc[m][n] += I_g[m, n] * (sx[m, g] * sw[n, g])
+//     acc[n][m] += I_g[n, m] * (sw[n, g] * sx[m, g])
 // which is two VALU operations per output and group (an int8 matrix-core
-// product would need a third, the int -> float conversion, and the VALU work
-// is what bounds this kernel). With one scale per weight row (the per-row
-// formats) the group's factor is sx alone, one VALU operation per output and
-// group, and the row's scale multiplies the finished sum:
-//     acc[m][n] = sw[n] * sum_g I_g[m, n] * sx[m, g]
+// product would need a third, the int -> float conversion). The VALU work
+// bounds this kernel, so the layout is chosen to spend as little of it as
+// possible besides those two operations: with one scale per weight row (the
+// per-row formats) the group's factor is sx alone, one operation per output
+// and group, and the row's scale multiplies the finished sum.
 //
-// Block tile: 128 rows (tokens of one expert) x 128 weight rows (four 32-row
-// tiles), staged through LDS one group pair (64 k) at a time, double
-// buffered, by direct global -> LDS loads: no staging registers; weight
-// blocks land exactly as they are stored. Four waves in 2 x 2; each wave owns
-// 64 rows (four 16-row tiles) and two weight tiles (four 16-row halves), 16
-// matrix-core products per group. 16-row tiles past the tile's row count
-// are neither loaded nor multiplied (wave-uniform), so a short tile costs
-// little more than its rows.
-//   gate/up kernel: the wave's two weight tiles are gate and up of the same 32
-//     outputs, so SwiGLU and the Q8_0 quantisation of H (32 outputs = one
-//     group) happen in registers; H leaves as f16 codes in operand-slot
-//     order + one fp32 scale per 32, ready to be the down kernel's A operand.
-//   down kernel: two adjacent 32-row weight tiles; Y leaves fp32.
+// Block tile: 128 token rows (one work-list tile: rows of one expert) x four
+// 32-row weight tiles; four waves, each owning ONE weight tile (gate/up: two
+// gate tiles and the same two up tiles; down: four adjacent tiles) for ALL of
+// the block's token rows. The weights are the matrix core's A operand (output
+// rows = weight rows) and the token codes its B operand (output columns =
+// tokens), so
+//   - a wave converts each weight code to f16 once and uses it for every
+//     live 16-token tile (up to eight products per conversion);
+//   - a lane's outputs share one token per 16-token tile: its activation
+//     scale is one float per tile and group, its weight scales four floats
+//     per 16-row half and group, read once per stage.
+// Operands are staged through LDS one group pair (64 k) at a time, double
+// buffered, by direct global -> LDS loads (no staging registers; weight
+// blocks land exactly as they are stored in HBM). 16-token tiles past the
+// tile's row count are neither loaded nor multiplied: the live count (1, 2,
+// 4 or 8 tiles) is a compile-time constant of the whole K loop, chosen once
+// per block, so no branch ever separates a product from its use.
+//   gate/up kernel: the up waves hand U to the gate waves through LDS, which
+//     form H = silu(G) * U and quantise it (Q8_0, one group = the 32 outputs
+//     of a weight tile) in registers; H leaves as f16 codes in operand-slot
+//     order + one fp32 scale per 32, ready to be the down kernel's B operand.
+//   down kernel: Y leaves fp32, four consecutive outputs per 16-byte store.
 // Work list: one tile per (expert, 128-row block) from the dispatch kernel;
 // blocks past the live tile count exit at once (no host read-back).
 #include <type_traits>
@@ -44,31 +53,29 @@
 namespace moe {
 
 constexpr int kBM = kTileRows;       // 128 token rows per block
-constexpr int kSG = 2;               // groups per LDS stage (one pair, 64 k)
-constexpr int kM16 = kBM / 16;       // 16-row tiles per block
+constexpr int kM16 = kBM / 16;       // 16-token tiles per block
 
 // One LDS stage (bytes), filled by direct global -> LDS loads (each wave
 // load writes 64 lanes x 16 (or 4) bytes contiguously):
-//   A  [kSG groups][kM16 tiles][64 lanes][16 B]  f16 activation codes; block
-//      (g, i) is the MFMA A operand of 16-row tile i, lane l = r + 16 h
-//      holding row 16 i + r, slice h (k 8h .. 8h+7 in slot order): one
-//      contiguous 1 KB read per operand
-//   B  int8: [4 tiles][kSG groups][1 KB]  weight blocks exactly as in HBM
-//      int4: [4 tiles][1 KB]              (one block holds the pair)
-//      int2: [4 tiles][kSG groups][256 B] the pair's dwords of each lane (a
-//                                         block holds two pairs)
-//   SX [kSG groups][kBM rows] fp32        activation scales
-//   SW [4 tiles][64] fp32                 the tiles' scale blocks of the pair
+//   TOK [2 groups][8 tiles][64 lanes][16 B]  f16 activation codes; block
+//       (g, i) is the B operand of 16-token tile i: lane l = r + 16 h holds
+//       token 16 i + r, slice h (k 8h .. 8h+7 in operand-slot order)
+//   W   int8: [4 tiles][2 groups][1 KB]  weight blocks exactly as in HBM
+//       int4: [4 tiles][1 KB]            (one block holds the pair)
+//       int2: [4 tiles][2 groups][256 B] the pair's dwords of each lane (a
+//                                        block holds two pairs)
+//   SX  [16 r][8 tiles][2 groups] fp32    activation scales of token 16 i + r
+//   SW  [4 tiles][64] fp32                the tiles' scale blocks of the pair
 //                                         (group-scale formats only)
-constexpr int kLdsA = kSG * kM16 * 1024;   // 16384
-constexpr int kLdsSX = kSG * kBM * 4;      // 1024
+constexpr int kLdsTok = 2 * kM16 * 1024;   // 16384
+constexpr int kLdsSX = 2 * kBM * 4;        // 1024
 constexpr int kLdsSW = 4 * 64 * 4;         // 1024
 template <int FMT>
-constexpr int lds_b_bytes() {
-    return FMT == MOE_W_INT8_G32 ? 4 * kSG * 1024 : FMT == MOE_W_INT4_G32 ? 4 * 1024 : 4 * kSG * 256;
+constexpr int lds_w_bytes() {
+    return FMT == MOE_W_INT8_G32 ? 4 * 2 * 1024 : FMT == MOE_W_INT4_G32 ? 4 * 1024 : 4 * 2 * 256;
 }
 template <int FMT>
-constexpr int lds_stage_bytes() { return kLdsA + lds_b_bytes<FMT>() + kLdsSX + kLdsSW; }
+constexpr int lds_stage_bytes() { return kLdsTok + lds_w_bytes<FMT>() + kLdsSX + kLdsSW; }
 
 struct MfmaMat {
     const uint8_t* q;
@@ -109,17 +116,13 @@ __device__ __forceinline__ T lds_read(const lds_byte* p) {
     return __builtin_bit_cast(T, v);
 }
 
-// one wave's direct load of 64 x BYTES from per-lane global addresses into
-// LDS at `dst` (wave-uniform), lane L at dst + L * BYTES
-template <int BYTES>
-__device__ __forceinline__ void wave_load_lds(const void* src, lds_byte* dst) {
-    if constexpr (BYTES == 16)
-        __builtin_amdgcn_global_load_lds(src, (lds_ptr_t)dst, 16, 0, 0);
-    else
-        __builtin_amdgcn_global_load_lds(src, (lds_ptr_t)dst, 4, 0, 0);
+__device__ __forceinline__ uint32_t lds_read_u32(const lds_byte* p) {
+    return *reinterpret_cast<const __attribute__((address_space(3))) uint32_t*>(p);
 }
 
-// the same through a buffer resource: lane L reads BYTES at voff + soff
+// one wave's load of 64 x BYTES through a buffer resource into LDS at `dst`
+// (wave-uniform), lane L at dst + L * BYTES: lane L reads BYTES at
+// voff + soff (soff wave-uniform); a read past the resource's end gives zeros
 template <int BYTES>
 __device__ __forceinline__ void buffer_load_lds(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff, lds_byte* dst) {
     const uint32_t so = __builtin_amdgcn_readfirstlane(soff);
@@ -129,22 +132,294 @@ __device__ __forceinline__ void buffer_load_lds(__amdgpu_buffer_rsrc_t r, uint32
         __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr_t)dst, 4, voff, so, 0, 0);
 }
 
-__device__ __forceinline__ uint32_t lds_read_u32(const lds_byte* p) {
-    return *reinterpret_cast<const __attribute__((address_space(3))) uint32_t*>(p);
-}
+// live 16-token tiles -> the compile-time count the K loop runs with
+__device__ __forceinline__ int live_bucket(int m16) { return m16 <= 1 ? 1 : m16 <= 2 ? 2 : m16 <= 4 ? 4 : 8; }
 
-template <int CTRL>
-__device__ __forceinline__ float dpp_f32(float v) {
-    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, true));
-}
+// Everything a block needs besides its K loop's live-tile count.
+struct TileCtx {
+    int e, row_begin, rows, m16_live;
+    int tt;                         // this wave's weight tile (may be >= NT: loads clamped, nothing stored)
+    int T0;
+    bool is_shared;
+    int K, N, G, P, NT;
+    int lane, wave, nl, rq;
+    const float* wsb;               // this wave's matrix scales (expert base)
+    __amdgpu_buffer_rsrc_t ra, rsx, rw, rsw;
+    uint32_t tok_off[2];            // per-lane source offsets of this wave's token-tile loads
+    uint32_t sx_off;                // per-lane source offset of this wave's scale load
+};
 
-// max over the 16 lanes of a DPP row, result in every lane of the row
-__device__ __forceinline__ float row16_max(float v) {
-    v = fmaxf(v, dpp_f32<0xB1>(v));    // quad_perm [1,0,3,2]
-    v = fmaxf(v, dpp_f32<0x4E>(v));    // quad_perm [2,3,0,1]
-    v = fmaxf(v, dpp_f32<0x141>(v));   // row_half_mirror
-    v = fmaxf(v, dpp_f32<0x140>(v));   // row_mirror
-    return v;
+template <int FMT, bool GATEUP, bool DBG, bool ROW, int LIVE>
+__device__ __forceinline__ void gemm_tile(const MfmaArgs& a, const TileCtx& c, lds_byte* const buf0,
+                                          lds_byte* const buf1) {
+    constexpr int kW = lds_w_bytes<FMT>();
+    const int lane = c.lane, wave = c.wave, nl = c.nl, rq = c.rq;
+    const int P = c.P, NT = c.NT;
+    const int ttl = min(c.tt, NT - 1);   // tile index for loads
+
+    // Stage jobs, each a wave-wide direct load; job j runs on wave j % 4
+    // (wave-uniform): token tiles i = wave and wave + 4 of both groups (live
+    // ones only), this wave's weight block(s), a quarter of the activation
+    // scales, and this wave's weight scale block.
+    auto issue_stage = [&](int pc, lds_byte* base) __attribute__((always_inline)) {
+        lds_byte* TOK = base;
+        lds_byte* W = base + kLdsTok;
+        lds_byte* SX = W + kW;
+        lds_byte* SW = SX + kLdsSX;
+#pragma unroll
+        for (int s = 0; s < 2; ++s) {
+            const int i = wave + 4 * s;
+            if (i < LIVE) {
+#pragma unroll
+                for (int g = 0; g < 2; ++g)
+                    buffer_load_lds<16>(c.ra, c.tok_off[s], (2 * pc + g) * kGroup * 2, TOK + (g * kM16 + i) * 1024);
+            }
+        }
+        if constexpr (FMT == MOE_W_INT8_G32) {
+#pragma unroll
+            for (int g = 0; g < 2; ++g)
+                buffer_load_lds<16>(c.rw, lane * 16, ((2 * pc + g) * NT + ttl) * 1024, W + (wave * 2 + g) * 1024);
+        } else if constexpr (FMT == MOE_W_INT2_G32) {
+            // dwords 2 (pc % 2) + g of each lane's 16 bytes in the quad block
+#pragma unroll
+            for (int g = 0; g < 2; ++g)
+                buffer_load_lds<4>(c.rw, lane * 16, ((pc >> 1) * NT + ttl) * 1024 + (2 * (pc & 1) + g) * 4,
+                                   W + (wave * 2 + g) * 256);
+        } else {
+            buffer_load_lds<16>(c.rw, lane * 16, (pc * NT + ttl) * 1024, W + wave * 1024);
+        }
+        buffer_load_lds<4>(c.rsx, c.sx_off, 2 * pc * 4, SX + wave * 256);
+        if constexpr (!ROW) buffer_load_lds<4>(c.rsw, lane * 4, pc * 256, SW + wave * 256);
+    };
+
+    // per-lane LDS byte offsets of the operands inside a stage buffer, kept
+    // opaque to the optimiser: every LDS read is then the buffer plus one
+    // offset plus a constant, which the compiler can tell apart from the
+    // direct loads in flight into the other buffer (a longer address chain
+    // made it wait for every load before each read)
+    auto opaque = [](int v) __attribute__((always_inline)) {
+        asm volatile("" : "+v"(v));
+        return v;
+    };
+    const int oTok = opaque(lane * 16);
+    const int oW = opaque(kLdsTok + (FMT == MOE_W_INT2_G32 ? wave * 2 * 256 + lane * 4
+                                                           : (FMT == MOE_W_INT8_G32 ? wave * 2 : wave) * 1024 +
+                                                                 lane * 16));
+    const int oSX = opaque(kLdsTok + kW + nl * 64);
+    const int oSW = opaque(kLdsTok + kW + kLdsSX + wave * 256 + rq * 64);
+
+    // acc[i][hh][r]: weight row 16 hh + 4 rq + r of the wave's tile, token
+    // 16 i + nl of the block
+    v4f acc[LIVE][2];
+#pragma unroll
+    for (int i = 0; i < LIVE; ++i)
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) acc[i][hh] = v4f{0.f, 0.f, 0.f, 0.f};
+
+    // One stage: 2 groups x LIVE token tiles = 2 LIVE steps, each two
+    // products (the wave's two 16-row weight halves against one token tile)
+    // and their epilogue. Software pipelined by hand: the products of step
+    // s + 1 are issued before the epilogue of step s (so the matrix core runs
+    // while the VALU scales), the token operand and activation scale of step
+    // s + 2 are read from LDS meanwhile, and a scheduling barrier closes every
+    // step, which keeps the live registers to a few steps' worth.
+    auto compute = [&](const lds_byte* base, int pc) __attribute__((always_inline)) {
+        constexpr int NS = 2 * LIVE;
+        // the weight codes of both halves and groups
+        uint4 cw[2] = {};
+        uint32_t cw2[2] = {};
+        if constexpr (FMT == MOE_W_INT4_G32) {
+            cw[0] = lds_read<uint4>(base + oW);
+        } else if constexpr (FMT == MOE_W_INT8_G32) {
+            cw[0] = lds_read<uint4>(base + oW);
+            cw[1] = lds_read<uint4>(base + oW + 1024);
+        } else {
+            cw2[0] = lds_read_u32(base + oW);
+            cw2[1] = lds_read_u32(base + oW + 256);
+        }
+        // weight scales of the lane's rows 4 rq + r: swr[r] = {g0 h0, g0 h1, g1 h0, g1 h1}
+        float4 swr[4];
+        if constexpr (!ROW) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) swr[r] = lds_read<float4>(base + oSW + r * 16);
+        }
+        // step s: group g = s / LIVE, token tile i = s % LIVE
+        auto tok = [&](int st) __attribute__((always_inline)) {
+            return lds_read<v8h>(base + oTok + ((st / LIVE) * kM16 + st % LIVE) * 1024);
+        };
+        auto sxs = [&](int st) __attribute__((always_inline)) {
+            return *reinterpret_cast<const __attribute__((address_space(3))) float*>(
+                base + oSX + ((st % LIVE) * 2 + st / LIVE) * 4);
+        };
+        // both halves of group g as f16 A operands
+        auto weights = [&](int g, v8h* wa) __attribute__((always_inline)) {
+            if constexpr (FMT == MOE_W_INT8_G32) {
+                wa[0] = codes_to_f16<FMT>(cw[g].x, cw[g].y);
+                wa[1] = codes_to_f16<FMT>(cw[g].z, cw[g].w);
+            } else if constexpr (FMT == MOE_W_INT2_G32) {
+                wa[0] = int2_codes_to_f16<0>(cw2[g]);
+                wa[1] = int2_codes_to_f16<1>(cw2[g]);
+            } else {
+                wa[0] = codes_to_f16<FMT>(g ? cw[0].z : cw[0].x, 0u);
+                wa[1] = codes_to_f16<FMT>(g ? cw[0].w : cw[0].y, 0u);
+            }
+        };
+        v8h wa0[2], wa1[2];
+        v8h tb[NS];
+        float sx[NS];
+        v4f d[NS][2];
+        tb[0] = tok(0);
+        sx[0] = sxs(0);
+        if (NS > 1) {
+            tb[1] = tok(1);
+            sx[1] = sxs(1);
+        }
+        weights(0, wa0);
+        d[0][0] = __builtin_amdgcn_mfma_f32_16x16x32_f16(wa0[0], tb[0], v4f{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+        d[0][1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(wa0[1], tb[0], v4f{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+#pragma unroll
+        for (int st = 0; st < NS; ++st) {
+            if (st + 2 < NS) {
+                tb[st + 2] = tok(st + 2);
+                sx[st + 2] = sxs(st + 2);
+            }
+            if (st + 1 < NS) {
+                const int g1 = (st + 1) / LIVE;
+                if ((st + 1) % LIVE == 0) weights(1, wa1);
+                const v8h* wa = g1 ? wa1 : wa0;
+                d[st + 1][0] = __builtin_amdgcn_mfma_f32_16x16x32_f16(wa[0], tb[st + 1], v4f{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+                d[st + 1][1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(wa[1], tb[st + 1], v4f{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+            }
+            const int g = st / LIVE, i = st % LIVE;
+#pragma unroll
+            for (int hh = 0; hh < 2; ++hh) {
+                if constexpr (ROW) {
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) acc[i][hh][r] = fmaf(d[st][hh][r], sx[st], acc[i][hh][r]);
+                } else {
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const float sw = g ? (hh ? swr[r].w : swr[r].z) : (hh ? swr[r].y : swr[r].x);
+                        acc[i][hh][r] = fmaf(d[st][hh][r], sw * sx[st], acc[i][hh][r]);
+                    }
+                }
+                if constexpr (DBG) {
+                    const int col = c.tt * kTile + 16 * hh + 4 * rq;   // weight rows col .. col + 3
+                    const int row = 16 * i + nl;                       // token row of the block
+                    int32_t* dst = (GATEUP && (wave >> 1)) ? a.dbg1 : a.dbg0;
+                    if (row < c.rows && c.tt < NT) {
+#pragma unroll
+                        for (int r = 0; r < 4; ++r)
+                            dst[((size_t)(c.row_begin + row) * c.N + col + r) * c.G + 2 * pc + g] = (int32_t)d[st][hh][r];
+                    }
+                }
+                // the step's accumulators are final here: without this pin,
+                // earlier passes sink the scaling past the stage barrier,
+                // where every product of the stage would stay live at once
+                asm volatile("" : "+v"(acc[i][hh]));
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    };
+
+    // Stages alternate between the two buffers (separate LDS objects, so a
+    // read of one is never held up by the direct loads into the other); each
+    // stage's loads for the next one are in flight while it is multiplied.
+    issue_stage(0, buf0);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    for (int pc = 0; pc < P; pc += 2) {
+        if (pc + 1 < P) issue_stage(pc + 1, buf1);
+        compute(buf0, pc);
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __syncthreads();
+        if (pc + 1 < P) {
+            if (pc + 2 < P) issue_stage(pc + 2, buf0);
+            compute(buf1, pc + 1);
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+            __syncthreads();
+        }
+    }
+
+    // ---- epilogue ----
+    if constexpr (ROW) {
+        // the lane's rows' scales (a tile past the matrix reads row NT*32-1's; not stored)
+        const float* srow = c.wsb + ttl * kTile + 4 * rq;
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+            const float4 s = *reinterpret_cast<const float4*>(srow + 16 * hh);
+#pragma unroll
+            for (int i = 0; i < LIVE; ++i) {
+                acc[i][hh][0] *= s.x;
+                acc[i][hh][1] *= s.y;
+                acc[i][hh][2] *= s.z;
+                acc[i][hh][3] *= s.w;
+            }
+        }
+    }
+    if constexpr (GATEUP) {
+        // up waves (2, 3) hand U to the gate waves (0, 1) of the same tile
+        // through the stage buffers (free after the loop's last barrier):
+        // wave 2 -> 0 in buf0, wave 3 -> 1 in buf1, lane-major float4s
+        lds_byte* xb = (wave & 1) ? buf1 : buf0;
+        if (wave >= 2) {
+#pragma unroll
+            for (int i = 0; i < LIVE; ++i)
+#pragma unroll
+                for (int hh = 0; hh < 2; ++hh)
+                    *reinterpret_cast<__attribute__((address_space(3))) v4f*>(xb + ((i * 2 + hh) * 64 + lane) * 16) =
+                        acc[i][hh];
+        }
+        __syncthreads();
+        if (wave >= 2) return;
+        const int GN = c.N / kGroup;
+#pragma unroll
+        for (int i = 0; i < LIVE; ++i) {
+            const v4f u0 = *reinterpret_cast<const __attribute__((address_space(3))) v4f*>(xb + ((i * 2) * 64 + lane) * 16);
+            const v4f u1 =
+                *reinterpret_cast<const __attribute__((address_space(3))) v4f*>(xb + ((i * 2 + 1) * 64 + lane) * 16);
+            float h[2][4];
+            float amax = 0.0f;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                h[0][r] = silu(acc[i][0][r]) * u0[r];   // output 32 tt + 4 rq + r
+                h[1][r] = silu(acc[i][1][r]) * u1[r];   // output 32 tt + 16 + 4 rq + r
+                amax = fmaxf(amax, fmaxf(fabsf(h[0][r]), fabsf(h[1][r])));
+            }
+            // the token's 32 outputs sit in lanes nl, nl + 16, nl + 32, nl + 48
+            amax = fmaxf(amax, __shfl_xor(amax, 16, kWave));
+            amax = fmaxf(amax, __shfl_xor(amax, 32, kWave));
+            const float dd = __fdiv_rn(amax, 127.0f);
+            const float inv = dd != 0.0f ? __fdiv_rn(1.0f, dd) : 0.0f;
+            const int row = 16 * i + nl;
+            if (row < c.rows && c.tt < NT) {
+                const size_t R = (size_t)(c.row_begin + row);
+                _Float16* hrow = a.hq + R * c.N + c.tt * kTile;
+#pragma unroll
+                for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const int kk = 16 * hh + 4 * rq + r;     // H column inside the group
+                        const float q = fminf(fmaxf(rintf(__fmul_rn(h[hh][r], inv)), -127.0f), 127.0f);
+                        hrow[(kk & ~7) + k_slot(FMT, kk & 7)] = (_Float16)q;
+                        if constexpr (DBG) a.dbg_hq[R * c.N + c.tt * kTile + kk] = (int8_t)(int)q;
+                    }
+                if (rq == 0) a.hd[R * GN + c.tt] = dd;
+            }
+        }
+    } else {
+        if (c.tt >= NT) return;
+#pragma unroll
+        for (int i = 0; i < LIVE; ++i) {
+            const int row = 16 * i + nl;
+            if (row >= c.rows) continue;
+            float* yrow = a.y + (size_t)(c.row_begin + row) * c.N + c.tt * kTile + 4 * rq;
+#pragma unroll
+            for (int hh = 0; hh < 2; ++hh)
+                *reinterpret_cast<float4*>(yrow + 16 * hh) =
+                    make_float4(acc[i][hh][0], acc[i][hh][1], acc[i][hh][2], acc[i][hh][3]);
+        }
+    }
 }
 
 template <int FMT, bool GATEUP, bool DBG, bool ROW>
@@ -154,12 +429,13 @@ __global__ __launch_bounds__(256) void q8_mfma_kernel(const MfmaArgs a) {
     // that reading one does not wait for the direct loads into the other
     __shared__ __attribute__((aligned(1024))) uint8_t lds0[kStage];
     __shared__ __attribute__((aligned(1024))) uint8_t lds1[kStage];
+    static_assert(kStage >= 2 * kM16 * 64 * 16, "the U hand-over needs 16 KB per buffer");
     // XCD-aware order: the hardware deals blocks to the 8 XCDs in turn by
     // linear id, so linear id L runs on XCD L % 8. Block L takes column block
     // (L / 8) % ncol of row tile ((L / 8) / ncol) * 8 + L % 8: all column
-    // blocks of one row tile share an XCD, and its activation rows are
-    // fetched into that XCD's L2 once (the grid's tile count is a multiple
-    // of 8, so this is a bijection).
+    // blocks of one row tile share an XCD, and its token rows are fetched
+    // into that XCD's L2 once (the grid's tile count is a multiple of 8, so
+    // this is a bijection).
     const int ncol = gridDim.x;
     const int lin = blockIdx.y * ncol + blockIdx.x;
     const int xcd = lin & 7, sl = lin >> 3;
@@ -167,305 +443,60 @@ __global__ __launch_bounds__(256) void q8_mfma_kernel(const MfmaArgs a) {
     const int tile_id = (sl / ncol) * 8 + xcd;
     if (tile_id >= a.meta[1]) return;
     const int4 td = a.tiles[tile_id];
-    const int e = td.x, row_begin = td.y, rows = td.z - td.y;
-    const bool is_shared = e == a.E;
-    const MfmaMat* M = is_shared ? a.shared : a.routed;
-    const int64_t eo = is_shared ? 0 : e;
 
-    const int tid = threadIdx.x, lane = tid & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int wm = wave & 1, wn = wave >> 1;
-    const int K = a.K, N = a.N, G = K / kGroup, P = G / 2, NT = N / kTile;
-    const int T0 = col_blk * (GATEUP ? 2 : 4);         // first 32-row weight tile of the block
-    const int m16_live = (rows + 15) >> 4;               // 16-row tiles holding rows (1 .. 8)
-    const int my_live = min(max(m16_live - 4 * wm, 0), 4);
-
-    // block weight tile j (0..3) -> matrix and tile index (clamped to the
-    // matrix: loads stay inside it; results of a clamped tile are not stored)
-    auto tile_of = [&](int j) { return min(T0 + (GATEUP ? (j & 1) : j), NT - 1); };
-    auto mat_of = [&](int j) { return GATEUP ? (j >> 1) : 0; };
-    const uint8_t* wq[2];
-    const float* wsb[2];
-#pragma unroll
-    for (int m = 0; m < 2; ++m) {
-        wq[m] = M[m].q + eo * M[m].q_stride;
-        wsb[m] = M[m].s + eo * M[m].s_stride;
-    }
+    TileCtx c;
+    c.e = td.x;
+    c.row_begin = td.y;
+    c.rows = td.z - td.y;
+    c.m16_live = (c.rows + 15) >> 4;
+    c.is_shared = c.e == a.E;
+    c.K = a.K;
+    c.N = a.N;
+    c.G = a.K / kGroup;
+    c.P = c.G / 2;
+    c.NT = a.N / kTile;
+    c.lane = threadIdx.x & 63;
+    c.wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    c.nl = c.lane & 15;
+    c.rq = c.lane >> 4;
+    c.T0 = col_blk * (GATEUP ? 2 : 4);
+    c.tt = c.T0 + (GATEUP ? (c.wave & 1) : c.wave);
+    const int mat = GATEUP ? (c.wave >> 1) : 0;
+    const MfmaMat& M = (c.is_shared ? a.shared : a.routed)[mat];
+    const int64_t eo = c.is_shared ? 0 : c.e;
+    const uint8_t* wq = M.q + eo * M.q_stride;
+    c.wsb = M.s + eo * M.s_stride;
+    c.ra = __builtin_amdgcn_make_buffer_rsrc((void*)a.a_q, 0, a.a_bytes, 0x00020000);
+    c.rsx = __builtin_amdgcn_make_buffer_rsrc((void*)a.a_s, 0, a.s_bytes, 0x00020000);
+    c.rw = __builtin_amdgcn_make_buffer_rsrc((void*)wq, 0, (int)M.q_stride, 0x00020000);
+    // this wave's scale block of each pair: (tile, pair) blocks of 64 floats, tile-major
+    const int ttl = min(c.tt, c.NT - 1);
+    c.rsw = __builtin_amdgcn_make_buffer_rsrc((void*)(c.wsb + (size_t)ttl * c.P * 64), 0, c.P * 256, 0x00020000);
     // activation row of a block row (clamped to the tile's rows: rows past it
-    // are loaded only inside a live 16-row tile and never stored)
+    // are loaded only inside a live 16-token tile and never stored)
     auto src_row = [&](int r) {
-        const int pr = row_begin + min(r, rows - 1);
+        const int pr = c.row_begin + min(r, c.rows - 1);
         return a.row_token ? a.row_token[pr] : pr;
     };
-    // this wave's stage jobs are fixed (job index % 4 == wave): A tiles
-    // i = wave and wave + 4 of both groups, and the scale job of (group
-    // wave / 2, rows 64 * (wave % 2) ..). Activation rows, their scales and
-    // the weight codes are read through buffer resources: the per-lane byte
-    // offset stays in a register for the whole kernel and the stage's offset
-    // goes in a scalar register, so issuing a stage costs no vector ALU work
-    // (and a read past a resource's end returns zeros).
-    uint32_t a_off[2];
+    // token tiles i = wave, wave + 4: lane l = r + 16 h reads token 16 i + r, slice h
 #pragma unroll
     for (int s = 0; s < 2; ++s)
-        a_off[s] = ((uint32_t)src_row(16 * (wave + 4 * s) + (lane & 15)) * K + 8 * (lane >> 4)) * 2;
-    const uint32_t s_off = (uint32_t)src_row(64 * (wave & 1) + lane) * G * 4;
-    const uint32_t l_off = lane * 16;
-    const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc((void*)a.a_q, 0, a.a_bytes, 0x00020000);
-    const __amdgpu_buffer_rsrc_t rsx = __builtin_amdgcn_make_buffer_rsrc((void*)a.a_s, 0, a.s_bytes, 0x00020000);
-    __amdgpu_buffer_rsrc_t rw[2];
-#pragma unroll
-    for (int m = 0; m < 2; ++m)
-        rw[m] = __builtin_amdgcn_make_buffer_rsrc((void*)wq[m], 0, (int)M[m].q_stride, 0x00020000);
-
-    auto issue_stage = [&](int st, lds_byte* base) __attribute__((always_inline)) {
-        lds_byte* A = base;
-        lds_byte* B = base + kLdsA;
-        lds_byte* SX = B + lds_b_bytes<FMT>();
-        lds_byte* SW = SX + kLdsSX;
-        const int pc = min(st, P - 1);
-        constexpr int nA = kSG * kM16;
-        constexpr int nB = FMT == MOE_W_INT4_G32 ? 4 : 4 * kSG;
-        constexpr int nSX = kSG * 2;
-        constexpr int nJobs = nA + nB + nSX + (ROW ? 0 : 1);
-        static_assert((nA + nB) % 4 == 0, "scale jobs must start on wave 0");
-#pragma unroll
-        for (int job = 0; job < nJobs; ++job) {
-            if (job % 4 != (wave & 3)) continue;   // wave-uniform
-            if (job < nA) {
-                const int g = job / kM16, i = job % kM16;
-                if (i < m16_live) buffer_load_lds<16>(ra, a_off[i >= 4], (2 * pc + g) * kGroup * 2, A + (g * kM16 + i) * 1024);
-            } else if (job < nA + nB) {
-                const int b = job - nA;
-                if constexpr (FMT == MOE_W_INT8_G32) {
-                    const int j = b / kSG, g = b % kSG;
-                    buffer_load_lds<16>(rw[mat_of(j)], l_off, ((2 * pc + g) * NT + tile_of(j)) * 1024,
-                                        B + (j * kSG + g) * 1024);
-                } else if constexpr (FMT == MOE_W_INT2_G32) {
-                    // dword 2 (pc % 2) + g of each lane's 16 bytes in the quad block
-                    const int j = b / kSG, g = b % kSG;
-                    buffer_load_lds<4>(rw[mat_of(j)], l_off, ((pc >> 1) * NT + tile_of(j)) * 1024 + (2 * (pc & 1) + g) * 4,
-                                       B + (j * kSG + g) * 256);
-                } else {
-                    const int j = b;
-                    buffer_load_lds<16>(rw[mat_of(j)], l_off, (pc * NT + tile_of(j)) * 1024, B + j * 1024);
-                }
-            } else if (job < nA + nB + nSX) {
-                // job q = wave: group q / 2, rows 64 * (q % 2) + lane
-                const int q = job - nA - nB;
-                buffer_load_lds<4>(rsx, s_off, (2 * pc + (q >> 1)) * 4, SX + ((q >> 1) * kBM + 64 * (q & 1)) * 4);
-            } else {
-                // the four tiles' scale blocks of pair pc, 256 B each
-                const int j = lane >> 4;
-                wave_load_lds<16>(wsb[mat_of(j)] + ((size_t)tile_of(j) * P + pc) * 64 + (lane & 15) * 4, SW);
-            }
-        }
-    };
-
-    // output (i, n, r): row 64 wm + 16 i + 4 (lane / 16) + r of the block,
-    // weight row 16 (n % 2) + lane % 16 of the wave's weight tile n / 2
-    const int nl = lane & 15, rq = lane >> 4;
-    const int jt0 = GATEUP ? wn : 2 * wn;       // block weight tiles of the wave
-    const int jt1 = GATEUP ? 2 + wn : 2 * wn + 1;
-
-    v4f acc[4][4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int n = 0; n < 4; ++n) acc[i][n] = v4f{0.f, 0.f, 0.f, 0.f};
-
-    // Per-lane LDS byte offsets of the operands inside a stage buffer, kept
-    // opaque to the optimiser: every LDS read is then the buffer plus one
-    // offset plus a constant. The compiler proves that a read of one buffer
-    // does not alias the direct loads into the other only for addresses it
-    // can trace back to the buffer in a few steps; a longer chain makes it
-    // wait for every load in flight.
-    auto opaque = [](int v) __attribute__((always_inline)) {
-        asm volatile("" : "+v"(v));
-        return v;
-    };
-    const int oA = opaque((4 * wm * 64 + lane) * 16);
-    const int oB0 = opaque(kLdsA + (FMT == MOE_W_INT2_G32 ? jt0 * kSG * 256 + lane * 4
-                                                          : (FMT == MOE_W_INT8_G32 ? jt0 * kSG : jt0) * 1024 + lane * 16));
-    const int oB1 = opaque(kLdsA + (FMT == MOE_W_INT2_G32 ? jt1 * kSG * 256 + lane * 4
-                                                          : (FMT == MOE_W_INT8_G32 ? jt1 * kSG : jt1) * 1024 + lane * 16));
-    const int oSX = opaque(kLdsA + lds_b_bytes<FMT>() + (64 * wm + 4 * rq) * 4);
-    const int oSW0 = opaque(kLdsA + lds_b_bytes<FMT>() + kLdsSX + (jt0 * 64 + nl * 4) * 4);
-    const int oSW1 = opaque(kLdsA + lds_b_bytes<FMT>() + kLdsSX + (jt1 * 64 + nl * 4) * 4);
-
-    // ROW: the scales of the wave's four 16-row weight halves, lane row nl
-    float srow[4];
-    if constexpr (ROW) {
-#pragma unroll
-        for (int n = 0; n < 4; ++n) {
-            const int jt = n < 2 ? jt0 : jt1;
-            srow[n] = wsb[mat_of(jt)][tile_of(jt) * kTile + 16 * (n & 1) + nl];
-        }
+        c.tok_off[s] = ((uint32_t)src_row(16 * (c.wave + 4 * s) + c.nl) * c.K + 8 * c.rq) * 2;
+    // scale job of this wave: floats 64 wave + lane of the SX layout
+    // [16 r][8 tiles][2 groups]: token 16 i + r, group g of the pair
+    {
+        const int f = 64 * c.wave + c.lane;
+        const int r = f >> 4, i = (f >> 1) & 7, g = f & 1;
+        c.sx_off = ((uint32_t)src_row(16 * i + r) * c.G + g) * 4;
     }
-
-    auto compute = [&](const lds_byte* base, int st) __attribute__((always_inline)) {
-        // [row nl, g0][row 16+nl, g0][row nl, g1][row 16+nl, g1] of each tile
-        // (zero for the padding stage past the last pair)
-        const bool real = st < P;
-        float4 sw0 = make_float4(0.f, 0.f, 0.f, 0.f), sw1 = sw0;
-        if constexpr (!ROW) {
-            sw0 = lds_read<float4>(base + oSW0);
-            sw1 = lds_read<float4>(base + oSW1);
-            if (!real) sw0 = sw1 = make_float4(0.f, 0.f, 0.f, 0.f);
-        }
-        uint4 c4[2];
-        if constexpr (FMT == MOE_W_INT4_G32) {
-            c4[0] = lds_read<uint4>(base + oB0);
-            c4[1] = lds_read<uint4>(base + oB1);
-        }
-        // One group for a wave with LIVE live 16-row tiles. The count is a
-        // compile-time constant inside, so no branch separates a product from
-        // the instructions that read it (the compiler's wait-state insertion
-        // does not cover a matrix-core result read across a branch).
-        auto group = [&](auto live_c, int g) __attribute__((always_inline)) {
-            constexpr int LIVE = decltype(live_c)::value;
-            v8h af[LIVE];
-            float4 sx[LIVE];
-#pragma unroll
-            for (int i = 0; i < LIVE; ++i) {
-                af[i] = lds_read<v8h>(base + oA + (g * kM16 + i) * 1024);
-                sx[i] = lds_read<float4>(base + oSX + (g * kBM + 16 * i) * 4);
-            }
-            // one weight half-tile (16 rows) at a time: convert its codes,
-            // then its products with every live 16-row tile
-#pragma unroll
-            for (int n = 0; n < 4; ++n) {
-                const int t = n >> 1, hh = n & 1;
-                v8h bf;
-                if constexpr (FMT == MOE_W_INT8_G32) {
-                    const uint4 c = lds_read<uint4>(base + (t ? oB1 : oB0) + g * 1024);
-                    bf = hh ? codes_to_f16<FMT>(c.z, c.w) : codes_to_f16<FMT>(c.x, c.y);
-                } else if constexpr (FMT == MOE_W_INT2_G32) {
-                    const uint32_t c = lds_read_u32(base + (t ? oB1 : oB0) + g * 256);
-                    bf = hh ? int2_codes_to_f16<1>(c) : int2_codes_to_f16<0>(c);
-                } else {
-                    const uint4 c = c4[t];
-                    bf = codes_to_f16<FMT>(g ? (hh ? c.w : c.z) : (hh ? c.y : c.x), 0u);
-                }
-                const float4 swt = t ? sw1 : sw0;
-                const float sw = g ? (hh ? swt.w : swt.z) : (hh ? swt.y : swt.x);
-#pragma unroll
-                for (int i = 0; i < LIVE; ++i) {
-                    const v4f d = __builtin_amdgcn_mfma_f32_16x16x32_f16(af[i], bf, v4f{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
-                    if constexpr (ROW) {
-                        acc[i][n][0] = fmaf(d[0], sx[i].x, acc[i][n][0]);
-                        acc[i][n][1] = fmaf(d[1], sx[i].y, acc[i][n][1]);
-                        acc[i][n][2] = fmaf(d[2], sx[i].z, acc[i][n][2]);
-                        acc[i][n][3] = fmaf(d[3], sx[i].w, acc[i][n][3]);
-                    } else {
-                        acc[i][n][0] = fmaf(d[0], sx[i].x * sw, acc[i][n][0]);
-                        acc[i][n][1] = fmaf(d[1], sx[i].y * sw, acc[i][n][1]);
-                        acc[i][n][2] = fmaf(d[2], sx[i].z * sw, acc[i][n][2]);
-                        acc[i][n][3] = fmaf(d[3], sx[i].w * sw, acc[i][n][3]);
-                    }
-                    if constexpr (DBG) {
-                        const int jt = t ? jt1 : jt0;
-                        const int wt = T0 + (GATEUP ? (jt & 1) : jt);
-                        const int col = wt * kTile + 16 * hh + nl;
-                        int32_t* dst = (GATEUP && t) ? a.dbg1 : a.dbg0;
-#pragma unroll
-                        for (int r = 0; r < 4; ++r) {
-                            const int row = 64 * wm + 16 * i + 4 * rq + r;
-                            if (row < rows && wt < NT && real)
-                                dst[((size_t)(row_begin + row) * N + col) * G + 2 * st + g] = (int32_t)d[r];
-                        }
-                    }
-                }
-            }
-        };
-#pragma unroll
-        for (int g = 0; g < kSG; ++g) {
-            // wave-uniform: a wave with 2 or 3 live tiles computes all four
-            // (the rows of a dead tile are never stored)
-            if (my_live >= 2) group(std::integral_constant<int, 4>{}, g);
-            else if (my_live == 1) group(std::integral_constant<int, 1>{}, g);
-        }
-    };
 
     lds_byte* const buf0 = (lds_byte*)lds0;
     lds_byte* const buf1 = (lds_byte*)lds1;
-    issue_stage(0, buf0);
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
-    // Stages alternate between the buffers; each stage's direct loads for the
-    // next one are in flight while it is multiplied. An odd stage count runs
-    // one more stage whose weight scales are taken as zero (its loads repeat
-    // the last pair), so the loop body has no exit in its middle.
-    const int P2 = (P + 1) & ~1;
-    for (int st = 0; st < P2; st += 2) {
-        issue_stage(st + 1, buf1);
-        compute(buf0, st);
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-        __syncthreads();
-        if (st + 2 < P2) issue_stage(st + 2, buf0);
-        // per-row formats have no weight scale to zero: they skip the
-        // padding stage's products
-        if (!ROW || st + 1 < P) compute(buf1, st + 1);
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-        __syncthreads();
-    }
-
-    // ---- epilogue ----
-    if constexpr (ROW) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-            for (int n = 0; n < 4; ++n)
-#pragma unroll
-                for (int r = 0; r < 4; ++r) acc[i][n][r] *= srow[n];
-    }
-    if constexpr (GATEUP) {
-        const int t = T0 + wn;                  // weight tile = group of H's columns
-        const int GN = N / kGroup;
-        // H column 32 t + kk sits at slot position (kk & ~7) + k_slot(kk & 7)
-        const int pos0 = (nl & 8) + k_slot(FMT, nl & 7);
-        const int pos1 = 16 + pos0;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            if (i >= my_live) continue;
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const float h0 = silu(acc[i][0][r]) * acc[i][2][r];   // H column 32 t + nl
-                const float h1 = silu(acc[i][1][r]) * acc[i][3][r];   // H column 32 t + 16 + nl
-                const float amax = row16_max(fmaxf(fabsf(h0), fabsf(h1)));
-                const float dd = __fdiv_rn(amax, 127.0f);
-                const float inv = dd != 0.0f ? __fdiv_rn(1.0f, dd) : 0.0f;
-                const float q0 = fminf(fmaxf(rintf(__fmul_rn(h0, inv)), -127.0f), 127.0f);
-                const float q1 = fminf(fmaxf(rintf(__fmul_rn(h1, inv)), -127.0f), 127.0f);
-                const int row = 64 * wm + 16 * i + 4 * rq + r;
-                if (row < rows) {
-                    const size_t R = (size_t)(row_begin + row);
-                    _Float16* hrow = a.hq + R * N + t * kTile;
-                    hrow[pos0] = (_Float16)q0;
-                    hrow[pos1] = (_Float16)q1;
-                    if (nl == 0) a.hd[R * GN + t] = dd;
-                    if constexpr (DBG) {
-                        a.dbg_hq[R * N + t * kTile + nl] = (int8_t)(int)q0;
-                        a.dbg_hq[R * N + t * kTile + 16 + nl] = (int8_t)(int)q1;
-                    }
-                }
-            }
-        }
-    } else {
-#pragma unroll
-        for (int n = 0; n < 4; ++n) {
-            const int t = T0 + (n < 2 ? jt0 : jt1);
-            if (t >= NT) continue;
-            const int col = t * kTile + 16 * (n & 1) + nl;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                if (i >= my_live) continue;
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int row = 64 * wm + 16 * i + 4 * rq + r;
-                    if (row < rows) a.y[(size_t)(row_begin + row) * N + col] = acc[i][n][r];
-                }
-            }
-        }
+    switch (live_bucket(c.m16_live)) {   // block-uniform
+        case 1: gemm_tile<FMT, GATEUP, DBG, ROW, 1>(a, c, buf0, buf1); break;
+        case 2: gemm_tile<FMT, GATEUP, DBG, ROW, 2>(a, c, buf0, buf1); break;
+        case 4: gemm_tile<FMT, GATEUP, DBG, ROW, 4>(a, c, buf0, buf1); break;
+        default: gemm_tile<FMT, GATEUP, DBG, ROW, 8>(a, c, buf0, buf1); break;
     }
 }
 
