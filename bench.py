@@ -90,6 +90,26 @@ def stream_read_ceiling(dev, reps: int = 5) -> float:
     return best
 
 
+def prefill_mix_ceiling(dev, reps: int = 5) -> float:
+    """What the prefill GEMM's inner loop reaches with its operands resident in
+    LDS (include/moe_calib.h): best of `reps` launches of 768 blocks (three
+    per CU), useful int8 TOPS."""
+    import torch
+    import quantized_expert_ffn_amd as qe
+    blocks, stages = 768, 200
+    sink = torch.empty(blocks * 256, dtype=torch.float32, device=dev)
+    qe.moe_calib_prefill_mix(blocks, stages, sink)
+    best = 0.0
+    for _ in range(reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        ops = qe.moe_calib_prefill_mix(blocks, stages, sink)
+        e1.record()
+        torch.cuda.synchronize(dev)
+        best = max(best, ops / (e0.elapsed_time(e1) * 1e-3) / 1e12)
+    return best
+
+
 def cpu_baseline(wl, target_s: float):
     """The oracle (plain numpy) on the whole batch of the same workload, on
     this host's cores, repeated until about target_s of CPU time (at most 5
@@ -281,9 +301,11 @@ def main():
     per_step = np.array([step_evs[i].elapsed_time(step_evs[i + 1]) * 1e3 for i in range(args.steps)])
     step_pct = {q: round(float(np.percentile(per_step, v)), 2) for q, v in (("p10", 10), ("p50", 50), ("p90", 90))}
 
-    # (4) the reference measured in the same run
+    # (4) the references measured in the same run
     stream_gbs = stream_read_ceiling(dev)
-    print(f"[bench] streaming read: {stream_gbs:.0f} GB/s", file=sys.stderr, flush=True)
+    mix_tops = prefill_mix_ceiling(dev)
+    print(f"[bench] streaming read: {stream_gbs:.0f} GB/s; prefill GEMM inner loop alone: {mix_tops:.0f} TOPS",
+          file=sys.stderr, flush=True)
 
     # the kernel the library launches for the gate/up stage of this workload:
     # the GEMV for decode and for Q8_0 batches of up to 16 tokens (HBM bound),
@@ -316,6 +338,9 @@ def main():
     roof["ceiling_stream_read_gbs"] = round(stream_gbs, 1)
     if gemv:
         roof["frac_of_stream_read"] = round(achieved / stream_gbs, 4)
+    else:
+        roof["ceiling_instr_mix_tops"] = round(mix_tops, 1)
+        roof["frac_of_instr_mix"] = round(achieved / mix_tops, 4)
 
     line = {
         "metric": "MoE-layer tokens/s at 1 GPU (decode HBM GB/s or prefill int8 TOPS vs peak in roofline)",

@@ -90,6 +90,7 @@ _SIGNATURES = {
     "moe_status_string": (ctypes.c_char_p, [_I32]),
     # include/moe_calib.h: measurement references
     "moe_calib_stream_read": (_I32, [_P, ctypes.c_uint64, _P, _I32, _P]),
+    "moe_calib_prefill_mix": (_I32, [_I32, _I32, _P, ctypes.POINTER(ctypes.c_uint64), _P]),
     "moe_last_error_detail": (ctypes.c_char_p, []),
 }
 
@@ -316,6 +317,15 @@ def moe_calib_stream_read(buf: torch.Tensor, sink: torch.Tensor, blocks: int, st
     sink: uint32-sized [blocks] device tensor."""
     _check(load().moe_calib_stream_read(_ptr(buf, None, "buf"), buf.numel() * buf.element_size(),
                                         _ptr(sink, None, "sink"), blocks, _stream(stream)), "moe_calib_stream_read")
+
+
+def moe_calib_prefill_mix(blocks: int, stages: int, sink: torch.Tensor, stream=None) -> int:
+    """The prefill GEMM's inner loop alone (include/moe_calib.h); sink: fp32
+    [blocks * 256] device tensor. Returns the useful int8 operations launched."""
+    ops = ctypes.c_uint64(0)
+    _check(load().moe_calib_prefill_mix(blocks, stages, _ptr(sink, torch.float32, "sink"), ctypes.byref(ops),
+                                        _stream(stream)), "moe_calib_prefill_mix")
+    return int(ops.value)
 
 
 def moe_combine(y_perm: torch.Tensor, topk_w: torch.Tensor, inv_perm: torch.Tensor,

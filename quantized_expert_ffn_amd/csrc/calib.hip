@@ -1,9 +1,12 @@
 // Reference kernels for pricing the layer's kernels against what the chip
 // reaches in practice (include/moe_calib.h), next to the vendor peaks: a
-// plain streaming read of HBM. Nothing of the layer's arithmetic is here.
+// plain streaming read of HBM, and the prefill GEMM's own stage computation
+// (q8_stage.h) run on operands that stay in LDS, with no global memory and no
+// barriers, which bounds what the GEMM's instruction mix can reach.
 #include "common.h"
 #include "kernels.h"
 #include "moe_calib.h"
+#include "q8_stage.h"
 
 namespace moe {
 
@@ -52,7 +55,63 @@ __global__ __launch_bounds__(kStreamThreads) void stream_read_kernel(const uint8
     }
 }
 
+// The prefill GEMM's stage (int4 weight codes, group scales, all eight
+// 16-token tiles live) over and over on one stage of operands resident in
+// LDS: the instruction mix of its inner loop alone. Two stage buffers are
+// allocated and alternated, as in the GEMM, so the occupancy is the same
+// (three blocks of four waves per CU). Operands: token codes 1, weight codes
+// 1, activation scales 1, weight scales 2^-20 (the sums stay finite).
+constexpr int kMixLive = 8;
+__global__ __launch_bounds__(256) void prefill_mix_kernel(int stages, float* __restrict__ sink) {
+    constexpr int FMT = MOE_W_INT4_G32;
+    constexpr int kStage = kLdsTok + 4 * 1024 + kLdsSX + kLdsSW;
+    __shared__ __attribute__((aligned(1024))) uint8_t lds0[kStage];
+    __shared__ __attribute__((aligned(1024))) uint8_t lds1[kStage];
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    for (int b = 0; b < 2; ++b) {
+        uint32_t* w = reinterpret_cast<uint32_t*>(b ? lds1 : lds0);
+        for (int i = tid; i < kLdsTok / 4; i += 256) w[i] = 0x3C003C00u;                    // f16 1.0, 1.0
+        for (int i = tid; i < 4 * 1024 / 4; i += 256) w[kLdsTok / 4 + i] = 0x11111111u;      // int4 codes 1
+        float* f = reinterpret_cast<float*>(b ? lds1 : lds0) + (kLdsTok + 4 * 1024) / 4;
+        for (int i = tid; i < kLdsSX / 4; i += 256) f[i] = 1.0f;
+        for (int i = tid; i < kLdsSW / 4; i += 256) f[kLdsSX / 4 + i] = 0x1p-20f;
+    }
+    __syncthreads();
+    auto opaque = [](int v) __attribute__((always_inline)) {
+        asm volatile("" : "+v"(v));
+        return v;
+    };
+    const int nl = lane & 15, rq = lane >> 4;
+    const StageOffsets o{opaque(lane * 16), opaque(kLdsTok + wave * 1024 + lane * 16), opaque(kLdsTok + 4096 + nl * 4),
+                         opaque(kLdsTok + 4096 + kLdsSX + wave * 256 + rq * 64)};
+    v4f acc[kMixLive][2];
+#pragma unroll
+    for (int i = 0; i < kMixLive; ++i)
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) acc[i][hh] = v4f{0.f, 0.f, 0.f, 0.f};
+    auto none = [](int, int, const v4f&) __attribute__((always_inline)) {};
+    for (int st = 0; st < stages; st += 2) {
+        q8_stage<FMT, false, kMixLive>((const lds_byte*)lds0, o, acc, none);
+        q8_stage<FMT, false, kMixLive>((const lds_byte*)lds1, o, acc, none);
+    }
+    float sum = 0.0f;
+#pragma unroll
+    for (int i = 0; i < kMixLive; ++i)
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) sum += acc[i][hh][0] + acc[i][hh][1] + acc[i][hh][2] + acc[i][hh][3];
+    sink[(size_t)blockIdx.x * 256 + tid] = sum;
+}
+
 }  // namespace moe
+
+extern "C" moe_status moe_calib_prefill_mix(int32_t blocks, int32_t stages, float* sink, uint64_t* ops,
+                                            hipStream_t stream) {
+    if (sink == nullptr || blocks < 1 || stages < 2 || (stages & 1)) return MOE_ERR_INVALID_ARG;
+    if (ops) *ops = (uint64_t)blocks * stages * 4 /* waves */ * (2 * moe::kMixLive * 2) /* products */ * 16384;
+    hipLaunchKernelGGL(moe::prefill_mix_kernel, dim3(blocks), dim3(256), 0, stream, stages, sink);
+    return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_HIP;
+}
 
 extern "C" moe_status moe_calib_stream_read(const void* buf, uint64_t bytes, uint32_t* sink, int32_t blocks,
                                             hipStream_t stream) {

@@ -84,7 +84,21 @@ __device__ __forceinline__ int block_exclusive_scan(int v, int* tmp, int* total)
     return res;
 }
 
+// Size class of a tile of r rows for the tile list's order: 0 for a full
+// tile, then partial tiles by the live 16-row tiles the prefill kernel runs
+// them with (8, 4, 2, 1).
+__device__ __forceinline__ int tile_class(int r, int tile_rows) {
+    if (r >= tile_rows) return 0;
+    const int m16 = (r + 15) >> 4;
+    return m16 > 4 ? 1 : m16 > 2 ? 2 : m16 > 1 ? 3 : 4;
+}
+
 // Work lists from counts/offsets (thread e < E holds counts[e], offsets[e]).
+// Slots are in expert order (the shared expert last). Tiles are ordered by
+// size, largest first: every full tile (routed experts in expert order, then
+// the shared expert's), then the partial tiles class by class (tile_class);
+// a grid that walks the list in order then ends on its cheapest blocks. Each
+// tile computes only its own rows, so the order changes no result.
 __device__ __forceinline__ void build_work_lists(int E, int cnt, int off, int n_rows_routed, int T, int has_shared,
                                  int tile_rows, int* scan_tmp, int* __restrict__ slots, int* __restrict__ tiles,
                                  int* __restrict__ meta) {
@@ -97,28 +111,43 @@ __device__ __forceinline__ void build_work_lists(int E, int cnt, int off, int n_
         int4* s = reinterpret_cast<int4*>(slots) + slot;
         *s = make_int4(e, off, cnt, 0);
     }
-    int n_tiles = 0;
-    const int nt = valid ? (cnt + tile_rows - 1) / tile_rows : 0;
-    const int tbase = block_exclusive_scan(nt, scan_tmp, &n_tiles);
-    for (int i = 0; i < nt; ++i) {
+    int4* tl = reinterpret_cast<int4*>(tiles);
+    const int full = valid ? cnt / tile_rows : 0;
+    const int part = valid ? cnt - full * tile_rows : 0;
+    const int cls = part > 0 ? tile_class(part, tile_rows) : -1;
+    int n_full = 0;
+    const int fbase = block_exclusive_scan(full, scan_tmp, &n_full);
+    for (int i = 0; i < full; ++i) {
         const int rb = off + i * tile_rows;
-        const int re = min(off + cnt, rb + tile_rows);
-        reinterpret_cast<int4*>(tiles)[tbase + i] = make_int4(e, rb, re, 0);
+        tl[fbase + i] = make_int4(e, rb, rb + tile_rows, 0);
+    }
+    const int s_full = has_shared ? T / tile_rows : 0;
+    const int s_part = has_shared ? T - s_full * tile_rows : 0;
+    const int s_cls = s_part > 0 ? tile_class(s_part, tile_rows) : -1;
+    for (int i = threadIdx.x; i < s_full; i += blockDim.x) {
+        const int rb = n_rows_routed + i * tile_rows;
+        tl[n_full + i] = make_int4(E, rb, rb + tile_rows, 0);
+    }
+    int pos = n_full + s_full;
+#pragma unroll 1
+    for (int c = 1; c <= 4; ++c) {
+        int n_c = 0;
+        const int b = block_exclusive_scan(cls == c ? 1 : 0, scan_tmp, &n_c);
+        if (cls == c) tl[pos + b] = make_int4(e, off + full * tile_rows, off + cnt, 0);
+        pos += n_c;
+        if (s_cls == c) {
+            if (threadIdx.x == 0)
+                tl[pos] = make_int4(E, n_rows_routed + s_full * tile_rows, n_rows_routed + T, 0);
+            pos += 1;
+        }
     }
     if (has_shared) {
-        const int shared_tiles = (T + tile_rows - 1) / tile_rows;
-        for (int i = threadIdx.x; i < shared_tiles; i += blockDim.x) {
-            const int rb = n_rows_routed + i * tile_rows;
-            const int re = min(n_rows_routed + T, rb + tile_rows);
-            reinterpret_cast<int4*>(tiles)[n_tiles + i] = make_int4(E, rb, re, 0);
-        }
         if (threadIdx.x == 0) reinterpret_cast<int4*>(slots)[n_active] = make_int4(E, n_rows_routed, T, 0);
-        n_tiles += shared_tiles;
         n_active += 1;
     }
     if (threadIdx.x == 0) {
         meta[0] = n_active;
-        meta[1] = n_tiles;
+        meta[1] = pos;
     }
 }
 

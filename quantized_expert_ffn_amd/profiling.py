@@ -14,6 +14,9 @@ folder keep.
     # a kernel-trace --stats table as markdown
     python -m quantized_expert_ffn_amd.profiling stats run_kernel_stats.csv --command "..."
 
+    # the mean per dispatch of every counter of one kernel, from --pmc runs
+    python -m quantized_expert_ffn_amd.profiling pmc A.csv B.csv --kernel "q8_mfma_kernel<1, true" --command "..."
+
 Only rocprofv3's CSV files are read; nothing here touches the GPU except the
 copy command.
 """
@@ -131,6 +134,27 @@ def cmd_stats(args):
               f"{float(r['MaxNs']) / 1e3:.2f} | {float(r['Percentage']):.1f}% |")
 
 
+def cmd_pmc(args):
+    """Mean per dispatch of every counter in one or more --pmc CSVs, for the
+    dispatches of one kernel, as a markdown table."""
+    sums, counts = {}, {}
+    for path in args.csv:
+        for r in csv.DictReader(open(path)):
+            if args.kernel not in r.get("Kernel_Name", ""):
+                continue
+            k = r["Counter_Name"]
+            sums[k] = sums.get(k, 0.0) + float(r["Counter_Value"])
+            counts[k] = counts.get(k, 0) + 1
+    if not sums:
+        raise SystemExit(f"no rows for a kernel matching {args.kernel!r}")
+    print(f"Command: `{args.command}`\n")
+    print(f"Kernel: `{args.kernel}`\n")
+    print("| counter | mean per dispatch | dispatches |")
+    print("|---|---:|---:|")
+    for k in sorted(sums):
+        print(f"| {k} | {sums[k] / counts[k]:.6g} | {counts[k]} |")
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     sub = ap.add_subparsers(dest="cmd", required=True)
@@ -153,8 +177,12 @@ def main(argv=None):
     s.add_argument("csv")
     s.add_argument("--command", required=True)
     s.add_argument("--top", type=int, default=14)
+    m = sub.add_parser("pmc")
+    m.add_argument("csv", nargs="+")
+    m.add_argument("--kernel", required=True, help="substring of the kernel name")
+    m.add_argument("--command", required=True)
     args = ap.parse_args(argv)
-    {"copy": cmd_copy, "traffic": cmd_traffic, "stats": cmd_stats}[args.cmd](args)
+    {"copy": cmd_copy, "traffic": cmd_traffic, "stats": cmd_stats, "pmc": cmd_pmc}[args.cmd](args)
 
 
 if __name__ == "__main__":

@@ -281,3 +281,11 @@ def test_calib_stream_read_rejects_bad_arguments(lib):
     assert f(FAKE, 1000, FAKE, 64, None) == INVALID                   # not a multiple of 16
     assert f(FAKE, 0, FAKE, 64, None) == INVALID
     assert f(FAKE, 1 << 20, FAKE, 0, None) == INVALID
+
+
+def test_calib_prefill_mix_rejects_bad_arguments(lib):
+    f = lib.moe_calib_prefill_mix
+    assert f(16, 8, None, None, None) == INVALID
+    assert f(0, 8, FAKE, None, None) == INVALID
+    assert f(16, 7, FAKE, None, None) == INVALID                     # odd stage count
+    assert f(16, 0, FAKE, None, None) == INVALID
