@@ -307,6 +307,30 @@ moe_status moe_layer_forward(const float* x, int32_t T, const float* gate_w,
                              const moe_experts* shared, int32_t act_mode, float* out,
                              void* ws, size_t ws_bytes, hipStream_t stream);
 
+/* moe_layer_forward without a workspace argument, for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc. The call allocates nothing (no
+ * hipMalloc, hipFree or allocating library routine): its scratch is an
+ * array of MOE_NOALLOC_SCRATCH_BYTES bytes in the library's device code, one
+ * per GPU, held from the library's load until the process ends; the first
+ * call on a device looks up that device's copy.
+ *   Everything else as moe_layer_forward (the caller still passes x, the
+ *   weights and out).
+ *   A call whose moe_workspace_size(T, k, E, d, d_ff, act_mode, shared !=
+ *   NULL) exceeds MOE_NOALLOC_SCRATCH_BYTES returns MOE_ERR_UNSUPPORTED
+ *   before anything is enqueued (decode and verification batches fit; large
+ *   prefills need moe_layer_forward and a workspace).
+ *   Every call on one GPU shares that GPU's array: calls that can overlap on
+ *   one GPU (several streams, or several host threads) race and must be
+ *   serialised by the caller. Calls on one stream run in order. Nothing in
+ *   the array needs to start at any value (every kernel writes what it
+ *   reads), so the contents a previous call left are harmless.
+ */
+#define MOE_NOALLOC_SCRATCH_BYTES (32u << 20)
+moe_status moe_layer_forward_noalloc(const float* x, int32_t T, const float* gate_w, const moe_router_params* p,
+                                     const moe_experts* routed, const moe_experts* shared, int32_t act_mode,
+                                     float* out, hipStream_t stream);
+
 /* moe_layer_forward that also records stage_events[2*s] before and
  * stage_events[2*s+1] after stage s (moe_stage) on `stream`. stage_events
  * is a host array of 2*MOE_STAGE_COUNT hipEvent_t created by the caller;

@@ -12,7 +12,8 @@ from ._lib import (  # noqa: F401
     MoeError, QuantExperts, RouterParams, Experts,
     load, exported_names, router_params, with_top_p, quantize_experts, workspace,
     moe_workspace_size, moe_quantize_weights, moe_quantize_q8_0, moe_route, moe_dispatch,
-    moe_expert_ffn, moe_debug_q8_expert_ffn, moe_debug_workspace_sections, moe_combine, moe_layer_forward, moe_layer_forward_timed,
+    moe_expert_ffn, moe_debug_q8_expert_ffn, moe_debug_workspace_sections, moe_combine, moe_layer_forward,
+    moe_layer_forward_noalloc, moe_layer_forward_timed, MOE_NOALLOC_SCRATCH_BYTES,
     moe_block_forward, moe_calib_stream_read, moe_calib_prefill_mix,
     moe_status_string, moe_last_error_detail,
 )

@@ -80,6 +80,8 @@ _SIGNATURES = {
     "moe_combine": (_I32, [_P, _P, _P, _P, _I32, _I32, _I32, _P, _P]),
     "moe_layer_forward": (_I32, [_P, _I32, _P, ctypes.POINTER(RouterParams), ctypes.POINTER(Experts),
                                  ctypes.POINTER(Experts), _I32, _P, _P, _SZ, _P]),
+    "moe_layer_forward_noalloc": (_I32, [_P, _I32, _P, ctypes.POINTER(RouterParams), ctypes.POINTER(Experts),
+                                         ctypes.POINTER(Experts), _I32, _P, _P]),
     "moe_layer_forward_timed": (_I32, [_P, _I32, _P, ctypes.POINTER(RouterParams), ctypes.POINTER(Experts),
                                        ctypes.POINTER(Experts), _I32, _P, _P, _SZ, _P, _P]),
     "moe_block_forward": (_I32, [_P, _I32, _P, ctypes.c_float, _P, ctypes.POINTER(RouterParams),
@@ -345,6 +347,23 @@ def moe_layer_forward(x: torch.Tensor, gate_w: torch.Tensor, params: RouterParam
                                     ctypes.byref(params), ctypes.byref(r), ctypes.byref(s) if s is not None else None,
                                     act_mode, _ptr(out, torch.float32, "out"), _ptr(ws, None, "ws"),
                                     ws.numel() * ws.element_size(), _stream(stream)), "moe_layer_forward")
+
+
+MOE_NOALLOC_SCRATCH_BYTES = 32 << 20   # include/moe.h
+
+
+def moe_layer_forward_noalloc(x: torch.Tensor, gate_w: torch.Tensor, params: RouterParams, routed: QuantExperts,
+                              shared: Optional[QuantExperts], act_mode: int, out: torch.Tensor, stream=None) -> None:
+    """moe_layer_forward with the library's own per-GPU scratch instead of a
+    workspace (no allocation); calls needing more than
+    MOE_NOALLOC_SCRATCH_BYTES of workspace are rejected."""
+    r = routed.abi()
+    s = shared.abi() if shared is not None else None
+    _check(load().moe_layer_forward_noalloc(_ptr(x, torch.float32, "x"), x.shape[0],
+                                            _ptr(gate_w, torch.float32, "gate_w"), ctypes.byref(params),
+                                            ctypes.byref(r), ctypes.byref(s) if s is not None else None, act_mode,
+                                            _ptr(out, torch.float32, "out"), _stream(stream)),
+           "moe_layer_forward_noalloc")
 
 
 def moe_layer_forward_timed(x, gate_w, params: RouterParams, routed: QuantExperts, shared: Optional[QuantExperts],

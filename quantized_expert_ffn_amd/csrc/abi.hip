@@ -7,10 +7,18 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <mutex>
 #include <string>
 
 #include "common.h"
 #include "kernels.h"
+
+// The scratch of moe_layer_forward_noalloc: one array per GPU, part of the
+// library's device code object, so it exists on every device the library is
+// loaded on and lives until the process ends. Host code never uses this name
+// as an address (it is a host-side stand-in there): it asks the runtime for
+// the current device's copy (scratch_for_current_device).
+static __device__ __align__(256) uint8_t scratch[MOE_NOALLOC_SCRATCH_BYTES];
 
 namespace {
 
@@ -244,10 +252,10 @@ moe_status expert_ffn_impl(const float* x, int32_t T, int32_t k, const moe_exper
 
 // The layer; with `block`, between its neighbours: out = x + layer(RMSNorm(x))
 // (norm_w null: no normalisation, the residual is still added).
-moe_status layer_forward_impl(const float* x, int32_t T, const float* gate_w, const moe_router_params* p,
-                              const moe_experts* routed, const moe_experts* shared, int32_t act_mode, float* out,
-                              void* ws, size_t ws_bytes, const hipEvent_t* ev, hipStream_t st, bool block = false,
-                              const float* norm_w = nullptr, float eps = 0.0f) {
+// Every check of the layer's arguments except the workspace's (host only).
+moe_status check_layer(const float* x, int32_t T, const float* gate_w, const moe_router_params* p,
+                       const moe_experts* routed, const moe_experts* shared, int32_t act_mode, const float* out,
+                       const float* norm_w, float eps) {
     moe_status s;
     if ((s = check_act_mode(act_mode)) != MOE_OK) return s;
     if ((s = check_experts(routed, "routed", act_mode, T)) != MOE_OK) return s;
@@ -271,6 +279,16 @@ moe_status layer_forward_impl(const float* x, int32_t T, const float* gate_w, co
     MOE_REQUIRE(norm_w == nullptr || aligned16(norm_w), MOE_ERR_INVALID_ARG, "norm_w must be 16-byte aligned");
     MOE_REQUIRE(std::isfinite(eps) && eps >= 0.0f, MOE_ERR_INVALID_ARG, "eps = %g must be finite and >= 0",
                 (double)eps);
+    return MOE_OK;
+}
+
+moe_status layer_forward_impl(const float* x, int32_t T, const float* gate_w, const moe_router_params* p,
+                              const moe_experts* routed, const moe_experts* shared, int32_t act_mode, float* out,
+                              void* ws, size_t ws_bytes, const hipEvent_t* ev, hipStream_t st, bool block = false,
+                              const float* norm_w = nullptr, float eps = 0.0f) {
+    moe_status s;
+    if ((s = check_layer(x, T, gate_w, p, routed, shared, act_mode, out, norm_w, eps)) != MOE_OK) return s;
+    if (T == 0) return ok();
     const int E = routed->n_experts, k = p->top_k, d = routed->d_model;
     const int has_shared = shared != nullptr;
     const moe::WsLayout L = moe::ws_layout(T, k, E, d, routed->d_ff, act_mode, has_shared);
@@ -335,6 +353,28 @@ moe_status layer_forward_impl(const float* x, int32_t T, const float* gate_w, co
             "combine");
     record(ev, 2 * MOE_STAGE_COMBINE + 1, st);
     return ok();
+}
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// The address of this device's scratch array, looked up once per device
+// (with that device current) and kept.
+moe_status scratch_for_current_device(void** out) {
+    int dev = 0;
+    MOE_HIP(hipGetDevice(&dev), "hipGetDevice");
+    MOE_REQUIRE(dev >= 0 && dev < kMaxDevices, MOE_ERR_UNSUPPORTED, "device %d is beyond the %d the library tracks",
+                dev, kMaxDevices);
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (g_scratch_ptr[dev] == nullptr) {
+        void* p = nullptr;
+        MOE_HIP(hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)), "hipGetSymbolAddress(scratch)");
+        MOE_REQUIRE(p != nullptr, MOE_ERR_HIP, "no scratch address for device %d", dev);
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return MOE_OK;
 }
 
 }  // namespace
@@ -454,6 +494,24 @@ moe_status moe_layer_forward(const float* x, int32_t T, const float* gate_w, con
                              const moe_experts* routed, const moe_experts* shared, int32_t act_mode, float* out,
                              void* ws, size_t ws_bytes, hipStream_t stream) {
     return layer_forward_impl(x, T, gate_w, p, routed, shared, act_mode, out, ws, ws_bytes, nullptr, stream);
+}
+
+moe_status moe_layer_forward_noalloc(const float* x, int32_t T, const float* gate_w, const moe_router_params* p,
+                                     const moe_experts* routed, const moe_experts* shared, int32_t act_mode, float* out,
+                                     hipStream_t stream) {
+    moe_status s;
+    if ((s = check_layer(x, T, gate_w, p, routed, shared, act_mode, out, nullptr, 0.0f)) != MOE_OK) return s;
+    if (T == 0) return ok();
+    const size_t need = moe_workspace_size(T, p->top_k, routed->n_experts, routed->d_model, routed->d_ff, act_mode,
+                                           shared != nullptr);
+    MOE_REQUIRE(need <= (size_t)MOE_NOALLOC_SCRATCH_BYTES, MOE_ERR_UNSUPPORTED,
+                "this call needs %zu bytes of scratch, more than the %zu the allocation-free entry point holds "
+                "(moe_layer_forward takes a workspace of any size)",
+                need, (size_t)MOE_NOALLOC_SCRATCH_BYTES);
+    void* ws = nullptr;
+    if ((s = scratch_for_current_device(&ws)) != MOE_OK) return s;
+    return layer_forward_impl(x, T, gate_w, p, routed, shared, act_mode, out, ws, MOE_NOALLOC_SCRATCH_BYTES, nullptr,
+                              stream);
 }
 
 moe_status moe_layer_forward_timed(const float* x, int32_t T, const float* gate_w, const moe_router_params* p,

@@ -289,3 +289,22 @@ def test_calib_prefill_mix_rejects_bad_arguments(lib):
     assert f(0, 8, FAKE, None, None) == INVALID
     assert f(16, 7, FAKE, None, None) == INVALID                     # odd stage count
     assert f(16, 0, FAKE, None, None) == INVALID
+
+
+def test_noalloc_entry_point_checks_before_any_gpu_call(lib):
+    """The allocation-free layer entry point: null arguments and calls whose
+    workspace would exceed its scratch are rejected on the host, before any
+    HIP call (no GPU here)."""
+    p, r = _params(), _experts()
+    f = lib.moe_layer_forward_noalloc
+    assert f(FAKE, 4, FAKE, None, ctypes.byref(r), None, 0, FAKE, None) == INVALID
+    assert f(FAKE, 4, FAKE, ctypes.byref(p), None, None, 0, FAKE, None) == INVALID
+    assert f(FAKE, -1, FAKE, ctypes.byref(p), ctypes.byref(r), None, 0, FAKE, None) == INVALID
+    big_t = 200_000           # this layer's workspace at this T is far beyond the scratch
+    assert qe.moe_workspace_size(big_t, 2, 8, 64, 128, 0, 0) > qe.MOE_NOALLOC_SCRATCH_BYTES
+    assert f(FAKE, big_t, FAKE, ctypes.byref(p), ctypes.byref(r), None, 0, FAKE, None) == UNSUPPORTED
+    assert "scratch" in qe.moe_last_error_detail()
+    # sizes the layer itself rejects still name the bad argument
+    bad = _experts(d_model=96)
+    assert f(FAKE, 4, FAKE, ctypes.byref(p), ctypes.byref(bad), None, 0, FAKE, None) == UNSUPPORTED
+    assert f(FAKE, 4, FAKE, ctypes.byref(_params(top_k=9)), ctypes.byref(r), None, 0, FAKE, None) == INVALID
