@@ -217,7 +217,8 @@ __host__ __device__ __forceinline__ size_t scale_index(size_t row, size_t g, siz
 // ---------------------------------------------------------------------------
 // Activations of the f32 path on the f16 matrix cores. Per group of 32 along
 // the reduction axis, a power of two p = 2^(e-15) with max|x| < 2^e over the
-// rows that share an MFMA operand, and x/p split exactly into two f16 parts
+// values that share it (X: the whole batch; H: one row), and x/p split
+// exactly into two f16 parts
 // (hi = f16(x/p), lo = f16(x/p - hi)). Inside each 8-wide slice the parts are
 // stored in the order in which the weight-code conversion produces its
 // operand slots (int8: bytes (0,2),(1,3) of a dword; int4: nibbles (0,4),

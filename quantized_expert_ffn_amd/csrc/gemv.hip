@@ -5,8 +5,8 @@
 //
 // Exact fp32-level activations on f16 matrix cores. For every group of 32
 // along the reduction axis, a power of two p = 2^(e-15) with max|x| < 2^e over
-// the rows that share it (the whole batch for X, a 16-row tile for H) is
-// chosen and x/p (exact) is split into hi = f16(x/p) and lo = f16(x/p - hi):
+// the values that share it (the whole batch for X, one row for H) is chosen
+// and x/p (exact) is split into hi = f16(x/p) and lo = f16(x/p - hi):
 // together 22 significant bits. Weight codes are small integers, exact in f16
 // (f16codes.h). So
 //     sum_k x_k q_k = p * (MFMA(hi, q) + MFMA(lo, q))
@@ -17,8 +17,8 @@
 // Two kernels (the hidden states' f16 parts come from the router, one power
 // of two per 32-group over the batch):
 //   gate/up: per (expert, 32 weight rows): G and U for the expert's tokens,
-//            H = silu(G) * U written straight back as hi/lo + p per (16-row
-//            tile, 32 columns), so the down kernel reads it as it is.
+//            H = silu(G) * U written straight back as hi/lo + p per (row,
+//            32 columns), so the down kernel reads it as it is.
 //   down:    Y = H Wd^T, fp32, rows in permuted order.
 // Weight codes come straight from HBM into operand registers: in the
 // lane-tiled layout one 16-byte load per lane brings a wave the B operands of
@@ -38,8 +38,8 @@ namespace moe {
 
 struct GemvArgs {
     // f32 path: activation parts in slot order (gate/up [T, K] token rows,
-    // down [R, K]) and powers of two (gate/up [K/32]; down [R, K/32] at the
-    // first row of each 16-row tile). Q8_0 path: ahi holds the Q8_0 codes as
+    // down [R, K]) and powers of two (gate/up [K/32]; down [R, K/32], one per
+    // row and group). Q8_0 path: ahi holds the Q8_0 codes as
     // f16 in slot order, alo is unused and apow holds the per-row scales
     // [rows, K/32].
     const _Float16* ahi;
@@ -56,7 +56,7 @@ struct GemvArgs {
     int64_t q_stride, s_stride;   // per expert (bytes, floats)
     int E, K, N, R;
     // gate/up output, as the down kernel reads it: f32 path H as parts +
-    // powers of two ([R, N/32] at the first row of each 16-row tile); Q8_0
+    // powers of two ([R, N/32], one per row and group); Q8_0
     // path H's codes as f16 in hhi and its per-row scales in hpow [R, N/32]
     _Float16* hhi;
     _Float16* hlo;
@@ -104,7 +104,11 @@ __global__ __launch_bounds__(64 * KS) void gemv_kernel(const GemvArgs a) {
     // token measured ~3% slower with it, so they keep the default policy
     constexpr int kCodePolicy = (Q8 || KS == 1) ? kStreamed : 0;
     constexpr bool I2 = FMT == MOE_W_INT2_G32;
-    __shared__ float pwtab[Q8 ? 16 * kMaxGemvGroups : kMaxGemvGroups];   // Q8: [group][16 rows]
+    // the activation side's per-group factors: one per group over the batch
+    // (f32 gate/up), or one per group and row of the 16-row tile, [group][16]
+    // (Q8: the rows' Q8_0 scales; f32 down: H's powers of two per row)
+    constexpr bool kRowFactors = Q8 || !GATEUP;
+    __shared__ float pwtab[kRowFactors ? 16 * kMaxGemvGroups : kMaxGemvGroups];
     __shared__ float red[KS > 1 ? KS - 1 : 1][2][2][4][64];
 
     const int slot = blockIdx.y;
@@ -180,7 +184,7 @@ __global__ __launch_bounds__(64 * KS) void gemv_kernel(const GemvArgs a) {
         const int prow = row_begin + mt + 4 * h;   // output rows 4h .. 4h+3 of the tile
 
         __syncthreads();   // pwtab is written; the previous tile's readers of red are done
-        if constexpr (Q8) {
+        if constexpr (kRowFactors) {
             for (int i = threadIdx.x; i < 16 * G; i += 64 * KS) {
                 const int g = i >> 4, rr = i & 15;
                 float v = 0.0f;
@@ -190,9 +194,6 @@ __global__ __launch_bounds__(64 * KS) void gemv_kernel(const GemvArgs a) {
                 }
                 pwtab[i] = v;
             }
-            __syncthreads();
-        } else if constexpr (!GATEUP) {
-            for (int i = threadIdx.x; i < G; i += 64 * KS) pwtab[i] = a.apow[(size_t)(row_begin + mt) * G + i];
             __syncthreads();
         }
 
@@ -259,8 +260,8 @@ __global__ __launch_bounds__(64 * KS) void gemv_kernel(const GemvArgs a) {
             const int p = c0 + j;
             float pw0 = 0.0f, pw1 = 0.0f;
             float4 sx[2];
-            if constexpr (Q8) {
-                // activation scales of the lane's rows 4h .. 4h+3, both groups
+            if constexpr (kRowFactors) {
+                // activation factors of the lane's rows 4h .. 4h+3, both groups
                 sx[0] = *reinterpret_cast<const float4*>(&pwtab[(2 * p) * 16 + 4 * h]);
                 sx[1] = *reinterpret_cast<const float4*>(&pwtab[(2 * p + 1) * 16 + 4 * h]);
             } else {
@@ -336,7 +337,7 @@ __global__ __launch_bounds__(64 * KS) void gemv_kernel(const GemvArgs a) {
                         acc[t][1][1] = fmaf(d1[1], s1 * x.y, acc[t][1][1]);
                         acc[t][1][2] = fmaf(d1[2], s1 * x.z, acc[t][1][2]);
                         acc[t][1][3] = fmaf(d1[3], s1 * x.w, acc[t][1][3]);
-                    } else {
+                    } else if constexpr (GATEUP) {
                         d0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(xl[jj][gi], b0, d0, 0, 0, 0);
                         d1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(xl[jj][gi], b1, d1, 0, 0, 0);
                         const float f0 = ROW ? pw : sc[t][2 * gi] * pw;
@@ -346,6 +347,20 @@ __global__ __launch_bounds__(64 * KS) void gemv_kernel(const GemvArgs a) {
                             acc[t][0][i] = fmaf(d0[i], f0, acc[t][0][i]);
                             acc[t][1][i] = fmaf(d1[i], f1, acc[t][1][i]);
                         }
+                    } else {
+                        // f32 down: H's power of two differs per row
+                        d0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(xl[jj][gi], b0, d0, 0, 0, 0);
+                        d1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(xl[jj][gi], b1, d1, 0, 0, 0);
+                        const float4 x = sx[gi];
+                        const float s0 = ROW ? 1.0f : sc[t][2 * gi], s1 = ROW ? 1.0f : sc[t][2 * gi + 1];
+                        acc[t][0][0] = fmaf(d0[0], s0 * x.x, acc[t][0][0]);
+                        acc[t][0][1] = fmaf(d0[1], s0 * x.y, acc[t][0][1]);
+                        acc[t][0][2] = fmaf(d0[2], s0 * x.z, acc[t][0][2]);
+                        acc[t][0][3] = fmaf(d0[3], s0 * x.w, acc[t][0][3]);
+                        acc[t][1][0] = fmaf(d1[0], s1 * x.x, acc[t][1][0]);
+                        acc[t][1][1] = fmaf(d1[1], s1 * x.y, acc[t][1][1]);
+                        acc[t][1][2] = fmaf(d1[2], s1 * x.z, acc[t][1][2]);
+                        acc[t][1][3] = fmaf(d1[3], s1 * x.w, acc[t][1][3]);
                     }
                 }
             }
@@ -446,45 +461,37 @@ __global__ __launch_bounds__(64 * KS) void gemv_kernel(const GemvArgs a) {
             }
         } else if constexpr (GATEUP) {
             // H = silu(G) * U for tokens 4h + i and columns nl, 16 + nl of the
-            // tile: 16 tokens x 32 columns, one group of the down projection's
-            // reduction axis, one power of two for all of it
-            float hv[2][4], am = 0.0f;
+            // tile: per token, 32 columns (one group of the down projection's
+            // reduction axis) under one power of two of their own
+            const int GN = N / kGroup;
+            float hv[2][4];
 #pragma unroll
-            for (int r = 0; r < 2; ++r)
+            for (int i = 0; i < 4; ++i) {
+                hv[0][i] = (4 * h + i < rows_here) ? silu(acc[0][0][i]) * acc[1][0][i] : 0.0f;
+                hv[1][i] = (4 * h + i < rows_here) ? silu(acc[0][1][i]) * acc[1][1][i] : 0.0f;
+                // the token's 32 columns sit in the 16 lanes of this DPP row
+                float am = fmaxf(fabsf(hv[0][i]), fabsf(hv[1][i]));
+                am = fmaxf(am, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(am), 0xB1, 0xF, 0xF, true)));
+                am = fmaxf(am, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(am), 0x4E, 0xF, 0xF, true)));
+                am = fmaxf(am, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(am), 0x141, 0xF, 0xF, true)));
+                am = fmaxf(am, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(am), 0x140, 0xF, 0xF, true)));
+                const int ex = pow2_exponent(am);
+                const float up = ldexpf(1.0f, 15 - ex);
+                if (4 * h + i < rows_here) {
+                    const size_t row = (size_t)(prow + i);
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    hv[r][i] = (4 * h + i < rows_here) ? silu(acc[0][r][i]) * acc[1][r][i] : 0.0f;
-                    am = fmaxf(am, fabsf(hv[r][i]));
-                }
-            am = fmaxf(am, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(am), 0xB1, 0xF, 0xF, true)));
-            am = fmaxf(am, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(am), 0x4E, 0xF, 0xF, true)));
-            am = fmaxf(am, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(am), 0x141, 0xF, 0xF, true)));
-            am = fmaxf(am, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(am), 0x140, 0xF, 0xF, true)));
-            {
-                const float r0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(am), 0));
-                const float r1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(am), 16));
-                const float r2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(am), 32));
-                const float r3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(am), 48));
-                am = fmaxf(fmaxf(r0, r1), fmaxf(r2, r3));
-            }
-            const int ex = pow2_exponent(am);
-            const float up = ldexpf(1.0f, 15 - ex);
-#pragma unroll
-            for (int r = 0; r < 2; ++r) {
-                const int kk = 16 * r + nl;                       // k of this column inside the group
-                const int pos = 8 * (kk >> 3) + k_slot(FMT, kk & 7);
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    if (4 * h + i < rows_here) {
+                    for (int r = 0; r < 2; ++r) {
+                        const int kk = 16 * r + nl;                       // k of this column inside the group
+                        const int pos = 8 * (kk >> 3) + k_slot(FMT, kk & 7);
                         const float sv = hv[r][i] * up;
                         const _Float16 hh = (_Float16)sv;
-                        const size_t off = (size_t)(prow + i) * N + (size_t)tile[0] * kGroup + pos;
+                        const size_t off = row * N + (size_t)tile[0] * kGroup + pos;
                         a.hhi[off] = hh;
                         a.hlo[off] = (_Float16)(sv - (float)hh);
                     }
+                    if (nl == 0) a.hpow[row * GN + tile[0]] = ldexpf(1.0f, ex - 15);
                 }
             }
-            if (lane == 0) a.hpow[(size_t)(row_begin + mt) * n_tiles + tile[0]] = ldexpf(1.0f, ex - 15);
         } else {
 #pragma unroll
             for (int t = 0; t < 2; ++t) {

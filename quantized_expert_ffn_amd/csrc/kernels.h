@@ -65,8 +65,8 @@ hipError_t launch_plan(const int* counts, const int* offsets, const int* perm, i
 
 // Decode path (fp32 activations). gate/up: A = the token rows' f16 parts
 // [T, d] (read through row_token) with one power of two per 32-group, [d/32];
-// it writes H's parts [R, I] with one power per (16-row tile of a slot,
-// 32-group), [R, I/32]. down: A = H's parts -> Y fp32 [R, d].
+// it writes H's parts [R, I] with one power of two per (row, 32-group),
+// [R, I/32]. down: A = H's parts -> Y fp32 [R, d].
 // q8 (small-batch Q8_0 path): A = Q8_0 codes as f16 in slot order with
 // per-row scales in apow ([rows, K/32]); gate/up writes H's Q8_0 codes to hhi
 // and its per-row scales to hpow; alo and hlo are unused. Every slot must

@@ -123,7 +123,8 @@ def workspace_sections(ws: torch.Tensor, T: int, shape, act_mode: str, has_share
         order = SLOT_K[shape.wformat.split("_")[0]]
         nat = np.empty_like(codes)
         nat[:, :, order] = codes
-        out["hq"] = nat.reshape(R, I).astype(np.int64)
+        # rows no slot was dispatched to hold whatever the workspace held
+        out["hq"] = np.where(np.isfinite(nat), nat, 0).reshape(R, I).astype(np.int64)
         out["hd"] = take("h_scales", np.float32, R * (I // 32)).reshape(R, I // 32)
     return out
 

@@ -651,3 +651,44 @@ def test_block_forward_full_size(wname):
         rows = np.sort(np.random.default_rng(6).choice(wl.tokens, SAMPLE, replace=False))
     ref = oracle_block(shape, x[rows], wl.act_mode, gamma, 1e-5, name=shape.name)
     assert_close_rel(got[rows] - x[rows], ref["out"] - x[rows].astype(np.float64), what=f"{wname} block layer part")
+
+
+# ---------------------------------------------------------------------------
+# tokens of very different magnitudes in one batch
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("act_mode", ["f32", "q8_0"])
+@pytest.mark.parametrize("name", ["tiny", "tiny_int4", "tiny_shared_noaux", "olmoe", "glm"])
+def test_layer_mixed_token_magnitudes(name, act_mode):
+    """16 tokens whose rows are scaled by 2^-10 .. 2^10. Every token is checked
+    against the oracle relative to its own largest output: the f32 path keeps
+    one power of two per 32-column group of X over the whole batch and one per
+    row and group of H, so a small token next to a large one keeps its own
+    precision. Tokens whose top-k boundary lies within fp32 rounding of their
+    own logits are left out of the comparison."""
+    need_gpu()
+    T = 16
+    if name in ("olmoe", "glm"):
+        shape, dl, key = synth.LAYERS[name], device_layer(name), name
+    else:
+        shape, dl = tiny_layer(name)
+        key = shape
+    scales = np.exp2(np.linspace(-10.0, 10.0, T))
+    x = (synth.activations(shape, T) * scales[:, None]).astype(np.float32)
+    got = run_layer(dl, x, act_mode)
+    ref = oracle_layer(shape, x, act_mode, name=key)
+    spec = router_spec(shape)
+    keys = orouter.selection_keys(ref["logits"], spec.mode, spec.bias, spec.n_group, spec.topk_group)
+    margin = orouter.boundary_margin(keys, spec.top_k)
+    if spec.mode == "noaux_tc":
+        margin = np.minimum(margin, orouter.group_margin(ref["logits"], spec.bias, spec.n_group, spec.topk_group))
+    key_scale = np.abs(np.where(np.isfinite(keys), keys, 0.0)).max(axis=1)   # ineligible experts hold -inf
+    settled = margin >= 1e-5 * key_scale + 1e-30
+    assert settled.sum() >= T - 2
+    worst = 0.0
+    for t in np.nonzero(settled)[0]:
+        scale = np.abs(ref["out"][t]).max()
+        err = np.abs(got[t] - ref["out"][t]).max() / scale
+        worst = max(worst, err)
+        assert err <= REL_TOL, f"token {t} (row scale 2^{np.log2(scales[t]):.1f}): rel err {err:.3e}"
+    say(f"[mixed] {name}/{act_mode}: worst per-token rel err {worst:.3e} over {int(settled.sum())} tokens "
+        f"(row scales 2^-10 .. 2^10)")
