@@ -65,5 +65,38 @@ def build(verbose: bool = True) -> str:
     return LIB
 
 
+# The host ABI check: the ABI layer's translation unit with AddressSanitizer
+# on its host code only (the device code of that file is unchanged), linked
+# with the kernels' objects and a driver that exercises every host-side
+# check without a GPU.
+ASAN_HOST = "-Xarch_host -fsanitize=address -Xarch_host -fno-omit-frame-pointer".split()
+
+
+def build_host_check(out_dir: str, driver: str) -> str:
+    """Build the AddressSanitizer host check of the ABI layer into out_dir and
+    return the executable's path. The kernels' objects come from _build/ (the
+    library is built first when they are missing)."""
+    os.makedirs(out_dir, exist_ok=True)
+    sources = sorted(glob.glob(os.path.join(CSRC, "*.hip")))
+    kernel_objs = [os.path.join(BUILD, os.path.basename(s) + ".o") for s in sources
+                   if os.path.basename(s) != "abi.hip"]
+    if not all(os.path.exists(o) for o in kernel_objs):
+        build(verbose=False)
+    flags = ["-O1", "-g", "-std=c++17", f"--offload-arch={ARCH}", "-I", INCLUDE, "-I", CSRC] + DEVICE_FLAGS
+    abi_obj = os.path.join(out_dir, "abi_asan.o")
+    drv_obj = os.path.join(out_dir, "driver_asan.o")
+    exe = os.path.join(out_dir, "abi_host_check")
+    steps = [
+        [hipcc()] + flags + ASAN_HOST + ["-c", os.path.join(CSRC, "abi.hip"), "-o", abi_obj],
+        [hipcc()] + flags + ASAN_HOST + ["-x", "hip", "-c", driver, "-o", drv_obj],
+        [hipcc(), f"--offload-arch={ARCH}"] + ASAN_HOST + ["-o", exe, drv_obj, abi_obj] + kernel_objs,
+    ]
+    for cmd in steps:
+        res = subprocess.run(cmd, capture_output=True, text=True)
+        if res.returncode != 0:
+            raise RuntimeError(f"host check build failed: {' '.join(cmd)}\n{res.stdout}\n{res.stderr}")
+    return exe
+
+
 if __name__ == "__main__":
     build()

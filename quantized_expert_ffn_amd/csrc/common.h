@@ -28,7 +28,7 @@ struct WsLayout {
     size_t inv_perm = 0;   // i32  [T*k]
     size_t row_token = 0;  // i32  [T*k + T]   permuted row -> token
     size_t slots = 0;      // i32  [E + 1][4]  (expert, row_begin, n_rows, 0)
-    size_t tiles = 0;      // i32  [max_tiles][4] (expert, row_begin, row_end, 0)
+    size_t tiles = 0;      // i32  [max_tiles][4] (expert, row_begin, row_end, 0); row_end == row_begin: empty
     size_t meta = 0;       // i32  [4]  n_slots, n_tiles, status, 0
     size_t xq = 0;         // Q8_0: f16 codes [T, d]  F32: f16 hi parts [T, d]
     size_t xd = 0;         // Q8_0: f32 [T, d/32]  F32: f16 lo parts [T, d]
@@ -98,8 +98,10 @@ inline WsLayout ws_layout(int T, int k, int E, int d, int I, int act_mode, int h
     auto take = [&](size_t bytes) { size_t o = off; off = align256(off + (bytes ? bytes : 1)); return o; };
     const size_t n = (size_t)T * k;
     const size_t R = n + (has_shared ? (size_t)T : 0);
+    // full and partial tiles, plus up to 7 empty ones that even the full
+    // tiles out over the 8 XCDs
     L.max_tiles = (int)((n + kTileRows - 1) / kTileRows + (size_t)(E < (long long)n ? E : n) +
-                        (has_shared ? (T + kTileRows - 1) / kTileRows : 0));
+                        (has_shared ? (T + kTileRows - 1) / kTileRows : 0)) + (n > 0 ? 7 : 0);
     const int S = router_splits(T, E, d);
     const int SL = router_slices(T, E, d, false);   // the most slices any path writes
     L.logits = take((size_t)SL * T * E * 4);

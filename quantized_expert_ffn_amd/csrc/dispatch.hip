@@ -95,10 +95,20 @@ __device__ __forceinline__ int tile_class(int r, int tile_rows) {
 
 // Work lists from counts/offsets (thread e < E holds counts[e], offsets[e]).
 // Slots are in expert order (the shared expert last). Tiles are ordered by
-// size, largest first: every full tile (routed experts in expert order, then
-// the shared expert's), then the partial tiles class by class (tile_class);
-// a grid that walks the list in order then ends on its cheapest blocks. Each
-// tile computes only its own rows, so the order changes no result.
+// size, largest first: every full tile, then the partial tiles class by
+// class (tile_class); a grid that walks the list in order then ends on its
+// cheapest blocks. Each tile computes only its own rows, so the order
+// changes no result.
+// The prefill kernels run tile position p on XCD p % 8 (blocks are dealt to
+// the XCDs in turn), and each XCD walks its positions in order. The full
+// tiles (routed experts in expert order, then the shared expert's) are cut
+// into 8 contiguous runs of ceil(n_full / 8) tiles, and run x takes
+// positions x, x + 8, x + 16, ...: every XCD gets the same number of full
+// tiles, and an expert's tiles sit on one XCD (two where a run boundary cuts
+// it, more only for an expert larger than a run), one after the other, so
+// its weights leave HBM for that XCD's L2 about once. The up to 7 positions
+// past the last run's end hold empty tiles (no rows), which the kernels
+// skip.
 __device__ __forceinline__ void build_work_lists(int E, int cnt, int off, int n_rows_routed, int T, int has_shared,
                                  int tile_rows, int* scan_tmp, int* __restrict__ slots, int* __restrict__ tiles,
                                  int* __restrict__ meta) {
@@ -117,18 +127,21 @@ __device__ __forceinline__ void build_work_lists(int E, int cnt, int off, int n_
     const int cls = part > 0 ? tile_class(part, tile_rows) : -1;
     int n_full = 0;
     const int fbase = block_exclusive_scan(full, scan_tmp, &n_full);
-    for (int i = 0; i < full; ++i) {
-        const int rb = off + i * tile_rows;
-        tl[fbase + i] = make_int4(e, rb, rb + tile_rows, 0);
-    }
     const int s_full = has_shared ? T / tile_rows : 0;
     const int s_part = has_shared ? T - s_full * tile_rows : 0;
     const int s_cls = s_part > 0 ? tile_class(s_part, tile_rows) : -1;
+    const int run = (n_full + s_full + 7) / 8;                    // full tiles per XCD
+    auto fpos = [run](int f) { return (f % run) * 8 + f / run; };  // f-th full tile -> position
+    for (int i = 0; i < full; ++i) {
+        const int rb = off + i * tile_rows;
+        tl[fpos(fbase + i)] = make_int4(e, rb, rb + tile_rows, 0);
+    }
     for (int i = threadIdx.x; i < s_full; i += blockDim.x) {
         const int rb = n_rows_routed + i * tile_rows;
-        tl[n_full + i] = make_int4(E, rb, rb + tile_rows, 0);
+        tl[fpos(n_full + i)] = make_int4(E, rb, rb + tile_rows, 0);
     }
-    int pos = n_full + s_full;
+    for (int f = n_full + s_full + threadIdx.x; f < 8 * run; f += blockDim.x) tl[fpos(f)] = make_int4(0, 0, 0, 0);
+    int pos = 8 * run;
 #pragma unroll 1
     for (int c = 1; c <= 4; ++c) {
         int n_c = 0;
@@ -589,7 +602,7 @@ __global__ __launch_bounds__(kDispThreads) void plan_kernel(const int* __restric
     // A caller's counts / offsets are clamped so that every row stays inside
     // the permuted range [0, T*k) and the counts sum to at most T*k: then
     // the tiles number at most ceil(T*k / tile_rows) + min(E, T*k) (plus the
-    // shared expert's), the size of the tile list. Counts and offsets that
+    // shared expert's and up to 7 empty ones), the size of the tile list. Counts and offsets that
     // are not the exclusive prefix sum of each other set the status flag
     // meta[2] (the results are then unspecified, but every access stays in
     // bounds).

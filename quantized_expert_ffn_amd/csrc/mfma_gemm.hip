@@ -313,6 +313,7 @@ __global__ __launch_bounds__(256) void q8_mfma_kernel(const MfmaArgs a) {
     const int tile_id = (sl / ncol) * 8 + xcd;
     if (tile_id >= a.meta[1]) return;
     const int4 td = a.tiles[tile_id];
+    if (td.z <= td.y) return;   // an empty tile (evens the full tiles out over the XCDs)
 
     TileCtx c;
     c.e = td.x;

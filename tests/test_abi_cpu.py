@@ -308,3 +308,20 @@ def test_noalloc_entry_point_checks_before_any_gpu_call(lib):
     bad = _experts(d_model=96)
     assert f(FAKE, 4, FAKE, ctypes.byref(p), ctypes.byref(bad), None, 0, FAKE, None) == UNSUPPORTED
     assert f(FAKE, 4, FAKE, ctypes.byref(_params(top_k=9)), ctypes.byref(r), None, 0, FAKE, None) == INVALID
+
+
+def test_host_abi_layer_under_address_sanitizer(tmp_path):
+    """The ABI layer's host code built with AddressSanitizer (its device code
+    and the kernels unchanged) and driven through every host-side check of
+    tests/abi_host_check.cpp without a GPU: the validation tables, a sweep of
+    workspace sizes and sections from 1 to 65536 tokens and 1 to 1024
+    experts, the error details. Any out-of-bounds or use-after-free access in
+    that code ends the run with a sanitizer report."""
+    import subprocess
+    from quantized_expert_ffn_amd import build as qbuild
+    exe = qbuild.build_host_check(str(tmp_path), os.path.join(ROOT, "tests", "abi_host_check.cpp"))
+    assert b"__asan_report_load" in open(exe, "rb").read(), "the check was not built with the sanitizer"
+    res = subprocess.run([exe], capture_output=True, text=True, timeout=300)
+    assert "AddressSanitizer" not in res.stderr, res.stderr[-4000:]
+    assert res.returncode == 0, res.stdout + res.stderr[-4000:]
+    assert "passed" in res.stdout
