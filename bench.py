@@ -92,12 +92,12 @@ def stream_read_ceiling(dev, reps: int = 5) -> float:
 
 def prefill_mix_ceiling(dev, reps: int = 5) -> float:
     """What the prefill GEMM's inner loop reaches with its operands resident in
-    LDS (include/moe_calib.h): best of `reps` launches of 768 blocks (three
-    per CU), useful int8 TOPS."""
+    LDS (include/moe_calib.h): best of `reps` launches of 512 blocks of eight
+    waves (two per CU, as the GEMM runs), useful int8 TOPS."""
     import torch
     import quantized_expert_ffn_amd as qe
-    blocks, stages = 768, 200
-    sink = torch.empty(blocks * 256, dtype=torch.float32, device=dev)
+    blocks, stages = 512, 300
+    sink = torch.empty(blocks * 512, dtype=torch.float32, device=dev)
     qe.moe_calib_prefill_mix(blocks, stages, sink)
     best = 0.0
     for _ in range(reps):

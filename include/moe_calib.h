@@ -33,12 +33,12 @@ moe_status moe_calib_stream_read(const void* buf, uint64_t bytes, uint32_t* sink
                                  hipStream_t stream);
 
 /* The prefill grouped GEMM's inner loop alone: each of `blocks` workgroups of
- * four waves runs the GEMM's stage computation (int4 weight codes with group
+ * eight waves runs the GEMM's stage computation (int4 weight codes with group
  * scales, eight 16-token tiles, two 16-row weight halves per wave; see
  * moe.h, moe_expert_ffn with MOE_ACT_Q8_0) `stages` times over operands that
  * stay in LDS: no global memory, no barriers. Its rate bounds what that
  * instruction mix can reach. Writes one float per thread to sink
- * (device fp32 [blocks * 256]) so no work can be dropped, and, if ops is
+ * (device fp32 [blocks * 512]) so no work can be dropped, and, if ops is
  * not NULL, the useful int8 operations the launch performs to *ops (host):
  * 2 * 16 * 16 * 32 per matrix-core product.
  * Returns MOE_ERR_INVALID_ARG for a null sink, blocks < 1, or a stage count

@@ -323,7 +323,9 @@ def moe_calib_stream_read(buf: torch.Tensor, sink: torch.Tensor, blocks: int, st
 
 def moe_calib_prefill_mix(blocks: int, stages: int, sink: torch.Tensor, stream=None) -> int:
     """The prefill GEMM's inner loop alone (include/moe_calib.h); sink: fp32
-    [blocks * 256] device tensor. Returns the useful int8 operations launched."""
+    [blocks * 512] device tensor. Returns the useful int8 operations launched."""
+    if sink.numel() < blocks * 512:
+        raise ValueError(f"sink holds {sink.numel()} floats, the launch writes {blocks * 512}")
     ops = ctypes.c_uint64(0)
     _check(load().moe_calib_prefill_mix(blocks, stages, _ptr(sink, torch.float32, "sink"), ctypes.byref(ops),
                                         _stream(stream)), "moe_calib_prefill_mix")

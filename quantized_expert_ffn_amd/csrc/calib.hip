@@ -59,23 +59,25 @@ __global__ __launch_bounds__(kStreamThreads) void stream_read_kernel(const uint8
 // 16-token tiles live) over and over on one stage of operands resident in
 // LDS: the instruction mix of its inner loop alone. Two stage buffers are
 // allocated and alternated, as in the GEMM, so the occupancy is the same
-// (three blocks of four waves per CU). Operands: token codes 1, weight codes
+// (two blocks of eight waves per CU). Operands: token codes 1, weight codes
 // 1, activation scales 1, weight scales 2^-20 (the sums stay finite).
 constexpr int kMixLive = 8;
-__global__ __launch_bounds__(256) void prefill_mix_kernel(int stages, float* __restrict__ sink) {
+constexpr int kMixThreads = 64 * kGemmWaves;
+__global__ __launch_bounds__(kMixThreads) void prefill_mix_kernel(int stages, float* __restrict__ sink) {
     constexpr int FMT = MOE_W_INT4_G32;
-    constexpr int kStage = kLdsTok + 4 * 1024 + kLdsSX + kLdsSW;
+    constexpr int kW = lds_w_bytes<FMT>();
+    constexpr int kStage = lds_gemm_buffer_bytes<FMT>();
     __shared__ __attribute__((aligned(1024))) uint8_t lds0[kStage];
     __shared__ __attribute__((aligned(1024))) uint8_t lds1[kStage];
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     for (int b = 0; b < 2; ++b) {
         uint32_t* w = reinterpret_cast<uint32_t*>(b ? lds1 : lds0);
-        for (int i = tid; i < kLdsTok / 4; i += 256) w[i] = 0x3C003C00u;                    // f16 1.0, 1.0
-        for (int i = tid; i < 4 * 1024 / 4; i += 256) w[kLdsTok / 4 + i] = 0x11111111u;      // int4 codes 1
-        float* f = reinterpret_cast<float*>(b ? lds1 : lds0) + (kLdsTok + 4 * 1024) / 4;
-        for (int i = tid; i < kLdsSX / 4; i += 256) f[i] = 1.0f;
-        for (int i = tid; i < kLdsSW / 4; i += 256) f[kLdsSX / 4 + i] = 0x1p-20f;
+        for (int i = tid; i < kLdsTok / 4; i += kMixThreads) w[i] = 0x3C003C00u;             // f16 1.0, 1.0
+        for (int i = tid; i < kW / 4; i += kMixThreads) w[kLdsTok / 4 + i] = 0x11111111u;     // int4 codes 1
+        float* f = reinterpret_cast<float*>(b ? lds1 : lds0) + (kLdsTok + kW) / 4;
+        for (int i = tid; i < kLdsSX / 4; i += kMixThreads) f[i] = 1.0f;
+        for (int i = tid; i < kLdsSW / 4; i += kMixThreads) f[kLdsSX / 4 + i] = 0x1p-20f;
     }
     __syncthreads();
     auto opaque = [](int v) __attribute__((always_inline)) {
@@ -83,8 +85,8 @@ __global__ __launch_bounds__(256) void prefill_mix_kernel(int stages, float* __r
         return v;
     };
     const int nl = lane & 15, rq = lane >> 4;
-    const StageOffsets o{opaque(lane * 16), opaque(kLdsTok + wave * 1024 + lane * 16), opaque(kLdsTok + 4096 + nl * 4),
-                         opaque(kLdsTok + 4096 + kLdsSX + wave * 256 + rq * 64)};
+    const StageOffsets o{opaque(lane * 16), opaque(kLdsTok + lds_w_wave<FMT>(wave) + lane * 16),
+                         opaque(kLdsTok + kW + nl * 4), opaque(kLdsTok + kW + kLdsSX + wave * 256 + rq * 64)};
     v4f acc[kMixLive][2];
 #pragma unroll
     for (int i = 0; i < kMixLive; ++i)
@@ -100,7 +102,7 @@ __global__ __launch_bounds__(256) void prefill_mix_kernel(int stages, float* __r
     for (int i = 0; i < kMixLive; ++i)
 #pragma unroll
         for (int hh = 0; hh < 2; ++hh) sum += acc[i][hh][0] + acc[i][hh][1] + acc[i][hh][2] + acc[i][hh][3];
-    sink[(size_t)blockIdx.x * 256 + tid] = sum;
+    sink[(size_t)blockIdx.x * kMixThreads + tid] = sum;
 }
 
 }  // namespace moe
@@ -108,8 +110,8 @@ __global__ __launch_bounds__(256) void prefill_mix_kernel(int stages, float* __r
 extern "C" moe_status moe_calib_prefill_mix(int32_t blocks, int32_t stages, float* sink, uint64_t* ops,
                                             hipStream_t stream) {
     if (sink == nullptr || blocks < 1 || stages < 2 || (stages & 1)) return MOE_ERR_INVALID_ARG;
-    if (ops) *ops = (uint64_t)blocks * stages * 4 /* waves */ * (2 * moe::kMixLive * 2) /* products */ * 16384;
-    hipLaunchKernelGGL(moe::prefill_mix_kernel, dim3(blocks), dim3(256), 0, stream, stages, sink);
+    if (ops) *ops = (uint64_t)blocks * stages * moe::kGemmWaves * (2 * moe::kMixLive * 2) /* products */ * 16384;
+    hipLaunchKernelGGL(moe::prefill_mix_kernel, dim3(blocks), dim3(moe::kMixThreads), 0, stream, stages, sink);
     return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_HIP;
 }
 

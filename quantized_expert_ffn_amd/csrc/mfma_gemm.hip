@@ -20,10 +20,11 @@
 // per-row formats) the group's factor is sx alone, one operation per output
 // and group, and the row's scale multiplies the finished sum.
 //
-// Block tile: 128 token rows (one work-list tile: rows of one expert) x four
-// 32-row weight tiles; four waves, each owning ONE weight tile (gate/up: two
-// gate tiles and the same two up tiles; down: four adjacent tiles) for ALL of
-// the block's token rows. The weights are the matrix core's A operand (output
+// Block tile: 128 token rows (one work-list tile: rows of one expert) x eight
+// 32-row weight tiles; eight waves, each owning ONE weight tile (gate/up: four
+// gate tiles and the same four up tiles; down: eight adjacent tiles) for ALL
+// of the block's token rows. The eight waves share each staged token tile, and
+// two blocks (four waves per SIMD) fit a CU. The weights are the matrix core's A operand (output
 // rows = weight rows) and the token codes its B operand (output columns =
 // tokens), so
 //   - a wave converts each weight code to f16 once and uses it for every
@@ -37,7 +38,8 @@
 // tile's row count are neither loaded nor multiplied: the live count (1, 2,
 // 4 or 8 tiles) is a compile-time constant of the whole K loop, chosen once
 // per block, so no branch ever separates a product from its use.
-//   gate/up kernel: the up waves hand U to the gate waves through LDS, which
+//   gate/up kernel: the up waves hand U to the gate waves through LDS (the
+//     stage buffers, free after the K loop), and the gate waves
 //     form H = silu(G) * U and quantise it (Q8_0, one group = the 32 outputs
 //     of a weight tile) in registers; H leaves as f16 codes in operand-slot
 //     order + one fp32 scale per 32, ready to be the down kernel's B operand.
@@ -104,7 +106,7 @@ struct TileCtx {
     int lane, wave, nl, rq;
     const float* wsb;               // this wave's matrix scales (expert base)
     __amdgpu_buffer_rsrc_t ra, rsx, rw, rsw;
-    uint32_t tok_off[2];            // per-lane source offsets of this wave's token-tile loads
+    uint32_t tok_off;               // per-lane source offset of this wave's token-tile loads
     uint32_t sx_off;                // per-lane source offset of this wave's scale load
 };
 
@@ -116,38 +118,35 @@ __device__ __forceinline__ void gemm_tile(const MfmaArgs& a, const TileCtx& c, l
     const int P = c.P, NT = c.NT;
     const int ttl = min(c.tt, NT - 1);   // tile index for loads
 
-    // Stage jobs, each a wave-wide direct load; job j runs on wave j % 4
-    // (wave-uniform): token tiles i = wave and wave + 4 of both groups (live
-    // ones only), this wave's weight block(s), a quarter of the activation
-    // scales, and this wave's weight scale block.
+    // Stage jobs, each a wave-wide direct load (wave-uniform): token tile
+    // i = wave of both groups (live tiles only), this wave's weight
+    // block(s), a quarter of the activation scales (waves 0 .. 3), and this
+    // wave's weight scale block.
     auto issue_stage = [&](int pc, lds_byte* base) __attribute__((always_inline)) {
         lds_byte* TOK = base;
         lds_byte* W = base + kLdsTok;
         lds_byte* SX = W + kW;
         lds_byte* SW = SX + kLdsSX;
+        if (wave < LIVE) {
 #pragma unroll
-        for (int s = 0; s < 2; ++s) {
-            const int i = wave + 4 * s;
-            if (i < LIVE) {
-#pragma unroll
-                for (int g = 0; g < 2; ++g)
-                    buffer_load_lds<16>(c.ra, c.tok_off[s], (2 * pc + g) * kGroup * 2, TOK + (g * kM16 + i) * 1024);
-            }
+            for (int g = 0; g < 2; ++g)
+                buffer_load_lds<16>(c.ra, c.tok_off, (2 * pc + g) * kGroup * 2, TOK + (g * kM16 + wave) * 1024);
         }
         if constexpr (FMT == MOE_W_INT8_G32) {
 #pragma unroll
             for (int g = 0; g < 2; ++g)
-                buffer_load_lds<16>(c.rw, lane * 16, ((2 * pc + g) * NT + ttl) * 1024, W + (wave * 2 + g) * 1024);
+                buffer_load_lds<16>(c.rw, lane * 16, ((2 * pc + g) * NT + ttl) * 1024,
+                                    W + lds_w_wave<FMT>(wave) + g * 1024);
         } else if constexpr (FMT == MOE_W_INT2_G32) {
             // dwords 2 (pc % 2) + g of each lane's 16 bytes in the quad block
 #pragma unroll
             for (int g = 0; g < 2; ++g)
                 buffer_load_lds<4>(c.rw, lane * 16, ((pc >> 1) * NT + ttl) * 1024 + (2 * (pc & 1) + g) * 4,
-                                   W + (wave * 2 + g) * 256);
+                                   W + lds_w_wave<FMT>(wave) + g * 256);
         } else {
-            buffer_load_lds<16>(c.rw, lane * 16, (pc * NT + ttl) * 1024, W + wave * 1024);
+            buffer_load_lds<16>(c.rw, lane * 16, (pc * NT + ttl) * 1024, W + lds_w_wave<FMT>(wave));
         }
-        buffer_load_lds<4>(c.rsx, c.sx_off, 2 * pc * 4, SX + wave * 256);
+        if (wave < 4) buffer_load_lds<4>(c.rsx, c.sx_off, 2 * pc * 4, SX + wave * 256);
         if constexpr (!ROW) buffer_load_lds<4>(c.rsw, lane * 4, pc * 256, SW + wave * 256);
     };
 
@@ -161,9 +160,7 @@ __device__ __forceinline__ void gemm_tile(const MfmaArgs& a, const TileCtx& c, l
         return v;
     };
     const int oTok = opaque(lane * 16);
-    const int oW = opaque(kLdsTok + (FMT == MOE_W_INT2_G32 ? wave * 2 * 256 + lane * 4
-                                                           : (FMT == MOE_W_INT8_G32 ? wave * 2 : wave) * 1024 +
-                                                                 lane * 16));
+    const int oW = opaque(kLdsTok + lds_w_wave<FMT>(wave) + (FMT == MOE_W_INT2_G32 ? lane * 4 : lane * 16));
     const int oSX = opaque(kLdsTok + kW + nl * 4);
     const int oSW = opaque(kLdsTok + kW + kLdsSX + wave * 256 + rq * 64);
 
@@ -182,7 +179,7 @@ __device__ __forceinline__ void gemm_tile(const MfmaArgs& a, const TileCtx& c, l
                 const int g = st / LIVE, i = st % LIVE;
                 const int col = c.tt * kTile + 16 * hh + 4 * rq;   // weight rows col .. col + 3
                 const int row = 16 * i + nl;                       // token row of the block
-                int32_t* dst = (GATEUP && (wave >> 1)) ? a.dbg1 : a.dbg0;
+                int32_t* dst = (GATEUP && (wave >> 2)) ? a.dbg1 : a.dbg0;
                 if (row < c.rows && c.tt < NT) {
 #pragma unroll
                     for (int r = 0; r < 4; ++r)
@@ -228,11 +225,12 @@ __device__ __forceinline__ void gemm_tile(const MfmaArgs& a, const TileCtx& c, l
         }
     }
     if constexpr (GATEUP) {
-        // up waves (2, 3) hand U to the gate waves (0, 1) of the same tile
-        // through the stage buffers (free after the loop's last barrier):
-        // wave 2 -> 0 in buf0, wave 3 -> 1 in buf1, lane-major float4s
-        lds_byte* xb = (wave & 1) ? buf1 : buf0;
-        if (wave >= 2) {
+        // up waves (4 .. 7) hand U to the gate waves (0 .. 3) of the same
+        // tile through the stage buffers (free after the loop's last
+        // barrier): waves 4, 5 -> 0, 1 in the two halves of buf0, waves 6, 7
+        // -> 2, 3 in those of buf1; lane-major float4s, 16 KB per wave
+        lds_byte* xb = ((wave >> 1) & 1 ? buf1 : buf0) + (wave & 1) * kHandoverBytes;
+        if (wave >= 4) {
 #pragma unroll
             for (int i = 0; i < LIVE; ++i)
 #pragma unroll
@@ -241,7 +239,7 @@ __device__ __forceinline__ void gemm_tile(const MfmaArgs& a, const TileCtx& c, l
                         acc[i][hh];
         }
         __syncthreads();
-        if (wave >= 2) return;
+        if (wave >= 4) return;
         const int GN = c.N / kGroup;
 #pragma unroll
         for (int i = 0; i < LIVE; ++i) {
@@ -293,13 +291,12 @@ __device__ __forceinline__ void gemm_tile(const MfmaArgs& a, const TileCtx& c, l
 }
 
 template <int FMT, bool GATEUP, bool DBG, bool ROW>
-__global__ __launch_bounds__(256) void q8_mfma_kernel(const MfmaArgs a) {
-    constexpr int kStage = lds_stage_bytes<FMT>();
+__device__ __forceinline__ void q8_mfma_body(const MfmaArgs& a) {
+    constexpr int kStage = lds_gemm_buffer_bytes<FMT>();
     // the two stage buffers are separate objects, so the compiler can tell
     // that reading one does not wait for the direct loads into the other
     __shared__ __attribute__((aligned(1024))) uint8_t lds0[kStage];
     __shared__ __attribute__((aligned(1024))) uint8_t lds1[kStage];
-    static_assert(kStage >= 2 * kM16 * 64 * 16, "the U hand-over needs 16 KB per buffer");
     // XCD-aware order: the hardware deals blocks to the 8 XCDs in turn by
     // linear id, so linear id L runs on XCD L % 8. Block L takes column block
     // (L / 8) % ncol of row tile ((L / 8) / ncol) * 8 + L % 8: all column
@@ -330,9 +327,9 @@ __global__ __launch_bounds__(256) void q8_mfma_kernel(const MfmaArgs a) {
     c.wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     c.nl = c.lane & 15;
     c.rq = c.lane >> 4;
-    c.T0 = col_blk * (GATEUP ? 2 : 4);
-    c.tt = c.T0 + (GATEUP ? (c.wave & 1) : c.wave);
-    const int mat = GATEUP ? (c.wave >> 1) : 0;
+    c.T0 = col_blk * (GATEUP ? kGemmWaves / 2 : kGemmWaves);
+    c.tt = c.T0 + (GATEUP ? (c.wave & (kGemmWaves / 2 - 1)) : c.wave);
+    const int mat = GATEUP ? (c.wave >> 2) : 0;
     const MfmaMat& M = (c.is_shared ? a.shared : a.routed)[mat];
     const int64_t eo = c.is_shared ? 0 : c.e;
     const uint8_t* wq = M.q + eo * M.q_stride;
@@ -349,14 +346,12 @@ __global__ __launch_bounds__(256) void q8_mfma_kernel(const MfmaArgs a) {
         const int pr = c.row_begin + min(r, c.rows - 1);
         return a.row_token ? a.row_token[pr] : pr;
     };
-    // token tiles i = wave, wave + 4: lane l = r + 16 h reads token 16 i + r, slice h
-#pragma unroll
-    for (int s = 0; s < 2; ++s)
-        c.tok_off[s] = ((uint32_t)src_row(16 * (c.wave + 4 * s) + c.nl) * c.K + 8 * c.rq) * 2;
-    // scale job of this wave: floats 64 wave + lane of the SX layout
+    // token tile i = wave: lane l = r + 16 h reads token 16 i + r, slice h
+    c.tok_off = ((uint32_t)src_row(16 * c.wave + c.nl) * c.K + 8 * c.rq) * 2;
+    // scale job of waves 0 .. 3: floats 64 wave + lane of the SX layout
     // [8 tiles][2 groups][16 r]: token 16 i + r, group g of the pair
     {
-        const int f = 64 * c.wave + c.lane;
+        const int f = 64 * (c.wave & 3) + c.lane;
         const int i = f >> 5, g = (f >> 4) & 1, r = f & 15;
         c.sx_off = ((uint32_t)src_row(16 * i + r) * c.G + g) * 4;
     }
@@ -369,6 +364,21 @@ __global__ __launch_bounds__(256) void q8_mfma_kernel(const MfmaArgs a) {
         case 4: gemm_tile<FMT, GATEUP, DBG, ROW, 4>(a, c, buf0, buf1); break;
         default: gemm_tile<FMT, GATEUP, DBG, ROW, 8>(a, c, buf0, buf1); break;
     }
+}
+
+// Two blocks of eight waves share a CU (LDS), so the kernel is held to the
+// registers of four waves per SIMD.
+template <int FMT, bool GATEUP, bool ROW>
+__global__ __launch_bounds__(64 * kGemmWaves) __attribute__((amdgpu_waves_per_eu(4, 4))) void q8_mfma_kernel(
+    const MfmaArgs a) {
+    q8_mfma_body<FMT, GATEUP, false, ROW>(a);
+}
+
+// The test hook's variant (every group dot and H code written out): the
+// same body without the register limit.
+template <int FMT, bool GATEUP, bool ROW>
+__global__ __launch_bounds__(64 * kGemmWaves) void q8_mfma_dbg_kernel(const MfmaArgs a) {
+    q8_mfma_body<FMT, GATEUP, true, ROW>(a);
 }
 
 hipError_t launch_q8_mfma(const moe_experts& routed, const moe_experts* shared, bool gateup, const _Float16* a_q,
@@ -406,10 +416,14 @@ hipError_t launch_q8_mfma(const moe_experts& routed, const moe_experts* shared, 
     };
     fill(a.routed, routed);
     fill(a.shared, shared ? *shared : routed);
-    const int bn = gateup ? 2 * kTile : 4 * kTile;   // output columns per block
+    const int bn = (gateup ? kGemmWaves / 2 : kGemmWaves) * kTile;   // output columns per block
     const dim3 grid((a.N + bn - 1) / bn, (max_tiles + 7) / 8 * 8);   // tile count padded for the XCD order
     const bool dbg = dbg0 != nullptr;
-#define MOE_Q8(FMT, GU, DB, RW) launch_timed(q8_mfma_kernel<FMT, GU, DB, RW>, grid, dim3(256), st, ev0, ev1, a)
+#define MOE_Q8(FMT, GU, DB, RW)                                                                          \
+    do {                                                                                                  \
+        if (DB) launch_timed(q8_mfma_dbg_kernel<FMT, GU, RW>, grid, dim3(64 * kGemmWaves), st, ev0, ev1, a); \
+        else launch_timed(q8_mfma_kernel<FMT, GU, RW>, grid, dim3(64 * kGemmWaves), st, ev0, ev1, a);        \
+    } while (0)
 #define MOE_Q8_GU(FMT, RW)                                                              \
     if (gateup) { if (dbg) MOE_Q8(FMT, true, true, RW); else MOE_Q8(FMT, true, false, RW); } \
     else { if (dbg) MOE_Q8(FMT, false, true, RW); else MOE_Q8(FMT, false, false, RW); }

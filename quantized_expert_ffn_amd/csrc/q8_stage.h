@@ -20,29 +20,44 @@ namespace moe {
 
 constexpr int kBM = kTileRows;       // 128 token rows per block
 constexpr int kM16 = kBM / 16;       // 16-token tiles per block
+constexpr int kGemmWaves = 8;        // waves per block, one 32-row weight tile each
 
 // One LDS stage (bytes), filled by direct global -> LDS loads (each wave
 // load writes 64 lanes x 16 (or 4) bytes contiguously):
 //   TOK [2 groups][8 tiles][64 lanes][16 B]  f16 activation codes; block
 //       (g, i) is the B operand of 16-token tile i: lane l = r + 16 h holds
 //       token 16 i + r, slice h (k 8h .. 8h+7 in operand-slot order)
-//   W   int8: [4 tiles][2 groups][1 KB]  weight blocks exactly as in HBM
-//       int4: [4 tiles][1 KB]            (one block holds the pair)
-//       int2: [4 tiles][2 groups][256 B] the pair's dwords of each lane (a
+//   W   int8: [8 tiles][2 groups][1 KB]  weight blocks exactly as in HBM
+//       int4: [8 tiles][1 KB]            (one block holds the pair)
+//       int2: [8 tiles][2 groups][256 B] the pair's dwords of each lane (a
 //                                        block holds two pairs)
 //   SX  [8 tiles][2 groups][16 r] fp32    activation scales of token 16 i + r
 //       (the 16 tokens a read serves lie in 16 different banks)
-//   SW  [4 tiles][64] fp32                the tiles' scale blocks of the pair
+//   SW  [8 tiles][64] fp32                the tiles' scale blocks of the pair
 //                                         (group-scale formats only)
-constexpr int kLdsTok = 2 * kM16 * 1024;   // 16384
-constexpr int kLdsSX = 2 * kBM * 4;        // 1024
-constexpr int kLdsSW = 4 * 64 * 4;         // 1024
+constexpr int kLdsTok = 2 * kM16 * 1024;           // 16384
+constexpr int kLdsSX = 2 * kBM * 4;                // 1024
+constexpr int kLdsSW = kGemmWaves * 64 * 4;        // 2048
 template <int FMT>
 constexpr int lds_w_bytes() {
-    return FMT == MOE_W_INT8_G32 ? 4 * 2 * 1024 : FMT == MOE_W_INT4_G32 ? 4 * 1024 : 4 * 2 * 256;
+    return kGemmWaves * (FMT == MOE_W_INT8_G32 ? 2 * 1024 : FMT == MOE_W_INT4_G32 ? 1024 : 2 * 256);
+}
+// byte offset of wave w's weight block(s) inside W
+template <int FMT>
+constexpr int lds_w_wave(int w) {
+    return w * (FMT == MOE_W_INT8_G32 ? 2 * 1024 : FMT == MOE_W_INT4_G32 ? 1024 : 2 * 256);
 }
 template <int FMT>
 constexpr int lds_stage_bytes() { return kLdsTok + lds_w_bytes<FMT>() + kLdsSX + kLdsSW; }
+// After the K loop the gate/up kernel's up waves hand U (up to 16 KB per
+// wave: eight 16-token tiles x two halves x 64 lanes x 16 B) to the gate
+// waves through the two stage buffers, two waves per buffer: each buffer
+// holds at least a stage and 32 KB.
+constexpr int kHandoverBytes = kM16 * 2 * 64 * 16;
+template <int FMT>
+constexpr int lds_gemm_buffer_bytes() {
+    return lds_stage_bytes<FMT>() > 2 * kHandoverBytes ? lds_stage_bytes<FMT>() : 2 * kHandoverBytes;
+}
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 typedef __attribute__((address_space(3))) uint8_t lds_byte;
@@ -55,6 +70,12 @@ __device__ __forceinline__ T lds_read(const lds_byte* p) {
     static_assert(sizeof(T) == 16, "16-byte reads only");
     const v4u v = *reinterpret_cast<const __attribute__((address_space(3))) v4u*>(p);
     return __builtin_bit_cast(T, v);
+}
+
+typedef float v2f __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ v2f lds_read_f2(const lds_byte* p) {
+    return *reinterpret_cast<const __attribute__((address_space(3))) v2f*>(p);
 }
 
 __device__ __forceinline__ uint32_t lds_read_u32(const lds_byte* p) {
@@ -96,12 +117,15 @@ __device__ __forceinline__ void q8_stage(const lds_byte* base, const StageOffset
         cw2[0] = lds_read_u32(base + o.w);
         cw2[1] = lds_read_u32(base + o.w + 256);
     }
-    // weight scales of the lane's rows 4 rq + r: swr[r] = {g0 h0, g0 h1, g1 h0, g1 h1}
-    float4 swr[4];
-    if constexpr (!ROW) {
+    // weight scales of the lane's rows 4 rq + r for the current group g:
+    // swg[r] = {half 0, half 1} (the block holds {g0 h0, g0 h1, g1 h0, g1 h1}
+    // per row); one group at a time keeps eight registers, not sixteen
+    v2f swg[4];
+    auto load_sw = [&](int g) __attribute__((always_inline)) {
 #pragma unroll
-        for (int r = 0; r < 4; ++r) swr[r] = lds_read<float4>(base + o.sw + r * 16);
-    }
+        for (int r = 0; r < 4; ++r) swg[r] = lds_read_f2(base + o.sw + r * 16 + g * 8);
+    };
+    if constexpr (!ROW) load_sw(0);
     // step s: group g = s / LIVE, token tile i = s % LIVE
     auto tok = [&](int st) __attribute__((always_inline)) {
         return lds_read<v8h>(base + o.tok + ((st / LIVE) * kM16 + st % LIVE) * 1024);
@@ -149,7 +173,9 @@ __device__ __forceinline__ void q8_stage(const lds_byte* base, const StageOffset
             d[st + 1][0] = __builtin_amdgcn_mfma_f32_16x16x32_f16(wa[0], tb[st + 1], v4f{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
             d[st + 1][1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(wa[1], tb[st + 1], v4f{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
         }
-        const int g = st / LIVE, i = st % LIVE;
+        const int i = st % LIVE;
+        if constexpr (!ROW)
+            if (st == LIVE) load_sw(1);
 #pragma unroll
         for (int hh = 0; hh < 2; ++hh) {
             if constexpr (ROW) {
@@ -158,7 +184,7 @@ __device__ __forceinline__ void q8_stage(const lds_byte* base, const StageOffset
             } else {
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
-                    const float sw = g ? (hh ? swr[r].w : swr[r].z) : (hh ? swr[r].y : swr[r].x);
+                    const float sw = hh ? swg[r].y : swg[r].x;
                     acc[i][hh][r] = fmaf(d[st][hh][r], sw * sx[st], acc[i][hh][r]);
                 }
             }
