@@ -568,6 +568,35 @@ def test_layer_fused_routing_tiny(variant, act_mode):
         check_layer_routing(sec, shape, x)
 
 
+@pytest.mark.parametrize("variant,T", [("tiny_shared_noaux", 700), ("tiny", 1400), ("tiny_int4", 1100)])
+def test_layer_prefill_tile_layout(variant, T):
+    """Batches large enough for the multi-block dispatch (T*k > 2048), whose
+    work lists lay the full 128-row tiles out in 8 runs, one per XCD, with
+    empty tiles evening the runs out. For each case the host counts, from the
+    oracle's routing, how many full tiles there are: the cases are chosen so
+    that the count is not a multiple of 8 (empty tiles exist and are skipped)
+    or a run boundary splits an expert's tiles. Q8_0 outputs against the
+    oracle."""
+    need_gpu()
+    shape, dl = tiny_layer(variant)
+    assert T * shape.top_k > 2048
+    x = synth.activations(shape, T)
+    spec = router_spec(shape)
+    idx, _, _ = olayer.route(x, synth.gate_weight(shape), spec)
+    counts = np.bincount(idx[idx >= 0].ravel(), minlength=shape.n_experts)
+    n_full = int((counts // 128).sum()) + (T // 128 if shape.shared_expert else 0)
+    run = (n_full + 7) // 8
+    empty = 8 * run - n_full
+    starts = np.concatenate([[0], np.cumsum(counts // 128)])
+    split = any(s0 // run != (s0 + c - 1) // run for s0, c in zip(starts[:-1], counts // 128) if c > 0)
+    say(f"[tiles] {variant}/T={T}: {n_full} full tiles, runs of {run}, {empty} empty, expert split across runs: {split}")
+    assert empty > 0 or split
+    got = run_layer(dl, x, "q8_0")
+    ref = oracle_layer(shape, x, "q8_0")
+    ok = top_p_settled(shape, x)
+    assert_close_rel(got[ok], ref["out"][ok], what=f"{variant}/q8_0/T={T} out")
+
+
 @pytest.mark.parametrize("act_mode", ["f32", "q8_0"])
 @pytest.mark.parametrize("variant,T", [("tiny_shared_noaux", 67), ("tiny_gated", 1100)])
 def test_layer_hip_graph_replay(act_mode, variant, T):
