@@ -107,13 +107,30 @@ __device__ __forceinline__ void topk_token(const TopkArgs& a, int t, bool active
     // the slices' partial sums, added in slice order; a batch of slices is
     // loaded before any of it is added, so the loads overlap
     constexpr int SB = EPL >= 16 ? 2 : EPL >= 8 ? 4 : 8;
+    // a lane's EPL experts are consecutive: 16-byte loads when they all lie
+    // inside the row and the rows are 16-byte aligned (E % 4 == 0)
+    const bool vec = (EPL % 4 == 0) && (E % 4 == 0) && lane * EPL + EPL <= E;
     for (int s0 = 0; s0 < a.S; s0 += SB) {
         float pv[SB][EPL];
 #pragma unroll
         for (int u = 0; u < SB; ++u) {
             const int s = min(s0 + u, a.S - 1);
+            const float* row = a.L + ((size_t)s * a.T + tc) * E;
+            if constexpr (EPL % 4 == 0) {
+                if (vec) {
 #pragma unroll
-            for (int i = 0; i < EPL; ++i) pv[u][i] = a.L[((size_t)s * a.T + tc) * E + min(lane * EPL + i, E - 1)];
+                    for (int i = 0; i < EPL; i += 4) {
+                        const float4 q = *reinterpret_cast<const float4*>(row + lane * EPL + i);
+                        pv[u][i] = q.x;
+                        pv[u][i + 1] = q.y;
+                        pv[u][i + 2] = q.z;
+                        pv[u][i + 3] = q.w;
+                    }
+                    continue;
+                }
+            }
+#pragma unroll
+            for (int i = 0; i < EPL; ++i) pv[u][i] = row[min(lane * EPL + i, E - 1)];
         }
 #pragma unroll
         for (int u = 0; u < SB; ++u)
