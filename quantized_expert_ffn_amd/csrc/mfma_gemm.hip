@@ -23,15 +23,15 @@
 // Block tile: 128 token rows (one work-list tile: rows of one expert) x eight
 // 32-row weight tiles; eight waves, each owning ONE weight tile (gate/up: four
 // gate tiles and the same four up tiles; down: eight adjacent tiles) for ALL
-// of the block's token rows. The eight waves share each staged token tile, and
-// two blocks (four waves per SIMD) fit a CU. The weights are the matrix core's A operand (output
-// rows = weight rows) and the token codes its B operand (output columns =
-// tokens), so
+// of the block's token rows. The eight waves share each staged token tile,
+// and two blocks (four waves per SIMD) fit a CU. The weights are the matrix
+// core's A operand (output rows = weight rows) and the token codes its B
+// operand (output columns = tokens), so
 //   - a wave converts each weight code to f16 once and uses it for every
 //     live 16-token tile (up to eight products per conversion);
 //   - a lane's outputs share one token per 16-token tile: its activation
 //     scale is one float per tile and group, its weight scales four floats
-//     per 16-row half and group, read once per stage.
+//     per 16-row half and group, read one group at a time.
 // Operands are staged through LDS one group pair (64 k) at a time, double
 // buffered, by direct global -> LDS loads (no staging registers; weight
 // blocks land exactly as they are stored in HBM). 16-token tiles past the
@@ -39,10 +39,10 @@
 // 4 or 8 tiles) is a compile-time constant of the whole K loop, chosen once
 // per block, so no branch ever separates a product from its use.
 //   gate/up kernel: the up waves hand U to the gate waves through LDS (the
-//     stage buffers, free after the K loop), and the gate waves
-//     form H = silu(G) * U and quantise it (Q8_0, one group = the 32 outputs
-//     of a weight tile) in registers; H leaves as f16 codes in operand-slot
-//     order + one fp32 scale per 32, ready to be the down kernel's B operand.
+//     stage buffers, free after the K loop), and the gate waves form
+//     H = silu(G) * U and quantise it (Q8_0, one group = the 32 outputs of a
+//     weight tile) in registers; H leaves as f16 codes in operand-slot order
+//     + one fp32 scale per 32, ready to be the down kernel's B operand.
 //   down kernel: Y leaves fp32, four consecutive outputs per 16-byte store.
 // Work list: one tile per (expert, 128-row block) from the dispatch kernel;
 // blocks past the live tile count exit at once (no host read-back).
@@ -116,13 +116,17 @@ __device__ __forceinline__ void gemm_tile(const MfmaArgs& a, const TileCtx& c, l
     constexpr int kW = lds_w_bytes<FMT>();
     const int lane = c.lane, wave = c.wave, nl = c.nl, rq = c.rq;
     const int P = c.P, NT = c.NT;
-    const int ttl = min(c.tt, NT - 1);   // tile index for loads
+    // this wave's weight tile (tt may be >= NT: loads clamped to ttl,
+    // nothing stored) and its scale-block resource
+    const int tt = c.tt;
+    const int ttl = min(tt, NT - 1);
+    const __amdgpu_buffer_rsrc_t rsw = c.rsw;
 
     // Stage jobs, each a wave-wide direct load (wave-uniform): token tile
     // i = wave of both groups (live tiles only), this wave's weight
-    // block(s), a quarter of the activation scales (waves 0 .. 3), and this
-    // wave's weight scale block.
-    auto issue_stage = [&](int pc, lds_byte* base) __attribute__((always_inline)) {
+    // block(s) of tile tl, a quarter of the activation scales (waves 0 .. 3),
+    // and this wave's weight scale block (through rs).
+    auto issue_stage = [&](int pc, lds_byte* base, int tl, __amdgpu_buffer_rsrc_t rs) __attribute__((always_inline)) {
         lds_byte* TOK = base;
         lds_byte* W = base + kLdsTok;
         lds_byte* SX = W + kW;
@@ -135,19 +139,19 @@ __device__ __forceinline__ void gemm_tile(const MfmaArgs& a, const TileCtx& c, l
         if constexpr (FMT == MOE_W_INT8_G32) {
 #pragma unroll
             for (int g = 0; g < 2; ++g)
-                buffer_load_lds<16>(c.rw, lane * 16, ((2 * pc + g) * NT + ttl) * 1024,
+                buffer_load_lds<16>(c.rw, lane * 16, ((2 * pc + g) * NT + tl) * 1024,
                                     W + lds_w_wave<FMT>(wave) + g * 1024);
         } else if constexpr (FMT == MOE_W_INT2_G32) {
             // dwords 2 (pc % 2) + g of each lane's 16 bytes in the quad block
 #pragma unroll
             for (int g = 0; g < 2; ++g)
-                buffer_load_lds<4>(c.rw, lane * 16, ((pc >> 1) * NT + ttl) * 1024 + (2 * (pc & 1) + g) * 4,
+                buffer_load_lds<4>(c.rw, lane * 16, ((pc >> 1) * NT + tl) * 1024 + (2 * (pc & 1) + g) * 4,
                                    W + lds_w_wave<FMT>(wave) + g * 256);
         } else {
-            buffer_load_lds<16>(c.rw, lane * 16, (pc * NT + ttl) * 1024, W + lds_w_wave<FMT>(wave));
+            buffer_load_lds<16>(c.rw, lane * 16, (pc * NT + tl) * 1024, W + lds_w_wave<FMT>(wave));
         }
         if (wave < 4) buffer_load_lds<4>(c.rsx, c.sx_off, 2 * pc * 4, SX + wave * 256);
-        if constexpr (!ROW) buffer_load_lds<4>(c.rsw, lane * 4, pc * 256, SW + wave * 256);
+        if constexpr (!ROW) buffer_load_lds<4>(rs, lane * 4, pc * 256, SW + wave * 256);
     };
 
     // per-lane LDS byte offsets of the operands inside a stage buffer, kept
@@ -177,10 +181,10 @@ __device__ __forceinline__ void gemm_tile(const MfmaArgs& a, const TileCtx& c, l
         q8_stage<FMT, ROW, LIVE>(base, so, acc, [&](int st, int hh, const v4f& d) __attribute__((always_inline)) {
             if constexpr (DBG) {
                 const int g = st / LIVE, i = st % LIVE;
-                const int col = c.tt * kTile + 16 * hh + 4 * rq;   // weight rows col .. col + 3
+                const int col = tt * kTile + 16 * hh + 4 * rq;     // weight rows col .. col + 3
                 const int row = 16 * i + nl;                       // token row of the block
                 int32_t* dst = (GATEUP && (wave >> 2)) ? a.dbg1 : a.dbg0;
-                if (row < c.rows && c.tt < NT) {
+                if (row < c.rows && tt < NT) {
 #pragma unroll
                     for (int r = 0; r < 4; ++r)
                         dst[((size_t)(c.row_begin + row) * c.N + col + r) * c.G + 2 * pc + g] = (int32_t)d[r];
@@ -192,38 +196,54 @@ __device__ __forceinline__ void gemm_tile(const MfmaArgs& a, const TileCtx& c, l
     // Stages alternate between the two buffers (separate LDS objects, so a
     // read of one is never held up by the direct loads into the other); each
     // stage's loads for the next one are in flight while it is multiplied.
-    issue_stage(0, buf0);
+    issue_stage(0, buf0, ttl, rsw);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
     for (int pc = 0; pc < P; pc += 2) {
-        if (pc + 1 < P) issue_stage(pc + 1, buf1);
+        if (pc + 1 < P) issue_stage(pc + 1, buf1, ttl, rsw);
         compute(buf0, pc);
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         __syncthreads();
         if (pc + 1 < P) {
-            if (pc + 2 < P) issue_stage(pc + 2, buf0);
+            if (pc + 2 < P) issue_stage(pc + 2, buf0, ttl, rsw);
             compute(buf1, pc + 1);
             asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
             __syncthreads();
         }
     }
 
-    // ---- epilogue ----
     if constexpr (ROW) {
         // the lane's rows' scales (a tile past the matrix reads row NT*32-1's; not stored)
         const float* srow = c.wsb + ttl * kTile + 4 * rq;
 #pragma unroll
         for (int hh = 0; hh < 2; ++hh) {
-            const float4 s = *reinterpret_cast<const float4*>(srow + 16 * hh);
+            const float4 sr = *reinterpret_cast<const float4*>(srow + 16 * hh);
 #pragma unroll
             for (int i = 0; i < LIVE; ++i) {
-                acc[i][hh][0] *= s.x;
-                acc[i][hh][1] *= s.y;
-                acc[i][hh][2] *= s.z;
-                acc[i][hh][3] *= s.w;
+                acc[i][hh][0] *= sr.x;
+                acc[i][hh][1] *= sr.y;
+                acc[i][hh][2] *= sr.z;
+                acc[i][hh][3] *= sr.w;
             }
         }
     }
+    if constexpr (!GATEUP) {
+        // ---- down epilogue: Y, four consecutive outputs per 16-byte store ----
+        if (tt >= NT) return;
+#pragma unroll
+        for (int i = 0; i < LIVE; ++i) {
+            const int row = 16 * i + nl;
+            if (row >= c.rows) continue;
+            float* yrow = a.y + (size_t)(c.row_begin + row) * c.N + tt * kTile + 4 * rq;
+#pragma unroll
+            for (int hh = 0; hh < 2; ++hh)
+                *reinterpret_cast<float4*>(yrow + 16 * hh) =
+                    make_float4(acc[i][hh][0], acc[i][hh][1], acc[i][hh][2], acc[i][hh][3]);
+        }
+        return;
+    }
+
+    // ---- gate/up epilogue ----
     if constexpr (GATEUP) {
         // up waves (4 .. 7) hand U to the gate waves (0 .. 3) of the same
         // tile through the stage buffers (free after the loop's last
@@ -260,9 +280,9 @@ __device__ __forceinline__ void gemm_tile(const MfmaArgs& a, const TileCtx& c, l
             const float dd = __fdiv_rn(amax, 127.0f);
             const float inv = dd != 0.0f ? __fdiv_rn(1.0f, dd) : 0.0f;
             const int row = 16 * i + nl;
-            if (row < c.rows && c.tt < NT) {
+            if (row < c.rows && tt < NT) {
                 const size_t R = (size_t)(c.row_begin + row);
-                _Float16* hrow = a.hq + R * c.N + c.tt * kTile;
+                _Float16* hrow = a.hq + R * c.N + tt * kTile;
 #pragma unroll
                 for (int hh = 0; hh < 2; ++hh)
 #pragma unroll
@@ -270,22 +290,10 @@ __device__ __forceinline__ void gemm_tile(const MfmaArgs& a, const TileCtx& c, l
                         const int kk = 16 * hh + 4 * rq + r;     // H column inside the group
                         const float q = fminf(fmaxf(rintf(__fmul_rn(h[hh][r], inv)), -127.0f), 127.0f);
                         hrow[(kk & ~7) + k_slot(FMT, kk & 7)] = (_Float16)q;
-                        if constexpr (DBG) a.dbg_hq[R * c.N + c.tt * kTile + kk] = (int8_t)(int)q;
+                        if constexpr (DBG) a.dbg_hq[R * c.N + tt * kTile + kk] = (int8_t)(int)q;
                     }
-                if (rq == 0) a.hd[R * GN + c.tt] = dd;
+                if (rq == 0) a.hd[R * GN + tt] = dd;
             }
-        }
-    } else {
-        if (c.tt >= NT) return;
-#pragma unroll
-        for (int i = 0; i < LIVE; ++i) {
-            const int row = 16 * i + nl;
-            if (row >= c.rows) continue;
-            float* yrow = a.y + (size_t)(c.row_begin + row) * c.N + c.tt * kTile + 4 * rq;
-#pragma unroll
-            for (int hh = 0; hh < 2; ++hh)
-                *reinterpret_cast<float4*>(yrow + 16 * hh) =
-                    make_float4(acc[i][hh][0], acc[i][hh][1], acc[i][hh][2], acc[i][hh][3]);
         }
     }
 }
