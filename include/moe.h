@@ -107,10 +107,11 @@ typedef enum {
 
 /* Timed stages of moe_layer_forward_timed. */
 typedef enum {
-    MOE_STAGE_ROUTE = 0,     /* router logits (T <= 16: + hidden-state preparation); T > 16: + top-k */
+    MOE_STAGE_ROUTE = 0,     /* router logits + hidden-state preparation (Q8_0 codes or f32 parts), one
+                                launch; T > 16: + top-k */
     MOE_STAGE_DISPATCH = 1,  /* (T <= 16: top-k +) counts, offsets, permutation, work lists */
-    MOE_STAGE_QUANT_X = 2,   /* hidden-state preparation (Q8_0 codes or f32 parts) as a kernel of its
-                                own: T > 16 only */
+    MOE_STAGE_QUANT_X = 2,   /* not recorded by the layer calls (their router launch prepares the hidden
+                                states): its two events are left untouched */
     MOE_STAGE_GATEUP = 3,    /* gate and up projections + SwiGLU (all experts) */
     MOE_STAGE_DOWN = 4,      /* down projections (all experts) */
     MOE_STAGE_COMBINE = 5,   /* weighted gather-sum + shared expert */

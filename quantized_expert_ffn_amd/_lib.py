@@ -144,6 +144,34 @@ def _ptr(t: Optional[torch.Tensor], dtype=None, name: str = "tensor") -> Optiona
     return t.data_ptr()
 
 
+def _shape(t: Optional[torch.Tensor], shape, name: str) -> None:
+    """The kernels index the tensors by the sizes the call passes: a tensor of
+    another shape is an error here, not an access past its end there."""
+    if t is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+
+
+def _at_least(t: Optional[torch.Tensor], numel: int, name: str) -> None:
+    if t is not None and t.numel() < numel:
+        raise ValueError(f"{name} holds {t.numel()} elements, the call uses {numel}")
+
+
+def _rows(t: torch.Tensor, rows: int, cols: int, name: str) -> None:
+    """An output of rows x cols: rows of exactly cols elements, at least rows of them."""
+    if t.dim() != 2 or t.shape[1] != cols or t.shape[0] < rows:
+        raise ValueError(f"{name} must be [>= {rows}, {cols}], got {tuple(t.shape)}")
+
+
+def _layer_shapes(x, gate_w, params, routed, out, norm_w=None) -> None:
+    if x.dim() != 2:
+        raise ValueError(f"x must be [T, d_model], got {tuple(x.shape)}")
+    T, d = x.shape[0], routed.d_model
+    _shape(x, (T, d), "x")
+    _shape(gate_w, (params.n_experts, d), "gate_w")
+    _rows(out, T, d, "out")
+    _shape(norm_w, (d,), "norm_w")
+
+
 def _stream(stream) -> Optional[int]:
     if stream is None:
         stream = torch.cuda.current_stream()
@@ -199,6 +227,20 @@ class QuantExperts:
         self.down_q, self.down_s = down_q, down_s
         self.n_experts, self.d_ff = gate_s.shape[0], gate_s.shape[1]
         self.d_model = down_s.shape[1]
+        if fmt not in FORMATS:
+            raise ValueError(f"unknown weight format {fmt!r}")
+        div = {"int8": 1, "int4": 2, "int2": 4}[fmt.split("_")[0]]
+        per_row = fmt.endswith("_row")
+        E, I, d = self.n_experts, self.d_ff, self.d_model
+        need = {"gate_q": (gate_q, E * I * d // div), "up_q": (up_q, E * I * d // div),
+                "down_q": (down_q, E * d * I // div),
+                "gate_s": (gate_s, E * I * (1 if per_row else d // 32)),
+                "up_s": (up_s, E * I * (1 if per_row else d // 32)),
+                "down_s": (down_s, E * d * (1 if per_row else I // 32))}
+        for name, (t, n) in need.items():
+            if t.numel() * t.element_size() // (4 if name.endswith("_s") else 1) != n:
+                raise ValueError(f"{name} of a {fmt} stack of {E} experts (d_model {d}, d_ff {I}) must hold {n} "
+                                 f"{'floats' if name.endswith('_s') else 'bytes'}")
 
     @classmethod
     def empty(cls, n_experts: int, d_model: int, d_ff: int, fmt: str, device="cuda"):
@@ -263,6 +305,9 @@ def moe_quantize_q8_0(x: torch.Tensor, q: torch.Tensor, d: torch.Tensor, stream=
 def moe_route(x: torch.Tensor, gate_w: torch.Tensor, params: RouterParams, topk_idx: torch.Tensor,
               topk_w: torch.Tensor, ws: torch.Tensor, stream=None) -> None:
     T, d = x.shape
+    _shape(gate_w, (params.n_experts, d), "gate_w")
+    _at_least(topk_idx, T * params.top_k, "topk_idx")
+    _at_least(topk_w, T * params.top_k, "topk_w")
     _check(load().moe_route(_ptr(x, torch.float32, "x"), T, d, _ptr(gate_w, torch.float32, "gate_w"),
                             ctypes.byref(params), _ptr(topk_idx, torch.int32, "topk_idx"),
                             _ptr(topk_w, torch.float32, "topk_w"), _ptr(ws, None, "ws"),
@@ -274,6 +319,10 @@ def moe_dispatch(topk_idx: torch.Tensor, E: int, counts: torch.Tensor, offsets: 
                  stream=None) -> None:
     """ws (optional): scratch that lets large batches dispatch over many blocks."""
     T, k = topk_idx.shape
+    _at_least(counts, E, "counts")
+    _at_least(offsets, E + 1, "offsets")
+    _at_least(perm, T * k, "perm")
+    _at_least(inv_perm, T * k, "inv_perm")
     nbytes = ws.numel() * ws.element_size() if ws is not None else 0
     _check(load().moe_dispatch(_ptr(topk_idx, torch.int32, "topk_idx"), T, k, E, _ptr(counts, torch.int32, "counts"),
                                _ptr(offsets, torch.int32, "offsets"), _ptr(perm, torch.int32, "perm"),
@@ -284,6 +333,12 @@ def moe_dispatch(topk_idx: torch.Tensor, E: int, counts: torch.Tensor, offsets: 
 def moe_expert_ffn(x: torch.Tensor, k: int, experts: QuantExperts, counts: torch.Tensor, offsets: torch.Tensor,
                    perm: torch.Tensor, act_mode: int, y_perm: torch.Tensor, ws: torch.Tensor, stream=None) -> None:
     ex = experts.abi()
+    T, d = x.shape[0], experts.d_model
+    _shape(x, (T, d), "x")
+    _at_least(counts, experts.n_experts, "counts")
+    _at_least(offsets, experts.n_experts + 1, "offsets")
+    _at_least(perm, T * k, "perm")
+    _at_least(y_perm, T * k * d, "y_perm")
     _check(load().moe_expert_ffn(_ptr(x, torch.float32, "x"), x.shape[0], k, ctypes.byref(ex),
                                  _ptr(counts, torch.int32, "counts"), _ptr(offsets, torch.int32, "offsets"),
                                  _ptr(perm, torch.int32, "perm"), act_mode, _ptr(y_perm, torch.float32, "y_perm"),
@@ -317,6 +372,8 @@ def moe_debug_workspace_sections(T: int, k: int, E: int, d: int, d_ff: int, act_
 def moe_calib_stream_read(buf: torch.Tensor, sink: torch.Tensor, blocks: int, stream=None) -> None:
     """Reference streaming read of every byte of buf (include/moe_calib.h);
     sink: uint32-sized [blocks] device tensor."""
+    if sink.numel() * sink.element_size() < 4 * blocks:
+        raise ValueError(f"sink holds {sink.numel() * sink.element_size()} bytes, the launch writes {4 * blocks}")
     _check(load().moe_calib_stream_read(_ptr(buf, None, "buf"), buf.numel() * buf.element_size(),
                                         _ptr(sink, None, "sink"), blocks, _stream(stream)), "moe_calib_stream_read")
 
@@ -335,6 +392,11 @@ def moe_calib_prefill_mix(blocks: int, stages: int, sink: torch.Tensor, stream=N
 def moe_combine(y_perm: torch.Tensor, topk_w: torch.Tensor, inv_perm: torch.Tensor,
                 shared_y: Optional[torch.Tensor], out: torch.Tensor, stream=None) -> None:
     T, k = topk_w.shape
+    d = out.shape[1]
+    _rows(out, T, d, "out")
+    _at_least(inv_perm, T * k, "inv_perm")
+    _at_least(y_perm, T * k * d, "y_perm")
+    _shape(shared_y, (T, d), "shared_y")
     _check(load().moe_combine(_ptr(y_perm, torch.float32, "y_perm"), _ptr(topk_w, torch.float32, "topk_w"),
                               _ptr(inv_perm, torch.int32, "inv_perm"), _ptr(shared_y, torch.float32, "shared_y"),
                               T, k, out.shape[1], _ptr(out, torch.float32, "out"), _stream(stream)), "moe_combine")
@@ -343,6 +405,7 @@ def moe_combine(y_perm: torch.Tensor, topk_w: torch.Tensor, inv_perm: torch.Tens
 def moe_layer_forward(x: torch.Tensor, gate_w: torch.Tensor, params: RouterParams, routed: QuantExperts,
                       shared: Optional[QuantExperts], act_mode: int, out: torch.Tensor, ws: torch.Tensor,
                       stream=None, _abi_cache=None) -> None:
+    _layer_shapes(x, gate_w, params, routed, out)
     r = routed.abi()
     s = shared.abi() if shared is not None else None
     _check(load().moe_layer_forward(_ptr(x, torch.float32, "x"), x.shape[0], _ptr(gate_w, torch.float32, "gate_w"),
@@ -359,6 +422,7 @@ def moe_layer_forward_noalloc(x: torch.Tensor, gate_w: torch.Tensor, params: Rou
     """moe_layer_forward with the library's own per-GPU scratch instead of a
     workspace (no allocation); calls needing more than
     MOE_NOALLOC_SCRATCH_BYTES of workspace are rejected."""
+    _layer_shapes(x, gate_w, params, routed, out)
     r = routed.abi()
     s = shared.abi() if shared is not None else None
     _check(load().moe_layer_forward_noalloc(_ptr(x, torch.float32, "x"), x.shape[0],
@@ -384,6 +448,7 @@ def moe_layer_forward_timed(x, gate_w, params: RouterParams, routed: QuantExpert
             ev.record()        # torch creates the HIP event on its first record
         handles.append(ev.cuda_event)
     arr = (ctypes.c_void_p * len(events))(*handles)
+    _layer_shapes(x, gate_w, params, routed, out)
     r = routed.abi()
     s = shared.abi() if shared is not None else None
     _check(load().moe_layer_forward_timed(
@@ -411,6 +476,7 @@ def moe_block_forward(x, norm_w: Optional[torch.Tensor], eps: float, gate_w, par
                       events: Optional[Sequence[Optional[torch.cuda.Event]]] = None, stream=None) -> None:
     """out = x + layer(RMSNorm(x)) (norm_w None: out = x + layer(x)); out may be x."""
     arr = _event_array(events) if events is not None else None
+    _layer_shapes(x, gate_w, params, routed, out, norm_w)
     r = routed.abi()
     s = shared.abi() if shared is not None else None
     _check(load().moe_block_forward(

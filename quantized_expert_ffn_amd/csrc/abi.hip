@@ -301,8 +301,8 @@ moe_status layer_forward_impl(const float* x, int32_t T, const float* gate_w, co
     int* inv_perm = ws_at<int>(ws, L.inv_perm);
     float* logits = ws_at<float>(ws, L.logits);
     const moe::XPrep xp = xprep_for(act_mode, routed->format, L, ws);
-    // small T: the logits kernel also prepares the hidden states, and top-k +
-    // dispatch are one block; larger T: each step is a kernel of its own
+    // the logits launch also prepares the hidden states; small T: top-k +
+    // dispatch are one block, larger T: kernels of their own
     const bool small = moe::router_splits(T, E, d) == 0;
     const bool fused = T <= moe::kFusedRouteT;
     const bool norm = block && norm_w != nullptr;
@@ -319,16 +319,13 @@ moe_status layer_forward_impl(const float* x, int32_t T, const float* gate_w, co
     // the shared expert's gate logit rides along as one more router row
     const float* sg = has_shared ? p->shared_gate : nullptr;
     float* sgl = sg ? ws_at<float>(ws, L.sgl) : nullptr;
+    const moe::RouterParts rp = small ? moe::RouterParts{} : moe::router_parts_at(ws_at<char>(ws, L.rparts), T, E, d);
     MOE_HIP(moe::launch_router_logits(xl, T, d, gate_w, E, logits, xp, (norm && small) ? norm_w : nullptr, eps, sg,
-                                      sgl, st),
+                                      sgl, &rp, st),
             "router logits");
     if (!fused) MOE_HIP(moe::launch_router_topk(logits, T, S, *p, idx, w, st), "router top-k");
     record(ev, 2 * MOE_STAGE_ROUTE + 1, st);
-    if (!small) {
-        record(ev, 2 * MOE_STAGE_QUANT_X, st);
-        MOE_HIP(moe::launch_xprep(xl, T, d, xp, st), "hidden states");
-        record(ev, 2 * MOE_STAGE_QUANT_X + 1, st);
-    }
+
     record(ev, 2 * MOE_STAGE_DISPATCH, st);
     if (fused)
         MOE_HIP(moe::launch_route_dispatch(logits, T, S, *p, idx, w, ws_at<int>(ws, L.counts),
@@ -427,10 +424,16 @@ moe_status moe_route(const float* x, int32_t T, int32_t d, const float* gate_w, 
     if (T == 0) return ok();
     MOE_REQUIRE(x && gate_w && topk_idx && topk_w, MOE_ERR_INVALID_ARG, "NULL tensor argument");
     MOE_REQUIRE(aligned16(x) && aligned16(gate_w), MOE_ERR_INVALID_ARG, "x and gate_w must be 16-byte aligned");
-    const size_t need = (size_t)moe::router_slices(T, p->n_experts, d, false) * T * p->n_experts * sizeof(float);
+    // the logits' slices, then the matrix-core router's operands (larger T)
+    const int E = p->n_experts;
+    const size_t lbytes = moe::align256((size_t)moe::router_slices(T, E, d, false) * T * E * sizeof(float));
+    const size_t need = lbytes + moe::router_parts_bytes(T, E, d);
     MOE_REQUIRE(ws != nullptr && ws_bytes >= need, MOE_ERR_WORKSPACE, "workspace %zu bytes < %zu needed",
                 ws ? ws_bytes : 0, need);
-    MOE_HIP(moe::launch_router(x, T, d, gate_w, *p, static_cast<float*>(ws), topk_idx, topk_w, stream), "router");
+    MOE_REQUIRE(aligned16(ws), MOE_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
+    const moe::RouterParts rp = moe::router_parts_at(static_cast<char*>(ws) + lbytes, T, E, d);
+    MOE_HIP(moe::launch_router(x, T, d, gate_w, *p, static_cast<float*>(ws), &rp, topk_idx, topk_w, stream),
+            "router");
     return ok();
 }
 

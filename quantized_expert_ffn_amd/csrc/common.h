@@ -41,6 +41,7 @@ struct WsLayout {
     size_t sgl = 0;        // f32  [S, T]  shared-expert gate logits per d slice (with a shared expert)
     size_t dhist = 0;      // i32  [chunks, E]  multi-block dispatch histograms (T*k > kDispatchWaveMax)
     size_t dbad = 0;       // i32  [chunks]
+    size_t rparts = 0;     // the matrix-core router's operands (router_parts_bytes), T > 16 only
     size_t total = 0;
     int max_tiles = 0;
 };
@@ -92,6 +93,42 @@ inline int router_slices(int T, int E, int d, bool norm) {
 
 inline size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
 
+// Operands of the matrix-core router (router_splits(T, E, d) > 0): every row
+// of X [T, d] and of the gate matrix [E, d] as f16 hi + lo parts of x / p,
+// with one power of two p per row (kept beside them), rows padded with zeros
+// to dp = d rounded up to 32.
+struct RouterParts {
+    _Float16* xh = nullptr;   // [T, dp]
+    _Float16* xl = nullptr;
+    _Float16* wh = nullptr;   // [E, dp]
+    _Float16* wl = nullptr;
+    float* xp = nullptr;      // [T]
+    float* wp = nullptr;      // [E]
+    int dp = 0;
+};
+inline int router_row_pad(int d) { return (d + 31) / 32 * 32; }
+inline size_t router_parts_bytes(int T, int E, int d) {
+    if (router_splits(T, E, d) == 0) return 0;
+    const size_t dp = (size_t)router_row_pad(d);
+    return 2 * align256((size_t)T * dp * 2) + 2 * align256((size_t)E * dp * 2) + align256((size_t)T * 4) +
+           align256((size_t)E * 4);
+}
+// the parts laid out from base (256-byte aligned), in router_parts_bytes bytes
+inline RouterParts router_parts_at(void* base, int T, int E, int d) {
+    RouterParts r;
+    r.dp = router_row_pad(d);
+    char* b = static_cast<char*>(base);
+    size_t off = 0;
+    auto take = [&](size_t bytes) { char* q = b + off; off += align256(bytes); return q; };
+    r.xh = reinterpret_cast<_Float16*>(take((size_t)T * r.dp * 2));
+    r.xl = reinterpret_cast<_Float16*>(take((size_t)T * r.dp * 2));
+    r.wh = reinterpret_cast<_Float16*>(take((size_t)E * r.dp * 2));
+    r.wl = reinterpret_cast<_Float16*>(take((size_t)E * r.dp * 2));
+    r.xp = reinterpret_cast<float*>(take((size_t)T * 4));
+    r.wp = reinterpret_cast<float*>(take((size_t)E * 4));
+    return r;
+}
+
 inline WsLayout ws_layout(int T, int k, int E, int d, int I, int act_mode, int has_shared) {
     WsLayout L;
     size_t off = 0;
@@ -131,6 +168,7 @@ inline WsLayout ws_layout(int T, int k, int E, int d, int I, int act_mode, int h
     L.y = take(R * d * 4);
     if (S > 0) L.xn = take((size_t)T * d * 4);
     if (has_shared) L.sgl = take((size_t)SL * T * 4);
+    if (S > 0) L.rparts = take(router_parts_bytes(T, E, d));
     if (n > (size_t)kDispatchWaveMax) {
         L.dhist = take((size_t)dispatch_chunk_count((int64_t)n) * E * 4);
         L.dbad = take((size_t)dispatch_chunk_count((int64_t)n) * 4);

@@ -68,20 +68,52 @@ __device__ __forceinline__ int block_exclusive_scan(int v, int* tmp, int* total)
     const int incl = wave_inclusive_scan(v);
     if (lane == kWave - 1) tmp[wave] = incl;
     __syncthreads();
-    if (threadIdx.x == 0) {
-        int run = 0;
-        for (int w = 0; w < kDispWaves; ++w) {
-            const int c = tmp[w];
-            tmp[w] = run;
-            run += c;
-        }
-        tmp[kDispWaves] = run;
+    if (wave == 0) {
+        // the wave totals, scanned by wave 0 (one lane each)
+        static_assert(kDispWaves <= kWave, "one lane per wave total");
+        const int t = lane < kDispWaves ? tmp[lane] : 0;
+        const int ti = wave_inclusive_scan(t);
+        if (lane < kDispWaves) tmp[lane] = ti - t;
+        if (lane == kDispWaves - 1) tmp[kDispWaves] = ti;
     }
     __syncthreads();
     const int res = tmp[wave] + incl - v;
     *total = tmp[kDispWaves];
     __syncthreads();
     return res;
+}
+
+// N exclusive scans at once, one value each per thread over the whole block
+// (every thread of the kDispThreads present), for the barriers of one scan.
+// tmp: N * (kDispWaves + 1) ints. ex[q] gets the exclusive prefix of v[q],
+// total[q] the sum.
+template <int N>
+__device__ __forceinline__ void block_exclusive_scan_n(const int (&v)[N], int* tmp, int (&ex)[N], int (&total)[N]) {
+    constexpr int W = kDispWaves + 1;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    int incl[N];
+#pragma unroll
+    for (int q = 0; q < N; ++q) {
+        incl[q] = wave_inclusive_scan(v[q]);
+        if (lane == kWave - 1) tmp[q * W + wave] = incl[q];
+    }
+    __syncthreads();
+    if (wave == 0) {
+#pragma unroll
+        for (int q = 0; q < N; ++q) {
+            const int t = lane < kDispWaves ? tmp[q * W + lane] : 0;
+            const int ti = wave_inclusive_scan(t);
+            if (lane < kDispWaves) tmp[q * W + lane] = ti - t;
+            if (lane == kDispWaves - 1) tmp[q * W + kDispWaves] = ti;
+        }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int q = 0; q < N; ++q) {
+        ex[q] = tmp[q * W + wave] + incl[q] - v[q];
+        total[q] = tmp[q * W + kDispWaves];
+    }
+    __syncthreads();
 }
 
 // Size class of a tile of r rows for the tile list's order: 0 for a full
@@ -110,23 +142,27 @@ __device__ __forceinline__ int tile_class(int r, int tile_rows) {
 // past the last run's end hold empty tiles (no rows), which the kernels
 // skip.
 __device__ __forceinline__ void build_work_lists(int E, int cnt, int off, int n_rows_routed, int T, int has_shared,
-                                 int tile_rows, int* scan_tmp, int* __restrict__ slots, int* __restrict__ tiles,
+                                 int tile_rows, int* __restrict__ slots, int* __restrict__ tiles,
                                  int* __restrict__ meta) {
+    __shared__ int wl_tmp[6 * (kDispWaves + 1)];
     const int e = threadIdx.x;
     const bool valid = e < E;
-    int n_active = 0;
     const int act = (valid && cnt > 0) ? 1 : 0;
-    const int slot = block_exclusive_scan(act, scan_tmp, &n_active);
-    if (act) {
-        int4* s = reinterpret_cast<int4*>(slots) + slot;
-        *s = make_int4(e, off, cnt, 0);
-    }
-    int4* tl = reinterpret_cast<int4*>(tiles);
     const int full = valid ? cnt / tile_rows : 0;
     const int part = valid ? cnt - full * tile_rows : 0;
     const int cls = part > 0 ? tile_class(part, tile_rows) : -1;
-    int n_full = 0;
-    const int fbase = block_exclusive_scan(full, scan_tmp, &n_full);
+    // the slot, the first full tile and the place among the partial tiles of
+    // its class, all in one set of scans
+    const int v[6] = {act, full, cls == 1, cls == 2, cls == 3, cls == 4};
+    int ex[6], tot[6];
+    block_exclusive_scan_n<6>(v, wl_tmp, ex, tot);
+    int n_active = tot[0];
+    if (act) {
+        int4* s = reinterpret_cast<int4*>(slots) + ex[0];
+        *s = make_int4(e, off, cnt, 0);
+    }
+    int4* tl = reinterpret_cast<int4*>(tiles);
+    const int n_full = tot[1], fbase = ex[1];
     const int s_full = has_shared ? T / tile_rows : 0;
     const int s_part = has_shared ? T - s_full * tile_rows : 0;
     const int s_cls = s_part > 0 ? tile_class(s_part, tile_rows) : -1;
@@ -142,12 +178,10 @@ __device__ __forceinline__ void build_work_lists(int E, int cnt, int off, int n_
     }
     for (int f = n_full + s_full + threadIdx.x; f < 8 * run; f += blockDim.x) tl[fpos(f)] = make_int4(0, 0, 0, 0);
     int pos = 8 * run;
-#pragma unroll 1
+#pragma unroll
     for (int c = 1; c <= 4; ++c) {
-        int n_c = 0;
-        const int b = block_exclusive_scan(cls == c ? 1 : 0, scan_tmp, &n_c);
-        if (cls == c) tl[pos + b] = make_int4(e, off + full * tile_rows, off + cnt, 0);
-        pos += n_c;
+        if (cls == c) tl[pos + ex[1 + c]] = make_int4(e, off + full * tile_rows, off + cnt, 0);
+        pos += tot[1 + c];
         if (s_cls == c) {
             if (threadIdx.x == 0)
                 tl[pos] = make_int4(E, n_rows_routed + s_full * tile_rows, n_rows_routed + T, 0);
@@ -268,7 +302,7 @@ __device__ __forceinline__ void dispatch_block(const int* idx, int* tmp, int T, 
         for (int t = tid; t < T; t += kDispThreads) row_token[n + t] = t;
 
     if (slots) {
-        build_work_lists(E, cnt, off, n, T, has_shared, tile_rows, scan_tmp, slots, tiles, meta);
+        build_work_lists(E, cnt, off, n, T, has_shared, tile_rows, slots, tiles, meta);
         __syncthreads();
         if (tid == 0) meta[2] = *bad_flag;
     }
@@ -486,6 +520,11 @@ __global__ __launch_bounds__(kDispThreads) void dispatch_scan_kernel(int* __rest
     __shared__ int scan_tmp[kDispWaves + 1];
     const int tid = threadIdx.x;
     const int n = T * k;
+    // the chunks' bad-id flags, spread over the threads so that their loads
+    // overlap the counts' loads below
+    int bad = 0;
+    if (slots)
+        for (int c = tid; c < nch; c += kDispThreads) bad |= chunk_bad[c];
     int cnt = 0;
     if (tid < E) {
         // 32 chunks' loads in flight at a time (40 chunks for a 4096-token,
@@ -513,12 +552,9 @@ __global__ __launch_bounds__(kDispThreads) void dispatch_scan_kernel(int* __rest
     if (row_token && has_shared)
         for (int t = tid; t < T; t += kDispThreads) row_token[n + t] = t;
     if (slots) {
-        build_work_lists(E, cnt, off, n, T, has_shared, tile_rows, scan_tmp, slots, tiles, meta);
-        if (tid == 0) {
-            int bad = 0;
-            for (int c = 0; c < nch; ++c) bad |= chunk_bad[c];
-            meta[2] = bad;
-        }
+        build_work_lists(E, cnt, off, n, T, has_shared, tile_rows, slots, tiles, meta);
+        const int any_bad = __syncthreads_or(bad);
+        if (tid == 0) meta[2] = any_bad;
     }
 }
 
@@ -617,7 +653,7 @@ __global__ __launch_bounds__(kDispThreads) void plan_kernel(const int* __restric
     const int before = block_exclusive_scan(cnt, scan_tmp, &total);
     cnt = min(cnt, max(n - before, 0));
     const int bad = __syncthreads_or(tid < E && (off_in != before || cnt != cnt_in));
-    build_work_lists(E, cnt, off, n, T, has_shared, tile_rows, scan_tmp, slots, tiles, meta);
+    build_work_lists(E, cnt, off, n, T, has_shared, tile_rows, slots, tiles, meta);
     if (tid == 0) meta[2] = bad;
 }
 

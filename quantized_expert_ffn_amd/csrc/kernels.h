@@ -10,8 +10,8 @@ hipError_t launch_quantize_weights(const float* w, int64_t rows, int cols, int m
                                    float* s, hipStream_t st);
 hipError_t launch_quantize_q8_0(const float* x, int64_t rows, int cols, int8_t* q, float* d, hipStream_t st);
 
-// Hidden-state preparation for the expert kernels, done by the router's
-// logits kernel at small T (else by a kernel of its own).
+// Hidden-state preparation for the expert kernels, done inside the router's
+// logits launch (or, for moe_expert_ffn, by a kernel of its own).
 enum { XPREP_NONE = 0, XPREP_SPLIT = 1, XPREP_Q8_0 = 2 };
 struct XPrep {
     int mode = XPREP_NONE;
@@ -27,17 +27,20 @@ struct XPrep {
     const float* inv_rms = nullptr;
 };
 
+// rp: the operand parts' memory (router_parts_at) when router_splits(T, E, d)
+// > 0, else unused (may be null)
 hipError_t launch_router(const float* x, int T, int d, const float* wg, const moe_router_params& p, float* logits,
-                         int* idx, float* w, hipStream_t st);
-// With router_splits(T, E, d) == 0 (small T) the logits kernel also does xp;
-// otherwise xp is ignored and the caller runs launch_xprep. norm_w (small T
-// only, else null): the logits and xp see RMSNorm(x) with gain norm_w and eps.
+                         const RouterParts* rp, int* idx, float* w, hipStream_t st);
+// The logits launches also do xp: waves of the small-T kernels, or the
+// operand preparation kernel of larger T (router_splits(T, E, d) > 0, which
+// needs rp). norm_w (router_splits(T, E, d) == 0 only, else null): the
+// logits and xp see RMSNorm(x) with gain norm_w and eps.
 // The logits leave as S = router_slices(T, E, d, norm_w != null) slice sums
 // [S, T, E]; sg (or null): the shared-expert gate vector, whose logit x . sg
 // goes to sgl as slice sums [S, T].
 hipError_t launch_router_logits(const float* x, int T, int d, const float* wg, int E, float* logits,
                                 const XPrep& xp, const float* norm_w, float eps, const float* sg, float* sgl,
-                                hipStream_t st);
+                                const RouterParts* rp, hipStream_t st);
 // RMSNorm of T rows into xn [T, d] (the larger-T path)
 hipError_t launch_rmsnorm(const float* x, int T, int d, const float* norm_w, float eps, float* xn, hipStream_t st);
 hipError_t launch_router_topk(const float* logits, int T, int S, const moe_router_params& p, int* idx, float* w,

@@ -79,14 +79,11 @@ __device__ __forceinline__ void split_group(const float* __restrict__ x, int T, 
 // fp32 steps of quantize_q8_0_kernel: d = amax / 127, inv = 1 / d,
 // q = rne(x * inv). The codes leave as f16 (exact) in operand-slot order,
 // ready to be a matrix-core operand.
+// v: the lane's 8 values, off: their position in [T, d], item = t * G + g;
+// the group's four lanes are neighbours (lane / 4 the same).
 template <int FMT>
-__device__ __forceinline__ void q8_item(const float* __restrict__ x, int d, int G, int item, const XPrep& xp) {
+__device__ __forceinline__ void q8_store(const float (&v)[8], size_t off, int item, const XPrep& xp) {
     const int sub = threadIdx.x & 3;
-    const int t = item / G, g = item - t * G;
-    const size_t off = (size_t)t * d + g * kGroup + 8 * sub;
-    float4 a, b;
-    load8(x, t, d, g * kGroup + 8 * sub, xp, a, b);
-    const float v[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
     float amax = 0.0f;
 #pragma unroll
     for (int j = 0; j < 8; ++j) amax = fmaxf(amax, fabsf(v[j]));
@@ -102,6 +99,16 @@ __device__ __forceinline__ void q8_item(const float* __restrict__ x, int d, int 
     }
     *reinterpret_cast<v8h*>(xp.q + off) = q;
     if (sub == 0) xp.qd[item] = dd;
+}
+
+template <int FMT>
+__device__ __forceinline__ void q8_item(const float* __restrict__ x, int d, int G, int item, const XPrep& xp) {
+    const int sub = threadIdx.x & 3;
+    const int t = item / G, g = item - t * G;
+    float4 a, b;
+    load8(x, t, d, g * kGroup + 8 * sub, xp, a, b);
+    const float v[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+    q8_store<FMT>(v, (size_t)t * d + g * kGroup + 8 * sub, item, xp);
 }
 
 // the preparation job, spread over every wave of the grid
@@ -123,6 +130,13 @@ __device__ __forceinline__ void xprep_waves(const float* __restrict__ x, int T, 
             else q8_item<MOE_W_INT2_G32>(x, d, G, item, xp);
         }
     }
+}
+
+// waves for one pass over the preparation job: one per group column (the
+// split), one per 16 (token, group) items (Q8_0)
+inline int xprep_waves_wanted(int T, int d, const XPrep& xp) {
+    const int G = d / kGroup;
+    return xp.mode == XPREP_SPLIT ? G : xp.mode == XPREP_Q8_0 ? (T * G + 15) / 16 : 0;
 }
 
 __global__ __launch_bounds__(256) void xprep_kernel(const float* __restrict__ x, int T, int d, const XPrep xp) {
@@ -314,60 +328,146 @@ __global__ __launch_bounds__(256) void rmsnorm_kernel(const float* __restrict__ 
 }
 
 // ---------------------------------------------------------------------------
-// Logits, larger T: fp32-level products on the bf16 matrix cores
-// (v_mfma_f32_16x16x32_bf16), split over d.
+// Logits, larger T: fp32-level products on the f16 matrix cores
+// (v_mfma_f32_16x16x32_f16), split over d, in two kernels.
 //
-// Each fp32 value v is split into three bf16 parts, v = h + m + l exactly
-// (h = bf16(v), m = bf16(v - h), l = bf16(v - h - m): 8 significant bits
-// each, and bf16 has the fp32 exponent range, so no scaling is needed). A
-// product of two parts is exact in fp32, and the six products
-//     hh + hm + mh + hl + lh + mm
-// are the fp32 product up to terms of 2^-24 relative; the matrix core adds
-// them in fp32. Six bf16 products take a third of the time of the same MACs
-// on the fp32 matrix cores.
+// router_prep_kernel, one wave per row of X and of the gate matrix: with
+// p = 2^(e-15) where e is the smallest exponent such that the row's largest
+// |v| < 2^e, each value splits as v/p = hi + lo, hi = f16(v/p) and
+// lo = f16(v/p - hi), both rounded to nearest even (the scaling by a power of
+// two and the difference are exact; |v/p| < 2^15 keeps hi finite). Then
+// |v/p - hi - lo| <= 2^-22 |v/p| while lo is a normal f16, else <= 2^-25 (an
+// absolute bound, 2^-39 of the row's largest value). A product of two parts
+// is exact in fp32; hi*hi + hi*lo + lo*hi leaves out lo*lo (<= 2^-22 of
+// |x w|), so each product x*w carries a relative error of about 2^-21, below
+// the rounding of the fp32 sums it enters. X's waves also take the rest of
+// the preparation while they hold the row: the Q8_0 codes of the expert
+// kernels, and the shared-expert gate's logit x . sg (fp32 sums in a fixed
+// order) into slice 0 of sgl [S, T] with zeros in the other slices. With the
+// f32 path's preparation (a power per 32-column group over all rows), waves
+// past the rows do that job.
 //
-// Block: kRBM tokens x kRBN experts, four waves of 64 tokens x 32 experts
-// (4 x 2 products of 16 x 16 per part pair); blockIdx.z = slice. The slice
-// goes through LDS kRKC = 32 k (one product) at a time: each row's chunk is
-// one 128-byte line read by 8 neighbouring lanes, split into its parts on the
-// way in, and the next chunk's loads are in flight while the current one is
-// multiplied. Rows past T or E read a valid row and are never stored. A
-// shared-expert gate vector sg is expert row E; its slice sums go to
-// sgl [S, T].
+// router_logits_f16_kernel: block = kRBM tokens x kRBN experts, four waves of
+// 64 tokens x 32 experts (4 x 2 products of 16 x 16 per part pair);
+// blockIdx.z = slice. The slice goes through LDS kRKC = 32 k (one product) at
+// a time, the next chunk's loads in flight while the current one is
+// multiplied; the products of the parts are added small ones first, and the
+// sum is scaled by the two rows' powers (exact). Rows past T or E read a
+// valid row and are never stored.
 // ---------------------------------------------------------------------------
 constexpr int kRBM = 128, kRBN = 64, kRKC = 32;
-constexpr int kRPad = kRKC + 8;   // LDS row stride (bf16): 16-byte reads of 16 rows hit distinct banks
+constexpr int kRPad = kRKC + 8;   // LDS row stride (f16): 16-byte reads of 16 rows hit distinct banks
 
-typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
-
-// v = h + m + l, each part bf16 (round to nearest even), packed two per dword
-__device__ __forceinline__ void split3_bf16(float4 v, uint2& h, uint2& m, uint2& l) {
-    const float a[4] = {v.x, v.y, v.z, v.w};
-    uint16_t ph[4], pm[4], pl[4];
+// one row (X row t, or gate row e) by one wave: 8 values per lane and pass
+// of 512. NP > 0: the row has at most NP passes and stays in registers (all
+// its loads go out together); NP == 0: any length, read twice (the second
+// read comes from the cache).
+template <int NP>
+__device__ __forceinline__ void prep_row(const float* __restrict__ src, int d, int dp, _Float16* __restrict__ hi_out,
+                                         _Float16* __restrict__ lo_out, float* __restrict__ pow_out, int t,
+                                         const XPrep& xp, bool q8, const float* __restrict__ sg,
+                                         float* __restrict__ sgl, int T, int S) {
+    constexpr int kPass = 8 * kWave;
+    const int lane = threadIdx.x & 63;
+    auto load = [&](const float* __restrict__ p, int c, float (&v)[8]) __attribute__((always_inline)) {
+        // d % 4 == 0: a float4 is wholly in or out; zeros pad to dp
+        const float4 a = c + 4 <= d ? *reinterpret_cast<const float4*>(p + c) : make_float4(0.f, 0.f, 0.f, 0.f);
+        const float4 b = c + 8 <= d ? *reinterpret_cast<const float4*>(p + c + 4) : make_float4(0.f, 0.f, 0.f, 0.f);
+        v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+        v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+    };
+    auto scan = [&](const float (&v)[8], int c, float& amax, float& dot) __attribute__((always_inline)) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const __bf16 bh = (__bf16)a[i];
-        const float r1 = a[i] - (float)bh;
-        const __bf16 bm = (__bf16)r1;
-        const float r2 = r1 - (float)bm;
-        const __bf16 bl = (__bf16)r2;
-        ph[i] = __builtin_bit_cast(uint16_t, bh);
-        pm[i] = __builtin_bit_cast(uint16_t, bm);
-        pl[i] = __builtin_bit_cast(uint16_t, bl);
+        for (int j = 0; j < 8; ++j) amax = fmaxf(amax, fabsf(v[j]));
+        if (sg) {
+            float w[8];
+            load(sg, c, w);
+#pragma unroll
+            for (int j = 0; j < 8; ++j) dot = fmaf(v[j], w[j], dot);
+        }
+    };
+    auto emit = [&](const float (&v)[8], int c, float up) __attribute__((always_inline)) {
+        v8h h, l;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const float sv = v[j] * up;
+            const _Float16 hv = (_Float16)sv;
+            h[j] = hv;
+            l[j] = (_Float16)(sv - (float)hv);
+        }
+        *reinterpret_cast<v8h*>(hi_out + c) = h;
+        *reinterpret_cast<v8h*>(lo_out + c) = l;
+        if (q8 && c < d) {
+            // the layer path has d % 32 == 0: the group's four lanes are all here
+            const int G = d / kGroup, g = c / kGroup;
+            const size_t off = (size_t)t * d + c;
+            if (xp.fmt == MOE_W_INT8_G32) q8_store<MOE_W_INT8_G32>(v, off, t * G + g, xp);
+            else if (xp.fmt == MOE_W_INT4_G32) q8_store<MOE_W_INT4_G32>(v, off, t * G + g, xp);
+            else q8_store<MOE_W_INT2_G32>(v, off, t * G + g, xp);
+        }
+    };
+    float amax = 0.0f, dot = 0.0f;
+    int ex;
+    if constexpr (NP > 0) {
+        float v[NP][8];
+#pragma unroll
+        for (int p = 0; p < NP; ++p) load(src, p * kPass + 8 * lane, v[p]);
+#pragma unroll
+        for (int p = 0; p < NP; ++p) scan(v[p], p * kPass + 8 * lane, amax, dot);
+        amax = wave_max_all(amax);
+        ex = pow2_exponent(amax);
+        const float up = ldexpf(1.0f, 15 - ex);
+#pragma unroll
+        for (int p = 0; p < NP; ++p)
+            if (p * kPass + 8 * lane < dp) emit(v[p], p * kPass + 8 * lane, up);
+    } else {
+        for (int c = 8 * lane; c < dp; c += kPass) {
+            float v[8];
+            load(src, c, v);
+            scan(v, c, amax, dot);
+        }
+        amax = wave_max_all(amax);
+        ex = pow2_exponent(amax);
+        const float up = ldexpf(1.0f, 15 - ex);
+        for (int c = 8 * lane; c < dp; c += kPass) {
+            float v[8];
+            load(src, c, v);
+            emit(v, c, up);
+        }
     }
-    h = make_uint2(ph[0] | ((uint32_t)ph[1] << 16), ph[2] | ((uint32_t)ph[3] << 16));
-    m = make_uint2(pm[0] | ((uint32_t)pm[1] << 16), pm[2] | ((uint32_t)pm[3] << 16));
-    l = make_uint2(pl[0] | ((uint32_t)pl[1] << 16), pl[2] | ((uint32_t)pl[3] << 16));
+    if (sg) dot = wave_sum_all(dot);
+    if (lane == 0) pow_out[t] = ldexpf(1.0f, ex - 15);
+    if (sg)
+        for (int s = lane; s < S; s += kWave) sgl[(size_t)s * T + t] = s == 0 ? dot : 0.0f;
 }
 
-__global__ __launch_bounds__(256) void router_logits_mfma_kernel(const float* __restrict__ x,
-                                                                 const float* __restrict__ wg, int T, int d,
-                                                                 int E, int kslice, float* __restrict__ L,
-                                                                 const float* __restrict__ sg,
-                                                                 float* __restrict__ sgl) {
-    // [part][row][k], parts h, m, l
-    __shared__ __attribute__((aligned(16))) uint16_t xs[3][kRBM * kRPad];
-    __shared__ __attribute__((aligned(16))) uint16_t wsh[3][kRBN * kRPad];
+// waves 0 .. T-1: rows of X; T .. T+E-1: gate rows; then the f32 path's
+// preparation job (XPREP_SPLIT), if any
+template <int NP>
+__global__ __launch_bounds__(256) void router_prep_kernel(const float* __restrict__ x, int T, int d,
+                                                          const float* __restrict__ wg, int E,
+                                                          const RouterParts rp, const XPrep xp,
+                                                          const float* __restrict__ sg, float* __restrict__ sgl,
+                                                          int S) {
+    const int gw = blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (gw < T) {
+        prep_row<NP>(x + (size_t)gw * d, d, rp.dp, rp.xh + (size_t)gw * rp.dp, rp.xl + (size_t)gw * rp.dp, rp.xp,
+                     gw, xp, xp.mode == XPREP_Q8_0, sg, sgl, T, S);
+    } else if (gw < T + E) {
+        const int e = gw - T;
+        prep_row<NP>(wg + (size_t)e * d, d, rp.dp, rp.wh + (size_t)e * rp.dp, rp.wl + (size_t)e * rp.dp, rp.wp, e,
+                     xp, false, nullptr, nullptr, T, S);
+    } else if (xp.mode == XPREP_SPLIT) {
+        xprep_waves(x, T, d, xp, gw - T - E, gridDim.x * 4 - T - E);
+    }
+}
+
+__global__ __launch_bounds__(256) void router_logits_f16_kernel(const RouterParts rp, int T, int E, int kslice,
+                                                                float* __restrict__ L) {
+    // [part][row][k], parts hi, lo
+    __shared__ __attribute__((aligned(16))) _Float16 xs[2][kRBM * kRPad];
+    __shared__ __attribute__((aligned(16))) _Float16 wsh[2][kRBN * kRPad];
+    static_assert(kRBM == 128 && kRBN == 64, "two token rows and one expert row per thread");
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int wm = wave & 1, wn = wave >> 1;
     // XCD-aware order (blocks go to the 8 XCDs in turn by linear id): every
@@ -381,27 +481,24 @@ __global__ __launch_bounds__(256) void router_logits_mfma_kernel(const float* __
     if (tb >= T) return;
     const int eb = (col % gridDim.x) * kRBN;
     const int ks = col / gridDim.x;
-    const int kbeg = ks * kslice, kend = min(d, kbeg + kslice);
-    // loads: rows lr + 32 j, k quad lq of each chunk
-    const int lr = tid >> 3, lq = (tid & 7) * 4;
-    const float* xsrc[kRBM / 32];
-    const float* wsrc[kRBN / 32];
-#pragma unroll
-    for (int j = 0; j < kRBM / 32; ++j) xsrc[j] = x + (size_t)min(tb + lr + 32 * j, T - 1) * d + lq;
-#pragma unroll
-    for (int j = 0; j < kRBN / 32; ++j) {
-        const int e = eb + lr + 32 * j;
-        wsrc[j] = (sg != nullptr && e == E) ? sg + lq : wg + (size_t)min(e, E - 1) * d + lq;
-    }
-    float4 xr[kRBM / 32], wr[kRBN / 32];
+    const int dp = rp.dp;
+    const int kbeg = ks * kslice, kend = min(dp, kbeg + kslice);
+    // loads: rows lr and lr + 64 of the token tile and row lr of the expert
+    // tile, halves 8 lq .. 8 lq + 7 of each 32-wide chunk (dp % 32 == 0 and
+    // kslice % 64 == 0: every chunk is whole); rows past T or E read the last
+    // valid row (never stored)
+    const int lr = tid >> 2, lq = (tid & 3) * 8;
+    const size_t xr0 = (size_t)min(tb + lr, T - 1) * dp + lq, xr1 = (size_t)min(tb + lr + 64, T - 1) * dp + lq;
+    const size_t wrow = (size_t)min(eb + lr, E - 1) * dp + lq;
+    uint4 xh0, xh1, xl0, xl1, wh0, wl0;
+    auto ld16 = [](const _Float16* p) { return *reinterpret_cast<const uint4*>(p); };
     auto gload = [&](int k0) {
-        const bool ok = k0 + lq < kend;   // d % 4 == 0: a quad is all in or all out
-#pragma unroll
-        for (int j = 0; j < kRBM / 32; ++j)
-            xr[j] = ok ? *reinterpret_cast<const float4*>(xsrc[j] + k0) : make_float4(0.f, 0.f, 0.f, 0.f);
-#pragma unroll
-        for (int j = 0; j < kRBN / 32; ++j)
-            wr[j] = ok ? *reinterpret_cast<const float4*>(wsrc[j] + k0) : make_float4(0.f, 0.f, 0.f, 0.f);
+        xh0 = ld16(rp.xh + xr0 + k0);
+        xh1 = ld16(rp.xh + xr1 + k0);
+        xl0 = ld16(rp.xl + xr0 + k0);
+        xl1 = ld16(rp.xl + xr1 + k0);
+        wh0 = ld16(rp.wh + wrow + k0);
+        wl0 = ld16(rp.wl + wrow + k0);
     };
     // operand rows of this lane: tokens 64 wm + 16 i + (lane % 16), experts
     // 32 wn + 16 j + (lane % 16); k 8 (lane / 16) .. + 7 of the chunk
@@ -414,65 +511,58 @@ __global__ __launch_bounds__(256) void router_logits_mfma_kernel(const float* __
     if (kbeg < kend) gload(kbeg);
     for (int k0 = kbeg; k0 < kend; k0 += kRKC) {
         __syncthreads();   // the previous chunk's readers are done
-#pragma unroll
-        for (int j = 0; j < kRBM / 32; ++j) {
-            uint2 h, m, l;
-            split3_bf16(xr[j], h, m, l);
-            const int o = (lr + 32 * j) * kRPad + lq;
-            *reinterpret_cast<uint2*>(&xs[0][o]) = h;
-            *reinterpret_cast<uint2*>(&xs[1][o]) = m;
-            *reinterpret_cast<uint2*>(&xs[2][o]) = l;
-        }
-#pragma unroll
-        for (int j = 0; j < kRBN / 32; ++j) {
-            uint2 h, m, l;
-            split3_bf16(wr[j], h, m, l);
-            const int o = (lr + 32 * j) * kRPad + lq;
-            *reinterpret_cast<uint2*>(&wsh[0][o]) = h;
-            *reinterpret_cast<uint2*>(&wsh[1][o]) = m;
-            *reinterpret_cast<uint2*>(&wsh[2][o]) = l;
-        }
-        __syncthreads();
+        *reinterpret_cast<uint4*>(&xs[0][lr * kRPad + lq]) = xh0;
+        *reinterpret_cast<uint4*>(&xs[0][(lr + 64) * kRPad + lq]) = xh1;
+        *reinterpret_cast<uint4*>(&xs[1][lr * kRPad + lq]) = xl0;
+        *reinterpret_cast<uint4*>(&xs[1][(lr + 64) * kRPad + lq]) = xl1;
+        *reinterpret_cast<uint4*>(&wsh[0][lr * kRPad + lq]) = wh0;
+        *reinterpret_cast<uint4*>(&wsh[1][lr * kRPad + lq]) = wl0;
+        // the next chunk's loads go out before the barrier: they have the
+        // wait and this chunk's products to arrive
         if (k0 + kRKC < kend) gload(k0 + kRKC);
+        __syncthreads();
         __builtin_amdgcn_sched_barrier(0);
-        v8bf b[2][3];
+        v8h b[2][2];
 #pragma unroll
         for (int j = 0; j < 2; ++j)
 #pragma unroll
-            for (int p = 0; p < 3; ++p)
-                b[j][p] = __builtin_bit_cast(v8bf, *reinterpret_cast<const uint4*>(
-                                                        &wsh[p][(32 * wn + 16 * j + orow) * kRPad + ok8]));
+            for (int p = 0; p < 2; ++p)
+                b[j][p] = *reinterpret_cast<const v8h*>(&wsh[p][(32 * wn + 16 * j + orow) * kRPad + ok8]);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            v8bf a[3];
+            v8h a[2];
 #pragma unroll
-            for (int p = 0; p < 3; ++p)
-                a[p] = __builtin_bit_cast(v8bf, *reinterpret_cast<const uint4*>(
-                                                    &xs[p][(64 * wm + 16 * i + orow) * kRPad + ok8]));
+            for (int p = 0; p < 2; ++p)
+                a[p] = *reinterpret_cast<const v8h*>(&xs[p][(64 * wm + 16 * i + orow) * kRPad + ok8]);
 #pragma unroll
             for (int j = 0; j < 2; ++j) {
                 // the small terms first
-                acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[1], b[j][1], acc[i][j], 0, 0, 0);
-                acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[0], b[j][2], acc[i][j], 0, 0, 0);
-                acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[2], b[j][0], acc[i][j], 0, 0, 0);
-                acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[0], b[j][1], acc[i][j], 0, 0, 0);
-                acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[1], b[j][0], acc[i][j], 0, 0, 0);
-                acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[0], b[j][0], acc[i][j], 0, 0, 0);
+                acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[1], b[j][0], acc[i][j], 0, 0, 0);
+                acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[0], b[j][1], acc[i][j], 0, 0, 0);
+                acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[0], b[j][0], acc[i][j], 0, 0, 0);
             }
         }
     }
+    // output lane l, register r: token 4 (l / 16) + r, expert l % 16 of the
+    // tile pair; the rows' powers first (all loads out together), then the
+    // stores
     float* out = L + (size_t)ks * T * E;
+    float pe[2], pt[4][4];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) pe[j] = rp.wp[min(eb + 32 * wn + 16 * j + orow, E - 1)];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) pt[i][r] = rp.xp[min(tb + 64 * wm + 16 * i + 4 * (lane >> 4) + r, T - 1)];
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
         const int e = eb + 32 * wn + 16 * j + orow;
-        const bool is_sg = sg != nullptr && e == E;
 #pragma unroll
         for (int i = 0; i < 4; ++i)
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int t = tb + 64 * wm + 16 * i + 4 * (lane >> 4) + r;
-                if (t < T && e < E) out[(size_t)t * E + e] = acc[i][j][r];
-                if (t < T && is_sg) sgl[(size_t)ks * T + t] = acc[i][j][r];
+                if (t < T && e < E) out[(size_t)t * E + e] = (acc[i][j][r] * pt[i][r]) * pe[j];
             }
     }
 }
@@ -515,16 +605,14 @@ TopkArgs topk_args(const float* logits, int T, int S, const moe_router_params& p
 
 hipError_t launch_router_logits(const float* x, int T, int d, const float* wg, int E, float* logits,
                                 const XPrep& xp, const float* norm_w, float eps, const float* sg, float* sgl,
-                                hipStream_t st) {
+                                const RouterParts* rp, hipStream_t st) {
     if (T == 0) return hipSuccess;
     const int S = router_splits(T, E, d);
     const int rows = E + (sg ? 1 : 0);   // experts, then the shared-expert gate
     if (S == 0 && !norm_w && T > kSmallSplitMinT) {
         const int nrb = (rows + 15) / 16, SS = router_slices(T, E, d, false);
         // preparation blocks: enough waves for one pass over the job
-        const int G = d / kGroup;
-        const int prep_waves = xp.mode == XPREP_SPLIT ? G : xp.mode == XPREP_Q8_0 ? (T * G + 15) / 16 : 0;
-        const int nprep = (prep_waves + 3) / 4;
+        const int nprep = (xprep_waves_wanted(T, d, xp) + 3) / 4;
         hipLaunchKernelGGL(router_logits_small_kernel, dim3(nrb * SS + nprep), dim3(256), 0, st, x, wg, T, d, E,
                            router_small_units(d), nrb, SS, logits, xp, sg, sgl);
         return hipGetLastError();
@@ -542,10 +630,22 @@ hipError_t launch_router_logits(const float* x, int T, int d, const float* wg, i
 #undef MOE_RL
         return hipGetLastError();
     }
-    // larger T: the preparation is the caller's own launch (launch_xprep)
-    const int kslice = router_kslice(d, S);
-    const dim3 grid((rows + kRBN - 1) / kRBN, ((T + kRBM - 1) / kRBM + 7) / 8 * 8, S);
-    hipLaunchKernelGGL(router_logits_mfma_kernel, grid, dim3(256), 0, st, x, wg, T, d, E, kslice, logits, sg, sgl);
+    // larger T: the operand parts (and the rest of the preparation), then
+    // the products
+    if (rp == nullptr || rp->dp != router_row_pad(d)) return hipErrorInvalidValue;
+    const int split_waves = xp.mode == XPREP_SPLIT ? xprep_waves_wanted(T, d, xp) : 0;
+    const dim3 pgrid((T + E + split_waves + 3) / 4);
+    const int passes = (rp->dp + 8 * kWave - 1) / (8 * kWave);
+#define MOE_PREP(NP) hipLaunchKernelGGL(router_prep_kernel<NP>, pgrid, dim3(256), 0, st, x, T, d, wg, E, *rp, xp, sg, sgl, S)
+    if (passes <= 1) MOE_PREP(1);
+    else if (passes <= 2) MOE_PREP(2);
+    else if (passes <= 4) MOE_PREP(4);
+    else MOE_PREP(0);
+#undef MOE_PREP
+    const hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+    const dim3 grid((E + kRBN - 1) / kRBN, ((T + kRBM - 1) / kRBM + 7) / 8 * 8, S);
+    hipLaunchKernelGGL(router_logits_f16_kernel, grid, dim3(256), 0, st, *rp, T, E, router_kslice(d, S), logits);
     return hipGetLastError();
 }
 
@@ -556,9 +656,8 @@ hipError_t launch_rmsnorm(const float* x, int T, int d, const float* norm_w, flo
 }
 
 hipError_t launch_xprep(const float* x, int T, int d, const XPrep& xp, hipStream_t st) {
-    if (T == 0 || xp.mode == XPREP_NONE) return hipSuccess;
-    const int G = d / kGroup;
-    const int waves = xp.mode == XPREP_SPLIT ? G : (T * G + 15) / 16;
+    const int waves = xprep_waves_wanted(T, d, xp);
+    if (T == 0 || waves == 0) return hipSuccess;
     hipLaunchKernelGGL(xprep_kernel, dim3((waves + 3) / 4), dim3(256), 0, st, x, T, d, xp);
     return hipGetLastError();
 }
@@ -581,8 +680,9 @@ hipError_t launch_router_topk(const float* logits, int T, int S, const moe_route
 }
 
 hipError_t launch_router(const float* x, int T, int d, const float* wg, const moe_router_params& p,
-                         float* logits, int* idx, float* w, hipStream_t st) {
-    hipError_t err = launch_router_logits(x, T, d, wg, p.n_experts, logits, XPrep{}, nullptr, 0.0f, nullptr, nullptr, st);
+                         float* logits, const RouterParts* rp, int* idx, float* w, hipStream_t st) {
+    hipError_t err =
+        launch_router_logits(x, T, d, wg, p.n_experts, logits, XPrep{}, nullptr, 0.0f, nullptr, nullptr, rp, st);
     if (err != hipSuccess) return err;
     return launch_router_topk(logits, T, router_slices(T, p.n_experts, d, false), p, idx, w, st);
 }

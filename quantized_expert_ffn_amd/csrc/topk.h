@@ -211,30 +211,64 @@ __device__ __forceinline__ void topk_token(const TopkArgs& a, int t, bool active
         }
     }
 
-    // k rounds of wave argmax; lane j keeps slot j's expert and value
-    uint32_t taken = 0;
+    // Each lane sorts its EPL (key, id) pairs by rank (Batcher's odd-even
+    // merge sort, a fixed network), so a lane's best candidate is its head.
+    // Then k rounds: the wave argmax of the heads (a lane's ids are all below
+    // the next lane's, so the first lane holding the largest head key holds
+    // the winner, ties to the lower id), and the winning lane drops its head.
+    // Lane j keeps slot j's expert and key.
+    int id[EPL];
+#pragma unroll
+    for (int i = 0; i < EPL; ++i) id[i] = lane * EPL + i;
+#pragma unroll
+    for (int p = 1; p < EPL; p <<= 1)
+#pragma unroll
+        for (int q = p; q >= 1; q >>= 1)
+#pragma unroll
+            for (int j = q % p; j + q < EPL; j += 2 * q)
+#pragma unroll
+                for (int i = 0; i < q; ++i) {
+                    const int u = i + j, v = i + j + q;
+                    if (v < EPL && u / (2 * p) == v / (2 * p) && ranks_before(key[v], id[v], key[u], id[u])) {
+                        const float tk = key[u];
+                        key[u] = key[v];
+                        key[v] = tk;
+                        const int ti = id[u];
+                        id[u] = id[v];
+                        id[v] = ti;
+                    }
+                }
+    if (a.mode != MOE_ROUTER_SOFTMAX_TOPK) {
+        // the selected experts' sigmoid scores, looked up by expert after the
+        // rounds (the group scores above read keybuf before these writes, and
+        // a wave executes its LDS operations in order)
+#pragma unroll
+        for (int i = 0; i < EPL; ++i)
+            if (lane * EPL + i < E) keybuf[lane * EPL + i] = val[i];
+    }
     int my_e = -1;
     float my_v = 0.0f;
     for (int j = 0; j < k; ++j) {
-        float bk = NEG_INF;
-        int be = INT_MAX;
+        const float m = wave_max_all(key[0]);
+        if (!(m > NEG_INF)) break;               // no candidate left: cannot happen for validated k
+        const uint64_t b = __ballot(key[0] == m);
+        const int src = b ? __builtin_ctzll(b) : 0;
+        const int be = __builtin_amdgcn_readlane(id[0], src);
+        if (lane == j) { my_e = be; my_v = m; }
+        if (lane == src) {
 #pragma unroll
-        for (int i = 0; i < EPL; ++i) {
-            const int e = lane * EPL + i;
-            const bool cand = e < E && !((taken >> i) & 1u) && key[i] != NEG_INF;
-            if (cand && ranks_before(key[i], e, bk, be)) { bk = key[i]; be = e; }
+            for (int i = 0; i + 1 < EPL; ++i) {
+                key[i] = key[i + 1];
+                id[i] = id[i + 1];
+            }
+            key[EPL - 1] = NEG_INF;
         }
-        wave_argmax(bk, be);
-        if (be == INT_MAX) break;                 // cannot happen for validated k
-        float v = 0.0f;
-        const int owner = be / EPL;
-        if (lane == owner) {
-#pragma unroll
-            for (int i = 0; i < EPL; ++i)
-                if (i == be - owner * EPL) { v = val[i]; taken |= 1u << i; }
-        }
-        v = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), owner));
-        if (lane == j) { my_e = be; my_v = v; }
+    }
+    if (a.mode != MOE_ROUTER_SOFTMAX_TOPK) {
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        my_v = my_e >= 0 ? keybuf[my_e] : 0.0f;
     }
 
     float wj = 0.0f;

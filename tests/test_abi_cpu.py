@@ -325,3 +325,36 @@ def test_host_abi_layer_under_address_sanitizer(tmp_path):
     assert "AddressSanitizer" not in res.stderr, res.stderr[-4000:]
     assert res.returncode == 0, res.stdout + res.stderr[-4000:]
     assert "passed" in res.stdout
+
+
+def test_binding_rejects_mismatched_shapes():
+    """The binding checks every tensor against the sizes it passes to the
+    library before any pointer is taken: a tensor of the wrong shape is a
+    ValueError on the host, never a kernel reading or writing past its end
+    (CPU tensors here; the checks come before the device check)."""
+    import torch
+    E, d, I, T, k = 8, 64, 128, 4, 2
+    routed = _lib.QuantExperts.empty(E, d, I, "int8", device="cpu")
+    p = _lib.router_params(E, k)
+    x = torch.zeros((T, d))
+    gate_w = torch.zeros((E, d))
+    out = torch.zeros((T, d))
+    ws = torch.zeros(1 << 16, dtype=torch.uint8)
+    for bad in (dict(x=torch.zeros((T, d + 32))), dict(gate_w=torch.zeros((E - 1, d))),
+                dict(out=torch.zeros((T - 1, d))), dict(x=torch.zeros(T * d))):
+        a = dict(x=x, gate_w=gate_w, out=out)
+        a.update(bad)
+        with pytest.raises(ValueError):
+            qe.moe_layer_forward(a["x"], a["gate_w"], p, routed, None, 0, a["out"], ws)
+        with pytest.raises(ValueError):
+            qe.moe_layer_forward_noalloc(a["x"], a["gate_w"], p, routed, None, 0, a["out"])
+    with pytest.raises(ValueError):
+        qe.moe_block_forward(x, torch.zeros(d + 1), 1e-5, gate_w, p, routed, None, 0, out, ws)
+    with pytest.raises(ValueError):   # codes of a stack that does not match its scales
+        _lib.QuantExperts("int8", routed.gate_q[:, :-32], routed.gate_s, routed.up_q, routed.up_s, routed.down_q,
+                          routed.down_s)
+    with pytest.raises(ValueError):
+        qe.moe_combine(torch.zeros((T * k, d)), torch.zeros((T, k)), torch.zeros(T * k - 1, dtype=torch.int32),
+                       None, torch.zeros((T, d)))
+    with pytest.raises(ValueError):
+        qe.moe_calib_prefill_mix(4, 2, torch.zeros(4 * 512 - 1))
