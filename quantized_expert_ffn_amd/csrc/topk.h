@@ -107,36 +107,39 @@ __device__ __forceinline__ void topk_token(const TopkArgs& a, int t, bool active
     // the slices' partial sums, added in slice order; a batch of slices is
     // loaded before any of it is added, so the loads overlap
     constexpr int SB = EPL >= 16 ? 2 : EPL >= 8 ? 4 : 8;
-    // a lane's EPL experts are consecutive: 16-byte loads when they all lie
-    // inside the row and the rows are 16-byte aligned (E % 4 == 0)
-    const bool vec = (EPL % 4 == 0) && (E % 4 == 0) && lane * EPL + EPL <= E;
-    for (int s0 = 0; s0 < a.S; s0 += SB) {
-        float pv[SB][EPL];
+    // a lane's EPL experts are consecutive: 16-byte loads when every lane's
+    // run lies inside the row (E == 64 EPL, so the rows are 16-byte aligned
+    // too). The condition is the same for the whole wave, and each path has
+    // its own loop: with one loop, the compiler merged the two paths into
+    // 4-byte loads.
+    auto add_slices = [&](auto load_row) __attribute__((always_inline)) {
+        for (int s0 = 0; s0 < a.S; s0 += SB) {
+            float pv[SB][EPL];
 #pragma unroll
-        for (int u = 0; u < SB; ++u) {
-            const int s = min(s0 + u, a.S - 1);
-            const float* row = a.L + ((size_t)s * a.T + tc) * E;
-            if constexpr (EPL % 4 == 0) {
-                if (vec) {
+            for (int u = 0; u < SB; ++u) load_row(a.L + ((size_t)min(s0 + u, a.S - 1) * a.T + tc) * E, pv[u]);
 #pragma unroll
-                    for (int i = 0; i < EPL; i += 4) {
-                        const float4 q = *reinterpret_cast<const float4*>(row + lane * EPL + i);
-                        pv[u][i] = q.x;
-                        pv[u][i + 1] = q.y;
-                        pv[u][i + 2] = q.z;
-                        pv[u][i + 3] = q.w;
-                    }
-                    continue;
-                }
-            }
+            for (int u = 0; u < SB; ++u)
+                if (s0 + u < a.S)
 #pragma unroll
-            for (int i = 0; i < EPL; ++i) pv[u][i] = row[min(lane * EPL + i, E - 1)];
+                    for (int i = 0; i < EPL; ++i) lv[i] = u == 0 && s0 == 0 ? pv[0][i] : lv[i] + pv[u][i];
         }
+    };
+    if (EPL % 4 == 0 && E == kWave * EPL) {
+        add_slices([&](const float* row, float (&v)[EPL]) __attribute__((always_inline)) {
 #pragma unroll
-        for (int u = 0; u < SB; ++u)
-            if (s0 + u < a.S)
+            for (int i = 0; i < EPL; i += 4) {
+                const float4 q = *reinterpret_cast<const float4*>(row + lane * EPL + (i & ~3));
+                v[i] = q.x;
+                v[(i + 1) % EPL] = q.y;
+                v[(i + 2) % EPL] = q.z;
+                v[(i + 3) % EPL] = q.w;
+            }
+        });
+    } else {
+        add_slices([&](const float* row, float (&v)[EPL]) __attribute__((always_inline)) {
 #pragma unroll
-                for (int i = 0; i < EPL; ++i) lv[i] = u == 0 && s0 == 0 ? pv[0][i] : lv[i] + pv[u][i];
+            for (int i = 0; i < EPL; ++i) v[i] = row[min(lane * EPL + i, E - 1)];
+        });
     }
 
     float key[EPL], val[EPL];
