@@ -17,9 +17,10 @@ typedef float v4f_t __attribute__((ext_vector_type(4)));
 
 // Grid (column blocks of 256 floats, tokens); one wave per block, one float4
 // column per lane. The token's weights and row indices are uniform loads.
-// Slots go in batches of 8 whose rows are all loaded before the first is
-// added (a dropped slot loads row 0 and adds nothing), so the loads overlap;
-// the sum still runs in slot order.
+// Slots go in batches of 16 whose rows are all loaded before the first is
+// added (a slot past k or dropped by top-p loads nothing; every such test is
+// the same for the whole wave), so the loads overlap; the sum still runs in
+// slot order.
 __global__ __launch_bounds__(64) void combine_kernel(const float* __restrict__ y, const float* __restrict__ w,
                                                      const int* __restrict__ inv_perm,
                                                      const float* __restrict__ shared_y,
@@ -34,13 +35,15 @@ __global__ __launch_bounds__(64) void combine_kernel(const float* __restrict__ y
     const bool col_in = c0 < (d >> 2);
     const int c = col_in ? c0 : 0;
     float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-    constexpr int kB = 8;
-    for (int j0 = 0; j0 < k; j0 += kB) {
-        // lane u < kB fetches slot j0 + u's row and weight (clamped index),
-        // then every lane reads them from lane u: one load each for the batch
+    constexpr int kB = 16;
+    // lane u < kB fetches slot j0 + u's row and weight (clamped index), then
+    // every lane reads them from lane u: one load each for a batch
+    auto slot_loads = [&](int j0, int& rl, float& wl) __attribute__((always_inline)) {
         const int jl = min(j0 + (int)(threadIdx.x % kB), k - 1);
-        const int rl = inv_perm[(size_t)t * k + jl];   // -1: dropped by top-p
-        const float wl = w[(size_t)t * k + jl];
+        rl = inv_perm[(size_t)t * k + jl];   // -1: dropped by top-p
+        wl = w[(size_t)t * k + jl];
+    };
+    auto batch = [&](int j0, int rl, float wl) __attribute__((always_inline)) {
         float4 v[kB];
         float wv[kB];
         bool use[kB];
@@ -49,9 +52,12 @@ __global__ __launch_bounds__(64) void combine_kernel(const float* __restrict__ y
             const int row = __builtin_amdgcn_readlane(rl, u);
             use[u] = j0 + u < k && row >= 0;
             wv[u] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wl), u));
-            // expert outputs are read once: non-temporal loads
-            const v4f_t nv = __builtin_nontemporal_load(reinterpret_cast<const v4f_t*>(y + (size_t)(use[u] ? row : 0) * d) + c);
-            v[u] = make_float4(nv[0], nv[1], nv[2], nv[3]);
+            v[u] = make_float4(0.f, 0.f, 0.f, 0.f);
+            if (use[u]) {
+                // expert outputs are read once: non-temporal loads
+                const v4f_t nv = __builtin_nontemporal_load(reinterpret_cast<const v4f_t*>(y + (size_t)row * d) + c);
+                v[u] = make_float4(nv[0], nv[1], nv[2], nv[3]);
+            }
         }
 #pragma unroll
         for (int u = 0; u < kB; ++u) {
@@ -61,9 +67,22 @@ __global__ __launch_bounds__(64) void combine_kernel(const float* __restrict__ y
             acc.z = fmaf(wv[u], v[u].z, acc.z);
             acc.w = fmaf(wv[u], v[u].w, acc.w);
         }
+    };
+    // one batch covers the usual k (no loop for the compiler to wait at);
+    // the shared expert's row goes out right after its indices
+    int rl;
+    float wl;
+    slot_loads(0, rl, wl);
+    // (without a shared expert the load reads Y's first row and is unused:
+    // an unconditional load keeps the count of loads in flight the same on
+    // every path, so that the wait for the indices does not also wait for it)
+    const float4 s = reinterpret_cast<const float4*>(shared_y ? shared_y + (size_t)t * d : y)[c];
+    batch(0, rl, wl);
+    for (int j0 = kB; j0 < k; j0 += kB) {
+        slot_loads(j0, rl, wl);
+        batch(j0, rl, wl);
     }
     if (shared_y) {
-        const float4 s = reinterpret_cast<const float4*>(shared_y + (size_t)t * d)[c];
         if (sgl) {
             float z = 0.0f;
             for (int i = 0; i < sgl_slices; ++i) z += sgl[(size_t)i * T + t];

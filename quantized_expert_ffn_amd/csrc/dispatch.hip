@@ -520,11 +520,9 @@ __global__ __launch_bounds__(kDispThreads) void dispatch_scan_kernel(int* __rest
     __shared__ int scan_tmp[kDispWaves + 1];
     const int tid = threadIdx.x;
     const int n = T * k;
-    // the chunks' bad-id flags, spread over the threads so that their loads
-    // overlap the counts' loads below
-    int bad = 0;
-    if (slots)
-        for (int c = tid; c < nch; c += kDispThreads) bad |= chunk_bad[c];
+    // the chunks' bad-id flags, one per thread (more, rarely, after the
+    // scan), so that the load overlaps the counts' loads below
+    int bad = (slots && tid < nch) ? chunk_bad[tid] : 0;
     int cnt = 0;
     if (tid < E) {
         // 32 chunks' loads in flight at a time (40 chunks for a 4096-token,
@@ -553,6 +551,7 @@ __global__ __launch_bounds__(kDispThreads) void dispatch_scan_kernel(int* __rest
         for (int t = tid; t < T; t += kDispThreads) row_token[n + t] = t;
     if (slots) {
         build_work_lists(E, cnt, off, n, T, has_shared, tile_rows, slots, tiles, meta);
+        for (int c = tid + kDispThreads; c < nch; c += kDispThreads) bad |= chunk_bad[c];
         const int any_bad = __syncthreads_or(bad);
         if (tid == 0) meta[2] = any_bad;
     }
