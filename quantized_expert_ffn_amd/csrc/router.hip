@@ -347,16 +347,16 @@ __global__ __launch_bounds__(256) void rmsnorm_kernel(const float* __restrict__ 
 // f32 path's preparation (a power per 32-column group over all rows), waves
 // past the rows do that job.
 //
-// router_logits_f16_kernel: block = kRBM tokens x kRBN experts, four waves of
-// 64 tokens x 32 experts (4 x 2 products of 16 x 16 per part pair);
+// router_logits_f16_kernel<RBN>: block = kRBM tokens x RBN experts (64, or
+// 128 where E > 64), RBN / 16 waves of 64 tokens x 32 experts (4 x 2
+// products of 16 x 16 per part pair);
 // blockIdx.z = slice. The slice goes through LDS kRKC = 32 k (one product) at
 // a time, the next chunk's loads in flight while the current one is
 // multiplied; the products of the parts are added small ones first, and the
 // sum is scaled by the two rows' powers (exact). Rows past T or E read a
 // valid row and are never stored.
 // ---------------------------------------------------------------------------
-constexpr int kRBM = 128, kRBN = 64, kRKC = 32;
-constexpr int kRPad = kRKC + 8;   // LDS row stride (f16): 16-byte reads of 16 rows hit distinct banks
+constexpr int kRBM = 128, kRKC = 32;
 
 // one row (X row t, or gate row e) by one wave: 8 values per lane and pass
 // of 512. NP > 0: the row has at most NP passes and stays in registers (all
@@ -462,12 +462,18 @@ __global__ __launch_bounds__(256) void router_prep_kernel(const float* __restric
     }
 }
 
-__global__ __launch_bounds__(256) void router_logits_f16_kernel(const RouterParts rp, int T, int E, int kslice,
-                                                                float* __restrict__ L) {
-    // [part][row][k], parts hi, lo
-    __shared__ __attribute__((aligned(16))) _Float16 xs[2][kRBM * kRPad];
-    __shared__ __attribute__((aligned(16))) _Float16 wsh[2][kRBN * kRPad];
-    static_assert(kRBM == 128 && kRBN == 64, "two token rows and one expert row per thread");
+template <int RBN>
+__global__ __launch_bounds__(4 * RBN) void router_logits_f16_kernel(const RouterParts rp, int T, int E, int kslice,
+                                                                    float* __restrict__ L) {
+    // [part][16-row tile][64 lanes][8 halves], parts hi, lo: lane l = r + 16 h
+    // of a tile holds row r, k 8 h .. 8 h + 7 (the matrix-core operand as it
+    // is read: every 16-byte read and write of a wave covers 1 KB without bank
+    // conflicts)
+    __shared__ __attribute__((aligned(16))) _Float16 xs[2 * kRBM * kRKC];
+    __shared__ __attribute__((aligned(16))) _Float16 wsh[2 * RBN * kRKC];
+    constexpr int kThreads = 4 * RBN;           // RBN / 16 waves
+    constexpr int kXR = kRBM * 4 / kThreads;    // token rows per thread (one expert row each)
+    static_assert(kRBM == 128 && (RBN == 64 || RBN == 128), "tile shapes");
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int wm = wave & 1, wn = wave >> 1;
     // XCD-aware order (blocks go to the 8 XCDs in turn by linear id): every
@@ -479,30 +485,40 @@ __global__ __launch_bounds__(256) void router_logits_f16_kernel(const RouterPart
     const int sl = lin >> 3, col = sl % ncol;
     const int tb = ((sl / ncol) * 8 + (lin & 7)) * kRBM;
     if (tb >= T) return;
-    const int eb = (col % gridDim.x) * kRBN;
+    const int eb = (col % gridDim.x) * RBN;
     const int ks = col / gridDim.x;
     const int dp = rp.dp;
     const int kbeg = ks * kslice, kend = min(dp, kbeg + kslice);
-    // loads: rows lr and lr + 64 of the token tile and row lr of the expert
-    // tile, halves 8 lq .. 8 lq + 7 of each 32-wide chunk (dp % 32 == 0 and
-    // kslice % 64 == 0: every chunk is whole); rows past T or E read the last
-    // valid row (never stored)
+    // loads: token rows lr + (kThreads / 4) j and expert row lr, halves
+    // 8 lq .. 8 lq + 7 of each 32-wide chunk (four neighbouring lanes read one
+    // row's 64 bytes); dp % 32 == 0 and kslice % 64 == 0: every chunk is
+    // whole; rows past T or E read the last valid row (never stored)
     const int lr = tid >> 2, lq = (tid & 3) * 8;
-    const size_t xr0 = (size_t)min(tb + lr, T - 1) * dp + lq, xr1 = (size_t)min(tb + lr + 64, T - 1) * dp + lq;
+    size_t xr[kXR];
+#pragma unroll
+    for (int j = 0; j < kXR; ++j) xr[j] = (size_t)min(tb + lr + (kThreads / 4) * j, T - 1) * dp + lq;
     const size_t wrow = (size_t)min(eb + lr, E - 1) * dp + lq;
-    uint4 xh0, xh1, xl0, xl1, wh0, wl0;
+    uint4 xh[kXR], xl[kXR], wh0, wl0;
+    // LDS position (16-byte units) of row r % 16 of a tile, halves 8 h ..:
+    // slot r + 16 h with r XOR (4 h ^ (h & 2)). Each 8 (and 16) lanes of a
+    // write (two (four) rows x four quads) and of a read (eight (sixteen)
+    // rows, one quad) then land in 8 (16) different 16-byte bank groups.
+    auto pos = [](int r, int h) { return ((r & 15) ^ (4 * h ^ (h & 2))) + 16 * h; };
+    const int hq = tid & 3;
     auto ld16 = [](const _Float16* p) { return *reinterpret_cast<const uint4*>(p); };
-    auto gload = [&](int k0) {
-        xh0 = ld16(rp.xh + xr0 + k0);
-        xh1 = ld16(rp.xh + xr1 + k0);
-        xl0 = ld16(rp.xl + xr0 + k0);
-        xl1 = ld16(rp.xl + xr1 + k0);
+    auto gload = [&](int k0) __attribute__((always_inline)) {
+#pragma unroll
+        for (int j = 0; j < kXR; ++j) {
+            xh[j] = ld16(rp.xh + xr[j] + k0);
+            xl[j] = ld16(rp.xl + xr[j] + k0);
+        }
         wh0 = ld16(rp.wh + wrow + k0);
         wl0 = ld16(rp.wl + wrow + k0);
     };
     // operand rows of this lane: tokens 64 wm + 16 i + (lane % 16), experts
-    // 32 wn + 16 j + (lane % 16); k 8 (lane / 16) .. + 7 of the chunk
-    const int orow = lane & 15, ok8 = (lane >> 4) * 8;
+    // 32 wn + 16 j + (lane % 16); k 8 (lane / 16) .. + 7 of the chunk, at
+    // position rl of each tile
+    const int orow = lane & 15, rl = pos(orow, lane >> 4);
     v4f acc[4][2];
 #pragma unroll
     for (int i = 0; i < 4; ++i)
@@ -511,12 +527,14 @@ __global__ __launch_bounds__(256) void router_logits_f16_kernel(const RouterPart
     if (kbeg < kend) gload(kbeg);
     for (int k0 = kbeg; k0 < kend; k0 += kRKC) {
         __syncthreads();   // the previous chunk's readers are done
-        *reinterpret_cast<uint4*>(&xs[0][lr * kRPad + lq]) = xh0;
-        *reinterpret_cast<uint4*>(&xs[0][(lr + 64) * kRPad + lq]) = xh1;
-        *reinterpret_cast<uint4*>(&xs[1][lr * kRPad + lq]) = xl0;
-        *reinterpret_cast<uint4*>(&xs[1][(lr + 64) * kRPad + lq]) = xl1;
-        *reinterpret_cast<uint4*>(&wsh[0][lr * kRPad + lq]) = wh0;
-        *reinterpret_cast<uint4*>(&wsh[1][lr * kRPad + lq]) = wl0;
+#pragma unroll
+        for (int j = 0; j < kXR; ++j) {
+            const int rr = lr + (kThreads / 4) * j;
+            *reinterpret_cast<uint4*>(&xs[((rr >> 4) * 64 + pos(rr, hq)) * 8]) = xh[j];
+            *reinterpret_cast<uint4*>(&xs[(((kRBM >> 4) + (rr >> 4)) * 64 + pos(rr, hq)) * 8]) = xl[j];
+        }
+        *reinterpret_cast<uint4*>(&wsh[((lr >> 4) * 64 + pos(lr, hq)) * 8]) = wh0;
+        *reinterpret_cast<uint4*>(&wsh[(((RBN >> 4) + (lr >> 4)) * 64 + pos(lr, hq)) * 8]) = wl0;
         // the next chunk's loads go out before the barrier: they have the
         // wait and this chunk's products to arrive
         if (k0 + kRKC < kend) gload(k0 + kRKC);
@@ -527,13 +545,13 @@ __global__ __launch_bounds__(256) void router_logits_f16_kernel(const RouterPart
         for (int j = 0; j < 2; ++j)
 #pragma unroll
             for (int p = 0; p < 2; ++p)
-                b[j][p] = *reinterpret_cast<const v8h*>(&wsh[p][(32 * wn + 16 * j + orow) * kRPad + ok8]);
+                b[j][p] = *reinterpret_cast<const v8h*>(&wsh[((p * (RBN >> 4) + 2 * wn + j) * 64 + rl) * 8]);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             v8h a[2];
 #pragma unroll
             for (int p = 0; p < 2; ++p)
-                a[p] = *reinterpret_cast<const v8h*>(&xs[p][(64 * wm + 16 * i + orow) * kRPad + ok8]);
+                a[p] = *reinterpret_cast<const v8h*>(&xs[((p * (kRBM >> 4) + 4 * wm + i) * 64 + rl) * 8]);
 #pragma unroll
             for (int j = 0; j < 2; ++j) {
                 // the small terms first
@@ -644,8 +662,12 @@ hipError_t launch_router_logits(const float* x, int T, int d, const float* wg, i
 #undef MOE_PREP
     const hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
-    const dim3 grid((E + kRBN - 1) / kRBN, ((T + kRBM - 1) / kRBM + 7) / 8 * 8, S);
-    hipLaunchKernelGGL(router_logits_f16_kernel, grid, dim3(256), 0, st, *rp, T, E, router_kslice(d, S), logits);
+    const int gy = ((T + kRBM - 1) / kRBM + 7) / 8 * 8, kslice = router_kslice(d, S);
+    if (E > 64)
+        hipLaunchKernelGGL(router_logits_f16_kernel<128>, dim3((E + 127) / 128, gy, S), dim3(512), 0, st, *rp, T, E,
+                           kslice, logits);
+    else
+        hipLaunchKernelGGL(router_logits_f16_kernel<64>, dim3(1, gy, S), dim3(256), 0, st, *rp, T, E, kslice, logits);
     return hipGetLastError();
 }
 
