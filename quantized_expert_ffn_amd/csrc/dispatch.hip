@@ -168,9 +168,18 @@ __device__ __forceinline__ void build_work_lists(int E, int cnt, int off, int n_
     const int s_cls = s_part > 0 ? tile_class(s_part, tile_rows) : -1;
     const int run = (n_full + s_full + 7) / 8;                    // full tiles per XCD
     auto fpos = [run](int f) { return (f % run) * 8 + f / run; };  // f-th full tile -> position
-    for (int i = 0; i < full; ++i) {
-        const int rb = off + i * tile_rows;
-        tl[fpos(fbase + i)] = make_int4(e, rb, rb + tile_rows, 0);
+    if (full > 0) {   // then run >= 1
+        // fpos(fbase + i) for i = 0, 1, ...: one division, then the quotient
+        // and remainder step by one (a popular expert has tens of tiles)
+        int q = fbase / run, r = fbase - (fbase / run) * run;
+        for (int i = 0; i < full; ++i) {
+            const int rb = off + i * tile_rows;
+            tl[r * 8 + q] = make_int4(e, rb, rb + tile_rows, 0);
+            if (++r == run) {
+                r = 0;
+                ++q;
+            }
+        }
     }
     for (int i = threadIdx.x; i < s_full; i += blockDim.x) {
         const int rb = n_rows_routed + i * tile_rows;
@@ -506,9 +515,9 @@ __global__ __launch_bounds__(256) void dispatch_rank_kernel(const int* __restric
     if (tid == 0) chunk_bad[c] = bad_any;
 }
 
-// 2. one block: per expert, chunk offsets (exclusive over chunks, in place;
-//    32 chunks' loads at a time) and the count; offsets over experts. Then the
-//    perm tail, the shared rows of row_token and the work lists.
+// 2. one block: per expert, chunk offsets (exclusive over chunks, in place)
+//    and the count; offsets over experts. Then the perm tail, the shared rows
+//    of row_token and the work lists.
 __global__ __launch_bounds__(kDispThreads) void dispatch_scan_kernel(int* __restrict__ chunk_hist,
                                                                      const int* __restrict__ chunk_bad, int nch,
                                                                      int T, int k, int E, int* __restrict__ counts,
@@ -524,10 +533,36 @@ __global__ __launch_bounds__(kDispThreads) void dispatch_scan_kernel(int* __rest
     // scan), so that the load overlaps the counts' loads below
     int bad = (slots && tid < nch) ? chunk_bad[tid] : 0;
     int cnt = 0;
-    if (tid < E) {
-        // 32 chunks' loads in flight at a time (40 chunks for a 4096-token,
-        // top-10 prefill: two round trips instead of five)
-        constexpr int kB = 32;
+    constexpr int kB = 32;
+    if (2 * E <= kDispThreads && nch <= 2 * kB) {
+        // two threads per expert, each with half of the chunks: one round of
+        // loads; thread e (< E) ends with the total, thread e + 512 offsets
+        // its half's prefixes by the first half's sum
+        __shared__ int half_sum[2][kDispThreads / 2];
+        constexpr int kHalf = kDispThreads / 2;
+        const int part = tid / kHalf, e = tid - part * kHalf;
+        const int nh = (nch + 1) / 2, cb = part * nh, nmine = min(nch, cb + nh) - cb;
+        int v[kB];
+#pragma unroll
+        for (int u = 0; u < kB; ++u) v[u] = (e < E && u < nmine) ? chunk_hist[(size_t)(cb + u) * E + e] : 0;
+        int local = 0;
+#pragma unroll
+        for (int u = 0; u < kB; ++u) {
+            const int x = v[u];
+            v[u] = local;
+            local += x;
+        }
+        if (e < E) half_sum[part][e] = local;
+        __syncthreads();
+        const int base = (part == 1 && e < E) ? half_sum[0][e] : 0;
+        if (e < E) {
+#pragma unroll
+            for (int u = 0; u < kB; ++u)
+                if (u < nmine) chunk_hist[(size_t)(cb + u) * E + e] = base + v[u];
+        }
+        if (part == 0 && e < E) cnt = local + half_sum[1][e];
+    } else if (tid < E) {
+        // 32 chunks' loads in flight at a time
         for (int c0 = 0; c0 < nch; c0 += kB) {
             int v[kB];
 #pragma unroll
