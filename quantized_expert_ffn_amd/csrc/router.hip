@@ -469,8 +469,10 @@ __global__ __launch_bounds__(4 * RBN) void router_logits_f16_kernel(const Router
     // of a tile holds row r, k 8 h .. 8 h + 7 (the matrix-core operand as it
     // is read: every 16-byte read and write of a wave covers 1 KB without bank
     // conflicts)
-    __shared__ __attribute__((aligned(16))) _Float16 xs[2 * kRBM * kRKC];
-    __shared__ __attribute__((aligned(16))) _Float16 wsh[2 * RBN * kRKC];
+    // two buffers: chunk c + 1 is stored into one while chunk c is multiplied
+    // out of the other, one barrier per chunk
+    __shared__ __attribute__((aligned(16))) _Float16 xsb[2][2 * kRBM * kRKC];
+    __shared__ __attribute__((aligned(16))) _Float16 wsb[2][2 * RBN * kRKC];
     constexpr int kThreads = 4 * RBN;           // RBN / 16 waves
     constexpr int kXR = kRBM * 4 / kThreads;    // token rows per thread (one expert row each)
     static_assert(kRBM == 128 && (RBN == 64 || RBN == 128), "tile shapes");
@@ -524,9 +526,7 @@ __global__ __launch_bounds__(4 * RBN) void router_logits_f16_kernel(const Router
     for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int j = 0; j < 2; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
-    if (kbeg < kend) gload(kbeg);
-    for (int k0 = kbeg; k0 < kend; k0 += kRKC) {
-        __syncthreads();   // the previous chunk's readers are done
+    auto stage = [&](_Float16* xs, _Float16* wsh) __attribute__((always_inline)) {
 #pragma unroll
         for (int j = 0; j < kXR; ++j) {
             const int rr = lr + (kThreads / 4) * j;
@@ -535,11 +535,8 @@ __global__ __launch_bounds__(4 * RBN) void router_logits_f16_kernel(const Router
         }
         *reinterpret_cast<uint4*>(&wsh[((lr >> 4) * 64 + pos(lr, hq)) * 8]) = wh0;
         *reinterpret_cast<uint4*>(&wsh[(((RBN >> 4) + (lr >> 4)) * 64 + pos(lr, hq)) * 8]) = wl0;
-        // the next chunk's loads go out before the barrier: they have the
-        // wait and this chunk's products to arrive
-        if (k0 + kRKC < kend) gload(k0 + kRKC);
-        __syncthreads();
-        __builtin_amdgcn_sched_barrier(0);
+    };
+    auto multiply = [&](const _Float16* xs, const _Float16* wsh) __attribute__((always_inline)) {
         v8h b[2][2];
 #pragma unroll
         for (int j = 0; j < 2; ++j)
@@ -560,6 +557,26 @@ __global__ __launch_bounds__(4 * RBN) void router_logits_f16_kernel(const Router
                 acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[0], b[j][0], acc[i][j], 0, 0, 0);
             }
         }
+    };
+    // chunk c lives in buffer c % 2; at step c the registers hold chunk c + 1,
+    // which goes into the other buffer (read last at step c - 1, before the
+    // barrier that ended it) while chunk c is multiplied; then the loads of
+    // chunk c + 2 go out
+    const int nchunk = kend > kbeg ? (kend - kbeg) / kRKC : 0;
+    if (nchunk > 0) {
+        gload(kbeg);
+        stage(xsb[0], wsb[0]);
+        if (nchunk > 1) gload(kbeg + kRKC);
+        __syncthreads();
+    }
+    for (int c = 0; c < nchunk; ++c) {
+        const int cur = c & 1;
+        if (c + 1 < nchunk) {
+            stage(xsb[cur ^ 1], wsb[cur ^ 1]);
+            if (c + 2 < nchunk) gload(kbeg + (c + 2) * kRKC);
+        }
+        multiply(xsb[cur], wsb[cur]);
+        __syncthreads();
     }
     // output lane l, register r: token 4 (l / 16) + r, expert l % 16 of the
     // tile pair; the rows' powers first (all loads out together), then the
