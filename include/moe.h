@@ -234,7 +234,10 @@ moe_status moe_quantize_q8_0(const float* x, int64_t rows, int32_t cols,
  *            equal keys to the lower expert id.
  *   topk_w   device fp32 [T, k]: the weight of each selected expert.
  *            With top_p, dropped slots hold -1 and 0.
- *   ws       device workspace (moe_workspace_size with this T, k, E, d).
+ *   ws       device workspace, 16-byte aligned: moe_workspace_size with this
+ *            T, k, E and d (d rounded up to a multiple of 32 where it is not
+ *            one) is enough. It holds the logits' slice sums first, then for
+ *            T > 16 the f16 operand parts of the matrix-core router.
  * Logits are fp32 on the GPU; a selection whose margin lies within fp32
  * rounding of the logits may differ from an exact-arithmetic ranking.
  */

@@ -192,6 +192,58 @@ def test_route_full_size(name, tokens):
     check_route(synth.activations(lay, tokens), synth.gate_weight(lay), router_spec(lay), synth.score_bias(lay))
 
 
+def router_slices(T, E, d):
+    """How many d-slices the router's logits come in for a batch of T
+    (moe_route, no RMSNorm): the library's own choice, restated; a wrong
+    count would make the sums below wrong and the test fail."""
+    if T <= 16:
+        if T <= 4:
+            return 1
+        u = -(-d // 256)
+        pu = -(-u // 8)
+        return -(-u // pu)
+    tiles = -(-T // 128) * -(-E // 64)
+    return max(1, min(-(-1024 // tiles), max(d // 128, 1)))
+
+
+@pytest.mark.parametrize("T,E,d,name", [(1, 64, 2048, None), (8, 64, 2048, None), (16, 512, 2048, None),
+                                        (300, 64, 2048, None), (300, 512, 2048, None), (200, 100, 196, None),
+                                        (4096, 512, 2048, "qwen")])
+def test_route_logits_values(T, E, d, name):
+    """The router's logits (the slice sums moe_route leaves at the start of
+    its workspace) against fp64 X Wg^T, within 1e-6 of sum_k |x_k w_k| for
+    every logit: each decode path multiplies in fp32, the prefill path f16
+    hi/lo parts of each value with a power of two per row (products within
+    about 2^-21 of x w), all of them sum in fp32. Shapes cover the one-row,
+    split-d and matrix-core logits kernels, both tile widths of the last,
+    and rows that are not a multiple of 32 (padded parts)."""
+    need_gpu()
+    if name:
+        lay = synth.LAYERS[name]
+        x, wg = synth.activations(lay, T), synth.gate_weight(lay)
+    else:
+        rng = np.random.default_rng(T * 7 + E)
+        x = (rng.standard_normal((T, d)) * rng.uniform(0.01, 100, (T, 1))).astype(np.float32)
+        wg = (rng.standard_normal((E, d)) * 0.02).astype(np.float32)
+    params = qe.router_params(E, min(8, E), "softmax", False)
+    xd = torch.from_numpy(np.ascontiguousarray(x)).cuda()
+    wgd = torch.from_numpy(np.ascontiguousarray(wg)).cuda()
+    idx = torch.empty((T, params.top_k), dtype=torch.int32, device="cuda")
+    w = torch.empty((T, params.top_k), dtype=torch.float32, device="cuda")
+    # (the workspace of d rounded up to 32 covers moe_route's need for d)
+    ws = qe.workspace(T, params.top_k, E, -(-d // 32) * 32, 32, qe.MOE_ACT_F32, False)
+    qe.moe_route(xd, wgd, params, idx, w, ws)
+    torch.cuda.synchronize()
+    S = router_slices(T, E, d)
+    raw = ws.detach().cpu().numpy().view(np.uint8)[:S * T * E * 4].view(np.float32).reshape(S, T, E)
+    got = raw.astype(np.float64).sum(axis=0)
+    ref = x.astype(np.float64) @ wg.astype(np.float64).T
+    scale = np.abs(x).astype(np.float64) @ np.abs(wg).astype(np.float64).T
+    err = np.abs(got - ref) / (scale + 1e-30)
+    say(f"[route logits] T={T} E={E} d={d} slices={S}: max error {err.max():.2e} of sum |x w|")
+    assert err.max() <= 1e-6
+
+
 # ---------------------------------------------------------------------------
 # dispatch
 # ---------------------------------------------------------------------------
