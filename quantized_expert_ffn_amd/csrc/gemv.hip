@@ -123,7 +123,10 @@ __global__ __launch_bounds__(64 * KS) void gemv_kernel(const GemvArgs a) {
     const int n_tiles = N / kTile;
     int tile[2];
     tile[0] = GATEUP ? blockIdx.x : 2 * blockIdx.x;
-    tile[1] = GATEUP ? blockIdx.x : 2 * blockIdx.x + 1;   // may be n_tiles: reads as zeros, not stored
+    // down with an odd tile count: tile[1] of the last block is n_tiles, a
+    // phantom whose code loads land on real bytes but whose scales read as
+    // zeros (past the scale resource), so it adds zeros and is not stored
+    tile[1] = GATEUP ? blockIdx.x : 2 * blockIdx.x + 1;
 
     // operands through buffer resources: a lane offset per stream, the pair
     // step in a uniform register; offsets past a resource's end read as 0
